@@ -1,0 +1,217 @@
+"""Layer-sliced, block-quantised single-token decode on AMD MI355X (gfx950).
+
+Python front end of libslq (include/slice.h).  The functions and the Slice
+class marshal arguments for the C ABI; the work itself runs in libslq's HIP
+kernels on the caller's current torch stream.  Without the built library every
+call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+import torch
+
+from ._native import (Q4_0, Q8_0, TENSOR_IDS, SliceConfig, SliceError, check, lib)  # noqa: F401
+
+__all__ = ["Q4_0", "Q8_0", "SliceConfig", "SliceError", "Slice", "make_config",
+           "packed_bytes", "repack", "dequant", "gemv", "gemv_workspace_bytes", "lib"]
+
+
+def _stream(stream=None) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _dev(arr, device="cuda") -> torch.Tensor:
+    """numpy array -> contiguous device tensor with the same bytes."""
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+
+
+# ------------------------------------------------------------ kernel level
+
+def packed_bytes(qtype: int, rows: int, cols: int) -> int:
+    return int(lib().slq_packed_bytes(qtype, rows, cols))
+
+
+def repack(qtype: int, raw: torch.Tensor, rows: int, cols: int, stream=None) -> torch.Tensor:
+    """GGUF blocks (uint8 device tensor) -> packed device layout."""
+    n = packed_bytes(qtype, rows, cols)
+    if n == 0:
+        raise SliceError(-2, "bad qtype or shape")
+    out = torch.empty(n, dtype=torch.uint8, device=raw.device)
+    check(lib().slq_repack(qtype, _ptr(raw), rows, cols, _ptr(out), _stream(stream)))
+    return out
+
+
+def dequant(qtype: int, packed: torch.Tensor, rows: int, cols: int, stream=None) -> torch.Tensor:
+    out = torch.empty((rows, cols), dtype=torch.float32, device=packed.device)
+    check(lib().slq_dequant(qtype, _ptr(packed), rows, cols, _ptr(out), _stream(stream)))
+    return out
+
+
+def gemv_workspace_bytes(qtype: int, rows: int, cols: int, batch: int) -> int:
+    return int(lib().slq_gemv_workspace_bytes(qtype, rows, cols, batch))
+
+
+def gemv(qtype: int, packed: torch.Tensor, rows: int, cols: int, x: torch.Tensor,
+         out: torch.Tensor | None = None, ws: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """y = W x for x fp32 [batch, cols] (batch <= 16) -> y fp32 [batch, rows]."""
+    x2 = x.reshape(-1, cols)
+    b = x2.shape[0]
+    if out is None:
+        out = torch.empty((b, rows), dtype=torch.float32, device=x.device)
+    need = gemv_workspace_bytes(qtype, rows, cols, b)
+    if ws is None or ws.numel() < need:
+        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    check(lib().slq_gemv(qtype, _ptr(packed), rows, cols, b, _ptr(x2), _ptr(out), _ptr(ws), ws.numel(),
+                         _stream(stream)))
+    return out
+
+
+# ------------------------------------------------------------------- slice
+
+def make_config(shape, qtype: int, begin: int, end: int, *, max_seq: int = 1024, max_verify: int = 16,
+                io_fp32: bool = False, has_embed: bool = False, has_head: bool = False) -> SliceConfig:
+    """Build a slice_config from any object with the model-shape attributes."""
+    c = SliceConfig()
+    c.hidden = shape.hidden
+    c.n_layers = shape.n_layers
+    c.layer_begin, c.layer_end = begin, end
+    c.attn_period = shape.attn_period
+    c.dn_heads, c.dn_dk, c.dn_dv = shape.dn_heads, shape.dn_dk, shape.dn_dv
+    c.q_heads, c.kv_heads, c.head_dim = shape.q_heads, shape.kv_heads, shape.head_dim
+    c.rope_dims = shape.rope_dims
+    c.rope_theta = float(shape.rope_theta)
+    c.qk_norm = int(bool(shape.qk_norm))
+    c.attn_gate = int(bool(shape.attn_gate))
+    c.eps = float(shape.eps)
+    c.dn_a_scale, c.dn_a_bias = float(shape.dn_a_scale), float(shape.dn_a_bias)
+    c.dn_b_scale, c.dn_z_scale = float(shape.dn_b_scale), float(shape.dn_z_scale)
+    c.ffn = shape.ffn
+    c.vocab = shape.vocab
+    c.has_embed, c.has_head = int(has_embed), int(has_head)
+    c.tied_head = int(bool(shape.tied_head))
+    c.max_seq, c.max_verify = max_seq, max_verify
+    c.qtype = qtype
+    c.io_fp32 = int(io_fp32)
+    return c
+
+
+class Slice:
+    """A loaded layer slice: caller-owned weights and workspace on the GPU."""
+
+    def __init__(self, cfg: SliceConfig, device: str = "cuda", stream=None):
+        self.cfg = cfg
+        self.device = torch.device(device)
+        wb = int(lib().slice_weights_bytes(ctypes.byref(cfg)))
+        sb = int(lib().slice_workspace_bytes(ctypes.byref(cfg)))
+        if wb == 0 or sb == 0:
+            check(-1)
+        self.weights = torch.empty(wb, dtype=torch.uint8, device=self.device)
+        self.workspace = torch.empty(sb, dtype=torch.uint8, device=self.device)
+        h = ctypes.c_void_p()
+        check(lib().slice_load(ctypes.byref(cfg), _ptr(self.weights), _ptr(self.workspace), _stream(stream),
+                               ctypes.byref(h)))
+        self.handle = h
+        self.io_dtype = torch.float32 if cfg.io_fp32 else torch.float16
+
+    # ---- weights
+    def set_tensor(self, layer: int, name: str, t: torch.Tensor, stream=None):
+        t = t.contiguous()
+        check(lib().slice_set_tensor(self.handle, layer, TENSOR_IDS[name], _ptr(t), _stream(stream)))
+
+    def load_numpy(self, tensors: dict, glob: dict | None = None, stream=None):
+        """tensors: {layer: {name: np.ndarray}} (GGUF blocks or fp32 vectors); glob: embedding etc."""
+        for layer, d in tensors.items():
+            if not (self.cfg.layer_begin <= layer < self.cfg.layer_end):
+                continue
+            for name, arr in d.items():
+                t = _dev(arr, self.device)
+                self.set_tensor(layer, name, t, stream)
+                torch.cuda.current_stream().synchronize() if stream is None else stream.synchronize()
+                del t
+        for name, arr in (glob or {}).items():
+            if name == "embed" and not (self.cfg.has_embed or (self.cfg.has_head and self.cfg.tied_head)):
+                continue
+            if name in ("head", "out_norm") and not self.cfg.has_head:
+                continue
+            self.set_tensor(0, name, _dev(arr, self.device), stream)
+        torch.cuda.synchronize()
+
+    # ---- state
+    def reset(self, kv_len: int, stream=None):
+        check(lib().slice_reset(self.handle, kv_len, _stream(stream)))
+
+    def set_state(self, layer: int, S: torch.Tensor, stream=None):
+        S = S.to(device=self.device, dtype=torch.float32).contiguous()
+        check(lib().slice_dbg_set_state(self.handle, layer, _ptr(S), _stream(stream)))
+        torch.cuda.synchronize()
+
+    def get_state(self, layer: int, stream=None) -> torch.Tensor:
+        c = self.cfg
+        out = torch.empty((c.dn_heads, c.dn_dv, c.dn_dk), dtype=torch.float32, device=self.device)
+        check(lib().slice_dbg_get_state(self.handle, layer, _ptr(out), _stream(stream)))
+        return out
+
+    def set_kv(self, layer: int, K: torch.Tensor, V: torch.Tensor, stream=None):
+        K = K.to(self.device).contiguous().view(torch.int16)
+        V = V.to(self.device).contiguous().view(torch.int16)
+        check(lib().slice_dbg_set_kv(self.handle, layer, _ptr(K), _ptr(V), K.shape[1], _stream(stream)))
+        torch.cuda.synchronize()
+
+    def get_kv(self, layer: int, rows: int, stream=None):
+        c = self.cfg
+        K = torch.empty((c.kv_heads, rows, c.head_dim), dtype=torch.float16, device=self.device)
+        V = torch.empty_like(K)
+        check(lib().slice_dbg_get_kv(self.handle, layer, _ptr(K), _ptr(V), rows, _stream(stream)))
+        return K, V
+
+    # ---- steps
+    def decode(self, h_in: torch.Tensor, h_out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        if h_out is None:
+            h_out = torch.empty(self.cfg.hidden, dtype=self.io_dtype, device=self.device)
+        check(lib().slice_decode(self.handle, _ptr(h_in), _ptr(h_out), _stream(stream)))
+        return h_out
+
+    def verify(self, h_in: torch.Tensor, h_out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        k = h_in.shape[0]
+        if h_out is None:
+            h_out = torch.empty((k, self.cfg.hidden), dtype=self.io_dtype, device=self.device)
+        check(lib().slice_verify(self.handle, k, _ptr(h_in), _ptr(h_out), _stream(stream)))
+        return h_out
+
+    def commit(self, accepted: int, stream=None):
+        check(lib().slice_commit(self.handle, accepted, _stream(stream)))
+
+    def embed(self, tok: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty(self.cfg.hidden, dtype=self.io_dtype, device=self.device)
+        check(lib().slice_embed(self.handle, _ptr(tok), _ptr(out), _stream(stream)))
+        return out
+
+    def head_argmax(self, h: torch.Tensor, logits: torch.Tensor | None = None, tok: torch.Tensor | None = None,
+                    stream=None):
+        if tok is None:
+            tok = torch.empty(1, dtype=torch.int32, device=self.device)
+        check(lib().slice_head_argmax(self.handle, _ptr(h), _ptr(tok), _ptr(logits), _stream(stream)))
+        return tok
+
+    @property
+    def position(self) -> int:
+        return int(lib().slice_position(self.handle))
+
+    def free(self):
+        if getattr(self, "handle", None):
+            lib().slice_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.free()
+        except Exception:
+            pass

@@ -1,0 +1,109 @@
+// Device helpers shared by the kernels of libslq.
+#pragma once
+#include "slq.h"
+
+namespace slq {
+
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
+
+// Butterfly reductions: every lane ends with the same value, and the value does
+// not depend on the lane (each level adds commutative pairs).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+// over each 32-lane half separately
+__device__ __forceinline__ float half_max(float v) {
+#pragma unroll
+  for (int m = 16; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  return v;
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
+
+// RMSNorm factor from a producer's partial sums of squares (fixed order).
+__device__ __forceinline__ float rnorm_from(const NormIn& n, int t) {
+  if (!n.ssq) return 1.0f;
+  const float* s = n.ssq + (size_t)t * n.n_part;
+  float a = 0.0f;
+  for (int i = 0; i < n.n_part; ++i) a += s[i];
+  return 1.0f / sqrtf(a * n.inv_n + n.eps);
+}
+
+// Quantise one block of 32 activations held one per lane by a 32-lane half of
+// the wave (element e = lane & 31) into digits, in the order the weight codes
+// of format QT are packed.  Every lane of the wave must call this (shuffles);
+// `write` selects which halves store.
+//
+//   s = max|x| / M,  x_int = rint(x / s)  (|x_int| <= M),  u = x_int + OFF
+//   Q4_0: digit d = ((u >> 4d) & 15) - 8, nibble 2k of dword (d, m) <- element 4m+k,
+//         nibble 2k+1 <- element 4m+k+16  (byte j of a Q4_0 block holds weights j, j+16)
+//   Q8_0: digit d = ((u >> 8d) & 255) - 128, byte k of dword (d, m) <- element 4m+k
+template <int QT>
+__device__ __forceinline__ void quant_block_half(float v, int32_t* xd, float* xs, bool write) {
+  const int lane = threadIdx.x & 63;
+  const int e = lane & 31;
+  const int base = lane & 32;
+  const float M = QT == QT_Q4 ? M_Q4 : M_Q8;
+  const float amax = half_max(fabsf(v));
+  const float inv = amax > 0.0f ? M / amax : 0.0f;
+  // v * (M / amax) can round one unit past M for the largest entry; clamp so
+  // the digits stay in range (the clamped unit is below fp32 resolution of x)
+  const int Mi = QT == QT_Q4 ? 7829367 : 8355711;
+  const int xi = min(max((int)rintf(v * inv), -Mi), Mi);
+  const uint32_t u = (uint32_t)(xi + (QT == QT_Q4 ? 0x888888 : 0x808080));
+  uint32_t word = 0;
+  if (QT == QT_Q4) {
+    const int d = (e >> 2) % 6, m = e & 3;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t ul = (uint32_t)__shfl((int)u, base + 4 * m + k, 64);
+      const uint32_t uh = (uint32_t)__shfl((int)u, base + 4 * m + k + 16, 64);
+      const uint32_t nl = ((ul >> (4 * d)) & 15u) ^ 8u;
+      const uint32_t nh = ((uh >> (4 * d)) & 15u) ^ 8u;
+      word |= (nl | (nh << 4)) << (8 * k);
+    }
+  } else {
+    const int d = (e >> 3) % 3, m = e & 7;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t uk = (uint32_t)__shfl((int)u, base + 4 * m + k, 64);
+      word |= (((uk >> (8 * d)) & 255u) ^ 0x80u) << (8 * k);
+    }
+  }
+  if (write) {
+    if (e < XW) xd[e] = (int32_t)word;
+    if (e == 0) *xs = amax / M;
+  }
+}
+
+__device__ __forceinline__ void quant_block_half_qt(int qt, float v, int32_t* xd, float* xs, bool write) {
+  if (qt == QT_Q4) quant_block_half<QT_Q4>(v, xd, xs, write);
+  else quant_block_half<QT_Q8>(v, xd, xs, write);
+}
+
+// Shared tail of every producer of a residual-stream vector: lane holds h_new
+// for row rg*64+lane (0 beyond H).  Writes h, the sum of squares of the 64 rows,
+// and the digits of norm_w*h for blocks 2rg and 2rg+1.
+__device__ __forceinline__ void resid_tail(int t, int rg, int H, float hn, float* h, int64_t h_ts,
+                                           const float* norm_w, int qt, const Act& next,
+                                           float* ssq_out, int nrg) {
+  const int lane = threadIdx.x & 63;
+  const int row = rg * RG + lane;
+  if (row < H) h[(size_t)t * h_ts + row] = hn;
+  const float ss = wave_sum(hn * hn);
+  if (lane == 0) ssq_out[(size_t)t * nrg + rg] = ss;
+  const float w = row < H ? norm_w[row] : 0.0f;
+  const int blk = 2 * rg + (lane >> 5);
+  const bool wr = blk < next.nblk;
+  quant_block_half_qt(qt, w * hn, next.xd + ((size_t)t * next.nblk + blk) * XW,
+                      next.xs + (size_t)t * next.nblk + blk, wr);
+}
+
+}  // namespace slq

@@ -1,0 +1,255 @@
+// Streaming GEMV kernel template (included by the per-format instantiation units).
+//
+// Each lane owns one output row of a 64-row group and streams whole blocks of
+// that row with one 128-bit load per block; the activation is wave-uniform and
+// comes from scalar registers as integer digits, so every block's dot product
+// is an exact int32 sum (v_dot8c_i32_i4 for Q4_0, v_dot4c_i32_i8 for Q8_0) and
+// only the per-block scales are applied in fp32.  The waves of a workgroup split
+// K and are summed in LDS in wave order; every token of a batched call goes
+// through the same operations as a batch-1 call.
+#pragma once
+#include "dev.h"
+
+namespace slq {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int QT>
+struct TileRegs {
+  static constexpr int NH = QT == QT_Q4 ? 1 : 2;
+  u32x4 c[TB * NH];
+  u32x4 sc;
+};
+
+template <int QT>
+__device__ __forceinline__ void load_tile(const uint8_t* tile, int lane, int nb, TileRegs<QT>& r) {
+  constexpr int NH = TileRegs<QT>::NH;
+  const u32x4* cp = reinterpret_cast<const u32x4*>(tile) + lane;
+#pragma unroll
+  for (int b = 0; b < TB * NH; ++b)
+    if (b < nb * NH) r.c[b] = __builtin_nontemporal_load(cp + b * RG);
+  r.sc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + (size_t)nb * NH * RG * 16) + lane);
+}
+
+__device__ __forceinline__ float scale_of(const u32x4& sc, int b) {
+  const uint32_t w = b < 2 ? sc.x : b < 4 ? sc.y : b < 6 ? sc.z : sc.w;
+  const unsigned short hb = (unsigned short)((b & 1) ? (w >> 16) : (w & 0xffff));
+  return __half2float(__ushort_as_half(hb));
+}
+
+// Digits and scale of one activation block of one token (wave-uniform: SGPRs).
+struct XRegs {
+  int32_t d[XW];
+  float s;
+};
+
+__device__ __forceinline__ void load_x(const Act& x, int j, int blk, XRegs& r) {
+  const int32_t* X = x.xd + ((size_t)j * x.nblk + blk) * XW;
+#pragma unroll
+  for (int i = 0; i < XW; ++i) r.d[i] = X[i];
+  r.s = x.xs[(size_t)j * x.nblk + blk];
+}
+
+// Exact integer dot product of one block's codes with one token's digits, as
+// fp32.  The digit sums are combined Horner-style inside the accumulator:
+// ((a2 * 16) + a1) * 16 + a0 is a2*256 + a1*16 + a0 exactly.
+template <int QT>
+__device__ __forceinline__ float block_dot(const TileRegs<QT>& r, int b, const XRegs& X) {
+  if constexpr (QT == QT_Q4) {
+    const u32x4 c = r.c[b];
+    int h = __builtin_amdgcn_sdot8((int)c.x, X.d[20], 0, false);
+    h = __builtin_amdgcn_sdot8((int)c.y, X.d[21], h, false);
+    h = __builtin_amdgcn_sdot8((int)c.z, X.d[22], h, false);
+    h = __builtin_amdgcn_sdot8((int)c.w, X.d[23], h, false);
+    int l = __builtin_amdgcn_sdot8((int)c.x, X.d[8], 0, false);
+    l = __builtin_amdgcn_sdot8((int)c.y, X.d[9], l, false);
+    l = __builtin_amdgcn_sdot8((int)c.z, X.d[10], l, false);
+    l = __builtin_amdgcn_sdot8((int)c.w, X.d[11], l, false);
+    h *= 16;
+    l *= 16;
+    h = __builtin_amdgcn_sdot8((int)c.x, X.d[16], h, false);
+    h = __builtin_amdgcn_sdot8((int)c.y, X.d[17], h, false);
+    h = __builtin_amdgcn_sdot8((int)c.z, X.d[18], h, false);
+    h = __builtin_amdgcn_sdot8((int)c.w, X.d[19], h, false);
+    l = __builtin_amdgcn_sdot8((int)c.x, X.d[4], l, false);
+    l = __builtin_amdgcn_sdot8((int)c.y, X.d[5], l, false);
+    l = __builtin_amdgcn_sdot8((int)c.z, X.d[6], l, false);
+    l = __builtin_amdgcn_sdot8((int)c.w, X.d[7], l, false);
+    h *= 16;
+    l *= 16;
+    h = __builtin_amdgcn_sdot8((int)c.x, X.d[12], h, false);
+    h = __builtin_amdgcn_sdot8((int)c.y, X.d[13], h, false);
+    h = __builtin_amdgcn_sdot8((int)c.z, X.d[14], h, false);
+    h = __builtin_amdgcn_sdot8((int)c.w, X.d[15], h, false);
+    l = __builtin_amdgcn_sdot8((int)c.x, X.d[0], l, false);
+    l = __builtin_amdgcn_sdot8((int)c.y, X.d[1], l, false);
+    l = __builtin_amdgcn_sdot8((int)c.z, X.d[2], l, false);
+    l = __builtin_amdgcn_sdot8((int)c.w, X.d[3], l, false);
+    return __builtin_fmaf((float)h, 4096.0f, (float)l);
+  } else {
+    const u32x4 c0 = r.c[2 * b], c1 = r.c[2 * b + 1];
+    int a = 0, l;
+    // a2
+    a = __builtin_amdgcn_sdot4((int)c0.x, X.d[16], a, false);
+    a = __builtin_amdgcn_sdot4((int)c0.y, X.d[17], a, false);
+    a = __builtin_amdgcn_sdot4((int)c0.z, X.d[18], a, false);
+    a = __builtin_amdgcn_sdot4((int)c0.w, X.d[19], a, false);
+    a = __builtin_amdgcn_sdot4((int)c1.x, X.d[20], a, false);
+    a = __builtin_amdgcn_sdot4((int)c1.y, X.d[21], a, false);
+    a = __builtin_amdgcn_sdot4((int)c1.z, X.d[22], a, false);
+    a = __builtin_amdgcn_sdot4((int)c1.w, X.d[23], a, false);
+    // a1 * 256 + a0
+    l = __builtin_amdgcn_sdot4((int)c0.x, X.d[8], 0, false);
+    l = __builtin_amdgcn_sdot4((int)c0.y, X.d[9], l, false);
+    l = __builtin_amdgcn_sdot4((int)c0.z, X.d[10], l, false);
+    l = __builtin_amdgcn_sdot4((int)c0.w, X.d[11], l, false);
+    l = __builtin_amdgcn_sdot4((int)c1.x, X.d[12], l, false);
+    l = __builtin_amdgcn_sdot4((int)c1.y, X.d[13], l, false);
+    l = __builtin_amdgcn_sdot4((int)c1.z, X.d[14], l, false);
+    l = __builtin_amdgcn_sdot4((int)c1.w, X.d[15], l, false);
+    l *= 256;
+    l = __builtin_amdgcn_sdot4((int)c0.x, X.d[0], l, false);
+    l = __builtin_amdgcn_sdot4((int)c0.y, X.d[1], l, false);
+    l = __builtin_amdgcn_sdot4((int)c0.z, X.d[2], l, false);
+    l = __builtin_amdgcn_sdot4((int)c0.w, X.d[3], l, false);
+    l = __builtin_amdgcn_sdot4((int)c1.x, X.d[4], l, false);
+    l = __builtin_amdgcn_sdot4((int)c1.y, X.d[5], l, false);
+    l = __builtin_amdgcn_sdot4((int)c1.z, X.d[6], l, false);
+    l = __builtin_amdgcn_sdot4((int)c1.w, X.d[7], l, false);
+    return __builtin_fmaf((float)a, 65536.0f, (float)l);
+  }
+}
+
+// All blocks of one tile for T tokens.  The digits of the next (block, token)
+// are requested before the current one is used, so the scalar loads overlap
+// the dot products.
+template <int QT, int T>
+__device__ __forceinline__ void tile_math(const TileRegs<QT>& r, int nb, int kb, const Act& x,
+                                          float (&acc)[T]) {
+  XRegs cur, nxt;
+  load_x(x, 0, kb, cur);
+#pragma unroll
+  for (int b = 0; b < TB; ++b) {
+    if (b < nb) {
+      const float d = scale_of(r.sc, b);
+#pragma unroll
+      for (int j = 0; j < T; ++j) {
+        const bool more = (j + 1 < T) || (b + 1 < nb);
+        const float dsx = d * cur.s;
+        if (more) load_x(x, j + 1 < T ? j + 1 : 0, j + 1 < T ? kb + b : kb + b + 1, nxt);
+        const float bf = block_dot<QT>(r, b, cur);
+        acc[j] = __builtin_fmaf(bf, dsx, acc[j]);
+        if (more) cur = nxt;
+      }
+    }
+  }
+}
+
+template <int QT, int T, int EPI>
+__global__ __launch_bounds__(1024) void k_gemv(Packed W, Act x, NormIn nin, GemvOut out, int ksplit) {
+  constexpr int TBY = tile_bytes(QT);
+  __shared__ float red[16][RG];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int nw = blockDim.x >> 6;
+  const int rg = blockIdx.x / ksplit, ks = blockIdx.x % ksplit;
+  const int nblk = W.nblk(), ntiles = W.ntiles(), full = nblk / TB;
+  const int w0 = ntiles * ks / ksplit, w1 = ntiles * (ks + 1) / ksplit;
+  // tile range of this wave; readfirstlane keeps the loop and the digit
+  // addresses in scalar registers
+  const int t0 = __builtin_amdgcn_readfirstlane(w0 + (w1 - w0) * wave / nw);
+  const int t1 = __builtin_amdgcn_readfirstlane(w0 + (w1 - w0) * (wave + 1) / nw);
+  const uint8_t* base = W.w + (size_t)rg * rg_bytes(QT, W.cols);
+
+  float acc[T];
+#pragma unroll
+  for (int j = 0; j < T; ++j) acc[j] = 0.0f;
+
+  // full tiles, two register sets in turn so the next tile's loads overlap this tile's math
+  const int te = t1 < full ? t1 : full;
+  if (t0 < te) {
+    TileRegs<QT> A, B;
+    load_tile<QT>(base + (size_t)t0 * TBY, lane, TB, A);
+    for (int t = t0; t < te; t += 2) {
+      if (t + 1 < te) load_tile<QT>(base + (size_t)(t + 1) * TBY, lane, TB, B);
+      tile_math<QT, T>(A, TB, t * TB, x, acc);
+      if (t + 1 < te) {
+        if (t + 2 < te) load_tile<QT>(base + (size_t)(t + 2) * TBY, lane, TB, A);
+        tile_math<QT, T>(B, TB, (t + 1) * TB, x, acc);
+      }
+    }
+  }
+  // the ragged last tile (< 8 blocks), owned by whichever wave's range ends there
+  if (t1 > full) {
+    const int nb = nblk - full * TB;
+    TileRegs<QT> A;
+    load_tile<QT>(base + (size_t)full * TBY, lane, nb, A);
+    tile_math<QT, T>(A, nb, full * TB, x, acc);
+  }
+
+  // waves meet in LDS, summed in wave order
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    if (nw > 1) {
+      red[wave][lane] = acc[j];
+      __syncthreads();
+      if (wave == 0) {
+        float s = red[0][lane];
+        for (int w = 1; w < nw; ++w) s += red[w][lane];
+        acc[j] = s;
+      }
+      __syncthreads();
+    }
+  }
+  if (wave != 0) return;
+
+  const int64_t row = (int64_t)rg * RG + lane;
+  const bool rv = row < W.rows;
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    if constexpr (EPI == EPI_PARTIAL) {
+      if (rv) out.y[((size_t)ks * T + j) * out.y_tstride + row] = acc[j];
+    } else if constexpr (EPI == EPI_STORE) {
+      const float rn = rnorm_from(nin, j);
+      if (rv) out.y[(size_t)j * out.y_tstride + row] = acc[j] * rn;
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      // lanes 0..31: gate rows, lanes 32..63: the matching up rows
+      const float rn = rnorm_from(nin, j);
+      const float v = acc[j] * rn;
+      const float up = __shfl(v, (lane + 32) & 63, 64);
+      const float m = (v / (1.0f + expf(-v))) * up;
+      if (out.y && lane < 32) out.y[(size_t)j * out.y_tstride + rg * 32 + lane] = m;
+      quant_block_half_qt(out.next_qt, m, out.next.xd + ((size_t)j * out.next.nblk + rg) * XW,
+                          out.next.xs + (size_t)j * out.next.nblk + rg, lane < 32);
+    } else {  // EPI_RESID, whole K in this workgroup
+      const float hn = rv ? out.y[(size_t)j * out.y_tstride + row] + acc[j] : 0.0f;
+      resid_tail(j, rg, (int)W.rows, hn, out.y, out.y_tstride, out.norm_w, out.next_qt, out.next,
+                 out.ssq_out, W.nrg());
+    }
+  }
+}
+
+
+template <int QT, int EPI>
+hipError_t gemv_inst(const Packed& W, int T, Act x, NormIn nin, GemvOut out, int ksplit, int waves,
+                     hipStream_t s) {
+  dim3 grid((unsigned)(W.nrg() * ksplit)), block(64 * waves);
+  switch (T) {
+#define SLQ_T(n) case n: k_gemv<QT, n, EPI><<<grid, block, 0, s>>>(W, x, nin, out, ksplit); break;
+    SLQ_T(1) SLQ_T(2) SLQ_T(3) SLQ_T(4) SLQ_T(5) SLQ_T(6) SLQ_T(7) SLQ_T(8)
+    SLQ_T(9) SLQ_T(10) SLQ_T(11) SLQ_T(12) SLQ_T(13) SLQ_T(14) SLQ_T(15) SLQ_T(16)
+#undef SLQ_T
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+#define SLQ_DECLARE_GEMV(QT, EPI) \
+  extern template hipError_t gemv_inst<QT, EPI>(const Packed&, int, Act, NormIn, GemvOut, int, int, hipStream_t);
+SLQ_DECLARE_GEMV(QT_Q4, EPI_STORE) SLQ_DECLARE_GEMV(QT_Q4, EPI_PARTIAL)
+SLQ_DECLARE_GEMV(QT_Q4, EPI_SWIGLU) SLQ_DECLARE_GEMV(QT_Q4, EPI_RESID)
+SLQ_DECLARE_GEMV(QT_Q8, EPI_STORE) SLQ_DECLARE_GEMV(QT_Q8, EPI_PARTIAL)
+SLQ_DECLARE_GEMV(QT_Q8, EPI_SWIGLU) SLQ_DECLARE_GEMV(QT_Q8, EPI_RESID)
+#undef SLQ_DECLARE_GEMV
+
+}  // namespace slq

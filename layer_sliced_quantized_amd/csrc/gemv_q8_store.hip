@@ -1,0 +1,6 @@
+// Instantiation of the streaming GEMV for Q8_0 weights, epilogue STORE.
+#include "gemv_kernel.h"
+
+namespace slq {
+template hipError_t gemv_inst<QT_Q8, EPI_STORE>(const Packed&, int, Act, NormIn, GemvOut, int, int, hipStream_t);
+}  // namespace slq

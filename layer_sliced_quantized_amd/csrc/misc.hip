@@ -1,0 +1,138 @@
+// Boundary conversion, step control, embedding lookup and greedy argmax.
+//
+// A stage hands one token's hidden state on (5,120 x f16 on the pages' wire,
+// SwarmLLM README, bench paragraph); the first stage owns the embedding and
+// the last one the head and the sampling ("Unstable Legion", section
+// "Splitting the workload").  Sampling here is greedy, as in the pages'
+// benchmark rows ("Qwen 3.8 27B Q4_0, greedy").
+#include "dev.h"
+
+namespace slq {
+
+// h fp32 [T][H] -> boundary vector (fp16 round-to-nearest-even, or fp32 copy).
+__global__ void k_store_out(const float* __restrict__ h, int n, void* out, int fp32, Ctrl* ctrl,
+                            int advance) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (!out) out = ctrl->out;
+  if (i < n) {
+    if (fp32) reinterpret_cast<float*>(out)[i] = h[i];
+    else reinterpret_cast<__half*>(out)[i] = __float2half_rn(h[i]);
+  }
+  if (advance && i == 0) ctrl->pos += 1;
+}
+
+hipError_t launch_store_out(const float* h, int T, int H, void* out, int fp32, Ctrl* ctrl, int advance,
+                            hipStream_t s) {
+  const int n = T * H;
+  k_store_out<<<(n + 255) / 256, 256, 0, s>>>(h, n, out, fp32, ctrl, advance);
+  return hipGetLastError();
+}
+
+__global__ void k_ctrl_io(Ctrl* c, const void* in, void* out) {
+  c->in = in;
+  c->out = out;
+}
+
+hipError_t launch_ctrl_io(Ctrl* c, const void* in, void* out, hipStream_t s) {
+  k_ctrl_io<<<1, 1, 0, s>>>(c, in, out);
+  return hipGetLastError();
+}
+
+__global__ void k_ctrl_set(Ctrl* c, int pos, int cur) {
+  c->pos = pos;
+  c->cur = cur;
+}
+
+hipError_t launch_ctrl_set(Ctrl* c, int pos, int cur, hipStream_t s) {
+  k_ctrl_set<<<1, 1, 0, s>>>(c, pos, cur);
+  return hipGetLastError();
+}
+
+// Dequantise row *tok of a packed embedding table into a boundary vector.
+template <int QT>
+__global__ void k_embed(Packed E, const int32_t* __restrict__ tok, void* out, int fp32) {
+  constexpr int NH = QT == QT_Q4 ? 1 : 2;
+  const int b = blockIdx.x * blockDim.x + threadIdx.x;   // block along the row
+  const int nblk = E.nblk();
+  if (b >= nblk) return;
+  int64_t r = *tok;
+  if (r < 0 || r >= E.rows) r = 0;
+  const int64_t rg = r / RG;
+  const int lane = (int)(r % RG);
+  const int t = b / TB, bi = b % TB;
+  const int nb_t = min(TB, nblk - t * TB);
+  const uint8_t* tile = E.w + rg * rg_bytes(QT, E.cols) + (size_t)t * tile_bytes(QT);
+  const uint8_t* sc = tile + (size_t)nb_t * NH * RG * 16 + lane * 16 + bi * 2;
+  const float d = __half2float(__ushort_as_half((unsigned short)(sc[0] | (sc[1] << 8))));
+  float v[QK];
+  for (int h = 0; h < NH; ++h) {
+    const uint8_t* c = tile + (size_t)(bi * NH + h) * RG * 16 + lane * 16;
+    for (int j = 0; j < 16; ++j) {
+      if (QT == QT_Q4) {
+        v[j] = (float)((int)((c[j] & 15) ^ 8) - 8) * d;
+        v[j + 16] = (float)((int)((c[j] >> 4) ^ 8) - 8) * d;
+      } else {
+        v[h * 16 + j] = (float)(int8_t)c[j] * d;
+      }
+    }
+  }
+  for (int j = 0; j < QK; ++j) {
+    const int64_t i = (int64_t)b * QK + j;
+    if (fp32) reinterpret_cast<float*>(out)[i] = v[j];
+    else reinterpret_cast<__half*>(out)[i] = __float2half_rn(v[j]);
+  }
+}
+
+hipError_t launch_embed(const Packed& E, const int32_t* tok, void* out, int fp32, hipStream_t s) {
+  const int nblk = E.nblk();
+  if (E.qt == QT_Q4) k_embed<QT_Q4><<<(nblk + 63) / 64, 64, 0, s>>>(E, tok, out, fp32);
+  else k_embed<QT_Q8><<<(nblk + 63) / 64, 64, 0, s>>>(E, tok, out, fp32);
+  return hipGetLastError();
+}
+
+// Greedy argmax in two passes; the larger value wins, the lower index wins a tie.
+__device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
+  if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }
+}
+
+__device__ __forceinline__ void block_argmax(float& bv, int& bi) {
+  __shared__ float sv[16];
+  __shared__ int si[16];
+  for (int m = 32; m >= 1; m >>= 1) {
+    const float ov = __shfl_xor(bv, m, 64);
+    const int oi = __shfl_xor(bi, m, 64);
+    better(bv, bi, ov, oi);
+  }
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  if ((threadIdx.x & 63) == 0) { sv[w] = bv; si[w] = bi; }
+  __syncthreads();
+  bv = sv[0]; bi = si[0];
+  for (int k = 1; k < nw; ++k) better(bv, bi, sv[k], si[k]);
+}
+
+__global__ void k_argmax_part(const float* __restrict__ x, int n, float* pv, int* pi) {
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
+    better(bv, bi, x[i], i);
+  block_argmax(bv, bi);
+  if (threadIdx.x == 0) { pv[blockIdx.x] = bv; pi[blockIdx.x] = bi; }
+}
+
+__global__ void k_argmax_final(const float* __restrict__ pv, const int* __restrict__ pi, int np,
+                               int32_t* tok) {
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int i = threadIdx.x; i < np; i += blockDim.x) better(bv, bi, pv[i], pi[i]);
+  block_argmax(bv, bi);
+  if (threadIdx.x == 0) *tok = bi == 0x7fffffff ? 0 : bi;
+}
+
+hipError_t launch_argmax(const float* logits, int n, float* part_v, int* part_i, int nparts, int32_t* tok,
+                         hipStream_t s) {
+  k_argmax_part<<<nparts, 256, 0, s>>>(logits, n, part_v, part_i);
+  k_argmax_final<<<1, 256, 0, s>>>(part_v, part_i, nparts, tok);
+  return hipGetLastError();
+}
+
+}  // namespace slq

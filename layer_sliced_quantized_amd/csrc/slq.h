@@ -1,0 +1,158 @@
+// Internal declarations shared by the HIP sources of libslq (not part of the ABI).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace slq {
+
+constexpr int QK = 32;          // weights per block
+constexpr int TB = 8;           // blocks per tile along K
+constexpr int RG = 64;          // rows per row group: one row per lane of a wave64
+constexpr int XW = 24;          // digit dwords per activation block (both formats)
+constexpr int MAX_T = 16;       // tokens per batched pass
+constexpr int QT_Q4 = 2;
+constexpr int QT_Q8 = 8;
+
+// Bytes of one row's codes for one block in the packed layout.
+__host__ __device__ constexpr int code_bytes(int qt) { return qt == QT_Q4 ? 16 : 32; }
+// Bytes of one full tile: 8 blocks x 64 rows of codes + 64 rows x 8 fp16 scales.
+__host__ __device__ constexpr int tile_bytes(int qt) { return TB * RG * code_bytes(qt) + RG * TB * 2; }
+
+struct Packed {
+  const uint8_t* w;   // packed bytes
+  int64_t rows, cols;
+  int qt;
+  __host__ __device__ int nblk() const { return (int)(cols / QK); }
+  __host__ __device__ int ntiles() const { return (nblk() + TB - 1) / TB; }
+  __host__ __device__ int nrg() const { return (int)((rows + RG - 1) / RG); }
+};
+
+// Bytes of one 64-row group (all tiles along K; the last tile may hold < 8 blocks).
+__host__ __device__ inline size_t rg_bytes(int qt, int64_t cols) {
+  int nb = (int)(cols / QK);
+  int full = nb / TB, tail = nb % TB;
+  size_t b = (size_t)full * tile_bytes(qt);
+  if (tail) b += (size_t)tail * RG * code_bytes(qt) + RG * TB * 2;
+  return b;
+}
+inline size_t packed_bytes(int qt, int64_t rows, int64_t cols) {
+  return (size_t)((rows + RG - 1) / RG) * rg_bytes(qt, cols);
+}
+
+// ---------------------------------------------------------------- activations
+// An activation vector of n = 32*nblk floats is handed to a GEMV as integer
+// digits: per block b, scale s_b = max|x| / M and x_int = rint(x / s_b), split
+// into balanced digits (Q4_0: six base-16 digits in [-8,7]; Q8_0: three base-256
+// digits in [-128,127]) and packed in the order the weight codes use, so the
+// GEMV takes exact integer dot products of codes and digits.
+struct Act {
+  int32_t* xd;   // [T][nblk][24]
+  float* xs;     // [T][nblk]
+  int nblk;      // blocks per token
+};
+
+constexpr float M_Q4 = 7829367.0f;   // 7 * 0x111111
+constexpr float M_Q8 = 8355711.0f;   // 127 * 0x010101
+
+// RMSNorm statistic handed from a producer to a consumer GEMV: per token,
+// n_part partial sums of squares; rnorm = 1 / sqrt(sum / n + eps).
+struct NormIn {
+  const float* ssq;   // [T][n_part] or nullptr (no normalisation)
+  int n_part;
+  float inv_n, eps;
+};
+
+// GEMV epilogues
+enum Epi { EPI_STORE = 0, EPI_PARTIAL = 1, EPI_SWIGLU = 2, EPI_RESID = 3 };
+
+struct GemvOut {
+  int kind;
+  float* y;            // STORE: [T][rows]; PARTIAL: [ksplit][T][rows]; SWIGLU: m [T][rows/2]
+                       // (nullable); RESID: residual h [T][rows] updated in place
+  int64_t y_tstride;   // token stride of y in floats
+  Act next;            // SWIGLU/RESID: digits of the next GEMV input
+  int next_qt;
+  float* ssq_out;      // RESID: [T][nrg] sums of squares of h
+  const float* norm_w; // RESID: weights of the next RMSNorm (digits are of w*h)
+};
+
+struct Ctrl {         // device-resident step control
+  int pos;            // decode position p
+  int cur;            // current DeltaNet state slot
+  const void* in;     // boundary input of the step being run
+  void* out;          // boundary output of the step being run
+  int pad[58];
+};
+
+// -------------------------------------------------------------------- launchers
+// All return hipError_t from the launch.
+hipError_t launch_repack(int qt, const uint8_t* raw, int64_t rows, int64_t cols, uint8_t* packed,
+                         int64_t dst_rows, int map_kind, int64_t row_off, hipStream_t s);
+hipError_t launch_dequant(const Packed& W, float* out, hipStream_t s);
+// x fp32 [T][n] -> digits; optional ssq partials [T][nrg] of x (not of w*x).
+hipError_t launch_quant_act(int qt, const float* x, int T, int n, int64_t x_tstride, Act a,
+                            hipStream_t s);
+hipError_t launch_gemv(const Packed& W, int T, Act x, NormIn nin, GemvOut out, int ksplit,
+                       int waves, hipStream_t s);
+hipError_t launch_reduce_partials(const float* part, int ksplit, int T, int64_t rows,
+                                  NormIn nin, float* y, hipStream_t s);
+// h [T][H] (+)= sum of partials / input, then digits of norm_w*h and ssq partials.
+// in_kind: 0 = h += partials, 1 = h = fp16 input, 2 = h = fp32 input; with in == nullptr
+// the input pointer is read from ctrl->in.
+hipError_t launch_resid_finish(int in_kind, const void* in, const Ctrl* ctrl, int64_t in_tstride,
+                               const float* part, int ksplit, int T, int H, float* h,
+                               const float* norm_w, int qt, Act next, float* ssq_out,
+                               hipStream_t s);
+// out == nullptr: write to ctrl->out.
+hipError_t launch_store_out(const float* h, int T, int H, void* out, int fp32, Ctrl* ctrl,
+                            int advance_pos, hipStream_t s);
+hipError_t launch_ctrl_io(Ctrl* c, const void* in, void* out, hipStream_t s);
+hipError_t launch_ctrl_set(Ctrl* c, int pos, int cur, hipStream_t s);
+hipError_t launch_embed(const Packed& E, const int32_t* tok, void* out, int fp32, hipStream_t s);
+hipError_t launch_argmax(const float* logits, int n, float* part_v, int* part_i, int nparts,
+                         int32_t* tok, hipStream_t s);
+
+struct DnParams {
+  const float* y;        // G1 output [T][y_stride]
+  int64_t y_stride;
+  int off_q, off_k, off_v, off_a, off_b, off_z;
+  int heads, dk, dv;
+  float a_scale, a_bias, b_scale, z_scale;
+  float* state;          // slot 0 of this layer: [nslots][heads][dk][dv] (transposed)
+  int nslots;
+  int verify;            // 0: in place on slot cur; 1: token t -> slot (cur+1+t) % nslots
+  const Ctrl* ctrl;
+  float* u_out;          // [T][heads*dv] (nullable)
+  Act next; int next_qt;
+};
+hipError_t launch_deltanet(const DnParams& p, int T, hipStream_t s);
+hipError_t launch_state_io(float* state, int nslots, const Ctrl* ctrl, int heads, int dk, int dv,
+                           float* canon, int to_device, hipStream_t s);
+
+struct AttnParams {
+  const float* y;        // G1 output [T][y_stride]
+  int64_t y_stride;
+  int off_q, off_g, off_k, off_v;   // off_g < 0: no gate
+  int q_heads, kv_heads, hd, rope_dims;
+  double rope_theta;
+  int qk_norm;
+  const float* q_norm; const float* k_norm;
+  float eps;
+  __half* kc;            // K cache, tiled: [kv][max_seq/64][hd/8][64][8]
+  __half* vc;            // V cache: [kv][max_seq][hd]
+  int max_seq;
+  const Ctrl* ctrl;
+  float* qhat;           // [T][q_heads][hd]
+  float* part;           // [T][q_heads][nchunk][hd + 2]
+  int nchunk;            // max_seq / chunk
+  float* u_out;          // [T][q_heads*hd] (nullable)
+  Act next; int next_qt;
+};
+constexpr int ATT_CHUNK = 256;
+hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s);
+hipError_t launch_kv_io(__half* kc, __half* vc, int kv_heads, int max_seq, int hd,
+                        uint16_t* k, uint16_t* v, int rows, int to_device, hipStream_t s);
+
+}  // namespace slq

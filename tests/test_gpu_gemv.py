@@ -1,0 +1,128 @@
+"""GPU parity of the Q4_0 / Q8_0 decode and GEMV kernels against the CPU oracle.
+
+Called through the C ABI (slq_repack, slq_dequant, slq_gemv).  Decode must be
+bit-exact (every (q-8)*d and q*d is exact in fp32); products must be within
+max relative error 2e-3 of the fp64 oracle (they land near 1e-6).
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import qref
+from helpers import rel_err, TOL
+
+import layer_sliced_quantized_amd as slq
+
+pytestmark = pytest.mark.gpu
+
+QTYPES = [synth.Q4_0, synth.Q8_0]
+
+
+def _dev(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _raw(qtype, rows, cols, tag):
+    return synth.quant_blocks(synth.stream(11, synth.WL_GEMV, tag, rows % 1000, cols % 1000), qtype, rows, cols)
+
+
+# several tiles, ragged row groups (rows % 64) and a ragged last tile (blocks % 8)
+SMALL = [(64, 256), (200, 32 * 19), (1000, 32 * 37), (37, 32 * 3), (5120, 512)]
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("rows,cols", SMALL)
+def test_dequant_bit_exact(qtype, rows, cols):
+    raw = _raw(qtype, rows, cols, 1)
+    packed = slq.repack(qtype, _dev(raw), rows, cols)
+    got = slq.dequant(qtype, packed, rows, cols).cpu().numpy()
+    ref = qref.dequant(qtype, raw, rows, cols)
+    np.testing.assert_array_equal(got.astype(np.float64), ref)
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("rows,cols", SMALL)
+@pytest.mark.parametrize("batch", [1, 3, 16])
+def test_gemv_parity_small(qtype, rows, cols, batch):
+    raw = _raw(qtype, rows, cols, 2)
+    packed = slq.repack(qtype, _dev(raw), rows, cols)
+    x = synth.gemv_x(5, batch, cols, tag=rows)
+    y = slq.gemv(qtype, packed, rows, cols, _dev(x)).cpu().numpy()
+    ref = qref.gemv(qtype, raw, rows, cols, x.astype(np.float64))
+    for t in range(batch):
+        e = rel_err(y[t], ref[t])
+        assert e <= TOL, (t, e)
+        assert e <= 1e-5, (t, e)     # integer block dots: expected ~1e-7
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_gemv_batch_equals_single_bitwise(qtype):
+    rows, cols = 1000, 32 * 37
+    raw = _raw(qtype, rows, cols, 3)
+    packed = slq.repack(qtype, _dev(raw), rows, cols)
+    x = synth.gemv_x(6, 16, cols)
+    y16 = slq.gemv(qtype, packed, rows, cols, _dev(x)).cpu().numpy()
+    for t in (0, 7, 15):
+        y1 = slq.gemv(qtype, packed, rows, cols, _dev(x[t:t + 1])).cpu().numpy()
+        np.testing.assert_array_equal(y1[0], y16[t])
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_gemv_many_blocks(qtype):
+    """4000 activation blocks: the largest entry of a block sits on the
+    quantiser's range limit, which must not overflow the digits."""
+    rows, cols = 64, 32 * 4000
+    raw = _raw(qtype, rows, cols, 5)
+    packed = slq.repack(qtype, _dev(raw), rows, cols)
+    for tag in range(3):
+        x = synth.gemv_x(8, 2, cols, tag=tag)
+        y = slq.gemv(qtype, packed, rows, cols, _dev(x)).cpu().numpy()
+        ref = qref.gemv(qtype, raw, rows, cols, x.astype(np.float64))
+        for t in range(2):
+            assert rel_err(y[t], ref[t]) <= 1e-5
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_gemv_edge_inputs(qtype):
+    rows, cols = 128, 32 * 10
+    raw = _raw(qtype, rows, cols, 4)
+    packed = slq.repack(qtype, _dev(raw), rows, cols)
+    W = qref.dequant(qtype, raw, rows, cols)
+    # zero input -> exactly zero
+    y = slq.gemv(qtype, packed, rows, cols, torch.zeros((1, cols), device="cuda")).cpu().numpy()
+    assert np.all(y == 0)
+    # unit vector -> one column
+    for j in (0, 17, 31, 32, 319):
+        x = np.zeros((1, cols), np.float32)
+        x[0, j] = 1.0
+        y = slq.gemv(qtype, packed, rows, cols, _dev(x)).cpu().numpy()
+        assert rel_err(y[0], W[:, j]) <= 1e-6
+    # wide dynamic range inside a block
+    x = synth.gemv_x(7, 1, cols)
+    x[0, ::7] *= 1e4
+    x[0, 1::11] *= 1e-4
+    y = slq.gemv(qtype, packed, rows, cols, _dev(x)).cpu().numpy()
+    assert rel_err(y[0], W @ x[0].astype(np.float64)) <= TOL
+    # determinism: same call, same bits
+    y2 = slq.gemv(qtype, packed, rows, cols, _dev(x)).cpu().numpy()
+    np.testing.assert_array_equal(y, y2)
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("rows,cols", synth.GEMV_SHAPES)
+@pytest.mark.timeout(300)
+def test_gemv_full_shapes_sampled_rows(qtype, rows, cols):
+    """The GEMV sweep shapes at full size, batch 1 and 16; 96 sampled rows against the oracle."""
+    raw = synth.quant_blocks(synth.stream(0, synth.WL_GEMV, 100, rows, cols), qtype, rows, cols)
+    packed = slq.repack(qtype, _dev(raw), rows, cols)
+    rng = np.random.default_rng(rows + cols)
+    sample = np.sort(np.concatenate([[0, rows - 1], rng.choice(rows, 94, replace=False)]))
+    for batch in (1, 16):
+        x = synth.gemv_x(0, batch, cols, tag=batch)
+        y = slq.gemv(qtype, packed, rows, cols, _dev(x)).cpu().numpy()
+        ref = qref.gemv(qtype, raw[sample], len(sample), cols, x.astype(np.float64))
+        for t in range(batch):
+            assert rel_err(y[t, sample], ref[t]) <= TOL
+    del packed
+    torch.cuda.empty_cache()
