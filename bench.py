@@ -1,0 +1,296 @@
+#!/usr/bin/env python3
+"""Decode benchmark of a 64-layer Q4_0 hybrid slice on one MI355X.
+
+Workload: layers 0..63 of the hybrid Gated-DeltaNet + gated-attention model at
+hidden 5120 (3 DeltaNet layers then 1 attention layer, repeated; SwiGLU 17408
+in every layer; all matrices Q4_0, 13.4 GB), synthetic seeded weights, a
+512-row fp16 KV prefix per attention layer, DeltaNet states N(0, 0.02), and a
+fresh N(0,1) fp16 hidden state per step, as a middle pipeline stage receives
+it.  One step = one token through all 64 layers (one HIP graph launch).
+
+Printed JSON (one line on stdout): decode tok/s, the roofline of the dominant
+kernel (the fused RMSNorm + gate/up + SwiGLU GEMV, measured with HIP events),
+the CPU oracle timed on a bounded sample, 4-draft verify with rollback, the
+Q8_0 slice, and the standalone GEMV sweep.  Progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+METRIC = "decode tok/s, 64-layer Q4_0 hybrid slice (b=1); GEMV HBM GB/s vs peak"
+PREFILL = 512
+
+
+def log(msg: str) -> None:
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def gemv_bytes(rows: int, cols: int, qtype: int, batch: int = 1) -> int:
+    """Algorithmic bytes of one GEMV: packed weights + fp32 activations in and out."""
+    bb = 18 if qtype == 2 else 34
+    return rows * cols // 32 * bb + 4 * batch * (rows + cols)
+
+
+def build_slice(shape, qtype, max_seq, max_verify, seed, threads):
+    import torch
+    import synth
+    import layer_sliced_quantized_amd as slq
+    t0 = time.time()
+    cfg = slq.make_config(shape, qtype, 0, shape.n_layers, max_seq=max_seq, max_verify=max_verify, io_fp32=False)
+    s = slq.Slice(cfg)
+    tensors = {}
+    for l in range(shape.n_layers):
+        tensors[l] = synth.layer_tensors(shape, qtype, seed, synth.WL_SLICE, l, threads=threads)
+        s.load_numpy({l: tensors[l]})
+        if shape.is_attention(l):
+            K, V = synth.kv_prefill(seed, synth.WL_SLICE, l, shape.kv_heads, PREFILL, shape.head_dim)
+            s.set_kv(l, torch.from_numpy(K), torch.from_numpy(V))
+        else:
+            S0 = synth.dn_state0(seed, synth.WL_SLICE, l, shape.dn_heads, shape.dn_dv, shape.dn_dk)
+            s.set_state(l, torch.from_numpy(S0))
+    s.reset(PREFILL)
+    torch.cuda.synchronize()
+    log(f"slice qtype={qtype}: {s.weights.numel() / 1e9:.2f} GB weights generated and loaded in {time.time() - t0:.1f}s")
+    return s, tensors
+
+
+def time_decode(s, H, steps, warmup):
+    """Warm up, then time exactly `steps` graph-launched decode steps."""
+    import torch
+    out = torch.empty((H.shape[0], H.shape[1]), dtype=torch.float16, device="cuda")
+    for i in range(warmup):
+        s.decode(H[i], out[i])
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    t0 = time.perf_counter()
+    ev0.record()
+    for i in range(warmup, warmup + steps):
+        s.decode(H[i], out[i])
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    return ev0.elapsed_time(ev1) / 1e3, wall, out
+
+
+def profile_ops(s, H, n):
+    """Eager steps with a HIP event at every op boundary; mean ms per op kind and per step."""
+    import torch
+    out = torch.empty(H.shape[1], dtype=torch.float16, device="cuda")
+    per = {}
+    step_ms = []
+    for i in range(n):
+        _, ops = s.decode_profiled(H[i], out)
+        step_ms.append(sum(ms for _, ms in ops))
+        for name, ms in ops:
+            per.setdefault(name, []).append(ms)
+    return {k: (float(np.mean(v)), len(v) // n) for k, v in per.items()}, float(np.mean(step_ms))
+
+
+def run_verify(s, H, rounds, k, seed):
+    import torch
+    import synth
+    acc = synth.accept_pattern(seed, rounds, k)
+    out = torch.empty((k, H.shape[1]), dtype=torch.float16, device="cuda")
+    s.verify(H[0:k], out)          # warm the k-token graph
+    s.commit(0)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for r in range(rounds):
+        s.verify(H[r * k:(r + 1) * k], out)
+        s.commit(int(acc[r]))
+    ev1.record()
+    torch.cuda.synchronize()
+    sec = ev0.elapsed_time(ev1) / 1e3
+    return {"k": k, "rounds": rounds, "us_per_verify": sec / rounds * 1e6,
+            "accepted_tokens": int(acc.sum()), "committed_tok_s": float(acc.sum() / sec),
+            "verified_tok_s": rounds * k / sec}
+
+
+def gemv_sweep(seed, reps):
+    import torch
+    import synth
+    import layer_sliced_quantized_amd as slq
+    res = []
+    for qtype in (synth.Q4_0, synth.Q8_0):
+        for rows, cols in synth.GEMV_SHAPES:
+            raw = synth.quant_blocks(synth.stream(seed, synth.WL_GEMV, 200, rows, cols), qtype, rows, cols)
+            rawd = torch.from_numpy(raw).cuda()
+            nbytes = slq.packed_bytes(qtype, rows, cols)
+            copies = max(1, int(np.ceil(1.2e9 / nbytes)))   # > 1 GB in rotation: HBM, not Infinity Cache
+            packs = [slq.repack(qtype, rawd, rows, cols) for _ in range(copies)]
+            del rawd
+            for batch in (1, 16):
+                x = torch.from_numpy(synth.gemv_x(seed, batch, cols, tag=7)).cuda()
+                y = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
+                ws = torch.empty(slq.gemv_workspace_bytes(qtype, rows, cols, batch), dtype=torch.uint8, device="cuda")
+                for i in range(min(copies, 4)):
+                    slq.gemv(qtype, packs[i % copies], rows, cols, x, out=y, ws=ws)
+                torch.cuda.synchronize()
+                n = max(reps, copies)
+                ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                ev0.record()
+                for i in range(n):
+                    slq.gemv(qtype, packs[i % copies], rows, cols, x, out=y, ws=ws)
+                ev1.record()
+                torch.cuda.synchronize()
+                us = ev0.elapsed_time(ev1) / n * 1e3
+                gbs = gemv_bytes(rows, cols, qtype, batch) / (us * 1e-6) / 1e9
+                res.append({"qtype": "Q4_0" if qtype == 2 else "Q8_0", "rows": rows, "cols": cols, "batch": batch,
+                            "us": round(us, 2), "GB_s": round(gbs, 1), "frac_peak": round(gbs / HBM_PEAK_GBS, 3)})
+                log(f"gemv {res[-1]}")
+            del packs
+            torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(shape, qtype, tensors, H, n_tokens, seed, gpu_first):
+    """The oracle, as it stands, decoding n_tokens of the same slice on the host cores."""
+    import synth
+    from oracle import SliceOracle
+    from oracle import qref
+    qref.build(force=False)
+    orc = SliceOracle(shape, qtype, 0, shape.n_layers, tensors, max_seq=PREFILL + 64, io_fp32=False)
+    for l in range(shape.n_layers):
+        if shape.is_attention(l):
+            K, V = synth.kv_prefill(seed, synth.WL_SLICE, l, shape.kv_heads, PREFILL, shape.head_dim)
+            orc.set_kv(l, K, V)
+        else:
+            orc.set_state(l, synth.dn_state0(seed, synth.WL_SLICE, l, shape.dn_heads, shape.dn_dv, shape.dn_dk))
+    orc.reset(PREFILL)
+    t0 = time.perf_counter()
+    outs = []
+    for i in range(n_tokens):
+        outs.append(orc.decode(H[i]))
+        log(f"oracle token {i}: {time.perf_counter() - t0:.1f}s")
+    sec = time.perf_counter() - t0
+    ref = outs[0].astype(np.float64)
+    got = gpu_first.astype(np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    rel = float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), rms)))
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(n_tokens / sec, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
+            "sample": f"{n_tokens} decode tokens of the same 64-layer slice (fp64 C GEMV + numpy)"}, rel
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=256)
+    ap.add_argument("--warmup", type=int, default=8)
+    ap.add_argument("--profile-steps", type=int, default=4)
+    ap.add_argument("--verify-rounds", type=int, default=32)
+    ap.add_argument("--cpu-tokens", type=int, default=2)
+    ap.add_argument("--sweep-reps", type=int, default=50)
+    ap.add_argument("--no-q8", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU: the slice runs on a single MI355X and this build has no "
+              "multi-GPU path (a layer pipeline across GPUs is described in the design notes); run with --gpus 1",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    import synth
+    torch.cuda.set_device(0)
+    threads = min(16, os.cpu_count() or 8)
+    shape = synth.HYBRID_5120
+    n_in = args.warmup + args.steps + args.profile_steps + 4 * (args.verify_rounds + 1) + 8
+    max_seq = ((PREFILL + n_in + 63) // 64) * 64
+    log(f"inputs: {n_in} fresh fp16 hidden states; max_seq {max_seq}")
+    H_host = synth.hidden_inputs(args.seed, synth.WL_SLICE, n_in, shape.hidden)
+    H = torch.from_numpy(H_host).cuda()
+
+    # ---- Q4_0 slice: timed decode
+    s, tensors = build_slice(shape, synth.Q4_0, max_seq, 4, args.seed, threads)
+    sec, wall, out = time_decode(s, H, args.steps, args.warmup)
+    tok_s = args.steps / sec
+    gpu_first = out[0].cpu().numpy()
+    log(f"Q4_0 decode: {args.steps} steps in {sec * 1e3:.1f} ms (wall {wall * 1e3:.1f} ms): {tok_s:.1f} tok/s")
+
+    # ---- per-op times (eager, HIP events) -> roofline of the dominant kernel
+    base = args.warmup + args.steps
+    ops, step_ms = profile_ops(s, H[base:], args.profile_steps)
+    for k, (ms, n) in sorted(ops.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
+        log(f"op {k:10s}: {ms * 1e3:8.2f} us x {n}/step")
+    f1_rows, f1_cols = 2 * shape.ffn, shape.hidden
+    f1_ms = ops["ffn_in"][0]
+    f1_bytes = gemv_bytes(f1_rows, f1_cols, synth.Q4_0)
+    achieved = f1_bytes / (f1_ms * 1e-3) / 1e9
+    weight_bytes = s.weights.numel()
+    slice_bytes_tok = weight_bytes + 48 * 2 * 32 * 128 * 128 * 4 + 16 * (PREFILL + args.steps // 2) * 4096
+    log(f"F1 GEMV {f1_rows}x{f1_cols}: {f1_ms * 1e3:.2f} us -> {achieved:.0f} GB/s; eager step {step_ms:.3f} ms")
+
+    # ---- verify with rollback
+    base += args.profile_steps
+    ver = run_verify(s, H[base:], args.verify_rounds, 4, args.seed)
+    ver["speedup_vs_4_decodes"] = round(4 * (1.0 / tok_s) / (ver["us_per_verify"] * 1e-6), 3)
+    log(f"verify k=4: {ver}")
+    del s
+    torch.cuda.empty_cache()
+
+    extra = {}
+    # ---- standalone GEMV sweep
+    if not args.no_sweep:
+        extra["gemv_sweep"] = gemv_sweep(args.seed, args.sweep_reps)
+
+    # ---- CPU oracle on a bounded sample of the same workload
+    cpu = None
+    if not args.no_cpu:
+        cpu, rel = cpu_baseline(shape, synth.Q4_0, tensors, H_host, args.cpu_tokens, args.seed, gpu_first)
+        extra["parity_first_token_max_rel_err"] = rel
+        log(f"cpu baseline {cpu}, GPU vs oracle first token rel err {rel:.2e}")
+    del tensors
+
+    # ---- Q8_0 slice
+    if not args.no_q8:
+        s8, t8 = build_slice(shape, synth.Q8_0, max_seq, 4, args.seed, threads)
+        del t8
+        sec8, _, _ = time_decode(s8, H, args.steps, args.warmup)
+        ops8, _ = profile_ops(s8, H[args.warmup + args.steps:], 2)
+        extra["q8_0_slice"] = {"tok_s": round(args.steps / sec8, 2), "weights_GB": round(s8.weights.numel() / 1e9, 2),
+                               "ffn_in_us": round(ops8["ffn_in"][0] * 1e3, 2)}
+        log(f"Q8_0 decode: {extra['q8_0_slice']}")
+        del s8
+        torch.cuda.empty_cache()
+
+    res = {
+        "metric": METRIC, "value": round(tok_s, 2), "unit": "tok/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(sec / args.steps * 1e3, 4), "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None,
+        "dtype": "int4 x int4 -> int32 block dots, fp32 scales/accumulate",
+        "data": "synthetic (seeded Q4_0 weights, fp16 KV prefix, N(0,1) fp16 inputs)",
+        "config": {"workload": "hybrid_5120 layers 0-63 (48 Gated DeltaNet + 16 gated attention, SwiGLU 17408), "
+                               f"Q4_0 {weight_bytes / 1e9:.2f} GB, batch 1 decode from position {PREFILL}",
+                   "global_batch": 1, "seq_len": PREFILL, "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": f"k_gemv Q4_0 SwiGLU epilogue ({f1_rows}x{f1_cols}), mean of "
+                               f"{args.profile_steps * 64} launches"},
+        "cpu_baseline": cpu,
+        "slice_GB_per_token": round(slice_bytes_tok / 1e9, 3),
+        "slice_effective_GB_s": round(slice_bytes_tok * tok_s / 1e9, 1),
+        "ops_us_per_step": {k: round(v[0] * v[1] * 1e3, 1) for k, v in ops.items()},
+        "eager_step_ms": round(step_ms, 4),
+        "verify": ver,
+    }
+    res.update(extra)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

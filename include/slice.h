@@ -162,6 +162,27 @@ int slice_reset(slice_t *s, int kv_len, void *stream);
  * p + 1 > max_seq.  One graph launch per call. */
 int slice_decode(slice_t *s, const void *hid_in_dev, void *hid_out_dev, void *stream);
 
+/* Op kinds reported by slice_decode_profiled. */
+enum {
+    SLICE_OP_ENTRY = 0,      /* boundary vector in, first RMSNorm statistics          */
+    SLICE_OP_DN_IN = 1,      /* DeltaNet input projections [q|k|v|a|b|z] (GEMV)        */
+    SLICE_OP_DELTANET = 2,   /* DeltaNet state update and gated output                */
+    SLICE_OP_DN_OUT = 3,     /* DeltaNet output projection + residual (GEMV)          */
+    SLICE_OP_ATT_IN = 4,     /* attention input projections [q|g|k|v] (GEMV)          */
+    SLICE_OP_ATTENTION = 5,  /* QK-norm, RoPE, KV append, split attention, combine    */
+    SLICE_OP_ATT_OUT = 6,    /* attention output projection + residual (GEMV)         */
+    SLICE_OP_FFN_IN = 7,     /* RMSNorm + fused gate/up projection + SwiGLU (GEMV)    */
+    SLICE_OP_FFN_OUT = 8,    /* down projection + residual (GEMV)                     */
+    SLICE_OP_EXIT = 9        /* boundary vector out                                   */
+};
+
+/* Same as slice_decode, but launched op by op (no graph) with a HIP event on
+ * `stream` at every op boundary; waits for the step to finish.  Writes, in
+ * order, the kind and the duration in ms of each op (at most max_ops) and
+ * returns how many were written (>= 0) or a negative slice_status. */
+int slice_decode_profiled(slice_t *s, const void *hid_in_dev, void *hid_out_dev,
+                          int *op_kind, float *op_ms, int max_ops, void *stream);
+
 /* Batched verify of k inputs at positions p .. p+k-1: hid_in_dev [k][H] ->
  * hid_out_dev [k][H].  Output t equals what slice_decode would give after the
  * first t inputs.  The weights are read once for all k tokens.  The DeltaNet

@@ -178,6 +178,22 @@ class Slice:
         check(lib().slice_decode(self.handle, _ptr(h_in), _ptr(h_out), _stream(stream)))
         return h_out
 
+    OP_NAMES = ["entry", "dn_in", "deltanet", "dn_out", "att_in", "attention", "att_out", "ffn_in", "ffn_out",
+                "exit"]
+
+    def decode_profiled(self, h_in: torch.Tensor, h_out: torch.Tensor | None = None, stream=None):
+        """One decode step, op by op, with a HIP event at every op boundary.
+        Returns (h_out, [(op_name, ms), ...])."""
+        if h_out is None:
+            h_out = torch.empty(self.cfg.hidden, dtype=self.io_dtype, device=self.device)
+        cap = 16 * (self.cfg.layer_end - self.cfg.layer_begin) + 8
+        kinds = (ctypes.c_int * cap)()
+        ms = (ctypes.c_float * cap)()
+        n = lib().slice_decode_profiled(self.handle, _ptr(h_in), _ptr(h_out), kinds, ms, cap, _stream(stream))
+        if n < 0:
+            check(n)
+        return h_out, [(self.OP_NAMES[kinds[i]], float(ms[i])) for i in range(n)]
+
     def verify(self, h_in: torch.Tensor, h_out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
         k = h_in.shape[0]
         if h_out is None:

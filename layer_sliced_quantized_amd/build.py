@@ -16,7 +16,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "slq")
 LIB = os.path.join(HERE, "libslq.so")
 SOURCES = ["gemv.hip", "deltanet.hip", "attn.hip", "misc.hip", "slice.cpp"] + [
-    f"gemv_{q}_{e}.hip" for q in ("q4", "q8") for e in ("store", "partial", "swiglu", "resid")]
+    f"gemv_{q}_{e}.hip" for q in ("q4", "q8") for e in ("store", "swiglu", "resid")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

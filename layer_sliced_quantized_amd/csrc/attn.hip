@@ -10,12 +10,12 @@
 //            rope_dims entries (angle pos * theta^(-2i/r) taken in fp64),
 //            q scaled by 1/sqrt(head_dim); K/V row p+t rounded to fp16 and
 //            appended to the cache.
-//   split:   one workgroup per (KV head, 256-row chunk); scores of the group's
+//   split:   one workgroup per (KV head, 64-row chunk); scores of the group's
 //            query heads against the chunk, chunk-local max / sum of exp and
 //            the unnormalised P V.  Query t (position p+t) sees rows <= p+t.
 //   combine: per (token, query head): merge the chunks' partials, apply the
 //            gate sigmoid(g), and quantise the result for the output GEMV.
-// Chunk boundaries are absolute (multiples of 256), so query t of a verify
+// Chunk boundaries are absolute (multiples of 64), so query t of a verify
 // pass is computed with exactly the operations a decode at p+t would use.
 //
 // K cache layout: [kv][pos/64][head_dim/8][64 pos][8] (a wave reads 64 rows'
@@ -67,10 +67,15 @@ __global__ __launch_bounds__(256) void k_attn_prep(AttnParams p) {
   }
 }
 
+// One workgroup per (KV head g, 64-row chunk c), 4 waves.  Scores: wave w
+// takes rows 16w..16w+15 of the chunk, 4 lanes per row each over a quarter of
+// the head dimensions, summed with two butterfly steps.  P V: one thread per
+// head dimension over the chunk's rows.
 template <int GRP>
 __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   constexpr int C = ATT_CHUNK;
-  __shared__ float pl[GRP][C];
+  __shared__ __attribute__((aligned(16))) float pl[GRP][C];
+  __shared__ __attribute__((aligned(16))) float qsh[GRP * 256];
   __shared__ float wm[4][GRP];
   const int g = blockIdx.x / p.nchunk, c = blockIdx.x % p.nchunk;
   const int p0 = p.ctrl->pos;
@@ -78,17 +83,24 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   if (r0 > p0 + T - 1) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
-  const int r = r0 + tid;
+  const int rr = wave * 16 + (lane & 15);      // row of this lane inside the chunk
+  const int dq = lane >> 4;                    // quarter of the head dimensions
+  const int qd = p.hd / 4;                     // dims per quarter (16 or 64 ...)
+  const int r = r0 + rr;
   for (int t = 0; t < T; ++t) {
     const int P = p0 + t;
     const int nvalid = min(C, P + 1 - r0);
     if (nvalid <= 0) continue;
-    const float* qh = p.qhat + ((size_t)t * p.q_heads + g * GRP) * p.hd;
+    {
+      const float* qg = p.qhat + ((size_t)t * p.q_heads + g * GRP) * p.hd;
+      for (int i = tid; i < GRP * p.hd; i += 256) qsh[i] = qg[i];
+    }
+    __syncthreads();
     float s[GRP];
 #pragma unroll
     for (int h = 0; h < GRP; ++h) s[h] = 0.0f;
-    if (tid < nvalid) {
-      for (int dc = 0; dc < p.hd / 8; ++dc) {
+    if (rr < nvalid) {
+      for (int dc = dq * qd / 8; dc < (dq + 1) * qd / 8; ++dc) {
         const uint4 kw = *reinterpret_cast<const uint4*>(p.kc + kidx(g, r, dc * 8, p.max_seq, p.hd));
         float kf[8];
         const uint32_t ws[4] = {kw.x, kw.y, kw.z, kw.w};
@@ -99,48 +111,68 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
         }
 #pragma unroll
         for (int h = 0; h < GRP; ++h) {
-          const float* q = qh + (size_t)h * p.hd + dc * 8;
-#pragma unroll
-          for (int e = 0; e < 8; ++e) s[h] = __builtin_fmaf(kf[e], q[e], s[h]);
+          const float4 qa = *reinterpret_cast<const float4*>(qsh + h * p.hd + dc * 8);
+          const float4 qb = *reinterpret_cast<const float4*>(qsh + h * p.hd + dc * 8 + 4);
+          s[h] = __builtin_fmaf(kf[0], qa.x, s[h]);
+          s[h] = __builtin_fmaf(kf[1], qa.y, s[h]);
+          s[h] = __builtin_fmaf(kf[2], qa.z, s[h]);
+          s[h] = __builtin_fmaf(kf[3], qa.w, s[h]);
+          s[h] = __builtin_fmaf(kf[4], qb.x, s[h]);
+          s[h] = __builtin_fmaf(kf[5], qb.y, s[h]);
+          s[h] = __builtin_fmaf(kf[6], qb.z, s[h]);
+          s[h] = __builtin_fmaf(kf[7], qb.w, s[h]);
         }
       }
     }
-    // chunk max per head
-    float m[GRP];
 #pragma unroll
     for (int h = 0; h < GRP; ++h) {
-      const float v = wave_max(tid < nvalid ? s[h] : -INFINITY);
+      s[h] += __shfl_xor(s[h], 16, 64);
+      s[h] += __shfl_xor(s[h], 32, 64);
+    }
+    // chunk max per head
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) {
+      const float v = wave_max(rr < nvalid ? s[h] : -INFINITY);
       if (lane == 0) wm[wave][h] = v;
     }
     __syncthreads();
+    float m[GRP];
 #pragma unroll
-    for (int h = 0; h < GRP; ++h) {
-      float v = wm[0][h];
-      for (int w = 1; w < 4; ++w) v = fmaxf(v, wm[w][h]);
-      m[h] = v;
-    }
+    for (int h = 0; h < GRP; ++h) m[h] = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));
     __syncthreads();
     float l[GRP];
 #pragma unroll
     for (int h = 0; h < GRP; ++h) {
-      const float e = tid < nvalid ? __expf(s[h] - m[h]) : 0.0f;
-      pl[h][tid] = e;
-      const float v = wave_sum(e);
+      const float e = rr < nvalid ? __expf(s[h] - m[h]) : 0.0f;
+      if (dq == 0) pl[h][rr] = e;
+      // each row's weight appears on 4 lanes; count it once
+      const float v = wave_sum(dq == 0 ? e : 0.0f);
       if (lane == 0) wm[wave][h] = v;
     }
     __syncthreads();
 #pragma unroll
-    for (int h = 0; h < GRP; ++h) l[h] = wm[0][h] + wm[1][h] + wm[2][h] + wm[3][h];
+    for (int h = 0; h < GRP; ++h) l[h] = (wm[0][h] + wm[1][h]) + (wm[2][h] + wm[3][h]);
     // P V: thread = dimension
     if (tid < p.hd) {
       float o[GRP];
 #pragma unroll
       for (int h = 0; h < GRP; ++h) o[h] = 0.0f;
       const __half* vrow = p.vc + ((size_t)g * p.max_seq + r0) * p.hd + tid;
-      for (int rr = 0; rr < nvalid; ++rr) {
-        const float v = __half2float(vrow[(size_t)rr * p.hd]);
+      // rows past nvalid have weight 0 and lie inside the cache (r0 + C <= max_seq)
+      const int n4 = (nvalid + 3) & ~3;
+      for (int q = 0; q < n4; q += 4) {
+        const float v0 = __half2float(vrow[(size_t)(q + 0) * p.hd]);
+        const float v1 = __half2float(vrow[(size_t)(q + 1) * p.hd]);
+        const float v2 = __half2float(vrow[(size_t)(q + 2) * p.hd]);
+        const float v3 = __half2float(vrow[(size_t)(q + 3) * p.hd]);
 #pragma unroll
-        for (int h = 0; h < GRP; ++h) o[h] = __builtin_fmaf(pl[h][rr], v, o[h]);
+        for (int h = 0; h < GRP; ++h) {
+          const float4 w4 = *reinterpret_cast<const float4*>(&pl[h][q]);
+          o[h] = __builtin_fmaf(w4.x, v0, o[h]);
+          o[h] = __builtin_fmaf(w4.y, v1, o[h]);
+          o[h] = __builtin_fmaf(w4.z, v2, o[h]);
+          o[h] = __builtin_fmaf(w4.w, v3, o[h]);
+        }
       }
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
@@ -153,20 +185,40 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   }
 }
 
-__global__ __launch_bounds__(256) void k_attn_combine(AttnParams p) {
-  const int t = blockIdx.x / p.q_heads, h = blockIdx.x % p.q_heads;
-  const int d = threadIdx.x;
+// One workgroup per (token, query head, 64 dimensions): merge the chunks,
+// normalise, apply the gate and quantise the two 32-dim blocks.  Lane c loads
+// chunk c's max and sum (several rounds beyond 64 chunks), the weights
+// exp(m_c - M) go through LDS, and every lane then folds its dimension.
+__global__ __launch_bounds__(64) void k_attn_combine(AttnParams p) {
+  __shared__ float wsh[1024];
+  const int ndg = p.hd / 64;
+  const int t = blockIdx.x / (p.q_heads * ndg);
+  const int h = (blockIdx.x / ndg) % p.q_heads;
+  const int lane = threadIdx.x;
+  const int d = (blockIdx.x % ndg) * 64 + lane;
   const int P = p.ctrl->pos + t;
   const int nc = P / ATT_CHUNK + 1;
-  const float* base = p.part + ((size_t)t * p.q_heads + h) * p.nchunk * (p.hd + 2);
+  const int stride = p.hd + 2;
+  const float* base = p.part + ((size_t)t * p.q_heads + h) * p.nchunk * stride;
   float M = -INFINITY;
-  for (int c = 0; c < nc; ++c) M = fmaxf(M, base[(size_t)c * (p.hd + 2)]);
-  float L = 0.0f, o = 0.0f;
+  for (int c = lane; c < nc; c += 64) M = fmaxf(M, base[(size_t)c * stride]);
+  M = wave_max(M);
+  float L = 0.0f;
+  for (int c0 = 0; c0 < nc; c0 += 64) {
+    const int c = c0 + lane;
+    float w = 0.0f, l = 0.0f;
+    if (c < nc) {
+      w = __expf(base[(size_t)c * stride] - M);
+      l = base[(size_t)c * stride + 1];
+    }
+    L += wave_sum(l * w);
+    if (c < nc && c < 1024) wsh[c] = w;
+  }
+  __syncthreads();
+  float o = 0.0f;
   for (int c = 0; c < nc; ++c) {
-    const float* pc = base + (size_t)c * (p.hd + 2);
-    const float w = __expf(pc[0] - M);
-    L = __builtin_fmaf(pc[1], w, L);
-    o = __builtin_fmaf(pc[2 + d], w, o);
+    const float w = c < 1024 ? wsh[c] : __expf(base[(size_t)c * stride] - M);
+    o = __builtin_fmaf(base[(size_t)c * stride + 2 + d], w, o);
   }
   o = o / L;
   if (p.off_g >= 0) o = o * sigmoidf_(p.y[(size_t)t * p.y_stride + p.off_g + h * p.hd + d]);
@@ -190,7 +242,7 @@ hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {
 #undef SLQ_G
     default: return hipErrorInvalidValue;
   }
-  k_attn_combine<<<T * p.q_heads, p.hd, 0, s>>>(p);
+  k_attn_combine<<<T * p.q_heads * (p.hd / 64), 64, 0, s>>>(p);
   return hipGetLastError();
 }
 

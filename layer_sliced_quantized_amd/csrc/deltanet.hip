@@ -8,9 +8,8 @@
 // with q, k divided by sqrt(sum of squares + 1e-6).  Row i of S only needs the
 // whole k and q plus v_i, so rows are independent:
 //     u_i = S_i . k,   S'_ij = alpha S_ij + beta (v_i - alpha u_i) k_j,   o_i = S'_i . q
-// Each lane owns one row i and 32 consecutive j of it (the state lives in
-// registers across the tokens of a verify pass); the waves of a workgroup
-// cover the j range and meet in LDS in a fixed order.
+// Two lanes own one row i, each with half of the j range (the state lives in
+// registers across the tokens of a verify pass) and meet with one shuffle.
 //
 // State layout in HBM: [slot][head][j][i] (i fastest) so that a wave's loads
 // and stores of one j are contiguous.  Decode updates slot `cur` in place;
@@ -20,89 +19,80 @@
 
 namespace slq {
 
-__global__ __launch_bounds__(256) void k_deltanet(DnParams p, int T) {
-  __shared__ float qs[128], ksh[128];
-  __shared__ float red[4][RG];
-  __shared__ float red2[4][2];
-  const int nic = (p.dv + RG - 1) / RG;
-  const int h = blockIdx.x / nic, ic = blockIdx.x % nic;
-  const int lane = threadIdx.x & 63;
-  const int wave = wave_id();
-  const int nw = blockDim.x >> 6;          // == dk / 32
-  const int i = ic * RG + lane;
-  const bool iv = i < p.dv;
+// One wave per (head, 32 rows of S).  Lane (i, half) owns row i and the
+// half of the key dimension j in [half*DKH, half*DKH + DKH); the two halves of
+// a row meet with one butterfly step, so nothing leaves the wave.
+template <int DKH>
+__global__ __launch_bounds__(64) void k_deltanet(DnParams p, int T) {
+  __shared__ float qs[2 * DKH], ksh[2 * DKH];
+  const int nib = p.dv / 32;
+  const int h = blockIdx.x / nib, ib = blockIdx.x % nib;
+  const int lane = threadIdx.x;
+  const int half = lane >> 5;
+  const int i = ib * 32 + (lane & 31);
+  const int dk = 2 * DKH;
   const int cur = p.ctrl->cur;
-  const size_t hs = (size_t)p.dk * p.dv;
+  const size_t hs = (size_t)dk * p.dv;
   const float* S_in = p.state + ((size_t)cur * p.heads + h) * hs;
-  const int j0 = wave * 32;
+  const int j0 = half * DKH;
 
-  float S[32];
+  float S[DKH];
 #pragma unroll
-  for (int jj = 0; jj < 32; ++jj) S[jj] = iv ? S_in[(size_t)(j0 + jj) * p.dv + i] : 0.0f;
+  for (int jj = 0; jj < DKH; ++jj) S[jj] = S_in[(size_t)(j0 + jj) * p.dv + i];
 
   for (int t = 0; t < T; ++t) {
     const float* y = p.y + (size_t)t * p.y_stride;
-    float qv = 0.0f, kv = 0.0f;
-    if ((int)threadIdx.x < p.dk) {
-      qv = y[p.off_q + h * p.dk + threadIdx.x];
-      kv = y[p.off_k + h * p.dk + threadIdx.x];
-    }
-    const float sq = wave_sum(qv * qv), sk = wave_sum(kv * kv);
-    if (lane == 0) { red2[wave][0] = sq; red2[wave][1] = sk; }
-    __syncthreads();
-    float Sq = 0.0f, Sk = 0.0f;
-    for (int w = 0; w < nw; ++w) { Sq += red2[w][0]; Sk += red2[w][1]; }
-    const float rq = 1.0f / sqrtf(Sq + 1e-6f), rk = 1.0f / sqrtf(Sk + 1e-6f);
-    if ((int)threadIdx.x < p.dk) { qs[threadIdx.x] = qv * rq; ksh[threadIdx.x] = kv * rk; }
+    // q, k of head h: lanes hold entries lane and lane + 64
+    float q0 = 0.0f, q1 = 0.0f, k0 = 0.0f, k1 = 0.0f;
+    if (lane < dk) { q0 = y[p.off_q + h * dk + lane]; k0 = y[p.off_k + h * dk + lane]; }
+    if (lane + 64 < dk) { q1 = y[p.off_q + h * dk + lane + 64]; k1 = y[p.off_k + h * dk + lane + 64]; }
+    const float sq = wave_sum(q0 * q0 + q1 * q1), sk = wave_sum(k0 * k0 + k1 * k1);
+    const float rq = 1.0f / sqrtf(sq + 1e-6f), rk = 1.0f / sqrtf(sk + 1e-6f);
+    if (lane < dk) { qs[lane] = q0 * rq; ksh[lane] = k0 * rk; }
+    if (lane + 64 < dk) { qs[lane + 64] = q1 * rq; ksh[lane + 64] = k1 * rk; }
     const float alpha = sigmoidf_(p.a_scale * y[p.off_a + h] + p.a_bias);
     const float beta = sigmoidf_(p.b_scale * y[p.off_b + h]);
-    const float vi = iv ? y[p.off_v + h * p.dv + i] : 0.0f;
-    const float zi = iv ? y[p.off_z + h * p.dv + i] : 0.0f;
+    const float vi = y[p.off_v + h * p.dv + i];
+    const float zi = y[p.off_z + h * p.dv + i];
     __syncthreads();
 
     float up = 0.0f;
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj) up = __builtin_fmaf(S[jj], ksh[j0 + jj], up);
-    red[wave][lane] = up;
-    __syncthreads();
-    float u = 0.0f;
-    for (int w = 0; w < nw; ++w) u += red[w][lane];
+    for (int jj = 0; jj < DKH; ++jj) up = __builtin_fmaf(S[jj], ksh[j0 + jj], up);
+    const float u = up + __shfl_xor(up, 32, 64);
     const float c = beta * (vi - alpha * u);
     float op = 0.0f;
 #pragma unroll
-    for (int jj = 0; jj < 32; ++jj) {
+    for (int jj = 0; jj < DKH; ++jj) {
       S[jj] = __builtin_fmaf(c, ksh[j0 + jj], alpha * S[jj]);
       op = __builtin_fmaf(S[jj], qs[j0 + jj], op);
     }
-    __syncthreads();
-    red[wave][lane] = op;
-    __syncthreads();
-    float o = 0.0f;
-    for (int w = 0; w < nw; ++w) o += red[w][lane];
+    const float o = op + __shfl_xor(op, 32, 64);
 
     float* S_out = p.verify ? p.state + ((size_t)((cur + 1 + t) % p.nslots) * p.heads + h) * hs
                             : const_cast<float*>(S_in);
-    if (iv) {
 #pragma unroll
-      for (int jj = 0; jj < 32; ++jj) S_out[(size_t)(j0 + jj) * p.dv + i] = S[jj];
-    }
-    if (wave == 0) {
-      const float uo = o * sigmoidf_(p.z_scale * zi);
-      const int nv = p.heads * p.dv;
-      if (p.u_out && iv) p.u_out[(size_t)t * nv + h * p.dv + i] = uo;
-      const int blk = (h * p.dv + ic * RG) / QK + (lane >> 5);
-      const bool wr = (ic * RG + (lane & 32)) < p.dv;
-      quant_block_half_qt(p.next_qt, iv ? uo : 0.0f, p.next.xd + ((size_t)t * p.next.nblk + blk) * XW,
-                          p.next.xs + (size_t)t * p.next.nblk + blk, wr);
-    }
+    for (int jj = 0; jj < DKH; ++jj) S_out[(size_t)(j0 + jj) * p.dv + i] = S[jj];
+    const float uo = o * sigmoidf_(p.z_scale * zi);
+    const int nv = p.heads * p.dv;
+    if (p.u_out && half == 0) p.u_out[(size_t)t * nv + h * p.dv + i] = uo;
+    const int blk = (h * p.dv + ib * 32) / QK;
+    quant_block_half_qt(p.next_qt, uo, p.next.xd + ((size_t)t * p.next.nblk + blk) * XW,
+                        p.next.xs + (size_t)t * p.next.nblk + blk, half == 0);
     __syncthreads();
   }
 }
 
 hipError_t launch_deltanet(const DnParams& p, int T, hipStream_t s) {
   if (p.dk % 32 || p.dk > 128 || p.dv % 32) return hipErrorInvalidValue;
-  const int nic = (p.dv + RG - 1) / RG;
-  k_deltanet<<<p.heads * nic, 64 * (p.dk / 32), 0, s>>>(p, T);
+  const unsigned grid = (unsigned)(p.heads * (p.dv / 32));
+  switch (p.dk) {
+    case 32: k_deltanet<16><<<grid, 64, 0, s>>>(p, T); break;
+    case 64: k_deltanet<32><<<grid, 64, 0, s>>>(p, T); break;
+    case 96: k_deltanet<48><<<grid, 64, 0, s>>>(p, T); break;
+    case 128: k_deltanet<64><<<grid, 64, 0, s>>>(p, T); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -137,13 +137,11 @@ hipError_t launch_quant_act(int qt, const float* x, int T, int n, int64_t x_ts, 
 hipError_t launch_gemv(const Packed& W, int T, Act x, NormIn nin, GemvOut out, int ksplit, int waves,
                        hipStream_t s) {
   if (waves < 1 || waves > 16 || ksplit < 1) return hipErrorInvalidValue;
-  if ((out.kind == EPI_SWIGLU || out.kind == EPI_RESID) && ksplit != 1) return hipErrorInvalidValue;
+  if (ksplit > 1 && (!out.part || !out.cnt)) return hipErrorInvalidValue;
   const bool q4 = W.qt == QT_Q4;
   switch (out.kind) {
     case EPI_STORE: return q4 ? gemv_inst<QT_Q4, EPI_STORE>(W, T, x, nin, out, ksplit, waves, s)
                               : gemv_inst<QT_Q8, EPI_STORE>(W, T, x, nin, out, ksplit, waves, s);
-    case EPI_PARTIAL: return q4 ? gemv_inst<QT_Q4, EPI_PARTIAL>(W, T, x, nin, out, ksplit, waves, s)
-                                : gemv_inst<QT_Q8, EPI_PARTIAL>(W, T, x, nin, out, ksplit, waves, s);
     case EPI_SWIGLU: return q4 ? gemv_inst<QT_Q4, EPI_SWIGLU>(W, T, x, nin, out, ksplit, waves, s)
                                : gemv_inst<QT_Q8, EPI_SWIGLU>(W, T, x, nin, out, ksplit, waves, s);
     case EPI_RESID: return q4 ? gemv_inst<QT_Q4, EPI_RESID>(W, T, x, nin, out, ksplit, waves, s)
@@ -152,55 +150,28 @@ hipError_t launch_gemv(const Packed& W, int T, Act x, NormIn nin, GemvOut out, i
   return hipErrorInvalidValue;
 }
 
-// ------------------------------------------- split-K partials -> outputs
+// ------------------------------------------------- boundary vector -> h
 
-__global__ void k_reduce_partials(const float* __restrict__ part, int ksplit, int T, int64_t rows,
-                                  NormIn nin, float* __restrict__ y) {
-  const int t = blockIdx.y;
-  const int64_t r = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (r >= rows) return;
-  float s = 0.0f;
-  for (int k = 0; k < ksplit; ++k) s += part[((size_t)k * T + t) * rows + r];
-  y[(size_t)t * rows + r] = s * rnorm_from(nin, t);
-}
-
-hipError_t launch_reduce_partials(const float* part, int ksplit, int T, int64_t rows, NormIn nin,
-                                  float* y, hipStream_t s) {
-  dim3 grid((unsigned)((rows + 255) / 256), T);
-  k_reduce_partials<<<grid, 256, 0, s>>>(part, ksplit, T, rows, nin, y);
-  return hipGetLastError();
-}
-
-// h (+)= partials or input; then digits of norm_w*h and sums of squares.
-__global__ void k_resid_finish(int in_kind, const void* in, const Ctrl* ctrl, int64_t in_ts,
-                               const float* __restrict__ part, int ksplit, int T, int H, float* h,
-                               const float* __restrict__ norm_w, int qt, Act next, float* ssq_out) {
+// h = boundary input (fp16 or fp32); then digits of norm_w*h and sums of squares.
+__global__ void k_resid_finish(int in_kind, const void* in, const Ctrl* ctrl, int64_t in_ts, int T, int H,
+                               float* h, const float* __restrict__ norm_w, int qt, Act next, float* ssq_out) {
   const int rg = blockIdx.x;
   const int t = blockIdx.y;
   const int lane = threadIdx.x;
   const int row = rg * RG + lane;
+  if (!in) in = ctrl->in;
   float hn = 0.0f;
-  if (in_kind != 0 && !in) in = ctrl->in;
   if (row < H) {
-    if (in_kind == 0) {
-      hn = h[(size_t)t * H + row];
-      float s = 0.0f;
-      for (int k = 0; k < ksplit; ++k) s += part[((size_t)k * T + t) * H + row];
-      hn += s;
-    } else if (in_kind == 1) {
-      hn = __half2float(reinterpret_cast<const __half*>(in)[(size_t)t * in_ts + row]);
-    } else {
-      hn = reinterpret_cast<const float*>(in)[(size_t)t * in_ts + row];
-    }
+    if (in_kind == 1) hn = __half2float(reinterpret_cast<const __half*>(in)[(size_t)t * in_ts + row]);
+    else hn = reinterpret_cast<const float*>(in)[(size_t)t * in_ts + row];
   }
   resid_tail(t, rg, H, hn, h, H, norm_w, qt, next, ssq_out, (H + RG - 1) / RG);
 }
 
-hipError_t launch_resid_finish(int in_kind, const void* in, const Ctrl* ctrl, int64_t in_ts, const float* part,
-                               int ksplit, int T, int H, float* h, const float* norm_w, int qt, Act next,
-                               float* ssq_out, hipStream_t s) {
+hipError_t launch_resid_finish(int in_kind, const void* in, const Ctrl* ctrl, int64_t in_ts, int T, int H,
+                               float* h, const float* norm_w, int qt, Act next, float* ssq_out, hipStream_t s) {
   dim3 grid((unsigned)((H + RG - 1) / RG), T);
-  k_resid_finish<<<grid, 64, 0, s>>>(in_kind, in, ctrl, in_ts, part, ksplit, T, H, h, norm_w, qt, next, ssq_out);
+  k_resid_finish<<<grid, 64, 0, s>>>(in_kind, in, ctrl, in_ts, T, H, h, norm_w, qt, next, ssq_out);
   return hipGetLastError();
 }
 

@@ -203,13 +203,40 @@ __global__ __launch_bounds__(1024) void k_gemv(Packed W, Act x, NormIn nin, Gemv
   }
   if (wave != 0) return;
 
+  if (ksplit > 1) {
+    // Publish this split's sums and take a ticket; the last split of the row
+    // group adds all of them in split order (so the result does not depend on
+    // arrival order) and runs the epilogue.  Partials and the ticket only move
+    // through agent-scope atomic accesses, which are coherent across the XCDs
+    // by themselves; waiting for the stores (vmcnt 0) before taking the ticket
+    // orders them.  No cache-wide write-back or invalidate is needed.
+    float* my = out.part + ((size_t)rg * ksplit + ks) * T * RG;
+#pragma unroll
+    for (int j = 0; j < T; ++j)
+      __hip_atomic_store(my + j * RG + lane, acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    __builtin_amdgcn_s_waitcnt(0);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);
+    unsigned ticket = 0;
+    if (lane == 0) ticket = __hip_atomic_fetch_add(out.cnt + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    ticket = __shfl(ticket, 0, 64);
+    if (ticket != (unsigned)(ksplit - 1)) return;
+    const float* all = out.part + (size_t)rg * ksplit * T * RG;
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+      float s = 0.0f;
+      for (int k2 = 0; k2 < ksplit; ++k2)
+        s += __hip_atomic_load(all + ((size_t)k2 * T + j) * RG + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      acc[j] = s;
+    }
+    if (lane == 0) __hip_atomic_store(out.cnt + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+
   const int64_t row = (int64_t)rg * RG + lane;
   const bool rv = row < W.rows;
 #pragma unroll
   for (int j = 0; j < T; ++j) {
-    if constexpr (EPI == EPI_PARTIAL) {
-      if (rv) out.y[((size_t)ks * T + j) * out.y_tstride + row] = acc[j];
-    } else if constexpr (EPI == EPI_STORE) {
+    if constexpr (EPI == EPI_STORE) {
       const float rn = rnorm_from(nin, j);
       if (rv) out.y[(size_t)j * out.y_tstride + row] = acc[j] * rn;
     } else if constexpr (EPI == EPI_SWIGLU) {
@@ -246,10 +273,8 @@ hipError_t gemv_inst(const Packed& W, int T, Act x, NormIn nin, GemvOut out, int
 
 #define SLQ_DECLARE_GEMV(QT, EPI) \
   extern template hipError_t gemv_inst<QT, EPI>(const Packed&, int, Act, NormIn, GemvOut, int, int, hipStream_t);
-SLQ_DECLARE_GEMV(QT_Q4, EPI_STORE) SLQ_DECLARE_GEMV(QT_Q4, EPI_PARTIAL)
-SLQ_DECLARE_GEMV(QT_Q4, EPI_SWIGLU) SLQ_DECLARE_GEMV(QT_Q4, EPI_RESID)
-SLQ_DECLARE_GEMV(QT_Q8, EPI_STORE) SLQ_DECLARE_GEMV(QT_Q8, EPI_PARTIAL)
-SLQ_DECLARE_GEMV(QT_Q8, EPI_SWIGLU) SLQ_DECLARE_GEMV(QT_Q8, EPI_RESID)
+SLQ_DECLARE_GEMV(QT_Q4, EPI_STORE) SLQ_DECLARE_GEMV(QT_Q4, EPI_SWIGLU) SLQ_DECLARE_GEMV(QT_Q4, EPI_RESID)
+SLQ_DECLARE_GEMV(QT_Q8, EPI_STORE) SLQ_DECLARE_GEMV(QT_Q8, EPI_SWIGLU) SLQ_DECLARE_GEMV(QT_Q8, EPI_RESID)
 #undef SLQ_DECLARE_GEMV
 
 }  // namespace slq

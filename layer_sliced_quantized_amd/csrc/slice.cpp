@@ -12,6 +12,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <algorithm>
 #include <map>
 #include <string>
 #include <vector>
@@ -44,14 +45,38 @@ int env_int(const char* name, int dflt) {
   return v && *v ? atoi(v) : dflt;
 }
 
-// Waves per workgroup for a GEMV with whole K in each workgroup: aim for about
-// 2048 resident waves (8 per CU) without giving a wave less than one tile.
-int pick_waves(int nrg, int ntiles) {
-  int w = (2048 + nrg - 1) / nrg;
-  if (w > 16) w = 16;
-  if (w > ntiles) w = ntiles;
-  if (w < 1) w = 1;
-  return w;
+// Launch shape of one GEMV: `ks` workgroups share the K tiles of each 64-row
+// group (their partial sums meet through atomics), `w` waves per workgroup.
+// Defaults come from kernel-trace sweeps on MI355X at hidden 5120 (all Q4_0):
+//   input projections (16448/14336 x 5120): ks 4, w 4
+//   gate/up + SwiGLU (34816 x 5120):        ks 2, w 4
+//   down projection (5120 x 17408):         ks 8, w 4
+//   mixer output (5120 x 4096 / 6144):      ks 1, w 16
+// Other shapes: enough splits for ~1000 workgroups, about two tiles per wave.
+// SLQ_KS_<kind> / SLQ_W_<kind> override (kinds G1, G2, F1, F2, HEAD, GEMV).
+struct Plan {
+  int ks, w;
+};
+
+int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
+
+Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
+  const int nrg = (int)((rows + RG - 1) / RG);
+  const int ntiles = (int)((cols / QK + TB - 1) / TB);
+  const std::string k(kind);
+  Plan p;
+  if (k == "G2" && nrg <= 128) {
+    p.ks = 1;
+    p.w = clampi(ntiles, 1, 16);
+  } else {
+    p.ks = clampi((1024 + nrg - 1) / nrg, 1, ntiles < 16 ? ntiles : 16);
+    if (k == "F1") p.ks = clampi(p.ks, 1, 2);
+    if (k == "F2" || k == "G1") p.ks = clampi(p.ks, 1, k == "F2" ? 8 : 4);
+    p.w = clampi(k == "GEMV" || k == "HEAD" ? (ntiles / p.ks + 1) / 2 : 4, 1, 16);
+  }
+  p.ks = clampi(env_int(("SLQ_KS_" + k).c_str(), p.ks), 1, 16);
+  p.w = clampi(env_int(("SLQ_W_" + k).c_str(), p.w), 1, 16);
+  return p;
 }
 
 struct Mat {
@@ -76,12 +101,12 @@ struct Layout {
   size_t wbytes = 0;
   // workspace
   size_t ctrl = 0, h = 0, xa_d = 0, xa_s = 0, xu_d = 0, xu_s = 0, xm_d = 0, xm_s = 0, ssq = 0, y1 = 0,
-         part = 0, qhat = 0, apart = 0, logits = 0, amax_v = 0, amax_i = 0, kv = 0, dn = 0;
+         part = 0, cnt = 0, qhat = 0, apart = 0, logits = 0, amax_v = 0, amax_i = 0, kv = 0, dn = 0;
   size_t kv_layer_bytes = 0, dn_layer_bytes = 0;
   size_t wsbytes = 0;
   int64_t g1_rows_max = 0;
   int nu = 0;              // width of the mixer output (G2 input)
-  int nchunk = 0, n_dn = 0, n_attn = 0, nslots = 0, mt = 1, ksplit_resid = 1, amax_parts = 256;
+  int nchunk = 0, n_dn = 0, n_attn = 0, nslots = 0, mt = 1, amax_parts = 256;
 };
 
 std::string validate(const slice_config& c) {
@@ -184,9 +209,6 @@ Layout make_layout(const slice_config& c) {
   const int nblkH = H / QK;
   const int nblkU = (L.nu + QK - 1) / QK;
   const int nblkM = c.ffn / QK;
-  L.ksplit_resid = env_int("SLQ_RESID_KSPLIT", 1);
-  if (L.ksplit_resid < 1) L.ksplit_resid = 1;
-  if (L.ksplit_resid > 16) L.ksplit_resid = 16;
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t r = o;
@@ -203,7 +225,14 @@ Layout make_layout(const slice_config& c) {
   L.xm_s = take((size_t)mt * (nblkM ? nblkM : 1) * 4);
   L.ssq = take((size_t)mt * (H / RG) * 4);
   L.y1 = take((size_t)mt * (L.g1_rows_max ? L.g1_rows_max : 1) * 4);
-  L.part = take((size_t)L.ksplit_resid * mt * H * 4);
+  // split-K scratch: any GEMV of the slice with up to 16 splits
+  int64_t rg_max = 0;
+  auto upd = [&](const Mat& m) { if (m.present) rg_max = std::max<int64_t>(rg_max, (m.rows + RG - 1) / RG); };
+  for (const LayerLayout& ll : L.layers) { upd(ll.g1); upd(ll.g2); upd(ll.f1); upd(ll.f2); }
+  upd(L.embed);
+  upd(L.head);
+  L.part = take((size_t)rg_max * 16 * mt * RG * 4);
+  L.cnt = take((size_t)rg_max * 4);
   if (L.n_attn) {
     L.nchunk = (c.max_seq + ATT_CHUNK - 1) / ATT_CHUNK;
     L.qhat = take((size_t)mt * nq * 4);
@@ -246,9 +275,24 @@ struct slice {
   }
 };
 
+// Optional per-op timing: an event is recorded at every op boundary.
+struct Prof {
+  std::vector<hipEvent_t> ev;
+  std::vector<int> kind;   // kind of the op that ends at ev[i+1]
+  int mark(int k, hipStream_t st) {
+    hipEvent_t e;
+    HIPCHK(hipEventCreate(&e));
+    HIPCHK(hipEventRecord(e, st));
+    ev.push_back(e);
+    if (ev.size() > 1) kind.push_back(k);
+    return SLICE_OK;
+  }
+};
+
 // One step with T tokens: entry, every layer, exit.  Reads the input/output
 // pointers from the control block so a captured graph serves any buffers.
-static int enqueue_step(slice* s, int T, bool decode, hipStream_t st) {
+static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof = nullptr) {
+#define SLQ_MARK(k) do { if (prof) { int r_ = prof->mark(k, st); if (r_) return r_; } } while (0)
   const slice_config& c = s->cfg;
   const Layout& L = s->L;
   const int H = c.hidden;
@@ -265,9 +309,11 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st) {
     return reinterpret_cast<const float*>(s->w + L.out_norm);
   };
   // entry: boundary vector -> h, digits of attn_norm(first layer) * h
-  HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, nullptr, ctrl, H, nullptr, 0, T, H, h, attn_norm_of(0), qt,
-                             s->act_a(), ssq, st));
-  const int ks = L.ksplit_resid;
+  SLQ_MARK(-1);
+  HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, nullptr, ctrl, H, T, H, h, attn_norm_of(0), qt, s->act_a(), ssq, st));
+  SLQ_MARK(SLICE_OP_ENTRY);
+  float* part = s->wsp<float>(L.part);
+  unsigned* cnt = s->wsp<unsigned>(L.cnt);
   for (int i = 0; i < nlay; ++i) {
     const LayerLayout& ll = L.layers[i];
     // mixer input projections: G1 = [q|k|v|a|b|z] or [q|g|k|v] of RMSNorm(h)
@@ -277,7 +323,11 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st) {
       o.kind = EPI_STORE;
       o.y = y1;
       o.y_tstride = W.rows;
-      HIPCHK(launch_gemv(W, T, s->act_a(), s->norm_h(), o, 1, env_int("SLQ_W_G1", pick_waves(W.nrg(), W.ntiles())), st));
+      o.part = part;
+      o.cnt = cnt;
+      const Plan pl = plan_gemv("G1", W.rows, W.cols);
+      HIPCHK(launch_gemv(W, T, s->act_a(), s->norm_h(), o, pl.ks, pl.w, st));
+      SLQ_MARK(ll.attn ? SLICE_OP_ATT_IN : SLICE_OP_DN_IN);
     }
     if (ll.attn) {
       AttnParams p{};
@@ -302,6 +352,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st) {
       p.next = s->act_u();
       p.next_qt = qt;
       HIPCHK(launch_attention(p, T, st));
+      SLQ_MARK(SLICE_OP_ATTENTION);
     } else {
       DnParams p{};
       p.y = y1;
@@ -318,35 +369,29 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st) {
       p.next = s->act_u();
       p.next_qt = qt;
       HIPCHK(launch_deltanet(p, T, st));
+      SLQ_MARK(SLICE_OP_DELTANET);
     }
     // residual update after the mixer: h += W_o u, then digits for the next RMSNorm
     const float* nw_after_mixer = c.ffn ? reinterpret_cast<const float*>(s->w + ll.ffn_norm) : attn_norm_of(i + 1);
-    auto residual = [&](const Mat& m, Act in, const float* next_norm) -> int {
+    auto residual = [&](const Mat& m, Act in, const float* next_norm, const char* kind) -> int {
       const Packed W = s->packed(m);
-      if (ks <= 1) {
-        GemvOut o{};
-        o.kind = EPI_RESID;
-        o.y = h;
-        o.y_tstride = H;
-        o.next = s->act_a();
-        o.next_qt = qt;
-        o.ssq_out = ssq;
-        o.norm_w = next_norm;
-        HIPCHK(launch_gemv(W, T, in, NormIn{nullptr, 0, 0.f, 0.f}, o, 1, env_int("SLQ_W_RESID", 16), st));
-      } else {
-        GemvOut o{};
-        o.kind = EPI_PARTIAL;
-        o.y = s->wsp<float>(L.part);
-        o.y_tstride = H;
-        HIPCHK(launch_gemv(W, T, in, NormIn{nullptr, 0, 0.f, 0.f}, o, ks,
-                           env_int("SLQ_W_RESID", pick_waves(W.nrg() * ks, (W.ntiles() + ks - 1) / ks)), st));
-        HIPCHK(launch_resid_finish(0, nullptr, nullptr, 0, s->wsp<float>(L.part), ks, T, H, h, next_norm, qt,
-                                   s->act_a(), ssq, st));
-      }
+      GemvOut o{};
+      o.kind = EPI_RESID;
+      o.y = h;
+      o.y_tstride = H;
+      o.next = s->act_a();
+      o.next_qt = qt;
+      o.ssq_out = ssq;
+      o.norm_w = next_norm;
+      o.part = part;
+      o.cnt = cnt;
+      const Plan pl = plan_gemv(kind, W.rows, W.cols);
+      HIPCHK(launch_gemv(W, T, in, NormIn{nullptr, 0, 0.f, 0.f}, o, pl.ks, pl.w, st));
       return SLICE_OK;
     };
-    int rc = residual(ll.g2, s->act_u(), nw_after_mixer);
+    int rc = residual(ll.g2, s->act_u(), nw_after_mixer, "G2");
     if (rc) return rc;
+    SLQ_MARK(ll.attn ? SLICE_OP_ATT_OUT : SLICE_OP_DN_OUT);
     if (c.ffn) {
       const Packed W = s->packed(ll.f1);
       GemvOut o{};
@@ -355,13 +400,20 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st) {
       o.y_tstride = c.ffn;
       o.next = s->act_m();
       o.next_qt = qt;
-      HIPCHK(launch_gemv(W, T, s->act_a(), s->norm_h(), o, 1, env_int("SLQ_W_F1", pick_waves(W.nrg(), W.ntiles())), st));
-      rc = residual(ll.f2, s->act_m(), attn_norm_of(i + 1));
+      o.part = part;
+      o.cnt = cnt;
+      const Plan pl = plan_gemv("F1", W.rows, W.cols);
+      HIPCHK(launch_gemv(W, T, s->act_a(), s->norm_h(), o, pl.ks, pl.w, st));
+      SLQ_MARK(SLICE_OP_FFN_IN);
+      rc = residual(ll.f2, s->act_m(), attn_norm_of(i + 1), "F2");
       if (rc) return rc;
+      SLQ_MARK(SLICE_OP_FFN_OUT);
     }
   }
   HIPCHK(launch_store_out(h, T, H, nullptr, c.io_fp32, ctrl, decode ? 1 : 0, st));
+  SLQ_MARK(SLICE_OP_EXIT);
   return SLICE_OK;
+#undef SLQ_MARK
 }
 
 static int run_step(slice* s, int T, bool decode, const void* in, void* out, hipStream_t st) {
@@ -421,26 +473,12 @@ int slq_dequant(int qtype, const void* packed_dev, int64_t rows, int64_t cols, f
   return SLICE_OK;
 }
 
-static void gemv_plan(int64_t rows, int64_t cols, int* ksplit, int* waves) {
-  const int nrg = (int)((rows + RG - 1) / RG);
-  const int ntiles = (int)((cols / QK + TB - 1) / TB);
-  int ks = 1;
-  if (nrg < 256) ks = (256 + nrg - 1) / nrg;
-  if (ks > ntiles) ks = ntiles;
-  if (ks > 16) ks = 16;
-  ks = env_int("SLQ_GEMV_KSPLIT", ks);
-  if (ks < 1) ks = 1;
-  int w = pick_waves(nrg * ks, (ntiles + ks - 1) / ks);
-  w = env_int("SLQ_GEMV_WAVES", w);
-  *ksplit = ks;
-  *waves = w;
-}
-
 size_t slq_gemv_workspace_bytes(int qtype, int64_t rows, int64_t cols, int batch) {
   if (!slq_packed_bytes(qtype, rows, cols) || batch < 1 || batch > MAX_T) return 0;
   const int nblk = (int)(cols / QK);
+  const int64_t nrg = (rows + RG - 1) / RG;
   return al256((size_t)batch * nblk * XW * 4) + al256((size_t)batch * nblk * 4) +
-         al256((size_t)16 * batch * rows * 4);
+         al256((size_t)nrg * 16 * batch * RG * 4) + al256((size_t)nrg * 4);
 }
 
 int slq_gemv(int qtype, const void* packed_dev, int64_t rows, int64_t cols, int batch, const float* x_dev,
@@ -452,24 +490,20 @@ int slq_gemv(int qtype, const void* packed_dev, int64_t rows, int64_t cols, int 
   const int nblk = (int)(cols / QK);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
   Act a{reinterpret_cast<int32_t*>(ws), reinterpret_cast<float*>(ws + al256((size_t)batch * nblk * XW * 4)), nblk};
+  const int64_t nrg = (rows + RG - 1) / RG;
   float* part = reinterpret_cast<float*>(ws + al256((size_t)batch * nblk * XW * 4) + al256((size_t)batch * nblk * 4));
+  unsigned* cnt = reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(part) + al256((size_t)nrg * 16 * batch * RG * 4));
   HIPCHK(launch_quant_act(qtype, x_dev, batch, (int)cols, cols, a, S(stream)));
-  int ks, w;
-  gemv_plan(rows, cols, &ks, &w);
+  const Plan pl = plan_gemv("GEMV", rows, cols);
+  if (pl.ks > 1) HIPCHK(hipMemsetAsync(cnt, 0, (size_t)nrg * 4, S(stream)));
   const Packed W{static_cast<const uint8_t*>(packed_dev), rows, cols, qtype};
   GemvOut o{};
-  if (ks == 1) {
-    o.kind = EPI_STORE;
-    o.y = y_dev;
-    o.y_tstride = rows;
-    HIPCHK(launch_gemv(W, batch, a, NormIn{nullptr, 0, 0.f, 0.f}, o, 1, w, S(stream)));
-  } else {
-    o.kind = EPI_PARTIAL;
-    o.y = part;
-    o.y_tstride = rows;
-    HIPCHK(launch_gemv(W, batch, a, NormIn{nullptr, 0, 0.f, 0.f}, o, ks, w, S(stream)));
-    HIPCHK(launch_reduce_partials(part, ks, batch, rows, NormIn{nullptr, 0, 0.f, 0.f}, y_dev, S(stream)));
-  }
+  o.kind = EPI_STORE;
+  o.y = y_dev;
+  o.y_tstride = rows;
+  o.part = part;
+  o.cnt = cnt;
+  HIPCHK(launch_gemv(W, batch, a, NormIn{nullptr, 0, 0.f, 0.f}, o, pl.ks, pl.w, S(stream)));
   return SLICE_OK;
 }
 
@@ -592,6 +626,35 @@ int slice_decode(slice_t* s, const void* in, void* out, void* stream) {
   return SLICE_OK;
 }
 
+int slice_decode_profiled(slice_t* s, const void* in, void* out, int* op_kind, float* op_ms, int max_ops,
+                          void* stream) {
+  if (!s || !in || !out || !op_kind || !op_ms) return fail(SLICE_EINVAL, "slice_decode_profiled: null argument");
+  if (s->pending) return fail(SLICE_ESTATE, "slice_decode_profiled: a verify is waiting for slice_commit");
+  if (s->L.n_attn && s->pos + 1 > s->cfg.max_seq) return fail(SLICE_ERANGE, "slice_decode_profiled: position reached max_seq");
+  const hipStream_t st = S(stream);
+  if (in != s->last_in || out != s->last_out) {
+    HIPCHK(launch_ctrl_io(s->ctrl(), in, out, st));
+    s->last_in = in;
+    s->last_out = out;
+  }
+  Prof prof;
+  int rc = enqueue_step(s, 1, true, st, &prof);
+  int n = 0;
+  if (!rc) {
+    hipError_t e = hipEventSynchronize(prof.ev.back());
+    if (e != hipSuccess) rc = fail(SLICE_EHIP, std::string("hipEventSynchronize: ") + hipGetErrorString(e));
+    for (size_t i = 0; !rc && i < prof.kind.size() && n < max_ops; ++i, ++n) {
+      op_kind[n] = prof.kind[i];
+      e = hipEventElapsedTime(&op_ms[n], prof.ev[i], prof.ev[i + 1]);
+      if (e != hipSuccess) rc = fail(SLICE_EHIP, std::string("hipEventElapsedTime: ") + hipGetErrorString(e));
+    }
+  }
+  for (hipEvent_t e : prof.ev) hipEventDestroy(e);
+  if (rc) return rc;
+  s->pos += 1;
+  return n;
+}
+
 int slice_verify(slice_t* s, int k, const void* in, void* out, void* stream) {
   if (!s || !in || !out) return fail(SLICE_EINVAL, "slice_verify: null argument");
   if (s->pending) return fail(SLICE_ESTATE, "slice_verify: a verify is waiting for slice_commit");
@@ -629,7 +692,7 @@ int slice_head_argmax(slice_t* s, const void* in, int32_t* tok, float* logits, v
   const Layout& L = s->L;
   const hipStream_t st = S(stream);
   float* lg = logits ? logits : s->wsp<float>(L.logits);
-  HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, in, nullptr, c.hidden, nullptr, 0, 1, c.hidden, s->wsp<float>(L.h),
+  HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, in, nullptr, c.hidden, 1, c.hidden, s->wsp<float>(L.h),
                              reinterpret_cast<const float*>(s->w + L.out_norm), c.qtype, s->act_a(),
                              s->wsp<float>(L.ssq), st));
   const Packed W = s->packed(c.tied_head ? L.embed : L.head);
@@ -637,7 +700,10 @@ int slice_head_argmax(slice_t* s, const void* in, int32_t* tok, float* logits, v
   o.kind = EPI_STORE;
   o.y = lg;
   o.y_tstride = W.rows;
-  HIPCHK(launch_gemv(W, 1, s->act_a(), s->norm_h(), o, 1, pick_waves(W.nrg(), W.ntiles()), st));
+  o.part = s->wsp<float>(L.part);
+  o.cnt = s->wsp<unsigned>(L.cnt);
+  const Plan pl = plan_gemv("HEAD", W.rows, W.cols);
+  HIPCHK(launch_gemv(W, 1, s->act_a(), s->norm_h(), o, pl.ks, pl.w, st));
   HIPCHK(launch_argmax(lg, c.vocab, s->wsp<float>(L.amax_v), s->wsp<int>(L.amax_i), L.amax_parts, tok, st));
   return SLICE_OK;
 }

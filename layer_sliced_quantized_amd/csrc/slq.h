@@ -65,17 +65,22 @@ struct NormIn {
 };
 
 // GEMV epilogues
-enum Epi { EPI_STORE = 0, EPI_PARTIAL = 1, EPI_SWIGLU = 2, EPI_RESID = 3 };
+enum Epi { EPI_STORE = 0, EPI_SWIGLU = 2, EPI_RESID = 3 };
 
+// With ksplit > 1 the K tiles of a 64-row group are spread over ksplit
+// workgroups; each publishes its partial sums, and the last one to finish
+// (atomic ticket per row group) adds them in split order and runs the epilogue.
 struct GemvOut {
   int kind;
-  float* y;            // STORE: [T][rows]; PARTIAL: [ksplit][T][rows]; SWIGLU: m [T][rows/2]
-                       // (nullable); RESID: residual h [T][rows] updated in place
+  float* y;            // STORE: [T][rows]; SWIGLU: m [T][rows/2] (nullable);
+                       // RESID: residual h [T][rows] updated in place
   int64_t y_tstride;   // token stride of y in floats
   Act next;            // SWIGLU/RESID: digits of the next GEMV input
   int next_qt;
   float* ssq_out;      // RESID: [T][nrg] sums of squares of h
   const float* norm_w; // RESID: weights of the next RMSNorm (digits are of w*h)
+  float* part;         // ksplit > 1: partial sums [nrg][ksplit][T][64]
+  unsigned* cnt;       // ksplit > 1: one ticket counter per row group, zero before and after
 };
 
 struct Ctrl {         // device-resident step control
@@ -96,15 +101,12 @@ hipError_t launch_quant_act(int qt, const float* x, int T, int n, int64_t x_tstr
                             hipStream_t s);
 hipError_t launch_gemv(const Packed& W, int T, Act x, NormIn nin, GemvOut out, int ksplit,
                        int waves, hipStream_t s);
-hipError_t launch_reduce_partials(const float* part, int ksplit, int T, int64_t rows,
-                                  NormIn nin, float* y, hipStream_t s);
-// h [T][H] (+)= sum of partials / input, then digits of norm_w*h and ssq partials.
-// in_kind: 0 = h += partials, 1 = h = fp16 input, 2 = h = fp32 input; with in == nullptr
-// the input pointer is read from ctrl->in.
+// h [T][H] = boundary input, then digits of norm_w*h and ssq partials.
+// in_kind: 1 = fp16 input, 2 = fp32 input; with in == nullptr the input pointer
+// is read from ctrl->in.
 hipError_t launch_resid_finish(int in_kind, const void* in, const Ctrl* ctrl, int64_t in_tstride,
-                               const float* part, int ksplit, int T, int H, float* h,
-                               const float* norm_w, int qt, Act next, float* ssq_out,
-                               hipStream_t s);
+                               int T, int H, float* h, const float* norm_w, int qt, Act next,
+                               float* ssq_out, hipStream_t s);
 // out == nullptr: write to ctrl->out.
 hipError_t launch_store_out(const float* h, int T, int H, void* out, int fp32, Ctrl* ctrl,
                             int advance_pos, hipStream_t s);
@@ -150,7 +152,7 @@ struct AttnParams {
   float* u_out;          // [T][q_heads*hd] (nullable)
   Act next; int next_qt;
 };
-constexpr int ATT_CHUNK = 256;
+constexpr int ATT_CHUNK = 64;    // KV rows per split-attention workgroup
 hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s);
 hipError_t launch_kv_io(__half* kc, __half* vc, int kv_heads, int max_seq, int hd,
                         uint16_t* k, uint16_t* v, int rows, int to_device, hipStream_t s);
