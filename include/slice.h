@@ -219,6 +219,11 @@ int slice_dbg_set_kv(slice_t *s, int layer, const uint16_t *k_dev, const uint16_
 int slice_dbg_get_kv(slice_t *s, int layer, uint16_t *k_dev, uint16_t *v_dev,
                      int rows, void *stream);
 
+/* fp32 residual stream h [k][hidden] at the end of the last decode (k = 1) or
+ * verify (k tokens) step, before the boundary conversion.  For checking
+ * results when the boundary is fp16 and |h| passes the fp16 range. */
+int slice_dbg_get_hidden(slice_t *s, float *dst_dev, int k, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

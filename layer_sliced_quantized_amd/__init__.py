@@ -171,6 +171,12 @@ class Slice:
         check(lib().slice_dbg_get_kv(self.handle, layer, _ptr(K), _ptr(V), rows, _stream(stream)))
         return K, V
 
+    def get_hidden(self, k: int = 1, stream=None) -> torch.Tensor:
+        """fp32 residual stream of the last step (before the boundary conversion)."""
+        out = torch.empty((k, self.cfg.hidden), dtype=torch.float32, device=self.device)
+        check(lib().slice_dbg_get_hidden(self.handle, _ptr(out), k, _stream(stream)))
+        return out
+
     # ---- steps
     def decode(self, h_in: torch.Tensor, h_out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
         if h_out is None:

@@ -83,6 +83,7 @@ _SIGS = {
     "slice_dbg_get_state": (_I, [_V, _I, _V, _V]),
     "slice_dbg_set_kv": (_I, [_V, _I, _V, _V, _I, _V]),
     "slice_dbg_get_kv": (_I, [_V, _I, _V, _V, _I, _V]),
+    "slice_dbg_get_hidden": (_I, [_V, _V, _I, _V]),
 }
 
 

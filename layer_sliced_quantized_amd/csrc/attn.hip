@@ -71,11 +71,11 @@ __global__ __launch_bounds__(256) void k_attn_prep(AttnParams p) {
 // takes rows 16w..16w+15 of the chunk, 4 lanes per row each over a quarter of
 // the head dimensions, summed with two butterfly steps.  P V: one thread per
 // head dimension over the chunk's rows.
-template <int GRP>
+template <int GRP, int HD>
 __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   constexpr int C = ATT_CHUNK;
   __shared__ __attribute__((aligned(16))) float pl[GRP][C];
-  __shared__ __attribute__((aligned(16))) float qsh[GRP * 256];
+  __shared__ __attribute__((aligned(16))) float qsh[GRP * HD];
   __shared__ float wm[4][GRP];
   const int g = blockIdx.x / p.nchunk, c = blockIdx.x % p.nchunk;
   const int p0 = p.ctrl->pos;
@@ -85,7 +85,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   const int lane = tid & 63, wave = wave_id();
   const int rr = wave * 16 + (lane & 15);      // row of this lane inside the chunk
   const int dq = lane >> 4;                    // quarter of the head dimensions
-  const int qd = p.hd / 4;                     // dims per quarter (16 or 64 ...)
+  constexpr int NC = HD / 32;                  // 8-dim pieces per quarter of the head
   const int r = r0 + rr;
   for (int t = 0; t < T; ++t) {
     const int P = p0 + t;
@@ -93,17 +93,28 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
     if (nvalid <= 0) continue;
     {
       const float* qg = p.qhat + ((size_t)t * p.q_heads + g * GRP) * p.hd;
-      for (int i = tid; i < GRP * p.hd; i += 256) qsh[i] = qg[i];
+      float qv[GRP];
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) qv[h] = tid < HD ? qg[h * HD + tid] : 0.0f;
+#pragma unroll
+      for (int h = 0; h < GRP; ++h)
+        if (tid < HD) qsh[h * HD + tid] = qv[h];
     }
     __syncthreads();
     float s[GRP];
 #pragma unroll
     for (int h = 0; h < GRP; ++h) s[h] = 0.0f;
     if (rr < nvalid) {
-      for (int dc = dq * qd / 8; dc < (dq + 1) * qd / 8; ++dc) {
-        const uint4 kw = *reinterpret_cast<const uint4*>(p.kc + kidx(g, r, dc * 8, p.max_seq, p.hd));
+      // this lane's NC pieces of the key row, all requested before any math
+      uint4 kw[NC];
+#pragma unroll
+      for (int i = 0; i < NC; ++i)
+        kw[i] = *reinterpret_cast<const uint4*>(p.kc + kidx(g, r, (dq * NC + i) * 8, p.max_seq, HD));
+#pragma unroll
+      for (int i = 0; i < NC; ++i) {
+        const int dc = dq * NC + i;
         float kf[8];
-        const uint32_t ws[4] = {kw.x, kw.y, kw.z, kw.w};
+        const uint32_t ws[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           kf[2 * e] = __half2float(__ushort_as_half((unsigned short)(ws[e] & 0xffff)));
@@ -111,8 +122,8 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
         }
 #pragma unroll
         for (int h = 0; h < GRP; ++h) {
-          const float4 qa = *reinterpret_cast<const float4*>(qsh + h * p.hd + dc * 8);
-          const float4 qb = *reinterpret_cast<const float4*>(qsh + h * p.hd + dc * 8 + 4);
+          const float4 qa = *reinterpret_cast<const float4*>(qsh + h * HD + dc * 8);
+          const float4 qb = *reinterpret_cast<const float4*>(qsh + h * HD + dc * 8 + 4);
           s[h] = __builtin_fmaf(kf[0], qa.x, s[h]);
           s[h] = __builtin_fmaf(kf[1], qa.y, s[h]);
           s[h] = __builtin_fmaf(kf[2], qa.z, s[h]);
@@ -153,30 +164,31 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
 #pragma unroll
     for (int h = 0; h < GRP; ++h) l[h] = (wm[0][h] + wm[1][h]) + (wm[2][h] + wm[3][h]);
     // P V: thread = dimension
-    if (tid < p.hd) {
+    if (tid < HD) {
       float o[GRP];
 #pragma unroll
       for (int h = 0; h < GRP; ++h) o[h] = 0.0f;
-      const __half* vrow = p.vc + ((size_t)g * p.max_seq + r0) * p.hd + tid;
+      const __half* vrow = p.vc + ((size_t)g * p.max_seq + r0) * HD + tid;
       // rows past nvalid have weight 0 and lie inside the cache (r0 + C <= max_seq)
-      const int n4 = (nvalid + 3) & ~3;
-      for (int q = 0; q < n4; q += 4) {
-        const float v0 = __half2float(vrow[(size_t)(q + 0) * p.hd]);
-        const float v1 = __half2float(vrow[(size_t)(q + 1) * p.hd]);
-        const float v2 = __half2float(vrow[(size_t)(q + 2) * p.hd]);
-        const float v3 = __half2float(vrow[(size_t)(q + 3) * p.hd]);
+      for (int q0 = 0; q0 < nvalid; q0 += 16) {
+        float v[16];
 #pragma unroll
-        for (int h = 0; h < GRP; ++h) {
-          const float4 w4 = *reinterpret_cast<const float4*>(&pl[h][q]);
-          o[h] = __builtin_fmaf(w4.x, v0, o[h]);
-          o[h] = __builtin_fmaf(w4.y, v1, o[h]);
-          o[h] = __builtin_fmaf(w4.z, v2, o[h]);
-          o[h] = __builtin_fmaf(w4.w, v3, o[h]);
+        for (int u = 0; u < 16; ++u) v[u] = __half2float(vrow[(size_t)(q0 + u) * HD]);
+#pragma unroll
+        for (int u = 0; u < 16; u += 4) {
+#pragma unroll
+          for (int h = 0; h < GRP; ++h) {
+            const float4 w4 = *reinterpret_cast<const float4*>(&pl[h][q0 + u]);
+            o[h] = __builtin_fmaf(w4.x, v[u], o[h]);
+            o[h] = __builtin_fmaf(w4.y, v[u + 1], o[h]);
+            o[h] = __builtin_fmaf(w4.z, v[u + 2], o[h]);
+            o[h] = __builtin_fmaf(w4.w, v[u + 3], o[h]);
+          }
         }
       }
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
-        float* dst = p.part + (((size_t)t * p.q_heads + g * GRP + h) * p.nchunk + c) * (p.hd + 2);
+        float* dst = p.part + (((size_t)t * p.q_heads + g * GRP + h) * p.nchunk + c) * (HD + 2);
         dst[2 + tid] = o[h];
         if (tid == 0) { dst[0] = m[h]; dst[1] = l[h]; }
       }
@@ -216,9 +228,19 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnParams p) {
   }
   __syncthreads();
   float o = 0.0f;
-  for (int c = 0; c < nc; ++c) {
-    const float w = c < 1024 ? wsh[c] : __expf(base[(size_t)c * stride] - M);
-    o = __builtin_fmaf(base[(size_t)c * stride + 2 + d], w, o);
+  for (int c0 = 0; c0 < nc; c0 += 8) {
+    // eight loads in flight, then the adds in chunk order
+    float v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) v[u] = c0 + u < nc ? base[(size_t)(c0 + u) * stride + 2 + d] : 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int c = c0 + u;
+      if (c < nc) {
+        const float w = c < 1024 ? wsh[c] : __expf(base[(size_t)c * stride] - M);
+        o = __builtin_fmaf(v[u], w, o);
+      }
+    }
   }
   o = o / L;
   if (p.off_g >= 0) o = o * sigmoidf_(p.y[(size_t)t * p.y_stride + p.off_g + h * p.hd + d]);
@@ -236,12 +258,21 @@ hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {
   k_attn_prep<<<T * (p.q_heads + p.kv_heads), p.hd, 0, s>>>(p);
   const int grp = p.q_heads / p.kv_heads;
   const unsigned grid = (unsigned)(p.kv_heads * p.nchunk);
-  switch (grp) {
-#define SLQ_G(n) case n: k_attn_split<n><<<grid, 256, 0, s>>>(p, T); break;
-    SLQ_G(1) SLQ_G(2) SLQ_G(3) SLQ_G(4) SLQ_G(5) SLQ_G(6) SLQ_G(7) SLQ_G(8)
-#undef SLQ_G
+#define SLQ_G(n, hd) case n: k_attn_split<n, hd><<<grid, 256, 0, s>>>(p, T); break;
+#define SLQ_HD(hd)                                                                        \
+  case hd:                                                                                \
+    switch (grp) {                                                                        \
+      SLQ_G(1, hd) SLQ_G(2, hd) SLQ_G(3, hd) SLQ_G(4, hd) SLQ_G(5, hd) SLQ_G(6, hd)       \
+      SLQ_G(7, hd) SLQ_G(8, hd)                                                           \
+      default: return hipErrorInvalidValue;                                               \
+    }                                                                                     \
+    break;
+  switch (p.hd) {
+    SLQ_HD(64) SLQ_HD(128) SLQ_HD(192) SLQ_HD(256)
     default: return hipErrorInvalidValue;
   }
+#undef SLQ_HD
+#undef SLQ_G
   k_attn_combine<<<T * p.q_heads * (p.hd / 64), 64, 0, s>>>(p);
   return hipGetLastError();
 }

@@ -27,12 +27,16 @@ __device__ __forceinline__ float half_max(float v) {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
-// RMSNorm factor from a producer's partial sums of squares (fixed order).
+// RMSNorm factor from a producer's partial sums of squares: one load per lane
+// (all in flight together), then a butterfly sum, so every wave that calls
+// this gets the same value.
 __device__ __forceinline__ float rnorm_from(const NormIn& n, int t) {
   if (!n.ssq) return 1.0f;
+  const int lane = threadIdx.x & 63;
   const float* s = n.ssq + (size_t)t * n.n_part;
   float a = 0.0f;
-  for (int i = 0; i < n.n_part; ++i) a += s[i];
+  for (int i = lane; i < n.n_part; i += 64) a += s[i];
+  a = wave_sum(a);
   return 1.0f / sqrtf(a * n.inv_n + n.eps);
 }
 

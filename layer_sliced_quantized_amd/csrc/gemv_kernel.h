@@ -164,6 +164,11 @@ __global__ __launch_bounds__(1024) void k_gemv(Packed W, Act x, NormIn nin, Gemv
   float acc[T];
 #pragma unroll
   for (int j = 0; j < T; ++j) acc[j] = 0.0f;
+  // RMSNorm factor of the input (STORE / SWIGLU), fetched now so its latency
+  // hides under the weight stream
+  float rn[T];
+#pragma unroll
+  for (int j = 0; j < T; ++j) rn[j] = (EPI != EPI_RESID && wave == 0) ? rnorm_from(nin, j) : 1.0f;
 
   // full tiles, two register sets in turn so the next tile's loads overlap this tile's math
   const int te = t1 < full ? t1 : full;
@@ -224,9 +229,17 @@ __global__ __launch_bounds__(1024) void k_gemv(Packed W, Act x, NormIn nin, Gemv
     const float* all = out.part + (size_t)rg * ksplit * T * RG;
 #pragma unroll
     for (int j = 0; j < T; ++j) {
+      // all loads in flight before the first add; the adds run in split order
+      float pv[16];
+#pragma unroll
+      for (int k2 = 0; k2 < 16; ++k2)
+        pv[k2] = k2 < ksplit ? __hip_atomic_load(all + ((size_t)k2 * T + j) * RG + lane, __ATOMIC_RELAXED,
+                                                 __HIP_MEMORY_SCOPE_AGENT)
+                             : 0.0f;
       float s = 0.0f;
-      for (int k2 = 0; k2 < ksplit; ++k2)
-        s += __hip_atomic_load(all + ((size_t)k2 * T + j) * RG + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+      for (int k2 = 0; k2 < 16; ++k2)
+        if (k2 < ksplit) s += pv[k2];
       acc[j] = s;
     }
     if (lane == 0) __hip_atomic_store(out.cnt + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -237,12 +250,10 @@ __global__ __launch_bounds__(1024) void k_gemv(Packed W, Act x, NormIn nin, Gemv
 #pragma unroll
   for (int j = 0; j < T; ++j) {
     if constexpr (EPI == EPI_STORE) {
-      const float rn = rnorm_from(nin, j);
-      if (rv) out.y[(size_t)j * out.y_tstride + row] = acc[j] * rn;
+      if (rv) out.y[(size_t)j * out.y_tstride + row] = acc[j] * rn[j];
     } else if constexpr (EPI == EPI_SWIGLU) {
       // lanes 0..31: gate rows, lanes 32..63: the matching up rows
-      const float rn = rnorm_from(nin, j);
-      const float v = acc[j] * rn;
+      const float v = acc[j] * rn[j];
       const float up = __shfl(v, (lane + 32) & 63, 64);
       const float m = (v / (1.0f + expf(-v))) * up;
       if (out.y && lane < 32) out.y[(size_t)j * out.y_tstride + rg * 32 + lane] = m;

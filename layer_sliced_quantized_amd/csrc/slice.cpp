@@ -753,6 +753,13 @@ static int kv_io(slice_t* s, int layer, uint16_t* k, uint16_t* v, int rows, int 
   return SLICE_OK;
 }
 
+int slice_dbg_get_hidden(slice_t* s, float* dst, int k, void* stream) {
+  if (!s || !dst) return fail(SLICE_EINVAL, "null argument");
+  if (k < 1 || k > s->L.mt) return fail(SLICE_ERANGE, "k outside 1..max_verify");
+  HIPCHK(hipMemcpyAsync(dst, s->ws + s->L.h, (size_t)k * s->cfg.hidden * 4, hipMemcpyDeviceToDevice, S(stream)));
+  return SLICE_OK;
+}
+
 int slice_dbg_set_kv(slice_t* s, int layer, const uint16_t* k, const uint16_t* v, int rows, void* stream) {
   return kv_io(s, layer, const_cast<uint16_t*>(k), const_cast<uint16_t*>(v), rows, 1, stream);
 }

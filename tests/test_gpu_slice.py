@@ -18,7 +18,7 @@ import layer_sliced_quantized_amd as slq
 pytestmark = pytest.mark.gpu
 
 # Small hybrid: every kernel of the 5120-wide model at toy width; the KV prefix
-# spans two 256-row attention chunks and ends inside the second.
+# spans several 64-row attention chunks and ends inside one.
 TINY_H = synth.ModelShape(
     name="tiny_hybrid_128", hidden=128, n_layers=4, attn_period=4,
     dn_heads=2, dn_dk=64, dn_dv=64, q_heads=4, kv_heads=2, head_dim=64, rope_dims=32,
@@ -223,23 +223,27 @@ def test_attention_layer_5120_decode_and_verify(L):
 @pytest.mark.timeout(900)
 def test_hybrid_64_layer_q4_slice():
     """64-layer Q4_0 hybrid slice: decode two tokens, verify 4 drafts, commit
-    the seeded number of accepted drafts, decode once more.  fp16 boundary."""
+    the seeded number of accepted drafts, decode once more.  fp16 inputs as a
+    middle stage receives them; the outputs are compared on the fp32 residual
+    stream, because with these synthetic weights |h| grows past the fp16 range
+    within two layers (every fp16 output entry saturates)."""
     sh = synth.HYBRID_5120
     s, orc, _, _ = make_pair(sh, synth.Q4_0, 0, 64, workload=synth.WL_SLICE, prefill=512, max_seq=1024,
                              max_verify=4, io_fp32=False, threads=16)
     H = inputs(sh, 7, workload=synth.WL_SLICE, io_fp32=False)
     for t in range(2):
-        out = s.decode(_t(H[t])).cpu().numpy()
-        assert rel_err(out, orc.decode(H[t])) <= TOL, t
-    out = s.verify(_t(H[2:6])).cpu().numpy()
-    ref = orc.verify(H[2:6])
+        s.decode(_t(H[t]))
+        assert rel_err(s.get_hidden().cpu().numpy()[0], orc.decode(H[t], raw=True)) <= TOL, t
+    s.verify(_t(H[2:6]))
+    out = s.get_hidden(4).cpu().numpy()
+    ref = orc.verify(H[2:6], raw=True)
     for t in range(4):
         assert rel_err(out[t], ref[t]) <= TOL, t
     j = int(synth.accept_pattern(0, 1, 4)[0])
     s.commit(j)
     orc.commit(j)
-    out = s.decode(_t(H[6])).cpu().numpy()
-    assert rel_err(out, orc.decode(H[6])) <= TOL
+    s.decode(_t(H[6]))
+    assert rel_err(s.get_hidden().cpu().numpy()[0], orc.decode(H[6], raw=True)) <= TOL
 
 
 @pytest.mark.timeout(600)
@@ -248,9 +252,10 @@ def test_hybrid_q8_slice_8_layers():
     s, orc, _, _ = make_pair(sh, synth.Q8_0, 0, 8, workload=synth.WL_SLICE, prefill=512, max_seq=1024,
                              max_verify=4, io_fp32=False, threads=16)
     H = inputs(sh, 5, workload=synth.WL_SLICE, io_fp32=False, step0=100)
-    out = s.decode(_t(H[0])).cpu().numpy()
-    assert rel_err(out, orc.decode(H[0])) <= TOL
-    out = s.verify(_t(H[1:5])).cpu().numpy()
-    ref = orc.verify(H[1:5])
+    s.decode(_t(H[0]))
+    assert rel_err(s.get_hidden().cpu().numpy()[0], orc.decode(H[0], raw=True)) <= TOL
+    s.verify(_t(H[1:5]))
+    out = s.get_hidden(4).cpu().numpy()
+    ref = orc.verify(H[1:5], raw=True)
     for t in range(4):
         assert rel_err(out[t], ref[t]) <= TOL, t
