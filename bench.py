@@ -99,6 +99,21 @@ def profile_ops(s, H, n):
     return {k: (float(np.mean(v)), len(v) // n) for k, v in per.items()}, float(np.mean(step_ms))
 
 
+def time_gemv_op(s, op, reps):
+    """Mean duration of one GEMV op kind: HIP events on the launch stream around
+    reps x (one launch per layer), back to back, on the last step's activations."""
+    import torch
+    s.run_gemv_op(op)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        s.run_gemv_op(op)
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / reps
+
+
 def run_verify(s, H, rounds, k, seed):
     import torch
     import synth
@@ -136,17 +151,25 @@ def gemv_sweep(seed, reps):
             for batch in (1, 16):
                 x = torch.from_numpy(synth.gemv_x(seed, batch, cols, tag=7)).cuda()
                 y = torch.empty((batch, rows), dtype=torch.float32, device="cuda")
-                ws = torch.empty(slq.gemv_workspace_bytes(qtype, rows, cols, batch), dtype=torch.uint8, device="cuda")
+                ws = torch.zeros(slq.gemv_workspace_bytes(qtype, rows, cols, batch), dtype=torch.uint8, device="cuda")
                 for i in range(min(copies, 4)):
                     slq.gemv(qtype, packs[i % copies], rows, cols, x, out=y, ws=ws)
                 torch.cuda.synchronize()
+                # n calls (activation quantiser + GEMV each) replayed from one graph,
+                # so host-side launch cost does not enter the figure
                 n = max(reps, copies)
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g):
+                    for i in range(n):
+                        slq.gemv(qtype, packs[i % copies], rows, cols, x, out=y, ws=ws)
+                g.replay()
+                torch.cuda.synchronize()
                 ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
                 ev0.record()
-                for i in range(n):
-                    slq.gemv(qtype, packs[i % copies], rows, cols, x, out=y, ws=ws)
+                g.replay()
                 ev1.record()
                 torch.cuda.synchronize()
+                del g
                 us = ev0.elapsed_time(ev1) / n * 1e3
                 gbs = gemv_bytes(rows, cols, qtype, batch) / (us * 1e-6) / 1e9
                 res.append({"qtype": "Q4_0" if qtype == 2 else "Q8_0", "rows": rows, "cols": cols, "batch": batch,
@@ -192,6 +215,7 @@ def main() -> int:
     ap.add_argument("--steps", type=int, default=256)
     ap.add_argument("--warmup", type=int, default=8)
     ap.add_argument("--profile-steps", type=int, default=4)
+    ap.add_argument("--gemv-reps", type=int, default=8, help="repetitions of the 64-layer GEMV timing runs")
     ap.add_argument("--verify-rounds", type=int, default=32)
     ap.add_argument("--cpu-tokens", type=int, default=2)
     ap.add_argument("--sweep-reps", type=int, default=50)
@@ -199,6 +223,8 @@ def main() -> int:
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--copy-calib", action="store_true",
+                    help="also run 3 plain copies of a 512 MiB buffer (a known-size reference for PMC byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the slice runs on a single MI355X and this build has no "
@@ -211,11 +237,19 @@ def main() -> int:
     torch.cuda.set_device(0)
     threads = min(16, os.cpu_count() or 8)
     shape = synth.HYBRID_5120
-    n_in = args.warmup + args.steps + args.profile_steps + 4 * (args.verify_rounds + 1) + 8
+    n_in = args.warmup + args.steps + args.profile_steps + 4 * (args.verify_rounds + 1) + 16
     max_seq = ((PREFILL + n_in + 63) // 64) * 64
     log(f"inputs: {n_in} fresh fp16 hidden states; max_seq {max_seq}")
     H_host = synth.hidden_inputs(args.seed, synth.WL_SLICE, n_in, shape.hidden)
     H = torch.from_numpy(H_host).cuda()
+
+    if args.copy_calib:
+        a = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        for _ in range(3):
+            b = a.clone()
+        torch.cuda.synchronize()
+        del a, b
+        log("copy calibration: 3 x 512 MiB device-to-device copies")
 
     # ---- Q4_0 slice: timed decode
     s, tensors = build_slice(shape, synth.Q4_0, max_seq, 4, args.seed, threads)
@@ -223,18 +257,31 @@ def main() -> int:
     tok_s = args.steps / sec
     log(f"Q4_0 decode: {args.steps} steps in {sec * 1e3:.1f} ms (wall {wall * 1e3:.1f} ms): {tok_s:.1f} tok/s")
 
-    # ---- per-op times (eager, HIP events) -> roofline of the dominant kernel
+    # ---- per-op breakdown (eager, event per op) and the dominant kernel timed
+    # back to back with HIP events -> roofline
     base = args.warmup + args.steps
     ops, step_ms = profile_ops(s, H[base:], args.profile_steps)
     for k, (ms, n) in sorted(ops.items(), key=lambda kv: -kv[1][0] * kv[1][1]):
-        log(f"op {k:10s}: {ms * 1e3:8.2f} us x {n}/step")
+        log(f"op {k:10s}: {ms * 1e3:8.2f} us x {n}/step (eager, incl. dispatch)")
     f1_rows, f1_cols = 2 * shape.ffn, shape.hidden
-    f1_ms = ops["ffn_in"][0]
+    gemv_ms = {op: time_gemv_op(s, op, args.gemv_reps) / n_op
+               for op, n_op in (("ffn_in", 64), ("ffn_out", 64), ("dn_in", 48), ("dn_out", 48), ("att_in", 16),
+                                ("att_out", 16))}
+    f1_ms = gemv_ms["ffn_in"]
+    f1_launches = 64 * args.gemv_reps
     f1_bytes = gemv_bytes(f1_rows, f1_cols, synth.Q4_0)
     achieved = f1_bytes / (f1_ms * 1e-3) / 1e9
     weight_bytes = s.weights.numel()
     slice_bytes_tok = weight_bytes + 48 * 2 * 32 * 128 * 128 * 4 + 16 * (PREFILL + args.steps // 2) * 4096
-    log(f"F1 GEMV {f1_rows}x{f1_cols}: {f1_ms * 1e3:.2f} us -> {achieved:.0f} GB/s; eager step {step_ms:.3f} ms")
+    log(f"F1 GEMV {f1_rows}x{f1_cols}: {f1_ms * 1e3:.2f} us -> {achieved:.0f} GB/s; eager op sum per step {step_ms:.3f} ms")
+    gemv_shapes = {"ffn_in": (2 * shape.ffn, shape.hidden), "ffn_out": (shape.hidden, shape.ffn),
+                   "dn_in": (3 * 4096 + 64 + 4096, shape.hidden), "dn_out": (shape.hidden, 4096),
+                   "att_in": (2 * 6144 + 2 * 1024, shape.hidden), "att_out": (shape.hidden, 6144)}
+    gemv_in_slice = {op: {"us": round(ms * 1e3, 2), "rows": r, "cols": c,
+                          "GB_s": round(gemv_bytes(r, c, synth.Q4_0) / (ms * 1e-3) / 1e9, 1)}
+                     for op, ms in gemv_ms.items() for r, c in [gemv_shapes[op]]}
+    for op, v in gemv_in_slice.items():
+        log(f"gemv {op:8s} {v}")
 
     # ---- verify with rollback
     base += args.profile_steps
@@ -263,9 +310,10 @@ def main() -> int:
         s8, t8 = build_slice(shape, synth.Q8_0, max_seq, 4, args.seed, threads)
         del t8
         sec8, _, _ = time_decode(s8, H, args.steps, args.warmup)
-        ops8, _ = profile_ops(s8, H[args.warmup + args.steps:], 2)
+        f1_8 = time_gemv_op(s8, "ffn_in", args.gemv_reps) / 64
         extra["q8_0_slice"] = {"tok_s": round(args.steps / sec8, 2), "weights_GB": round(s8.weights.numel() / 1e9, 2),
-                               "ffn_in_us": round(ops8["ffn_in"][0] * 1e3, 2)}
+                               "ffn_in_us": round(f1_8 * 1e3, 2),
+                               "ffn_in_GB_s": round(gemv_bytes(f1_rows, f1_cols, synth.Q8_0) / (f1_8 * 1e-3) / 1e9, 1)}
         log(f"Q8_0 decode: {extra['q8_0_slice']}")
         del s8
         torch.cuda.empty_cache()
@@ -281,12 +329,14 @@ def main() -> int:
                    "global_batch": 1, "seq_len": PREFILL, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": f"k_gemv Q4_0 SwiGLU epilogue ({f1_rows}x{f1_cols}), mean of "
-                               f"{args.profile_steps * 64} launches"},
+                     "kernel": f"k_gemv<2,1,2>: fused RMSNorm + gate/up ({f1_rows}x{f1_cols} Q4_0) + SwiGLU, "
+                               f"mean of {f1_launches} back-to-back launches over the 64 layers' weights, HIP events",
+                     "bytes_per_launch": f1_bytes},
         "cpu_baseline": cpu,
         "slice_GB_per_token": round(slice_bytes_tok / 1e9, 3),
         "slice_effective_GB_s": round(slice_bytes_tok * tok_s / 1e9, 1),
-        "ops_us_per_step": {k: round(v[0] * v[1] * 1e3, 1) for k, v in ops.items()},
+        "gemv_in_slice": gemv_in_slice,
+        "eager_ops_us_per_step": {k: round(v[0] * v[1] * 1e3, 1) for k, v in ops.items()},
         "eager_step_ms": round(step_ms, 4),
         "verify": ver,
     }

@@ -82,8 +82,11 @@ size_t slq_gemv_workspace_bytes(int qtype, int64_t rows, int64_t cols, int batch
 
 /* Y = W X for batch right-hand sides (1 <= batch <= 16): x_dev fp32
  * [batch][cols], y_dev fp32 [batch][rows], ws_dev at least
- * slq_gemv_workspace_bytes() bytes.  batch 1 runs the streaming GEMV; larger
- * batches read each weight once for all right-hand sides.  Sums are fp32.   */
+ * slq_gemv_workspace_bytes() bytes and zero-filled before its first use (the
+ * calls leave the counters in it at zero again, so a workspace can be reused
+ * without clearing; calls that share one workspace must not overlap).  Each
+ * weight is read once for all right-hand sides.  Two kernel launches, no
+ * memory set, so the call can be captured in a HIP graph.                   */
 int slq_gemv(int qtype, const void *packed_dev, int64_t rows, int64_t cols, int batch,
              const float *x_dev, float *y_dev, void *ws_dev, size_t ws_bytes, void *stream);
 
@@ -182,6 +185,15 @@ enum {
  * returns how many were written (>= 0) or a negative slice_status. */
 int slice_decode_profiled(slice_t *s, const void *hid_in_dev, void *hid_out_dev,
                           int *op_kind, float *op_ms, int max_ops, void *stream);
+
+/* Launch, back to back on `stream`, the GEMV of one op kind (SLICE_OP_DN_IN,
+ * _DN_OUT, _ATT_IN, _ATT_OUT, _FFN_IN or _FFN_OUT) for every layer of the
+ * slice that has it, on the activations the last decode left in the
+ * workspace; nothing else runs.  For timing one kernel in isolation.  The
+ * residual-update kinds (_OUT) modify the workspace copy of h, which the next
+ * decode overwrites; DeltaNet states, KV caches and the position are not
+ * touched. */
+int slice_run_gemv_op(slice_t *s, int op_kind, void *stream);
 
 /* Batched verify of k inputs at positions p .. p+k-1: hid_in_dev [k][H] ->
  * hid_out_dev [k][H].  Output t equals what slice_decode would give after the

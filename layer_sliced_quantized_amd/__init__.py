@@ -67,7 +67,7 @@ def gemv(qtype: int, packed: torch.Tensor, rows: int, cols: int, x: torch.Tensor
         out = torch.empty((b, rows), dtype=torch.float32, device=x.device)
     need = gemv_workspace_bytes(qtype, rows, cols, b)
     if ws is None or ws.numel() < need:
-        ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        ws = torch.zeros(max(need, 1), dtype=torch.uint8, device=x.device)
     check(lib().slq_gemv(qtype, _ptr(packed), rows, cols, b, _ptr(x2), _ptr(out), _ptr(ws), ws.numel(),
                          _stream(stream)))
     return out
@@ -199,6 +199,10 @@ class Slice:
         if n < 0:
             check(n)
         return h_out, [(self.OP_NAMES[kinds[i]], float(ms[i])) for i in range(n)]
+
+    def run_gemv_op(self, op_name: str, stream=None):
+        """Launch one GEMV op kind for every layer, back to back (timing aid)."""
+        check(lib().slice_run_gemv_op(self.handle, self.OP_NAMES.index(op_name), _stream(stream)))
 
     def verify(self, h_in: torch.Tensor, h_out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
         k = h_in.shape[0]

@@ -72,6 +72,7 @@ _SIGS = {
     "slice_reset": (_I, [_V, _I, _V]),
     "slice_decode": (_I, [_V, _V, _V, _V]),
     "slice_decode_profiled": (_I, [_V, _V, _V, ctypes.POINTER(_I), ctypes.POINTER(ctypes.c_float), _I, _V]),
+    "slice_run_gemv_op": (_I, [_V, _I, _V]),
     "slice_verify": (_I, [_V, _I, _V, _V, _V]),
     "slice_commit": (_I, [_V, _I, _V]),
     "slice_embed": (_I, [_V, _V, _V, _V]),

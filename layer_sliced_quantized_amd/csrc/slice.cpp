@@ -253,6 +253,25 @@ Layout make_layout(const slice_config& c) {
 
 }  // namespace
 
+// Optional per-op timing: an event is recorded at every op boundary.
+struct Prof {
+  std::vector<hipEvent_t> ev;
+  std::vector<int> kind;   // kind of the op that ends at ev[i+1]
+  int mark(int k, hipStream_t st) {
+    hipEvent_t e;
+    HIPCHK(hipEventCreate(&e));
+    ev.push_back(e);
+    if (ev.size() > 1) kind.push_back(k);
+    HIPCHK(hipEventRecord(e, st));
+    return SLICE_OK;
+  }
+  void destroy() {
+    for (hipEvent_t e : ev) hipEventDestroy(e);
+    ev.clear();
+    kind.clear();
+  }
+};
+
 struct slice {
   slice_config cfg;
   Layout L;
@@ -275,23 +294,11 @@ struct slice {
   }
 };
 
-// Optional per-op timing: an event is recorded at every op boundary.
-struct Prof {
-  std::vector<hipEvent_t> ev;
-  std::vector<int> kind;   // kind of the op that ends at ev[i+1]
-  int mark(int k, hipStream_t st) {
-    hipEvent_t e;
-    HIPCHK(hipEventCreate(&e));
-    HIPCHK(hipEventRecord(e, st));
-    ev.push_back(e);
-    if (ev.size() > 1) kind.push_back(k);
-    return SLICE_OK;
-  }
-};
-
 // One step with T tokens: entry, every layer, exit.  Reads the input/output
 // pointers from the control block so a captured graph serves any buffers.
-static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof = nullptr) {
+// only >= 0: enqueue just the GEMV op of that kind for every layer (no entry,
+// mixers or exit), reading the activations the last step left in the workspace.
+static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof = nullptr, int only = -1) {
 #define SLQ_MARK(k) do { if (prof) { int r_ = prof->mark(k, st); if (r_) return r_; } } while (0)
   const slice_config& c = s->cfg;
   const Layout& L = s->L;
@@ -310,14 +317,17 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
   };
   // entry: boundary vector -> h, digits of attn_norm(first layer) * h
   SLQ_MARK(-1);
-  HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, nullptr, ctrl, H, T, H, h, attn_norm_of(0), qt, s->act_a(), ssq, st));
+  if (only < 0) HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, nullptr, ctrl, H, T, H, h, attn_norm_of(0), qt, s->act_a(), ssq, st));
   SLQ_MARK(SLICE_OP_ENTRY);
   float* part = s->wsp<float>(L.part);
   unsigned* cnt = s->wsp<unsigned>(L.cnt);
   for (int i = 0; i < nlay; ++i) {
     const LayerLayout& ll = L.layers[i];
+    const int k_in = ll.attn ? SLICE_OP_ATT_IN : SLICE_OP_DN_IN;
+    const int k_mix = ll.attn ? SLICE_OP_ATTENTION : SLICE_OP_DELTANET;
+    const int k_out = ll.attn ? SLICE_OP_ATT_OUT : SLICE_OP_DN_OUT;
     // mixer input projections: G1 = [q|k|v|a|b|z] or [q|g|k|v] of RMSNorm(h)
-    {
+    if (only < 0 || only == k_in) {
       const Packed W = s->packed(ll.g1);
       GemvOut o{};
       o.kind = EPI_STORE;
@@ -329,7 +339,8 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       HIPCHK(launch_gemv(W, T, s->act_a(), s->norm_h(), o, pl.ks, pl.w, st));
       SLQ_MARK(ll.attn ? SLICE_OP_ATT_IN : SLICE_OP_DN_IN);
     }
-    if (ll.attn) {
+    if (only >= 0 && only != k_mix) {
+    } else if (ll.attn) {
       AttnParams p{};
       p.y = y1;
       p.y_stride = ll.g1.rows;
@@ -389,10 +400,10 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       HIPCHK(launch_gemv(W, T, in, NormIn{nullptr, 0, 0.f, 0.f}, o, pl.ks, pl.w, st));
       return SLICE_OK;
     };
-    int rc = residual(ll.g2, s->act_u(), nw_after_mixer, "G2");
+    int rc = (only < 0 || only == k_out) ? residual(ll.g2, s->act_u(), nw_after_mixer, "G2") : SLICE_OK;
     if (rc) return rc;
-    SLQ_MARK(ll.attn ? SLICE_OP_ATT_OUT : SLICE_OP_DN_OUT);
-    if (c.ffn) {
+    SLQ_MARK(k_out);
+    if (c.ffn && (only < 0 || only == SLICE_OP_FFN_IN)) {
       const Packed W = s->packed(ll.f1);
       GemvOut o{};
       o.kind = EPI_SWIGLU;
@@ -405,12 +416,14 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       const Plan pl = plan_gemv("F1", W.rows, W.cols);
       HIPCHK(launch_gemv(W, T, s->act_a(), s->norm_h(), o, pl.ks, pl.w, st));
       SLQ_MARK(SLICE_OP_FFN_IN);
+    }
+    if (c.ffn && (only < 0 || only == SLICE_OP_FFN_OUT)) {
       rc = residual(ll.f2, s->act_m(), attn_norm_of(i + 1), "F2");
       if (rc) return rc;
       SLQ_MARK(SLICE_OP_FFN_OUT);
     }
   }
-  HIPCHK(launch_store_out(h, T, H, nullptr, c.io_fp32, ctrl, decode ? 1 : 0, st));
+  if (only < 0) HIPCHK(launch_store_out(h, T, H, nullptr, c.io_fp32, ctrl, decode ? 1 : 0, st));
   SLQ_MARK(SLICE_OP_EXIT);
   return SLICE_OK;
 #undef SLQ_MARK
@@ -495,7 +508,6 @@ int slq_gemv(int qtype, const void* packed_dev, int64_t rows, int64_t cols, int 
   unsigned* cnt = reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(part) + al256((size_t)nrg * 16 * batch * RG * 4));
   HIPCHK(launch_quant_act(qtype, x_dev, batch, (int)cols, cols, a, S(stream)));
   const Plan pl = plan_gemv("GEMV", rows, cols);
-  if (pl.ks > 1) HIPCHK(hipMemsetAsync(cnt, 0, (size_t)nrg * 4, S(stream)));
   const Packed W{static_cast<const uint8_t*>(packed_dev), rows, cols, qtype};
   GemvOut o{};
   o.kind = EPI_STORE;
@@ -653,6 +665,15 @@ int slice_decode_profiled(slice_t* s, const void* in, void* out, int* op_kind, f
   if (rc) return rc;
   s->pos += 1;
   return n;
+}
+
+int slice_run_gemv_op(slice_t* s, int op_kind, void* stream) {
+  if (!s) return fail(SLICE_EINVAL, "null slice");
+  if (op_kind != SLICE_OP_DN_IN && op_kind != SLICE_OP_DN_OUT && op_kind != SLICE_OP_ATT_IN &&
+      op_kind != SLICE_OP_ATT_OUT && op_kind != SLICE_OP_FFN_IN && op_kind != SLICE_OP_FFN_OUT)
+    return fail(SLICE_EINVAL, "slice_run_gemv_op: not a GEMV op kind");
+  if (s->pending) return fail(SLICE_ESTATE, "slice_run_gemv_op: a verify is waiting for slice_commit");
+  return enqueue_step(s, 1, true, S(stream), nullptr, op_kind);
 }
 
 int slice_verify(slice_t* s, int k, const void* in, void* out, void* stream) {
