@@ -18,6 +18,7 @@ from __future__ import annotations
 import argparse
 import json
 import os
+import re
 import sys
 import time
 
@@ -29,6 +30,35 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 METRIC = "decode tok/s, 64-layer Q4_0 hybrid slice (b=1); GEMV HBM GB/s vs peak"
 PREFILL = 512
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_hybrid64_q4_decode.md")
+F1_SOURCES = ("slq.h", "dev.h", "gemv_kernel.h", "gemv_q4_swiglu.hip")
+
+
+def f1_source_hash() -> str:
+    """sha256 over the sources that define the fused gate/up GEMV kernel."""
+    import hashlib
+    h = hashlib.sha256()
+    for name in F1_SOURCES:
+        with open(os.path.join(ROOT, "layer_sliced_quantized_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def profiled_traffic():
+    """HBM bytes per launch of the gate/up GEMV from the committed PMC summary
+    (FETCH_SIZE and WRITE_SIZE scaled by a known-size copy), or None when the
+    kernel sources changed after the counters were taken."""
+    try:
+        text = open(TRAFFIC_PROFILE).read()
+    except OSError:
+        return None
+    m_b = re.search(r"traffic_bytes_per_launch: (\d+)", text)
+    m_h = re.search(r"kernel_sources_sha256: ([0-9a-f]{64})", text)
+    if not m_b or not m_h or m_h.group(1) != f1_source_hash():
+        return None
+    return int(m_b.group(1))
 
 
 def log(msg: str) -> None:
@@ -328,7 +358,7 @@ def main() -> int:
                                f"Q4_0 {weight_bytes / 1e9:.2f} GB, batch 1 decode from position {PREFILL}",
                    "global_batch": 1, "seq_len": PREFILL, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(),
                      "kernel": f"k_gemv<2,1,2>: fused RMSNorm + gate/up ({f1_rows}x{f1_cols} Q4_0) + SwiGLU, "
                                f"mean of {f1_launches} back-to-back launches over the 64 layers' weights, HIP events",
                      "bytes_per_launch": f1_bytes},
