@@ -3,16 +3,16 @@
  * transformer layers with Q4_0 / Q8_0 block-quantised weights, on AMD
  * Instinct MI355X (gfx950).
  *
- * What is computed.  A stage "runs its own range of layers and keeps its own
- * attention cache", receiving one token's hidden state and handing one on
- * ("Unstable Legion: the peer-to-peer ChatGPT", section "Splitting the
- * workload"; "activation in, activation out", section "The runtime:
- * legion-stage-runtime").  The hidden state on the wire is 5,120 x f16 for the
+ * What is computed.  A pipeline stage owns a contiguous range of layers and
+ * its own attention cache; per token it takes one hidden state in and hands
+ * one hidden state on ("Unstable Legion: the peer-to-peer ChatGPT", sections
+ * "Splitting the workload" and "The runtime: legion-stage-runtime").  The
+ * hidden state on the wire is 5,120 x f16 for the
  * hybrid model (SwarmLLM README, bench paragraph).  Layers are either
  * Llama-style attention blocks or the qwen3_5 hybrid's Gated DeltaNet and
  * gated full-attention blocks (ChatTorrent README, "What it can run").  Weights
- * are 4-bit blocks with f16 scales, read once per token (SwarmLLM README,
- * architecture paragraph).  Drafts are verified in one batched pass with exact
+ * are block-quantised (Q4_0: 4-bit codes, one fp16 scale per 32) and each
+ * weight is read once per token (SwarmLLM README, architecture paragraph).  Drafts are verified in one batched pass with exact
  * rollback of the recurrent state (same paragraph and feature list).
  *
  * Conventions for every entry point:

@@ -1,9 +1,10 @@
 // Gated DeltaNet recurrent update for decode and verify.
 //
-// The hybrid's linear-attention layers (ChatTorrent README, "What it can run":
-// "Gated DeltaNet linear-attention layers") carry a per-head state S (d_v x
-// d_k, fp32) updated once per token, serially ("the DeltaNet recurrence is
-// serial", SwarmLLM README, bench paragraph):
+// The hybrid model's linear-attention layers are Gated DeltaNet (ChatTorrent
+// README, "What it can run").  Each head carries a state S (d_v x d_k, fp32)
+// that is updated once per token, one token after the other (the pages note
+// that this recurrence cannot be parallelised over tokens; SwarmLLM README,
+// bench paragraph):
 //     S' = alpha S (I - beta k k^T) + beta v k^T,   o = S' q
 // with q, k divided by sqrt(sum of squares + 1e-6).  Row i of S only needs the
 // whole k and q plus v_i, so rows are independent:

@@ -1,9 +1,9 @@
 // Q4_0 / Q8_0 matrix-vector products for gfx950.
 //
-// The pages' decode kernel streams every weight once per token: "64 threads
-// sweep each row together, dequantize in registers, reduce in shared memory"
-// (SwarmLLM README, architecture paragraph), over "4-bit blocks with f16
-// scales".  On CDNA4 this kernel keeps the 64-lane sweep but turns it 90
+// In the pages' decode kernel (SwarmLLM README, architecture paragraph) every
+// weight is read once per token: a 64-thread group walks one row of Q4_0
+// blocks, dequantises in registers and reduces through shared memory.  On
+// CDNA4 this kernel keeps the 64-lane sweep but turns it 90
 // degrees: each lane owns one output row of a 64-row group and streams whole
 // blocks of that row with one 128-bit load per block (the load-time repack puts
 // 64 rows' 16-byte code chunks side by side, so a wave's load is 1 KiB

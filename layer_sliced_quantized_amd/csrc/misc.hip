@@ -4,7 +4,7 @@
 // SwarmLLM README, bench paragraph); the first stage owns the embedding and
 // the last one the head and the sampling ("Unstable Legion", section
 // "Splitting the workload").  Sampling here is greedy, as in the pages'
-// benchmark rows ("Qwen 3.8 27B Q4_0, greedy").
+// benchmark table (SwarmLLM README).
 #include "dev.h"
 
 namespace slq {

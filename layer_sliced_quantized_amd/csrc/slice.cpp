@@ -1,10 +1,11 @@
 // Host side of libslq: the C ABI declared in include/slice.h.
 //
-// A slice is the layer range [begin, end) of a decoder ("Unstable Legion",
-// section "Splitting the workload": contiguous layer stages, each with its own
-// cache; "activation in, activation out", section "The runtime").  One decode
-// step is one HIP graph launch, the MI355X analogue of the pages' "one command
-// submit per token" (SwarmLLM README, architecture paragraph).  The verify
+// A slice is the layer range [begin, end) of a decoder: one pipeline stage
+// owns a contiguous run of layers and its own cache, and maps one hidden state
+// to the next ("Unstable Legion", sections "Splitting the workload" and "The
+// runtime").  One decode step is one HIP graph launch, where the pages' WebGPU
+// engine submits one command buffer per token (SwarmLLM README, architecture
+// paragraph).  The verify
 // pass for k drafts uses the same kernels with k right-hand sides and writes
 // each token's DeltaNet state to its own slot, so commit(j) is a slot switch.
 #include <hip/hip_runtime.h>

@@ -4,8 +4,8 @@
  * baseline leg of the benchmark do.
  *
  * What it computes (plain definitions, fp64):
- *   - decode of GGUF Q4_0 / Q8_0 blocks (the "4-bit blocks with f16 scales"
- *     of the SwarmLLM README, "How it works"; ChatTorrent's q8 weights,
+ *   - decode of GGUF Q4_0 / Q8_0 blocks (Q4_0 weights: SwarmLLM README, model
+ *     table and architecture paragraph; 8-bit weights: ChatTorrent README,
  *     "What it can run"):
  *       Q4_0: 18 bytes = fp16 d, 16 code bytes; byte j holds weight j in the
  *             low nibble and weight j+16 in the high nibble; w = (q - 8) * d
