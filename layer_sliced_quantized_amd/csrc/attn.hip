@@ -247,8 +247,7 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnParams p) {
   const int nu = p.q_heads * p.hd;
   if (p.u_out) p.u_out[(size_t)t * nu + h * p.hd + d] = o;
   const int blk = (h * p.hd + d) / QK;
-  quant_block_half_qt(p.next_qt, o, p.next.xd + ((size_t)t * p.next.nblk + blk) * XW,
-                      p.next.xs + (size_t)t * p.next.nblk + blk, true);
+  put_digits(p.next, p.next_qt, t, blk, o, true);
 }
 
 hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {

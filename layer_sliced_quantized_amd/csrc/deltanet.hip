@@ -78,8 +78,7 @@ __global__ __launch_bounds__(64) void k_deltanet(DnParams p, int T) {
     const int nv = p.heads * p.dv;
     if (p.u_out && half == 0) p.u_out[(size_t)t * nv + h * p.dv + i] = uo;
     const int blk = (h * p.dv + ib * 32) / QK;
-    quant_block_half_qt(p.next_qt, uo, p.next.xd + ((size_t)t * p.next.nblk + blk) * XW,
-                        p.next.xs + (size_t)t * p.next.nblk + blk, half == 0);
+    put_digits(p.next, p.next_qt, t, blk, uo, half == 0);
     __syncthreads();
   }
 }

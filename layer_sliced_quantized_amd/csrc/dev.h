@@ -40,28 +40,35 @@ __device__ __forceinline__ float rnorm_from(const NormIn& n, int t) {
   return 1.0f / sqrtf(a * n.inv_n + n.eps);
 }
 
-// Quantise one block of 32 activations held one per lane by a 32-lane half of
-// the wave (element e = lane & 31) into digits, in the order the weight codes
-// of format QT are packed.  Every lane of the wave must call this (shuffles);
-// `write` selects which halves store.
-//
+// Integer form of one block of 32 activations held one per lane by a 32-lane
+// half of the wave (element e = lane & 31):
 //   s = max|x| / M,  x_int = rint(x / s)  (|x_int| <= M),  u = x_int + OFF
-//   Q4_0: digit d = ((u >> 4d) & 15) - 8, nibble 2k of dword (d, m) <- element 4m+k,
-//         nibble 2k+1 <- element 4m+k+16  (byte j of a Q4_0 block holds weights j, j+16)
-//   Q8_0: digit d = ((u >> 8d) & 255) - 128, byte k of dword (d, m) <- element 4m+k
+// with OFF = 0x888888 (Q4_0) or 0x808080 (Q8_0), so that the balanced digits
+// are ((u >> 4d) & 15) - 8 (six base-16 digits) or ((u >> 8d) & 255) - 128
+// (three base-256 digits).  Every lane of the wave must call this (shuffles).
 template <int QT>
-__device__ __forceinline__ void quant_block_half(float v, int32_t* xd, float* xs, bool write) {
-  const int lane = threadIdx.x & 63;
-  const int e = lane & 31;
-  const int base = lane & 32;
+__device__ __forceinline__ uint32_t quant_int(float v, float& amax) {
   const float M = QT == QT_Q4 ? M_Q4 : M_Q8;
-  const float amax = half_max(fabsf(v));
+  amax = half_max(fabsf(v));
   const float inv = amax > 0.0f ? M / amax : 0.0f;
   // v * (M / amax) can round one unit past M for the largest entry; clamp so
   // the digits stay in range (the clamped unit is below fp32 resolution of x)
   const int Mi = QT == QT_Q4 ? 7829367 : 8355711;
   const int xi = min(max((int)rintf(v * inv), -Mi), Mi);
-  const uint32_t u = (uint32_t)(xi + (QT == QT_Q4 ? 0x888888 : 0x808080));
+  return (uint32_t)(xi + (QT == QT_Q4 ? 0x888888 : 0x808080));
+}
+
+// Layout fmt 0, in the order the weight codes of format QT are packed:
+//   Q4_0: nibble 2k of dword (d, m) <- digit d of element 4m+k, nibble 2k+1 <- of
+//         element 4m+k+16  (byte j of a Q4_0 block holds weights j, j+16)
+//   Q8_0: byte k of dword (d, m) <- digit d of element 4m+k
+template <int QT>
+__device__ __forceinline__ void quant_block_half(float v, int32_t* xd, float* xs, bool write) {
+  const int lane = threadIdx.x & 63;
+  const int e = lane & 31;
+  const int base = lane & 32;
+  float amax;
+  const uint32_t u = quant_int<QT>(v, amax);
   uint32_t word = 0;
   if (QT == QT_Q4) {
     const int d = (e >> 2) % 6, m = e & 3;
@@ -83,13 +90,64 @@ __device__ __forceinline__ void quant_block_half(float v, int32_t* xd, float* xs
   }
   if (write) {
     if (e < XW) xd[e] = (int32_t)word;
-    if (e == 0) *xs = amax / M;
+    if (e == 0) *xs = amax / (QT == QT_Q4 ? M_Q4 : M_Q8);
   }
 }
 
-__device__ __forceinline__ void quant_block_half_qt(int qt, float v, int32_t* xd, float* xs, bool write) {
-  if (qt == QT_Q4) quant_block_half<QT_Q4>(v, xd, xs, write);
-  else quant_block_half<QT_Q8>(v, xd, xs, write);
+// Layout fmt 1 (MFMA operand order, see Act): the same x_int and scale as fmt 0.
+template <int QT>
+__device__ __forceinline__ void quant_block_mx(float v, const Act& a, int t, int blk, bool write) {
+  const int lane = threadIdx.x & 63;
+  const int e = lane & 31;
+  const int base = lane & 32;
+  float amax;
+  const uint32_t u = quant_int<QT>(v, amax);
+  if (QT == QT_Q4) {
+    // 48 dwords: chunk c = w >> 2 (p = c >> 2, g = c & 3), dword q = w & 3;
+    // lane e makes dword e and, for e < 16, dword e + 32
+#pragma unroll
+    for (int r = 0; r < 2; ++r) {
+      const int w = e + 32 * r;
+      const int c = (w >> 2) % 12, q = w & 3, p = c >> 2, g = c & 3;
+      const int d = 2 * p + (g >> 1);
+      uint32_t word = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t uk = (uint32_t)__shfl((int)u, base + 16 * (g & 1) + 4 * q + k, 64);
+        int dig = (int)((uk >> (4 * d)) & 15u) - 8;
+        if (g >= 2) dig *= 16;
+        word |= ((uint32_t)dig & 255u) << (8 * k);
+      }
+      if (write && w < 48)
+        a.xd[(((size_t)blk * 12 + c) * MX_SLOTS + t) * 4 + q] = (int32_t)word;
+    }
+  } else {
+    // 24 dwords: w = e < 24, chunk (p, g) = (w >> 3, (w >> 1) & 3), dword q = w & 1
+    const int w = e % 24;
+    const int p = w >> 3, g = (w >> 1) & 3, q = w & 1;
+    uint32_t word = 0;
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t uk = (uint32_t)__shfl((int)u, base + 8 * g + 4 * q + k, 64);
+      word |= (((uk >> (8 * p)) & 255u) ^ 0x80u) << (8 * k);
+    }
+    if (write && e < 24) a.xd[(((size_t)blk * 12 + 4 * p + g) * MX_SLOTS + t) * 2 + q] = (int32_t)word;
+  }
+  if (write && e == 0) a.xs[(size_t)blk * MX_SLOTS + t] = amax / (QT == QT_Q4 ? M_Q4 : M_Q8);
+}
+
+// Digits of block blk of token t of `a`, in a's layout.  Every lane of the
+// wave must call this; `write` selects which 32-lane halves store.
+__device__ __forceinline__ void put_digits(const Act& a, int qt, int t, int blk, float v, bool write) {
+  if (a.fmt == 0) {
+    int32_t* xd = a.xd + ((size_t)t * a.nblk + blk) * XW;
+    float* xs = a.xs + (size_t)t * a.nblk + blk;
+    if (qt == QT_Q4) quant_block_half<QT_Q4>(v, xd, xs, write);
+    else quant_block_half<QT_Q8>(v, xd, xs, write);
+  } else {
+    if (qt == QT_Q4) quant_block_mx<QT_Q4>(v, a, t, blk, write);
+    else quant_block_mx<QT_Q8>(v, a, t, blk, write);
+  }
 }
 
 // Shared tail of every producer of a residual-stream vector: lane holds h_new
@@ -105,9 +163,7 @@ __device__ __forceinline__ void resid_tail(int t, int rg, int H, float hn, float
   if (lane == 0) ssq_out[(size_t)t * nrg + rg] = ss;
   const float w = row < H ? norm_w[row] : 0.0f;
   const int blk = 2 * rg + (lane >> 5);
-  const bool wr = blk < next.nblk;
-  quant_block_half_qt(qt, w * hn, next.xd + ((size_t)t * next.nblk + blk) * XW,
-                      next.xs + (size_t)t * next.nblk + blk, wr);
+  put_digits(next, qt, t, blk, w * hn, blk < next.nblk);
 }
 
 }  // namespace slq

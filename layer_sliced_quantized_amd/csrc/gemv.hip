@@ -120,8 +120,7 @@ __global__ void k_quant_act(int qt, const float* __restrict__ x, int n, int64_t 
   const int i = blk * QK + (lane & 31);
   const float v = (blk < a.nblk && i < n) ? x[(size_t)t * x_ts + i] : 0.0f;
   const int bsafe = blk < a.nblk ? blk : 0;
-  quant_block_half_qt(qt, v, a.xd + ((size_t)t * a.nblk + bsafe) * XW, a.xs + (size_t)t * a.nblk + bsafe,
-                      blk < a.nblk);
+  put_digits(a, qt, t, bsafe, v, blk < a.nblk);
 }
 
 hipError_t launch_quant_act(int qt, const float* x, int T, int n, int64_t x_ts, Act a, hipStream_t s) {
@@ -138,6 +137,7 @@ hipError_t launch_gemv(const Packed& W, int T, Act x, NormIn nin, GemvOut out, i
                        hipStream_t s) {
   if (waves < 1 || waves > 16 || ksplit < 1) return hipErrorInvalidValue;
   if (ksplit > 1 && (!out.part || !out.cnt)) return hipErrorInvalidValue;
+  if (x.fmt == 1) return launch_gemm(W, T, x, nin, out, ksplit, waves, s);
   const bool q4 = W.qt == QT_Q4;
   switch (out.kind) {
     case EPI_STORE: return q4 ? gemv_inst<QT_Q4, EPI_STORE>(W, T, x, nin, out, ksplit, waves, s)

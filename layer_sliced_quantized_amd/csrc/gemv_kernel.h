@@ -257,8 +257,7 @@ __global__ __launch_bounds__(1024) void k_gemv(Packed W, Act x, NormIn nin, Gemv
       const float up = __shfl(v, (lane + 32) & 63, 64);
       const float m = (v / (1.0f + expf(-v))) * up;
       if (out.y && lane < 32) out.y[(size_t)j * out.y_tstride + rg * 32 + lane] = m;
-      quant_block_half_qt(out.next_qt, m, out.next.xd + ((size_t)j * out.next.nblk + rg) * XW,
-                          out.next.xs + (size_t)j * out.next.nblk + rg, lane < 32);
+      put_digits(out.next, out.next_qt, j, rg, m, lane < 32);
     } else {  // EPI_RESID, whole K in this workgroup
       const float hn = rv ? out.y[(size_t)j * out.y_tstride + row] + acc[j] : 0.0f;
       resid_tail(j, rg, (int)W.rows, hn, out.y, out.y_tstride, out.norm_w, out.next_qt, out.next,

@@ -66,17 +66,19 @@ Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
   const int ntiles = (int)((cols / QK + TB - 1) / TB);
   const std::string k(kind);
   Plan p;
+  // at most 8 waves per workgroup: the batched MFMA kernel uses the same
+  // split (so its sums are added in the same order) and holds 8 waves at most
   if (k == "G2" && nrg <= 128) {
-    p.ks = 1;
-    p.w = clampi(ntiles, 1, 16);
+    p.w = clampi(ntiles, 1, 8);
+    p.ks = clampi((ntiles + 7) / 8, 1, 4);
   } else {
     p.ks = clampi((1024 + nrg - 1) / nrg, 1, ntiles < 16 ? ntiles : 16);
     if (k == "F1") p.ks = clampi(p.ks, 1, 2);
     if (k == "F2" || k == "G1") p.ks = clampi(p.ks, 1, k == "F2" ? 8 : 4);
-    p.w = clampi(k == "GEMV" || k == "HEAD" ? (ntiles / p.ks + 1) / 2 : 4, 1, 16);
+    p.w = clampi(k == "GEMV" || k == "HEAD" ? (ntiles / p.ks + 1) / 2 : 4, 1, 8);
   }
   p.ks = clampi(env_int(("SLQ_KS_" + k).c_str(), p.ks), 1, 16);
-  p.w = clampi(env_int(("SLQ_W_" + k).c_str(), p.w), 1, 16);
+  p.w = clampi(env_int(("SLQ_W_" + k).c_str(), p.w), 1, 8);
   return p;
 }
 
@@ -218,12 +220,16 @@ Layout make_layout(const slice_config& c) {
   };
   L.ctrl = take(sizeof(Ctrl));
   L.h = take((size_t)mt * H * 4);
-  L.xa_d = take((size_t)mt * nblkH * XW * 4);
-  L.xa_s = take((size_t)mt * nblkH * 4);
-  L.xu_d = take((size_t)mt * (nblkU ? nblkU : 1) * XW * 4);
-  L.xu_s = take((size_t)mt * (nblkU ? nblkU : 1) * 4);
-  L.xm_d = take((size_t)mt * (nblkM ? nblkM : 1) * XW * 4);
-  L.xm_s = take((size_t)mt * (nblkM ? nblkM : 1) * 4);
+  // activation digits, room for either layout (one row of digits per token, or
+  // the 16-slot MFMA operand layout)
+  auto digits = [&](int nblk) { return std::max<size_t>((size_t)mt * XW * 4, mx_block_bytes(c.qtype)) * (nblk ? nblk : 1); };
+  auto scales = [&](int nblk) { return (size_t)std::max(mt, MX_SLOTS) * (nblk ? nblk : 1) * 4; };
+  L.xa_d = take(digits(nblkH));
+  L.xa_s = take(scales(nblkH));
+  L.xu_d = take(digits(nblkU));
+  L.xu_s = take(scales(nblkU));
+  L.xm_d = take(digits(nblkM));
+  L.xm_s = take(scales(nblkM));
   L.ssq = take((size_t)mt * (H / RG) * 4);
   L.y1 = take((size_t)mt * (L.g1_rows_max ? L.g1_rows_max : 1) * 4);
   // split-K scratch: any GEMV of the slice with up to 16 splits
@@ -287,9 +293,11 @@ struct slice {
   Ctrl* ctrl() const { return reinterpret_cast<Ctrl*>(ws + L.ctrl); }
   template <class X> X* wsp(size_t off) const { return reinterpret_cast<X*>(ws + off); }
   Packed packed(const Mat& m) const { return Packed{w + m.off, m.rows, m.cols, cfg.qtype}; }
-  Act act_a() const { return Act{wsp<int32_t>(L.xa_d), wsp<float>(L.xa_s), cfg.hidden / QK}; }
-  Act act_u() const { return Act{wsp<int32_t>(L.xu_d), wsp<float>(L.xu_s), (L.nu + QK - 1) / QK}; }
-  Act act_m() const { return Act{wsp<int32_t>(L.xm_d), wsp<float>(L.xm_s), cfg.ffn / QK}; }
+  int mx_min_t = 2;   // steps with at least this many tokens use the MFMA products
+  int fmt_for(int T) const { return T >= mx_min_t ? 1 : 0; }
+  Act act_a(int fmt) const { return Act{wsp<int32_t>(L.xa_d), wsp<float>(L.xa_s), cfg.hidden / QK, fmt}; }
+  Act act_u(int fmt) const { return Act{wsp<int32_t>(L.xu_d), wsp<float>(L.xu_s), (L.nu + QK - 1) / QK, fmt}; }
+  Act act_m(int fmt) const { return Act{wsp<int32_t>(L.xm_d), wsp<float>(L.xm_s), cfg.ffn / QK, fmt}; }
   NormIn norm_h() const {
     return NormIn{wsp<float>(L.ssq), cfg.hidden / RG, 1.0f / (float)cfg.hidden, cfg.eps};
   }
@@ -305,6 +313,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
   const Layout& L = s->L;
   const int H = c.hidden;
   const int qt = c.qtype;
+  const int fmt = s->fmt_for(T);
   float* h = s->wsp<float>(L.h);
   float* ssq = s->wsp<float>(L.ssq);
   float* y1 = s->wsp<float>(L.y1);
@@ -318,7 +327,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
   };
   // entry: boundary vector -> h, digits of attn_norm(first layer) * h
   SLQ_MARK(-1);
-  if (only < 0) HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, nullptr, ctrl, H, T, H, h, attn_norm_of(0), qt, s->act_a(), ssq, st));
+  if (only < 0) HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, nullptr, ctrl, H, T, H, h, attn_norm_of(0), qt, s->act_a(fmt), ssq, st));
   SLQ_MARK(SLICE_OP_ENTRY);
   float* part = s->wsp<float>(L.part);
   unsigned* cnt = s->wsp<unsigned>(L.cnt);
@@ -337,7 +346,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       o.part = part;
       o.cnt = cnt;
       const Plan pl = plan_gemv("G1", W.rows, W.cols);
-      HIPCHK(launch_gemv(W, T, s->act_a(), s->norm_h(), o, pl.ks, pl.w, st));
+      HIPCHK(launch_gemv(W, T, s->act_a(fmt), s->norm_h(), o, pl.ks, pl.w, st));
       SLQ_MARK(ll.attn ? SLICE_OP_ATT_IN : SLICE_OP_DN_IN);
     }
     if (only >= 0 && only != k_mix) {
@@ -361,7 +370,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       p.part = s->wsp<float>(L.apart);
       p.nchunk = L.nchunk;
       p.u_out = nullptr;
-      p.next = s->act_u();
+      p.next = s->act_u(fmt);
       p.next_qt = qt;
       HIPCHK(launch_attention(p, T, st));
       SLQ_MARK(SLICE_OP_ATTENTION);
@@ -378,7 +387,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       p.verify = decode ? 0 : 1;
       p.ctrl = ctrl;
       p.u_out = nullptr;
-      p.next = s->act_u();
+      p.next = s->act_u(fmt);
       p.next_qt = qt;
       HIPCHK(launch_deltanet(p, T, st));
       SLQ_MARK(SLICE_OP_DELTANET);
@@ -391,7 +400,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       o.kind = EPI_RESID;
       o.y = h;
       o.y_tstride = H;
-      o.next = s->act_a();
+      o.next = s->act_a(fmt);
       o.next_qt = qt;
       o.ssq_out = ssq;
       o.norm_w = next_norm;
@@ -401,7 +410,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       HIPCHK(launch_gemv(W, T, in, NormIn{nullptr, 0, 0.f, 0.f}, o, pl.ks, pl.w, st));
       return SLICE_OK;
     };
-    int rc = (only < 0 || only == k_out) ? residual(ll.g2, s->act_u(), nw_after_mixer, "G2") : SLICE_OK;
+    int rc = (only < 0 || only == k_out) ? residual(ll.g2, s->act_u(fmt), nw_after_mixer, "G2") : SLICE_OK;
     if (rc) return rc;
     SLQ_MARK(k_out);
     if (c.ffn && (only < 0 || only == SLICE_OP_FFN_IN)) {
@@ -410,16 +419,16 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       o.kind = EPI_SWIGLU;
       o.y = nullptr;
       o.y_tstride = c.ffn;
-      o.next = s->act_m();
+      o.next = s->act_m(fmt);
       o.next_qt = qt;
       o.part = part;
       o.cnt = cnt;
       const Plan pl = plan_gemv("F1", W.rows, W.cols);
-      HIPCHK(launch_gemv(W, T, s->act_a(), s->norm_h(), o, pl.ks, pl.w, st));
+      HIPCHK(launch_gemv(W, T, s->act_a(fmt), s->norm_h(), o, pl.ks, pl.w, st));
       SLQ_MARK(SLICE_OP_FFN_IN);
     }
     if (c.ffn && (only < 0 || only == SLICE_OP_FFN_OUT)) {
-      rc = residual(ll.f2, s->act_m(), attn_norm_of(i + 1), "F2");
+      rc = residual(ll.f2, s->act_m(fmt), attn_norm_of(i + 1), "F2");
       if (rc) return rc;
       SLQ_MARK(SLICE_OP_FFN_OUT);
     }
@@ -487,11 +496,18 @@ int slq_dequant(int qtype, const void* packed_dev, int64_t rows, int64_t cols, f
   return SLICE_OK;
 }
 
+// Standalone GEMV workspace: activation digits (room for both layouts), their
+// scales, split-K partials, ticket counters.
+static size_t gemv_ws_digits(int qtype, int nblk, int batch) {
+  return al256(std::max<size_t>((size_t)batch * XW * 4, mx_block_bytes(qtype)) * nblk);
+}
+static size_t gemv_ws_scales(int nblk, int batch) { return al256((size_t)std::max(batch, MX_SLOTS) * nblk * 4); }
+
 size_t slq_gemv_workspace_bytes(int qtype, int64_t rows, int64_t cols, int batch) {
   if (!slq_packed_bytes(qtype, rows, cols) || batch < 1 || batch > MAX_T) return 0;
   const int nblk = (int)(cols / QK);
   const int64_t nrg = (rows + RG - 1) / RG;
-  return al256((size_t)batch * nblk * XW * 4) + al256((size_t)batch * nblk * 4) +
+  return gemv_ws_digits(qtype, nblk, batch) + gemv_ws_scales(nblk, batch) +
          al256((size_t)nrg * 16 * batch * RG * 4) + al256((size_t)nrg * 4);
 }
 
@@ -503,9 +519,11 @@ int slq_gemv(int qtype, const void* packed_dev, int64_t rows, int64_t cols, int 
   if (!packed_dev || !x_dev || !y_dev || !ws_dev) return fail(SLICE_EINVAL, "slq_gemv: null pointer");
   const int nblk = (int)(cols / QK);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
-  Act a{reinterpret_cast<int32_t*>(ws), reinterpret_cast<float*>(ws + al256((size_t)batch * nblk * XW * 4)), nblk};
+  const int fmt = batch >= clampi(env_int("SLQ_MFMA_MIN_T", 2), 1, MAX_T + 1) ? 1 : 0;
+  const size_t dig = gemv_ws_digits(qtype, nblk, batch);
+  Act a{reinterpret_cast<int32_t*>(ws), reinterpret_cast<float*>(ws + dig), nblk, fmt};
   const int64_t nrg = (rows + RG - 1) / RG;
-  float* part = reinterpret_cast<float*>(ws + al256((size_t)batch * nblk * XW * 4) + al256((size_t)batch * nblk * 4));
+  float* part = reinterpret_cast<float*>(ws + dig + gemv_ws_scales(nblk, batch));
   unsigned* cnt = reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(part) + al256((size_t)nrg * 16 * batch * RG * 4));
   HIPCHK(launch_quant_act(qtype, x_dev, batch, (int)cols, cols, a, S(stream)));
   const Plan pl = plan_gemv("GEMV", rows, cols);
@@ -548,6 +566,7 @@ int slice_load(const slice_config* cfg, void* weights_dev, void* workspace_dev, 
   s->w = static_cast<uint8_t*>(weights_dev);
   s->ws = static_cast<uint8_t*>(workspace_dev);
   s->eager = env_int("SLQ_EAGER", 0) != 0;
+  s->mx_min_t = clampi(env_int("SLQ_MFMA_MIN_T", 2), 1, MAX_T + 1);
   hipError_t he = hipMemsetAsync(s->w, 0, s->L.wbytes, S(stream));
   if (he == hipSuccess) he = hipMemsetAsync(s->ws, 0, s->L.wsbytes, S(stream));
   if (he == hipSuccess) he = hipStreamCreate(&s->cap);
@@ -715,7 +734,7 @@ int slice_head_argmax(slice_t* s, const void* in, int32_t* tok, float* logits, v
   const hipStream_t st = S(stream);
   float* lg = logits ? logits : s->wsp<float>(L.logits);
   HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, in, nullptr, c.hidden, 1, c.hidden, s->wsp<float>(L.h),
-                             reinterpret_cast<const float*>(s->w + L.out_norm), c.qtype, s->act_a(),
+                             reinterpret_cast<const float*>(s->w + L.out_norm), c.qtype, s->act_a(s->fmt_for(1)),
                              s->wsp<float>(L.ssq), st));
   const Packed W = s->packed(c.tied_head ? L.embed : L.head);
   GemvOut o{};
@@ -725,7 +744,7 @@ int slice_head_argmax(slice_t* s, const void* in, int32_t* tok, float* logits, v
   o.part = s->wsp<float>(L.part);
   o.cnt = s->wsp<unsigned>(L.cnt);
   const Plan pl = plan_gemv("HEAD", W.rows, W.cols);
-  HIPCHK(launch_gemv(W, 1, s->act_a(), s->norm_h(), o, pl.ks, pl.w, st));
+  HIPCHK(launch_gemv(W, 1, s->act_a(s->fmt_for(1)), s->norm_h(), o, pl.ks, pl.w, st));
   HIPCHK(launch_argmax(lg, c.vocab, s->wsp<float>(L.amax_v), s->wsp<int>(L.amax_i), L.amax_parts, tok, st));
   return SLICE_OK;
 }

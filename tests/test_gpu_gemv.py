@@ -68,6 +68,47 @@ def test_gemv_batch_equals_single_bitwise(qtype):
         np.testing.assert_array_equal(y1[0], y16[t])
 
 
+# (split-K workgroups, waves per workgroup) of the standalone GEMV, forced
+# through the plan overrides; batched calls (int8 MFMA) must reproduce the
+# single-token GEMV bit for bit under every split
+SPLITS = [(1, 1), (1, 8), (3, 2), (16, 1), (2, 8), (5, 3)]
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("ks,w", SPLITS)
+@pytest.mark.parametrize("rows,cols", [(200, 32 * 19), (1000, 32 * 37), (64, 32 * 130)])
+def test_gemm_batch_equals_single_bitwise(qtype, ks, w, rows, cols, monkeypatch):
+    monkeypatch.setenv("SLQ_KS_GEMV", str(ks))
+    monkeypatch.setenv("SLQ_W_GEMV", str(w))
+    raw = _raw(qtype, rows, cols, 9)
+    packed = slq.repack(qtype, _dev(raw), rows, cols)
+    x = synth.gemv_x(12, 16, cols, tag=ks * 10 + w)
+    x[3] = 0.0                      # an all-zero token
+    x[5, 64:96] = 0.0               # an all-zero block inside a token
+    x[9, ::5] *= 1e3                # wide range inside blocks
+    y1 = np.stack([slq.gemv(qtype, packed, rows, cols, _dev(x[t:t + 1])).cpu().numpy()[0] for t in range(16)])
+    assert np.all(y1[3] == 0)
+    for batch in (2, 5, 16):
+        yb = slq.gemv(qtype, packed, rows, cols, _dev(x[:batch])).cpu().numpy()
+        np.testing.assert_array_equal(yb, y1[:batch])
+    ref = qref.gemv(qtype, raw, rows, cols, x.astype(np.float64))
+    for t in range(16):
+        assert rel_err(y1[t], ref[t]) <= 1e-5, t
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
+def test_gemm_single_token_through_mfma(qtype, monkeypatch):
+    """With the MFMA path forced for one token the result equals the GEMV's."""
+    rows, cols = 1000, 32 * 37
+    raw = _raw(qtype, rows, cols, 10)
+    packed = slq.repack(qtype, _dev(raw), rows, cols)
+    x = synth.gemv_x(13, 1, cols)
+    y_gemv = slq.gemv(qtype, packed, rows, cols, _dev(x)).cpu().numpy()
+    monkeypatch.setenv("SLQ_MFMA_MIN_T", "1")
+    y_mfma = slq.gemv(qtype, packed, rows, cols, _dev(x)).cpu().numpy()
+    np.testing.assert_array_equal(y_gemv, y_mfma)
+
+
 @pytest.mark.parametrize("qtype", QTYPES)
 def test_gemv_many_blocks(qtype):
     """4000 activation blocks: the largest entry of a block sits on the

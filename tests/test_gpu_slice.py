@@ -78,6 +78,25 @@ def test_tiny_hybrid_verify_commit(accepted):
     assert rel_err(nxt, orc.decode(H[4], raw=True)) <= TOL
 
 
+@pytest.mark.parametrize("k", [2, 3, 16])
+def test_tiny_hybrid_q8_verify_equals_plain(k):
+    """Q8_0 weights: a verify pass of k tokens (int8 MFMA products) gives the
+    bits of k plain decode steps, and stays within tolerance of the oracle."""
+    H = inputs(TINY_H, k, workload=WL, step0=40)
+    s, orc, _, _ = make_pair(TINY_H, synth.Q8_0, 0, 4, workload=WL, prefill=300, max_seq=512, max_verify=16)
+    out = s.verify(_t(H)).cpu().numpy()
+    ref = orc.verify(H, raw=True)
+    for t in range(k):
+        assert rel_err(out[t], ref[t]) <= TOL, t
+    p, _, _, _ = make_pair(TINY_H, synth.Q8_0, 0, 4, workload=WL, prefill=300, max_seq=512, max_verify=16,
+                           with_oracle=False)
+    for t in range(k):
+        np.testing.assert_array_equal(p.decode(_t(H[t])).cpu().numpy(), out[t])
+    s.commit(k)
+    for l in (0, 1, 2):
+        np.testing.assert_array_equal(s.get_state(l).cpu().numpy(), p.get_state(l).cpu().numpy())
+
+
 def test_commit_zero_restores_state_exactly():
     s, _, _, _ = _tiny(with_oracle=False)
     before = [s.get_state(l).cpu().numpy() for l in (0, 1, 2)]
