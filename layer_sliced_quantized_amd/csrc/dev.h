@@ -153,17 +153,23 @@ __device__ __forceinline__ void put_digits(const Act& a, int qt, int t, int blk,
 // Shared tail of every producer of a residual-stream vector: lane holds h_new
 // for row rg*64+lane (0 beyond H).  Writes h, the sum of squares of the 64 rows,
 // and the digits of norm_w*h for blocks 2rg and 2rg+1.
-__device__ __forceinline__ void resid_tail(int t, int rg, int H, float hn, float* h, int64_t h_ts,
-                                           const float* norm_w, int qt, const Act& next,
-                                           float* ssq_out, int nrg) {
+// `w` is norm_w of this lane's row (0 beyond H).
+__device__ __forceinline__ void resid_tail_w(int t, int rg, int H, float hn, float w, float* h, int64_t h_ts, int qt,
+                                             const Act& next, float* ssq_out, int nrg) {
   const int lane = threadIdx.x & 63;
   const int row = rg * RG + lane;
   if (row < H) h[(size_t)t * h_ts + row] = hn;
   const float ss = wave_sum(hn * hn);
   if (lane == 0) ssq_out[(size_t)t * nrg + rg] = ss;
-  const float w = row < H ? norm_w[row] : 0.0f;
   const int blk = 2 * rg + (lane >> 5);
   put_digits(next, qt, t, blk, w * hn, blk < next.nblk);
+}
+__device__ __forceinline__ void resid_tail(int t, int rg, int H, float hn, float* h, int64_t h_ts,
+                                           const float* norm_w, int qt, const Act& next,
+                                           float* ssq_out, int nrg) {
+  const int row = rg * RG + (int)(threadIdx.x & 63);
+  const float w = row < H ? norm_w[row] : 0.0f;
+  resid_tail_w(t, rg, H, hn, w, h, h_ts, qt, next, ssq_out, nrg);
 }
 
 }  // namespace slq

@@ -61,6 +61,11 @@ struct Plan {
 
 int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
 
+// Fewest tokens per call for which the int8-MFMA products beat the per-token
+// integer dot products on MI355X (measured on the 34816x5120, 5120x17408 and
+// 248320x5120 shapes): Q4_0 from 5 tokens, Q8_0 from 3.
+int mfma_min_tokens(int qtype) { return qtype == QT_Q4 ? 5 : 3; }
+
 Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
   const int nrg = (int)((rows + RG - 1) / RG);
   const int ntiles = (int)((cols / QK + TB - 1) / TB);
@@ -79,6 +84,7 @@ Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
   }
   p.ks = clampi(env_int(("SLQ_KS_" + k).c_str(), p.ks), 1, 16);
   p.w = clampi(env_int(("SLQ_W_" + k).c_str(), p.w), 1, 8);
+  p.w = clampi(p.w, 1, 64 / p.ks);   // the batched products keep ks * w <= 64 partials
   return p;
 }
 
@@ -91,6 +97,7 @@ struct Mat {
 struct LayerLayout {
   bool attn = false;
   Mat g1, g2, f1, f2;
+  Plan pg1{1, 1}, pg2{1, 1}, pf1{1, 1}, pf2{1, 1};   // GEMV splits, fixed at load
   size_t attn_norm = 0, ffn_norm = 0, q_norm = 0, k_norm = 0;
   // row offsets inside g1
   int off_q = 0, off_k = 0, off_v = 0, off_a = 0, off_b = 0, off_z = 0, off_g = -1;
@@ -100,6 +107,7 @@ struct LayerLayout {
 struct Layout {
   std::vector<LayerLayout> layers;   // index l - begin
   Mat embed, head;
+  Plan phead{1, 1};
   size_t out_norm = 0;
   size_t wbytes = 0;
   // workspace
@@ -233,13 +241,26 @@ Layout make_layout(const slice_config& c) {
   L.ssq = take((size_t)mt * (H / RG) * 4);
   L.y1 = take((size_t)mt * (L.g1_rows_max ? L.g1_rows_max : 1) * 4);
   // split-K scratch: any GEMV of the slice with up to 16 splits
+  // (split-K workgroups x waves per row group, of which the batched MFMA
+  // products keep one partial each; the single-token GEMV keeps one per split)
   int64_t rg_max = 0;
-  auto upd = [&](const Mat& m) { if (m.present) rg_max = std::max<int64_t>(rg_max, (m.rows + RG - 1) / RG); };
-  for (const LayerLayout& ll : L.layers) { upd(ll.g1); upd(ll.g2); upd(ll.f1); upd(ll.f2); }
-  upd(L.embed);
-  upd(L.head);
-  L.part = take((size_t)rg_max * 16 * mt * RG * 4);
-  L.cnt = take((size_t)rg_max * 4);
+  size_t part_floats = 0;
+  auto upd = [&](const Mat& m, Plan& p, const char* kind) {
+    if (!m.present) return;
+    p = plan_gemv(kind, m.rows, m.cols);
+    const int64_t nrg = (m.rows + RG - 1) / RG;
+    rg_max = std::max<int64_t>(rg_max, nrg);
+    part_floats = std::max<size_t>(part_floats, (size_t)nrg * p.ks * p.w * mt * RG);
+  };
+  for (LayerLayout& ll : L.layers) {
+    upd(ll.g1, ll.pg1, "G1");
+    upd(ll.g2, ll.pg2, "G2");
+    upd(ll.f1, ll.pf1, "F1");
+    upd(ll.f2, ll.pf2, "F2");
+  }
+  if (c.has_head) upd(c.tied_head ? L.embed : L.head, L.phead, "HEAD");
+  L.part = take(part_floats * 4);
+  L.cnt = take((size_t)std::max<int64_t>(rg_max, 1) * 4);
   if (L.n_attn) {
     L.nchunk = (c.max_seq + ATT_CHUNK - 1) / ATT_CHUNK;
     L.qhat = take((size_t)mt * nq * 4);
@@ -293,7 +314,7 @@ struct slice {
   Ctrl* ctrl() const { return reinterpret_cast<Ctrl*>(ws + L.ctrl); }
   template <class X> X* wsp(size_t off) const { return reinterpret_cast<X*>(ws + off); }
   Packed packed(const Mat& m) const { return Packed{w + m.off, m.rows, m.cols, cfg.qtype}; }
-  int mx_min_t = 2;   // steps with at least this many tokens use the MFMA products
+  int mx_min_t = 5;   // steps with at least this many tokens use the MFMA products
   int fmt_for(int T) const { return T >= mx_min_t ? 1 : 0; }
   Act act_a(int fmt) const { return Act{wsp<int32_t>(L.xa_d), wsp<float>(L.xa_s), cfg.hidden / QK, fmt}; }
   Act act_u(int fmt) const { return Act{wsp<int32_t>(L.xu_d), wsp<float>(L.xu_s), (L.nu + QK - 1) / QK, fmt}; }
@@ -345,7 +366,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       o.y_tstride = W.rows;
       o.part = part;
       o.cnt = cnt;
-      const Plan pl = plan_gemv("G1", W.rows, W.cols);
+      const Plan pl = ll.pg1;
       HIPCHK(launch_gemv(W, T, s->act_a(fmt), s->norm_h(), o, pl.ks, pl.w, st));
       SLQ_MARK(ll.attn ? SLICE_OP_ATT_IN : SLICE_OP_DN_IN);
     }
@@ -394,7 +415,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
     }
     // residual update after the mixer: h += W_o u, then digits for the next RMSNorm
     const float* nw_after_mixer = c.ffn ? reinterpret_cast<const float*>(s->w + ll.ffn_norm) : attn_norm_of(i + 1);
-    auto residual = [&](const Mat& m, Act in, const float* next_norm, const char* kind) -> int {
+    auto residual = [&](const Mat& m, Act in, const float* next_norm, const Plan& pl) -> int {
       const Packed W = s->packed(m);
       GemvOut o{};
       o.kind = EPI_RESID;
@@ -406,11 +427,10 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       o.norm_w = next_norm;
       o.part = part;
       o.cnt = cnt;
-      const Plan pl = plan_gemv(kind, W.rows, W.cols);
       HIPCHK(launch_gemv(W, T, in, NormIn{nullptr, 0, 0.f, 0.f}, o, pl.ks, pl.w, st));
       return SLICE_OK;
     };
-    int rc = (only < 0 || only == k_out) ? residual(ll.g2, s->act_u(fmt), nw_after_mixer, "G2") : SLICE_OK;
+    int rc = (only < 0 || only == k_out) ? residual(ll.g2, s->act_u(fmt), nw_after_mixer, ll.pg2) : SLICE_OK;
     if (rc) return rc;
     SLQ_MARK(k_out);
     if (c.ffn && (only < 0 || only == SLICE_OP_FFN_IN)) {
@@ -423,12 +443,12 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       o.next_qt = qt;
       o.part = part;
       o.cnt = cnt;
-      const Plan pl = plan_gemv("F1", W.rows, W.cols);
+      const Plan pl = ll.pf1;
       HIPCHK(launch_gemv(W, T, s->act_a(fmt), s->norm_h(), o, pl.ks, pl.w, st));
       SLQ_MARK(SLICE_OP_FFN_IN);
     }
     if (c.ffn && (only < 0 || only == SLICE_OP_FFN_OUT)) {
-      rc = residual(ll.f2, s->act_m(fmt), attn_norm_of(i + 1), "F2");
+      rc = residual(ll.f2, s->act_m(fmt), attn_norm_of(i + 1), ll.pf2);
       if (rc) return rc;
       SLQ_MARK(SLICE_OP_FFN_OUT);
     }
@@ -503,12 +523,17 @@ static size_t gemv_ws_digits(int qtype, int nblk, int batch) {
 }
 static size_t gemv_ws_scales(int nblk, int batch) { return al256((size_t)std::max(batch, MX_SLOTS) * nblk * 4); }
 
+static size_t gemv_ws_part(int64_t rows, int64_t cols, int batch) {
+  const Plan p = plan_gemv("GEMV", rows, cols);
+  return al256((size_t)((rows + RG - 1) / RG) * p.ks * p.w * batch * RG * 4);
+}
+
 size_t slq_gemv_workspace_bytes(int qtype, int64_t rows, int64_t cols, int batch) {
   if (!slq_packed_bytes(qtype, rows, cols) || batch < 1 || batch > MAX_T) return 0;
   const int nblk = (int)(cols / QK);
   const int64_t nrg = (rows + RG - 1) / RG;
-  return gemv_ws_digits(qtype, nblk, batch) + gemv_ws_scales(nblk, batch) +
-         al256((size_t)nrg * 16 * batch * RG * 4) + al256((size_t)nrg * 4);
+  return gemv_ws_digits(qtype, nblk, batch) + gemv_ws_scales(nblk, batch) + gemv_ws_part(rows, cols, batch) +
+         al256((size_t)nrg * 4);
 }
 
 int slq_gemv(int qtype, const void* packed_dev, int64_t rows, int64_t cols, int batch, const float* x_dev,
@@ -519,12 +544,12 @@ int slq_gemv(int qtype, const void* packed_dev, int64_t rows, int64_t cols, int 
   if (!packed_dev || !x_dev || !y_dev || !ws_dev) return fail(SLICE_EINVAL, "slq_gemv: null pointer");
   const int nblk = (int)(cols / QK);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
-  const int fmt = batch >= clampi(env_int("SLQ_MFMA_MIN_T", 2), 1, MAX_T + 1) ? 1 : 0;
+  const int fmt = batch >= clampi(env_int("SLQ_MFMA_MIN_T", mfma_min_tokens(qtype)), 1, MAX_T + 1) ? 1 : 0;
   const size_t dig = gemv_ws_digits(qtype, nblk, batch);
   Act a{reinterpret_cast<int32_t*>(ws), reinterpret_cast<float*>(ws + dig), nblk, fmt};
   const int64_t nrg = (rows + RG - 1) / RG;
   float* part = reinterpret_cast<float*>(ws + dig + gemv_ws_scales(nblk, batch));
-  unsigned* cnt = reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(part) + al256((size_t)nrg * 16 * batch * RG * 4));
+  unsigned* cnt = reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(part) + gemv_ws_part(rows, cols, batch));
   HIPCHK(launch_quant_act(qtype, x_dev, batch, (int)cols, cols, a, S(stream)));
   const Plan pl = plan_gemv("GEMV", rows, cols);
   const Packed W{static_cast<const uint8_t*>(packed_dev), rows, cols, qtype};
@@ -566,7 +591,7 @@ int slice_load(const slice_config* cfg, void* weights_dev, void* workspace_dev, 
   s->w = static_cast<uint8_t*>(weights_dev);
   s->ws = static_cast<uint8_t*>(workspace_dev);
   s->eager = env_int("SLQ_EAGER", 0) != 0;
-  s->mx_min_t = clampi(env_int("SLQ_MFMA_MIN_T", 2), 1, MAX_T + 1);
+  s->mx_min_t = clampi(env_int("SLQ_MFMA_MIN_T", mfma_min_tokens(cfg->qtype)), 1, MAX_T + 1);
   hipError_t he = hipMemsetAsync(s->w, 0, s->L.wbytes, S(stream));
   if (he == hipSuccess) he = hipMemsetAsync(s->ws, 0, s->L.wsbytes, S(stream));
   if (he == hipSuccess) he = hipStreamCreate(&s->cap);
@@ -743,7 +768,7 @@ int slice_head_argmax(slice_t* s, const void* in, int32_t* tok, float* logits, v
   o.y_tstride = W.rows;
   o.part = s->wsp<float>(L.part);
   o.cnt = s->wsp<unsigned>(L.cnt);
-  const Plan pl = plan_gemv("HEAD", W.rows, W.cols);
+  const Plan pl = L.phead;
   HIPCHK(launch_gemv(W, 1, s->act_a(s->fmt_for(1)), s->norm_h(), o, pl.ks, pl.w, st));
   HIPCHK(launch_argmax(lg, c.vocab, s->wsp<float>(L.amax_v), s->wsp<int>(L.amax_i), L.amax_parts, tok, st));
   return SLICE_OK;

@@ -78,6 +78,7 @@ SPLITS = [(1, 1), (1, 8), (3, 2), (16, 1), (2, 8), (5, 3)]
 @pytest.mark.parametrize("ks,w", SPLITS)
 @pytest.mark.parametrize("rows,cols", [(200, 32 * 19), (1000, 32 * 37), (64, 32 * 130)])
 def test_gemm_batch_equals_single_bitwise(qtype, ks, w, rows, cols, monkeypatch):
+    monkeypatch.setenv("SLQ_MFMA_MIN_T", "2")      # every batched call on the matrix cores
     monkeypatch.setenv("SLQ_KS_GEMV", str(ks))
     monkeypatch.setenv("SLQ_W_GEMV", str(w))
     raw = _raw(qtype, rows, cols, 9)

@@ -53,8 +53,12 @@ def test_tiny_hybrid_decode_states_and_cache():
     assert rel_err(V.cpu().numpy()[:, 300:303], Vo[:, 300:303]) <= TOL
 
 
+@pytest.mark.parametrize("mfma_min", ["2", "17"])
 @pytest.mark.parametrize("accepted", [0, 1, 2, 3, 4])
-def test_tiny_hybrid_verify_commit(accepted):
+def test_tiny_hybrid_verify_commit(accepted, mfma_min, monkeypatch):
+    """Verify 4 drafts through the int8-MFMA products (2) or the per-token
+    integer dot products (17), commit, continue."""
+    monkeypatch.setenv("SLQ_MFMA_MIN_T", mfma_min)
     H = inputs(TINY_H, 5, workload=WL, step0=10)
     s, orc, _, _ = _tiny()
     out = s.verify(_t(H[:4])).cpu().numpy()
