@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(ROOT, "_build", "slq")
 LIB = os.path.join(HERE, "libslq.so")
-SOURCES = ["gemv.hip", "gemm.hip", "deltanet.hip", "attn.hip", "misc.hip", "slice.cpp"] + [
+SOURCES = ["gemv.hip", "gemm.hip", "gemm_q4.hip", "gemm_q8.hip", "deltanet.hip", "attn.hip", "misc.hip", "slice.cpp"] + [
     f"gemv_{q}_{e}.hip" for q in ("q4", "q8") for e in ("store", "swiglu", "resid")]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -94,7 +94,7 @@ __device__ __forceinline__ void quant_block_half(float v, int32_t* xd, float* xs
   }
 }
 
-// Layout fmt 1 (MFMA operand order, see Act): the same x_int and scale as fmt 0.
+// MFMA layout (see Act): the same x_int and scale as the lane-row layout.
 template <int QT>
 __device__ __forceinline__ void quant_block_mx(float v, const Act& a, int t, int blk, bool write) {
   const int lane = threadIdx.x & 63;
@@ -118,33 +118,34 @@ __device__ __forceinline__ void quant_block_mx(float v, const Act& a, int t, int
         if (g >= 2) dig *= 16;
         word |= ((uint32_t)dig & 255u) << (8 * k);
       }
-      if (write && w < 48)
-        a.xd[(((size_t)blk * 12 + c) * MX_SLOTS + t) * 4 + q] = (int32_t)word;
+      if (write && w < 48) a.mxd[(size_t)blk * (mx_block_bytes(QT) / 4) + (c * MX_SLOTS + t) * 4 + q] = (int32_t)word;
     }
   } else {
-    // 24 dwords: w = e < 24, chunk (p, g) = (w >> 3, (w >> 1) & 3), dword q = w & 1
+    // 24 dwords: w = e < 24, chunk c = w >> 2 (p = c >> 1, h = c & 1), dword q = w & 3
     const int w = e % 24;
-    const int p = w >> 3, g = (w >> 1) & 3, q = w & 1;
+    const int c = w >> 2, q = w & 3, p = c >> 1, h = c & 1;
     uint32_t word = 0;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      const uint32_t uk = (uint32_t)__shfl((int)u, base + 8 * g + 4 * q + k, 64);
+      const uint32_t uk = (uint32_t)__shfl((int)u, base + 16 * h + 4 * q + k, 64);
       word |= (((uk >> (8 * p)) & 255u) ^ 0x80u) << (8 * k);
     }
-    if (write && e < 24) a.xd[(((size_t)blk * 12 + 4 * p + g) * MX_SLOTS + t) * 2 + q] = (int32_t)word;
+    if (write && e < 24) a.mxd[(size_t)blk * (mx_block_bytes(QT) / 4) + (c * MX_SLOTS + t) * 4 + q] = (int32_t)word;
   }
-  if (write && e == 0) a.xs[(size_t)blk * MX_SLOTS + t] = amax / (QT == QT_Q4 ? M_Q4 : M_Q8);
+  if (write && e == 0)
+    reinterpret_cast<float*>(a.mxd + (size_t)blk * (mx_block_bytes(QT) / 4) + mx_scale_off(QT) / 4)[t] =
+        amax / (QT == QT_Q4 ? M_Q4 : M_Q8);
 }
 
-// Digits of block blk of token t of `a`, in a's layout.  Every lane of the
-// wave must call this; `write` selects which 32-lane halves store.
+// Digits of block blk of token t of `a`, in the lane-row layout and, when a
+// has one, the MFMA layout.  Every lane of the wave must call this; `write`
+// selects which 32-lane halves store.
 __device__ __forceinline__ void put_digits(const Act& a, int qt, int t, int blk, float v, bool write) {
-  if (a.fmt == 0) {
-    int32_t* xd = a.xd + ((size_t)t * a.nblk + blk) * XW;
-    float* xs = a.xs + (size_t)t * a.nblk + blk;
-    if (qt == QT_Q4) quant_block_half<QT_Q4>(v, xd, xs, write);
-    else quant_block_half<QT_Q8>(v, xd, xs, write);
-  } else {
+  int32_t* xd = a.xd + ((size_t)t * a.nblk + blk) * XW;
+  float* xs = a.xs + (size_t)t * a.nblk + blk;
+  if (qt == QT_Q4) quant_block_half<QT_Q4>(v, xd, xs, write);
+  else quant_block_half<QT_Q8>(v, xd, xs, write);
+  if (a.mxd) {
     if (qt == QT_Q4) quant_block_mx<QT_Q4>(v, a, t, blk, write);
     else quant_block_mx<QT_Q8>(v, a, t, blk, write);
   }

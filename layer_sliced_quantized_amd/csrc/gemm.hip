@@ -1,4 +1,4 @@
-// Instantiations and dispatch of the batched int8-MFMA products.
+// Dispatch of the batched int8-MFMA products (instantiations: gemm_q4.hip, gemm_q8.hip).
 #include "gemm_kernel.h"
 
 namespace slq {
@@ -16,5 +16,7 @@ hipError_t launch_gemm(const Packed& W, int T, Act x, NormIn nin, GemvOut out, i
   }
   return hipErrorInvalidValue;
 }
+
+bool gemm_usable(int qt, int T, int waves) { return gemm_fits(qt, T, waves); }
 
 }  // namespace slq

@@ -1,35 +1,34 @@
 // Batched (2..16 tokens) Q4_0 / Q8_0 matrix products on the int8 matrix cores.
 //
-// Each token's result is bitwise the one the single-token GEMV gives.  The
-// single-token GEMV splits the K tiles of a 64-row group over ks workgroups and
-// w waves ("units" u = split * w + wave), adds the waves of a split in wave order
-// and the splits in split order, and applies the same fp32 operations to every
-// block.  This kernel keeps every unit's tile range and block order and the
-// order of the final sums; only the exact integer block sums come from the
-// matrix cores:
+// Same work split as the single-token GEMV (64-row group per wave, K tiles over
+// the waves of a workgroup and over split-K workgroups, waves summed in LDS in
+// wave order, splits in split order) and the same fp32 operations per (row,
+// token, block), so every token's result is bitwise the single-token one.  Only
+// the exact integer block sums come from the matrix cores.
 //
-//   Q4_0: v_mfma_i32_16x16x64_i8, A = digits of 16 token slots (activation
-//         layout fmt 1: 64 k-entries = digit 2p of the 32 elements and 16 x digit
-//         2p+1 of them), B = 16 weight rows, each 4-bit code widened to int8.
-//         Three MFMAs give P_p = C_2p + 16 C_2p+1 (C_d = codes . digit d); the
-//         block sum D = P_0 + 256 (P_1 + 256 P_2) is exact in int32 (|D| <= 32 *
-//         8 * 7829367 < 2^31), and (float)D is the single rounding of D that
-//         the GEMV's two-part fma also produces.
-//   Q8_0: v_mfma_i32_16x16x32_i8 per base-256 digit; combined exactly like the
-//         GEMV (digit 2 times 65536 fused with digit 1 * 256 + digit 0).
+// Operand layout (checked on gfx950) of v_mfma_i32_16x16x64_i8: lane l holds
+// row/column l % 16 and the 16-byte k-group l / 16 of A and of B alike; output
+// register i of lane l is C[4 (l / 16) + i][l % 16].
 //
-// Operand layout (checked on gfx950): lane l holds row/column l % 16 and
-// k-group l / 16 of A and of B alike; output register i of lane l is
-// C[4 (l / 16) + i][l % 16].  Here C rows are tokens and columns weight rows.
+// Block-diagonal use: A is the wave's own weights, lane l = row l, so k-group g
+// of A row m is weight row 16 g + m.  B column n = 4 s + t is token t of a group
+// of four, and its only nonzero k-group is g = s.  Then
+//     C[m][4 s + t] = row (16 s + m) . digits of token t,
+// i.e. 64 rows x 4 tokens per MFMA, with no data movement for the weights.
+//   Q4_0: per digit pair p, four MFMAs accumulate elements 0..15 / 16..31 of
+//         digit 2p and 16 x digit 2p+1 (activation layout), giving
+//         P_p = C_2p + 16 C_2p+1; the block sum D = P_0 + 256 (P_1 + 256 P_2)
+//         is exact in int32 (|D| <= 32 * 8 * 7829367 < 2^31), and (float)D is
+//         the single rounding of D the GEMV's fused two-part sum also gives.
+//   Q8_0: per base-256 digit two MFMAs (elements 0..15, 16..31); combined like
+//         the GEMV (digit 2 times 65536 fused with digit 1 * 256 + digit 0).
+// Lane l ends with rows 16 ((l & 15) >> 2) + 4 (l >> 4) + i, i = 0..3, of token
+// 4 group + (l & 3).
 //
-// Work split: a workgroup of R waves takes R consecutive row groups (one per
-// wave) and one unit u, so all its waves walk the same K tiles.  The
-// activation digits of a tile (only the token slots in use, rounded up to 4)
-// are copied once per workgroup into LDS with direct global->LDS loads one
-// tile ahead, next to each wave's next weight tile (registers), so no load has
-// to wait for a later-issued one.  Every unit publishes its partial sums; the
-// last unit of a row group (atomic ticket) adds them in the GEMV's order and
-// runs the epilogue.
+// The digits of the tokens in use come into a ring of 8 block slots in the
+// wave's own LDS by direct global->LDS loads, one tile ahead like the weights.
+// Every wait is an explicit vmcnt that counts only loads issued earlier than
+// the next tile's weights, so no read of the ring waits for HBM.
 #pragma once
 #include "gemv_kernel.h"
 
@@ -39,22 +38,45 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-constexpr int GEMM_R = 4;                       // row groups (waves) per workgroup
-constexpr int GEMM_STAGE = 3072;                // per wave: 2 KB staged codes + 1 KB tile scales
-constexpr int GEMM_MAX_UNITS = 64;              // split-K workgroups x waves of the single-token plan
-// bytes of one row of chunk slots per block in LDS: 12 chunks x tp slots x (16 or 8) B
-__host__ __device__ constexpr int gemm_blk_lds(int qt, int tp) { return 12 * tp * (qt == QT_Q4 ? 16 : 8); }
-// LDS of one tile of digits (tp slots) + its scales (16 slots)
-__host__ __device__ constexpr int gemm_act_tile(int qt, int tp) { return TB * gemm_blk_lds(qt, tp) + TB * MX_SLOTS * 4; }
-__host__ __device__ constexpr int gemm_lds_bytes(int qt, int tp) {
-  return 2 * gemm_act_tile(qt, tp) + GEMM_R * GEMM_STAGE > GEMM_R * 4096 ? 2 * gemm_act_tile(qt, tp) + GEMM_R * GEMM_STAGE
-                                                                         : GEMM_R * 4096;
+// LDS of one ring slot: chunks x tp token slots x 16 B, then 16 token scales.
+__host__ __device__ constexpr int gemm_slot(int qt, int tp) { return mx_chunks(qt) * tp * 16 + 64; }
+// copy instructions (64 lanes x 16 B) per block
+__host__ __device__ constexpr int gemm_dpb(int qt, int tp) { return (gemm_slot(qt, tp) / 16 + 63) / 64; }
+// LDS per wave: 8 ring slots, the tile's scales, and a zero area as large as
+// one slot's digits (read by the B lanes outside the diagonal), placed 64 B
+// further on so that its broadcast reads fall in other banks than the chunks
+// read by the lanes inside the diagonal; the epilogue reuses the start for
+// 16 tokens x 64 rows of sums
+__host__ __device__ constexpr int gemm_zero(int qt, int tp) { return 8 * gemm_slot(qt, tp) + 1024 + 64; }
+__host__ __device__ constexpr int gemm_region(int qt, int tp) {
+  return gemm_zero(qt, tp) + mx_chunks(qt) * tp * 16 > 4096 ? gemm_zero(qt, tp) + mx_chunks(qt) * tp * 16 : 4096;
+}
+constexpr int GEMM_LDS_MAX = 160 * 1024;
+// at most 8 waves (256 registers each: the explicit wait counts rely on the
+// kernel never spilling to scratch) and the LDS of every wave's ring
+__host__ __device__ constexpr bool gemm_fits(int qt, int T, int waves) {
+  return T >= 1 && T <= MX_SLOTS && waves <= 8 && waves * gemm_region(qt, (T + 3) & ~3) <= GEMM_LDS_MAX;
 }
 
-// 16 bytes per lane from global memory straight into LDS at dst + 16 * lane
-// (dst is the same for the whole wave).
-__device__ __forceinline__ void load_lds16(const void* src, void* dst) {
-  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+// s_waitcnt immediate on gfx9: wait until at most n vector-memory operations
+// are outstanding (expcnt and lgkmcnt left at their maxima).
+__host__ __device__ constexpr unsigned vmcnt_imm(int n) {
+  return (unsigned)((n & 15) | (7 << 4) | (15 << 8) | (((n >> 4) & 3) << 14));
+}
+
+// Byte-addressed buffer descriptor of x's MFMA records (reads past the last
+// block return zeros).  Copies go through buffer (not global) loads into LDS:
+// the compiler's wait tracking takes a global->LDS load as touching two
+// address spaces and then turns every later register wait into a full drain,
+// while buffer loads keep the ordinary in-order counting.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const Act& x, int qt) {
+  return __builtin_amdgcn_make_buffer_rsrc(x.mxd, 0, x.nblk * mx_block_bytes(qt), 0x00020000);
+}
+
+// 16 bytes per lane from byte off + 16-byte-piece voff of the buffer straight
+// into LDS at dst + 16 * lane (dst and off are the same for the whole wave).
+__device__ __forceinline__ void load_lds16(__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned off, void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void_t*)dst, 16, voff, off, 0, 0);
 }
 
 // Four two's-complement nibbles in the low halves of the bytes of t (high
@@ -64,127 +86,153 @@ __device__ __forceinline__ uint32_t sext_nibbles(uint32_t t) {
 }
 
 #define SLQ_COMPILER_FENCE() asm volatile("" ::: "memory")
-#define SLQ_SCHED_FENCE() __builtin_amdgcn_sched_barrier(0)
 
-// Copy the digits of tile blocks kb .. kb+nb-1, token slots 0 .. tp-1, into
-// LDS as [block][chunk][slot] (tp slots), then the block scales [block][16].
-// Every wave of the workgroup takes a share of the 16-byte pieces.
+// A tile's weights into registers with always TB * NH + 1 loads, whatever the
+// tile: the codes of a ragged tile (nb < TB) repeat its last block, and nb = 0
+// (no tile) reads the first 16 bytes at tile from every lane.  Every path thus
+// issues the same loads, which keeps the compiler's own waits on these
+// registers (and the explicit ring waits) exact.
 template <int QT>
-__device__ __forceinline__ void stage_act(const Act& x, int kb, int nb, int tp, uint8_t* dst, int wave, int R) {
-  constexpr int PB = QT == QT_Q4 ? 16 : 8;       // bytes per slot of a chunk
-  constexpr int SPP = 16 / PB;                   // slots per 16-byte piece
-  const int lane = threadIdx.x & 63;
-  const uint8_t* src = reinterpret_cast<const uint8_t*>(x.xd);
-  const int ppc = tp / SPP;                      // pieces per chunk
-  const int n16 = nb * 12 * ppc;
-  for (int i = wave * 64; i < n16; i += R * 64) {
-    const int q = i + lane;
-    if (q < n16) {
-      const int b = q / (12 * ppc), c = (q / ppc) % 12, m = (q % ppc) * SPP;
-      load_lds16(src + ((((size_t)(kb + b) * 12 + c) * MX_SLOTS + m) * PB), dst + (size_t)i * 16);
-    }
-  }
-  if (wave == R - 1 && lane < nb * (MX_SLOTS / 4))
-    load_lds16(reinterpret_cast<const uint8_t*>(x.xs + (size_t)kb * MX_SLOTS) + lane * 16,
-               dst + TB * gemm_blk_lds(QT, tp));
+__device__ __forceinline__ void load_tile_fixed(const uint8_t* tile, int lane, int nb, TileRegs<QT>& r) {
+  constexpr int NH = TileRegs<QT>::NH;
+  const int nc = nb * NH;
+  const u32x4* cp = reinterpret_cast<const u32x4*>(tile) + (nb ? lane : 0);
+#pragma unroll
+  for (int b = 0; b < TB * NH; ++b) r.c[b] = __builtin_nontemporal_load(cp + (nb ? (b < nc ? b : nc - 1) : 0) * RG);
+  r.sc = __builtin_nontemporal_load(nb ? reinterpret_cast<const u32x4*>(tile + (size_t)nc * RG * 16) + lane : cp);
 }
 
-// All blocks of one tile: stage the weights, multiply, fold into acc[s][i]
-// (row 16 s + (lane & 15), token 4 (lane >> 4) + i).  act: the tile's digits
-// (tp slots) and scales in LDS.
-template <int QT>
-__device__ __forceinline__ void tile_mma(const TileRegs<QT>& r, int nb, const uint8_t* act, int T, int tp,
-                                         uint8_t* my, float (&acc)[4][4]) {
-  constexpr int PB = QT == QT_Q4 ? 16 : 8;
-  const int BL = gemm_blk_lds(QT, tp);
+// Digits (token slots 0..tp-1) and scales of block blk into a ring slot:
+// piece q < NCH*tp is chunk q / tp, slot q % tp; the last 4 pieces are the
+// block's 16 scales.  Exactly DPB instructions (lane 0 is always active).
+template <int QT, int DPB>
+__device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t rs, int blk, int tp, uint8_t* slot) {
+  constexpr int NCH = QT == QT_Q4 ? 12 : 6;
   const int lane = threadIdx.x & 63;
-  const int n = lane & 15, g = lane >> 4;
-  const bool slot_ok = n < T;   // A operand: this lane carries token slot n
-  u32x4* sc_lds = reinterpret_cast<u32x4*>(my + 2048);
+  const int nd = NCH * tp;
+  const unsigned rec = (unsigned)blk * (unsigned)mx_block_bytes(QT);
+#pragma unroll
+  for (int i = 0; i < DPB; ++i) {
+    const int q = 64 * i + lane;
+    if (q < nd + 4) {
+      const unsigned voff =
+          q < nd ? (unsigned)(((q / tp) * MX_SLOTS + q % tp) * 16) : (unsigned)(mx_scale_off(QT) + 16 * (q - nd));
+      load_lds16(rs, voff, rec, slot + 1024 * i);
+    }
+  }
+}
+
+// One tile: for each block wait for its ring slot, multiply, fold into
+// acc[group][i], then refill the slot with the same block of the next tile.
+// nb: blocks of this tile; nbn: blocks of the next tile (0: none), whose
+// weights were requested after this tile's digits.
+template <int QT, int NG>
+__device__ __forceinline__ void tile_diag(const TileRegs<QT>& r, int nb, __amdgpu_buffer_rsrc_t rs, int kb_next,
+                                          int nbn, int T, uint8_t* ring, float (&acc)[NG][4]) {
+  constexpr int NCH = QT == QT_Q4 ? 12 : 6;
+  constexpr int TP = 4 * NG;
+  constexpr int SLOT = gemm_slot(QT, TP);
+  constexpr int DPB = gemm_dpb(QT, TP);
+  constexpr int NW = TB * TileRegs<QT>::NH + 1;   // weight loads of a full tile
+  static_assert(7 * DPB + NW <= 63, "vmcnt holds at most 63 outstanding loads");
+  const int lane = threadIdx.x & 63;
+  const bool bvalid = ((lane & 15) >> 2) == (lane >> 4);   // B lane inside the diagonal
+  const int rbase = 16 * ((lane & 15) >> 2) + 4 * (lane >> 4);
+  const uint8_t* zero = ring + gemm_zero(QT, TP);
+  u32x4* sc_lds = reinterpret_cast<u32x4*>(ring + 8 * SLOT);
   sc_lds[lane] = r.sc;
   SLQ_COMPILER_FENCE();
   u32x4 scw[4];
 #pragma unroll
-  for (int s = 0; s < 4; ++s) scw[s] = sc_lds[16 * s + n];
+  for (int i = 0; i < 4; ++i) scw[i] = sc_lds[rbase + i];
 #pragma unroll
   for (int b = 0; b < TB; ++b) {
     if (b < nb) {
-      SLQ_SCHED_FENCE();
-      // chunk c = 4p + g, slot n of block b
-      const uint8_t* ab = act + (size_t)b * BL + ((size_t)g * tp + n) * PB;
-      const float4 s4 = reinterpret_cast<const float4*>(act + TB * BL)[b * (MX_SLOTS / 4) + g];
-      const float xs[4] = {4 * g + 0 < T ? s4.x : 0.0f, 4 * g + 1 < T ? s4.y : 0.0f, 4 * g + 2 < T ? s4.z : 0.0f,
-                           4 * g + 3 < T ? s4.w : 0.0f};
+      // Ring slot b was filled by the DPB loads issued after block b of the
+      // previous tile (or in the prologue).  Issued later than those, in this
+      // order: slots b+1..7, the next tile's weights (NW loads, always) and the
+      // refills of slots 0..b-1 made in this tile (DPB each, always).  Loads
+      // complete in issue order, so slot b has landed once at most
+      // (7 - b) DPB + NW + b DPB = 7 DPB + NW are outstanding.  (In a wave's
+      // first tile the epilogue inputs fetched after the prologue make this
+      // wait a little longer than needed, never shorter.)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * DPB + NW));
+      SLQ_COMPILER_FENCE();
+      const uint8_t* slot = ring + b * SLOT;
+      const i32x4 z = {0, 0, 0, 0};
+      u32x4 a0, a1;   // A operands: elements 0..15 and 16..31 of the lane's row
       if constexpr (QT == QT_Q4) {
         const u32x4 c = r.c[b];
-        u32x4 lo, hi;
-        lo.x = sext_nibbles(c.x & 0x0F0F0F0Fu);
-        lo.y = sext_nibbles(c.y & 0x0F0F0F0Fu);
-        lo.z = sext_nibbles(c.z & 0x0F0F0F0Fu);
-        lo.w = sext_nibbles(c.w & 0x0F0F0F0Fu);
-        hi.x = sext_nibbles((c.x >> 4) & 0x0F0F0F0Fu);
-        hi.y = sext_nibbles((c.y >> 4) & 0x0F0F0F0Fu);
-        hi.z = sext_nibbles((c.z >> 4) & 0x0F0F0F0Fu);
-        hi.w = sext_nibbles((c.w >> 4) & 0x0F0F0F0Fu);
-        u32x4* st = reinterpret_cast<u32x4*>(my);
-        st[lane] = lo;        // weights j of row `lane`
-        st[RG + lane] = hi;   // weights j + 16
+        a0.x = sext_nibbles(c.x & 0x0F0F0F0Fu);
+        a0.y = sext_nibbles(c.y & 0x0F0F0F0Fu);
+        a0.z = sext_nibbles(c.z & 0x0F0F0F0Fu);
+        a0.w = sext_nibbles(c.w & 0x0F0F0F0Fu);
+        a1.x = sext_nibbles((c.x >> 4) & 0x0F0F0F0Fu);
+        a1.y = sext_nibbles((c.y >> 4) & 0x0F0F0F0Fu);
+        a1.z = sext_nibbles((c.z >> 4) & 0x0F0F0F0Fu);
+        a1.w = sext_nibbles((c.w >> 4) & 0x0F0F0F0Fu);
       } else {
-        u32x4* st = reinterpret_cast<u32x4*>(my);
-        st[2 * lane] = r.c[2 * b];
-        st[2 * lane + 1] = r.c[2 * b + 1];
+        a0 = r.c[2 * b];
+        a1 = r.c[2 * b + 1];
       }
-      SLQ_COMPILER_FENCE();
-      const i32x4 z = {0, 0, 0, 0};
-      if constexpr (QT == QT_Q4) {
-        i32x4 a[3];
+      const i32x4 A0 = {(int)a0.x, (int)a0.y, (int)a0.z, (int)a0.w};
+      const i32x4 A1 = {(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
+      float d[4];
 #pragma unroll
-        for (int p = 0; p < 3; ++p) a[p] = slot_ok ? *reinterpret_cast<const i32x4*>(ab + (size_t)p * 4 * tp * PB) : z;
+      for (int i = 0; i < 4; ++i) d[i] = scale_of(scw[i], b);
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const float d = scale_of(scw[s], b);
-          const u32x4 wu = reinterpret_cast<const u32x4*>(my)[(g & 1) * RG + 16 * s + n];
-          const i32x4 wv = {(int)wu.x, (int)wu.y, (int)wu.z, (int)wu.w};
-          const i32x4 C0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[0], wv, z, 0, 0, 0);
-          const i32x4 C1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[1], wv, z, 0, 0, 0);
-          const i32x4 C2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(a[2], wv, z, 0, 0, 0);
+      for (int g = 0; g < NG; ++g) {
+        SLQ_COMPILER_FENCE();
+        const int t = 4 * g + (lane & 3);
+        const float xs = t < T ? reinterpret_cast<const float*>(slot + NCH * TP * 16)[t] : 0.0f;
+        // B operand lanes: token t's chunks inside the diagonal, zeros outside
+        const uint8_t* bsrc = bvalid ? slot + t * 16 : zero;
+        i32x4 P[3];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int D = C0[i] + ((C1[i] + (C2[i] << 8)) << 8);
-            acc[s][i] = __builtin_fmaf((float)D, d * xs[i], acc[s][i]);
-            // keep the fold here: otherwise the compiler sinks every block's
-            // fold to the end of the tile and keeps all MFMA results live
-            asm volatile("" : "+v"(acc[s][i]));
+        for (int p = 0; p < 3; ++p) {
+          SLQ_COMPILER_FENCE();   // one pair's operands in registers at a time
+          if constexpr (QT == QT_Q4) {
+            i32x4 bq[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) bq[k] = *reinterpret_cast<const i32x4*>(bsrc + (4 * p + k) * TP * 16);
+            i32x4 C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, bq[0], z, 0, 0, 0);
+            C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, bq[1], C, 0, 0, 0);
+            C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, bq[2], C, 0, 0, 0);
+            P[p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, bq[3], C, 0, 0, 0);
+          } else {
+            i32x4 bq[2];
+#pragma unroll
+            for (int k = 0; k < 2; ++k) bq[k] = *reinterpret_cast<const i32x4*>(bsrc + (2 * p + k) * TP * 16);
+            const i32x4 C = __builtin_amdgcn_mfma_i32_16x16x64_i8(A0, bq[0], z, 0, 0, 0);
+            P[p] = __builtin_amdgcn_mfma_i32_16x16x64_i8(A1, bq[1], C, 0, 0, 0);
           }
         }
-      } else {
-        long a[3];
 #pragma unroll
-        for (int p = 0; p < 3; ++p) a[p] = slot_ok ? *reinterpret_cast<const long*>(ab + (size_t)p * 4 * tp * PB) : 0;
-#pragma unroll
-        for (int s = 0; s < 4; ++s) {
-          const float d = scale_of(scw[s], b);
-          const long wv = reinterpret_cast<const long*>(my)[(16 * s + n) * 4 + g];
-          const i32x4 C0 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[0], wv, z, 0, 0, 0);
-          const i32x4 C1 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[1], wv, z, 0, 0, 0);
-          const i32x4 C2 = __builtin_amdgcn_mfma_i32_16x16x32_i8(a[2], wv, z, 0, 0, 0);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int l = C0[i] + (C1[i] << 8);
-            const float bf = __builtin_fmaf((float)C2[i], 65536.0f, (float)l);
-            acc[s][i] = __builtin_fmaf(bf, d * xs[i], acc[s][i]);
-            asm volatile("" : "+v"(acc[s][i]));
+        for (int i = 0; i < 4; ++i) {
+          float bf;
+          if constexpr (QT == QT_Q4) {
+            bf = (float)(P[0][i] + ((P[1][i] + (P[2][i] << 8)) << 8));
+          } else {
+            bf = __builtin_fmaf((float)P[2][i], 65536.0f, (float)(P[0][i] + (P[1][i] << 8)));
           }
+          acc[g][i] = __builtin_fmaf(bf, d[i] * xs, acc[g][i]);
+          // keep the fold here: otherwise the compiler sinks every block's
+          // fold to the end of the tile and keeps all MFMA results live
+          asm volatile("" : "+v"(acc[g][i]));
         }
       }
-      SLQ_COMPILER_FENCE();
     }
+    // refill slot b with block b of the next tile; where there is none, a
+    // dummy copy of block 0 into the unused slot keeps the load count fixed
+    SLQ_COMPILER_FENCE();
+    dma_block<QT, DPB>(rs, b < nbn ? kb_next + b : 0, TP, ring + b * SLOT);
+    SLQ_COMPILER_FENCE();
   }
 }
 
 // Epilogue of token j for the 64 rows of group rg; lane = row, a = sum over K.
 // pre: the token's RMSNorm factor (STORE, SWIGLU) or its residual entry h
-// (RESID); nw_row: next RMSNorm weight of the row (RESID).
+// (RESID), fetched at kernel start; nw_row: next RMSNorm weight of the row.
 template <int QT, int EPI>
 __device__ __forceinline__ void gemm_epi(const Packed& W, const GemvOut& out, int rg, int j, float a, float pre,
                                          float nw_row) {
@@ -207,202 +255,200 @@ __device__ __forceinline__ void gemm_epi(const Packed& W, const GemvOut& out, in
 }
 
 // What token j's epilogue reads besides the sum: its RMSNorm factor (STORE,
-// SWIGLU) or residual entry (RESID).  Loads for all tokens are issued before
-// the first is used.
+// SWIGLU) or this row's residual entry (RESID); 1 / 0 for j >= T.
 template <int EPI>
-__device__ __forceinline__ void epi_inputs(const Packed& W, const GemvOut& out, const NormIn& nin, int rg, int T,
-                                           float (&pre)[MX_SLOTS]) {
+__device__ __forceinline__ float epi_input(const GemvOut& out, const NormIn& nin, int64_t row, bool rv, int j, int T) {
+  if constexpr (EPI == EPI_RESID) return (j < T && rv) ? out.y[(size_t)j * out.y_tstride + row] : 0.0f;
+  else return j < T ? rnorm_from(nin, j) : 1.0f;
+}
+
+// The same in two steps, so that the loads fly under the first tile: fetch
+// this row's residual entry (RESID) or the token's sum-of-squares partials,
+// two per lane (STORE, SWIGLU), and after the main loop fold them into the
+// RMSNorm factor with the additions of rnorm_from (bitwise the same value).
+struct EpiRaw {
+  float a, b;
+};
+template <int EPI>
+__device__ __forceinline__ EpiRaw epi_fetch(const GemvOut& out, const NormIn& nin, int64_t row, bool rv, int j, int T) {
   const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)rg * RG + lane;
   if constexpr (EPI == EPI_RESID) {
-#pragma unroll
-    for (int j = 0; j < MX_SLOTS; ++j) pre[j] = (j < T && row < W.rows) ? out.y[(size_t)j * out.y_tstride + row] : 0.0f;
-  } else if (!nin.ssq) {
-#pragma unroll
-    for (int j = 0; j < MX_SLOTS; ++j) pre[j] = 1.0f;
+    return {(j < T && rv) ? out.y[(size_t)j * out.y_tstride + row] : 0.0f, 0.0f};
   } else {
-    // n_part <= 128 partial sums per token: two loads per lane
-    float a0[MX_SLOTS], a1[MX_SLOTS];
-#pragma unroll
-    for (int j = 0; j < MX_SLOTS; ++j) {
-      const float* s = nin.ssq + (size_t)j * nin.n_part;
-      a0[j] = (j < T && lane < nin.n_part) ? s[lane] : 0.0f;
-      a1[j] = (j < T && lane + 64 < nin.n_part) ? s[lane + 64] : 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < MX_SLOTS; ++j) {
-      const float a = wave_sum(a0[j] + a1[j]);
-      pre[j] = 1.0f / sqrtf(a * nin.inv_n + nin.eps);
-    }
+    if (j >= T || !nin.ssq || nin.n_part > 128) return {0.0f, 0.0f};
+    const float* s = nin.ssq + (size_t)j * nin.n_part;
+    return {lane < nin.n_part ? s[lane] : 0.0f, lane + 64 < nin.n_part ? s[lane + 64] : 0.0f};
+  }
+}
+template <int EPI>
+__device__ __forceinline__ float epi_finish(const EpiRaw& r, const NormIn& nin, int j, int T) {
+  if constexpr (EPI == EPI_RESID) {
+    return r.a;
+  } else {
+    if (j >= T || !nin.ssq) return 1.0f;
+    if (nin.n_part > 128) return rnorm_from(nin, j);
+    const float a = wave_sum(r.a + r.b);
+    return 1.0f / sqrtf(a * nin.inv_n + nin.eps);
   }
 }
 
-// Units' partials of tokens j0 .. j0+NJ-1 added in the single-token GEMV's
-// order (per split its waves in wave order, then the splits in split order,
-// from 0.0f when there are several).  NJ * U_MAX loads in flight together.
-template <int U_MAX, int NJ>
-__device__ __forceinline__ void sum_units(const float* all, int ksplit, int wsplit, int T, int j0, float (&v)[NJ]) {
-  const int lane = threadIdx.x & 63;
-  const int units = ksplit * wsplit;
-  float pv[NJ][U_MAX];
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj)
-#pragma unroll
-    for (int k = 0; k < U_MAX; ++k)
-      pv[jj][k] = (k < units && j0 + jj < T)
-                      ? __hip_atomic_load(all + ((size_t)k * T + j0 + jj) * RG + lane, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT)
-                      : 0.0f;
-#pragma unroll
-  for (int jj = 0; jj < NJ; ++jj) {
-    float tot = 0.0f, s = pv[jj][0];
-    int wj = 0;
-#pragma unroll
-    for (int k = 1; k < U_MAX; ++k) {
-      if (k < units) {
-        wj = wj + 1 == wsplit ? 0 : wj + 1;
-        if (wj == 0) {   // unit k starts the next split
-          tot = tot + s;
-          s = pv[jj][k];
-        } else {
-          s += pv[jj][k];
-        }
-      }
-    }
-    v[jj] = ksplit > 1 ? tot + s : s;
-  }
-}
-
-template <int QT, int EPI, int U_MAX, int NJ>
-__device__ __forceinline__ void finish_units(const Packed& W, const GemvOut& out, const float* all, int ksplit,
-                                             int wsplit, int T, int rg, const float (&pre)[MX_SLOTS],
-                                             float nw_row) {
-#pragma unroll
-  for (int j0 = 0; j0 < MX_SLOTS; j0 += NJ) {
-    if (j0 < T) {
-      float v[NJ];
-      sum_units<U_MAX, NJ>(all, ksplit, wsplit, T, j0, v);
-#pragma unroll
-      for (int jj = 0; jj < NJ; ++jj)
-        if (j0 + jj < T) gemm_epi<QT, EPI>(W, out, rg, j0 + jj, v[jj], pre[j0 + jj], nw_row);
-    }
-  }
-}
-
-template <int QT, int EPI>
-__global__ __launch_bounds__(GEMM_R * 64) void k_gemm(Packed W, Act x, NormIn nin, GemvOut out, int ksplit,
-                                                       int wsplit, int T, int tp) {
+template <int QT, int EPI, int NG>
+__global__ __launch_bounds__(512) void k_gemm(Packed W, Act x, NormIn nin, GemvOut out, int ksplit, int T) {
   constexpr int TBY = tile_bytes(QT);
+  constexpr int TP = 4 * NG;
+  constexpr int REGION = gemm_region(QT, TP);
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
-  const int ACTB = gemm_act_tile(QT, tp);
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
-  const int R = blockDim.x >> 6;
-  const int units = ksplit * wsplit;
-  const int u = blockIdx.x % units, grp = blockIdx.x / units;
-  const int ks_i = u / wsplit, w_j = u % wsplit;
-  const int nrg = W.nrg();
-  const int rg = grp * R + wave;
-  const bool live = rg < nrg;
+  const int nw = blockDim.x >> 6;
+  const int rg = blockIdx.x / ksplit, ks = blockIdx.x % ksplit;
   const int nblk = W.nblk(), ntiles = W.ntiles(), full = nblk / TB;
-  // the single-token GEMV's tile range of unit (ks_i, w_j)
-  const int w0 = ntiles * ks_i / ksplit, w1 = ntiles * (ks_i + 1) / ksplit;
-  const int t0 = w0 + (w1 - w0) * w_j / wsplit, t1 = w0 + (w1 - w0) * (w_j + 1) / wsplit;
-  const uint8_t* base = W.w + (size_t)(live ? rg : 0) * rg_bytes(QT, W.cols);
-  uint8_t* act0 = lds;
-  uint8_t* act1 = lds + ACTB;
-  uint8_t* my = lds + 2 * ACTB + (size_t)wave * GEMM_STAGE;
+  const int w0 = ntiles * ks / ksplit, w1 = ntiles * (ks + 1) / ksplit;
+  const int t0 = __builtin_amdgcn_readfirstlane(w0 + (w1 - w0) * wave / nw);
+  const int t1 = __builtin_amdgcn_readfirstlane(w0 + (w1 - w0) * (wave + 1) / nw);
+  const uint8_t* base = W.w + (size_t)rg * rg_bytes(QT, W.cols);
+  uint8_t* ring = lds + (size_t)wave * REGION;
   auto nb_of = [&](int t) { return t < full ? TB : nblk - full * TB; };
-
-  float acc[4][4];
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) acc[s][i] = 0.0f;
-
-  if (t0 < t1) {
-    TileRegs<QT> A, B;
-    stage_act<QT>(x, t0 * TB, nb_of(t0), tp, act0, wave, R);
-    if (live) load_tile<QT>(base + (size_t)t0 * TBY, lane, nb_of(t0), A);
-    for (int t = t0; t < t1; t += 2) {
-      // tile t: weights in A, digits in act0; tile t+1 is requested meanwhile
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (t + 1 < t1) {
-        stage_act<QT>(x, (t + 1) * TB, nb_of(t + 1), tp, act1, wave, R);
-        if (live) load_tile<QT>(base + (size_t)(t + 1) * TBY, lane, nb_of(t + 1), B);
-      }
-      if (live) tile_mma<QT>(A, nb_of(t), act0, T, tp, my, acc);
-      if (t + 1 >= t1) break;
-      // tile t+1: weights in B, digits in act1
-      __builtin_amdgcn_s_waitcnt(0);
-      __syncthreads();
-      if (t + 2 < t1) {
-        stage_act<QT>(x, (t + 2) * TB, nb_of(t + 2), tp, act0, wave, R);
-        if (live) load_tile<QT>(base + (size_t)(t + 2) * TBY, lane, nb_of(t + 2), A);
-      }
-      if (live) tile_mma<QT>(B, nb_of(t + 1), act1, T, tp, my, acc);
-    }
+  {
+    constexpr int NZ = (QT == QT_Q4 ? 12 : 6) * TP;   // 16-byte pieces of the zero area
+    u32x4* zero = reinterpret_cast<u32x4*>(ring + gemm_zero(QT, TP));
+    for (int i = lane; i < NZ; i += 64) zero[i] = u32x4{0u, 0u, 0u, 0u};
   }
-  __syncthreads();   // every wave is done with the digit buffers
-  if (!live) return;
-  const int64_t erow = (int64_t)rg * RG + lane;
-  const float nw_row = (EPI == EPI_RESID && erow < W.rows) ? out.norm_w[erow] : 0.0f;
-  const int g = lane >> 4, n = lane & 15;
 
-  if (units == 1) {
-    // the whole sum is here: to lane = row through the wave's own 4 KB
-    float pre[MX_SLOTS];
-    epi_inputs<EPI>(W, out, nin, rg, T, pre);
-    float* red = reinterpret_cast<float*>(lds + (size_t)wave * 4096);
+  float acc[NG][4];
 #pragma unroll
-    for (int s = 0; s < 4; ++s)
+  for (int g = 0; g < NG; ++g)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) red[(4 * g + i) * RG + 16 * s + n] = acc[s][i];
+    for (int i = 0; i < 4; ++i) acc[g][i] = 0.0f;
+
+  const __amdgpu_buffer_rsrc_t rs = mx_rsrc(x, QT);
+  TileRegs<QT> A, B;
+  if (t0 < t1) {
+    // prologue: tile t0's weights, then its digits into the ring (all 8
+    // slots, block 0 again past a ragged tile's end)
+    load_tile_fixed<QT>(base + (size_t)t0 * TBY, lane, nb_of(t0), A);
     SLQ_COMPILER_FENCE();
 #pragma unroll
-    for (int j = 0; j < MX_SLOTS; ++j)
-      if (j < T) gemm_epi<QT, EPI>(W, out, rg, j, red[j * RG + lane], pre[j], nw_row);
+    for (int b = 0; b < TB; ++b)
+      dma_block<QT, gemm_dpb(QT, TP)>(rs, b < nb_of(t0) ? t0 * TB + b : 0, TP, ring + b * gemm_slot(QT, TP));
+    SLQ_COMPILER_FENCE();
+  }
+
+  // The first four tokens this wave finishes (j = wave + nw q): what their
+  // epilogues read is requested now, behind the first tile, so its latency
+  // hides under the weights.
+  const int64_t erow = (int64_t)rg * RG + lane;
+  const bool erv = erow < W.rows;
+  EpiRaw raw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) raw[q] = epi_fetch<EPI>(out, nin, erow, erv, wave + nw * q, T);
+  const float nw_row = EPI == EPI_RESID ? (erv ? out.norm_w[erow] : 0.0f) : 0.0f;
+  SLQ_COMPILER_FENCE();
+
+  if (t0 < t1) {
+    // Each step loads the next tile's weights (a lane-uniform dummy after the
+    // wave's last tile) before the math of this one.
+    for (int t = t0; t < t1; t += 2) {
+      const bool n1 = t + 1 < t1;
+      load_tile_fixed<QT>(base + (size_t)(n1 ? t + 1 : t) * TBY, lane, n1 ? nb_of(t + 1) : 0, B);
+      SLQ_COMPILER_FENCE();
+      tile_diag<QT, NG>(A, nb_of(t), rs, (t + 1) * TB, n1 ? nb_of(t + 1) : 0, T, ring, acc);
+      if (!n1) break;
+      const bool n2 = t + 2 < t1;
+      load_tile_fixed<QT>(base + (size_t)(n2 ? t + 2 : t + 1) * TBY, lane, n2 ? nb_of(t + 2) : 0, A);
+      SLQ_COMPILER_FENCE();
+      tile_diag<QT, NG>(B, nb_of(t + 1), rs, (t + 2) * TB, n2 ? nb_of(t + 2) : 0, T, ring, acc);
+    }
+    // the dummy refills of the last tile still write the ring, which the
+    // reduction below reuses
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+
+  float pre[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) pre[q] = epi_finish<EPI>(raw[q], nin, wave + nw * q, T);
+
+  // Waves meet in LDS: red[token][row] in each wave's own region.  Token j is
+  // finished by wave j % nw, which adds the waves in wave order.
+  __syncthreads();
+  {
+    float* red = reinterpret_cast<float*>(ring);
+    const int rbase = 16 * ((lane & 15) >> 2) + 4 * (lane >> 4);
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[(4 * g + (lane & 3)) * RG + rbase + i] = acc[g][i];
+  }
+  __syncthreads();
+  // token j of this wave: sum of the waves' values in wave order
+  auto wave_sum_of = [&](int j) {
+    float a = reinterpret_cast<const float*>(lds)[(size_t)j * RG + lane];
+    for (int w = 1; w < nw; ++w) a += reinterpret_cast<const float*>(lds + (size_t)w * REGION)[(size_t)j * RG + lane];
+    return a;
+  };
+  auto pre_of = [&](int q, int j) {
+    return q == 0 ? pre[0] : q == 1 ? pre[1] : q == 2 ? pre[2] : q == 3 ? pre[3] : epi_input<EPI>(out, nin, erow, erv, j, T);
+  };
+  if (ksplit == 1) {
+    for (int q = 0, j = wave; j < T; ++q, j += nw) gemm_epi<QT, EPI>(W, out, rg, j, wave_sum_of(j), pre_of(q, j), nw_row);
     return;
   }
 
-  // publish this unit's partial sums [rg][u][token][row], take a ticket
-  float* mine = out.part + ((size_t)rg * units + u) * T * RG;
-#pragma unroll
-  for (int s = 0; s < 4; ++s)
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (4 * g + i < T)
-        __hip_atomic_store(mine + (size_t)(4 * g + i) * RG + 16 * s + n, acc[s][i], __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+  // Same exchange as the GEMV: partials move through agent-scope atomics,
+  // every wave's stores are complete before the workgroup takes its ticket,
+  // and the last split adds them in split order.
+  for (int j = wave; j < T; j += nw)
+    __hip_atomic_store(out.part + (((size_t)rg * ksplit + ks) * T + j) * RG + lane, wave_sum_of(j), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  unsigned ticket = 0;
-  if (lane == 0) ticket = __hip_atomic_fetch_add(out.cnt + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  ticket = __shfl(ticket, 0, 64);
-  if (ticket != (unsigned)(units - 1)) return;
-  float pre[MX_SLOTS];
-  epi_inputs<EPI>(W, out, nin, rg, T, pre);
-  const float* all = out.part + (size_t)rg * units * T * RG;
-  if (units <= 16) finish_units<QT, EPI, 16, 4>(W, out, all, ksplit, wsplit, T, rg, pre, nw_row);
-  else if (units <= 32) finish_units<QT, EPI, 32, 2>(W, out, all, ksplit, wsplit, T, rg, pre, nw_row);
-  else finish_units<QT, EPI, GEMM_MAX_UNITS, 1>(W, out, all, ksplit, wsplit, T, rg, pre, nw_row);
-  if (lane == 0) __hip_atomic_store(out.cnt + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  unsigned* tk = reinterpret_cast<unsigned*>(lds);
+  if (threadIdx.x == 0) tk[0] = __hip_atomic_fetch_add(out.cnt + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const unsigned ticket = tk[0];
+  if (ticket != (unsigned)(ksplit - 1)) return;
+  const float* all = out.part + (size_t)rg * ksplit * T * RG;
+  for (int q = 0, j = wave; j < T; ++q, j += nw) {
+    float pv[16];   // all splits' loads in flight together
+#pragma unroll
+    for (int k2 = 0; k2 < 16; ++k2)
+      pv[k2] = k2 < ksplit ? __hip_atomic_load(all + ((size_t)k2 * T + j) * RG + lane, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.0f;
+    float sum = 0.0f;
+#pragma unroll
+    for (int k2 = 0; k2 < 16; ++k2)
+      if (k2 < ksplit) sum += pv[k2];
+    gemm_epi<QT, EPI>(W, out, rg, j, sum, pre_of(q, j), nw_row);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(out.cnt + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 template <int QT, int EPI>
 hipError_t gemm_inst(const Packed& W, int T, Act x, NormIn nin, GemvOut out, int ksplit, int waves,
                      hipStream_t s) {
-  if (T < 1 || T > MX_SLOTS || ksplit < 1 || waves < 1 || waves > 8 || ksplit * waves > GEMM_MAX_UNITS)
+  if (!x.mxd || ksplit < 1 || ksplit > 16 || waves < 1 || !gemm_fits(QT, T, waves))
     return hipErrorInvalidValue;
-  const int units = ksplit * waves;
-  if (units > 1 && (!out.part || !out.cnt)) return hipErrorInvalidValue;
-  const int tp = (T + 3) & ~3;
-  const int ngrp = (W.nrg() + GEMM_R - 1) / GEMM_R;
-  k_gemm<QT, EPI><<<dim3((unsigned)(ngrp * units)), dim3(GEMM_R * 64), gemm_lds_bytes(QT, tp), s>>>(
-      W, x, nin, out, ksplit, waves, T, tp);
+  if (ksplit > 1 && (!out.part || !out.cnt)) return hipErrorInvalidValue;
+  const int ng = (T + 3) / 4;
+  const dim3 grid((unsigned)(W.nrg() * ksplit)), block(64 * waves);
+  const size_t lds = (size_t)waves * gemm_region(QT, 4 * ng);
+  switch (ng) {
+    case 1: k_gemm<QT, EPI, 1><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T); break;
+    case 2: k_gemm<QT, EPI, 2><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T); break;
+    case 3: k_gemm<QT, EPI, 3><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T); break;
+    case 4: k_gemm<QT, EPI, 4><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
+
+#define SLQ_DECLARE_GEMM(QT, EPI) \
+  extern template hipError_t gemm_inst<QT, EPI>(const Packed&, int, Act, NormIn, GemvOut, int, int, hipStream_t);
+SLQ_DECLARE_GEMM(QT_Q4, EPI_STORE) SLQ_DECLARE_GEMM(QT_Q4, EPI_SWIGLU) SLQ_DECLARE_GEMM(QT_Q4, EPI_RESID)
+SLQ_DECLARE_GEMM(QT_Q8, EPI_STORE) SLQ_DECLARE_GEMM(QT_Q8, EPI_SWIGLU) SLQ_DECLARE_GEMM(QT_Q8, EPI_RESID)
+#undef SLQ_DECLARE_GEMM
 
 }  // namespace slq

@@ -137,7 +137,8 @@ hipError_t launch_gemv(const Packed& W, int T, Act x, NormIn nin, GemvOut out, i
                        hipStream_t s) {
   if (waves < 1 || waves > 16 || ksplit < 1) return hipErrorInvalidValue;
   if (ksplit > 1 && (!out.part || !out.cnt)) return hipErrorInvalidValue;
-  if (x.fmt == 1) return launch_gemm(W, T, x, nin, out, ksplit, waves, s);
+  if (x.mxd && T >= x.min_t && gemm_usable(W.qt, T, waves))
+    return launch_gemm(W, T, x, nin, out, ksplit, waves, s);
   const bool q4 = W.qt == QT_Q4;
   switch (out.kind) {
     case EPI_STORE: return q4 ? gemv_inst<QT_Q4, EPI_STORE>(W, T, x, nin, out, ksplit, waves, s)

@@ -61,21 +61,23 @@ struct Plan {
 
 int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
 
-// Fewest tokens per call for which the int8-MFMA products beat the per-token
-// integer dot products on MI355X (measured on the 34816x5120, 5120x17408 and
-// 248320x5120 shapes): Q4_0 from 5 tokens, Q8_0 from 3.
-int mfma_min_tokens(int qtype) { return qtype == QT_Q4 ? 5 : 3; }
+// Fewest tokens per call that go to the int8-MFMA products instead of the
+// per-token integer dot products (measured on MI355X over the slice's shapes):
+// Q8_0 blocks carry twice the bytes per block of work and the products win
+// from 2 tokens; for Q4_0 the per-token dot products stay faster up to 4-7
+// tokens.  SLQ_MFMA_MIN_T overrides.
+int mfma_min_tokens(int qt) { return qt == QT_Q4 ? 8 : 2; }
 
 Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
   const int nrg = (int)((rows + RG - 1) / RG);
   const int ntiles = (int)((cols / QK + TB - 1) / TB);
   const std::string k(kind);
   Plan p;
-  // at most 8 waves per workgroup: the batched MFMA kernel uses the same
-  // split (so its sums are added in the same order) and holds 8 waves at most
   if (k == "G2" && nrg <= 128) {
-    p.w = clampi(ntiles, 1, 8);
-    p.ks = clampi((ntiles + 7) / 8, 1, 4);
+    // few row groups, long K: one workgroup per row group, up to 16 waves
+    // splitting K and meeting in LDS (no cross-workgroup exchange)
+    p.ks = 1;
+    p.w = clampi(ntiles, 1, 16);
   } else {
     p.ks = clampi((1024 + nrg - 1) / nrg, 1, ntiles < 16 ? ntiles : 16);
     if (k == "F1") p.ks = clampi(p.ks, 1, 2);
@@ -83,8 +85,7 @@ Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
     p.w = clampi(k == "GEMV" || k == "HEAD" ? (ntiles / p.ks + 1) / 2 : 4, 1, 8);
   }
   p.ks = clampi(env_int(("SLQ_KS_" + k).c_str(), p.ks), 1, 16);
-  p.w = clampi(env_int(("SLQ_W_" + k).c_str(), p.w), 1, 8);
-  p.w = clampi(p.w, 1, 64 / p.ks);   // the batched products keep ks * w <= 64 partials
+  p.w = clampi(env_int(("SLQ_W_" + k).c_str(), p.w), 1, 16);
   return p;
 }
 
@@ -112,6 +113,7 @@ struct Layout {
   size_t wbytes = 0;
   // workspace
   size_t ctrl = 0, h = 0, xa_d = 0, xa_s = 0, xu_d = 0, xu_s = 0, xm_d = 0, xm_s = 0, ssq = 0, y1 = 0,
+         xa_md = 0, xu_md = 0, xm_md = 0,
          part = 0, cnt = 0, qhat = 0, apart = 0, logits = 0, amax_v = 0, amax_i = 0, kv = 0, dn = 0;
   size_t kv_layer_bytes = 0, dn_layer_bytes = 0;
   size_t wsbytes = 0;
@@ -228,21 +230,24 @@ Layout make_layout(const slice_config& c) {
   };
   L.ctrl = take(sizeof(Ctrl));
   L.h = take((size_t)mt * H * 4);
-  // activation digits, room for either layout (one row of digits per token, or
-  // the 16-slot MFMA operand layout)
-  auto digits = [&](int nblk) { return std::max<size_t>((size_t)mt * XW * 4, mx_block_bytes(c.qtype)) * (nblk ? nblk : 1); };
-  auto scales = [&](int nblk) { return (size_t)std::max(mt, MX_SLOTS) * (nblk ? nblk : 1) * 4; };
+  // activation digits: the lane-row layout for every step, and the 16-slot
+  // MFMA layout for steps of several tokens
+  auto digits = [&](int nblk) { return (size_t)mt * XW * 4 * (nblk ? nblk : 1); };
+  auto scales = [&](int nblk) { return (size_t)mt * (nblk ? nblk : 1) * 4; };
+  auto mdigits = [&](int nblk) { return mt > 1 ? (size_t)mx_block_bytes(c.qtype) * (nblk ? nblk : 1) : 0; };
   L.xa_d = take(digits(nblkH));
   L.xa_s = take(scales(nblkH));
   L.xu_d = take(digits(nblkU));
   L.xu_s = take(scales(nblkU));
   L.xm_d = take(digits(nblkM));
   L.xm_s = take(scales(nblkM));
+  L.xa_md = take(mdigits(nblkH));
+  L.xu_md = take(mdigits(nblkU));
+  L.xm_md = take(mdigits(nblkM));
   L.ssq = take((size_t)mt * (H / RG) * 4);
   L.y1 = take((size_t)mt * (L.g1_rows_max ? L.g1_rows_max : 1) * 4);
   // split-K scratch: any GEMV of the slice with up to 16 splits
-  // (split-K workgroups x waves per row group, of which the batched MFMA
-  // products keep one partial each; the single-token GEMV keeps one per split)
+  // (one partial per split-K workgroup and token)
   int64_t rg_max = 0;
   size_t part_floats = 0;
   auto upd = [&](const Mat& m, Plan& p, const char* kind) {
@@ -250,7 +255,7 @@ Layout make_layout(const slice_config& c) {
     p = plan_gemv(kind, m.rows, m.cols);
     const int64_t nrg = (m.rows + RG - 1) / RG;
     rg_max = std::max<int64_t>(rg_max, nrg);
-    part_floats = std::max<size_t>(part_floats, (size_t)nrg * p.ks * p.w * mt * RG);
+    part_floats = std::max<size_t>(part_floats, (size_t)nrg * p.ks * mt * RG);
   };
   for (LayerLayout& ll : L.layers) {
     upd(ll.g1, ll.pg1, "G1");
@@ -314,11 +319,15 @@ struct slice {
   Ctrl* ctrl() const { return reinterpret_cast<Ctrl*>(ws + L.ctrl); }
   template <class X> X* wsp(size_t off) const { return reinterpret_cast<X*>(ws + off); }
   Packed packed(const Mat& m) const { return Packed{w + m.off, m.rows, m.cols, cfg.qtype}; }
-  int mx_min_t = 5;   // steps with at least this many tokens use the MFMA products
-  int fmt_for(int T) const { return T >= mx_min_t ? 1 : 0; }
-  Act act_a(int fmt) const { return Act{wsp<int32_t>(L.xa_d), wsp<float>(L.xa_s), cfg.hidden / QK, fmt}; }
-  Act act_u(int fmt) const { return Act{wsp<int32_t>(L.xu_d), wsp<float>(L.xu_s), (L.nu + QK - 1) / QK, fmt}; }
-  Act act_m(int fmt) const { return Act{wsp<int32_t>(L.xm_d), wsp<float>(L.xm_s), cfg.ffn / QK, fmt}; }
+  int mx_min_t = 2;   // GEMVs with at least this many tokens use the MFMA products
+  // digits of a step of T tokens; the MFMA layout is written when it is used
+  Act act(size_t d, size_t s_, size_t md, int nblk, int T) const {
+    const bool mx = T >= mx_min_t && L.mt > 1;
+    return Act{wsp<int32_t>(d), wsp<float>(s_), nblk, mx ? wsp<int32_t>(md) : nullptr, mx_min_t};
+  }
+  Act act_a(int T) const { return act(L.xa_d, L.xa_s, L.xa_md, cfg.hidden / QK, T); }
+  Act act_u(int T) const { return act(L.xu_d, L.xu_s, L.xu_md, (L.nu + QK - 1) / QK, T); }
+  Act act_m(int T) const { return act(L.xm_d, L.xm_s, L.xm_md, cfg.ffn / QK, T); }
   NormIn norm_h() const {
     return NormIn{wsp<float>(L.ssq), cfg.hidden / RG, 1.0f / (float)cfg.hidden, cfg.eps};
   }
@@ -334,7 +343,6 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
   const Layout& L = s->L;
   const int H = c.hidden;
   const int qt = c.qtype;
-  const int fmt = s->fmt_for(T);
   float* h = s->wsp<float>(L.h);
   float* ssq = s->wsp<float>(L.ssq);
   float* y1 = s->wsp<float>(L.y1);
@@ -348,7 +356,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
   };
   // entry: boundary vector -> h, digits of attn_norm(first layer) * h
   SLQ_MARK(-1);
-  if (only < 0) HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, nullptr, ctrl, H, T, H, h, attn_norm_of(0), qt, s->act_a(fmt), ssq, st));
+  if (only < 0) HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, nullptr, ctrl, H, T, H, h, attn_norm_of(0), qt, s->act_a(T), ssq, st));
   SLQ_MARK(SLICE_OP_ENTRY);
   float* part = s->wsp<float>(L.part);
   unsigned* cnt = s->wsp<unsigned>(L.cnt);
@@ -367,7 +375,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       o.part = part;
       o.cnt = cnt;
       const Plan pl = ll.pg1;
-      HIPCHK(launch_gemv(W, T, s->act_a(fmt), s->norm_h(), o, pl.ks, pl.w, st));
+      HIPCHK(launch_gemv(W, T, s->act_a(T), s->norm_h(), o, pl.ks, pl.w, st));
       SLQ_MARK(ll.attn ? SLICE_OP_ATT_IN : SLICE_OP_DN_IN);
     }
     if (only >= 0 && only != k_mix) {
@@ -391,7 +399,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       p.part = s->wsp<float>(L.apart);
       p.nchunk = L.nchunk;
       p.u_out = nullptr;
-      p.next = s->act_u(fmt);
+      p.next = s->act_u(T);
       p.next_qt = qt;
       HIPCHK(launch_attention(p, T, st));
       SLQ_MARK(SLICE_OP_ATTENTION);
@@ -408,7 +416,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       p.verify = decode ? 0 : 1;
       p.ctrl = ctrl;
       p.u_out = nullptr;
-      p.next = s->act_u(fmt);
+      p.next = s->act_u(T);
       p.next_qt = qt;
       HIPCHK(launch_deltanet(p, T, st));
       SLQ_MARK(SLICE_OP_DELTANET);
@@ -421,7 +429,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       o.kind = EPI_RESID;
       o.y = h;
       o.y_tstride = H;
-      o.next = s->act_a(fmt);
+      o.next = s->act_a(T);
       o.next_qt = qt;
       o.ssq_out = ssq;
       o.norm_w = next_norm;
@@ -430,7 +438,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       HIPCHK(launch_gemv(W, T, in, NormIn{nullptr, 0, 0.f, 0.f}, o, pl.ks, pl.w, st));
       return SLICE_OK;
     };
-    int rc = (only < 0 || only == k_out) ? residual(ll.g2, s->act_u(fmt), nw_after_mixer, ll.pg2) : SLICE_OK;
+    int rc = (only < 0 || only == k_out) ? residual(ll.g2, s->act_u(T), nw_after_mixer, ll.pg2) : SLICE_OK;
     if (rc) return rc;
     SLQ_MARK(k_out);
     if (c.ffn && (only < 0 || only == SLICE_OP_FFN_IN)) {
@@ -439,16 +447,16 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       o.kind = EPI_SWIGLU;
       o.y = nullptr;
       o.y_tstride = c.ffn;
-      o.next = s->act_m(fmt);
+      o.next = s->act_m(T);
       o.next_qt = qt;
       o.part = part;
       o.cnt = cnt;
       const Plan pl = ll.pf1;
-      HIPCHK(launch_gemv(W, T, s->act_a(fmt), s->norm_h(), o, pl.ks, pl.w, st));
+      HIPCHK(launch_gemv(W, T, s->act_a(T), s->norm_h(), o, pl.ks, pl.w, st));
       SLQ_MARK(SLICE_OP_FFN_IN);
     }
     if (c.ffn && (only < 0 || only == SLICE_OP_FFN_OUT)) {
-      rc = residual(ll.f2, s->act_m(fmt), attn_norm_of(i + 1), ll.pf2);
+      rc = residual(ll.f2, s->act_m(T), attn_norm_of(i + 1), ll.pf2);
       if (rc) return rc;
       SLQ_MARK(SLICE_OP_FFN_OUT);
     }
@@ -518,22 +526,30 @@ int slq_dequant(int qtype, const void* packed_dev, int64_t rows, int64_t cols, f
 
 // Standalone GEMV workspace: activation digits (room for both layouts), their
 // scales, split-K partials, ticket counters.
-static size_t gemv_ws_digits(int qtype, int nblk, int batch) {
-  return al256(std::max<size_t>((size_t)batch * XW * 4, mx_block_bytes(qtype)) * nblk);
-}
-static size_t gemv_ws_scales(int nblk, int batch) { return al256((size_t)std::max(batch, MX_SLOTS) * nblk * 4); }
-
-static size_t gemv_ws_part(int64_t rows, int64_t cols, int batch) {
+// Standalone GEMV workspace, in order: lane-row digits [batch][nblk][24],
+// their scales, MFMA-layout block records, split-K partials
+// [nrg][ks][batch][64], ticket counters [nrg].
+struct GemvWs {
+  size_t dig, sc, mdig, part, cnt, total;
+};
+static GemvWs gemv_ws(int qtype, int64_t rows, int64_t cols, int batch) {
+  const int nblk = (int)(cols / QK);
+  const int64_t nrg = (rows + RG - 1) / RG;
   const Plan p = plan_gemv("GEMV", rows, cols);
-  return al256((size_t)((rows + RG - 1) / RG) * p.ks * p.w * batch * RG * 4);
+  GemvWs w{};
+  size_t o = 0;
+  w.dig = o; o += al256((size_t)batch * nblk * XW * 4);
+  w.sc = o; o += al256((size_t)batch * nblk * 4);
+  w.mdig = o; o += al256((size_t)nblk * mx_block_bytes(qtype));
+  w.part = o; o += al256((size_t)nrg * p.ks * batch * RG * 4);
+  w.cnt = o; o += al256((size_t)nrg * 4);
+  w.total = o;
+  return w;
 }
 
 size_t slq_gemv_workspace_bytes(int qtype, int64_t rows, int64_t cols, int batch) {
   if (!slq_packed_bytes(qtype, rows, cols) || batch < 1 || batch > MAX_T) return 0;
-  const int nblk = (int)(cols / QK);
-  const int64_t nrg = (rows + RG - 1) / RG;
-  return gemv_ws_digits(qtype, nblk, batch) + gemv_ws_scales(nblk, batch) + gemv_ws_part(rows, cols, batch) +
-         al256((size_t)nrg * 4);
+  return gemv_ws(qtype, rows, cols, batch).total;
 }
 
 int slq_gemv(int qtype, const void* packed_dev, int64_t rows, int64_t cols, int batch, const float* x_dev,
@@ -544,12 +560,13 @@ int slq_gemv(int qtype, const void* packed_dev, int64_t rows, int64_t cols, int 
   if (!packed_dev || !x_dev || !y_dev || !ws_dev) return fail(SLICE_EINVAL, "slq_gemv: null pointer");
   const int nblk = (int)(cols / QK);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
-  const int fmt = batch >= clampi(env_int("SLQ_MFMA_MIN_T", mfma_min_tokens(qtype)), 1, MAX_T + 1) ? 1 : 0;
-  const size_t dig = gemv_ws_digits(qtype, nblk, batch);
-  Act a{reinterpret_cast<int32_t*>(ws), reinterpret_cast<float*>(ws + dig), nblk, fmt};
-  const int64_t nrg = (rows + RG - 1) / RG;
-  float* part = reinterpret_cast<float*>(ws + dig + gemv_ws_scales(nblk, batch));
-  unsigned* cnt = reinterpret_cast<unsigned*>(reinterpret_cast<uint8_t*>(part) + gemv_ws_part(rows, cols, batch));
+  const GemvWs L = gemv_ws(qtype, rows, cols, batch);
+  const int min_t = clampi(env_int("SLQ_MFMA_MIN_T", mfma_min_tokens(qtype)), 1, MAX_T + 1);
+  const bool mx = batch >= min_t;
+  Act a{reinterpret_cast<int32_t*>(ws + L.dig), reinterpret_cast<float*>(ws + L.sc), nblk,
+        mx ? reinterpret_cast<int32_t*>(ws + L.mdig) : nullptr, min_t};
+  float* part = reinterpret_cast<float*>(ws + L.part);
+  unsigned* cnt = reinterpret_cast<unsigned*>(ws + L.cnt);
   HIPCHK(launch_quant_act(qtype, x_dev, batch, (int)cols, cols, a, S(stream)));
   const Plan pl = plan_gemv("GEMV", rows, cols);
   const Packed W{static_cast<const uint8_t*>(packed_dev), rows, cols, qtype};
@@ -759,7 +776,7 @@ int slice_head_argmax(slice_t* s, const void* in, int32_t* tok, float* logits, v
   const hipStream_t st = S(stream);
   float* lg = logits ? logits : s->wsp<float>(L.logits);
   HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, in, nullptr, c.hidden, 1, c.hidden, s->wsp<float>(L.h),
-                             reinterpret_cast<const float*>(s->w + L.out_norm), c.qtype, s->act_a(s->fmt_for(1)),
+                             reinterpret_cast<const float*>(s->w + L.out_norm), c.qtype, s->act_a(1),
                              s->wsp<float>(L.ssq), st));
   const Packed W = s->packed(c.tied_head ? L.embed : L.head);
   GemvOut o{};
@@ -769,7 +786,7 @@ int slice_head_argmax(slice_t* s, const void* in, int32_t* tok, float* logits, v
   o.part = s->wsp<float>(L.part);
   o.cnt = s->wsp<unsigned>(L.cnt);
   const Plan pl = L.phead;
-  HIPCHK(launch_gemv(W, 1, s->act_a(s->fmt_for(1)), s->norm_h(), o, pl.ks, pl.w, st));
+  HIPCHK(launch_gemv(W, 1, s->act_a(1), s->norm_h(), o, pl.ks, pl.w, st));
   HIPCHK(launch_argmax(lg, c.vocab, s->wsp<float>(L.amax_v), s->wsp<int>(L.amax_i), L.amax_parts, tok, st));
   return SLICE_OK;
 }

@@ -48,25 +48,28 @@ inline size_t packed_bytes(int qt, int64_t rows, int64_t cols) {
 // digits in [-128,127]) and packed in the order the weight codes use, so the
 // GEMV takes exact integer dot products of codes and digits.
 //
-// Two layouts of the same digits:
-//   fmt 0 (one token per lane-row GEMV): xd [T][nblk][24 dwords], xs [T][nblk].
-//   fmt 1 (MFMA operand order, 16 token slots): per block, 12 chunks c of
-//     16 slots x 16 bytes (Q4_0) or 16 slots x 8 bytes (Q8_0); slot = token.
-//     Q4_0: c = 4p + g, p = 0..2 digit pair, g = 0..3; byte j of chunk (p, g) is
-//           digit 2p of element 16(g&1)+j for g < 2 and 16 * digit 2p+1 of that
-//           element for g >= 2 (so one 64-deep int8 MFMA takes two digits).
-//     Q8_0: c = 4p + g, p = 0..2 digit, g = 0..3; byte j of chunk (p, g) is
-//           digit p of element 8g+j.
-//     xs [nblk][16].
+// Two layouts of the same digits (a producer writes both when mxd is set):
+//   lane-row layout (single-token GEMV): xd [T][nblk][24 dwords], xs [T][nblk].
+//   MFMA layout (batched products, 16 token slots): one record per block of
+//     NCH chunks of 16 slots x 16 bytes (slot = token), then the 16 token
+//     scales (fp32), so that one buffer holds everything a block needs.
+//     Q4_0 (NCH 12): c = 4p + g, p = 0..2 digit pair, g = 0..3; byte j of chunk
+//           (p, g) is digit 2p of element 16(g&1)+j for g < 2 and 16 * digit 2p+1
+//           of that element for g >= 2 (one 64-deep int8 MFMA takes two digits).
+//     Q8_0 (NCH 6): c = 2p + h, p = 0..2 digit; byte j is digit p of element 16h+j.
 struct Act {
   int32_t* xd;
   float* xs;
   int nblk;      // blocks per token
-  int fmt;       // 0 or 1, see above
+  int32_t* mxd;  // MFMA layout records, or nullptr (not written)
+  int min_t;     // calls with at least this many tokens use the MFMA products (when they fit)
 };
 constexpr int MX_SLOTS = 16;
-// Bytes of the digit array of one block in fmt 1.
-__host__ __device__ constexpr int mx_block_bytes(int qt) { return 12 * MX_SLOTS * (qt == QT_Q4 ? 16 : 8); }
+__host__ __device__ constexpr int mx_chunks(int qt) { return qt == QT_Q4 ? 12 : 6; }
+// Bytes of one block's MFMA-layout record: digits, then the token scales at
+// byte mx_scale_off(qt).
+__host__ __device__ constexpr int mx_scale_off(int qt) { return mx_chunks(qt) * MX_SLOTS * 16; }
+__host__ __device__ constexpr int mx_block_bytes(int qt) { return mx_scale_off(qt) + MX_SLOTS * 4; }
 
 constexpr float M_Q4 = 7829367.0f;   // 7 * 0x111111
 constexpr float M_Q8 = 8355711.0f;   // 127 * 0x010101
@@ -114,11 +117,13 @@ hipError_t launch_dequant(const Packed& W, float* out, hipStream_t s);
 // x fp32 [T][n] -> digits; optional ssq partials [T][nrg] of x (not of w*x).
 hipError_t launch_quant_act(int qt, const float* x, int T, int n, int64_t x_tstride, Act a,
                             hipStream_t s);
-// Dispatches on x.fmt: fmt 0 -> one-row-per-lane GEMV, fmt 1 -> int8 MFMA product.
+// The int8-MFMA product when x carries MFMA-layout digits, T >= x.min_t and
+// its LDS fits; otherwise the one-row-per-lane GEMV.  Same results either way.
 hipError_t launch_gemv(const Packed& W, int T, Act x, NormIn nin, GemvOut out, int ksplit,
                        int waves, hipStream_t s);
 hipError_t launch_gemm(const Packed& W, int T, Act x, NormIn nin, GemvOut out, int ksplit,
                        int waves, hipStream_t s);
+bool gemm_usable(int qt, int T, int waves);
 // h [T][H] = boundary input, then digits of norm_w*h and ssq partials.
 // in_kind: 1 = fp16 input, 2 = fp32 input; with in == nullptr the input pointer
 // is read from ctrl->in.
