@@ -5,17 +5,17 @@
 // partial RoPE, QK-norm and a sigmoid output gate.  Each stage keeps its own
 // KV cache ("Unstable Legion", section "Splitting the workload").
 //
-// Three kernels per layer:
-//   prep:    per query/KV head: RMSNorm (if QK-norm), RoPE on the first
-//            rope_dims entries (angle pos * theta^(-2i/r) taken in fp64),
-//            q scaled by 1/sqrt(head_dim); K/V row p+t rounded to fp16 and
-//            appended to the cache.
-//   split:   one workgroup per (KV head, 64-row chunk); scores of the group's
-//            query heads against the chunk, chunk-local max / sum of exp and
-//            the unnormalised P V.  Query t (position p+t) sees rows <= p+t.
+// Two kernels per layer:
+//   split:   one workgroup per (KV head, 32-row chunk).  It first appends the
+//            K/V rows of this step that fall in its chunk (RMSNorm if QK-norm,
+//            RoPE on the first rope_dims entries with the angle
+//            pos * theta^(-2i/r) taken in fp64, fp16 rounding), then prepares
+//            its query heads the same way (q also scaled by 1/sqrt(head_dim)),
+//            and computes the chunk-local max / sum of exp and the
+//            unnormalised P V.  Query t (position p+t) sees rows <= p+t.
 //   combine: per (token, query head): merge the chunks' partials, apply the
 //            gate sigmoid(g), and quantise the result for the output GEMV.
-// Chunk boundaries are absolute (multiples of 64), so query t of a verify
+// Chunk boundaries are absolute (multiples of 32), so query t of a verify
 // pass is computed with exactly the operations a decode at p+t would use.
 //
 // K cache layout: [kv][pos/64][head_dim/8][64 pos][8] (a wave reads 64 rows'
@@ -29,90 +29,165 @@ __device__ __forceinline__ size_t kidx(int g, int pos, int d, int max_seq, int h
   return ((((size_t)g * ntile + pos / 64) * (hd / 8) + d / 8) * 64 + (pos % 64)) * 8 + (d % 8);
 }
 
-__global__ __launch_bounds__(256) void k_attn_prep(AttnParams p) {
-  __shared__ float buf[256];
-  __shared__ float wred[4];
-  const int nh = p.q_heads + p.kv_heads;
-  const int t = blockIdx.x / nh, hh = blockIdx.x % nh;
-  const int d = threadIdx.x;
-  const int pos = p.ctrl->pos + t;
-  const float* y = p.y + (size_t)t * p.y_stride;
-  const bool isq = hh < p.q_heads;
-  const int kvh = hh - p.q_heads;
-  float x = isq ? y[p.off_q + hh * p.hd + d] : y[p.off_k + kvh * p.hd + d];
-  if (p.qk_norm) {
-    const float ss = wave_sum(x * x);
-    if ((d & 63) == 0) wred[d >> 6] = ss;
-    __syncthreads();
-    float tot = 0.0f;
-    for (int w = 0; w < (p.hd >> 6); ++w) tot += wred[w];
-    const float rn = 1.0f / sqrtf(tot / (float)p.hd + p.eps);
-    x = x * rn * (isq ? p.q_norm[d] : p.k_norm[d]);
-  }
-  buf[d] = x;
-  __syncthreads();
+// Table of the RoPE rotations, built once at load: entry (pos, i) holds cos
+// and sin of the angle pos * theta^(-2i/r), taken in fp64.
+__global__ void k_rope_table(float* cs, int max_seq, int rope_dims, double theta) {
+  const int half = rope_dims / 2;
+  const size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= (size_t)max_seq * half) return;
+  const int pos = (int)(idx / half), i = (int)(idx % half);
+  const double ang = (double)pos * pow(theta, -2.0 * (double)i / (double)rope_dims);
+  cs[2 * idx] = (float)cos(ang);
+  cs[2 * idx + 1] = (float)sin(ang);
+}
+
+hipError_t launch_rope_table(float* cs, int max_seq, int rope_dims, double theta, hipStream_t s) {
+  const size_t n = (size_t)max_seq * (rope_dims / 2);
+  if (n == 0) return hipSuccess;
+  k_rope_table<<<(unsigned)((n + 255) / 256), 256, 0, s>>>(cs, max_seq, rope_dims, theta);
+  return hipGetLastError();
+}
+
+// Rotation of entry d at position pos (identity past rope_dims).
+__device__ __forceinline__ void rope_cs(const AttnParams& p, int d, int pos, float& c, float& sn) {
+  c = 1.0f;
+  sn = 0.0f;
   if (d < p.rope_dims) {
     const int half = p.rope_dims / 2;
-    const int i = d % half;
-    const double ang = (double)pos * pow(p.rope_theta, -2.0 * (double)i / (double)p.rope_dims);
-    const float c = (float)cos(ang), sn = (float)sin(ang);
-    if (d < half) x = buf[d] * c - buf[d + half] * sn;
-    else x = buf[d] * c + buf[d - half] * sn;
-  }
-  if (isq) {
-    p.qhat[((size_t)t * p.q_heads + hh) * p.hd + d] = x * (1.0f / sqrtf((float)p.hd));
-  } else {
-    p.kc[kidx(kvh, pos, d, p.max_seq, p.hd)] = __float2half_rn(x);
-    p.vc[((size_t)kvh * p.max_seq + pos) * p.hd + d] = __float2half_rn(y[p.off_v + kvh * p.hd + d]);
+    const float* e = p.rope_cs + 2 * ((size_t)pos * half + d % half);
+    c = e[0];
+    sn = e[1];
   }
 }
 
-// One workgroup per (KV head g, 64-row chunk c), 4 waves.  Scores: wave w
-// takes rows 16w..16w+15 of the chunk, 4 lanes per row each over a quarter of
-// the head dimensions, summed with two butterfly steps.  P V: one thread per
-// head dimension over the chunk's rows.
-template <int GRP, int HD>
+// RMSNorm (when enabled) and RoPE of NH head vectors held one entry per
+// thread (x[h] = entry d of head h for d < hd, 0 elsewhere), all rotated by
+// (c, sn) of entry d.  Every thread of the workgroup calls it: buf (NH * hd
+// floats) and wred (4 x NH floats) are LDS, free again on return.
+template <int NH>
+__device__ __forceinline__ void heads_prep(float (&x)[NH], int d, const AttnParams& p, const float* norm_w, float c,
+                                           float sn, float* buf, float (*wred)[8]) {
+  const bool act = d < p.hd;
+  if (p.qk_norm) {
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const float ss = wave_sum(x[h] * x[h]);
+      if ((d & 63) == 0) wred[d >> 6][h] = ss;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      float tot = 0.0f;
+      for (int w = 0; w < (p.hd >> 6); ++w) tot += wred[w][h];
+      const float rn = 1.0f / sqrtf(tot / (float)p.hd + p.eps);
+      x[h] = act ? x[h] * rn * norm_w[d] : 0.0f;
+    }
+  }
+#pragma unroll
+  for (int h = 0; h < NH; ++h)
+    if (act) buf[h * p.hd + d] = x[h];
+  __syncthreads();
+  if (act && d < p.rope_dims) {
+    const int half = p.rope_dims / 2;
+#pragma unroll
+    for (int h = 0; h < NH; ++h) {
+      const float* b = buf + h * p.hd;
+      x[h] = d < half ? b[d] * c - b[d + half] * sn : b[d] * c + b[d - half] * sn;
+    }
+  }
+  __syncthreads();
+}
+
+// One workgroup per (KV head g, group of HPW of its query heads, 32-row chunk
+// c), 4 waves.  Scores: thread
+// (row rr = tid / 8, part = tid % 8) takes an eighth of the head dimensions
+// of key row rr, the eight parts meeting with three butterfly steps.  P V:
+// one thread per head dimension over the chunk's rows.  The chunk's keys and
+// values are requested once, before the query preparation, and serve every
+// token of the pass.
+template <int GRP, int HD>   // GRP: query heads per workgroup
 __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   constexpr int C = ATT_CHUNK;
-  __shared__ __attribute__((aligned(16))) float pl[GRP][C];
+  constexpr int NC = HD / 64;   // 8-dim pieces per eighth of the head
   __shared__ __attribute__((aligned(16))) float qsh[GRP * HD];
+  __shared__ __attribute__((aligned(16))) float pl[GRP][C];
+  __shared__ float buf[GRP * HD];
+  __shared__ float wred[4][8];
   __shared__ float wm[4][GRP];
-  const int g = blockIdx.x / p.nchunk, c = blockIdx.x % p.nchunk;
+  const int nsub = p.q_heads / p.kv_heads / GRP;   // query-head groups per KV head
+  const int g = blockIdx.x / (nsub * p.nchunk);
+  const int sub = (blockIdx.x / p.nchunk) % nsub, c = blockIdx.x % p.nchunk;
+  const int h0 = (g * nsub + sub) * GRP;            // first query head of this workgroup
   const int p0 = p.ctrl->pos;
   const int r0 = c * C;
   if (r0 > p0 + T - 1) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
-  const int rr = wave * 16 + (lane & 15);      // row of this lane inside the chunk
-  const int dq = lane >> 4;                    // quarter of the head dimensions
-  constexpr int NC = HD / 32;                  // 8-dim pieces per quarter of the head
+  const bool dact = tid < HD;
+
+  // this step's K/V rows inside the chunk: positions p0 + t in [r0, r0 + C).
+  // Every query-head group of the chunk computes and stores them itself
+  // (the same bits), so each reads them back after its own stores.
+  const int ta = max(0, r0 - p0), tb = min(T, r0 + C - p0);
+  for (int t = ta; t < tb; ++t) {
+    const float* y = p.y + (size_t)t * p.y_stride;
+    const int pos = p0 + t;
+    float k[1] = {dact ? y[p.off_k + g * HD + tid] : 0.0f};
+    const float vx = dact ? y[p.off_v + g * HD + tid] : 0.0f;
+    float c, sn;
+    rope_cs(p, tid, pos, c, sn);
+    heads_prep<1>(k, tid, p, p.k_norm, c, sn, buf, wred);
+    if (dact) {
+      p.kc[kidx(g, pos, tid, p.max_seq, HD)] = __float2half_rn(k[0]);
+      p.vc[((size_t)g * p.max_seq + pos) * HD + tid] = __float2half_rn(vx);
+    }
+  }
+  if (tb > ta) {
+    __threadfence_block();
+    __syncthreads();
+  }
+
+  // the chunk's keys (this thread's eighth of row rr) and values (dimension
+  // tid of every row); rows past the valid ones lie inside the cache and get
+  // weight 0
+  const int rr = tid >> 3, part = tid & 7;
   const int r = r0 + rr;
+  uint4 kw[NC];
+#pragma unroll
+  for (int i = 0; i < NC; ++i)
+    kw[i] = *reinterpret_cast<const uint4*>(p.kc + kidx(g, r, (part * NC + i) * 8, p.max_seq, HD));
+  unsigned short vv[C];
+  {
+    const unsigned short* vrow =
+        reinterpret_cast<const unsigned short*>(p.vc) + ((size_t)g * p.max_seq + r0) * HD + (dact ? tid : 0);
+#pragma unroll
+    for (int q = 0; q < C; ++q) vv[q] = vrow[(size_t)q * HD];
+  }
+
   for (int t = 0; t < T; ++t) {
     const int P = p0 + t;
     const int nvalid = min(C, P + 1 - r0);
     if (nvalid <= 0) continue;
     {
-      const float* qg = p.qhat + ((size_t)t * p.q_heads + g * GRP) * p.hd;
-      float qv[GRP];
+      const float* y = p.y + (size_t)t * p.y_stride;
+      float qx[GRP];
 #pragma unroll
-      for (int h = 0; h < GRP; ++h) qv[h] = tid < HD ? qg[h * HD + tid] : 0.0f;
+      for (int h = 0; h < GRP; ++h) qx[h] = dact ? y[p.off_q + (h0 + h) * HD + tid] : 0.0f;
+      float c, sn;
+      rope_cs(p, tid, P, c, sn);
+      heads_prep<GRP>(qx, tid, p, p.q_norm, c, sn, buf, wred);
 #pragma unroll
       for (int h = 0; h < GRP; ++h)
-        if (tid < HD) qsh[h * HD + tid] = qv[h];
+        if (dact) qsh[h * HD + tid] = qx[h] * (1.0f / sqrtf((float)HD));
     }
     __syncthreads();
     float s[GRP];
 #pragma unroll
     for (int h = 0; h < GRP; ++h) s[h] = 0.0f;
     if (rr < nvalid) {
-      // this lane's NC pieces of the key row, all requested before any math
-      uint4 kw[NC];
-#pragma unroll
-      for (int i = 0; i < NC; ++i)
-        kw[i] = *reinterpret_cast<const uint4*>(p.kc + kidx(g, r, (dq * NC + i) * 8, p.max_seq, HD));
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
-        const int dc = dq * NC + i;
+        const int dc = part * NC + i;
         float kf[8];
         const uint32_t ws[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
 #pragma unroll
@@ -133,14 +208,16 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
           s[h] = __builtin_fmaf(kf[6], qb.z, s[h]);
           s[h] = __builtin_fmaf(kf[7], qb.w, s[h]);
         }
+        asm volatile("" ::: "memory");   // one piece's query values in registers at a time
       }
     }
 #pragma unroll
     for (int h = 0; h < GRP; ++h) {
-      s[h] += __shfl_xor(s[h], 16, 64);
-      s[h] += __shfl_xor(s[h], 32, 64);
+      s[h] += __shfl_xor(s[h], 1, 64);
+      s[h] += __shfl_xor(s[h], 2, 64);
+      s[h] += __shfl_xor(s[h], 4, 64);
     }
-    // chunk max per head
+    // chunk max per head (each wave holds 8 rows)
 #pragma unroll
     for (int h = 0; h < GRP; ++h) {
       const float v = wave_max(rr < nvalid ? s[h] : -INFINITY);
@@ -155,45 +232,41 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
 #pragma unroll
     for (int h = 0; h < GRP; ++h) {
       const float e = rr < nvalid ? __expf(s[h] - m[h]) : 0.0f;
-      if (dq == 0) pl[h][rr] = e;
-      // each row's weight appears on 4 lanes; count it once
-      const float v = wave_sum(dq == 0 ? e : 0.0f);
+      if (part == 0) pl[h][rr] = e;
+      // each row's weight appears on 8 lanes; count it once
+      const float v = wave_sum(part == 0 ? e : 0.0f);
       if (lane == 0) wm[wave][h] = v;
     }
     __syncthreads();
 #pragma unroll
     for (int h = 0; h < GRP; ++h) l[h] = (wm[0][h] + wm[1][h]) + (wm[2][h] + wm[3][h]);
-    // P V: thread = dimension
-    if (tid < HD) {
+    if (dact) {
       float o[GRP];
 #pragma unroll
       for (int h = 0; h < GRP; ++h) o[h] = 0.0f;
-      const __half* vrow = p.vc + ((size_t)g * p.max_seq + r0) * HD + tid;
-      // rows past nvalid have weight 0 and lie inside the cache (r0 + C <= max_seq)
-      for (int q0 = 0; q0 < nvalid; q0 += 16) {
-        float v[16];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) v[u] = __half2float(vrow[(size_t)(q0 + u) * HD]);
+      for (int q = 0; q < C; q += 4) {
+        float v[4];
 #pragma unroll
-        for (int u = 0; u < 16; u += 4) {
+        for (int u = 0; u < 4; ++u) v[u] = q + u < nvalid ? __half2float(__ushort_as_half(vv[q + u])) : 0.0f;
 #pragma unroll
-          for (int h = 0; h < GRP; ++h) {
-            const float4 w4 = *reinterpret_cast<const float4*>(&pl[h][q0 + u]);
-            o[h] = __builtin_fmaf(w4.x, v[u], o[h]);
-            o[h] = __builtin_fmaf(w4.y, v[u + 1], o[h]);
-            o[h] = __builtin_fmaf(w4.z, v[u + 2], o[h]);
-            o[h] = __builtin_fmaf(w4.w, v[u + 3], o[h]);
-          }
+        for (int h = 0; h < GRP; ++h) {
+          const float4 w = *reinterpret_cast<const float4*>(&pl[h][q]);
+          o[h] = __builtin_fmaf(w.x, v[0], o[h]);
+          o[h] = __builtin_fmaf(w.y, v[1], o[h]);
+          o[h] = __builtin_fmaf(w.z, v[2], o[h]);
+          o[h] = __builtin_fmaf(w.w, v[3], o[h]);
         }
+        asm volatile("" ::: "memory");   // four rows' weights in registers at a time
       }
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
-        float* dst = p.part + (((size_t)t * p.q_heads + g * GRP + h) * p.nchunk + c) * (HD + 2);
+        float* dst = p.part + (((size_t)t * p.q_heads + h0 + h) * p.nchunk + c) * (HD + 2);
         dst[2 + tid] = o[h];
         if (tid == 0) { dst[0] = m[h]; dst[1] = l[h]; }
       }
     }
-    __syncthreads();
+    __syncthreads();   // qsh, pl and wm are rewritten by the next token
   }
 }
 
@@ -202,7 +275,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
 // chunk c's max and sum (several rounds beyond 64 chunks), the weights
 // exp(m_c - M) go through LDS, and every lane then folds its dimension.
 __global__ __launch_bounds__(64) void k_attn_combine(AttnParams p) {
-  __shared__ float wsh[1024];
+  __shared__ float wsh[2048];
   const int ndg = p.hd / 64;
   const int t = blockIdx.x / (p.q_heads * ndg);
   const int h = (blockIdx.x / ndg) % p.q_heads;
@@ -224,7 +297,7 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnParams p) {
       l = base[(size_t)c * stride + 1];
     }
     L += wave_sum(l * w);
-    if (c < nc && c < 1024) wsh[c] = w;
+    if (c < nc && c < 2048) wsh[c] = w;
   }
   __syncthreads();
   float o = 0.0f;
@@ -237,7 +310,7 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnParams p) {
     for (int u = 0; u < 8; ++u) {
       const int c = c0 + u;
       if (c < nc) {
-        const float w = c < 1024 ? wsh[c] : __expf(base[(size_t)c * stride] - M);
+        const float w = c < 2048 ? wsh[c] : __expf(base[(size_t)c * stride] - M);
         o = __builtin_fmaf(v[u], w, o);
       }
     }
@@ -252,19 +325,21 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnParams p) {
 
 hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {
   if (p.hd % 64 || p.hd > 256 || p.rope_dims % 2 || p.rope_dims > p.hd || p.max_seq % 64 ||
+      p.nchunk * ATT_CHUNK < p.max_seq || (p.rope_dims && !p.rope_cs) ||
       p.q_heads % p.kv_heads)
     return hipErrorInvalidValue;
-  k_attn_prep<<<T * (p.q_heads + p.kv_heads), p.hd, 0, s>>>(p);
+  // query heads per split workgroup: at most 2 of a KV head's group, so that
+  // the work of a chunk spreads over several workgroups
   const int grp = p.q_heads / p.kv_heads;
-  const unsigned grid = (unsigned)(p.kv_heads * p.nchunk);
+  const int hpw = grp % 2 == 0 ? 2 : 1;
+  const unsigned grid = (unsigned)(p.kv_heads * (grp / hpw) * p.nchunk);
 #define SLQ_G(n, hd) case n: k_attn_split<n, hd><<<grid, 256, 0, s>>>(p, T); break;
-#define SLQ_HD(hd)                                                                        \
-  case hd:                                                                                \
-    switch (grp) {                                                                        \
-      SLQ_G(1, hd) SLQ_G(2, hd) SLQ_G(3, hd) SLQ_G(4, hd) SLQ_G(5, hd) SLQ_G(6, hd)       \
-      SLQ_G(7, hd) SLQ_G(8, hd)                                                           \
-      default: return hipErrorInvalidValue;                                               \
-    }                                                                                     \
+#define SLQ_HD(hd)                                          \
+  case hd:                                                  \
+    switch (hpw) {                                          \
+      SLQ_G(1, hd) SLQ_G(2, hd)                             \
+      default: return hipErrorInvalidValue;                 \
+    }                                                       \
     break;
   switch (p.hd) {
     SLQ_HD(64) SLQ_HD(128) SLQ_HD(192) SLQ_HD(256)

@@ -87,20 +87,6 @@ __device__ __forceinline__ uint32_t sext_nibbles(uint32_t t) {
 
 #define SLQ_COMPILER_FENCE() asm volatile("" ::: "memory")
 
-// A tile's weights into registers with always TB * NH + 1 loads, whatever the
-// tile: the codes of a ragged tile (nb < TB) repeat its last block, and nb = 0
-// (no tile) reads the first 16 bytes at tile from every lane.  Every path thus
-// issues the same loads, which keeps the compiler's own waits on these
-// registers (and the explicit ring waits) exact.
-template <int QT>
-__device__ __forceinline__ void load_tile_fixed(const uint8_t* tile, int lane, int nb, TileRegs<QT>& r) {
-  constexpr int NH = TileRegs<QT>::NH;
-  const int nc = nb * NH;
-  const u32x4* cp = reinterpret_cast<const u32x4*>(tile) + (nb ? lane : 0);
-#pragma unroll
-  for (int b = 0; b < TB * NH; ++b) r.c[b] = __builtin_nontemporal_load(cp + (nb ? (b < nc ? b : nc - 1) : 0) * RG);
-  r.sc = __builtin_nontemporal_load(nb ? reinterpret_cast<const u32x4*>(tile + (size_t)nc * RG * 16) + lane : cp);
-}
 
 // Digits (token slots 0..tp-1) and scales of block blk into a ring slot:
 // piece q < NCH*tp is chunk q / tp, slot q % tp; the last 4 pieces are the

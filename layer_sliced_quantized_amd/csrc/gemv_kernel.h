@@ -31,6 +31,21 @@ __device__ __forceinline__ void load_tile(const uint8_t* tile, int lane, int nb,
   r.sc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + (size_t)nb * NH * RG * 16) + lane);
 }
 
+// A tile's weights into registers with always TB * NH + 1 loads, whatever the
+// tile: the codes of a ragged tile (nb < TB) repeat its last block, and nb = 0
+// (no tile) reads the first 16 bytes at tile from every lane.  Every path thus
+// issues the same loads, which keeps the compiler's own waits on these
+// registers (and the explicit ring waits) exact.
+template <int QT>
+__device__ __forceinline__ void load_tile_fixed(const uint8_t* tile, int lane, int nb, TileRegs<QT>& r) {
+  constexpr int NH = TileRegs<QT>::NH;
+  const int nc = nb * NH;
+  const u32x4* cp = reinterpret_cast<const u32x4*>(tile) + (nb ? lane : 0);
+#pragma unroll
+  for (int b = 0; b < TB * NH; ++b) r.c[b] = __builtin_nontemporal_load(cp + (nb ? (b < nc ? b : nc - 1) : 0) * RG);
+  r.sc = __builtin_nontemporal_load(nb ? reinterpret_cast<const u32x4*>(tile + (size_t)nc * RG * 16) + lane : cp);
+}
+
 __device__ __forceinline__ float scale_of(const u32x4& sc, int b) {
   const uint32_t w = b < 2 ? sc.x : b < 4 ? sc.y : b < 6 ? sc.z : sc.w;
   const unsigned short hb = (unsigned short)((b & 1) ? (w >> 16) : (w & 0xffff));

@@ -114,7 +114,7 @@ struct Layout {
   // workspace
   size_t ctrl = 0, h = 0, xa_d = 0, xa_s = 0, xu_d = 0, xu_s = 0, xm_d = 0, xm_s = 0, ssq = 0, y1 = 0,
          xa_md = 0, xu_md = 0, xm_md = 0,
-         part = 0, cnt = 0, qhat = 0, apart = 0, logits = 0, amax_v = 0, amax_i = 0, kv = 0, dn = 0;
+         part = 0, cnt = 0, apart = 0, rope = 0, logits = 0, amax_v = 0, amax_i = 0, kv = 0, dn = 0;
   size_t kv_layer_bytes = 0, dn_layer_bytes = 0;
   size_t wsbytes = 0;
   int64_t g1_rows_max = 0;
@@ -268,8 +268,8 @@ Layout make_layout(const slice_config& c) {
   L.cnt = take((size_t)std::max<int64_t>(rg_max, 1) * 4);
   if (L.n_attn) {
     L.nchunk = (c.max_seq + ATT_CHUNK - 1) / ATT_CHUNK;
-    L.qhat = take((size_t)mt * nq * 4);
     L.apart = take((size_t)mt * c.q_heads * L.nchunk * (c.head_dim + 2) * 4);
+    L.rope = take((size_t)c.max_seq * (c.rope_dims / 2 > 0 ? c.rope_dims / 2 : 1) * 8);
   }
   if (c.has_head) {
     L.logits = take((size_t)c.vocab * 4);
@@ -386,6 +386,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       p.off_q = ll.off_q; p.off_g = ll.off_g; p.off_k = ll.off_k; p.off_v = ll.off_v;
       p.q_heads = c.q_heads; p.kv_heads = c.kv_heads; p.hd = c.head_dim; p.rope_dims = c.rope_dims;
       p.rope_theta = c.rope_theta;
+      p.rope_cs = s->wsp<float>(L.rope);
       p.qk_norm = c.qk_norm;
       p.q_norm = reinterpret_cast<const float*>(s->w + ll.q_norm);
       p.k_norm = reinterpret_cast<const float*>(s->w + ll.k_norm);
@@ -395,7 +396,6 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       p.vc = reinterpret_cast<__half*>(kvb + (size_t)c.kv_heads * c.max_seq * c.head_dim * 2);
       p.max_seq = c.max_seq;
       p.ctrl = ctrl;
-      p.qhat = s->wsp<float>(L.qhat);
       p.part = s->wsp<float>(L.apart);
       p.nchunk = L.nchunk;
       p.u_out = nullptr;
@@ -611,6 +611,8 @@ int slice_load(const slice_config* cfg, void* weights_dev, void* workspace_dev, 
   s->mx_min_t = clampi(env_int("SLQ_MFMA_MIN_T", mfma_min_tokens(cfg->qtype)), 1, MAX_T + 1);
   hipError_t he = hipMemsetAsync(s->w, 0, s->L.wbytes, S(stream));
   if (he == hipSuccess) he = hipMemsetAsync(s->ws, 0, s->L.wsbytes, S(stream));
+  if (he == hipSuccess && s->L.n_attn && cfg->rope_dims > 0)
+    he = launch_rope_table(s->wsp<float>(s->L.rope), cfg->max_seq, cfg->rope_dims, cfg->rope_theta, S(stream));
   if (he == hipSuccess) he = hipStreamCreate(&s->cap);
   if (he != hipSuccess) {
     delete s;

@@ -162,6 +162,7 @@ struct AttnParams {
   int off_q, off_g, off_k, off_v;   // off_g < 0: no gate
   int q_heads, kv_heads, hd, rope_dims;
   double rope_theta;
+  const float* rope_cs;  // [max_seq][rope_dims / 2][2]: cos, sin of the RoPE angle
   int qk_norm;
   const float* q_norm; const float* k_norm;
   float eps;
@@ -169,14 +170,14 @@ struct AttnParams {
   __half* vc;            // V cache: [kv][max_seq][hd]
   int max_seq;
   const Ctrl* ctrl;
-  float* qhat;           // [T][q_heads][hd]
   float* part;           // [T][q_heads][nchunk][hd + 2]
   int nchunk;            // max_seq / chunk
   float* u_out;          // [T][q_heads*hd] (nullable)
   Act next; int next_qt;
 };
-constexpr int ATT_CHUNK = 64;    // KV rows per split-attention workgroup
+constexpr int ATT_CHUNK = 32;    // KV rows per split-attention workgroup
 hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s);
+hipError_t launch_rope_table(float* cs, int max_seq, int rope_dims, double theta, hipStream_t s);
 hipError_t launch_kv_io(__half* kc, __half* vc, int kv_heads, int max_seq, int hd,
                         uint16_t* k, uint16_t* v, int rows, int to_device, hipStream_t s);
 
