@@ -10,25 +10,39 @@
 // row/column l % 16 and the 16-byte k-group l / 16 of A and of B alike; output
 // register i of lane l is C[4 (l / 16) + i][l % 16].
 //
-// Block-diagonal use: A is the wave's own weights, lane l = row l, so k-group g
-// of A row m is weight row 16 g + m.  B column n = 4 s + t is token t of a group
-// of four, and its only nonzero k-group is g = s.  Then
-//     C[m][4 s + t] = row (16 s + m) . digits of token t,
-// i.e. 64 rows x 4 tokens per MFMA, with no data movement for the weights.
-//   Q4_0: per digit pair p, four MFMAs accumulate elements 0..15 / 16..31 of
-//         digit 2p and 16 x digit 2p+1 (activation layout), giving
-//         P_p = C_2p + 16 C_2p+1; the block sum D = P_0 + 256 (P_1 + 256 P_2)
-//         is exact in int32 (|D| <= 32 * 8 * 7829367 < 2^31), and (float)D is
-//         the single rounding of D the GEMV's fused two-part sum also gives.
-//   Q8_0: per base-256 digit two MFMAs (elements 0..15, 16..31); combined like
-//         the GEMV (digit 2 times 65536 fused with digit 1 * 256 + digit 0).
-// Lane l ends with rows 16 ((l & 15) >> 2) + 4 (l >> 4) + i, i = 0..3, of token
-// 4 group + (l & 3).
+// The activation record of a block (MFMA layout, see Act) holds its digits as
+// chunks: Q4_0 chunk 4p + g is digit 2p of elements 16 (g & 1) .. +15 for g < 2
+// and 16 x digit 2p+1 of those elements for g >= 2 (one 64-deep MFMA takes a
+// digit pair, P_p = C_2p + 16 C_2p+1); Q8_0 chunk 2p + h is digit p of
+// elements 16 h .. +15.  The block sum is exact in int32: Q4_0
+// D = P_0 + 256 (P_1 + 256 P_2) (|D| <= 32 * 8 * 7829367 < 2^31), and (float)D
+// is the single rounding of D the GEMV's fused two-part sum also gives; Q8_0
+// is combined like the GEMV (digit 2 times 65536 fused with digit 1 * 256 +
+// digit 0).
 //
-// The digits of the tokens in use come into a ring of 8 block slots in the
-// wave's own LDS by direct global->LDS loads, one tile ahead like the weights.
-// Every wait is an explicit vmcnt that counts only loads issued earlier than
-// the next tile's weights, so no read of the ring waits for HBM.
+// Two uses of the matrix cores, by batch size:
+//
+// Block-diagonal (2..8 tokens).  A is the wave's own weights, lane l = row l,
+// so k-group g of A row m is weight row 16 g + m; B column n = 4 s + t is token
+// t of a group of four, and its only nonzero k-group is g = s.  Then
+// C[m][4 s + t] = row (16 s + m) . digits of token t: 64 rows x 4 tokens per
+// MFMA with no data movement for the weights.  Lane l ends with rows
+// 16 ((l & 15) >> 2) + 4 (l >> 4) + i, i = 0..3, of token 4 group + (l & 3).
+//
+// Dense (9..16 tokens).  One MFMA multiplies 16 weight rows (A) by all 16
+// token slots (B) of one block: A's k-groups 0 and 1 hold the row's elements
+// 0..15 and 16..31 as int8, k-groups 2 and 3 repeat them (Q4_0) or are zero
+// (Q8_0); B's k-groups are the record's chunks of the digit (pair).  A wave's
+// 64 rows are 4 row tiles of 16, three MFMAs each per block; each block's rows
+// (as int8) and scales pass through a small per-wave LDS buffer so that lane
+// l can take row 16 r + l % 16.  Lane l ends with rows 16 r + 4 (l / 16) + i
+// (r, i = 0..3) of token slot l % 16.
+//
+// In both, the weights stream into registers one tile ahead, lane = row, as in
+// the GEMV, and the records of the blocks in use come into a ring of 8 block
+// slots in the wave's LDS by buffer loads into LDS, one tile ahead.  Every
+// wait is an explicit vmcnt that counts only loads issued earlier than the
+// next tile's weights, so no read of the ring waits for HBM.
 #pragma once
 #include "gemv_kernel.h"
 
@@ -38,24 +52,35 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) const void gbl_void_t;
 
-// LDS of one ring slot: chunks x tp token slots x 16 B, then 16 token scales.
+// LDS of one ring slot: chunks x tp token slots x 16 B, then the 16 token
+// scales.
 __host__ __device__ constexpr int gemm_slot(int qt, int tp) { return mx_chunks(qt) * tp * 16 + 64; }
 // copy instructions (64 lanes x 16 B) per block
 __host__ __device__ constexpr int gemm_dpb(int qt, int tp) { return (gemm_slot(qt, tp) / 16 + 63) / 64; }
-// LDS per wave: 8 ring slots, the tile's scales, and a zero area as large as
-// one slot's digits (read by the B lanes outside the diagonal), placed 64 B
-// further on so that its broadcast reads fall in other banks than the chunks
-// read by the lanes inside the diagonal; the epilogue reuses the start for
-// 16 tokens x 64 rows of sums
+// Block-diagonal LDS per wave: 8 ring slots, the tile's scales, and a zero
+// area as large as one slot's digits (read by the B lanes outside the
+// diagonal), placed 64 B further on so that its broadcast reads fall in other
+// banks than the chunks read by the lanes inside the diagonal.
 __host__ __device__ constexpr int gemm_zero(int qt, int tp) { return 8 * gemm_slot(qt, tp) + 1024 + 64; }
-__host__ __device__ constexpr int gemm_region(int qt, int tp) {
+__host__ __device__ constexpr int diag_region(int qt, int tp) {
   return gemm_zero(qt, tp) + mx_chunks(qt) * tp * 16 > 4096 ? gemm_zero(qt, tp) + mx_chunks(qt) * tp * 16 : 4096;
+}
+// Dense LDS per wave (16 token slots): the ring, then the block's int8 rows as
+// two planes (elements 0..15 and 16..31) [2][64][16 B], its row scales [64]
+// fp32 and 16 zero bytes.
+constexpr int DENSE_TP = 16;
+__host__ __device__ constexpr int dense_abuf(int qt) { return 8 * gemm_slot(qt, DENSE_TP); }
+__host__ __device__ constexpr int dense_region(int qt) { return dense_abuf(qt) + 64 * 32 + 64 * 4 + 16; }
+// Either kernel's epilogue reuses the start of each wave's region for
+// 16 tokens x 64 rows of sums.
+__host__ __device__ constexpr int gemm_region(int qt, int T) {
+  return T <= 8 ? diag_region(qt, (T + 3) & ~3) : (dense_region(qt) > 4096 ? dense_region(qt) : 4096);
 }
 constexpr int GEMM_LDS_MAX = 160 * 1024;
 // at most 8 waves (256 registers each: the explicit wait counts rely on the
 // kernel never spilling to scratch) and the LDS of every wave's ring
 __host__ __device__ constexpr bool gemm_fits(int qt, int T, int waves) {
-  return T >= 1 && T <= MX_SLOTS && waves <= 8 && waves * gemm_region(qt, (T + 3) & ~3) <= GEMM_LDS_MAX;
+  return T >= 1 && T <= MX_SLOTS && waves <= 8 && waves * gemm_region(qt, T) <= GEMM_LDS_MAX;
 }
 
 // s_waitcnt immediate on gfx9: wait until at most n vector-memory operations
@@ -216,6 +241,98 @@ __device__ __forceinline__ void tile_diag(const TileRegs<QT>& r, int nb, __amdgp
   }
 }
 
+// One tile: for each block wait for its ring slot, stage the block's rows and
+// scales, multiply, fold into acc[r][i]; then refill the slot with the same
+// block of the next tile.  nb: blocks of this tile; nbn: blocks of the next
+// tile (0: none), whose weights were requested after this tile's records.
+template <int QT, int TP>
+__device__ __forceinline__ void tile_dense(const TileRegs<QT>& w, int nb, __amdgpu_buffer_rsrc_t rs, int kb_next,
+                                           int nbn, uint8_t* ring, float (&acc)[4][4]) {
+  constexpr int NCH = QT == QT_Q4 ? 12 : 6;
+  constexpr int SLOT = gemm_slot(QT, TP);
+  constexpr int DPB = gemm_dpb(QT, TP);
+  constexpr int NW = TB * TileRegs<QT>::NH + 1;   // weight loads of a full tile
+  static_assert(7 * DPB + NW <= 63, "vmcnt holds at most 63 outstanding loads");
+  const int lane = threadIdx.x & 63;
+  const int g = lane >> 4, s = lane & 15;         // k-group and token slot (row in the tile) of this lane
+  uint8_t* abuf = ring + dense_abuf(QT);
+  float* sbuf = reinterpret_cast<float*>(abuf + 64 * 32);
+  const uint8_t* zero16 = abuf + 64 * 32 + 64 * 4;
+  // this lane's A source in row tile r: row 16 r + s, elements 16 (g & 1) ..
+  // (plane g & 1 of the staged rows; 16 lanes read 256 contiguous bytes)
+  const uint8_t* asrc = (QT == QT_Q8 && g >= 2) ? zero16 : abuf + (g & 1) * 64 * 16 + s * 16;
+  const int astep = (QT == QT_Q8 && g >= 2) ? 0 : 16 * 16;
+  // this lane's B chunk for digit (pair) p is c0 + p * cstep
+  const int c0 = QT == QT_Q4 ? g : (g & 1);
+  constexpr int cstep = QT == QT_Q4 ? 4 : 2;
+#pragma unroll
+  for (int b = 0; b < TB; ++b) {
+    if (b < nb) {
+      // Ring slot b was filled by the DPB loads issued after block b of the
+      // previous tile (or in the prologue).  Issued later than those, in this
+      // order: slots b+1..7, the next tile's weights (NW loads, always) and the
+      // refills of slots 0..b-1 made in this tile (DPB each, always).  Loads
+      // complete in issue order, so slot b has landed once at most
+      // (7 - b) DPB + NW + b DPB = 7 DPB + NW are outstanding.  (In a wave's
+      // first tile the epilogue inputs fetched after the prologue make this
+      // wait a little longer than needed, never shorter.)
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * DPB + NW));
+      SLQ_COMPILER_FENCE();
+      // stage row `lane` of block b: elements 0..31 as int8, and its scale
+      u32x4 lo, hi;
+      if constexpr (QT == QT_Q4) {
+        const u32x4 c = w.c[b];
+        lo.x = sext_nibbles(c.x & 0x0F0F0F0Fu);
+        lo.y = sext_nibbles(c.y & 0x0F0F0F0Fu);
+        lo.z = sext_nibbles(c.z & 0x0F0F0F0Fu);
+        lo.w = sext_nibbles(c.w & 0x0F0F0F0Fu);
+        hi.x = sext_nibbles((c.x >> 4) & 0x0F0F0F0Fu);
+        hi.y = sext_nibbles((c.y >> 4) & 0x0F0F0F0Fu);
+        hi.z = sext_nibbles((c.z >> 4) & 0x0F0F0F0Fu);
+        hi.w = sext_nibbles((c.w >> 4) & 0x0F0F0F0Fu);
+      } else {
+        lo = w.c[2 * b];
+        hi = w.c[2 * b + 1];
+      }
+      reinterpret_cast<u32x4*>(abuf)[lane] = lo;
+      reinterpret_cast<u32x4*>(abuf + 64 * 16)[lane] = hi;
+      sbuf[lane] = scale_of(w.sc, b);
+      // (LDS accesses of one wave take effect in program order: the reads
+      // below see these writes)
+      const uint8_t* slot = ring + b * SLOT;
+      i32x4 bq[3];
+#pragma unroll
+      for (int p = 0; p < 3; ++p) bq[p] = *reinterpret_cast<const i32x4*>(slot + ((c0 + p * cstep) * TP + s) * 16);
+      const float xs = reinterpret_cast<const float*>(slot + NCH * TP * 16)[s];
+      const i32x4 z = {0, 0, 0, 0};
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const i32x4 A = *reinterpret_cast<const i32x4*>(asrc + r * astep);
+        const float4 d4 = *reinterpret_cast<const float4*>(sbuf + 16 * r + 4 * g);
+        const i32x4 P0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bq[0], z, 0, 0, 0);
+        const i32x4 P1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bq[1], z, 0, 0, 0);
+        const i32x4 P2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bq[2], z, 0, 0, 0);
+        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          float bf;
+          if constexpr (QT == QT_Q4) {
+            bf = (float)(P0[i] + ((P1[i] + (P2[i] << 8)) << 8));
+          } else {
+            bf = __builtin_fmaf((float)P2[i], 65536.0f, (float)(P0[i] + (P1[i] << 8)));
+          }
+          acc[r][i] = __builtin_fmaf(bf, dd[i] * xs, acc[r][i]);
+        }
+      }
+    }
+    // refill slot b with block b of the next tile; where there is none, a
+    // dummy copy of block 0 into the unused slot keeps the load count fixed
+    SLQ_COMPILER_FENCE();
+    dma_block<QT, DPB>(rs, b < nbn ? kb_next + b : 0, TP, ring + b * SLOT);
+    SLQ_COMPILER_FENCE();
+  }
+}
+
 // Epilogue of token j for the 64 rows of group rg; lane = row, a = sum over K.
 // pre: the token's RMSNorm factor (STORE, SWIGLU) or its residual entry h
 // (RESID), fetched at kernel start; nw_row: next RMSNorm weight of the row.
@@ -279,10 +396,10 @@ __device__ __forceinline__ float epi_finish(const EpiRaw& r, const NormIn& nin, 
 }
 
 template <int QT, int EPI, int NG>
-__global__ __launch_bounds__(512) void k_gemm(Packed W, Act x, NormIn nin, GemvOut out, int ksplit, int T) {
+__global__ __launch_bounds__(512) void k_gemm_diag(Packed W, Act x, NormIn nin, GemvOut out, int ksplit, int T) {
   constexpr int TBY = tile_bytes(QT);
   constexpr int TP = 4 * NG;
-  constexpr int REGION = gemm_region(QT, TP);
+  constexpr int REGION = diag_region(QT, TP);
   extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
@@ -413,21 +530,146 @@ __global__ __launch_bounds__(512) void k_gemm(Packed W, Act x, NormIn nin, GemvO
 }
 
 template <int QT, int EPI>
+__global__ __launch_bounds__(512) void k_gemm_dense(Packed W, Act x, NormIn nin, GemvOut out, int ksplit, int T) {
+  constexpr int TBY = tile_bytes(QT);
+  constexpr int TP = DENSE_TP;
+  constexpr int REGION = dense_region(QT) > 4096 ? dense_region(QT) : 4096;
+  extern __shared__ __attribute__((aligned(16))) uint8_t lds[];
+  const int lane = threadIdx.x & 63;
+  const int wave = wave_id();
+  const int nw = blockDim.x >> 6;
+  const int rg = blockIdx.x / ksplit, ks = blockIdx.x % ksplit;
+  const int nblk = W.nblk(), ntiles = W.ntiles(), full = nblk / TB;
+  const int w0 = ntiles * ks / ksplit, w1 = ntiles * (ks + 1) / ksplit;
+  const int t0 = __builtin_amdgcn_readfirstlane(w0 + (w1 - w0) * wave / nw);
+  const int t1 = __builtin_amdgcn_readfirstlane(w0 + (w1 - w0) * (wave + 1) / nw);
+  const uint8_t* base = W.w + (size_t)rg * rg_bytes(QT, W.cols);
+  uint8_t* ring = lds + (size_t)wave * REGION;
+  auto nb_of = [&](int t) { return t < full ? TB : nblk - full * TB; };
+  if (lane == 0) *reinterpret_cast<u32x4*>(ring + dense_abuf(QT) + 64 * 32 + 64 * 4) = u32x4{0u, 0u, 0u, 0u};
+
+  float acc[4][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[r][i] = 0.0f;
+
+  const __amdgpu_buffer_rsrc_t rs = mx_rsrc(x, QT);
+  TileRegs<QT> A, B;
+  if (t0 < t1) {
+    // prologue: tile t0's weights, then its digits into the ring (all 8
+    // slots, block 0 again past a ragged tile's end)
+    load_tile_fixed<QT>(base + (size_t)t0 * TBY, lane, nb_of(t0), A);
+    SLQ_COMPILER_FENCE();
+#pragma unroll
+    for (int b = 0; b < TB; ++b)
+      dma_block<QT, gemm_dpb(QT, TP)>(rs, b < nb_of(t0) ? t0 * TB + b : 0, TP, ring + b * gemm_slot(QT, TP));
+    SLQ_COMPILER_FENCE();
+  }
+
+  // The first four tokens this wave finishes (j = wave + nw q): what their
+  // epilogues read is requested now, behind the first tile, so its latency
+  // hides under the weights.
+  const int64_t erow = (int64_t)rg * RG + lane;
+  const bool erv = erow < W.rows;
+  EpiRaw raw[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) raw[q] = epi_fetch<EPI>(out, nin, erow, erv, wave + nw * q, T);
+  const float nw_row = EPI == EPI_RESID ? (erv ? out.norm_w[erow] : 0.0f) : 0.0f;
+  SLQ_COMPILER_FENCE();
+
+  if (t0 < t1) {
+    // Each step loads the next tile's weights (a lane-uniform dummy after the
+    // wave's last tile) before the math of this one.
+    for (int t = t0; t < t1; t += 2) {
+      const bool n1 = t + 1 < t1;
+      load_tile_fixed<QT>(base + (size_t)(n1 ? t + 1 : t) * TBY, lane, n1 ? nb_of(t + 1) : 0, B);
+      SLQ_COMPILER_FENCE();
+      tile_dense<QT, TP>(A, nb_of(t), rs, (t + 1) * TB, n1 ? nb_of(t + 1) : 0, ring, acc);
+      if (!n1) break;
+      const bool n2 = t + 2 < t1;
+      load_tile_fixed<QT>(base + (size_t)(n2 ? t + 2 : t + 1) * TBY, lane, n2 ? nb_of(t + 2) : 0, A);
+      SLQ_COMPILER_FENCE();
+      tile_dense<QT, TP>(B, nb_of(t + 1), rs, (t + 2) * TB, n2 ? nb_of(t + 2) : 0, ring, acc);
+    }
+    // the dummy refills of the last tile still write the ring, which the
+    // reduction below reuses
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+  }
+
+  float pre[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) pre[q] = epi_finish<EPI>(raw[q], nin, wave + nw * q, T);
+
+  // Waves meet in LDS: red[token][row] in each wave's own region.  Token j is
+  // finished by wave j % nw, which adds the waves in wave order.
+  __syncthreads();
+  {
+    // lane l holds rows 16 r + 4 (l / 16) + i of token slot l % 16 (slots
+    // past T hold nothing of use and are never read)
+    float* red = reinterpret_cast<float*>(ring) + (lane & 15) * RG + 4 * (lane >> 4);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+      *reinterpret_cast<float4*>(red + 16 * r) = float4{acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
+  }
+  __syncthreads();
+  // token j of this wave: sum of the waves' values in wave order
+  auto wave_sum_of = [&](int j) {
+    float a = reinterpret_cast<const float*>(lds)[(size_t)j * RG + lane];
+    for (int w = 1; w < nw; ++w) a += reinterpret_cast<const float*>(lds + (size_t)w * REGION)[(size_t)j * RG + lane];
+    return a;
+  };
+  auto pre_of = [&](int q, int j) {
+    return q == 0 ? pre[0] : q == 1 ? pre[1] : q == 2 ? pre[2] : q == 3 ? pre[3] : epi_input<EPI>(out, nin, erow, erv, j, T);
+  };
+  if (ksplit == 1) {
+    for (int q = 0, j = wave; j < T; ++q, j += nw) gemm_epi<QT, EPI>(W, out, rg, j, wave_sum_of(j), pre_of(q, j), nw_row);
+    return;
+  }
+
+  // Same exchange as the GEMV: partials move through agent-scope atomics,
+  // every wave's stores are complete before the workgroup takes its ticket,
+  // and the last split adds them in split order.
+  for (int j = wave; j < T; j += nw)
+    __hip_atomic_store(out.part + (((size_t)rg * ksplit + ks) * T + j) * RG + lane, wave_sum_of(j), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  unsigned* tk = reinterpret_cast<unsigned*>(lds);
+  if (threadIdx.x == 0) tk[0] = __hip_atomic_fetch_add(out.cnt + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  const unsigned ticket = tk[0];
+  if (ticket != (unsigned)(ksplit - 1)) return;
+  const float* all = out.part + (size_t)rg * ksplit * T * RG;
+  for (int q = 0, j = wave; j < T; ++q, j += nw) {
+    float pv[16];   // all splits' loads in flight together
+#pragma unroll
+    for (int k2 = 0; k2 < 16; ++k2)
+      pv[k2] = k2 < ksplit ? __hip_atomic_load(all + ((size_t)k2 * T + j) * RG + lane, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.0f;
+    float sum = 0.0f;
+#pragma unroll
+    for (int k2 = 0; k2 < 16; ++k2)
+      if (k2 < ksplit) sum += pv[k2];
+    gemm_epi<QT, EPI>(W, out, rg, j, sum, pre_of(q, j), nw_row);
+  }
+  if (threadIdx.x == 0) __hip_atomic_store(out.cnt + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <int QT, int EPI>
 hipError_t gemm_inst(const Packed& W, int T, Act x, NormIn nin, GemvOut out, int ksplit, int waves,
                      hipStream_t s) {
   if (!x.mxd || ksplit < 1 || ksplit > 16 || waves < 1 || !gemm_fits(QT, T, waves))
     return hipErrorInvalidValue;
   if (ksplit > 1 && (!out.part || !out.cnt)) return hipErrorInvalidValue;
-  const int ng = (T + 3) / 4;
   const dim3 grid((unsigned)(W.nrg() * ksplit)), block(64 * waves);
-  const size_t lds = (size_t)waves * gemm_region(QT, 4 * ng);
-  switch (ng) {
-    case 1: k_gemm<QT, EPI, 1><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T); break;
-    case 2: k_gemm<QT, EPI, 2><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T); break;
-    case 3: k_gemm<QT, EPI, 3><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T); break;
-    case 4: k_gemm<QT, EPI, 4><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T); break;
-    default: return hipErrorInvalidValue;
-  }
+  const size_t lds = (size_t)waves * gemm_region(QT, T);
+  if (T <= 4) k_gemm_diag<QT, EPI, 1><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T);
+  else if (T <= 8) k_gemm_diag<QT, EPI, 2><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T);
+  else k_gemm_dense<QT, EPI><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T);
   return hipGetLastError();
 }
 
