@@ -19,4 +19,6 @@ hipError_t launch_gemm(const Packed& W, int T, Act x, NormIn nin, GemvOut out, i
 
 bool gemm_usable(int qt, int T, int waves) { return gemm_fits(qt, T, waves); }
 
+int gemm_min_tokens(int qt, int waves) { return qt == QT_Q8 ? 2 : waves <= 4 ? 4 : 8; }
+
 }  // namespace slq

@@ -137,7 +137,7 @@ hipError_t launch_gemv(const Packed& W, int T, Act x, NormIn nin, GemvOut out, i
                        hipStream_t s) {
   if (waves < 1 || waves > 16 || ksplit < 1) return hipErrorInvalidValue;
   if (ksplit > 1 && (!out.part || !out.cnt)) return hipErrorInvalidValue;
-  if (x.mxd && T >= x.min_t && gemm_usable(W.qt, T, waves))
+  if (x.mxd && T >= (x.min_t ? x.min_t : gemm_min_tokens(W.qt, waves)) && gemm_usable(W.qt, T, waves))
     return launch_gemm(W, T, x, nin, out, ksplit, waves, s);
   const bool q4 = W.qt == QT_Q4;
   switch (out.kind) {

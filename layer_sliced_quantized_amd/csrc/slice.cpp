@@ -61,12 +61,10 @@ struct Plan {
 
 int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
 
-// Fewest tokens per call that go to the int8-MFMA products instead of the
-// per-token integer dot products (measured on MI355X over the slice's shapes):
-// Q8_0 blocks carry twice the bytes per block of work and the products win
-// from 2 tokens; for Q4_0 the per-token dot products stay faster up to 4-7
-// tokens.  SLQ_MFMA_MIN_T overrides.
-int mfma_min_tokens(int qt) { return qt == QT_Q4 ? 8 : 2; }
+// Fewest tokens per call that go to the int8-MFMA products: 0 leaves the
+// choice to gemm_min_tokens (by format and waves per workgroup);
+// SLQ_MFMA_MIN_T sets a fixed count instead.
+int mfma_min_tokens() { return clampi(env_int("SLQ_MFMA_MIN_T", 0), 0, MAX_T + 1); }
 
 Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
   const int nrg = (int)((rows + RG - 1) / RG);
@@ -319,10 +317,10 @@ struct slice {
   Ctrl* ctrl() const { return reinterpret_cast<Ctrl*>(ws + L.ctrl); }
   template <class X> X* wsp(size_t off) const { return reinterpret_cast<X*>(ws + off); }
   Packed packed(const Mat& m) const { return Packed{w + m.off, m.rows, m.cols, cfg.qtype}; }
-  int mx_min_t = 2;   // GEMVs with at least this many tokens use the MFMA products
-  // digits of a step of T tokens; the MFMA layout is written when it is used
+  int mx_min_t = 0;   // GEMVs with at least this many tokens use the MFMA products (0: by format and plan)
+  // digits of a step of T tokens; the MFMA layout is written when it may be used
   Act act(size_t d, size_t s_, size_t md, int nblk, int T) const {
-    const bool mx = T >= mx_min_t && L.mt > 1;
+    const bool mx = T >= (mx_min_t ? mx_min_t : 2) && L.mt > 1;
     return Act{wsp<int32_t>(d), wsp<float>(s_), nblk, mx ? wsp<int32_t>(md) : nullptr, mx_min_t};
   }
   Act act_a(int T) const { return act(L.xa_d, L.xa_s, L.xa_md, cfg.hidden / QK, T); }
@@ -561,8 +559,8 @@ int slq_gemv(int qtype, const void* packed_dev, int64_t rows, int64_t cols, int 
   const int nblk = (int)(cols / QK);
   uint8_t* ws = static_cast<uint8_t*>(ws_dev);
   const GemvWs L = gemv_ws(qtype, rows, cols, batch);
-  const int min_t = clampi(env_int("SLQ_MFMA_MIN_T", mfma_min_tokens(qtype)), 1, MAX_T + 1);
-  const bool mx = batch >= min_t;
+  const int min_t = mfma_min_tokens();
+  const bool mx = batch >= (min_t ? min_t : 2);
   Act a{reinterpret_cast<int32_t*>(ws + L.dig), reinterpret_cast<float*>(ws + L.sc), nblk,
         mx ? reinterpret_cast<int32_t*>(ws + L.mdig) : nullptr, min_t};
   float* part = reinterpret_cast<float*>(ws + L.part);
@@ -608,7 +606,7 @@ int slice_load(const slice_config* cfg, void* weights_dev, void* workspace_dev, 
   s->w = static_cast<uint8_t*>(weights_dev);
   s->ws = static_cast<uint8_t*>(workspace_dev);
   s->eager = env_int("SLQ_EAGER", 0) != 0;
-  s->mx_min_t = clampi(env_int("SLQ_MFMA_MIN_T", mfma_min_tokens(cfg->qtype)), 1, MAX_T + 1);
+  s->mx_min_t = mfma_min_tokens();
   hipError_t he = hipMemsetAsync(s->w, 0, s->L.wbytes, S(stream));
   if (he == hipSuccess) he = hipMemsetAsync(s->ws, 0, s->L.wsbytes, S(stream));
   if (he == hipSuccess && s->L.n_attn && cfg->rope_dims > 0)

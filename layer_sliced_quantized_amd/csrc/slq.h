@@ -62,7 +62,8 @@ struct Act {
   float* xs;
   int nblk;      // blocks per token
   int32_t* mxd;  // MFMA layout records, or nullptr (not written)
-  int min_t;     // calls with at least this many tokens use the MFMA products (when they fit)
+  int min_t;     // calls with at least this many tokens use the MFMA products (when they
+                 // fit); 0: the measured default, gemm_min_tokens
 };
 constexpr int MX_SLOTS = 16;
 __host__ __device__ constexpr int mx_chunks(int qt) { return qt == QT_Q4 ? 12 : 6; }
@@ -124,6 +125,11 @@ hipError_t launch_gemv(const Packed& W, int T, Act x, NormIn nin, GemvOut out, i
 hipError_t launch_gemm(const Packed& W, int T, Act x, NormIn nin, GemvOut out, int ksplit,
                        int waves, hipStream_t s);
 bool gemm_usable(int qt, int T, int waves);
+// Fewest tokens for which the MFMA products beat the per-token integer dot
+// products (measured on MI355X over the slice's shapes): Q8_0 from 2 tokens;
+// Q4_0 from 4 tokens with at most 4 waves per workgroup, from 8 with more
+// (the batched kernels stream fewer tiles per wave as waves are added).
+int gemm_min_tokens(int qt, int waves);
 // h [T][H] = boundary input, then digits of norm_w*h and ssq partials.
 // in_kind: 1 = fp16 input, 2 = fp32 input; with in == nullptr the input pointer
 // is read from ctrl->in.

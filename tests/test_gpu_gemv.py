@@ -89,7 +89,7 @@ def test_gemm_batch_equals_single_bitwise(qtype, ks, w, rows, cols, monkeypatch)
     x[9, ::5] *= 1e3                # wide range inside blocks
     y1 = np.stack([slq.gemv(qtype, packed, rows, cols, _dev(x[t:t + 1])).cpu().numpy()[0] for t in range(16)])
     assert np.all(y1[3] == 0)
-    for batch in (2, 5, 16):
+    for batch in (2, 5, 11, 16):
         yb = slq.gemv(qtype, packed, rows, cols, _dev(x[:batch])).cpu().numpy()
         np.testing.assert_array_equal(yb, y1[:batch])
     ref = qref.gemv(qtype, raw, rows, cols, x.astype(np.float64))
