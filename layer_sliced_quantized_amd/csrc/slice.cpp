@@ -52,7 +52,9 @@ int env_int(const char* name, int dflt) {
 //   input projections (16448/14336 x 5120): ks 4, w 4
 //   gate/up + SwiGLU (34816 x 5120):        ks 2, w 4
 //   down projection (5120 x 17408):         ks 8, w 4
-//   mixer output (5120 x 4096 / 6144):      ks 1, w 16
+//   mixer output (5120 x 4096 / 6144):      ks 4, w 4
+// (one token: within 1 % of the best shape for every kind; at most 4 waves
+// per workgroup also lets a verify pass of 4 tokens use the MFMA products)
 // Other shapes: enough splits for ~1000 workgroups, about two tiles per wave.
 // SLQ_KS_<kind> / SLQ_W_<kind> override (kinds G1, G2, F1, F2, HEAD, GEMV).
 struct Plan {
@@ -72,10 +74,9 @@ Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
   const std::string k(kind);
   Plan p;
   if (k == "G2" && nrg <= 128) {
-    // few row groups, long K: one workgroup per row group, up to 16 waves
-    // splitting K and meeting in LDS (no cross-workgroup exchange)
-    p.ks = 1;
-    p.w = clampi(ntiles, 1, 16);
+    // few row groups: four splits of four waves (fewer where K is short)
+    p.ks = clampi(4, 1, ntiles);
+    p.w = clampi(ntiles / p.ks, 1, 4);
   } else {
     p.ks = clampi((1024 + nrg - 1) / nrg, 1, ntiles < 16 ? ntiles : 16);
     if (k == "F1") p.ks = clampi(p.ks, 1, 2);
