@@ -55,7 +55,8 @@ int env_int(const char* name, int dflt) {
 //   mixer output (5120 x 4096 / 6144):      ks 4, w 4
 // (one token: within 1 % of the best shape for every kind; at most 4 waves
 // per workgroup also lets a verify pass of 4 tokens use the MFMA products)
-// Other shapes: enough splits for ~1000 workgroups, about two tiles per wave.
+// Other shapes: enough splits for ~1000 workgroups, about two tiles per wave,
+// at most 4 waves per workgroup.
 // SLQ_KS_<kind> / SLQ_W_<kind> override (kinds G1, G2, F1, F2, HEAD, GEMV).
 struct Plan {
   int ks, w;
@@ -81,7 +82,10 @@ Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
     p.ks = clampi((1024 + nrg - 1) / nrg, 1, ntiles < 16 ? ntiles : 16);
     if (k == "F1") p.ks = clampi(p.ks, 1, 2);
     if (k == "F2" || k == "G1") p.ks = clampi(p.ks, 1, k == "F2" ? 8 : 4);
-    p.w = clampi(k == "GEMV" || k == "HEAD" ? (ntiles / p.ks + 1) / 2 : 4, 1, 8);
+    // at most 4 waves: one token is as fast as with 8 (LM head 248320 x 5120:
+    // 114.8 against 115.1 us) and the batched products fit and stream longer
+    // per wave (16 tokens: 474 against 874 us)
+    p.w = clampi(k == "GEMV" || k == "HEAD" ? (ntiles / p.ks + 1) / 2 : 4, 1, 4);
   }
   p.ks = clampi(env_int(("SLQ_KS_" + k).c_str(), p.ks), 1, 16);
   p.w = clampi(env_int(("SLQ_W_" + k).c_str(), p.w), 1, 16);
