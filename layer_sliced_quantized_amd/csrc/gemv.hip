@@ -135,7 +135,7 @@ hipError_t launch_quant_act(int qt, const float* x, int T, int n, int64_t x_ts, 
 
 hipError_t launch_gemv(const Packed& W, int T, Act x, NormIn nin, GemvOut out, int ksplit, int waves,
                        hipStream_t s) {
-  if (waves < 1 || waves > 16 || ksplit < 1) return hipErrorInvalidValue;
+  if (waves < 1 || waves > 8 || ksplit < 1) return hipErrorInvalidValue;
   if (ksplit > 1 && (!out.part || !out.cnt)) return hipErrorInvalidValue;
   if (x.mxd && T >= (x.min_t ? x.min_t : gemm_min_tokens(W.qt, waves)) && gemm_usable(W.qt, T, waves))
     return launch_gemm(W, T, x, nin, out, ksplit, waves, s);

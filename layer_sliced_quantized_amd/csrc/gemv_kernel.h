@@ -161,9 +161,9 @@ __device__ __forceinline__ void tile_math(const TileRegs<QT>& r, int nb, int kb,
 }
 
 template <int QT, int T, int EPI>
-__global__ __launch_bounds__(1024) void k_gemv(Packed W, Act x, NormIn nin, GemvOut out, int ksplit) {
+__global__ __launch_bounds__(512) void k_gemv(Packed W, Act x, NormIn nin, GemvOut out, int ksplit) {
   constexpr int TBY = tile_bytes(QT);
-  __shared__ float red[16][RG];
+  __shared__ float red[8][RG];
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int nw = blockDim.x >> 6;

@@ -88,7 +88,7 @@ Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
     p.w = clampi(k == "GEMV" || k == "HEAD" ? (ntiles / p.ks + 1) / 2 : 4, 1, 4);
   }
   p.ks = clampi(env_int(("SLQ_KS_" + k).c_str(), p.ks), 1, 16);
-  p.w = clampi(env_int(("SLQ_W_" + k).c_str(), p.w), 1, 16);
+  p.w = clampi(env_int(("SLQ_W_" + k).c_str(), p.w), 1, 8);
   return p;
 }
 
