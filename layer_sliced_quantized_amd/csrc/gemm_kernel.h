@@ -57,11 +57,12 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 __host__ __device__ constexpr int gemm_slot(int qt, int tp) { return mx_chunks(qt) * tp * 16 + 64; }
 // copy instructions (64 lanes x 16 B) per block
 __host__ __device__ constexpr int gemm_dpb(int qt, int tp) { return (gemm_slot(qt, tp) / 16 + 63) / 64; }
-// Block-diagonal LDS per wave: 8 ring slots, the tile's scales, and a zero
-// area as large as one slot's digits (read by the B lanes outside the
-// diagonal), placed 64 B further on so that its broadcast reads fall in other
-// banks than the chunks read by the lanes inside the diagonal.
-__host__ __device__ constexpr int gemm_zero(int qt, int tp) { return 8 * gemm_slot(qt, tp) + 1024 + 64; }
+// Block-diagonal LDS per wave: 8 ring slots, the tile's row scales as fp32
+// [8 blocks][64 rows], and a zero area as large as one slot's digits (read by
+// the B lanes outside the diagonal), placed 64 B further on so that its
+// broadcast reads fall in other banks than the chunks read by the lanes
+// inside the diagonal.
+__host__ __device__ constexpr int gemm_zero(int qt, int tp) { return 8 * gemm_slot(qt, tp) + 2048 + 64; }
 __host__ __device__ constexpr int diag_region(int qt, int tp) {
   return gemm_zero(qt, tp) + mx_chunks(qt) * tp * 16 > 4096 ? gemm_zero(qt, tp) + mx_chunks(qt) * tp * 16 : 4096;
 }
@@ -150,12 +151,12 @@ __device__ __forceinline__ void tile_diag(const TileRegs<QT>& r, int nb, __amdgp
   const bool bvalid = ((lane & 15) >> 2) == (lane >> 4);   // B lane inside the diagonal
   const int rbase = 16 * ((lane & 15) >> 2) + 4 * (lane >> 4);
   const uint8_t* zero = ring + gemm_zero(QT, TP);
-  u32x4* sc_lds = reinterpret_cast<u32x4*>(ring + 8 * SLOT);
-  sc_lds[lane] = r.sc;
-  SLQ_COMPILER_FENCE();
-  u32x4 scw[4];
+  // the tile's scales, transposed: sct[b][row] (one 16-byte read per block
+  // gives this lane's four rows)
+  float* sct = reinterpret_cast<float*>(ring + 8 * SLOT);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) scw[i] = sc_lds[rbase + i];
+  for (int b = 0; b < TB; ++b) sct[b * 64 + lane] = scale_of(r.sc, b);
+  SLQ_COMPILER_FENCE();
 #pragma unroll
   for (int b = 0; b < TB; ++b) {
     if (b < nb) {
@@ -190,7 +191,7 @@ __device__ __forceinline__ void tile_diag(const TileRegs<QT>& r, int nb, __amdgp
       const i32x4 A1 = {(int)a1.x, (int)a1.y, (int)a1.z, (int)a1.w};
       float d[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) d[i] = scale_of(scw[i], b);
+      for (int i = 0; i < 4; ++i) d[i] = sct[b * 64 + rbase + i];
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
         SLQ_COMPILER_FENCE();
@@ -201,7 +202,6 @@ __device__ __forceinline__ void tile_diag(const TileRegs<QT>& r, int nb, __amdgp
         i32x4 P[3];
 #pragma unroll
         for (int p = 0; p < 3; ++p) {
-          SLQ_COMPILER_FENCE();   // one pair's operands in registers at a time
           if constexpr (QT == QT_Q4) {
             i32x4 bq[4];
 #pragma unroll
