@@ -40,6 +40,27 @@ __device__ __forceinline__ float rnorm_from(const NormIn& n, int t) {
   return 1.0f / sqrtf(a * n.inv_n + n.eps);
 }
 
+// rnorm_from in two steps, so that the loads go out early and the wave-wide
+// sum is taken later: rnorm_fetch takes this lane's (at most two) partial
+// sums, rnorm_finish adds them with rnorm_from's additions (bitwise the same
+// value; more than 128 partials fall back to rnorm_from).  Every lane of the
+// wave must call rnorm_finish.
+struct RnRaw {
+  float a, b;
+};
+__device__ __forceinline__ RnRaw rnorm_fetch(const NormIn& n, int t) {
+  const int lane = threadIdx.x & 63;
+  if (!n.ssq || n.n_part > 128) return {0.0f, 0.0f};
+  const float* s = n.ssq + (size_t)t * n.n_part;
+  return {lane < n.n_part ? s[lane] : 0.0f, lane + 64 < n.n_part ? s[lane + 64] : 0.0f};
+}
+__device__ __forceinline__ float rnorm_finish(const RnRaw& r, const NormIn& n, int t) {
+  if (!n.ssq) return 1.0f;
+  if (n.n_part > 128) return rnorm_from(n, t);
+  const float a = wave_sum(r.a + r.b);
+  return 1.0f / sqrtf(a * n.inv_n + n.eps);
+}
+
 // Integer form of one block of 32 activations held one per lane by a 32-lane
 // half of the wave (element e = lane & 31):
 //   s = max|x| / M,  x_int = rint(x / s)  (|x_int| <= M),  u = x_int + OFF

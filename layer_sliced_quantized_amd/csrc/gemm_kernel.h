@@ -374,13 +374,12 @@ struct EpiRaw {
 };
 template <int EPI>
 __device__ __forceinline__ EpiRaw epi_fetch(const GemvOut& out, const NormIn& nin, int64_t row, bool rv, int j, int T) {
-  const int lane = threadIdx.x & 63;
   if constexpr (EPI == EPI_RESID) {
     return {(j < T && rv) ? out.y[(size_t)j * out.y_tstride + row] : 0.0f, 0.0f};
   } else {
-    if (j >= T || !nin.ssq || nin.n_part > 128) return {0.0f, 0.0f};
-    const float* s = nin.ssq + (size_t)j * nin.n_part;
-    return {lane < nin.n_part ? s[lane] : 0.0f, lane + 64 < nin.n_part ? s[lane + 64] : 0.0f};
+    if (j >= T) return {0.0f, 0.0f};
+    const RnRaw r = rnorm_fetch(nin, j);
+    return {r.a, r.b};
   }
 }
 template <int EPI>
@@ -388,10 +387,8 @@ __device__ __forceinline__ float epi_finish(const EpiRaw& r, const NormIn& nin, 
   if constexpr (EPI == EPI_RESID) {
     return r.a;
   } else {
-    if (j >= T || !nin.ssq) return 1.0f;
-    if (nin.n_part > 128) return rnorm_from(nin, j);
-    const float a = wave_sum(r.a + r.b);
-    return 1.0f / sqrtf(a * nin.inv_n + nin.eps);
+    if (j >= T) return 1.0f;
+    return rnorm_finish(RnRaw{r.a, r.b}, nin, j);
   }
 }
 

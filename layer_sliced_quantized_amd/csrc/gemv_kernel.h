@@ -179,11 +179,12 @@ __global__ __launch_bounds__(512) void k_gemv(Packed W, Act x, NormIn nin, GemvO
   float acc[T];
 #pragma unroll
   for (int j = 0; j < T; ++j) acc[j] = 0.0f;
-  // RMSNorm factor of the input (STORE / SWIGLU), fetched now so its latency
-  // hides under the weight stream
-  float rn[T];
+  // RMSNorm factor of the input (STORE / SWIGLU): its partial sums are
+  // requested now and summed after the main loop, so waiting for them does
+  // not hold back wave 0's first weight loads
+  RnRaw rr[T];
 #pragma unroll
-  for (int j = 0; j < T; ++j) rn[j] = (EPI != EPI_RESID && wave == 0) ? rnorm_from(nin, j) : 1.0f;
+  for (int j = 0; j < T; ++j) rr[j] = (EPI != EPI_RESID && wave == 0) ? rnorm_fetch(nin, j) : RnRaw{0.0f, 0.0f};
 
   // full tiles, two register sets in turn so the next tile's loads overlap this tile's math
   const int te = t1 < full ? t1 : full;
@@ -206,6 +207,10 @@ __global__ __launch_bounds__(512) void k_gemv(Packed W, Act x, NormIn nin, GemvO
     load_tile<QT>(base + (size_t)full * TBY, lane, nb, A);
     tile_math<QT, T>(A, nb, full * TB, x, acc);
   }
+
+  float rn[T];
+#pragma unroll
+  for (int j = 0; j < T; ++j) rn[j] = (EPI != EPI_RESID && wave == 0) ? rnorm_finish(rr[j], nin, j) : 1.0f;
 
   // waves meet in LDS, summed in wave order
 #pragma unroll
