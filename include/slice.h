@@ -139,15 +139,18 @@ enum {
 };
 
 /* Bytes of the weights buffer (packed layout of every tensor of the slice)
- * and of the workspace (KV caches, DeltaNet state slots, activations).
- * 0 means the configuration is invalid (see slice_last_error).             */
+ * and of the workspace (KV caches, DeltaNet state slots, activations, the
+ * RoPE rotation table).  0 means the configuration is invalid (see
+ * slice_last_error).                                                        */
 size_t slice_weights_bytes(const slice_config *cfg);
 size_t slice_workspace_bytes(const slice_config *cfg);
 
 /* Bind a slice to caller-owned device buffers (weights_dev: weights_bytes,
  * workspace_dev: workspace_bytes, both 256-byte aligned).  Validates the
- * configuration, carves the workspace and zeroes it on `stream`.  Weights are
- * filled afterwards with slice_set_tensor.  Position 0, state slot 0.        */
+ * configuration, carves the workspace, zeroes it and builds the RoPE table
+ * in it on `stream`.  Weights are filled afterwards with slice_set_tensor.
+ * Position 0, state slot 0.  The caller does not write to either buffer
+ * while the slice is loaded, except through these calls.                   */
 int slice_load(const slice_config *cfg, void *weights_dev, void *workspace_dev,
                void *stream, slice_t **out);
 
