@@ -40,9 +40,9 @@
 //
 // In both, the weights stream into registers one tile ahead, lane = row, as in
 // the GEMV, and the records of the blocks in use come into a ring of 8 block
-// slots in the wave's LDS by buffer loads into LDS, one tile ahead.  Every
-// wait is an explicit vmcnt that counts only loads issued earlier than the
-// next tile's weights, so no read of the ring waits for HBM.
+// slots in the wave's LDS by buffer loads into LDS, one tile ahead.  Each ring
+// wait is an explicit vmcnt that leaves the next tile's weights and the
+// refills issued after them in flight, so no read of the ring waits for them.
 #pragma once
 #include "gemv_kernel.h"
 
@@ -112,7 +112,6 @@ __device__ __forceinline__ uint32_t sext_nibbles(uint32_t t) {
 }
 
 #define SLQ_COMPILER_FENCE() asm volatile("" ::: "memory")
-
 
 // Digits (token slots 0..tp-1) and scales of block blk into a ring slot:
 // piece q < NCH*tp is chunk q / tp, slot q % tp; the last 4 pieces are the
