@@ -39,8 +39,8 @@
 // (r, i = 0..3) of token slot l % 16.
 //
 // In both, the weights stream into registers one tile ahead, lane = row, as in
-// the GEMV, and the records of the blocks in use come into a ring of 8 block
-// slots in the wave's LDS by buffer loads into LDS, one tile ahead.  Each ring
+// the GEMV, and the records of the blocks in use come into a ring of 4 block
+// slots in the wave's LDS by buffer loads into LDS, four blocks ahead.  Each ring
 // wait is an explicit vmcnt that leaves the next tile's weights and the
 // refills issued after them in flight, so no read of the ring waits for them.
 #pragma once
@@ -57,22 +57,24 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 __host__ __device__ constexpr int gemm_slot(int qt, int tp) { return mx_chunks(qt) * tp * 16 + 64; }
 // copy instructions (64 lanes x 16 B) per block
 __host__ __device__ constexpr int gemm_dpb(int qt, int tp) { return (gemm_slot(qt, tp) / 16 + 63) / 64; }
-// Block-diagonal LDS per wave: 8 ring slots, the tile's row scales as fp32
+// Both kernels keep a ring of 4 block slots per wave: the records are
+// L2-resident, so copies four blocks ahead arrive in time, and a small ring
+// lets more workgroups share a CU.
+constexpr int RING = 4;
+// Block-diagonal LDS per wave: the ring, the tile's row scales as fp32
 // [8 blocks][64 rows], and a zero area as large as one slot's digits (read by
 // the B lanes outside the diagonal), placed 64 B further on so that its
 // broadcast reads fall in other banks than the chunks read by the lanes
 // inside the diagonal.
-__host__ __device__ constexpr int gemm_zero(int qt, int tp) { return 8 * gemm_slot(qt, tp) + 2048 + 64; }
+__host__ __device__ constexpr int gemm_zero(int qt, int tp) { return RING * gemm_slot(qt, tp) + 2048 + 64; }
 __host__ __device__ constexpr int diag_region(int qt, int tp) {
   return gemm_zero(qt, tp) + mx_chunks(qt) * tp * 16 > 4096 ? gemm_zero(qt, tp) + mx_chunks(qt) * tp * 16 : 4096;
 }
-// Dense LDS per wave (16 token slots): a ring of 4 block slots (its records
-// are 3 KB each and L2-resident, so four blocks ahead suffice and twice as
-// many workgroups fit), then the block's int8 rows as two planes (elements
-// 0..15 and 16..31) [2][64][16 B], its row scales [64] fp32 and 16 zero bytes.
+// Dense LDS per wave (16 token slots): the ring, then the block's int8 rows
+// as two planes (elements 0..15 and 16..31) [2][64][16 B], its row scales
+// [64] fp32 and 16 zero bytes.
 constexpr int DENSE_TP = 16;
-constexpr int DENSE_RING = 4;
-__host__ __device__ constexpr int dense_abuf(int qt) { return DENSE_RING * gemm_slot(qt, DENSE_TP); }
+__host__ __device__ constexpr int dense_abuf(int qt) { return RING * gemm_slot(qt, DENSE_TP); }
 __host__ __device__ constexpr int dense_region(int qt) { return dense_abuf(qt) + 64 * 32 + 64 * 4 + 16; }
 // Either kernel's epilogue reuses the start of each wave's region for
 // 16 tokens x 64 rows of sums.
@@ -135,43 +137,45 @@ __device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t rs, int blk, in
   }
 }
 
-// One tile: for each block wait for its ring slot, multiply, fold into
-// acc[group][i], then refill the slot with the same block of the next tile.
-// nb: blocks of this tile; nbn: blocks of the next tile (0: none), whose
-// weights were requested after this tile's digits.
+// One tile: for each block wait for its ring slot (b mod 4), multiply, fold
+// into acc[group][i]; then refill the slot with the block four places on
+// (b + 4 of this tile, or b - 4 of the next).  kb: first block of this tile;
+// nb: its blocks; nbn: blocks of the next tile (0: none), whose weights were
+// requested at the start of this tile.
 template <int QT, int NG>
-__device__ __forceinline__ void tile_diag(const TileRegs<QT>& r, int nb, __amdgpu_buffer_rsrc_t rs, int kb_next,
-                                          int nbn, int T, uint8_t* ring, float (&acc)[NG][4]) {
+__device__ __forceinline__ void tile_diag(const TileRegs<QT>& r, int kb, int nb, __amdgpu_buffer_rsrc_t rs,
+                                          int kb_next, int nbn, int T, uint8_t* ring, float (&acc)[NG][4]) {
   constexpr int NCH = QT == QT_Q4 ? 12 : 6;
   constexpr int TP = 4 * NG;
   constexpr int SLOT = gemm_slot(QT, TP);
   constexpr int DPB = gemm_dpb(QT, TP);
   constexpr int NW = TB * TileRegs<QT>::NH + 1;   // weight loads of a full tile
-  static_assert(7 * DPB + NW <= 63, "vmcnt holds at most 63 outstanding loads");
+  static_assert(3 * DPB + NW <= 63, "vmcnt holds at most 63 outstanding loads");
   const int lane = threadIdx.x & 63;
   const bool bvalid = ((lane & 15) >> 2) == (lane >> 4);   // B lane inside the diagonal
   const int rbase = 16 * ((lane & 15) >> 2) + 4 * (lane >> 4);
   const uint8_t* zero = ring + gemm_zero(QT, TP);
   // the tile's scales, transposed: sct[b][row] (one 16-byte read per block
   // gives this lane's four rows)
-  float* sct = reinterpret_cast<float*>(ring + 8 * SLOT);
+  float* sct = reinterpret_cast<float*>(ring + RING * SLOT);
 #pragma unroll
   for (int b = 0; b < TB; ++b) sct[b * 64 + lane] = scale_of(r.sc, b);
   SLQ_COMPILER_FENCE();
 #pragma unroll
   for (int b = 0; b < TB; ++b) {
     if (b < nb) {
-      // Ring slot b was filled by the DPB loads issued after block b of the
-      // previous tile (or in the prologue).  Issued later than those, in this
-      // order: slots b+1..7, the next tile's weights (NW loads, always) and the
-      // refills of slots 0..b-1 made in this tile (DPB each, always).  Loads
-      // complete in issue order, so slot b has landed once at most
-      // (7 - b) DPB + NW + b DPB = 7 DPB + NW are outstanding.  (In a wave's
-      // first tile the epilogue inputs fetched after the prologue make this
-      // wait a little longer than needed, never shorter.)
-      __builtin_amdgcn_s_waitcnt(vmcnt_imm(7 * DPB + NW));
+      // Block b's record was copied (DPB loads, always) after block b - 4 (of
+      // the previous tile for b < 4, or in the prologue).  Issued later than
+      // that copy: the copies after blocks b-3..b-1 (3 DPB) and, for b < 4,
+      // the next tile's weights (NW loads, always), requested at this tile's
+      // start.  Loads complete in issue order, so the record has landed once
+      // at most 3 DPB (+ NW for b < 4) are outstanding.  (In a wave's first
+      // tile the epilogue inputs fetched after the prologue make this wait a
+      // little longer than needed, never shorter.)
+      if (b < 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DPB + NW));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DPB));
       SLQ_COMPILER_FENCE();
-      const uint8_t* slot = ring + b * SLOT;
+      const uint8_t* slot = ring + (b % RING) * SLOT;
       const i32x4 z = {0, 0, 0, 0};
       u32x4 a0, a1;   // A operands: elements 0..15 and 16..31 of the lane's row
       if constexpr (QT == QT_Q4) {
@@ -234,10 +238,12 @@ __device__ __forceinline__ void tile_diag(const TileRegs<QT>& r, int nb, __amdgp
         }
       }
     }
-    // refill slot b with block b of the next tile; where there is none, a
-    // dummy copy of block 0 into the unused slot keeps the load count fixed
+    // refill slot b mod 4 with the block four places on; where there is
+    // none, a dummy copy of block 0 into the unused slot keeps the load
+    // count fixed
     SLQ_COMPILER_FENCE();
-    dma_block<QT, DPB>(rs, b < nbn ? kb_next + b : 0, TP, ring + b * SLOT);
+    const int nxt = b < 4 ? (b + 4 < nb ? kb + b + 4 : 0) : (b - 4 < nbn ? kb_next + b - 4 : 0);
+    dma_block<QT, DPB>(rs, nxt, TP, ring + (b % RING) * SLOT);
     SLQ_COMPILER_FENCE();
   }
 }
@@ -302,7 +308,7 @@ __device__ __forceinline__ void tile_dense(const TileRegs<QT>& w, int kb, int nb
       sbuf[lane] = scale_of(w.sc, b);
       // (LDS accesses of one wave take effect in program order: the reads
       // below see these writes)
-      const uint8_t* slot = ring + (b % DENSE_RING) * SLOT;
+      const uint8_t* slot = ring + (b % RING) * SLOT;
       i32x4 bq[3];
 #pragma unroll
       for (int p = 0; p < 3; ++p) bq[p] = *reinterpret_cast<const i32x4*>(slot + ((c0 + p * cstep) * TP + s) * 16);
@@ -333,7 +339,7 @@ __device__ __forceinline__ void tile_dense(const TileRegs<QT>& w, int kb, int nb
     // count fixed
     SLQ_COMPILER_FENCE();
     const int nxt = b < 4 ? (b + 4 < nb ? kb + b + 4 : 0) : (b - 4 < nbn ? kb_next + b - 4 : 0);
-    dma_block<QT, DPB>(rs, nxt, TP, ring + (b % DENSE_RING) * SLOT);
+    dma_block<QT, DPB>(rs, nxt, TP, ring + (b % RING) * SLOT);
     SLQ_COMPILER_FENCE();
   }
 }
@@ -429,12 +435,12 @@ __global__ __launch_bounds__(512) void k_gemm_diag(Packed W, Act x, NormIn nin, 
   const __amdgpu_buffer_rsrc_t rs = mx_rsrc(x, QT);
   TileRegs<QT> A, B;
   if (t0 < t1) {
-    // prologue: tile t0's weights, then its digits into the ring (all 8
-    // slots, block 0 again past a ragged tile's end)
+    // prologue: tile t0's weights, then the records of its first 4 blocks
+    // into the ring (block 0 again past a ragged tile's end)
     load_tile_fixed<QT>(base + (size_t)t0 * TBY, lane, nb_of(t0), A);
     SLQ_COMPILER_FENCE();
 #pragma unroll
-    for (int b = 0; b < TB; ++b)
+    for (int b = 0; b < RING; ++b)
       dma_block<QT, gemm_dpb(QT, TP)>(rs, b < nb_of(t0) ? t0 * TB + b : 0, TP, ring + b * gemm_slot(QT, TP));
     SLQ_COMPILER_FENCE();
   }
@@ -457,12 +463,12 @@ __global__ __launch_bounds__(512) void k_gemm_diag(Packed W, Act x, NormIn nin, 
       const bool n1 = t + 1 < t1;
       load_tile_fixed<QT>(base + (size_t)(n1 ? t + 1 : t) * TBY, lane, n1 ? nb_of(t + 1) : 0, B);
       SLQ_COMPILER_FENCE();
-      tile_diag<QT, NG>(A, nb_of(t), rs, (t + 1) * TB, n1 ? nb_of(t + 1) : 0, T, ring, acc);
+      tile_diag<QT, NG>(A, t * TB, nb_of(t), rs, (t + 1) * TB, n1 ? nb_of(t + 1) : 0, T, ring, acc);
       if (!n1) break;
       const bool n2 = t + 2 < t1;
       load_tile_fixed<QT>(base + (size_t)(n2 ? t + 2 : t + 1) * TBY, lane, n2 ? nb_of(t + 2) : 0, A);
       SLQ_COMPILER_FENCE();
-      tile_diag<QT, NG>(B, nb_of(t + 1), rs, (t + 2) * TB, n2 ? nb_of(t + 2) : 0, T, ring, acc);
+      tile_diag<QT, NG>(B, (t + 1) * TB, nb_of(t + 1), rs, (t + 2) * TB, n2 ? nb_of(t + 2) : 0, T, ring, acc);
     }
     // the dummy refills of the last tile still write the ring, which the
     // reduction below reuses
@@ -564,7 +570,7 @@ __global__ __launch_bounds__(512) void k_gemm_dense(Packed W, Act x, NormIn nin,
     load_tile_fixed<QT>(base + (size_t)t0 * TBY, lane, nb_of(t0), A);
     SLQ_COMPILER_FENCE();
 #pragma unroll
-    for (int b = 0; b < DENSE_RING; ++b)
+    for (int b = 0; b < RING; ++b)
       dma_block<QT, gemm_dpb(QT, TP)>(rs, b < nb_of(t0) ? t0 * TB + b : 0, TP, ring + b * gemm_slot(QT, TP));
     SLQ_COMPILER_FENCE();
   }
