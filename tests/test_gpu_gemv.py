@@ -98,6 +98,32 @@ def test_gemm_batch_equals_single_bitwise(qtype, ks, w, rows, cols, monkeypatch)
 
 
 @pytest.mark.parametrize("qtype", QTYPES)
+@pytest.mark.parametrize("batch,min_t", [(1, "0"), (5, "17"), (5, "2"), (16, "2")])
+def test_split_tickets_reset_on_reuse(qtype, batch, min_t, monkeypatch):
+    """The split that takes a row group's last ticket resets it: one workspace
+    reused for different inputs gives each call the result of a fresh
+    workspace, and its tickets end at zero.  (min_t 17 keeps a 5-token call on
+    the per-row GEMV, 2 sends it to the MFMA products.)"""
+    ks, w = 5, 2
+    monkeypatch.setenv("SLQ_KS_GEMV", str(ks))
+    monkeypatch.setenv("SLQ_W_GEMV", str(w))
+    monkeypatch.setenv("SLQ_MFMA_MIN_T", min_t)
+    rows, cols = 1000, 32 * 37
+    raw = _raw(qtype, rows, cols, 14)
+    packed = slq.repack(qtype, _dev(raw), rows, cols)
+    xa = synth.gemv_x(21, batch, cols)
+    xb = synth.gemv_x(22, batch, cols)
+    fresh_a = slq.gemv(qtype, packed, rows, cols, _dev(xa)).cpu().numpy()
+    fresh_b = slq.gemv(qtype, packed, rows, cols, _dev(xb)).cpu().numpy()
+    ws = torch.zeros(slq.gemv_workspace_bytes(qtype, rows, cols, batch), dtype=torch.uint8, device="cuda")
+    for x, ref in ((xa, fresh_a), (xb, fresh_b), (xa, fresh_a)):
+        y = slq.gemv(qtype, packed, rows, cols, _dev(x), ws=ws).cpu().numpy()
+        np.testing.assert_array_equal(y, ref)
+    # the workspace ends with the 16 row groups' tickets (one 256-byte line)
+    assert int(torch.count_nonzero(ws[-256:])) == 0
+
+
+@pytest.mark.parametrize("qtype", QTYPES)
 def test_gemm_single_token_through_mfma(qtype, monkeypatch):
     """With the MFMA path forced for one token the result equals the GEMV's."""
     rows, cols = 1000, 32 * 37
