@@ -39,8 +39,10 @@
 // (r, i = 0..3) of token slot l % 16.
 //
 // In both, the weights stream into registers one tile ahead, lane = row, as in
-// the GEMV, and the records of the blocks in use come into a ring of 4 block
-// slots in the wave's LDS by buffer loads into LDS, four blocks ahead.  Each ring
+// the GEMV but block by block into one register set (each block's registers
+// are refilled with the next tile's block as soon as they are used), and the
+// records of the blocks in use come into a ring of 4 block slots in the
+// wave's LDS by buffer loads into LDS, four blocks ahead.  Each ring
 // wait is an explicit vmcnt that leaves the next tile's weights and the
 // refills issued after them in flight, so no read of the ring waits for them.
 #pragma once
@@ -71,11 +73,11 @@ __host__ __device__ constexpr int diag_region(int qt, int tp) {
   return gemm_zero(qt, tp) + mx_chunks(qt) * tp * 16 > 4096 ? gemm_zero(qt, tp) + mx_chunks(qt) * tp * 16 : 4096;
 }
 // Dense LDS per wave (16 token slots): the ring, then the block's int8 rows
-// as two planes (elements 0..15 and 16..31) [2][64][16 B], its row scales
-// [64] fp32 and 16 zero bytes.
+// as two planes (elements 0..15 and 16..31) [2][64][16 B], the tile's row
+// scales [8 blocks][64 rows] fp32 and 16 zero bytes.
 constexpr int DENSE_TP = 16;
 __host__ __device__ constexpr int dense_abuf(int qt) { return RING * gemm_slot(qt, DENSE_TP); }
-__host__ __device__ constexpr int dense_region(int qt) { return dense_abuf(qt) + 64 * 32 + 64 * 4 + 16; }
+__host__ __device__ constexpr int dense_region(int qt) { return dense_abuf(qt) + 64 * 32 + TB * 64 * 4 + 16; }
 // Either kernel's epilogue reuses the start of each wave's region for
 // 16 tokens x 64 rows of sums.
 __host__ __device__ constexpr int gemm_region(int qt, int T) {
@@ -137,20 +139,23 @@ __device__ __forceinline__ void dma_block(__amdgpu_buffer_rsrc_t rs, int blk, in
   }
 }
 
-// One tile: for each block wait for its ring slot (b mod 4), multiply, fold
-// into acc[group][i]; then refill the slot with the block four places on
-// (b + 4 of this tile, or b - 4 of the next).  kb: first block of this tile;
-// nb: its blocks; nbn: blocks of the next tile (0: none), whose weights were
-// requested at the start of this tile.
+// One tile: for each block wait for its record's ring slot (b mod 4),
+// multiply and fold into acc[group][i]; then (one step) refill the block's
+// weight registers with the same block of the next tile and the ring slot
+// with the record four blocks on (b + 4 of this tile, or b - 4 of the next).
+// The next tile's weights thus arrive one block at a time, a tile ahead of
+// their use, in the one register set.  kb: first block of this tile; nb: its
+// blocks; ntile, nbn: the next tile's bytes and blocks (nbn = 0: none).
 template <int QT, int NG>
-__device__ __forceinline__ void tile_diag(const TileRegs<QT>& r, int kb, int nb, __amdgpu_buffer_rsrc_t rs,
-                                          int kb_next, int nbn, int T, uint8_t* ring, float (&acc)[NG][4]) {
+__device__ __forceinline__ void tile_diag(TileRegs<QT>& r, int kb, int nb, __amdgpu_buffer_rsrc_t rs,
+                                          const uint8_t* ntile, int kb_next, int nbn, int T, uint8_t* ring,
+                                          float (&acc)[NG][4]) {
   constexpr int NCH = QT == QT_Q4 ? 12 : 6;
+  constexpr int NH = TileRegs<QT>::NH;
   constexpr int TP = 4 * NG;
   constexpr int SLOT = gemm_slot(QT, TP);
   constexpr int DPB = gemm_dpb(QT, TP);
-  constexpr int NW = TB * TileRegs<QT>::NH + 1;   // weight loads of a full tile
-  static_assert(3 * DPB + NW <= 63, "vmcnt holds at most 63 outstanding loads");
+  static_assert(3 * (NH + DPB) + 1 <= 63, "vmcnt holds at most 63 outstanding loads");
   const int lane = threadIdx.x & 63;
   const bool bvalid = ((lane & 15) >> 2) == (lane >> 4);   // B lane inside the diagonal
   const int rbase = 16 * ((lane & 15) >> 2) + 4 * (lane >> 4);
@@ -161,19 +166,21 @@ __device__ __forceinline__ void tile_diag(const TileRegs<QT>& r, int kb, int nb,
 #pragma unroll
   for (int b = 0; b < TB; ++b) sct[b * 64 + lane] = scale_of(r.sc, b);
   SLQ_COMPILER_FENCE();
+  r.sc = load_scales_fixed(ntile, lane, nbn, NH);
+  SLQ_COMPILER_FENCE();
 #pragma unroll
   for (int b = 0; b < TB; ++b) {
     if (b < nb) {
-      // Block b's record was copied (DPB loads, always) after block b - 4 (of
-      // the previous tile for b < 4, or in the prologue).  Issued later than
-      // that copy: the copies after blocks b-3..b-1 (3 DPB) and, for b < 4,
-      // the next tile's weights (NW loads, always), requested at this tile's
-      // start.  Loads complete in issue order, so the record has landed once
-      // at most 3 DPB (+ NW for b < 4) are outstanding.  (In a wave's first
-      // tile the epilogue inputs fetched after the prologue make this wait a
-      // little longer than needed, never shorter.)
-      if (b < 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DPB + NW));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DPB));
+      // Block b's record was copied (DPB loads, always) at the end of the step
+      // after block b - 4 (of the previous tile for b < 4).  Issued later: the
+      // next three steps (NH weight and DPB copy loads each, always) and, for
+      // b < 4, this tile's scale load.  Loads complete in issue order, so the
+      // record has landed once at most 3 (NH + DPB) (+ 1 for b < 4) are
+      // outstanding.  (In a wave's first tile the prologue copied blocks 0..3
+      // before the tile's weights, so more loads follow those copies: the wait
+      // is longer than needed there, never shorter.)
+      if (b < 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * (NH + DPB) + 1));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * (NH + DPB)));
       SLQ_COMPILER_FENCE();
       const uint8_t* slot = ring + (b % RING) * SLOT;
       const i32x4 z = {0, 0, 0, 0};
@@ -238,34 +245,38 @@ __device__ __forceinline__ void tile_diag(const TileRegs<QT>& r, int kb, int nb,
         }
       }
     }
-    // refill slot b mod 4 with the block four places on; where there is
-    // none, a dummy copy of block 0 into the unused slot keeps the load
-    // count fixed
+    // the step: block b of the next tile into the registers just used, and
+    // the record four blocks on into slot b mod 4; where there is none, dummy
+    // loads (the last block again, or block 0's record into the unused slot)
+    // keep the load count fixed
     SLQ_COMPILER_FENCE();
+    load_block_fixed<QT>(ntile, lane, nbn, b, r);
     const int nxt = b < 4 ? (b + 4 < nb ? kb + b + 4 : 0) : (b - 4 < nbn ? kb_next + b - 4 : 0);
     dma_block<QT, DPB>(rs, nxt, TP, ring + (b % RING) * SLOT);
     SLQ_COMPILER_FENCE();
   }
 }
 
-// One tile: for each block wait for its ring slot (b mod 4), stage the
-// block's rows and scales, multiply, fold into acc[r][i]; then refill the slot
-// with the block four places on (b + 4 of this tile, or b - 4 of the next).
-// kb: first block of this tile; nb: its blocks; nbn: blocks of the next tile
-// (0: none), whose weights were requested at the start of this tile.
+// One tile: for each block wait for its record's ring slot (b mod 4), stage
+// the block's rows and scales, multiply, fold into acc[r][i]; then (one step)
+// refill the block's weight registers with the same block of the next tile
+// and the ring slot with the record four blocks on (b + 4 of this tile, or
+// b - 4 of the next).  kb: first block of this tile; nb: its blocks; ntile,
+// nbn: the next tile's bytes and blocks (nbn = 0: none).
 template <int QT, int TP>
-__device__ __forceinline__ void tile_dense(const TileRegs<QT>& w, int kb, int nb, __amdgpu_buffer_rsrc_t rs,
-                                           int kb_next, int nbn, uint8_t* ring, float (&acc)[4][4]) {
+__device__ __forceinline__ void tile_dense(TileRegs<QT>& w, int kb, int nb, __amdgpu_buffer_rsrc_t rs,
+                                           const uint8_t* ntile, int kb_next, int nbn, uint8_t* ring,
+                                           float (&acc)[4][4]) {
   constexpr int NCH = QT == QT_Q4 ? 12 : 6;
+  constexpr int NH = TileRegs<QT>::NH;
   constexpr int SLOT = gemm_slot(QT, TP);
   constexpr int DPB = gemm_dpb(QT, TP);
-  constexpr int NW = TB * TileRegs<QT>::NH + 1;   // weight loads of a full tile
-  static_assert(3 * DPB + NW <= 63, "vmcnt holds at most 63 outstanding loads");
+  static_assert(3 * (NH + DPB) + 1 <= 63, "vmcnt holds at most 63 outstanding loads");
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, s = lane & 15;         // k-group and token slot (row in the tile) of this lane
   uint8_t* abuf = ring + dense_abuf(QT);
-  float* sbuf = reinterpret_cast<float*>(abuf + 64 * 32);
-  const uint8_t* zero16 = abuf + 64 * 32 + 64 * 4;
+  float* sct = reinterpret_cast<float*>(abuf + 64 * 32);
+  const uint8_t* zero16 = abuf + 64 * 32 + TB * 64 * 4;
   // this lane's A source in row tile r: row 16 r + s, elements 16 (g & 1) ..
   // (plane g & 1 of the staged rows; 16 lanes read 256 contiguous bytes)
   const uint8_t* asrc = (QT == QT_Q8 && g >= 2) ? zero16 : abuf + (g & 1) * 64 * 16 + s * 16;
@@ -273,21 +284,28 @@ __device__ __forceinline__ void tile_dense(const TileRegs<QT>& w, int kb, int nb
   // this lane's B chunk for digit (pair) p is c0 + p * cstep
   const int c0 = QT == QT_Q4 ? g : (g & 1);
   constexpr int cstep = QT == QT_Q4 ? 4 : 2;
+  // the tile's scales, transposed: sct[b][row]; then w.sc takes the next
+  // tile's
+#pragma unroll
+  for (int b = 0; b < TB; ++b) sct[b * 64 + lane] = scale_of(w.sc, b);
+  SLQ_COMPILER_FENCE();
+  w.sc = load_scales_fixed(ntile, lane, nbn, NH);
+  SLQ_COMPILER_FENCE();
 #pragma unroll
   for (int b = 0; b < TB; ++b) {
     if (b < nb) {
-      // Block b's record was copied (DPB loads, always) after block b - 4 (of
-      // the previous tile for b < 4, or in the prologue).  Issued later than
-      // that copy: the copies after blocks b-3..b-1 (3 DPB) and, for b < 4,
-      // the next tile's weights (NW loads, always), requested at this tile's
-      // start.  Loads complete in issue order, so the record has landed once
-      // at most 3 DPB (+ NW for b < 4) are outstanding.  (In a wave's first
-      // tile the epilogue inputs fetched after the prologue make this wait a
-      // little longer than needed, never shorter.)
-      if (b < 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DPB + NW));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * DPB));
+      // Block b's record was copied (DPB loads, always) at the end of the step
+      // after block b - 4 (of the previous tile for b < 4).  Issued later: the
+      // next three steps (NH weight and DPB copy loads each, always) and, for
+      // b < 4, this tile's scale load.  Loads complete in issue order, so the
+      // record has landed once at most 3 (NH + DPB) (+ 1 for b < 4) are
+      // outstanding.  (In a wave's first tile the prologue copied blocks 0..3
+      // before the tile's weights, so more loads follow those copies: the wait
+      // is longer than needed there, never shorter.)
+      if (b < 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * (NH + DPB) + 1));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * (NH + DPB)));
       SLQ_COMPILER_FENCE();
-      // stage row `lane` of block b: elements 0..31 as int8, and its scale
+      // stage row `lane` of block b: elements 0..31 as int8
       u32x4 lo, hi;
       if constexpr (QT == QT_Q4) {
         const u32x4 c = w.c[b];
@@ -305,7 +323,6 @@ __device__ __forceinline__ void tile_dense(const TileRegs<QT>& w, int kb, int nb
       }
       reinterpret_cast<u32x4*>(abuf)[lane] = lo;
       reinterpret_cast<u32x4*>(abuf + 64 * 16)[lane] = hi;
-      sbuf[lane] = scale_of(w.sc, b);
       // (LDS accesses of one wave take effect in program order: the reads
       // below see these writes)
       const uint8_t* slot = ring + (b % RING) * SLOT;
@@ -317,11 +334,12 @@ __device__ __forceinline__ void tile_dense(const TileRegs<QT>& w, int kb, int nb
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const i32x4 A = *reinterpret_cast<const i32x4*>(asrc + r * astep);
-        const float4 d4 = *reinterpret_cast<const float4*>(sbuf + 16 * r + 4 * g);
+        float dd[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dd[i] = sct[b * 64 + 16 * r + 4 * g + i];
         const i32x4 P0 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bq[0], z, 0, 0, 0);
         const i32x4 P1 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bq[1], z, 0, 0, 0);
         const i32x4 P2 = __builtin_amdgcn_mfma_i32_16x16x64_i8(A, bq[2], z, 0, 0, 0);
-        const float dd[4] = {d4.x, d4.y, d4.z, d4.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           float bf;
@@ -334,10 +352,12 @@ __device__ __forceinline__ void tile_dense(const TileRegs<QT>& w, int kb, int nb
         }
       }
     }
-    // refill slot b mod 4 with the block four places on; where there is
-    // none, a dummy copy of block 0 into the unused slot keeps the load
-    // count fixed
+    // the step: block b of the next tile into the registers just used, and
+    // the record four blocks on into slot b mod 4; where there is none, dummy
+    // loads (the last block again, or block 0's record into the unused slot)
+    // keep the load count fixed
     SLQ_COMPILER_FENCE();
+    load_block_fixed<QT>(ntile, lane, nbn, b, w);
     const int nxt = b < 4 ? (b + 4 < nb ? kb + b + 4 : 0) : (b - 4 < nbn ? kb_next + b - 4 : 0);
     dma_block<QT, DPB>(rs, nxt, TP, ring + (b % RING) * SLOT);
     SLQ_COMPILER_FENCE();
@@ -433,15 +453,15 @@ __global__ __launch_bounds__(512) void k_gemm_diag(Packed W, Act x, NormIn nin, 
     for (int i = 0; i < 4; ++i) acc[g][i] = 0.0f;
 
   const __amdgpu_buffer_rsrc_t rs = mx_rsrc(x, QT);
-  TileRegs<QT> A, B;
+  TileRegs<QT> R;
   if (t0 < t1) {
-    // prologue: tile t0's weights, then the records of its first 4 blocks
-    // into the ring (block 0 again past a ragged tile's end)
-    load_tile_fixed<QT>(base + (size_t)t0 * TBY, lane, nb_of(t0), A);
-    SLQ_COMPILER_FENCE();
+    // prologue: the records of tile t0's first 4 blocks into the ring (block
+    // 0 again past a ragged tile's end), then the tile's weights
 #pragma unroll
     for (int b = 0; b < RING; ++b)
       dma_block<QT, gemm_dpb(QT, TP)>(rs, b < nb_of(t0) ? t0 * TB + b : 0, TP, ring + b * gemm_slot(QT, TP));
+    SLQ_COMPILER_FENCE();
+    load_tile_fixed<QT>(base + (size_t)t0 * TBY, lane, nb_of(t0), R);
     SLQ_COMPILER_FENCE();
   }
 
@@ -457,19 +477,18 @@ __global__ __launch_bounds__(512) void k_gemm_diag(Packed W, Act x, NormIn nin, 
   SLQ_COMPILER_FENCE();
 
   if (t0 < t1) {
-    // Each step loads the next tile's weights (a lane-uniform dummy after the
-    // wave's last tile) before the math of this one.
-    for (int t = t0; t < t1; t += 2) {
+    // each tile refills the registers with the next tile's weights (lane-
+    // uniform dummies after the wave's last tile).  The first tile runs
+    // before the loop, so the loop is entered in the same state as it loops
+    // back, and the compiler's waits on the refilled registers stay exact
+    // instead of draining every load at the top of each tile.
+    auto one = [&](int t) {
       const bool n1 = t + 1 < t1;
-      load_tile_fixed<QT>(base + (size_t)(n1 ? t + 1 : t) * TBY, lane, n1 ? nb_of(t + 1) : 0, B);
-      SLQ_COMPILER_FENCE();
-      tile_diag<QT, NG>(A, t * TB, nb_of(t), rs, (t + 1) * TB, n1 ? nb_of(t + 1) : 0, T, ring, acc);
-      if (!n1) break;
-      const bool n2 = t + 2 < t1;
-      load_tile_fixed<QT>(base + (size_t)(n2 ? t + 2 : t + 1) * TBY, lane, n2 ? nb_of(t + 2) : 0, A);
-      SLQ_COMPILER_FENCE();
-      tile_diag<QT, NG>(B, (t + 1) * TB, nb_of(t + 1), rs, (t + 2) * TB, n2 ? nb_of(t + 2) : 0, T, ring, acc);
-    }
+      tile_diag<QT, NG>(R, t * TB, nb_of(t), rs, base + (size_t)(n1 ? t + 1 : t) * TBY, (t + 1) * TB,
+                        n1 ? nb_of(t + 1) : 0, T, ring, acc);
+    };
+    one(t0);
+    for (int t = t0 + 1; t < t1; ++t) one(t);
     // the dummy refills of the last tile still write the ring, which the
     // reduction below reuses
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
@@ -554,7 +573,7 @@ __global__ __launch_bounds__(512) void k_gemm_dense(Packed W, Act x, NormIn nin,
   const uint8_t* base = W.w + (size_t)rg * rg_bytes(QT, W.cols);
   uint8_t* ring = lds + (size_t)wave * REGION;
   auto nb_of = [&](int t) { return t < full ? TB : nblk - full * TB; };
-  if (lane == 0) *reinterpret_cast<u32x4*>(ring + dense_abuf(QT) + 64 * 32 + 64 * 4) = u32x4{0u, 0u, 0u, 0u};
+  if (lane == 0) *reinterpret_cast<u32x4*>(ring + dense_abuf(QT) + 64 * 32 + TB * 64 * 4) = u32x4{0u, 0u, 0u, 0u};
 
   float acc[4][4];
 #pragma unroll
@@ -563,15 +582,15 @@ __global__ __launch_bounds__(512) void k_gemm_dense(Packed W, Act x, NormIn nin,
     for (int i = 0; i < 4; ++i) acc[r][i] = 0.0f;
 
   const __amdgpu_buffer_rsrc_t rs = mx_rsrc(x, QT);
-  TileRegs<QT> A, B;
+  TileRegs<QT> R;
   if (t0 < t1) {
-    // prologue: tile t0's weights, then the records of its first 4 blocks
-    // into the ring (block 0 again past a ragged tile's end)
-    load_tile_fixed<QT>(base + (size_t)t0 * TBY, lane, nb_of(t0), A);
-    SLQ_COMPILER_FENCE();
+    // prologue: the records of tile t0's first 4 blocks into the ring (block
+    // 0 again past a ragged tile's end), then the tile's weights
 #pragma unroll
     for (int b = 0; b < RING; ++b)
       dma_block<QT, gemm_dpb(QT, TP)>(rs, b < nb_of(t0) ? t0 * TB + b : 0, TP, ring + b * gemm_slot(QT, TP));
+    SLQ_COMPILER_FENCE();
+    load_tile_fixed<QT>(base + (size_t)t0 * TBY, lane, nb_of(t0), R);
     SLQ_COMPILER_FENCE();
   }
 
@@ -587,19 +606,16 @@ __global__ __launch_bounds__(512) void k_gemm_dense(Packed W, Act x, NormIn nin,
   SLQ_COMPILER_FENCE();
 
   if (t0 < t1) {
-    // Each step loads the next tile's weights (a lane-uniform dummy after the
-    // wave's last tile) before the math of this one.
-    for (int t = t0; t < t1; t += 2) {
+    // each tile refills the registers with the next tile's weights (lane-
+    // uniform dummies after the wave's last tile); the first tile runs before
+    // the loop, as in the block-diagonal form
+    auto one = [&](int t) {
       const bool n1 = t + 1 < t1;
-      load_tile_fixed<QT>(base + (size_t)(n1 ? t + 1 : t) * TBY, lane, n1 ? nb_of(t + 1) : 0, B);
-      SLQ_COMPILER_FENCE();
-      tile_dense<QT, TP>(A, t * TB, nb_of(t), rs, (t + 1) * TB, n1 ? nb_of(t + 1) : 0, ring, acc);
-      if (!n1) break;
-      const bool n2 = t + 2 < t1;
-      load_tile_fixed<QT>(base + (size_t)(n2 ? t + 2 : t + 1) * TBY, lane, n2 ? nb_of(t + 2) : 0, A);
-      SLQ_COMPILER_FENCE();
-      tile_dense<QT, TP>(B, (t + 1) * TB, nb_of(t + 1), rs, (t + 2) * TB, n2 ? nb_of(t + 2) : 0, ring, acc);
-    }
+      tile_dense<QT, TP>(R, t * TB, nb_of(t), rs, base + (size_t)(n1 ? t + 1 : t) * TBY, (t + 1) * TB,
+                         n1 ? nb_of(t + 1) : 0, ring, acc);
+    };
+    one(t0);
+    for (int t = t0 + 1; t < t1; ++t) one(t);
     // the dummy refills of the last tile still write the ring, which the
     // reduction below reuses
     __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));

@@ -46,6 +46,25 @@ __device__ __forceinline__ void load_tile_fixed(const uint8_t* tile, int lane, i
   r.sc = __builtin_nontemporal_load(nb ? reinterpret_cast<const u32x4*>(tile + (size_t)nc * RG * 16) + lane : cp);
 }
 
+// One block's codes of a tile (r.c[b * NH + h], h < NH) with always NH loads,
+// and the tile's scales (r.sc) with always one, choosing their sources as
+// load_tile_fixed does; together they issue its loads one block at a time.
+template <int QT>
+__device__ __forceinline__ void load_block_fixed(const uint8_t* tile, int lane, int nb, int b, TileRegs<QT>& r) {
+  constexpr int NH = TileRegs<QT>::NH;
+  const int nc = nb * NH;
+  const u32x4* cp = reinterpret_cast<const u32x4*>(tile) + (nb ? lane : 0);
+#pragma unroll
+  for (int h = 0; h < NH; ++h) {
+    const int i = b * NH + h;
+    r.c[i] = __builtin_nontemporal_load(cp + (nb ? (i < nc ? i : nc - 1) : 0) * RG);
+  }
+}
+__device__ __forceinline__ u32x4 load_scales_fixed(const uint8_t* tile, int lane, int nb, int nh) {
+  const u32x4* cp = reinterpret_cast<const u32x4*>(tile) + (nb ? lane : 0);
+  return __builtin_nontemporal_load(nb ? reinterpret_cast<const u32x4*>(tile + (size_t)nb * nh * RG * 16) + lane : cp);
+}
+
 __device__ __forceinline__ float scale_of(const u32x4& sc, int b) {
   const uint32_t w = b < 2 ? sc.x : b < 4 ? sc.y : b < 6 ? sc.z : sc.w;
   const unsigned short hb = (unsigned short)((b & 1) ? (w >> 16) : (w & 0xffff));
