@@ -165,6 +165,26 @@ def run_verify(s, H, rounds, k, seed):
             "verified_tok_s": rounds * k / sec}
 
 
+def run_prefill(s, H, chunks, k=16):
+    """Prompt ingestion as batched passes: verify k fresh tokens and commit all
+    of them, chunk after chunk (HIP events around the chunks)."""
+    import torch
+    out = torch.empty((k, H.shape[1]), dtype=torch.float16, device="cuda")
+    s.verify(H[0:k], out)          # warm the k-token graph
+    s.commit(0)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for c in range(chunks):
+        s.verify(H[c * k:(c + 1) * k], out)
+        s.commit(k)
+    ev1.record()
+    torch.cuda.synchronize()
+    sec = ev0.elapsed_time(ev1) / 1e3
+    return {"tokens_per_pass": k, "passes": chunks, "ms_per_pass": round(sec / chunks * 1e3, 3),
+            "tok_s": round(chunks * k / sec, 1)}
+
+
 def gemv_sweep(seed, reps):
     import torch
     import synth
@@ -247,6 +267,7 @@ def main() -> int:
     ap.add_argument("--profile-steps", type=int, default=4)
     ap.add_argument("--gemv-reps", type=int, default=8, help="repetitions of the 64-layer GEMV timing runs")
     ap.add_argument("--verify-rounds", type=int, default=32)
+    ap.add_argument("--prefill-chunks", type=int, default=8, help="16-token verify+commit passes timed as prefill")
     ap.add_argument("--cpu-tokens", type=int, default=2)
     ap.add_argument("--sweep-reps", type=int, default=50)
     ap.add_argument("--no-q8", action="store_true")
@@ -267,7 +288,7 @@ def main() -> int:
     torch.cuda.set_device(0)
     threads = min(16, os.cpu_count() or 8)
     shape = synth.HYBRID_5120
-    n_in = args.warmup + args.steps + args.profile_steps + 4 * (args.verify_rounds + 1) + 16
+    n_in = args.warmup + args.steps + args.profile_steps + 4 * (args.verify_rounds + 1) + 16 * (args.prefill_chunks + 1) + 16
     max_seq = ((PREFILL + n_in + 63) // 64) * 64
     log(f"inputs: {n_in} fresh fp16 hidden states; max_seq {max_seq}")
     H_host = synth.hidden_inputs(args.seed, synth.WL_SLICE, n_in, shape.hidden)
@@ -282,7 +303,7 @@ def main() -> int:
         log("copy calibration: 3 x 512 MiB device-to-device copies")
 
     # ---- Q4_0 slice: timed decode
-    s, tensors = build_slice(shape, synth.Q4_0, max_seq, 4, args.seed, threads)
+    s, tensors = build_slice(shape, synth.Q4_0, max_seq, 16, args.seed, threads)
     sec, wall, gpu_first = time_decode(s, H, args.steps, args.warmup)
     tok_s = args.steps / sec
     log(f"Q4_0 decode: {args.steps} steps in {sec * 1e3:.1f} ms (wall {wall * 1e3:.1f} ms): {tok_s:.1f} tok/s")
@@ -318,6 +339,9 @@ def main() -> int:
     ver = run_verify(s, H[base:], args.verify_rounds, 4, args.seed)
     ver["speedup_vs_4_decodes"] = round(4 * (1.0 / tok_s) / (ver["us_per_verify"] * 1e-6), 3)
     log(f"verify k=4: {ver}")
+    base += 4 * (args.verify_rounds + 1)
+    pre = run_prefill(s, H[base:], args.prefill_chunks) if args.prefill_chunks > 0 else None
+    log(f"prefill (16-token passes): {pre}")
     del s
     torch.cuda.empty_cache()
 
@@ -369,6 +393,7 @@ def main() -> int:
         "eager_ops_us_per_step": {k: round(v[0] * v[1] * 1e3, 1) for k, v in ops.items()},
         "eager_step_ms": round(step_ms, 4),
         "verify": ver,
+        "prefill_16": pre,
     }
     res.update(extra)
     print(json.dumps(res), flush=True)
