@@ -59,10 +59,12 @@ typedef __attribute__((address_space(1))) const void gbl_void_t;
 __host__ __device__ constexpr int gemm_slot(int qt, int tp) { return mx_chunks(qt) * tp * 16 + 64; }
 // copy instructions (64 lanes x 16 B) per block
 __host__ __device__ constexpr int gemm_dpb(int qt, int tp) { return (gemm_slot(qt, tp) / 16 + 63) / 64; }
-// Both kernels keep a ring of 4 block slots per wave: the records are
-// L2-resident, so copies four blocks ahead arrive in time, and a small ring
-// lets more workgroups share a CU.
+// The block-diagonal kernel keeps a ring of 4 block slots per wave: the
+// records are L2-resident, so copies four blocks ahead arrive in time, and a
+// small ring lets more workgroups share a CU.  The dense kernel's records are
+// 3 KB (Q4_0), and LDS bounds its resident waves, so it keeps 2.
 constexpr int RING = 4;
+constexpr int DENSE_RING = 2;
 // Block-diagonal LDS per wave: the ring, the tile's row scales as fp32
 // [8 blocks][64 rows], and a zero area as large as one slot's digits (read by
 // the B lanes outside the diagonal), placed 64 B further on so that its
@@ -76,7 +78,7 @@ __host__ __device__ constexpr int diag_region(int qt, int tp) {
 // as two planes (elements 0..15 and 16..31) [2][64][16 B], the tile's row
 // scales [8 blocks][64 rows] fp32 and 16 zero bytes.
 constexpr int DENSE_TP = 16;
-__host__ __device__ constexpr int dense_abuf(int qt) { return RING * gemm_slot(qt, DENSE_TP); }
+__host__ __device__ constexpr int dense_abuf(int qt) { return DENSE_RING * gemm_slot(qt, DENSE_TP); }
 __host__ __device__ constexpr int dense_region(int qt) { return dense_abuf(qt) + 64 * 32 + TB * 64 * 4 + 16; }
 // Either kernel's epilogue reuses the start of each wave's region for
 // 16 tokens x 64 rows of sums.
@@ -257,11 +259,11 @@ __device__ __forceinline__ void tile_diag(TileRegs<QT>& r, int kb, int nb, __amd
   }
 }
 
-// One tile: for each block wait for its record's ring slot (b mod 4), stage
-// the block's rows and scales, multiply, fold into acc[r][i]; then (one step)
-// refill the block's weight registers with the same block of the next tile
-// and the ring slot with the record four blocks on (b + 4 of this tile, or
-// b - 4 of the next).  kb: first block of this tile; nb: its blocks; ntile,
+// One tile: for each block wait for its record's ring slot (b mod
+// DENSE_RING), stage the block's rows, multiply, fold into acc[r][i]; then
+// (one step) refill the block's weight registers with the same block of the
+// next tile and the ring slot with the record DENSE_RING blocks on (in this
+// tile or the next).  kb: first block of this tile; nb: its blocks; ntile,
 // nbn: the next tile's bytes and blocks (nbn = 0: none).
 template <int QT, int TP>
 __device__ __forceinline__ void tile_dense(TileRegs<QT>& w, int kb, int nb, __amdgpu_buffer_rsrc_t rs,
@@ -271,7 +273,8 @@ __device__ __forceinline__ void tile_dense(TileRegs<QT>& w, int kb, int nb, __am
   constexpr int NH = TileRegs<QT>::NH;
   constexpr int SLOT = gemm_slot(QT, TP);
   constexpr int DPB = gemm_dpb(QT, TP);
-  static_assert(3 * (NH + DPB) + 1 <= 63, "vmcnt holds at most 63 outstanding loads");
+  constexpr int DR = DENSE_RING;
+  static_assert(TB % DR == 0 && (DR - 1) * (NH + DPB) + 1 <= 63, "ring depth");
   const int lane = threadIdx.x & 63;
   const int g = lane >> 4, s = lane & 15;         // k-group and token slot (row in the tile) of this lane
   uint8_t* abuf = ring + dense_abuf(QT);
@@ -295,15 +298,15 @@ __device__ __forceinline__ void tile_dense(TileRegs<QT>& w, int kb, int nb, __am
   for (int b = 0; b < TB; ++b) {
     if (b < nb) {
       // Block b's record was copied (DPB loads, always) at the end of the step
-      // after block b - 4 (of the previous tile for b < 4).  Issued later: the
-      // next three steps (NH weight and DPB copy loads each, always) and, for
-      // b < 4, this tile's scale load.  Loads complete in issue order, so the
-      // record has landed once at most 3 (NH + DPB) (+ 1 for b < 4) are
-      // outstanding.  (In a wave's first tile the prologue copied blocks 0..3
-      // before the tile's weights, so more loads follow those copies: the wait
-      // is longer than needed there, never shorter.)
-      if (b < 4) __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * (NH + DPB) + 1));
-      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(3 * (NH + DPB)));
+      // after block b - DR (of the previous tile for b < DR).  Issued later:
+      // the next DR - 1 steps (NH weight and DPB copy loads each, always) and,
+      // for b < DR, this tile's scale load.  Loads complete in issue order, so
+      // the record has landed once at most (DR - 1)(NH + DPB) (+ 1 for b < DR)
+      // are outstanding.  (In a wave's first tile the prologue copied blocks
+      // 0..DR-1 before the tile's weights, so more loads follow those copies:
+      // the wait is longer than needed there, never shorter.)
+      if (b < DR) __builtin_amdgcn_s_waitcnt(vmcnt_imm((DR - 1) * (NH + DPB) + 1));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm((DR - 1) * (NH + DPB)));
       SLQ_COMPILER_FENCE();
       // stage row `lane` of block b: elements 0..31 as int8
       u32x4 lo, hi;
@@ -325,7 +328,7 @@ __device__ __forceinline__ void tile_dense(TileRegs<QT>& w, int kb, int nb, __am
       reinterpret_cast<u32x4*>(abuf + 64 * 16)[lane] = hi;
       // (LDS accesses of one wave take effect in program order: the reads
       // below see these writes)
-      const uint8_t* slot = ring + (b % RING) * SLOT;
+      const uint8_t* slot = ring + (b % DR) * SLOT;
       i32x4 bq[3];
 #pragma unroll
       for (int p = 0; p < 3; ++p) bq[p] = *reinterpret_cast<const i32x4*>(slot + ((c0 + p * cstep) * TP + s) * 16);
@@ -353,13 +356,13 @@ __device__ __forceinline__ void tile_dense(TileRegs<QT>& w, int kb, int nb, __am
       }
     }
     // the step: block b of the next tile into the registers just used, and
-    // the record four blocks on into slot b mod 4; where there is none, dummy
+    // the record DR blocks on into slot b mod DR; where there is none, dummy
     // loads (the last block again, or block 0's record into the unused slot)
     // keep the load count fixed
     SLQ_COMPILER_FENCE();
     load_block_fixed<QT>(ntile, lane, nbn, b, w);
-    const int nxt = b < 4 ? (b + 4 < nb ? kb + b + 4 : 0) : (b - 4 < nbn ? kb_next + b - 4 : 0);
-    dma_block<QT, DPB>(rs, nxt, TP, ring + (b % RING) * SLOT);
+    const int nxt = b < TB - DR ? (b + DR < nb ? kb + b + DR : 0) : (b + DR - TB < nbn ? kb_next + b + DR - TB : 0);
+    dma_block<QT, DPB>(rs, nxt, TP, ring + (b % DR) * SLOT);
     SLQ_COMPILER_FENCE();
   }
 }
@@ -584,10 +587,10 @@ __global__ __launch_bounds__(512) void k_gemm_dense(Packed W, Act x, NormIn nin,
   const __amdgpu_buffer_rsrc_t rs = mx_rsrc(x, QT);
   TileRegs<QT> R;
   if (t0 < t1) {
-    // prologue: the records of tile t0's first 4 blocks into the ring (block
-    // 0 again past a ragged tile's end), then the tile's weights
+    // prologue: the records of tile t0's first DENSE_RING blocks into the
+    // ring (block 0 again past a ragged tile's end), then the tile's weights
 #pragma unroll
-    for (int b = 0; b < RING; ++b)
+    for (int b = 0; b < DENSE_RING; ++b)
       dma_block<QT, gemm_dpb(QT, TP)>(rs, b < nb_of(t0) ? t0 * TB + b : 0, TP, ring + b * gemm_slot(QT, TP));
     SLQ_COMPILER_FENCE();
     load_tile_fixed<QT>(base + (size_t)t0 * TBY, lane, nb_of(t0), R);
