@@ -128,12 +128,23 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   // this step's K/V rows inside the chunk: positions p0 + t in [r0, r0 + C).
   // Every query-head group of the chunk computes and stores them itself
   // (the same bits), so each reads them back after its own stores.
+  // (each token's k and v are requested one token ahead)
   const int ta = max(0, r0 - p0), tb = min(T, r0 + C - p0);
+  float kn = 0.0f, vn = 0.0f;
+  if (ta < tb && dact) {
+    const float* y = p.y + (size_t)ta * p.y_stride;
+    kn = y[p.off_k + g * HD + tid];
+    vn = y[p.off_v + g * HD + tid];
+  }
   for (int t = ta; t < tb; ++t) {
-    const float* y = p.y + (size_t)t * p.y_stride;
     const int pos = p0 + t;
-    float k[1] = {dact ? y[p.off_k + g * HD + tid] : 0.0f};
-    const float vx = dact ? y[p.off_v + g * HD + tid] : 0.0f;
+    float k[1] = {kn};
+    const float vx = vn;
+    if (t + 1 < tb && dact) {
+      const float* y = p.y + (size_t)(t + 1) * p.y_stride;
+      kn = y[p.off_k + g * HD + tid];
+      vn = y[p.off_v + g * HD + tid];
+    }
     float c, sn;
     rope_cs(p, tid, pos, c, sn);
     heads_prep<1>(k, tid, p, p.k_norm, c, sn, buf, wred);
@@ -164,15 +175,24 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
     for (int q = 0; q < C; ++q) vv[q] = vrow[(size_t)q * HD];
   }
 
-  for (int t = 0; t < T; ++t) {
+  // tokens from the first whose position reaches this chunk; each token's
+  // query values are requested one token ahead
+  const int tq = max(0, r0 - p0);
+  float qn[GRP];
+#pragma unroll
+  for (int h = 0; h < GRP; ++h) qn[h] = dact && tq < T ? p.y[(size_t)tq * p.y_stride + p.off_q + (h0 + h) * HD + tid] : 0.0f;
+  for (int t = tq; t < T; ++t) {
     const int P = p0 + t;
     const int nvalid = min(C, P + 1 - r0);
-    if (nvalid <= 0) continue;
     {
-      const float* y = p.y + (size_t)t * p.y_stride;
       float qx[GRP];
 #pragma unroll
-      for (int h = 0; h < GRP; ++h) qx[h] = dact ? y[p.off_q + (h0 + h) * HD + tid] : 0.0f;
+      for (int h = 0; h < GRP; ++h) qx[h] = qn[h];
+      if (t + 1 < T && dact) {
+        const float* y = p.y + (size_t)(t + 1) * p.y_stride;
+#pragma unroll
+        for (int h = 0; h < GRP; ++h) qn[h] = y[p.off_q + (h0 + h) * HD + tid];
+      }
       float c, sn;
       rope_cs(p, tid, P, c, sn);
       heads_prep<GRP>(qx, tid, p, p.q_norm, c, sn, buf, wred);
