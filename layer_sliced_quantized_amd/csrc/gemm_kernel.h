@@ -34,17 +34,19 @@
 // 0..15 and 16..31 as int8, k-groups 2 and 3 repeat them (Q4_0) or are zero
 // (Q8_0); B's k-groups are the record's chunks of the digit (pair).  A wave's
 // 64 rows are 4 row tiles of 16, three MFMAs each per block; each block's rows
-// (as int8) and scales pass through a small per-wave LDS buffer so that lane
-// l can take row 16 r + l % 16.  Lane l ends with rows 16 r + 4 (l / 16) + i
-// (r, i = 0..3) of token slot l % 16.
+// (as int8) pass through a small per-wave LDS buffer so that lane l can take
+// row 16 r + l % 16, and the tile's row scales are staged there once per
+// tile.  Lane l ends with rows 16 r + 4 (l / 16) + i (r, i = 0..3) of token
+// slot l % 16.
 //
 // In both, the weights stream into registers one tile ahead, lane = row, as in
 // the GEMV but block by block into one register set (each block's registers
 // are refilled with the next tile's block as soon as they are used), and the
-// records of the blocks in use come into a ring of 4 block slots in the
-// wave's LDS by buffer loads into LDS, four blocks ahead.  Each ring
-// wait is an explicit vmcnt that leaves the next tile's weights and the
-// refills issued after them in flight, so no read of the ring waits for them.
+// records of the blocks in use come into a ring of block slots in the wave's
+// LDS by buffer loads into LDS (4 slots, four blocks ahead, block-diagonal; 2
+// slots, dense).  Each ring wait is an explicit vmcnt that leaves the later
+// weight refills and record copies in flight, so no read of the ring waits
+// for them.
 #pragma once
 #include "gemv_kernel.h"
 
