@@ -9,52 +9,60 @@
 // with q, k divided by sqrt(sum of squares + 1e-6).  Row i of S only needs the
 // whole k and q plus v_i, so rows are independent:
 //     u_i = S_i . k,   S'_ij = alpha S_ij + beta (v_i - alpha u_i) k_j,   o_i = S'_i . q
-// Eight threads own one row i, each with an eighth of the j range (the state
-// lives in registers across the tokens of a verify pass), and meet in LDS.
+// Eight lanes of one wave own one row i, each with an eighth of the j range
+// (the state lives in registers across the tokens of a verify pass), and
+// meet in three butterfly steps, so a token needs no workgroup barrier.
 //
-// State layout in HBM: [slot][head][j][i] (i fastest) so that a wave's loads
-// and stores of one j are contiguous.  Decode updates slot `cur` in place;
-// verify writes the state after token t to slot (cur + 1 + t) mod nslots and
-// never touches slot `cur`, which is what makes rollback exact.
+// State layout in HBM: [slot][head][i / 8][jj][part][i % 8] with
+// j = part * (d_k / 8) + jj, so that for one jj a wave's 64 lanes (8 parts x
+// 8 rows) load and store 256 contiguous bytes.  Decode updates slot `cur` in
+// place; verify writes the state after token t to slot (cur + 1 + t) mod
+// nslots and never touches slot `cur`, which is what makes rollback exact.
 #include "dev.h"
 
 namespace slq {
 
-// One workgroup of 4 waves per (head, 32 rows of S).  Thread (part, ii)
-// owns row i = 32 ib + ii over the key range [part*DKP, part*DKP + DKP),
-// part = 0..7; a half-wave (one part) reads 32 consecutive rows of one j as
-// 128 contiguous bytes.  The parts of a row meet in LDS and are added in part
-// order, so the two reductions per token are deterministic.
+// Offset of S[i][j] inside one head's state (d_k = 8 dkp).
+__host__ __device__ inline size_t dn_off(int i, int j, int dkp) {
+  return ((size_t)((i >> 3) * dkp + j % dkp) * 8 + j / dkp) * 8 + (i & 7);
+}
+
+// One workgroup of 4 waves per (head, 32 rows of S); wave w owns rows
+// 32 ib + 8 w + r, lane (part, r) = (lane / 8, lane % 8) the key range
+// [part*DKP, part*DKP + DKP) of its row.  The eight parts of a row meet in a
+// butterfly over lanes r, r + 8, ..., r + 56 (a fixed order, so the sums are
+// deterministic).
 //
 // Every token's inputs are requested together before the first update (the
 // recurrence itself runs token after token): the waves normalise q and k of
 // tokens wave, wave + 4, ... into LDS, and (for several tokens) the v, z,
 // decay and gate inputs go to LDS as well, so no token waits on a global
-// load inside the loop.  The
-// two reductions of a token use separate LDS areas, which leaves two
-// workgroup barriers per token.  Wave 0 quantises the 32 outputs of each
-// token (one digit block).
+// load inside the loop.  The outputs of all tokens are quantised after the
+// loop, one digit block of 32 rows per token, by wave t mod 4.
 template <int DKP>
 __global__ __launch_bounds__(256) void k_deltanet(DnParams p, int T) {
   constexpr int DK = 8 * DKP;
   __shared__ float qs[MAX_T][DK], ksh[MAX_T][DK];
   __shared__ float vsh[MAX_T][32], zsh[MAX_T][32];
   __shared__ float ab[MAX_T][2];
-  __shared__ float red_u[8][32], red_o[8][32];
+  __shared__ float osh[MAX_T][32];
   const int nib = p.dv / 32;
   const int h = blockIdx.x / nib, ib = blockIdx.x % nib;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int part = tid >> 5, ii = tid & 31;
+  const int part = lane >> 3, r = lane & 7;
+  const int ii = wave * 8 + r;          // row within the workgroup's 32
   const int i = ib * 32 + ii;
   const int cur = p.ctrl->cur;
   const size_t hs = (size_t)DK * p.dv;
   const float* S_in = p.state + ((size_t)cur * p.heads + h) * hs;
   const int j0 = part * DKP;
+  // this lane's state entries: jj = 0..DKP-1 at a stride of 64 floats
+  const size_t sbase = dn_off(i, j0, DKP);
 
   float S[DKP];
 #pragma unroll
-  for (int jj = 0; jj < DKP; ++jj) S[jj] = S_in[(size_t)(j0 + jj) * p.dv + i];
+  for (int jj = 0; jj < DKP; ++jj) S[jj] = S_in[sbase + (size_t)jj * 64];
 
   // q, k of head h for tokens wave + 4m: lanes hold entries lane and lane + 64
   {
@@ -80,7 +88,7 @@ __global__ __launch_bounds__(256) void k_deltanet(DnParams p, int T) {
       }
     }
   }
-  // v, z, decay and gate: with one token every thread takes its own from
+  // v, z, decay and gate: with one token every lane takes its own from
   // global memory (no LDS hop on the decode path); with several, v and z of
   // rows 32 ib + (tid % 32) for tokens tid / 32 and tid / 32 + 8, and the
   // gates of token tid, go to LDS
@@ -97,8 +105,8 @@ __global__ __launch_bounds__(256) void k_deltanet(DnParams p, int T) {
       const int t = tid / 32 + 8 * m;
       if (t < T) {
         const float* y = p.y + (size_t)t * p.y_stride;
-        vsh[t][ii] = y[p.off_v + h * p.dv + i];
-        zsh[t][ii] = y[p.off_z + h * p.dv + i];
+        vsh[t][tid & 31] = y[p.off_v + h * p.dv + ib * 32 + (tid & 31)];
+        zsh[t][tid & 31] = y[p.off_z + h * p.dv + ib * 32 + (tid & 31)];
       }
     }
     if (tid < T) {
@@ -115,40 +123,36 @@ __global__ __launch_bounds__(256) void k_deltanet(DnParams p, int T) {
     float up = 0.0f;
 #pragma unroll
     for (int jj = 0; jj < DKP; ++jj) up = __builtin_fmaf(S[jj], ksh[t][j0 + jj], up);
-    red_u[part][ii] = up;
-    __syncthreads();
-    float u = red_u[0][ii];
-#pragma unroll
-    for (int k = 1; k < 8; ++k) u += red_u[k][ii];
-    const float c = beta * (vi - alpha * u);
+    up += __shfl_xor(up, 8, 64);
+    up += __shfl_xor(up, 16, 64);
+    up += __shfl_xor(up, 32, 64);
+    const float c = beta * (vi - alpha * up);
     float op = 0.0f;
 #pragma unroll
     for (int jj = 0; jj < DKP; ++jj) {
       S[jj] = __builtin_fmaf(c, ksh[t][j0 + jj], alpha * S[jj]);
       op = __builtin_fmaf(S[jj], qs[t][j0 + jj], op);
     }
-    red_o[part][ii] = op;
+    op += __shfl_xor(op, 8, 64);
+    op += __shfl_xor(op, 16, 64);
+    op += __shfl_xor(op, 32, 64);
+    if (part == 0) osh[t][ii] = op * sigmoidf_(p.z_scale * (one ? z1 : zsh[t][ii]));
 
     float* S_out = p.verify ? p.state + ((size_t)((cur + 1 + t) % p.nslots) * p.heads + h) * hs
                             : const_cast<float*>(S_in);
 #pragma unroll
-    for (int jj = 0; jj < DKP; ++jj) S_out[(size_t)(j0 + jj) * p.dv + i] = S[jj];
-    // Every thread has read red_u (before writing red_o), so the next token
-    // may overwrite it after this barrier; wave 0 reads red_o before it
-    // reaches the next token's barrier, so red_o is not overwritten early.
-    __syncthreads();
-    if (tid < 64) {
-      // lanes ii and ii + 32 of wave 0 both hold row i's output; the first
-      // half stores it
-      float o = red_o[0][ii];
-#pragma unroll
-      for (int k = 1; k < 8; ++k) o += red_o[k][ii];
-      const float uo = o * sigmoidf_(p.z_scale * (one ? z1 : zsh[t][ii]));
-      const int nv = p.heads * p.dv;
-      if (p.u_out && lane < 32) p.u_out[(size_t)t * nv + h * p.dv + i] = uo;
-      const int blk = (h * p.dv + ib * 32) / QK;
-      put_digits(p.next, p.next_qt, t, blk, uo, lane < 32);
-    }
+    for (int jj = 0; jj < DKP; ++jj) S_out[sbase + (size_t)jj * 64] = S[jj];
+  }
+  __syncthreads();
+
+  // outputs: token t by wave t mod 4; lanes l and l + 32 hold row l's value,
+  // the first half stores it
+  const int blk = (h * p.dv + ib * 32) / QK;
+  const int nv = p.heads * p.dv;
+  for (int t = wave; t < T; t += 4) {
+    const float uo = osh[t][lane & 31];
+    if (p.u_out && lane < 32) p.u_out[(size_t)t * nv + h * p.dv + ib * 32 + lane] = uo;
+    put_digits(p.next, p.next_qt, t, blk, uo, lane < 32);
   }
 }
 
@@ -165,7 +169,7 @@ hipError_t launch_deltanet(const DnParams& p, int T, hipStream_t s) {
   return hipGetLastError();
 }
 
-// Canonical [head][i][j] <-> device [head][j][i] of the current slot.
+// Canonical [head][i][j] <-> the device layout of the current slot.
 __global__ void k_state_io(float* state, int nslots, const Ctrl* ctrl, int heads, int dk, int dv,
                            float* canon, int to_device) {
   const size_t n = (size_t)heads * dk * dv;
@@ -174,7 +178,7 @@ __global__ void k_state_io(float* state, int nslots, const Ctrl* ctrl, int heads
   const int h = (int)(idx / ((size_t)dk * dv));
   const int rem = (int)(idx % ((size_t)dk * dv));
   const int i = rem / dk, j = rem % dk;     // canonical index (h, i, j)
-  float* dev = state + (size_t)ctrl->cur * n + (size_t)h * dk * dv + (size_t)j * dv + i;
+  float* dev = state + (size_t)ctrl->cur * n + (size_t)h * dk * dv + dn_off(i, j, dk / 8);
   if (to_device) *dev = canon[idx];
   else canon[idx] = *dev;
   (void)nslots;
