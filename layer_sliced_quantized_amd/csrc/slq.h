@@ -151,7 +151,7 @@ struct DnParams {
   int off_q, off_k, off_v, off_a, off_b, off_z;
   int heads, dk, dv;
   float a_scale, a_bias, b_scale, z_scale;
-  float* state;          // slot 0 of this layer: [nslots][heads][dk][dv] (transposed)
+  float* state;          // slot 0 of this layer: [nslots][heads][dv/8][dk/8][8][8] (see k_deltanet)
   int nslots;
   int verify;            // 0: in place on slot cur; 1: token t -> slot (cur+1+t) % nslots
   const Ctrl* ctrl;
