@@ -6,13 +6,14 @@
 // KV cache ("Unstable Legion", section "Splitting the workload").
 //
 // Two kernels per layer:
-//   split:   one workgroup per (KV head, 32-row chunk).  It first appends the
-//            K/V rows of this step that fall in its chunk (RMSNorm if QK-norm,
-//            RoPE on the first rope_dims entries with the angle
-//            pos * theta^(-2i/r) taken in fp64, fp16 rounding), then prepares
-//            its query heads the same way (q also scaled by 1/sqrt(head_dim)),
-//            and computes the chunk-local max / sum of exp and the
-//            unnormalised P V.  Query t (position p+t) sees rows <= p+t.
+//   split:   one workgroup per (KV head, group of query heads, 32-row chunk).
+//            It first appends the K/V rows of this step that fall in its
+//            chunk (RMSNorm if QK-norm, RoPE on the first rope_dims entries
+//            with the angle pos * theta^(-2i/r) taken in fp64, fp16
+//            rounding), then prepares its query heads the same way (q also
+//            scaled by 1/sqrt(head_dim)), and computes the chunk-local max /
+//            sum of exp and the unnormalised P V for every token of the pass.
+//            Query t (position p+t) sees rows <= p+t.
 //   combine: per (token, query head): merge the chunks' partials, apply the
 //            gate sigmoid(g), and quantise the result for the output GEMV.
 // Chunk boundaries are absolute (multiples of 32), so query t of a verify
@@ -60,60 +61,67 @@ __device__ __forceinline__ void rope_cs(const AttnParams& p, int d, int pos, flo
   }
 }
 
-// RMSNorm (when enabled) and RoPE of NH head vectors held one entry per
-// thread (x[h] = entry d of head h for d < hd, 0 elsewhere), all rotated by
-// (c, sn) of entry d.  Every thread of the workgroup calls it: buf (NH * hd
-// floats) and wred (4 x NH floats) are LDS, free again on return.
-template <int NH>
-__device__ __forceinline__ void heads_prep(float (&x)[NH], int d, const AttnParams& p, const float* norm_w, float c,
-                                           float sn, float* buf, float (*wred)[8]) {
-  const bool act = d < p.hd;
+// RMSNorm (when enabled) and RoPE of one head vector held by one wave: lane l
+// holds entries l + 64 k, k < NC.  The sum of squares is a butterfly inside
+// the wave; the rotation pairs (d, d +- rope_dims/2) meet through the wave's
+// own LDS row rb (LDS operations of one wave take effect in program order), so
+// no workgroup barrier is needed.
+template <int NC>
+__device__ __forceinline__ void head_prep(float (&x)[NC], const AttnParams& p, const float* norm_w, int pos,
+                                          float* rb) {
+  const int lane = threadIdx.x & 63;
   if (p.qk_norm) {
+    float ss = 0.0f;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const float ss = wave_sum(x[h] * x[h]);
-      if ((d & 63) == 0) wred[d >> 6][h] = ss;
-    }
-    __syncthreads();
+    for (int k = 0; k < NC; ++k) ss += x[k] * x[k];
+    ss = wave_sum(ss);
+    const float rn = 1.0f / sqrtf(ss / (float)(64 * NC) + p.eps);
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      float tot = 0.0f;
-      for (int w = 0; w < (p.hd >> 6); ++w) tot += wred[w][h];
-      const float rn = 1.0f / sqrtf(tot / (float)p.hd + p.eps);
-      x[h] = act ? x[h] * rn * norm_w[d] : 0.0f;
-    }
+    for (int k = 0; k < NC; ++k) x[k] = x[k] * rn * norm_w[lane + 64 * k];
   }
+  if (p.rope_dims) {
+    asm volatile("" ::: "memory");
 #pragma unroll
-  for (int h = 0; h < NH; ++h)
-    if (act) buf[h * p.hd + d] = x[h];
-  __syncthreads();
-  if (act && d < p.rope_dims) {
+    for (int k = 0; k < NC; ++k) rb[lane + 64 * k] = x[k];
+    asm volatile("" ::: "memory");
     const int half = p.rope_dims / 2;
 #pragma unroll
-    for (int h = 0; h < NH; ++h) {
-      const float* b = buf + h * p.hd;
-      x[h] = d < half ? b[d] * c - b[d + half] * sn : b[d] * c + b[d - half] * sn;
+    for (int k = 0; k < NC; ++k) {
+      const int d = lane + 64 * k;
+      if (d < p.rope_dims) {
+        float c, sn;
+        rope_cs(p, d, pos, c, sn);
+        x[k] = d < half ? rb[d] * c - rb[d + half] * sn : rb[d] * c + rb[d - half] * sn;
+      }
     }
+    asm volatile("" ::: "memory");
   }
-  __syncthreads();
 }
 
-// One workgroup per (KV head g, group of HPW of its query heads, 32-row chunk
-// c), 4 waves.  Scores: thread
-// (row rr = tid / 8, part = tid % 8) takes an eighth of the head dimensions
-// of key row rr, the eight parts meeting with three butterfly steps.  P V:
-// one thread per head dimension over the chunk's rows.  The chunk's keys and
-// values are requested once, before the query preparation, and serve every
-// token of the pass.
+// One workgroup per (KV head g, group of GRP of its query heads, 32-row chunk
+// c), 4 waves, for all T tokens of the pass at once:
+//   1. the pass's K/V rows that fall in the chunk are prepared (wave w takes
+//      tokens w, w + 4, ...) and appended to the cache;
+//   2. the chunk's keys (thread (row rr = tid / 8, part = tid % 8): an eighth
+//      of the head dimensions of key row rr) and values (thread = dimension)
+//      are requested once;
+//   3. every (token, query head) is prepared into LDS (wave w takes pairs w,
+//      w + 4, ...) while those loads are in flight;
+//   4. scores for every (token, head): the eight parts meet in three butterfly
+//      steps; then one wave per (token, head) takes the chunk max, the
+//      weights exp(s - max) and their sum;
+//   5. P V per (token, head): one thread per dimension over the chunk's rows.
+// Four workgroup barriers in all, whatever T.  Every group of query heads of
+// the chunk appends the same rows itself (the same bits), so each reads them
+// back after its own stores.
 template <int GRP, int HD>   // GRP: query heads per workgroup
 __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   constexpr int C = ATT_CHUNK;
-  constexpr int NC = HD / 64;   // 8-dim pieces per eighth of the head
-  __shared__ __attribute__((aligned(16))) float qsh[GRP * HD];
-  __shared__ __attribute__((aligned(16))) float pl[GRP][C];
-  __shared__ float buf[GRP * HD];
-  __shared__ float wred[4][8];
-  __shared__ float wm[4][GRP];
+  constexpr int NC = HD / 64;   // entries per lane of a head vector; 8-dim pieces per eighth of the head
+  __shared__ __attribute__((aligned(16))) float qsh[MAX_T][GRP][HD];
+  __shared__ __attribute__((aligned(16))) float pl[MAX_T][GRP][C];
+  __shared__ float rbuf[4][HD];
+  __shared__ float ml[MAX_T][GRP][2];
   const int nsub = p.q_heads / p.kv_heads / GRP;   // query-head groups per KV head
   const int g = blockIdx.x / (nsub * p.nchunk);
   const int sub = (blockIdx.x / p.nchunk) % nsub, c = blockIdx.x % p.nchunk;
@@ -124,49 +132,54 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = wave_id();
   const bool dact = tid < HD;
+  float* rb = rbuf[wave];
 
-  // this step's K/V rows inside the chunk: positions p0 + t in [r0, r0 + C).
-  // Every query-head group of the chunk computes and stores them itself
-  // (the same bits), so each reads them back after its own stores.
-  // (each token's k and v are requested one token ahead)
+  // 1. this pass's K/V rows inside the chunk: positions p0 + t in [r0, r0 + C);
+  // wave w takes tokens ta + w + 4 m, all its loads first
   const int ta = max(0, r0 - p0), tb = min(T, r0 + C - p0);
-  float kn = 0.0f, vn = 0.0f;
-  if (ta < tb && dact) {
-    const float* y = p.y + (size_t)ta * p.y_stride;
-    kn = y[p.off_k + g * HD + tid];
-    vn = y[p.off_v + g * HD + tid];
-  }
-  for (int t = ta; t < tb; ++t) {
-    const int pos = p0 + t;
-    float k[1] = {kn};
-    const float vx = vn;
-    if (t + 1 < tb && dact) {
-      const float* y = p.y + (size_t)(t + 1) * p.y_stride;
-      kn = y[p.off_k + g * HD + tid];
-      vn = y[p.off_v + g * HD + tid];
-    }
-    float c, sn;
-    rope_cs(p, tid, pos, c, sn);
-    heads_prep<1>(k, tid, p, p.k_norm, c, sn, buf, wred);
-    if (dact) {
-      p.kc[kidx(g, pos, tid, p.max_seq, HD)] = __float2half_rn(k[0]);
-      p.vc[((size_t)g * p.max_seq + pos) * HD + tid] = __float2half_rn(vx);
-    }
-  }
   if (tb > ta) {
+    float k[MAX_T / 4][NC], v[MAX_T / 4][NC];
+#pragma unroll
+    for (int m = 0; m < MAX_T / 4; ++m) {
+      const int t = ta + wave + 4 * m;
+      if (t < tb) {
+        const float* y = p.y + (size_t)t * p.y_stride;
+#pragma unroll
+        for (int e = 0; e < NC; ++e) {
+          k[m][e] = y[p.off_k + g * HD + lane + 64 * e];
+          v[m][e] = y[p.off_v + g * HD + lane + 64 * e];
+        }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MAX_T / 4; ++m) {
+      const int t = ta + wave + 4 * m;
+      if (t < tb) {
+        const int pos = p0 + t;
+        head_prep<NC>(k[m], p, p.k_norm, pos, rb);
+#pragma unroll
+        for (int e = 0; e < NC; ++e) {
+          const int d = lane + 64 * e;
+          p.kc[kidx(g, pos, d, p.max_seq, HD)] = __float2half_rn(k[m][e]);
+          p.vc[((size_t)g * p.max_seq + pos) * HD + d] = __float2half_rn(v[m][e]);
+        }
+      }
+    }
     __threadfence_block();
     __syncthreads();
   }
 
-  // the chunk's keys (this thread's eighth of row rr) and values (dimension
-  // tid of every row); rows past the valid ones lie inside the cache and get
-  // weight 0
+  // 2. the chunk's keys (this thread's eighth of row rr) and values
+  // (dimension tid of every row) are requested now and converted after the
+  // queries are prepared; rows past the pass's last position lie inside the
+  // cache, get weight 0 and a value of 0
   const int rr = tid >> 3, part = tid & 7;
   const int r = r0 + rr;
   uint4 kw[NC];
 #pragma unroll
   for (int i = 0; i < NC; ++i)
     kw[i] = *reinterpret_cast<const uint4*>(p.kc + kidx(g, r, (part * NC + i) * 8, p.max_seq, HD));
+  const int nvmax = min(C, p0 + T - r0);   // rows valid for the pass's last token
   unsigned short vv[C];
   {
     const unsigned short* vrow =
@@ -175,118 +188,106 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
     for (int q = 0; q < C; ++q) vv[q] = vrow[(size_t)q * HD];
   }
 
-  // tokens from the first whose position reaches this chunk; each token's
-  // query values are requested one token ahead
+  // 3. queries of tokens tq.. (those whose position reaches this chunk):
+  // pair q = (t - tq) GRP + h, wave w takes pairs w + 4 m, all its loads first
   const int tq = max(0, r0 - p0);
-  float qn[GRP];
+  const int npair = (T - tq) * GRP;
+  {
+    constexpr int MQ = MAX_T * GRP / 4;
+    float x[MQ][NC];
 #pragma unroll
-  for (int h = 0; h < GRP; ++h) qn[h] = dact && tq < T ? p.y[(size_t)tq * p.y_stride + p.off_q + (h0 + h) * HD + tid] : 0.0f;
-  for (int t = tq; t < T; ++t) {
-    const int P = p0 + t;
-    const int nvalid = min(C, P + 1 - r0);
-    {
-      float qx[GRP];
+    for (int m = 0; m < MQ; ++m) {
+      const int q = wave + 4 * m;
+      if (q < npair) {
+        const float* y = p.y + (size_t)(tq + q / GRP) * p.y_stride + p.off_q + (h0 + q % GRP) * HD;
 #pragma unroll
-      for (int h = 0; h < GRP; ++h) qx[h] = qn[h];
-      if (t + 1 < T && dact) {
-        const float* y = p.y + (size_t)(t + 1) * p.y_stride;
-#pragma unroll
-        for (int h = 0; h < GRP; ++h) qn[h] = y[p.off_q + (h0 + h) * HD + tid];
+        for (int e = 0; e < NC; ++e) x[m][e] = y[lane + 64 * e];
       }
-      float c, sn;
-      rope_cs(p, tid, P, c, sn);
-      heads_prep<GRP>(qx, tid, p, p.q_norm, c, sn, buf, wred);
-#pragma unroll
-      for (int h = 0; h < GRP; ++h)
-        if (dact) qsh[h * HD + tid] = qx[h] * (1.0f / sqrtf((float)HD));
     }
-    __syncthreads();
-    float s[GRP];
 #pragma unroll
-    for (int h = 0; h < GRP; ++h) s[h] = 0.0f;
-    if (rr < nvalid) {
+    for (int m = 0; m < MQ; ++m) {
+      const int q = wave + 4 * m;
+      if (q < npair) {
+        const int t = tq + q / GRP, h = q % GRP;
+        head_prep<NC>(x[m], p, p.q_norm, p0 + t, rb);
+#pragma unroll
+        for (int e = 0; e < NC; ++e) qsh[t][h][lane + 64 * e] = x[m][e] * (1.0f / sqrtf((float)HD));
+      }
+    }
+  }
+  __syncthreads();
+  float kf[NC][8];
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    const uint32_t ws[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      kf[i][2 * e] = __half2float(__ushort_as_half((unsigned short)(ws[e] & 0xffff)));
+      kf[i][2 * e + 1] = __half2float(__ushort_as_half((unsigned short)(ws[e] >> 16)));
+    }
+  }
+  float vf[C];
+#pragma unroll
+  for (int q = 0; q < C; ++q) vf[q] = q < nvmax ? __half2float(__ushort_as_half(vv[q])) : 0.0f;
+
+  // 4. scores, then per (token, head) the max, weights and their sum
+  for (int t = tq; t < T; ++t) {
+    const int nvalid = min(C, p0 + t + 1 - r0);
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) {
+      float sc = 0.0f;
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
         const int dc = part * NC + i;
-        float kf[8];
-        const uint32_t ws[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          kf[2 * e] = __half2float(__ushort_as_half((unsigned short)(ws[e] & 0xffff)));
-          kf[2 * e + 1] = __half2float(__ushort_as_half((unsigned short)(ws[e] >> 16)));
-        }
-#pragma unroll
-        for (int h = 0; h < GRP; ++h) {
-          const float4 qa = *reinterpret_cast<const float4*>(qsh + h * HD + dc * 8);
-          const float4 qb = *reinterpret_cast<const float4*>(qsh + h * HD + dc * 8 + 4);
-          s[h] = __builtin_fmaf(kf[0], qa.x, s[h]);
-          s[h] = __builtin_fmaf(kf[1], qa.y, s[h]);
-          s[h] = __builtin_fmaf(kf[2], qa.z, s[h]);
-          s[h] = __builtin_fmaf(kf[3], qa.w, s[h]);
-          s[h] = __builtin_fmaf(kf[4], qb.x, s[h]);
-          s[h] = __builtin_fmaf(kf[5], qb.y, s[h]);
-          s[h] = __builtin_fmaf(kf[6], qb.z, s[h]);
-          s[h] = __builtin_fmaf(kf[7], qb.w, s[h]);
-        }
-        asm volatile("" ::: "memory");   // one piece's query values in registers at a time
+        const float4 qa = *reinterpret_cast<const float4*>(&qsh[t][h][dc * 8]);
+        const float4 qb = *reinterpret_cast<const float4*>(&qsh[t][h][dc * 8 + 4]);
+        sc = __builtin_fmaf(kf[i][0], qa.x, sc);
+        sc = __builtin_fmaf(kf[i][1], qa.y, sc);
+        sc = __builtin_fmaf(kf[i][2], qa.z, sc);
+        sc = __builtin_fmaf(kf[i][3], qa.w, sc);
+        sc = __builtin_fmaf(kf[i][4], qb.x, sc);
+        sc = __builtin_fmaf(kf[i][5], qb.y, sc);
+        sc = __builtin_fmaf(kf[i][6], qb.z, sc);
+        sc = __builtin_fmaf(kf[i][7], qb.w, sc);
       }
+      sc += __shfl_xor(sc, 1, 64);
+      sc += __shfl_xor(sc, 2, 64);
+      sc += __shfl_xor(sc, 4, 64);
+      if (part == 0) pl[t][h][rr] = rr < nvalid ? sc : -INFINITY;
     }
-#pragma unroll
-    for (int h = 0; h < GRP; ++h) {
-      s[h] += __shfl_xor(s[h], 1, 64);
-      s[h] += __shfl_xor(s[h], 2, 64);
-      s[h] += __shfl_xor(s[h], 4, 64);
-    }
-    // chunk max per head (each wave holds 8 rows)
-#pragma unroll
-    for (int h = 0; h < GRP; ++h) {
-      const float v = wave_max(rr < nvalid ? s[h] : -INFINITY);
-      if (lane == 0) wm[wave][h] = v;
-    }
-    __syncthreads();
-    float m[GRP];
-#pragma unroll
-    for (int h = 0; h < GRP; ++h) m[h] = fmaxf(fmaxf(wm[0][h], wm[1][h]), fmaxf(wm[2][h], wm[3][h]));
-    __syncthreads();
-    float l[GRP];
-#pragma unroll
-    for (int h = 0; h < GRP; ++h) {
-      const float e = rr < nvalid ? __expf(s[h] - m[h]) : 0.0f;
-      if (part == 0) pl[h][rr] = e;
-      // each row's weight appears on 8 lanes; count it once
-      const float v = wave_sum(part == 0 ? e : 0.0f);
-      if (lane == 0) wm[wave][h] = v;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int h = 0; h < GRP; ++h) l[h] = (wm[0][h] + wm[1][h]) + (wm[2][h] + wm[3][h]);
-    if (dact) {
-      float o[GRP];
-#pragma unroll
-      for (int h = 0; h < GRP; ++h) o[h] = 0.0f;
-#pragma unroll
-      for (int q = 0; q < C; q += 4) {
-        float v[4];
-#pragma unroll
-        for (int u = 0; u < 4; ++u) v[u] = q + u < nvalid ? __half2float(__ushort_as_half(vv[q + u])) : 0.0f;
-#pragma unroll
-        for (int h = 0; h < GRP; ++h) {
-          const float4 w = *reinterpret_cast<const float4*>(&pl[h][q]);
-          o[h] = __builtin_fmaf(w.x, v[0], o[h]);
-          o[h] = __builtin_fmaf(w.y, v[1], o[h]);
-          o[h] = __builtin_fmaf(w.z, v[2], o[h]);
-          o[h] = __builtin_fmaf(w.w, v[3], o[h]);
-        }
-        asm volatile("" ::: "memory");   // four rows' weights in registers at a time
-      }
+  }
+  __syncthreads();
+  for (int q = wave; q < npair; q += 4) {
+    const int t = tq + q / GRP, h = q % GRP;
+    const int nvalid = min(C, p0 + t + 1 - r0);
+    const float sc = lane < C ? pl[t][h][lane] : -INFINITY;
+    const float m = wave_max(sc);
+    const float e = lane < nvalid ? __expf(sc - m) : 0.0f;
+    if (lane < C) pl[t][h][lane] = e;
+    const float l = wave_sum(e);
+    if (lane == 0) { ml[t][h][0] = m; ml[t][h][1] = l; }
+  }
+  __syncthreads();
+
+  // 5. P V
+  if (dact) {
+    for (int t = tq; t < T; ++t) {
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
+        float o = 0.0f;
+#pragma unroll
+        for (int q = 0; q < C; q += 4) {
+          const float4 w = *reinterpret_cast<const float4*>(&pl[t][h][q]);
+          o = __builtin_fmaf(w.x, vf[q], o);
+          o = __builtin_fmaf(w.y, vf[q + 1], o);
+          o = __builtin_fmaf(w.z, vf[q + 2], o);
+          o = __builtin_fmaf(w.w, vf[q + 3], o);
+        }
         float* dst = p.part + (((size_t)t * p.q_heads + h0 + h) * p.nchunk + c) * (HD + 2);
-        dst[2 + tid] = o[h];
-        if (tid == 0) { dst[0] = m[h]; dst[1] = l[h]; }
+        dst[2 + tid] = o;
+        if (tid == 0) { dst[0] = ml[t][h][0]; dst[1] = ml[t][h][1]; }
       }
     }
-    __syncthreads();   // qsh, pl and wm are rewritten by the next token
   }
 }
 
