@@ -101,6 +101,30 @@ def test_tiny_hybrid_q8_verify_equals_plain(k):
         np.testing.assert_array_equal(s.get_state(l).cpu().numpy(), p.get_state(l).cpu().numpy())
 
 
+@pytest.mark.parametrize("prefill", [31, 250, 255])
+def test_tiny_hybrid_verify_across_chunk_boundary(prefill):
+    """A 16-token pass whose positions cross a 32-row attention chunk boundary
+    (its K/V rows land in two chunks, and each chunk sees a different first
+    token): the bits of 16 plain decode steps, within tolerance of the oracle,
+    and the same K/V rows after commit."""
+    k = 16
+    H = inputs(TINY_H, k, workload=WL, step0=60)
+    s, orc, _, _ = make_pair(TINY_H, synth.Q4_0, 0, 4, workload=WL, prefill=prefill, max_seq=512, max_verify=16)
+    out = s.verify(_t(H)).cpu().numpy()
+    ref = orc.verify(H, raw=True)
+    for t in range(k):
+        assert rel_err(out[t], ref[t]) <= TOL, t
+    p, _, _, _ = make_pair(TINY_H, synth.Q4_0, 0, 4, workload=WL, prefill=prefill, max_seq=512, max_verify=16,
+                           with_oracle=False)
+    for t in range(k):
+        np.testing.assert_array_equal(p.decode(_t(H[t])).cpu().numpy(), out[t])
+    s.commit(k)
+    K1, V1 = s.get_kv(3, prefill + k)
+    K2, V2 = p.get_kv(3, prefill + k)
+    np.testing.assert_array_equal(K1.cpu().numpy(), K2.cpu().numpy())
+    np.testing.assert_array_equal(V1.cpu().numpy(), V2.cpu().numpy())
+
+
 def test_commit_zero_restores_state_exactly():
     s, _, _, _ = _tiny(with_oracle=False)
     before = [s.get_state(l).cpu().numpy() for l in (0, 1, 2)]
