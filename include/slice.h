@@ -205,6 +205,17 @@ int slice_run_gemv_op(slice_t *s, int op_kind, void *stream);
  * own slot.  Must be followed by slice_commit before the next decode/verify.  */
 int slice_verify(slice_t *s, int k, const void *hid_in_dev, void *hid_out_dev, void *stream);
 
+/* Prompt ingestion of k inputs (1..max_verify) at positions p .. p+k-1:
+ * hid_in_dev [k][H] -> hid_out_dev [k][H], then p <- p + k (no commit).  The
+ * result is that of k slice_decode calls up to floating-point rounding, not
+ * bit for bit: the DeltaNet layers take all k tokens at once in the chunked
+ * form of the recurrence and keep only the final state (the pages name the
+ * serial recurrence as what makes prefill slow; SwarmLLM README, bench
+ * paragraph).  For a bit-exact pass use slice_verify + slice_commit(k).
+ * Errors: SLICE_ESTATE while a verify is pending, SLICE_ERANGE for k or
+ * positions out of range; nothing is enqueued then.  */
+int slice_prefill(slice_t *s, int k, const void *hid_in_dev, void *hid_out_dev, void *stream);
+
 /* Accept the first `accepted` (0..k) tokens of the pending verify: the state
  * becomes exactly the state after that many plain steps (a slot switch; no
  * values are recomputed) and p <- p + accepted.  Enqueues one tiny kernel.  */

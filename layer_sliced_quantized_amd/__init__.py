@@ -211,6 +211,14 @@ class Slice:
         check(lib().slice_verify(self.handle, k, _ptr(h_in), _ptr(h_out), _stream(stream)))
         return h_out
 
+    def prefill(self, h_in: torch.Tensor, h_out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """k prompt tokens in one pass (chunked DeltaNet); the position moves by k."""
+        k = h_in.shape[0]
+        if h_out is None:
+            h_out = torch.empty((k, self.cfg.hidden), dtype=self.io_dtype, device=self.device)
+        check(lib().slice_prefill(self.handle, k, _ptr(h_in), _ptr(h_out), _stream(stream)))
+        return h_out
+
     def commit(self, accepted: int, stream=None):
         check(lib().slice_commit(self.handle, accepted, _stream(stream)))
 

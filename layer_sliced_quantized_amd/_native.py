@@ -75,6 +75,7 @@ _SIGS = {
     "slice_run_gemv_op": (_I, [_V, _I, _V]),
     "slice_verify": (_I, [_V, _I, _V, _V, _V]),
     "slice_commit": (_I, [_V, _I, _V]),
+    "slice_prefill": (_I, [_V, _I, _V, _V, _V]),
     "slice_embed": (_I, [_V, _V, _V, _V]),
     "slice_head_argmax": (_I, [_V, _V, _V, _V, _V]),
     "slice_position": (_I, [_V]),

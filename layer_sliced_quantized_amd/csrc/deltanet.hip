@@ -1,10 +1,10 @@
-// Gated DeltaNet recurrent update for decode and verify.
+// Gated DeltaNet recurrent update for decode, verify and prompt ingestion.
 //
 // The hybrid model's linear-attention layers are Gated DeltaNet (ChatTorrent
 // README, "What it can run").  Each head carries a state S (d_v x d_k, fp32)
-// that is updated once per token, one token after the other (the pages note
-// that this recurrence cannot be parallelised over tokens; SwarmLLM README,
-// bench paragraph):
+// that is updated once per token, one token after the other (the pages name
+// this serial recurrence as the reason prompt ingestion is slow; SwarmLLM
+// README, bench paragraph):
 //     S' = alpha S (I - beta k k^T) + beta v k^T,   o = S' q
 // with q, k divided by sqrt(sum of squares + 1e-6).  Row i of S only needs the
 // whole k and q plus v_i, so rows are independent:
@@ -18,6 +18,7 @@
 // 8 rows) load and store 256 contiguous bytes.  Decode updates slot `cur` in
 // place; verify writes the state after token t to slot (cur + 1 + t) mod
 // nslots and never touches slot `cur`, which is what makes rollback exact.
+// Prompt ingestion takes the chunked form further down (k_deltanet_chunk).
 #include "dev.h"
 
 namespace slq {
@@ -138,7 +139,7 @@ __global__ __launch_bounds__(256) void k_deltanet(DnParams p, int T) {
     op += __shfl_xor(op, 32, 64);
     if (part == 0) osh[t][ii] = op * sigmoidf_(p.z_scale * (one ? z1 : zsh[t][ii]));
 
-    float* S_out = p.verify ? p.state + ((size_t)((cur + 1 + t) % p.nslots) * p.heads + h) * hs
+    float* S_out = p.mode == DN_VERIFY ? p.state + ((size_t)((cur + 1 + t) % p.nslots) * p.heads + h) * hs
                             : const_cast<float*>(S_in);
 #pragma unroll
     for (int jj = 0; jj < DKP; ++jj) S_out[sbase + (size_t)jj * 64] = S[jj];
@@ -156,14 +157,209 @@ __global__ __launch_bounds__(256) void k_deltanet(DnParams p, int T) {
   }
 }
 
+// Prompt ingestion: the T tokens of a pass at once (chunked form).
+//
+// Unrolling the row recurrence above over a chunk of T tokens, with
+// g(t, s) = alpha_{s+1} ... alpha_t (g(t, t) = 1) and gamma_t = alpha_0 ... alpha_t,
+// every state in the chunk is S0 plus rank-one terms:
+//     S_t = gamma_t S0 + sum_{s<=t} g(t, s) c_s k_s^T,
+// and the increments c_t (one value per row) solve a unit lower-triangular
+// system that is the same for all rows of a head:
+//     c_t + beta_t sum_{s<t} g(t, s) (k_t . k_s) c_s = beta_t (v_t - gamma_t S0 k_t).
+// Then o_t = gamma_t S0 q_t + sum_{s<=t} g(t, s) (k_s . q_t) c_s.  This is the
+// chunkwise (UT-transform) form of the delta rule published for DeltaNet and
+// Gated DeltaNet (Yang et al., "Parallelizing Linear Transformers with the
+// Delta Rule over Sequence Length", 2024; "Gated Delta Networks", 2025), here
+// solved by forward substitution per row.  Only the final state is stored
+// (slot cur, in place); a row's 2T dot products with S0 meet in one set of
+// butterflies instead of 2T dependent ones, and no state is written per token.
+// The result equals the recurrence up to rounding order, not bit for bit.
+template <int DKP>
+__global__ __launch_bounds__(256) void k_deltanet_chunk(DnParams p, int T) {
+  constexpr int DK = 8 * DKP;
+  __shared__ float qs[MAX_T][DK], ksh[MAX_T][DK];
+  __shared__ float vsh[MAX_T][32], zsh[MAX_T][32];
+  __shared__ float ab[MAX_T][2];
+  __shared__ float Am[MAX_T][MAX_T];   // beta_t g(t, s) k_t.k_s for s < t, else 0
+  __shared__ float Mm[MAX_T][MAX_T];   // g(t, s) k_s.q_t for s <= t, else 0
+  __shared__ float gam[MAX_T];         // gamma_t
+  __shared__ float gend[MAX_T];        // g(T-1, s)
+  __shared__ float osh[MAX_T][32];
+  const int nib = p.dv / 32;
+  const int h = blockIdx.x / nib, ib = blockIdx.x % nib;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int part = lane >> 3, r = lane & 7;
+  const int ii = wave * 8 + r;
+  const int i = ib * 32 + ii;
+  const int cur = p.ctrl->cur;
+  const size_t hs = (size_t)DK * p.dv;
+  float* Sp = p.state + ((size_t)cur * p.heads + h) * hs;
+  const int j0 = part * DKP;
+  const size_t sbase = dn_off(i, j0, DKP);
+
+  float S[DKP];
+#pragma unroll
+  for (int jj = 0; jj < DKP; ++jj) S[jj] = Sp[sbase + (size_t)jj * 64];
+
+  // normalised q, k of tokens wave + 4m; v, z of this workgroup's 32 rows; gates
+  {
+    float q0[4], q1[4], k0[4], k1[4];
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int t = wave + 4 * m;
+      q0[m] = q1[m] = k0[m] = k1[m] = 0.0f;
+      if (t < T) {
+        const float* y = p.y + (size_t)t * p.y_stride;
+        if (lane < DK) { q0[m] = y[p.off_q + h * DK + lane]; k0[m] = y[p.off_k + h * DK + lane]; }
+        if (lane + 64 < DK) { q1[m] = y[p.off_q + h * DK + lane + 64]; k1[m] = y[p.off_k + h * DK + lane + 64]; }
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const int t = tid / 32 + 8 * m;
+      if (t < T) {
+        const float* y = p.y + (size_t)t * p.y_stride;
+        vsh[t][tid & 31] = y[p.off_v + h * p.dv + ib * 32 + (tid & 31)];
+        zsh[t][tid & 31] = y[p.off_z + h * p.dv + ib * 32 + (tid & 31)];
+      }
+    }
+    if (tid < T) {
+      const float* y = p.y + (size_t)tid * p.y_stride;
+      ab[tid][0] = sigmoidf_(p.a_scale * y[p.off_a + h] + p.a_bias);
+      ab[tid][1] = sigmoidf_(p.b_scale * y[p.off_b + h]);
+    }
+#pragma unroll
+    for (int m = 0; m < 4; ++m) {
+      const int t = wave + 4 * m;
+      if (t < T) {
+        const float sq = wave_sum(q0[m] * q0[m] + q1[m] * q1[m]), sk = wave_sum(k0[m] * k0[m] + k1[m] * k1[m]);
+        const float rq = 1.0f / sqrtf(sq + 1e-6f), rk = 1.0f / sqrtf(sk + 1e-6f);
+        if (lane < DK) { qs[t][lane] = q0[m] * rq; ksh[t][lane] = k0[m] * rk; }
+        if (lane + 64 < DK) { qs[t][lane + 64] = q1[m] * rq; ksh[t][lane + 64] = k1[m] * rk; }
+      }
+    }
+  }
+  __syncthreads();
+
+  // the head's T x T coefficients: thread (t, s) = (tid / 16, tid % 16); the
+  // decay products are formed directly (no ratio of cumulative products, which
+  // could underflow)
+  {
+    const int t = tid >> 4, s2 = tid & 15;
+    float a_ = 0.0f, m_ = 0.0f;
+    if (t < T && s2 <= t) {
+      float g = 1.0f;
+      for (int x = s2 + 1; x <= t; ++x) g *= ab[x][0];
+      float kk = 0.0f, kq = 0.0f;
+      for (int j = 0; j < DK; ++j) {
+        const float ks = ksh[s2][j];
+        kk = __builtin_fmaf(ksh[t][j], ks, kk);
+        kq = __builtin_fmaf(ks, qs[t][j], kq);
+      }
+      if (s2 < t) a_ = ab[t][1] * g * kk;
+      m_ = g * kq;
+    }
+    Am[t][s2] = a_;
+    Mm[t][s2] = m_;
+    if (tid < MAX_T) {
+      float gg = 1.0f, ge = 1.0f;
+      if (tid < T) {
+        for (int x = 0; x <= tid; ++x) gg *= ab[x][0];
+        for (int x = tid + 1; x < T; ++x) ge *= ab[x][0];
+      }
+      gam[tid] = gg;
+      gend[tid] = ge;
+    }
+  }
+  __syncthreads();
+
+  // S0 k_t and S0 q_t for every token of this lane's row: partial dots, then
+  // the eight parts of the row meet (fixed butterfly order)
+  float wk[MAX_T], wq[MAX_T];
+#pragma unroll
+  for (int t = 0; t < MAX_T; ++t) {
+    float a_ = 0.0f, b_ = 0.0f;
+    if (t < T) {
+#pragma unroll
+      for (int jj = 0; jj < DKP; ++jj) {
+        a_ = __builtin_fmaf(S[jj], ksh[t][j0 + jj], a_);
+        b_ = __builtin_fmaf(S[jj], qs[t][j0 + jj], b_);
+      }
+    }
+    wk[t] = a_;
+    wq[t] = b_;
+  }
+#pragma unroll
+  for (int t = 0; t < MAX_T; ++t) {
+    wk[t] += __shfl_xor(wk[t], 8, 64);
+    wq[t] += __shfl_xor(wq[t], 8, 64);
+    wk[t] += __shfl_xor(wk[t], 16, 64);
+    wq[t] += __shfl_xor(wq[t], 16, 64);
+    wk[t] += __shfl_xor(wk[t], 32, 64);
+    wq[t] += __shfl_xor(wq[t], 32, 64);
+  }
+
+  // increments by forward substitution (every lane of the row does the same)
+  float c[MAX_T];
+#pragma unroll
+  for (int t = 0; t < MAX_T; ++t) {
+    float x = 0.0f;
+    if (t < T) {
+      x = ab[t][1] * (vsh[t][ii] - gam[t] * wk[t]);
+#pragma unroll
+      for (int s2 = 0; s2 < t; ++s2) x = __builtin_fmaf(-Am[t][s2], c[s2], x);
+    }
+    c[t] = x;
+  }
+  // outputs, gated
+  if (part == 0) {
+#pragma unroll
+    for (int t = 0; t < MAX_T; ++t) {
+      if (t < T) {
+        float o = gam[t] * wq[t];
+#pragma unroll
+        for (int s2 = 0; s2 <= t; ++s2) o = __builtin_fmaf(Mm[t][s2], c[s2], o);
+        osh[t][ii] = o * sigmoidf_(p.z_scale * zsh[t][ii]);
+      }
+    }
+  }
+  // final state, in place
+  const float gall = gam[T - 1];
+#pragma unroll
+  for (int jj = 0; jj < DKP; ++jj) {
+    float x = gall * S[jj];
+#pragma unroll
+    for (int t = 0; t < MAX_T; ++t)
+      if (t < T) x = __builtin_fmaf(gend[t] * c[t], ksh[t][j0 + jj], x);
+    Sp[sbase + (size_t)jj * 64] = x;
+  }
+  __syncthreads();
+
+  const int blk = (h * p.dv + ib * 32) / QK;
+  const int nv = p.heads * p.dv;
+  for (int t = wave; t < T; t += 4) {
+    const float uo = osh[t][lane & 31];
+    if (p.u_out && lane < 32) p.u_out[(size_t)t * nv + h * p.dv + ib * 32 + lane] = uo;
+    put_digits(p.next, p.next_qt, t, blk, uo, lane < 32);
+  }
+}
+
 hipError_t launch_deltanet(const DnParams& p, int T, hipStream_t s) {
   if (p.dk % 32 || p.dk > 128 || p.dv % 32 || T < 1 || T > MAX_T) return hipErrorInvalidValue;
+  if (p.mode != DN_DECODE && p.mode != DN_VERIFY && p.mode != DN_CHUNK) return hipErrorInvalidValue;
   const unsigned grid = (unsigned)(p.heads * (p.dv / 32));
+  const bool chunk = p.mode == DN_CHUNK;
   switch (p.dk) {
-    case 32: k_deltanet<4><<<grid, 256, 0, s>>>(p, T); break;
-    case 64: k_deltanet<8><<<grid, 256, 0, s>>>(p, T); break;
-    case 96: k_deltanet<12><<<grid, 256, 0, s>>>(p, T); break;
-    case 128: k_deltanet<16><<<grid, 256, 0, s>>>(p, T); break;
+#define SLQ_DN(DKP)                                            \
+  if (chunk) k_deltanet_chunk<DKP><<<grid, 256, 0, s>>>(p, T); \
+  else k_deltanet<DKP><<<grid, 256, 0, s>>>(p, T);             \
+  break;
+    case 32: SLQ_DN(4)
+    case 64: SLQ_DN(8)
+    case 96: SLQ_DN(12)
+    case 128: SLQ_DN(16)
+#undef SLQ_DN
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -18,7 +18,7 @@ __global__ void k_store_out(const float* __restrict__ h, int n, void* out, int f
     if (fp32) reinterpret_cast<float*>(out)[i] = h[i];
     else reinterpret_cast<__half*>(out)[i] = __float2half_rn(h[i]);
   }
-  if (advance && i == 0) ctrl->pos += 1;
+  if (advance && i == 0) ctrl->pos += advance;
 }
 
 hipError_t launch_store_out(const float* h, int T, int H, void* out, int fp32, Ctrl* ctrl, int advance,

@@ -318,7 +318,7 @@ struct slice {
   void* last_out = nullptr;
   bool eager = false;
   hipStream_t cap = nullptr;
-  std::map<int, hipGraphExec_t> graphs;   // key: T (decode = 0, verify k = k)
+  std::map<int, hipGraphExec_t> graphs;   // key: decode 0, verify k k, prefill k 100 + k
   Ctrl* ctrl() const { return reinterpret_cast<Ctrl*>(ws + L.ctrl); }
   template <class X> X* wsp(size_t off) const { return reinterpret_cast<X*>(ws + off); }
   Packed packed(const Mat& m) const { return Packed{w + m.off, m.rows, m.cols, cfg.qtype}; }
@@ -340,8 +340,9 @@ struct slice {
 // pointers from the control block so a captured graph serves any buffers.
 // only >= 0: enqueue just the GEMV op of that kind for every layer (no entry,
 // mixers or exit), reading the activations the last step left in the workspace.
-static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof = nullptr, int only = -1) {
+static int enqueue_step(slice* s, int T, int mode, hipStream_t st, Prof* prof = nullptr, int only = -1) {
 #define SLQ_MARK(k) do { if (prof) { int r_ = prof->mark(k, st); if (r_) return r_; } } while (0)
+  const bool decode = mode == DN_DECODE;
   const slice_config& c = s->cfg;
   const Layout& L = s->L;
   const int H = c.hidden;
@@ -416,7 +417,7 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       p.a_scale = c.dn_a_scale; p.a_bias = c.dn_a_bias; p.b_scale = c.dn_b_scale; p.z_scale = c.dn_z_scale;
       p.state = reinterpret_cast<float*>(s->ws + L.dn + (size_t)ll.dn_index * L.dn_layer_bytes);
       p.nslots = L.nslots;
-      p.verify = decode ? 0 : 1;
+      p.mode = mode;
       p.ctrl = ctrl;
       p.u_out = nullptr;
       p.next = s->act_u(T);
@@ -464,24 +465,26 @@ static int enqueue_step(slice* s, int T, bool decode, hipStream_t st, Prof* prof
       SLQ_MARK(SLICE_OP_FFN_OUT);
     }
   }
-  if (only < 0) HIPCHK(launch_store_out(h, T, H, nullptr, c.io_fp32, ctrl, decode ? 1 : 0, st));
+  // decode and prefill move the position on the device; a verify waits for commit
+  const int advance = decode ? 1 : mode == DN_CHUNK ? T : 0;
+  if (only < 0) HIPCHK(launch_store_out(h, T, H, nullptr, c.io_fp32, ctrl, advance, st));
   SLQ_MARK(SLICE_OP_EXIT);
   return SLICE_OK;
 #undef SLQ_MARK
 }
 
-static int run_step(slice* s, int T, bool decode, const void* in, void* out, hipStream_t st) {
+static int run_step(slice* s, int T, int mode, const void* in, void* out, hipStream_t st) {
   if (in != s->last_in || out != s->last_out) {
     HIPCHK(launch_ctrl_io(s->ctrl(), in, out, st));
     s->last_in = in;
     s->last_out = out;
   }
-  if (s->eager) return enqueue_step(s, T, decode, st);
-  const int key = decode ? 0 : T;
+  if (s->eager) return enqueue_step(s, T, mode, st);
+  const int key = mode == DN_DECODE ? 0 : mode == DN_CHUNK ? 100 + T : T;
   auto it = s->graphs.find(key);
   if (it == s->graphs.end()) {
     HIPCHK(hipStreamBeginCapture(s->cap, hipStreamCaptureModeThreadLocal));
-    int rc = enqueue_step(s, T, decode, s->cap);
+    int rc = enqueue_step(s, T, mode, s->cap);
     hipGraph_t g = nullptr;
     hipError_t e = hipStreamEndCapture(s->cap, &g);
     if (rc) {
@@ -699,7 +702,7 @@ int slice_decode(slice_t* s, const void* in, void* out, void* stream) {
   if (!s || !in || !out) return fail(SLICE_EINVAL, "slice_decode: null argument");
   if (s->pending) return fail(SLICE_ESTATE, "slice_decode: a verify is waiting for slice_commit");
   if (s->L.n_attn && s->pos + 1 > s->cfg.max_seq) return fail(SLICE_ERANGE, "slice_decode: position reached max_seq");
-  int rc = run_step(s, 1, true, in, out, S(stream));
+  int rc = run_step(s, 1, DN_DECODE, in, out, S(stream));
   if (rc) return rc;
   s->pos += 1;
   return SLICE_OK;
@@ -717,7 +720,7 @@ int slice_decode_profiled(slice_t* s, const void* in, void* out, int* op_kind, f
     s->last_out = out;
   }
   Prof prof;
-  int rc = enqueue_step(s, 1, true, st, &prof);
+  int rc = enqueue_step(s, 1, DN_DECODE, st, &prof);
   int n = 0;
   if (!rc) {
     hipError_t e = hipEventSynchronize(prof.ev.back());
@@ -740,7 +743,7 @@ int slice_run_gemv_op(slice_t* s, int op_kind, void* stream) {
       op_kind != SLICE_OP_ATT_OUT && op_kind != SLICE_OP_FFN_IN && op_kind != SLICE_OP_FFN_OUT)
     return fail(SLICE_EINVAL, "slice_run_gemv_op: not a GEMV op kind");
   if (s->pending) return fail(SLICE_ESTATE, "slice_run_gemv_op: a verify is waiting for slice_commit");
-  return enqueue_step(s, 1, true, S(stream), nullptr, op_kind);
+  return enqueue_step(s, 1, DN_DECODE, S(stream), nullptr, op_kind);
 }
 
 int slice_verify(slice_t* s, int k, const void* in, void* out, void* stream) {
@@ -748,9 +751,20 @@ int slice_verify(slice_t* s, int k, const void* in, void* out, void* stream) {
   if (s->pending) return fail(SLICE_ESTATE, "slice_verify: a verify is waiting for slice_commit");
   if (k < 1 || k > s->cfg.max_verify) return fail(SLICE_ERANGE, "slice_verify: k outside 1..max_verify");
   if (s->L.n_attn && s->pos + k > s->cfg.max_seq) return fail(SLICE_ERANGE, "slice_verify: positions pass max_seq");
-  int rc = run_step(s, k, false, in, out, S(stream));
+  int rc = run_step(s, k, DN_VERIFY, in, out, S(stream));
   if (rc) return rc;
   s->pending = k;
+  return SLICE_OK;
+}
+
+int slice_prefill(slice_t* s, int k, const void* in, void* out, void* stream) {
+  if (!s || !in || !out) return fail(SLICE_EINVAL, "slice_prefill: null argument");
+  if (s->pending) return fail(SLICE_ESTATE, "slice_prefill: a verify is waiting for slice_commit");
+  if (k < 1 || k > s->cfg.max_verify) return fail(SLICE_ERANGE, "slice_prefill: k outside 1..max_verify");
+  if (s->L.n_attn && s->pos + k > s->cfg.max_seq) return fail(SLICE_ERANGE, "slice_prefill: positions pass max_seq");
+  int rc = run_step(s, k, DN_CHUNK, in, out, S(stream));
+  if (rc) return rc;
+  s->pos += k;
   return SLICE_OK;
 }
 

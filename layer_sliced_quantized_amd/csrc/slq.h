@@ -136,7 +136,7 @@ int gemm_min_tokens(int qt, int waves);
 hipError_t launch_resid_finish(int in_kind, const void* in, const Ctrl* ctrl, int64_t in_tstride,
                                int T, int H, float* h, const float* norm_w, int qt, Act next,
                                float* ssq_out, hipStream_t s);
-// out == nullptr: write to ctrl->out.
+// out == nullptr: write to ctrl->out.  advance_pos: added to ctrl->pos.
 hipError_t launch_store_out(const float* h, int T, int H, void* out, int fp32, Ctrl* ctrl,
                             int advance_pos, hipStream_t s);
 hipError_t launch_ctrl_io(Ctrl* c, const void* in, void* out, hipStream_t s);
@@ -144,6 +144,12 @@ hipError_t launch_ctrl_set(Ctrl* c, int pos, int cur, hipStream_t s);
 hipError_t launch_embed(const Packed& E, const int32_t* tok, void* out, int fp32, hipStream_t s);
 hipError_t launch_argmax(const float* logits, int n, float* part_v, int* part_i, int nparts,
                          int32_t* tok, hipStream_t s);
+
+// DeltaNet update modes: DN_DECODE updates slot cur in place (one token);
+// DN_VERIFY writes the state after token t to slot (cur+1+t) % nslots and
+// leaves slot cur intact; DN_CHUNK takes all tokens at once in the chunked
+// form and leaves only the final state, in slot cur.
+enum { DN_DECODE = 0, DN_VERIFY = 1, DN_CHUNK = 2 };
 
 struct DnParams {
   const float* y;        // G1 output [T][y_stride]
@@ -153,7 +159,7 @@ struct DnParams {
   float a_scale, a_bias, b_scale, z_scale;
   float* state;          // slot 0 of this layer: [nslots][heads][dv/8][dk/8][8][8] (see k_deltanet)
   int nslots;
-  int verify;            // 0: in place on slot cur; 1: token t -> slot (cur+1+t) % nslots
+  int mode;              // DN_DECODE, DN_VERIFY or DN_CHUNK (below)
   const Ctrl* ctrl;
   float* u_out;          // [T][heads*dv] (nullable)
   Act next; int next_qt;

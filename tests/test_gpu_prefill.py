@@ -1,0 +1,108 @@
+"""GPU parity of prompt ingestion (slice_prefill): k tokens in one pass, the
+DeltaNet layers in the chunked form, against k plain steps of the CPU oracle.
+
+Hidden states, DeltaNet states and the new KV rows: max relative error <= 2e-3
+against the fp64 oracle; the position moves by k and decoding carries on from
+the prefilled state."""
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+import synth
+from helpers import make_pair, inputs, rel_err, TOL
+
+import layer_sliced_quantized_amd as slq
+
+pytestmark = pytest.mark.gpu
+
+TINY_H = synth.ModelShape(
+    name="tiny_hybrid_128", hidden=128, n_layers=4, attn_period=4,
+    dn_heads=2, dn_dk=64, dn_dv=64, q_heads=4, kv_heads=2, head_dim=64, rope_dims=32,
+    rope_theta=1e7, qk_norm=True, attn_gate=True, eps=1e-6, ffn=256, vocab=0)
+WL = 93
+
+
+def _t(a):
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+def _check_prefill(shape, qtype, k, prefill, *, workload=WL, max_seq=512, layers=4):
+    s, orc, _, _ = make_pair(shape, qtype, 0, layers, workload=workload, prefill=prefill, max_seq=max_seq)
+    H = inputs(shape, k + 1, workload=workload)
+    out = s.prefill(_t(H[:k])).cpu().numpy()
+    for t in range(k):
+        ref = orc.decode(H[t], raw=True)
+        assert np.isfinite(out[t]).all(), t
+        assert rel_err(out[t], ref) <= TOL, t
+    assert s.position == orc.pos == prefill + k
+    for l in range(layers):
+        if shape.is_attention(l):
+            K, V = s.get_kv(l, prefill + k)
+            Ko, Vo = orc.kv[l]
+            np.testing.assert_array_equal(K.cpu().numpy()[:, :prefill], Ko[:, :prefill])
+            assert rel_err(K.cpu().numpy()[:, prefill:prefill + k], Ko[:, prefill:prefill + k]) <= TOL
+            assert rel_err(V.cpu().numpy()[:, prefill:prefill + k], Vo[:, prefill:prefill + k]) <= TOL
+        else:
+            assert rel_err(s.get_state(l).cpu().numpy(), orc.dn[l]) <= TOL, l
+    # decoding carries on from the prefilled state and position
+    nxt = s.decode(_t(H[k])).cpu().numpy()
+    assert rel_err(nxt, orc.decode(H[k], raw=True)) <= TOL
+
+
+@pytest.mark.parametrize("k", [1, 2, 5, 9, 16])
+def test_tiny_hybrid_prefill(k):
+    _check_prefill(TINY_H, synth.Q4_0, k, 300)
+
+
+@pytest.mark.parametrize("prefill", [0, 250])
+def test_tiny_hybrid_prefill_16_from_empty_and_across_chunk(prefill):
+    _check_prefill(TINY_H, synth.Q4_0, 16, prefill)
+
+
+def test_tiny_hybrid_q8_prefill():
+    _check_prefill(TINY_H, synth.Q8_0, 16, 100)
+
+
+@pytest.mark.parametrize("a_bias", [-40.0, 40.0])
+def test_prefill_with_vanishing_and_unit_decay(a_bias):
+    # alpha ~ 4e-18: the decay products of a 16-token chunk underflow fp32;
+    # alpha = 1 in fp32: no decay at all
+    shape = dataclasses.replace(TINY_H, name=f"tiny_hybrid_a{a_bias:+.0f}", dn_a_bias=a_bias)
+    _check_prefill(shape, synth.Q4_0, 16, 300, layers=3)
+
+
+def test_prefill_after_verify_and_errors():
+    s, orc, _, _ = make_pair(TINY_H, synth.Q4_0, 0, 4, workload=WL, prefill=300, max_seq=320, max_verify=16)
+    H = inputs(TINY_H, 24, workload=WL)
+    s.verify(_t(H[:4]))
+    with pytest.raises(slq.SliceError):
+        s.prefill(_t(H[4:8]))            # a verify is pending
+    s.commit(2)
+    orc.decode(H[0], raw=True)
+    orc.decode(H[1], raw=True)
+    with pytest.raises(slq.SliceError):
+        s.prefill(_t(np.zeros((17, TINY_H.hidden), np.float32)))   # k > max_verify
+    out = s.prefill(_t(H[2:18])).cpu().numpy()
+    for t in range(16):
+        assert rel_err(out[t], orc.decode(H[2 + t], raw=True)) <= TOL, t
+    assert s.position == 318
+    with pytest.raises(slq.SliceError):
+        s.prefill(_t(H[18:21]))          # positions would pass max_seq
+    assert s.position == 318
+
+
+DN_LAYER = dataclasses.replace(synth.HYBRID_5120, name="deltanet_layer_5120", ffn=0)
+
+
+@pytest.mark.timeout(300)
+def test_deltanet_layer_5120_prefill_16():
+    s, orc, _, _ = make_pair(DN_LAYER, synth.Q4_0, 0, 1, workload=synth.WL_DELTANET, max_seq=64)
+    H = inputs(DN_LAYER, 17, workload=synth.WL_DELTANET)
+    s.decode(_t(H[0]))
+    orc.decode(H[0], raw=True)
+    out = s.prefill(_t(H[1:])).cpu().numpy()
+    for t in range(16):
+        assert rel_err(out[t], orc.decode(H[1 + t], raw=True)) <= TOL, t
+    assert rel_err(s.get_state(0).cpu().numpy(), orc.dn[0]) <= TOL
