@@ -185,6 +185,24 @@ def run_prefill(s, H, chunks, k=16):
             "tok_s": round(chunks * k / sec, 1)}
 
 
+def run_prefill_chunked(s, H, chunks, k=16):
+    """Prompt ingestion through slice_prefill (chunked DeltaNet, no commit),
+    pass after pass (HIP events around the passes)."""
+    import torch
+    out = torch.empty((k, H.shape[1]), dtype=torch.float16, device="cuda")
+    s.prefill(H[0:k], out)         # warm the k-token graph
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for c in range(1, chunks + 1):
+        s.prefill(H[c * k:(c + 1) * k], out)
+    ev1.record()
+    torch.cuda.synchronize()
+    sec = ev0.elapsed_time(ev1) / 1e3
+    return {"tokens_per_pass": k, "passes": chunks, "ms_per_pass": round(sec / chunks * 1e3, 3),
+            "tok_s": round(chunks * k / sec, 1)}
+
+
 def gemv_sweep(seed, reps):
     import torch
     import synth
@@ -267,7 +285,7 @@ def main() -> int:
     ap.add_argument("--profile-steps", type=int, default=4)
     ap.add_argument("--gemv-reps", type=int, default=8, help="repetitions of the 64-layer GEMV timing runs")
     ap.add_argument("--verify-rounds", type=int, default=32)
-    ap.add_argument("--prefill-chunks", type=int, default=8, help="16-token verify+commit passes timed as prefill")
+    ap.add_argument("--prefill-chunks", type=int, default=8, help="16-token passes timed as prefill, both as verify+commit and as slice_prefill")
     ap.add_argument("--cpu-tokens", type=int, default=2)
     ap.add_argument("--sweep-reps", type=int, default=50)
     ap.add_argument("--no-q8", action="store_true")
@@ -288,7 +306,7 @@ def main() -> int:
     torch.cuda.set_device(0)
     threads = min(16, os.cpu_count() or 8)
     shape = synth.HYBRID_5120
-    n_in = args.warmup + args.steps + args.profile_steps + 4 * (args.verify_rounds + 1) + 16 * (args.prefill_chunks + 1) + 16
+    n_in = args.warmup + args.steps + args.profile_steps + 4 * (args.verify_rounds + 1) + 32 * (args.prefill_chunks + 1) + 16
     max_seq = ((PREFILL + n_in + 63) // 64) * 64
     log(f"inputs: {n_in} fresh fp16 hidden states; max_seq {max_seq}")
     H_host = synth.hidden_inputs(args.seed, synth.WL_SLICE, n_in, shape.hidden)
@@ -342,6 +360,9 @@ def main() -> int:
     base += 4 * (args.verify_rounds + 1)
     pre = run_prefill(s, H[base:], args.prefill_chunks) if args.prefill_chunks > 0 else None
     log(f"prefill (16-token passes): {pre}")
+    base += 16 * (args.prefill_chunks + 1)
+    pre_c = run_prefill_chunked(s, H[base:], args.prefill_chunks) if args.prefill_chunks > 0 else None
+    log(f"prefill (16-token passes, chunked DeltaNet): {pre_c}")
     del s
     torch.cuda.empty_cache()
 
@@ -394,6 +415,7 @@ def main() -> int:
         "eager_step_ms": round(step_ms, 4),
         "verify": ver,
         "prefill_16": pre,
+        "prefill_16_chunked": pre_c,
     }
     res.update(extra)
     print(json.dumps(res), flush=True)

@@ -23,6 +23,25 @@
 
 namespace slq {
 
+// Sum over the eight lanes l, l ^ 8, ..., l ^ 56 that hold the parts of one
+// row, with the additions in the order x + x[l^8], then + [l^16], then
+// + [l^32], so every lane gets the same bits.  The exchanges stay in the
+// vector ALU (a DPP rotate by 8 within 16-lane rows is the xor 8 partner, and
+// gfx950's permlane16/32 swaps give the xor 16 and xor 32 partners), with no
+// LDS round trip.
+__device__ __forceinline__ float row_sum8(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128 /* row_ror:8 */, 0xf, 0xf, false));
+  {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v += __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+  }
+  {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    v += __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  }
+  return v;
+}
+
 // Offset of S[i][j] inside one head's state (d_k = 8 dkp).
 __host__ __device__ inline size_t dn_off(int i, int j, int dkp) {
   return ((size_t)((i >> 3) * dkp + j % dkp) * 8 + j / dkp) * 8 + (i & 7);
@@ -31,8 +50,8 @@ __host__ __device__ inline size_t dn_off(int i, int j, int dkp) {
 // One workgroup of 4 waves per (head, 32 rows of S); wave w owns rows
 // 32 ib + 8 w + r, lane (part, r) = (lane / 8, lane % 8) the key range
 // [part*DKP, part*DKP + DKP) of its row.  The eight parts of a row meet in a
-// butterfly over lanes r, r + 8, ..., r + 56 (a fixed order, so the sums are
-// deterministic).
+// butterfly over lanes r, r + 8, ..., r + 56 (row_sum8: a fixed order, so the
+// sums are deterministic).
 //
 // Every token's inputs are requested together before the first update (the
 // recurrence itself runs token after token): the waves normalise q and k of
@@ -124,9 +143,7 @@ __global__ __launch_bounds__(256) void k_deltanet(DnParams p, int T) {
     float up = 0.0f;
 #pragma unroll
     for (int jj = 0; jj < DKP; ++jj) up = __builtin_fmaf(S[jj], ksh[t][j0 + jj], up);
-    up += __shfl_xor(up, 8, 64);
-    up += __shfl_xor(up, 16, 64);
-    up += __shfl_xor(up, 32, 64);
+    up = row_sum8(up);
     const float c = beta * (vi - alpha * up);
     float op = 0.0f;
 #pragma unroll
@@ -134,9 +151,7 @@ __global__ __launch_bounds__(256) void k_deltanet(DnParams p, int T) {
       S[jj] = __builtin_fmaf(c, ksh[t][j0 + jj], alpha * S[jj]);
       op = __builtin_fmaf(S[jj], qs[t][j0 + jj], op);
     }
-    op += __shfl_xor(op, 8, 64);
-    op += __shfl_xor(op, 16, 64);
-    op += __shfl_xor(op, 32, 64);
+    op = row_sum8(op);
     if (part == 0) osh[t][ii] = op * sigmoidf_(p.z_scale * (one ? z1 : zsh[t][ii]));
 
     float* S_out = p.mode == DN_VERIFY ? p.state + ((size_t)((cur + 1 + t) % p.nslots) * p.heads + h) * hs
@@ -175,22 +190,30 @@ __global__ __launch_bounds__(256) void k_deltanet(DnParams p, int T) {
 // butterflies instead of 2T dependent ones, and no state is written per token.
 // The result equals the recurrence up to rounding order, not bit for bit.
 template <int DKP>
-__global__ __launch_bounds__(256) void k_deltanet_chunk(DnParams p, int T) {
+__global__ __launch_bounds__(1024) void k_deltanet_chunk(DnParams p, int T) {
   constexpr int DK = 8 * DKP;
-  __shared__ float qs[MAX_T][DK], ksh[MAX_T][DK];
+  constexpr int DKS = DK + 4;          // padded LDS row: rows of different tokens start in different banks
+  constexpr int JQ = DK / 4;           // key range of one coefficient partial
+  constexpr int JJ = DKP / 4;          // state entries a lane finalises
+  // Tokens T..MAX_T-1 are padding with q = k = v = 0, alpha = 1, beta = 0:
+  // their increments are zero and they change neither the outputs of real
+  // tokens nor the final state, so the loops run over MAX_T tokens.
+  __shared__ float qs[MAX_T][DKS], ksh[MAX_T][DKS];
   __shared__ float vsh[MAX_T][32], zsh[MAX_T][32];
-  __shared__ float ab[MAX_T][2];
+  __shared__ float al[MAX_T], be[MAX_T];
+  __shared__ float pk[4][MAX_T * MAX_T], pq[4][MAX_T * MAX_T];   // k_t.k_s, k_s.q_t over key quarters
   __shared__ float Am[MAX_T][MAX_T];   // beta_t g(t, s) k_t.k_s for s < t, else 0
   __shared__ float Mm[MAX_T][MAX_T];   // g(t, s) k_s.q_t for s <= t, else 0
-  __shared__ float gam[MAX_T];         // gamma_t
-  __shared__ float gend[MAX_T];        // g(T-1, s)
+  __shared__ float wkl[MAX_T][32], wql[MAX_T][32];   // S0_i . k_t, S0_i . q_t
+  __shared__ float csh[MAX_T][32];     // c_t
   __shared__ float osh[MAX_T][32];
   const int nib = p.dv / 32;
   const int h = blockIdx.x / nib, ib = blockIdx.x % nib;
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = tid & 63, w = tid >> 6;
+  const int rg = w & 3, tg = w >> 2;   // rows 8 rg .. 8 rg + 7; tokens (and state entries) of quarter tg
   const int part = lane >> 3, r = lane & 7;
-  const int ii = wave * 8 + r;
+  const int ii = rg * 8 + r;
   const int i = ib * 32 + ii;
   const int cur = p.ctrl->cur;
   const size_t hs = (size_t)DK * p.dv;
@@ -202,146 +225,142 @@ __global__ __launch_bounds__(256) void k_deltanet_chunk(DnParams p, int T) {
 #pragma unroll
   for (int jj = 0; jj < DKP; ++jj) S[jj] = Sp[sbase + (size_t)jj * 64];
 
-  // normalised q, k of tokens wave + 4m; v, z of this workgroup's 32 rows; gates
+  // wave w normalises q, k of token w; v (threads 0..511) and z (512..1023)
+  // of token (tid / 32) % 16, row tid % 32; gates of token tid
   {
-    float q0[4], q1[4], k0[4], k1[4];
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int t = wave + 4 * m;
-      q0[m] = q1[m] = k0[m] = k1[m] = 0.0f;
-      if (t < T) {
-        const float* y = p.y + (size_t)t * p.y_stride;
-        if (lane < DK) { q0[m] = y[p.off_q + h * DK + lane]; k0[m] = y[p.off_k + h * DK + lane]; }
-        if (lane + 64 < DK) { q1[m] = y[p.off_q + h * DK + lane + 64]; k1[m] = y[p.off_k + h * DK + lane + 64]; }
-      }
+    float q0 = 0.0f, q1 = 0.0f, k0 = 0.0f, k1 = 0.0f;
+    if (w < T) {
+      const float* y = p.y + (size_t)w * p.y_stride;
+      if (lane < DK) { q0 = y[p.off_q + h * DK + lane]; k0 = y[p.off_k + h * DK + lane]; }
+      if (lane + 64 < DK) { q1 = y[p.off_q + h * DK + lane + 64]; k1 = y[p.off_k + h * DK + lane + 64]; }
     }
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const int t = tid / 32 + 8 * m;
-      if (t < T) {
-        const float* y = p.y + (size_t)t * p.y_stride;
-        vsh[t][tid & 31] = y[p.off_v + h * p.dv + ib * 32 + (tid & 31)];
-        zsh[t][tid & 31] = y[p.off_z + h * p.dv + ib * 32 + (tid & 31)];
-      }
-    }
-    if (tid < T) {
-      const float* y = p.y + (size_t)tid * p.y_stride;
-      ab[tid][0] = sigmoidf_(p.a_scale * y[p.off_a + h] + p.a_bias);
-      ab[tid][1] = sigmoidf_(p.b_scale * y[p.off_b + h]);
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int t = wave + 4 * m;
-      if (t < T) {
-        const float sq = wave_sum(q0[m] * q0[m] + q1[m] * q1[m]), sk = wave_sum(k0[m] * k0[m] + k1[m] * k1[m]);
-        const float rq = 1.0f / sqrtf(sq + 1e-6f), rk = 1.0f / sqrtf(sk + 1e-6f);
-        if (lane < DK) { qs[t][lane] = q0[m] * rq; ksh[t][lane] = k0[m] * rk; }
-        if (lane + 64 < DK) { qs[t][lane + 64] = q1[m] * rq; ksh[t][lane + 64] = k1[m] * rk; }
-      }
-    }
-  }
-  __syncthreads();
-
-  // the head's T x T coefficients: thread (t, s) = (tid / 16, tid % 16); the
-  // decay products are formed directly (no ratio of cumulative products, which
-  // could underflow)
-  {
-    const int t = tid >> 4, s2 = tid & 15;
-    float a_ = 0.0f, m_ = 0.0f;
-    if (t < T && s2 <= t) {
-      float g = 1.0f;
-      for (int x = s2 + 1; x <= t; ++x) g *= ab[x][0];
-      float kk = 0.0f, kq = 0.0f;
-      for (int j = 0; j < DK; ++j) {
-        const float ks = ksh[s2][j];
-        kk = __builtin_fmaf(ksh[t][j], ks, kk);
-        kq = __builtin_fmaf(ks, qs[t][j], kq);
-      }
-      if (s2 < t) a_ = ab[t][1] * g * kk;
-      m_ = g * kq;
-    }
-    Am[t][s2] = a_;
-    Mm[t][s2] = m_;
-    if (tid < MAX_T) {
-      float gg = 1.0f, ge = 1.0f;
-      if (tid < T) {
-        for (int x = 0; x <= tid; ++x) gg *= ab[x][0];
-        for (int x = tid + 1; x < T; ++x) ge *= ab[x][0];
-      }
-      gam[tid] = gg;
-      gend[tid] = ge;
-    }
-  }
-  __syncthreads();
-
-  // S0 k_t and S0 q_t for every token of this lane's row: partial dots, then
-  // the eight parts of the row meet (fixed butterfly order)
-  float wk[MAX_T], wq[MAX_T];
-#pragma unroll
-  for (int t = 0; t < MAX_T; ++t) {
-    float a_ = 0.0f, b_ = 0.0f;
-    if (t < T) {
-#pragma unroll
-      for (int jj = 0; jj < DKP; ++jj) {
-        a_ = __builtin_fmaf(S[jj], ksh[t][j0 + jj], a_);
-        b_ = __builtin_fmaf(S[jj], qs[t][j0 + jj], b_);
-      }
-    }
-    wk[t] = a_;
-    wq[t] = b_;
-  }
-#pragma unroll
-  for (int t = 0; t < MAX_T; ++t) {
-    wk[t] += __shfl_xor(wk[t], 8, 64);
-    wq[t] += __shfl_xor(wq[t], 8, 64);
-    wk[t] += __shfl_xor(wk[t], 16, 64);
-    wq[t] += __shfl_xor(wq[t], 16, 64);
-    wk[t] += __shfl_xor(wk[t], 32, 64);
-    wq[t] += __shfl_xor(wq[t], 32, 64);
-  }
-
-  // increments by forward substitution (every lane of the row does the same)
-  float c[MAX_T];
-#pragma unroll
-  for (int t = 0; t < MAX_T; ++t) {
+    const int t2 = (tid >> 5) & 15, row = tid & 31;
     float x = 0.0f;
-    if (t < T) {
-      x = ab[t][1] * (vsh[t][ii] - gam[t] * wk[t]);
-#pragma unroll
-      for (int s2 = 0; s2 < t; ++s2) x = __builtin_fmaf(-Am[t][s2], c[s2], x);
+    if (t2 < T) x = p.y[(size_t)t2 * p.y_stride + (tid < 512 ? p.off_v : p.off_z) + h * p.dv + ib * 32 + row];
+    if (tid < 512) vsh[t2][row] = x;
+    else zsh[t2][row] = x;
+    if (tid < MAX_T) {
+      float a_ = 1.0f, b_ = 0.0f;
+      if (tid < T) {
+        const float* y = p.y + (size_t)tid * p.y_stride;
+        a_ = sigmoidf_(p.a_scale * y[p.off_a + h] + p.a_bias);
+        b_ = sigmoidf_(p.b_scale * y[p.off_b + h]);
+      }
+      al[tid] = a_;
+      be[tid] = b_;
     }
-    c[t] = x;
+    const float sq = wave_sum(q0 * q0 + q1 * q1), sk = wave_sum(k0 * k0 + k1 * k1);
+    const float rq = 1.0f / sqrtf(sq + 1e-6f), rk = 1.0f / sqrtf(sk + 1e-6f);
+    if (lane < DK) { qs[w][lane] = q0 * rq; ksh[w][lane] = k0 * rk; }
+    if (lane + 64 < DK) { qs[w][lane + 64] = q1 * rq; ksh[w][lane + 64] = k1 * rk; }
   }
-  // outputs, gated
-  if (part == 0) {
+  __syncthreads();
+
+  // decays: gamma_t = alpha_0 ... alpha_t, g(T-1, t) = alpha_{t+1} ... alpha_{MAX_T-1}
+  float a[MAX_T], gam[MAX_T], gend[MAX_T];
+#pragma unroll
+  for (int t = 0; t < MAX_T; ++t) a[t] = al[t];
+  gam[0] = a[0];
+#pragma unroll
+  for (int t = 1; t < MAX_T; ++t) gam[t] = gam[t - 1] * a[t];
+  gend[MAX_T - 1] = 1.0f;
+#pragma unroll
+  for (int t = MAX_T - 2; t >= 0; --t) gend[t] = gend[t + 1] * a[t + 1];
+
+  // partial k_t.k_s and k_s.q_t: thread (quarter, t, s) = (tid / 256, (tid / 16) % 16, tid % 16)
+  {
+    const int pr = tid & 255, qq = tid >> 8;
+    const int t = pr >> 4, s2 = pr & 15;
+    float kk = 0.0f, kq = 0.0f;
+#pragma unroll 8
+    for (int j = qq * JQ; j < qq * JQ + JQ; ++j) {
+      const float ks = ksh[s2][j];
+      kk = __builtin_fmaf(ksh[t][j], ks, kk);
+      kq = __builtin_fmaf(ks, qs[t][j], kq);
+    }
+    pk[qq][pr] = kk;
+    pq[qq][pr] = kq;
+  }
+  // S0_i . k_t and S0_i . q_t for the wave's four tokens: partial dots, then
+  // the eight parts of the row meet
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int t = tg * 4 + m;
+    float a_ = 0.0f, b_ = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < DKP; ++jj) {
+      a_ = __builtin_fmaf(S[jj], ksh[t][j0 + jj], a_);
+      b_ = __builtin_fmaf(S[jj], qs[t][j0 + jj], b_);
+    }
+    a_ = row_sum8(a_);
+    b_ = row_sum8(b_);
+    if (part == 0) {
+      wkl[t][ii] = a_;
+      wql[t][ii] = b_;
+    }
+  }
+  __syncthreads();
+
+  // the head's coefficients (decay products formed directly: a ratio of
+  // cumulative products could underflow)
+  if (tid < MAX_T * MAX_T) {
+    const int t = tid >> 4, s2 = tid & 15;
+    float g = 1.0f;
+#pragma unroll
+    for (int x = 1; x < MAX_T; ++x) g *= (x > s2 && x <= t) ? a[x] : 1.0f;
+    const float kk = ((pk[0][tid] + pk[1][tid]) + pk[2][tid]) + pk[3][tid];
+    const float kq = ((pq[0][tid] + pq[1][tid]) + pq[2][tid]) + pq[3][tid];
+    Am[t][s2] = s2 < t ? be[t] * g * kk : 0.0f;
+    Mm[t][s2] = s2 <= t ? g * kq : 0.0f;
+  }
+  __syncthreads();
+
+  // increments by forward substitution, one lane per row
+  if (tid < 32) {
+    float c[MAX_T];
 #pragma unroll
     for (int t = 0; t < MAX_T; ++t) {
-      if (t < T) {
-        float o = gam[t] * wq[t];
+      float x = be[t] * (vsh[t][tid] - gam[t] * wkl[t][tid]);
 #pragma unroll
-        for (int s2 = 0; s2 <= t; ++s2) o = __builtin_fmaf(Mm[t][s2], c[s2], o);
-        osh[t][ii] = o * sigmoidf_(p.z_scale * zsh[t][ii]);
-      }
+      for (int s2 = 0; s2 < t; ++s2) x = __builtin_fmaf(-Am[t][s2], c[s2], x);
+      c[t] = x;
+      csh[t][tid] = x;
     }
-  }
-  // final state, in place
-  const float gall = gam[T - 1];
-#pragma unroll
-  for (int jj = 0; jj < DKP; ++jj) {
-    float x = gall * S[jj];
-#pragma unroll
-    for (int t = 0; t < MAX_T; ++t)
-      if (t < T) x = __builtin_fmaf(gend[t] * c[t], ksh[t][j0 + jj], x);
-    Sp[sbase + (size_t)jj * 64] = x;
   }
   __syncthreads();
 
-  const int blk = (h * p.dv + ib * 32) / QK;
-  const int nv = p.heads * p.dv;
-  for (int t = wave; t < T; t += 4) {
-    const float uo = osh[t][lane & 31];
-    if (p.u_out && lane < 32) p.u_out[(size_t)t * nv + h * p.dv + ib * 32 + lane] = uo;
-    put_digits(p.next, p.next_qt, t, blk, uo, lane < 32);
+  // gated outputs: thread (token, row) = (tid / 32, tid % 32) for tid < 512
+  if (tid < MAX_T * 32) {
+    const int t = tid >> 5, row = tid & 31;
+    float o = gam[t] * wql[t][row];
+#pragma unroll
+    for (int s2 = 0; s2 < MAX_T; ++s2) o = __builtin_fmaf(Mm[t][s2], csh[s2][row], o);
+    osh[t][row] = o * sigmoidf_(p.z_scale * zsh[t][row]);
+  }
+  // final state, in place: the wave's quarter of each lane's entries
+  {
+    float cc[MAX_T];
+#pragma unroll
+    for (int t = 0; t < MAX_T; ++t) cc[t] = csh[t][ii] * gend[t];
+    const float gall = gam[MAX_T - 1];
+#pragma unroll
+    for (int jj = 0; jj < DKP; ++jj) {
+      if (jj / JJ != tg) continue;
+      float x = gall * S[jj];
+#pragma unroll
+      for (int t = 0; t < MAX_T; ++t) x = __builtin_fmaf(cc[t], ksh[t][j0 + jj], x);
+      Sp[sbase + (size_t)jj * 64] = x;
+    }
+  }
+
+  __syncthreads();
+
+  // digits: token w by wave w; lanes l and l + 32 hold row l's value
+  if (w < T) {
+    const int blk = (h * p.dv + ib * 32) / QK;
+    const float uo = osh[w][lane & 31];
+    if (p.u_out && lane < 32) p.u_out[(size_t)w * (p.heads * p.dv) + h * p.dv + ib * 32 + lane] = uo;
+    put_digits(p.next, p.next_qt, w, blk, uo, lane < 32);
   }
 }
 
@@ -352,7 +371,7 @@ hipError_t launch_deltanet(const DnParams& p, int T, hipStream_t s) {
   const bool chunk = p.mode == DN_CHUNK;
   switch (p.dk) {
 #define SLQ_DN(DKP)                                            \
-  if (chunk) k_deltanet_chunk<DKP><<<grid, 256, 0, s>>>(p, T); \
+  if (chunk) k_deltanet_chunk<DKP><<<grid, 1024, 0, s>>>(p, T); \
   else k_deltanet<DKP><<<grid, 256, 0, s>>>(p, T);             \
   break;
     case 32: SLQ_DN(4)
