@@ -106,3 +106,23 @@ def test_deltanet_layer_5120_prefill_16():
     for t in range(16):
         assert rel_err(out[t], orc.decode(H[1 + t], raw=True)) <= TOL, t
     assert rel_err(s.get_state(0).cpu().numpy(), orc.dn[0]) <= TOL
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 64), (96, 32)])
+def test_prefill_other_key_widths(dk, dv):
+    # d_k = 32 and 96: one and three state entries per lane to finalise
+    shape = dataclasses.replace(TINY_H, name=f"tiny_hybrid_dk{dk}", dn_dk=dk, dn_dv=dv)
+    _check_prefill(shape, synth.Q4_0, 16, 300, layers=3)
+    _check_prefill(shape, synth.Q4_0, 7, 300, layers=3)
+
+
+def test_tiny_llama_prefill():
+    """A slice without DeltaNet layers: the pass is products and attention only."""
+    sh = synth.TINY_LLAMA
+    s, orc, _, _ = make_pair(sh, synth.Q4_0, 0, 6, workload=synth.WL_TINY_LLAMA, prefill=128, max_seq=256)
+    H = inputs(sh, 13, workload=synth.WL_TINY_LLAMA)
+    out = s.prefill(_t(H[:12])).cpu().numpy()
+    for t in range(12):
+        assert rel_err(out[t], orc.decode(H[t], raw=True)) <= TOL, t
+    assert s.position == 140
+    assert rel_err(s.decode(_t(H[12])).cpu().numpy(), orc.decode(H[12], raw=True)) <= TOL
