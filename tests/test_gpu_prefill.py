@@ -126,3 +126,21 @@ def test_tiny_llama_prefill():
         assert rel_err(out[t], orc.decode(H[t], raw=True)) <= TOL, t
     assert s.position == 140
     assert rel_err(s.decode(_t(H[12])).cpu().numpy(), orc.decode(H[12], raw=True)) <= TOL
+
+
+@pytest.mark.timeout(900)
+def test_hybrid_64_layer_q4_prefill_16():
+    """The prompt pass the benchmark times: 64-layer Q4_0 hybrid slice, 512
+    prior KV rows, 16 fp16 inputs in one slice_prefill; every token's fp32
+    residual stream against 16 plain steps of the oracle, then one decode."""
+    sh = synth.HYBRID_5120
+    s, orc, _, _ = make_pair(sh, synth.Q4_0, 0, 64, workload=synth.WL_SLICE, prefill=512, max_seq=1024,
+                             max_verify=16, io_fp32=False, threads=16)
+    H = inputs(sh, 17, workload=synth.WL_SLICE, io_fp32=False, step0=200)
+    s.prefill(_t(H[:16]))
+    out = s.get_hidden(16).cpu().numpy()
+    for t in range(16):
+        assert rel_err(out[t], orc.decode(H[t], raw=True)) <= TOL, t
+    assert s.position == 528
+    s.decode(_t(H[16]))
+    assert rel_err(s.get_hidden().cpu().numpy()[0], orc.decode(H[16], raw=True)) <= TOL
