@@ -294,35 +294,55 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
 // One workgroup per (token, query head, 64 dimensions): merge the chunks,
 // normalise, apply the gate and quantise the two 32-dim blocks.  Lane c loads
 // chunk c's max and sum (several rounds beyond 64 chunks), the weights
-// exp(m_c - M) go through LDS, and every lane then folds its dimension.
+// exp(m_c - M) go through LDS, and every lane then folds its dimension.  The
+// gate input, the first 64 chunks' statistics and the first 32 chunks' values
+// are all requested before the statistics are used, so a context of up to 1024
+// rows costs one memory round trip after the position is read.
 __global__ __launch_bounds__(64) void k_attn_combine(AttnParams p) {
+  constexpr int VPRE = 32;   // chunks whose values are requested with the statistics
   __shared__ float wsh[2048];
   const int ndg = p.hd / 64;
   const int t = blockIdx.x / (p.q_heads * ndg);
   const int h = (blockIdx.x / ndg) % p.q_heads;
   const int lane = threadIdx.x;
   const int d = (blockIdx.x % ndg) * 64 + lane;
+  // the gate input does not depend on the position: request it first
+  const float gz = p.off_g >= 0 ? p.y[(size_t)t * p.y_stride + p.off_g + h * p.hd + d] : 0.0f;
   const int P = p.ctrl->pos + t;
   const int nc = P / ATT_CHUNK + 1;
   const int stride = p.hd + 2;
   const float* base = p.part + ((size_t)t * p.q_heads + h) * p.nchunk * stride;
-  float M = -INFINITY;
-  for (int c = lane; c < nc; c += 64) M = fmaxf(M, base[(size_t)c * stride]);
+  // one round of requests: the first 64 chunks' max and sum (lane c) and the
+  // first VPRE chunks' values of dimension d
+  float m0 = -INFINITY, l0 = 0.0f;
+  if (lane < nc) {
+    m0 = base[(size_t)lane * stride];
+    l0 = base[(size_t)lane * stride + 1];
+  }
+  float v0[VPRE];
+#pragma unroll
+  for (int u = 0; u < VPRE; ++u) v0[u] = u < nc ? base[(size_t)u * stride + 2 + d] : 0.0f;
+  float M = m0;
+  for (int c = lane + 64; c < nc; c += 64) M = fmaxf(M, base[(size_t)c * stride]);
   M = wave_max(M);
   float L = 0.0f;
   for (int c0 = 0; c0 < nc; c0 += 64) {
     const int c = c0 + lane;
     float w = 0.0f, l = 0.0f;
     if (c < nc) {
-      w = __expf(base[(size_t)c * stride] - M);
-      l = base[(size_t)c * stride + 1];
+      w = __expf((c0 == 0 ? m0 : base[(size_t)c * stride]) - M);
+      l = c0 == 0 ? l0 : base[(size_t)c * stride + 1];
     }
     L += wave_sum(l * w);
     if (c < nc && c < 2048) wsh[c] = w;
   }
   __syncthreads();
+  // the weighted values, added in chunk order
   float o = 0.0f;
-  for (int c0 = 0; c0 < nc; c0 += 8) {
+#pragma unroll
+  for (int u = 0; u < VPRE; ++u)
+    if (u < nc) o = __builtin_fmaf(v0[u], wsh[u], o);
+  for (int c0 = VPRE; c0 < nc; c0 += 8) {
     // eight loads in flight, then the adds in chunk order
     float v[8];
 #pragma unroll
@@ -337,7 +357,7 @@ __global__ __launch_bounds__(64) void k_attn_combine(AttnParams p) {
     }
   }
   o = o / L;
-  if (p.off_g >= 0) o = o * sigmoidf_(p.y[(size_t)t * p.y_stride + p.off_g + h * p.hd + d]);
+  if (p.off_g >= 0) o = o * sigmoidf_(gz);
   const int nu = p.q_heads * p.hd;
   if (p.u_out) p.u_out[(size_t)t * nu + h * p.hd + d] = o;
   const int blk = (h * p.hd + d) / QK;
