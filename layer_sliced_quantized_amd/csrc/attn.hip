@@ -250,9 +250,9 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
         sc = __builtin_fmaf(kf[i][6], qb.z, sc);
         sc = __builtin_fmaf(kf[i][7], qb.w, sc);
       }
-      sc += __shfl_xor(sc, 1, 64);
-      sc += __shfl_xor(sc, 2, 64);
-      sc += __shfl_xor(sc, 4, 64);
+      sc += xor_lane<1>(sc);
+      sc += xor_lane<2>(sc);
+      sc += xor_lane<4>(sc);
       if (part == 0) pl[t][h][rr] = rr < nvalid ? sc : -INFINITY;
     }
   }

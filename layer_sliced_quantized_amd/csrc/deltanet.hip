@@ -25,20 +25,11 @@ namespace slq {
 
 // Sum over the eight lanes l, l ^ 8, ..., l ^ 56 that hold the parts of one
 // row, with the additions in the order x + x[l^8], then + [l^16], then
-// + [l^32], so every lane gets the same bits.  The exchanges stay in the
-// vector ALU (a DPP rotate by 8 within 16-lane rows is the xor 8 partner, and
-// gfx950's permlane16/32 swaps give the xor 16 and xor 32 partners), with no
-// LDS round trip.
+// + [l^32], so every lane gets the same bits.
 __device__ __forceinline__ float row_sum8(float v) {
-  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128 /* row_ror:8 */, 0xf, 0xf, false));
-  {
-    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v += __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
-  }
-  {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-    v += __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
-  }
+  v += xor_lane<8>(v);
+  v += xor_lane<16>(v);
+  v += xor_lane<32>(v);
   return v;
 }
 

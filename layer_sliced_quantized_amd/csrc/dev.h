@@ -6,22 +6,60 @@ namespace slq {
 
 __device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane(threadIdx.x >> 6); }
 
+// Lane l ^ M's value, exchanged in the vector ALU (no LDS round trip): DPP
+// quad permutes for M = 1 and 2; for M = 4 the row shifts by 4 (left where bit
+// 2 of the lane is clear, right where it is set); a rotate by 8 within 16-lane
+// rows for M = 8; gfx950's permlane16 / permlane32 swaps for M = 16 and 32.
+template <int M>
+__device__ __forceinline__ float xor_lane(float v) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "xor partner");
+  const int x = __float_as_int(v);
+  if constexpr (M == 1) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0xB1 /* quad_perm 1,0,3,2 */, 0xf, 0xf, false));
+  if constexpr (M == 2) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x4E /* quad_perm 2,3,0,1 */, 0xf, 0xf, false));
+  if constexpr (M == 4) {
+    const int up = __builtin_amdgcn_update_dpp(0, x, 0x104 /* row_shl:4 */, 0xf, 0xf, false);
+    const int dn = __builtin_amdgcn_update_dpp(0, x, 0x114 /* row_shr:4 */, 0xf, 0xf, false);
+    return __int_as_float((threadIdx.x & 4) ? dn : up);
+  }
+  if constexpr (M == 8) return __int_as_float(__builtin_amdgcn_update_dpp(0, x, 0x128 /* row_ror:8 */, 0xf, 0xf, false));
+  if constexpr (M == 16) {
+    const auto r = __builtin_amdgcn_permlane16_swap((unsigned)x, (unsigned)x, false, false);
+    return __uint_as_float((threadIdx.x & 16) ? r[0] : r[1]);
+  }
+  if constexpr (M == 32) {
+    const auto r = __builtin_amdgcn_permlane32_swap((unsigned)x, (unsigned)x, false, false);
+    return __uint_as_float((threadIdx.x & 32) ? r[0] : r[1]);
+  }
+  return v;
+}
+
 // Butterfly reductions: every lane ends with the same value, and the value does
 // not depend on the lane (each level adds commutative pairs).
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, 64);
+  v += xor_lane<32>(v);
+  v += xor_lane<16>(v);
+  v += xor_lane<8>(v);
+  v += xor_lane<4>(v);
+  v += xor_lane<2>(v);
+  v += xor_lane<1>(v);
   return v;
 }
 __device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  v = fmaxf(v, xor_lane<32>(v));
+  v = fmaxf(v, xor_lane<16>(v));
+  v = fmaxf(v, xor_lane<8>(v));
+  v = fmaxf(v, xor_lane<4>(v));
+  v = fmaxf(v, xor_lane<2>(v));
+  v = fmaxf(v, xor_lane<1>(v));
   return v;
 }
 // over each 32-lane half separately
 __device__ __forceinline__ float half_max(float v) {
-#pragma unroll
-  for (int m = 16; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, 64));
+  v = fmaxf(v, xor_lane<16>(v));
+  v = fmaxf(v, xor_lane<8>(v));
+  v = fmaxf(v, xor_lane<4>(v));
+  v = fmaxf(v, xor_lane<2>(v));
+  v = fmaxf(v, xor_lane<1>(v));
   return v;
 }
 

@@ -383,7 +383,7 @@ __device__ __forceinline__ void gemm_epi(const Packed& W, const GemvOut& out, in
   } else if constexpr (EPI == EPI_SWIGLU) {
     // lanes 0..31: gate rows, lanes 32..63: the matching up rows
     const float v = a * pre;
-    const float up = __shfl(v, (lane + 32) & 63, 64);
+    const float up = xor_lane<32>(v);   // row lane ^ 32
     const float m = (v / (1.0f + expf(-v))) * up;
     if (out.y && lane < 32) out.y[(size_t)j * out.y_tstride + rg * 32 + lane] = m;
     put_digits(out.next, out.next_qt, j, rg, m, lane < 32);
