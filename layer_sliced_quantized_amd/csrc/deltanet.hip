@@ -64,6 +64,30 @@ __global__ __launch_bounds__(256) void k_deltanet(DnParams p, int T) {
   const int part = lane >> 3, r = lane & 7;
   const int ii = wave * 8 + r;          // row within the workgroup's 32
   const int i = ib * 32 + ii;
+  const bool one = T == 1;
+  // Vector inputs first (q, k of tokens wave + 4m, lanes holding entries lane
+  // and lane + 64; with one token also this lane's v and z): none of them
+  // depends on the state slot, so their latency overlaps the read of the slot
+  // index below.  (The gate inputs are uniform, so they come through scalar
+  // loads; requested here they would hold up the slot index, so they follow
+  // the state loads.)
+  float q0[4], q1[4], k0[4], k1[4];
+#pragma unroll
+  for (int m = 0; m < 4; ++m) {
+    const int t = wave + 4 * m;
+    q0[m] = q1[m] = k0[m] = k1[m] = 0.0f;
+    if (t < T) {
+      const float* y = p.y + (size_t)t * p.y_stride;
+      if (lane < DK) { q0[m] = y[p.off_q + h * DK + lane]; k0[m] = y[p.off_k + h * DK + lane]; }
+      if (lane + 64 < DK) { q1[m] = y[p.off_q + h * DK + lane + 64]; k1[m] = y[p.off_k + h * DK + lane + 64]; }
+    }
+  }
+  float v1 = 0.0f, z1 = 0.0f;
+  if (one) {
+    v1 = p.y[p.off_v + h * p.dv + i];
+    z1 = p.y[p.off_z + h * p.dv + i];
+  }
+
   const int cur = p.ctrl->cur;
   const size_t hs = (size_t)DK * p.dv;
   const float* S_in = p.state + ((size_t)cur * p.heads + h) * hs;
@@ -75,39 +99,22 @@ __global__ __launch_bounds__(256) void k_deltanet(DnParams p, int T) {
 #pragma unroll
   for (int jj = 0; jj < DKP; ++jj) S[jj] = S_in[sbase + (size_t)jj * 64];
 
-  // q, k of head h for tokens wave + 4m: lanes hold entries lane and lane + 64
-  {
-    float q0[4], q1[4], k0[4], k1[4];
+  // normalised q, k into LDS
 #pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int t = wave + 4 * m;
-      q0[m] = q1[m] = k0[m] = k1[m] = 0.0f;
-      if (t < T) {
-        const float* y = p.y + (size_t)t * p.y_stride;
-        if (lane < DK) { q0[m] = y[p.off_q + h * DK + lane]; k0[m] = y[p.off_k + h * DK + lane]; }
-        if (lane + 64 < DK) { q1[m] = y[p.off_q + h * DK + lane + 64]; k1[m] = y[p.off_k + h * DK + lane + 64]; }
-      }
-    }
-#pragma unroll
-    for (int m = 0; m < 4; ++m) {
-      const int t = wave + 4 * m;
-      if (t < T) {
-        const float sq = wave_sum(q0[m] * q0[m] + q1[m] * q1[m]), sk = wave_sum(k0[m] * k0[m] + k1[m] * k1[m]);
-        const float rq = 1.0f / sqrtf(sq + 1e-6f), rk = 1.0f / sqrtf(sk + 1e-6f);
-        if (lane < DK) { qs[t][lane] = q0[m] * rq; ksh[t][lane] = k0[m] * rk; }
-        if (lane + 64 < DK) { qs[t][lane + 64] = q1[m] * rq; ksh[t][lane + 64] = k1[m] * rk; }
-      }
+  for (int m = 0; m < 4; ++m) {
+    const int t = wave + 4 * m;
+    if (t < T) {
+      const float sq = wave_sum(q0[m] * q0[m] + q1[m] * q1[m]), sk = wave_sum(k0[m] * k0[m] + k1[m] * k1[m]);
+      const float rq = 1.0f / sqrtf(sq + 1e-6f), rk = 1.0f / sqrtf(sk + 1e-6f);
+      if (lane < DK) { qs[t][lane] = q0[m] * rq; ksh[t][lane] = k0[m] * rk; }
+      if (lane + 64 < DK) { qs[t][lane + 64] = q1[m] * rq; ksh[t][lane + 64] = k1[m] * rk; }
     }
   }
-  // v, z, decay and gate: with one token every lane takes its own from
-  // global memory (no LDS hop on the decode path); with several, v and z of
-  // rows 32 ib + (tid % 32) for tokens tid / 32 and tid / 32 + 8, and the
-  // gates of token tid, go to LDS
-  const bool one = T == 1;
-  float v1 = 0.0f, z1 = 0.0f, a1 = 0.0f, b1 = 0.0f;
+  // decay and gate: with one token every lane keeps its own (no LDS hop on
+  // the decode path); with several, v and z of rows 32 ib + (tid % 32) for
+  // tokens tid / 32 and tid / 32 + 8, and the gates of token tid, go to LDS
+  float a1 = 0.0f, b1 = 0.0f;
   if (one) {
-    v1 = p.y[p.off_v + h * p.dv + i];
-    z1 = p.y[p.off_z + h * p.dv + i];
     a1 = sigmoidf_(p.a_scale * p.y[p.off_a + h] + p.a_bias);
     b1 = sigmoidf_(p.b_scale * p.y[p.off_b + h]);
   } else {
