@@ -206,14 +206,17 @@ int slice_run_gemv_op(slice_t *s, int op_kind, void *stream);
 int slice_verify(slice_t *s, int k, const void *hid_in_dev, void *hid_out_dev, void *stream);
 
 /* Prompt ingestion of k inputs (1..max_verify) at positions p .. p+k-1:
- * hid_in_dev [k][H] -> hid_out_dev [k][H], then p <- p + k (no commit).  The
- * result is that of k slice_decode calls up to floating-point rounding, not
- * bit for bit: the DeltaNet layers take all k tokens at once in the chunked
- * form of the recurrence and keep only the final state (the pages name the
- * serial recurrence as what makes prefill slow; SwarmLLM README, bench
- * paragraph).  For a bit-exact pass use slice_verify + slice_commit(k).
- * Errors: SLICE_ESTATE while a verify is pending, SLICE_ERANGE for k or
- * positions out of range; nothing is enqueued then.  */
+ * hid_in_dev [k][H] -> hid_out_dev [k][H] (caller-owned device buffers in the
+ * boundary format), then p <- p + k (no commit).  The result is that of k
+ * slice_decode calls up to floating-point rounding, not bit for bit: the
+ * DeltaNet layers take all k tokens at once in the chunked form of the
+ * recurrence and keep only the final state (the pages name the serial
+ * recurrence as what makes prefill slow; SwarmLLM README, bench paragraph),
+ * and the products use launch shapes of their own, so their sums run in
+ * another order.  For a bit-exact pass use slice_verify + slice_commit(k).
+ * Errors: SLICE_EINVAL for a null argument, SLICE_ESTATE while a verify is
+ * pending, SLICE_ERANGE for k or positions out of range; nothing is enqueued
+ * then.  */
 int slice_prefill(slice_t *s, int k, const void *hid_in_dev, void *hid_out_dev, void *stream);
 
 /* Accept the first `accepted` (0..k) tokens of the pending verify: the state
