@@ -118,7 +118,11 @@ template <int GRP, int HD>   // GRP: query heads per workgroup
 __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   constexpr int C = ATT_CHUNK;
   constexpr int NC = HD / 64;   // entries per lane of a head vector; 8-dim pieces per eighth of the head
-  __shared__ __attribute__((aligned(16))) float qsh[MAX_T][GRP][HD];
+  // prepared queries; every 32 floats of a row are followed by 4 of padding,
+  // so the eight key parts of a score step (32 floats apart) read 16-byte
+  // pieces in eight different bank groups instead of two
+  constexpr int QW = HD + HD / 8;
+  __shared__ __attribute__((aligned(16))) float qsh[MAX_T][GRP][QW];
   __shared__ __attribute__((aligned(16))) float pl[MAX_T][GRP][C];
   __shared__ float rbuf[4][HD];
   __shared__ float ml[MAX_T][GRP][2];
@@ -211,7 +215,10 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
         const int t = tq + q / GRP, h = q % GRP;
         head_prep<NC>(x[m], p, p.q_norm, p0 + t, rb);
 #pragma unroll
-        for (int e = 0; e < NC; ++e) qsh[t][h][lane + 64 * e] = x[m][e] * (1.0f / sqrtf((float)HD));
+        for (int e = 0; e < NC; ++e) {
+          const int d = lane + 64 * e;
+          qsh[t][h][d + (d >> 5) * 4] = x[m][e] * (1.0f / sqrtf((float)HD));
+        }
       }
     }
   }
@@ -239,8 +246,9 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
 #pragma unroll
       for (int i = 0; i < NC; ++i) {
         const int dc = part * NC + i;
-        const float4 qa = *reinterpret_cast<const float4*>(&qsh[t][h][dc * 8]);
-        const float4 qb = *reinterpret_cast<const float4*>(&qsh[t][h][dc * 8 + 4]);
+        const int q8 = dc * 8 + (dc >> 2) * 4;   // dims dc*8 .. dc*8+7 lie in one padded group of 32
+        const float4 qa = *reinterpret_cast<const float4*>(&qsh[t][h][q8]);
+        const float4 qb = *reinterpret_cast<const float4*>(&qsh[t][h][q8 + 4]);
         sc = __builtin_fmaf(kf[i][0], qa.x, sc);
         sc = __builtin_fmaf(kf[i][1], qa.y, sc);
         sc = __builtin_fmaf(kf[i][2], qa.z, sc);
