@@ -121,3 +121,25 @@ def test_malformed_files_are_rejected(tmp_path):
     bad.write_bytes(good[:-10])
     with pytest.raises(gguf.GGUFError):
         gguf.GGUFFile(str(bad))
+
+
+def test_metadata_of_every_value_type_round_trips(tmp_path):
+    # one key per GGUF value type (0..12 except the array marker), plus arrays
+    # of strings and of floats, and an empty array
+    meta = {
+        "u8": (200, gguf.V_U8), "i8": (-100, gguf.V_I8), "u16": (60000, gguf.V_U16), "i16": (-30000, gguf.V_I16),
+        "u32": (4000000000, gguf.V_U32), "i32": (-2000000000, gguf.V_I32), "f32": (1.5, gguf.V_F32),
+        "bool": (True, gguf.V_BOOL), "str": ("Grüße", gguf.V_STR), "u64": (2 ** 63 + 5, gguf.V_U64),
+        "i64": (-(2 ** 62), gguf.V_I64), "f64": (0.1, gguf.V_F64),
+        "names": (["a", "bc", ""], gguf.V_STR), "scales": ([0.5, -2.0, 3.25], gguf.V_F32), "none": ([], gguf.V_I32),
+    }
+    path = tmp_path / "meta.gguf"
+    gguf.write_gguf(str(path), meta, {})
+    g = gguf.GGUFFile(str(path))
+    assert g.tensors == {}
+    for k, (v, _) in meta.items():
+        got = g.metadata[k]
+        if isinstance(v, list):
+            assert list(got) == v, k
+        else:
+            assert got == v, k
