@@ -203,6 +203,44 @@ def run_prefill_chunked(s, H, chunks, k=16):
             "tok_s": round(chunks * k / sec, 1)}
 
 
+def attention_sweep(seed, steps=32):
+    """Decode attention (the split and combine kernels of one step) of the
+    hidden-5120 attention layer over 512, 4096 and 32768 prior KV rows: the
+    median over `steps` eager steps of the op's time between HIP events, and the
+    K and V bytes a step reads (4 KB per cached row: 4 KV heads x 256 x fp16,
+    twice)."""
+    import dataclasses
+    import torch
+    import synth
+    import layer_sliced_quantized_amd as slq
+    shape = dataclasses.replace(synth.HYBRID_5120, name="attention_layer_5120", ffn=0)
+    tensors = {3: synth.layer_tensors(shape, synth.Q4_0, seed, synth.WL_ATTENTION, 3)}
+    res = []
+    for L in (512, 4096, 32768):
+        max_seq = (L + steps + 8 + 63) // 64 * 64
+        s = slq.Slice(slq.make_config(shape, synth.Q4_0, 3, 4, max_seq=max_seq, max_verify=4))
+        s.load_numpy(tensors)
+        K, V = synth.kv_prefill(seed, synth.WL_ATTENTION, 3, shape.kv_heads, L, shape.head_dim)
+        s.set_kv(3, torch.from_numpy(K), torch.from_numpy(V))
+        s.reset(L)
+        H = torch.from_numpy(synth.hidden_inputs(seed, synth.WL_ATTENTION, steps + 4, shape.hidden, step0=L)).cuda()
+        out = torch.empty(shape.hidden, dtype=torch.float16, device="cuda")
+        ts = []
+        for i in range(steps + 4):
+            _, ops = s.decode_profiled(H[i], out)
+            if i >= 4:
+                ts.append(sum(ms for name, ms in ops if name == "attention"))
+        us = float(np.median(ts)) * 1e3
+        rows = L + 4 + steps // 2 + 1          # rows attended at the median step
+        kv_bytes = rows * shape.kv_heads * shape.head_dim * 2 * 2
+        res.append({"kv_rows": L, "attention_us": round(us, 2), "kv_MB_read": round(kv_bytes / 1e6, 2),
+                    "GB_s": round(kv_bytes / (us * 1e-6) / 1e9, 1)})
+        log(f"attention {res[-1]}")
+        del s, K, V
+        torch.cuda.empty_cache()
+    return res
+
+
 def gemv_sweep(seed, reps):
     import torch
     import synth
@@ -290,6 +328,7 @@ def main() -> int:
     ap.add_argument("--sweep-reps", type=int, default=50)
     ap.add_argument("--no-q8", action="store_true")
     ap.add_argument("--no-sweep", action="store_true")
+    ap.add_argument("--no-attn-sweep", action="store_true", help="skip the decode-attention timing at 512/4096/32768 KV rows")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--copy-calib", action="store_true",
@@ -367,6 +406,9 @@ def main() -> int:
     torch.cuda.empty_cache()
 
     extra = {}
+    # ---- decode attention at three KV lengths
+    if not args.no_attn_sweep:
+        extra["attention_decode"] = attention_sweep(args.seed)
     # ---- standalone GEMV sweep
     if not args.no_sweep:
         extra["gemv_sweep"] = gemv_sweep(args.seed, args.sweep_reps)

@@ -299,70 +299,118 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   }
 }
 
-// One workgroup per (token, query head, 64 dimensions): merge the chunks,
-// normalise, apply the gate and quantise the two 32-dim blocks.  Lane c loads
-// chunk c's max and sum (several rounds beyond 64 chunks), the weights
-// exp(m_c - M) go through LDS, and every lane then folds its dimension.  The
-// gate input, the first 64 chunks' statistics and the first 32 chunks' values
-// are all requested before the statistics are used, so a context of up to 1024
-// rows costs one memory round trip after the position is read.
-__global__ __launch_bounds__(64) void k_attn_combine(AttnParams p) {
+// One workgroup of CW waves per (token, query head, 64 dimensions): merge the
+// chunks, normalise, apply the gate and quantise the two 32-dim blocks.
+//
+// Up to 64 chunks (2048 rows) wave 0 does it alone: lane c loads chunk c's max
+// and sum, the weights exp(m_c - M) go through LDS, and every lane then folds
+// its dimension over the chunks in order.  The gate input, the statistics and
+// the first 32 chunks' values are all requested before the statistics are
+// used, so this costs one memory round trip after the position is read.
+//
+// Beyond 64 chunks wave w of the NW = blockDim / 64 waves takes the
+// contiguous chunk range [nc w / NW, nc (w+1) / NW): the waves' maxima, their
+// sums of weighted chunk sums and their partial outputs meet in LDS in wave
+// order, and wave 0 finishes.  32 value loads per wave are in flight at a
+// time.  The launch takes CW waves when the cache has more than 64 chunks,
+// else one (the long branch is then never taken), so a slice's decode and
+// verify steps always sum in the same order.
+constexpr int CW = 8;
+__global__ __launch_bounds__(64 * CW) void k_attn_combine(AttnParams p) {
   constexpr int VPRE = 32;   // chunks whose values are requested with the statistics
   __shared__ float wsh[2048];
+  __shared__ float red[CW][64];
+  __shared__ float mred[CW], lred[CW];
   const int ndg = p.hd / 64;
   const int t = blockIdx.x / (p.q_heads * ndg);
   const int h = (blockIdx.x / ndg) % p.q_heads;
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int d = (blockIdx.x % ndg) * 64 + lane;
   // the gate input does not depend on the position: request it first
-  const float gz = p.off_g >= 0 ? p.y[(size_t)t * p.y_stride + p.off_g + h * p.hd + d] : 0.0f;
+  const float gz = p.off_g >= 0 && w == 0 ? p.y[(size_t)t * p.y_stride + p.off_g + h * p.hd + d] : 0.0f;
   const int P = p.ctrl->pos + t;
   const int nc = P / ATT_CHUNK + 1;
   const int stride = p.hd + 2;
   const float* base = p.part + ((size_t)t * p.q_heads + h) * p.nchunk * stride;
-  // one round of requests: the first 64 chunks' max and sum (lane c) and the
-  // first VPRE chunks' values of dimension d
-  float m0 = -INFINITY, l0 = 0.0f;
-  if (lane < nc) {
-    m0 = base[(size_t)lane * stride];
-    l0 = base[(size_t)lane * stride + 1];
-  }
-  float v0[VPRE];
+  float o = 0.0f, L = 0.0f;
+  if (nc <= 64) {
+    float M = -INFINITY;
+    float v0[VPRE];
+    if (w == 0) {
+      // one round of requests: every chunk's max and sum (lane c) and the
+      // first VPRE chunks' values of dimension d
+      float m0 = -INFINITY, l0 = 0.0f;
+      if (lane < nc) {
+        m0 = base[(size_t)lane * stride];
+        l0 = base[(size_t)lane * stride + 1];
+      }
 #pragma unroll
-  for (int u = 0; u < VPRE; ++u) v0[u] = u < nc ? base[(size_t)u * stride + 2 + d] : 0.0f;
-  float M = m0;
-  for (int c = lane + 64; c < nc; c += 64) M = fmaxf(M, base[(size_t)c * stride]);
-  M = wave_max(M);
-  float L = 0.0f;
-  for (int c0 = 0; c0 < nc; c0 += 64) {
-    const int c = c0 + lane;
-    float w = 0.0f, l = 0.0f;
-    if (c < nc) {
-      w = __expf((c0 == 0 ? m0 : base[(size_t)c * stride]) - M);
-      l = c0 == 0 ? l0 : base[(size_t)c * stride + 1];
+      for (int u = 0; u < VPRE; ++u) v0[u] = u < nc ? base[(size_t)u * stride + 2 + d] : 0.0f;
+      M = wave_max(m0);
+      const float wt = lane < nc ? __expf(m0 - M) : 0.0f;
+      L = wave_sum((lane < nc ? l0 : 0.0f) * wt);
+      if (lane < nc) wsh[lane] = wt;
     }
-    L += wave_sum(l * w);
-    if (c < nc && c < 2048) wsh[c] = w;
-  }
-  __syncthreads();
-  // the weighted values, added in chunk order
-  float o = 0.0f;
+    __syncthreads();
+    if (w != 0) return;
+    // the weighted values, added in chunk order
 #pragma unroll
-  for (int u = 0; u < VPRE; ++u)
-    if (u < nc) o = __builtin_fmaf(v0[u], wsh[u], o);
-  for (int c0 = VPRE; c0 < nc; c0 += 8) {
-    // eight loads in flight, then the adds in chunk order
-    float v[8];
+    for (int u = 0; u < VPRE; ++u)
+      if (u < nc) o = __builtin_fmaf(v0[u], wsh[u], o);
+    for (int c0 = VPRE; c0 < nc; c0 += 8) {
+      float v[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) v[u] = c0 + u < nc ? base[(size_t)(c0 + u) * stride + 2 + d] : 0.0f;
+      for (int u = 0; u < 8; ++u) v[u] = c0 + u < nc ? base[(size_t)(c0 + u) * stride + 2 + d] : 0.0f;
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int c = c0 + u;
-      if (c < nc) {
-        const float w = c < 2048 ? wsh[c] : __expf(base[(size_t)c * stride] - M);
-        o = __builtin_fmaf(v[u], w, o);
+      for (int u = 0; u < 8; ++u)
+        if (c0 + u < nc) o = __builtin_fmaf(v[u], wsh[c0 + u], o);
+    }
+  } else {
+    const int c_lo = nc * w / nw, c_hi = nc * (w + 1) / nw;
+    float mw = -INFINITY;
+    for (int c = c_lo + lane; c < c_hi; c += 64) mw = fmaxf(mw, base[(size_t)c * stride]);
+    mw = wave_max(mw);
+    if (lane == 0) mred[w] = mw;
+    __syncthreads();
+    float M = mred[0];
+#pragma unroll
+    for (int x = 1; x < CW; ++x)
+      if (x < nw) M = fmaxf(M, mred[x]);
+    float lw = 0.0f;
+    for (int c0 = c_lo; c0 < c_hi; c0 += 64) {
+      const int c = c0 + lane;
+      float wt = 0.0f, l = 0.0f;
+      if (c < c_hi) {
+        wt = __expf(base[(size_t)c * stride] - M);
+        l = base[(size_t)c * stride + 1];
+      }
+      lw += wave_sum(l * wt);
+      if (c < c_hi && c < 2048) wsh[c] = wt;
+    }
+    if (lane == 0) lred[w] = lw;
+    __syncthreads();
+    // the wave's weighted values in chunk order
+    for (int c0 = c_lo; c0 < c_hi; c0 += 32) {
+      float v[32];
+#pragma unroll
+      for (int u = 0; u < 32; ++u) v[u] = c0 + u < c_hi ? base[(size_t)(c0 + u) * stride + 2 + d] : 0.0f;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        const int c = c0 + u;
+        if (c < c_hi) o = __builtin_fmaf(v[u], c < 2048 ? wsh[c] : __expf(base[(size_t)c * stride] - M), o);
       }
     }
+    red[w][lane] = o;
+    __syncthreads();
+    if (w != 0) return;
+    L = lred[0];
+    o = red[0][lane];
+#pragma unroll
+    for (int x = 1; x < CW; ++x)
+      if (x < nw) {
+        L += lred[x];
+        o += red[x][lane];
+      }
   }
   o = o / L;
   if (p.off_g >= 0) o = o * sigmoidf_(gz);
@@ -396,7 +444,7 @@ hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {
   }
 #undef SLQ_HD
 #undef SLQ_G
-  k_attn_combine<<<T * p.q_heads * (p.hd / 64), 64, 0, s>>>(p);
+  k_attn_combine<<<T * p.q_heads * (p.hd / 64), p.nchunk > 64 ? 64 * CW : 64, 0, s>>>(p);
   return hipGetLastError();
 }
 
