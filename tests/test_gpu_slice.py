@@ -265,6 +265,22 @@ def test_attention_layer_5120_decode_and_verify(L):
     assert rel_err(V.cpu().numpy()[:, L:], orc.kv[3][1][:, L:L + 17]) <= TOL
 
 
+@pytest.mark.timeout(300)
+def test_attention_short_context_in_long_cache():
+    """A cache of more than 64 chunks launches the eight-wave combine; at 512
+    rows the merge still takes the one-wave branch while the other waves wait
+    at the barrier and leave."""
+    s, orc, _, _ = make_pair(ATT_LAYER, synth.Q4_0, 3, 4, workload=synth.WL_ATTENTION, prefill=512,
+                             max_seq=4160)
+    H = inputs(ATT_LAYER, 17, workload=synth.WL_ATTENTION, step0=512)
+    out0 = s.decode(_t(H[0])).cpu().numpy()
+    assert rel_err(out0, orc.decode(H[0], raw=True)) <= TOL
+    out = s.verify(_t(H[1:])).cpu().numpy()
+    ref = orc.verify(H[1:], raw=True)
+    for t in range(16):
+        assert rel_err(out[t], ref[t]) <= TOL, t
+
+
 # ------------------------------------------------------ the 64-layer slice
 
 @pytest.mark.timeout(900)
