@@ -127,8 +127,14 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   __shared__ float rbuf[4][HD];
   __shared__ float ml[MAX_T][GRP][2];
   const int nsub = p.q_heads / p.kv_heads / GRP;   // query-head groups per KV head
-  const int g = blockIdx.x / (nsub * p.nchunk);
-  const int sub = (blockIdx.x / p.nchunk) % nsub, c = blockIdx.x % p.nchunk;
+  // Workgroups go to the XCDs round robin by index.  The nsub workgroups that
+  // read the same (KV head, chunk) pair take indices 8 apart, i.e. one XCD and
+  // close in time, so the later ones find its keys and values in that XCD's
+  // L2: pairs come in groups of 8, each group once per query-head group.
+  const int pair = ((int)blockIdx.x / (8 * nsub)) * 8 + (int)blockIdx.x % 8;
+  const int sub = ((int)blockIdx.x / 8) % nsub;
+  if (pair >= p.kv_heads * p.nchunk) return;
+  const int g = pair / p.nchunk, c = pair % p.nchunk;
   const int h0 = (g * nsub + sub) * GRP;            // first query head of this workgroup
   const int p0 = p.ctrl->pos;
   const int r0 = c * C;
@@ -429,7 +435,8 @@ hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {
   // the work of a chunk spreads over several workgroups
   const int grp = p.q_heads / p.kv_heads;
   const int hpw = grp % 2 == 0 ? 2 : 1;
-  const unsigned grid = (unsigned)(p.kv_heads * (grp / hpw) * p.nchunk);
+  const int pairs = p.kv_heads * p.nchunk;         // (KV head, chunk) pairs, padded to groups of 8
+  const unsigned grid = (unsigned)(((pairs + 7) / 8) * 8 * (grp / hpw));
 #define SLQ_G(n, hd) case n: k_attn_split<n, hd><<<grid, 256, 0, s>>>(p, T); break;
 #define SLQ_HD(hd)                                          \
   case hd:                                                  \
