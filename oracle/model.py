@@ -15,10 +15,11 @@ What the pages fix, by page and section:
     peer-to-peer ChatGPT", sections "Splitting the workload" and "The runtime:
     legion-stage-runtime").  One token's hidden state at 5,120 x f16 crosses a
     boundary (SwarmLLM README, pipeline diagram and bench paragraph).
-  * Block kinds: Llama-style blocks (RMSNorm, GQA, RoPE, SwiGLU, tied head)
-    and the qwen3_5 hybrid, Gated DeltaNet layers mixed with full-attention
-    layers that have partial RoPE, QK-norm and an output gate (ChatTorrent
-    README, "What it can run").
+  * Block kinds: Llama-style blocks (RMSNorm, GQA, RoPE, SwiGLU, tied head),
+    and the qwen3_5 hybrid, whose linear-attention layers are Gated DeltaNet
+    and whose remaining layers are full attention with RoPE on part of each
+    head, per-head norms of q and k, and a sigmoid gate on the output
+    (ChatTorrent README, "What it can run").
   * Verify: drafts are checked in one batched pass and the recurrent state is
     rolled back exactly; the speculative stream equals the plain one (SwarmLLM
     README, feature list and architecture paragraph).  Here verify(k) is

@@ -1,0 +1,329 @@
+"""Closed-form pins of the oracle's sublayer wiring (CPU only).
+
+The primitives (RMSNorm, RoPE, softmax attention, the DeltaNet update, the
+block decoders) are pinned elsewhere; these tests pin how a layer wires them:
+which projection feeds which input, the attention scale, QK-norm and RoPE of
+the query at the current position, the per-head slicing of the DeltaNet
+projections and the affine maps of its decay, write strength and output gate.
+
+Every weight matrix here is "one-hot": a Q4_0 row is zero except for one code
+(nibble 9 or 7, i.e. +-1 times the row's fp16 scale), so each projection
+output is a known multiple of one entry of the normalised input.  The input
+h is a +-1 pattern, whose RMSNorm is h / sqrt(1 + eps) in closed form.  The
+expected outputs below are written out case by case from the layer
+definitions (ChatTorrent README, "What it can run": Llama-style blocks with
+SwiGLU, the hybrid's gated attention with QK-norm and partial RoPE, Gated
+DeltaNet), not by calling the oracle's layer code.
+
+Each pin is then re-run against deliberately broken copies of the oracle (a
+mistake planted in its source text): swapped gate/up, a dropped attention
+scale, RoPE of q one position off, a dropped q-norm, swapped q/k projections,
+wrong decay / write-strength / gate coefficients, a wrong head slice.  Every
+mutant must fail at least one pin.
+"""
+import inspect
+import math
+import textwrap
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from oracle import model as omodel
+from oracle import qref
+
+# the small hybrid of the other oracle pins: hidden 64, 2 DeltaNet heads of
+# 32, 4 query / 2 KV heads of 32 with 16 rotated dims, SwiGLU 96
+TINY = synth.ModelShape(
+    name="tiny_hybrid", hidden=64, n_layers=4, attn_period=4,
+    dn_heads=2, dn_dk=32, dn_dv=32, q_heads=4, kv_heads=2, head_dim=32, rope_dims=16,
+    rope_theta=1e7, qk_norm=True, attn_gate=True, eps=1e-6, ffn=96, vocab=0)
+EPS = TINY.eps
+S_NORM = 1.0 / math.sqrt(1.0 + EPS)      # RMSNorm of a +-1 vector (weights 1)
+
+
+def sig(z):
+    return 1.0 / (1.0 + math.exp(-z))
+
+
+def onehot_q4(rows: int, cols: int, entries: dict) -> np.ndarray:
+    """Q4_0 blocks of a rows x cols matrix that is zero except
+    W[r, c] = sgn * d for every r -> (c, d, sgn) in entries (d exact in fp16)."""
+    nb = cols // 32
+    blk = np.zeros((rows, nb, 18), np.uint8)
+    blk[:, :, 2:] = 0x88                      # every nibble 8: weight 0
+    for r, (c, d, sgn) in entries.items():
+        b, e = divmod(c, 32)
+        blk[r, b, 0:2] = np.array([d], np.float16).view(np.uint8)
+        byte, nib = 2 + e % 16, 8 + sgn
+        if e < 16:
+            blk[r, b, byte] = (blk[r, b, byte] & 0xF0) | nib
+        else:
+            blk[r, b, byte] = (blk[r, b, byte] & 0x0F) | (nib << 4)
+    return blk.reshape(rows, nb * 18)
+
+
+def test_onehot_blocks_decode_to_the_intended_matrix():
+    ent = {0: (5, 0.5, 1), 3: (17, 1.5, -1), 4: (40, 0.25, 1), 6: (63, 2.0, -1)}
+    W = qref.dequant(synth.Q4_0, onehot_q4(8, 64, ent), 8, 64)
+    ref = np.zeros((8, 64))
+    for r, (c, d, sgn) in ent.items():
+        ref[r, c] = sgn * d
+    np.testing.assert_array_equal(W, ref)
+
+
+def _pm1(seed, n):
+    return np.where(np.random.default_rng(seed).random(n) < 0.5, -1.0, 1.0).astype(np.float32)
+
+
+def _zero_all(T, layer, names):
+    """Set the named matrices of one layer's tensors to zero (scale 0 everywhere)."""
+    shapes = synth.matrix_shapes(TINY, layer)
+    for n in names:
+        T[n] = onehot_q4(*shapes[n], {})
+
+
+def _layer(l):
+    return synth.layer_tensors(TINY, synth.Q4_0, 0, 91, l)
+
+
+# ------------------------------------------------------------------ FFN
+
+def pin_ffn():
+    """Layer 1 (DeltaNet) with a zero mixer, which leaves h unchanged, and a
+    one-hot SwiGLU: m_i = silu(gate_i) * up_i, h += W_down m."""
+    T = _layer(1)
+    _zero_all(T, 1, ["dn_q", "dn_k", "dn_v", "dn_a", "dn_b", "dn_z", "dn_out"])
+    F, H = TINY.ffn, TINY.hidden
+    T["w_gate"] = onehot_q4(F, H, {0: (2, 1.5, 1), 1: (3, 0.5, -1), 7: (9, 2.0, 1)})
+    T["w_up"] = onehot_q4(F, H, {0: (4, 0.25, 1), 1: (5, 2.0, 1), 7: (10, 1.0, -1)})
+    T["w_down"] = onehot_q4(H, F, {0: (0, 1.0, 1), 1: (1, 0.5, 1), 2: (2, 1.0, 1), 9: (7, 0.75, -1)})
+    orc = oracle.SliceOracle(TINY, synth.Q4_0, 1, 2, {1: T}, max_seq=16, io_fp32=True)
+    orc.set_state(1, synth.dn_state0(0, 91, 1, 2, 32, 32))
+    orc.reset(3)
+    h = _pm1(1, H)
+    out = orc.decode(h, raw=True)
+    x = S_NORM * h.astype(np.float64)
+
+    def silu_times(g, u):
+        return g * sig(g) * u
+
+    m0 = silu_times(1.5 * x[2], 0.25 * x[4])
+    m1 = silu_times(-0.5 * x[3], 2.0 * x[5])
+    m7 = silu_times(2.0 * x[9], -1.0 * x[10])
+    exp = h.astype(np.float64).copy()
+    exp[0] += 1.0 * m0
+    exp[1] += 0.5 * m1
+    exp[2] += 1.0 * 0.0        # gate row 2 is zero, so m_2 = silu(0) * 0 = 0
+    exp[9] += -0.75 * m7
+    np.testing.assert_allclose(out, exp, rtol=1e-12, atol=1e-15)
+
+
+def test_ffn_closed_form():
+    pin_ffn()
+
+
+# ------------------------------------------------------------- attention
+
+def pin_attention():
+    """Layer 3 (attention), one prior cache row, decode at position p = 1.
+
+    Query head 0 is one-hot at dimension 0 (q_raw = 0.5 x[5]); QK-norm over
+    its 32 entries makes it qn = q_raw / sqrt(q_raw^2 / 32 + eps); RoPE at
+    p = 1 rotates the pair (0, 8) by 1 rad (frequency theta^0).  The prior key
+    row of KV head 0 holds 1.5 at dimension 0 and 1.0 at dimension 8, so its
+    score is qn (1.5 cos 1 + 1.0 sin 1) / sqrt(32); the new row's key and value
+    are 0 (W_k = W_v = 0), score 0.  Head 0 thus weights the prior value row by
+    sigmoid(s0).  Head 1 (q = 0) weights both rows 1/2; heads 2, 3 read KV head
+    1 likewise.  W_g = 0 gives the gate sigmoid(0) = 1/2; h += W_o u."""
+    T = _layer(3)
+    nq, H, hd = TINY.q_heads * TINY.head_dim, TINY.hidden, TINY.head_dim
+    T["wq"] = onehot_q4(nq, H, {0: (5, 0.5, 1)})
+    _zero_all(T, 3, ["wg", "wk", "wv", "w_gate", "w_up", "w_down"])
+    orc = oracle.SliceOracle(TINY, synth.Q4_0, 3, 4, {3: T}, max_seq=16, io_fp32=True)
+    K = np.zeros((2, 1, hd), np.float16)
+    K[0, 0, 0], K[0, 0, 8] = 1.5, 1.0
+    K[1, 0, 3] = -2.0
+    V = np.random.default_rng(2).standard_normal((2, 1, hd)).astype(np.float16)
+    orc.set_kv(3, K, V)
+    orc.reset(1)
+    h = _pm1(3, H)
+    out = orc.decode(h, raw=True)
+    x = S_NORM * h.astype(np.float64)
+    q_raw = 0.5 * x[5]
+    qn = q_raw / math.sqrt(q_raw * q_raw / hd + EPS)
+    s0 = qn * (1.5 * math.cos(1.0) + 1.0 * math.sin(1.0)) / math.sqrt(hd)
+    w0 = sig(s0)                     # softmax over [s0, 0]
+    V0, V1 = V[0, 0].astype(np.float64), V[1, 0].astype(np.float64)
+    o = np.concatenate([w0 * V0, 0.5 * V0, 0.5 * V1, 0.5 * V1])
+    u = 0.5 * o
+    Wo = qref.dequant(synth.Q4_0, T["wo"], H, nq)
+    np.testing.assert_allclose(out, h.astype(np.float64) + Wo @ u, rtol=1e-10, atol=1e-12)
+    # the new cache row: k = v = 0 after norm and RoPE
+    assert np.all(orc.kv[3][0][:, 1] == 0) and np.all(orc.kv[3][1][:, 1] == 0)
+
+
+def pin_attention_key():
+    """The key side: k of KV head 1 one-hot at dimension 1 (k_raw = -0.75 x[7]),
+    v one-hot at dimension 30.  The cache row written at p = 5 is
+    fp16(RoPE_5(k-norm(k))) and fp16(v): dimension 1 pairs with 9 and turns by
+    5 theta^(-1/8) rad.  Query head 2 (which reads KV head 1) is one-hot at
+    dimension 1 too, so its score against the new row is qn kn / sqrt(32)
+    whatever the angle, and against the 5 zero prior rows 0."""
+    T = _layer(3)
+    nq, nkv, H, hd = TINY.q_heads * TINY.head_dim, TINY.kv_heads * TINY.head_dim, TINY.hidden, TINY.head_dim
+    T["wq"] = onehot_q4(nq, H, {2 * hd + 1: (11, 1.0, 1)})
+    T["wk"] = onehot_q4(nkv, H, {hd + 1: (7, 0.75, -1)})
+    T["wv"] = onehot_q4(nkv, H, {hd + 30: (12, 2.0, 1)})
+    _zero_all(T, 3, ["wg", "w_gate", "w_up", "w_down"])
+    orc = oracle.SliceOracle(TINY, synth.Q4_0, 3, 4, {3: T}, max_seq=16, io_fp32=True)
+    z = np.zeros((2, 5, hd), np.float16)
+    orc.set_kv(3, z, z)
+    orc.reset(5)
+    h = _pm1(4, H)
+    out = orc.decode(h, raw=True)
+    x = S_NORM * h.astype(np.float64)
+    k_raw = -0.75 * x[7]
+    kn = k_raw / math.sqrt(k_raw * k_raw / hd + EPS)
+    ang = 5.0 * 1e7 ** (-2.0 / 16)
+    krow = np.zeros(hd)
+    krow[1], krow[9] = kn * math.cos(ang), kn * math.sin(ang)
+    np.testing.assert_array_equal(orc.kv[3][0][1, 5], krow.astype(np.float16))
+    vrow = np.zeros(hd)
+    vrow[30] = 2.0 * x[12]
+    np.testing.assert_array_equal(orc.kv[3][1][1, 5], vrow.astype(np.float16))
+    assert np.all(orc.kv[3][0][0, 5] == 0)
+    q_raw = 1.0 * x[11]
+    qn = q_raw / math.sqrt(q_raw * q_raw / hd + EPS)
+    # the rotated query: pair (1, 9) of R(5) qn e_1
+    qrot = np.zeros(hd)
+    qrot[1], qrot[9] = qn * math.cos(ang), qn * math.sin(ang)
+    kc = orc.kv[3][0][1, 5].astype(np.float64)
+    s_new = float(qrot @ kc) / math.sqrt(hd)
+    w_new = math.exp(s_new) / (math.exp(s_new) + 5.0)
+    vc = orc.kv[3][1][1, 5].astype(np.float64)
+    o = np.zeros((4, hd))
+    o[2] = w_new * vc
+    o[3] = vc / 6.0                 # head 3: q = 0, six equal scores
+    u = 0.5 * o.reshape(-1)
+    Wo = qref.dequant(synth.Q4_0, T["wo"], H, nq)
+    np.testing.assert_allclose(out, h.astype(np.float64) + Wo @ u, rtol=1e-10, atol=1e-12)
+
+
+def test_attention_query_side_closed_form():
+    pin_attention()
+
+
+def test_attention_key_side_closed_form():
+    pin_attention_key()
+
+
+# -------------------------------------------------------------- DeltaNet
+
+def pin_deltanet():
+    """Layer 0 (DeltaNet), two heads of 32.
+
+    Head 0: q and k one-hot at the same key dimension 3, v non-zero at value
+    dimensions 5 and 6, decay input a = 2 x[30], write strength b = 1.5 x[31].
+    Head 1: q at key dimension 10, k at 20, v at dimension 2, a = 0, b = x[32].
+    With kh = kappa e_j (kappa = k / sqrt(k^2 + 1e-6)) the update
+    S' = alpha S (I - beta kh kh^T) + beta v kh^T scales every column by alpha
+    and replaces column j by alpha (1 - beta kappa^2) S[:, j] + beta kappa v;
+    o = rho S'[:, j_q].  alpha = sigmoid(0.125 a + 2), beta = sigmoid(0.25 b);
+    the output is gated by sigmoid(0.25 z) (z one-hot at two rows, else 0)."""
+    T = _layer(0)
+    H, nk = TINY.hidden, TINY.dn_heads * TINY.dn_dk
+    T["dn_q"] = onehot_q4(nk, H, {3: (7, 0.25, 1), 32 + 10: (11, 0.5, -1)})
+    T["dn_k"] = onehot_q4(nk, H, {3: (13, 0.5, 1), 32 + 20: (17, 0.75, 1)})
+    T["dn_v"] = onehot_q4(nk, H, {5: (21, 1.0, 1), 6: (22, 0.5, -1), 32 + 2: (23, 0.25, 1)})
+    T["dn_a"] = onehot_q4(2, H, {0: (30, 2.0, 1)})
+    T["dn_b"] = onehot_q4(2, H, {0: (31, 1.5, 1), 1: (32, 1.0, -1)})
+    T["dn_z"] = onehot_q4(nk, H, {3: (33, 2.0, 1), 32 + 10: (34, 1.0, 1)})
+    _zero_all(T, 0, ["w_gate", "w_up", "w_down"])
+    orc = oracle.SliceOracle(TINY, synth.Q4_0, 0, 1, {0: T}, max_seq=16, io_fp32=True)
+    S0 = synth.dn_state0(0, 91, 0, 2, 32, 32) * 10
+    orc.set_state(0, S0)
+    orc.reset(4)
+    h = _pm1(5, H)
+    out = orc.decode(h, raw=True)
+    x = S_NORM * h.astype(np.float64)
+    S = S0.astype(np.float64)
+
+    def unit(a):
+        return a / math.sqrt(a * a + 1e-6)
+
+    alpha = [sig(0.125 * (2.0 * x[30]) + 2.0), sig(2.0)]
+    beta = [sig(0.25 * (1.5 * x[31])), sig(0.25 * (-1.0 * x[32]))]
+    kappa = [unit(0.5 * x[13]), unit(0.75 * x[17])]
+    rho = [unit(0.25 * x[7]), unit(-0.5 * x[11])]
+    jk, jq = [3, 20], [3, 10]
+    v = np.zeros((2, 32))
+    v[0, 5], v[0, 6], v[1, 2] = 1.0 * x[21], -0.5 * x[22], 0.25 * x[23]
+    Sn = np.empty_like(S)
+    o = np.empty((2, 32))
+    for hh in range(2):
+        Sn[hh] = alpha[hh] * S[hh]
+        Sn[hh][:, jk[hh]] = alpha[hh] * (1 - beta[hh] * kappa[hh] ** 2) * S[hh][:, jk[hh]] \
+            + beta[hh] * kappa[hh] * v[hh]
+        o[hh] = rho[hh] * Sn[hh][:, jq[hh]]
+    z = np.zeros(64)
+    z[3], z[32 + 10] = 2.0 * x[33], 1.0 * x[34]
+    u = o.reshape(-1) * np.array([sig(0.25 * zz) for zz in z])
+    Wout = qref.dequant(synth.Q4_0, T["dn_out"], H, nk)
+    np.testing.assert_allclose(orc.dn[0], Sn.astype(np.float32), rtol=1e-6, atol=1e-9)
+    np.testing.assert_allclose(out, h.astype(np.float64) + Wout @ u, rtol=1e-10, atol=1e-12)
+
+
+def test_deltanet_wiring_closed_form():
+    pin_deltanet()
+
+
+# ------------------------------------------------------- planted mistakes
+
+# (method of SliceOracle, text in its source, replacement): each is a
+# plausible wiring mistake that one of the pins above must catch.
+MUTANTS = {
+    "ffn_gate_up_swapped": ("ffn", 'silu(self._mv(l, "w_gate", x)) * self._mv(l, "w_up", x)',
+                            'silu(self._mv(l, "w_up", x)) * self._mv(l, "w_gate", x)'),
+    "attn_scale_dropped": ("attention", "scale = 1.0 / np.sqrt(hd)", "scale = 1.0"),
+    "attn_scale_head_count": ("attention", "scale = 1.0 / np.sqrt(hd)", "scale = 1.0 / np.sqrt(nq)"),
+    "attn_q_rope_next_pos": ("attention", "qi = rope(qi, p, ", "qi = rope(qi, p + 1, "),
+    "attn_q_rope_prev_pos": ("attention", "qi = rope(qi, p, ", "qi = rope(qi, p - 1, "),
+    "attn_q_norm_dropped": ("attention", 'qi = rmsnorm(q[i], W["q_norm"], s.eps) if s.qk_norm else q[i]',
+                            "qi = q[i]"),
+    "attn_k_rope_dropped": ("attention", "rope(kj, p, s.rope_dims, s.rope_theta)", "kj"),
+    "attn_head_map_mod": ("attention", "j = i // grp", "j = i % nkv"),
+    "attn_gate_dropped": ("attention", "u = u * sigmoid(g)", "u = u"),
+    "dn_q_k_swapped": ("deltanet", 'q = self._mv(l, "dn_q", x)\n    k = self._mv(l, "dn_k", x)',
+                       'k = self._mv(l, "dn_q", x)\n    q = self._mv(l, "dn_k", x)'),
+    "dn_beta_coeff": ("deltanet", "np.float32(s.dn_b_scale)", "np.float32(s.dn_a_scale)"),
+    "dn_gate_coeff": ("deltanet", "np.float32(s.dn_z_scale)", "np.float32(s.dn_a_scale)"),
+    "dn_gate_dropped": ("deltanet", "o * gate", "o"),
+    "dn_alpha_bias": ("deltanet", "+ np.float64(np.float32(s.dn_a_bias))", ""),
+    "dn_head_slice": ("deltanet", "kh = l2normalize(k[hh * dk:(hh + 1) * dk])", "kh = l2normalize(k[0:dk])"),
+    "dn_v_for_k": ("deltanet", "vh = v[hh * dv:(hh + 1) * dv]", "vh = k[hh * dv:(hh + 1) * dv]"),
+}
+
+PINS = [pin_ffn, pin_attention, pin_attention_key, pin_deltanet]
+
+
+def _mutant_method(meth: str, old: str, new: str):
+    src = textwrap.dedent(inspect.getsource(getattr(oracle.SliceOracle, meth)))
+    assert old in src, f"planted mistake no longer matches the oracle source: {old!r}"
+    g = dict(vars(omodel))
+    exec(compile(src.replace(old, new, 1), f"<mutant {meth}>", "exec"), g)
+    return g[meth]
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_pins_catch_planted_mistake(name, monkeypatch):
+    meth, old, new = MUTANTS[name]
+    monkeypatch.setattr(oracle.SliceOracle, meth, _mutant_method(meth, old, new))
+    caught = []
+    for pin in PINS:
+        try:
+            pin()
+        except AssertionError:
+            caught.append(pin.__name__)
+    assert caught, f"no pin fails when the oracle has the mistake {name}"
