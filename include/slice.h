@@ -61,7 +61,9 @@ enum { SLICE_Q4_0 = 2, SLICE_Q8_0 = 8 };
 
 /* Bytes of the device layout that slq_repack writes for a rows x cols matrix
  * (same bytes per weight as the GGUF blocks, padded to 64-row groups).
- * Returns 0 for an unsupported qtype or cols % 32 != 0.                      */
+ * Returns 0 for an unsupported qtype or cols % 32 != 0.  The weights are the
+ * GGUF Q4_0 / Q8_0 blocks the pages' models ship in (SwarmLLM README, model
+ * table; its repo layout has the GGUF reader repack quantised blocks at load). */
 size_t slq_packed_bytes(int qtype, int64_t rows, int64_t cols);
 
 /* Re-lay GGUF blocks for the GEMV.  raw_dev: rows x (cols/32) blocks exactly as
@@ -73,14 +75,20 @@ int slq_repack(int qtype, const void *raw_dev, int64_t rows, int64_t cols,
                void *packed_dev, void *stream);
 
 /* Decode a packed matrix to fp32, out_dev: rows x cols.  Every value
- * (q-8)*d or q*d is exact in fp32, so this equals the GGUF decode bit for bit. */
+ * (q-8)*d or q*d is exact in fp32, so this equals the GGUF decode bit for bit
+ * (the 4-bit blocks with fp16 scales of the SwarmLLM README, engine paragraph).
+ * Test access: the dequantised weights are compared with the oracle's.        */
 int slq_dequant(int qtype, const void *packed_dev, int64_t rows, int64_t cols,
                 float *out_dev, void *stream);
 
-/* Workspace bytes slq_gemv needs for `batch` right-hand sides.               */
+/* Workspace bytes slq_gemv needs for `batch` right-hand sides (0 for an
+ * unsupported qtype, shape, or batch outside 1..16).                        */
 size_t slq_gemv_workspace_bytes(int qtype, int64_t rows, int64_t cols, int batch);
 
-/* Y = W X for batch right-hand sides (1 <= batch <= 16): x_dev fp32
+/* Y = W X for batch right-hand sides (1 <= batch <= 16): the weight-streaming
+ * product that dominates decode, where every token reads every weight once
+ * (SwarmLLM README, engine paragraph); batch > 1 is the batched form a verify
+ * pass uses (same README, feature list).  x_dev fp32
  * [batch][cols], y_dev fp32 [batch][rows], ws_dev at least
  * slq_gemv_workspace_bytes() bytes and zero-filled before its first use (the
  * calls leave the counters in it at zero again, so a workspace can be reused
@@ -138,7 +146,11 @@ enum {
     SLICE_T_EMBED = 40, SLICE_T_HEAD = 41, SLICE_T_OUT_NORM = 42
 };
 
-/* Bytes of the weights buffer (packed layout of every tensor of the slice)
+/* A stage owns the weights, cache and recurrent state of its own layer range
+ * ("Unstable Legion", sections "Splitting the workload" and "The runtime:
+ * legion-stage-runtime").
+ *
+ * Bytes of the weights buffer (packed layout of every tensor of the slice)
  * and of the workspace (KV caches, DeltaNet state slots, activations, the
  * RoPE rotation table).  0 means the configuration is invalid (see
  * slice_last_error).                                                        */
@@ -154,15 +166,37 @@ size_t slice_workspace_bytes(const slice_config *cfg);
 int slice_load(const slice_config *cfg, void *weights_dev, void *workspace_dev,
                void *stream, slice_t **out);
 
-/* Repack / copy one tensor into the weights buffer (see the tensor ids). */
-int slice_set_tensor(slice_t *s, int layer, int tensor_id, const void *src_dev, void *stream);
+/* Expected source of one tensor for a configuration (host only; no GPU call):
+ * a quantised matrix of *rows x *cols weights as GGUF blocks in the slice's
+ * format (*kind = cfg->qtype, *src_bytes = rows * cols/32 * 18 or 34), or an
+ * fp32 vector of *rows entries (*kind = 0, *cols = 1, *src_bytes = 4 * rows).
+ * Any output pointer may be NULL.  SLICE_EINVAL for an invalid configuration
+ * or a tensor the slice does not hold (layer outside [begin, end), a tensor
+ * of the other layer kind, a gate or FFN the configuration has not).  A loader
+ * checks a file's tensors with this before it uploads anything (a stage loads
+ * only its own layer range: "Unstable Legion", "Splitting the workload").  */
+int slice_tensor_info(const slice_config *cfg, int layer, int tensor_id, int64_t *rows, int64_t *cols,
+                      int32_t *kind, size_t *src_bytes);
+
+/* Repack / copy one tensor into the weights buffer (see the tensor ids).
+ * src_dev holds src_bytes bytes of device memory: GGUF blocks or fp32
+ * values, exactly slice_tensor_info's *src_bytes.  A different byte count
+ * returns SLICE_ESHAPE and a tensor the slice does not hold SLICE_EINVAL,
+ * both before anything is enqueued, so a mis-shaped file cannot make the
+ * repack read past its source.  Asynchronous on `stream`; src_dev must stay
+ * valid until the stream has run the copy. */
+int slice_set_tensor(slice_t *s, int layer, int tensor_id, const void *src_dev, size_t src_bytes,
+                     void *stream);
 
 /* Set the decode position to kv_len (rows [0, kv_len) of every KV cache are
  * the context) and drop any uncommitted verify.  DeltaNet states are left as
- * they are. */
+ * they are.  The stage's prior context is its own cache ("Unstable Legion",
+ * "Splitting the workload").  SLICE_ERANGE if kv_len is outside 0..max_seq. */
 int slice_reset(slice_t *s, int kv_len, void *stream);
 
-/* One decode step at the current position p: hid_in_dev [H] -> hid_out_dev [H]
+/* One decode step at the current position p, activation in, activation out
+ * ("Unstable Legion", "The runtime: legion-stage-runtime"; one submission per
+ * token as in the SwarmLLM README, engine paragraph): hid_in_dev [H] -> hid_out_dev [H]
  * (fp16 or fp32 per io_fp32).  Appends K/V row p, updates every DeltaNet state
  * in place, then p <- p + 1.  ESTATE while a verify is uncommitted, ERANGE if
  * p + 1 > max_seq.  One graph launch per call. */
@@ -182,14 +216,17 @@ enum {
     SLICE_OP_EXIT = 9        /* boundary vector out                                   */
 };
 
-/* Same as slice_decode, but launched op by op (no graph) with a HIP event on
+/* Measurement (the pages' engine ships tok/s harnesses and a kernel-family
+ * profiler: SwarmLLM README, repo layout).
+ * Same as slice_decode, but launched op by op (no graph) with a HIP event on
  * `stream` at every op boundary; waits for the step to finish.  Writes, in
  * order, the kind and the duration in ms of each op (at most max_ops) and
  * returns how many were written (>= 0) or a negative slice_status. */
 int slice_decode_profiled(slice_t *s, const void *hid_in_dev, void *hid_out_dev,
                           int *op_kind, float *op_ms, int max_ops, void *stream);
 
-/* Launch, back to back on `stream`, the GEMV of one op kind (SLICE_OP_DN_IN,
+/* Measurement, as above.
+ * Launch, back to back on `stream`, the GEMV of one op kind (SLICE_OP_DN_IN,
  * _DN_OUT, _ATT_IN, _ATT_OUT, _FFN_IN or _FFN_OUT) for every layer of the
  * slice that has it, on the activations the last decode left in the
  * workspace; nothing else runs.  For timing one kernel in isolation.  The
@@ -198,7 +235,10 @@ int slice_decode_profiled(slice_t *s, const void *hid_in_dev, void *hid_out_dev,
  * touched. */
 int slice_run_gemv_op(slice_t *s, int op_kind, void *stream);
 
-/* Batched verify of k inputs at positions p .. p+k-1: hid_in_dev [k][H] ->
+/* Drafts are checked in one batched pass and the recurrent state is rolled
+ * back exactly on rejection (SwarmLLM README, feature list and engine
+ * paragraph).
+ * Batched verify of k inputs at positions p .. p+k-1: hid_in_dev [k][H] ->
  * hid_out_dev [k][H].  Output t equals what slice_decode would give after the
  * first t inputs.  The weights are read once for all k tokens.  The DeltaNet
  * state before the call is kept intact; the state after each token goes to its
@@ -219,25 +259,51 @@ int slice_verify(slice_t *s, int k, const void *hid_in_dev, void *hid_out_dev, v
  * then.  */
 int slice_prefill(slice_t *s, int k, const void *hid_in_dev, void *hid_out_dev, void *stream);
 
-/* Accept the first `accepted` (0..k) tokens of the pending verify: the state
- * becomes exactly the state after that many plain steps (a slot switch; no
- * values are recomputed) and p <- p + accepted.  Enqueues one tiny kernel.  */
+/* Exact rollback of the recurrent state after a verify pass (SwarmLLM README,
+ * feature list).  Accept the first `accepted` (0..k) tokens of the pending
+ * verify: the state becomes exactly the state after that many plain steps (a
+ * slot switch; no values are recomputed) and p <- p + accepted.  Enqueues one
+ * tiny kernel on `stream` (the device-side position and slot index), so later
+ * work on that stream sees the committed state.  SLICE_ESTATE when no verify
+ * is pending, SLICE_ERANGE for accepted outside 0..k.  */
 int slice_commit(slice_t *s, int accepted, void *stream);
 
-/* First stage: hid_out_dev [H] <- dequantised embedding row *tok_dev. */
+/* The first stage owns the embedding ("Unstable Legion", "Splitting the
+ * workload").  hid_out_dev [H] (boundary format) <- dequantised embedding row
+ * *tok_dev (int32 on the device; an id outside 0..vocab-1 reads row 0).
+ * SLICE_EINVAL if the slice has no embedding. */
 int slice_embed(slice_t *s, const int32_t *tok_dev, void *hid_out_dev, void *stream);
 
-/* Last stage: final RMSNorm, logits = W_head x (W_head = EMBED if tied),
- * greedy token = argmax (lowest index wins an exact tie).  logits_dev
- * ([vocab] fp32) may be NULL. */
+/* The last stage owns the head and the sampling ("Unstable Legion",
+ * "Splitting the workload"); sampling is greedy as in the SwarmLLM README's
+ * benchmark table.  Final RMSNorm, logits = W_head x (W_head = EMBED if tied),
+ * greedy token = argmax (lowest index wins an exact tie) into *tok_dev (int32,
+ * device).  hid_in_dev is in the boundary format; logits_dev ([vocab] fp32)
+ * may be NULL.  SLICE_EINVAL if the slice has no head. */
 int slice_head_argmax(slice_t *s, const void *hid_in_dev, int32_t *tok_dev,
                       float *logits_dev, void *stream);
 
+/* Host-side position p (-1 for NULL). */
 int  slice_position(const slice_t *s);
-void slice_free(slice_t *s);        /* releases host objects and graphs only */
+/* Releases host objects and graphs only; the caller frees its buffers. */
+void slice_free(slice_t *s);
+/* Thread-local message of the last failed call on this thread. */
 const char *slice_last_error(void);
 
+/* Launch-shape overrides for tests and tuning sweeps (the pages' engine
+ * tunes kernels per device: SwarmLLM README, repo layout, autotune).  Names:
+ * "KS_<kind>" / "W_<kind>" (split-K workgroups / waves per workgroup; kinds
+ * G1, G2, F1, F2, HEAD, GEMV, and G1P, G2P, F1P, F2P for prompt passes),
+ * "MFMA_MIN_T" (fewest tokens sent to the matrix-core products), "EAGER"
+ * (1: slices launch op by op instead of replaying graphs).  value < 0 removes
+ * the override.  Process-wide; slices take them at slice_load, slq_gemv at
+ * each call.  Nothing else (no environment variable) changes a launch shape,
+ * and so the summation order.  SLICE_EINVAL for an unknown name. */
+int slq_debug_override(const char *name, int value);
+
 /* ---- state access for tests and synthetic prior context ----
+ * (every optimisation of the pages' engine is gated on golden tests: SwarmLLM
+ * README, feature list; these calls give the tests the state to compare)
  * DeltaNet state of `layer` in canonical layout fp32 [dn_heads][dv][dk]
  * (S[h][i][j]: i indexes values, j keys), current slot.                   */
 int slice_dbg_set_state(slice_t *s, int layer, const float *src_dev, void *stream);

@@ -7,6 +7,7 @@ call raises.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 
 import numpy as np
@@ -14,8 +15,9 @@ import torch
 
 from ._native import (Q4_0, Q8_0, TENSOR_IDS, SliceConfig, SliceError, check, lib)  # noqa: F401
 
-__all__ = ["Q4_0", "Q8_0", "SliceConfig", "SliceError", "Slice", "make_config",
-           "packed_bytes", "repack", "dequant", "gemv", "gemv_workspace_bytes", "lib"]
+__all__ = ["Q4_0", "Q8_0", "SliceConfig", "SliceError", "Slice", "make_config", "tensor_info",
+           "packed_bytes", "repack", "dequant", "gemv", "gemv_workspace_bytes", "debug_override",
+           "overrides", "lib"]
 
 
 def _stream(stream=None) -> ctypes.c_void_p:
@@ -73,6 +75,24 @@ def gemv(qtype: int, packed: torch.Tensor, rows: int, cols: int, x: torch.Tensor
     return out
 
 
+def debug_override(name: str, value: int) -> None:
+    """Set a launch-shape override (value < 0 removes it); see slq_debug_override."""
+    check(lib().slq_debug_override(name.encode(), int(value)))
+
+
+@contextlib.contextmanager
+def overrides(**kw):
+    """Launch-shape overrides for the duration of a with-block, e.g.
+    ``with overrides(MFMA_MIN_T=2, KS_GEMV=3): ...``; removed afterwards."""
+    for k, v in kw.items():
+        debug_override(k, v)
+    try:
+        yield
+    finally:
+        for k in kw:
+            debug_override(k, -1)
+
+
 # ------------------------------------------------------------------- slice
 
 def make_config(shape, qtype: int, begin: int, end: int, *, max_seq: int = 1024, max_verify: int = 16,
@@ -102,6 +122,16 @@ def make_config(shape, qtype: int, begin: int, end: int, *, max_seq: int = 1024,
     return c
 
 
+def tensor_info(cfg: SliceConfig, layer: int, name: str) -> dict:
+    """Expected source of one tensor (host only): {"rows", "cols", "kind",
+    "src_bytes"}; kind is the GGUF type of a quantised matrix or 0 for an fp32
+    vector.  Raises SliceError if the slice does not hold the tensor."""
+    r, c, k, n = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32(), ctypes.c_size_t()
+    check(lib().slice_tensor_info(ctypes.byref(cfg), layer, TENSOR_IDS[name], ctypes.byref(r), ctypes.byref(c),
+                                  ctypes.byref(k), ctypes.byref(n)))
+    return {"rows": r.value, "cols": c.value, "kind": k.value, "src_bytes": n.value}
+
+
 class Slice:
     """A loaded layer slice: caller-owned weights and workspace on the GPU."""
 
@@ -123,7 +153,8 @@ class Slice:
     # ---- weights
     def set_tensor(self, layer: int, name: str, t: torch.Tensor, stream=None):
         t = t.contiguous()
-        check(lib().slice_set_tensor(self.handle, layer, TENSOR_IDS[name], _ptr(t), _stream(stream)))
+        check(lib().slice_set_tensor(self.handle, layer, TENSOR_IDS[name], _ptr(t), t.numel() * t.element_size(),
+                                     _stream(stream)))
 
     def load_numpy(self, tensors: dict, glob: dict | None = None, stream=None):
         """tensors: {layer: {name: np.ndarray}} (GGUF blocks or fp32 vectors); glob: embedding etc."""

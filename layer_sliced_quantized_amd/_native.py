@@ -68,7 +68,11 @@ _SIGS = {
     "slice_weights_bytes": (_SZ, [ctypes.POINTER(SliceConfig)]),
     "slice_workspace_bytes": (_SZ, [ctypes.POINTER(SliceConfig)]),
     "slice_load": (_I, [ctypes.POINTER(SliceConfig), _V, _V, _V, ctypes.POINTER(_V)]),
-    "slice_set_tensor": (_I, [_V, _I, _I, _V, _V]),
+    "slice_set_tensor": (_I, [_V, _I, _I, _V, _SZ, _V]),
+    "slice_tensor_info": (_I, [ctypes.POINTER(SliceConfig), _I, _I, ctypes.POINTER(ctypes.c_int64),
+                               ctypes.POINTER(ctypes.c_int64), ctypes.POINTER(ctypes.c_int32),
+                               ctypes.POINTER(ctypes.c_size_t)]),
+    "slq_debug_override": (_I, [ctypes.c_char_p, _I]),
     "slice_reset": (_I, [_V, _I, _V]),
     "slice_decode": (_I, [_V, _V, _V, _V]),
     "slice_decode_profiled": (_I, [_V, _V, _V, ctypes.POINTER(_I), ctypes.POINTER(ctypes.c_float), _I, _V]),

@@ -104,16 +104,23 @@ __device__ __forceinline__ float rnorm_finish(const RnRaw& r, const NormIn& n, i
 //   s = max|x| / M,  x_int = rint(x / s)  (|x_int| <= M),  u = x_int + OFF
 // with OFF = 0x888888 (Q4_0) or 0x808080 (Q8_0), so that the balanced digits
 // are ((u >> 4d) & 15) - 8 (six base-16 digits) or ((u >> 8d) & 255) - 128
-// (three base-256 digits).  Every lane of the wave must call this (shuffles).
+// (three base-256 digits).  Returns u and sets `scale` to s.  A block holding
+// an infinity or NaN gets scale NaN (digits 0), so every product that reads
+// it is NaN, as the exact sums would be; a block whose s underflows to zero
+// (max|x| below ~1e-38) is flushed to zero.  Every lane of the wave must call
+// this (cross-lane exchanges).
 template <int QT>
-__device__ __forceinline__ uint32_t quant_int(float v, float& amax) {
+__device__ __forceinline__ uint32_t quant_int(float v, float& scale) {
   const float M = QT == QT_Q4 ? M_Q4 : M_Q8;
-  amax = half_max(fabsf(v));
-  const float inv = amax > 0.0f ? M / amax : 0.0f;
-  // v * (M / amax) can round one unit past M for the largest entry; clamp so
-  // the digits stay in range (the clamped unit is below fp32 resolution of x)
   const int Mi = QT == QT_Q4 ? 7829367 : 8355711;
-  const int xi = min(max((int)rintf(v * inv), -Mi), Mi);
+  const float a = fabsf(v);
+  const float amax = half_max(a);                       // fmaxf skips NaN entries
+  const unsigned long long bad = __ballot(!(a <= 3.402823466e38f));   // NaN or infinity
+  const bool any_bad = (bad >> (threadIdx.x & 32)) & 0xffffffffull;
+  const float s = amax / M;
+  int xi = 0;
+  if (!any_bad && s > 0.0f) xi = min(max((int)rintf(v / s), -Mi), Mi);
+  scale = any_bad ? __builtin_nanf("") : (s > 0.0f ? s : 0.0f);
   return (uint32_t)(xi + (QT == QT_Q4 ? 0x888888 : 0x808080));
 }
 
@@ -126,8 +133,8 @@ __device__ __forceinline__ void quant_block_half(float v, int32_t* xd, float* xs
   const int lane = threadIdx.x & 63;
   const int e = lane & 31;
   const int base = lane & 32;
-  float amax;
-  const uint32_t u = quant_int<QT>(v, amax);
+  float sc;
+  const uint32_t u = quant_int<QT>(v, sc);
   uint32_t word = 0;
   if (QT == QT_Q4) {
     const int d = (e >> 2) % 6, m = e & 3;
@@ -149,7 +156,7 @@ __device__ __forceinline__ void quant_block_half(float v, int32_t* xd, float* xs
   }
   if (write) {
     if (e < XW) xd[e] = (int32_t)word;
-    if (e == 0) *xs = amax / (QT == QT_Q4 ? M_Q4 : M_Q8);
+    if (e == 0) *xs = sc;
   }
 }
 
@@ -159,8 +166,8 @@ __device__ __forceinline__ void quant_block_mx(float v, const Act& a, int t, int
   const int lane = threadIdx.x & 63;
   const int e = lane & 31;
   const int base = lane & 32;
-  float amax;
-  const uint32_t u = quant_int<QT>(v, amax);
+  float sc;
+  const uint32_t u = quant_int<QT>(v, sc);
   if (QT == QT_Q4) {
     // 48 dwords: chunk c = w >> 2 (p = c >> 2, g = c & 3), dword q = w & 3;
     // lane e makes dword e and, for e < 16, dword e + 32
@@ -192,8 +199,7 @@ __device__ __forceinline__ void quant_block_mx(float v, const Act& a, int t, int
     if (write && e < 24) a.mxd[(size_t)blk * (mx_block_bytes(QT) / 4) + (c * MX_SLOTS + t) * 4 + q] = (int32_t)word;
   }
   if (write && e == 0)
-    reinterpret_cast<float*>(a.mxd + (size_t)blk * (mx_block_bytes(QT) / 4) + mx_scale_off(QT) / 4)[t] =
-        amax / (QT == QT_Q4 ? M_Q4 : M_Q8);
+    reinterpret_cast<float*>(a.mxd + (size_t)blk * (mx_block_bytes(QT) / 4) + mx_scale_off(QT) / 4)[t] = sc;
 }
 
 // Digits of block blk of token t of `a`, in the lane-row layout and, when a

@@ -15,6 +15,7 @@
 #include <cstring>
 #include <algorithm>
 #include <map>
+#include <mutex>
 #include <string>
 #include <vector>
 
@@ -41,9 +42,25 @@ int fail(int code, const std::string& msg) {
 inline size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
 inline hipStream_t S(void* s) { return reinterpret_cast<hipStream_t>(s); }
 
-int env_int(const char* name, int dflt) {
-  const char* v = getenv(name);
-  return v && *v ? atoi(v) : dflt;
+// Launch-shape overrides for tests and tuning sweeps, set only through
+// slq_debug_override (never read from the environment, so a process cannot
+// change a product's summation order by inheriting a variable).  Slices take
+// them at slice_load; the standalone GEMV at each call.
+std::mutex g_ovr_mu;
+std::map<std::string, int> g_ovr;
+
+int override_int(const std::string& name, int dflt) {
+  std::lock_guard<std::mutex> lk(g_ovr_mu);
+  auto it = g_ovr.find(name);
+  return it == g_ovr.end() ? dflt : it->second;
+}
+
+bool override_name_ok(const std::string& n) {
+  if (n == "MFMA_MIN_T" || n == "EAGER") return true;
+  static const char* kinds[] = {"G1", "G2", "F1", "F2", "HEAD", "GEMV", "G1P", "G2P", "F1P", "F2P"};
+  for (const char* k : kinds)
+    if (n == std::string("KS_") + k || n == std::string("W_") + k) return true;
+  return false;
 }
 
 // Launch shape of one GEMV: `ks` workgroups share the K tiles of each 64-row
@@ -57,7 +74,8 @@ int env_int(const char* name, int dflt) {
 // per workgroup also lets a verify pass of 4 tokens use the MFMA products)
 // Other shapes: enough splits for ~1000 workgroups, about two tiles per wave,
 // at most 4 waves per workgroup.
-// SLQ_KS_<kind> / SLQ_W_<kind> override (kinds G1, G2, F1, F2, HEAD, GEMV).
+// Overrides KS_<kind> / W_<kind> (kinds G1, G2, F1, F2, HEAD, GEMV) through
+// slq_debug_override.
 struct Plan {
   int ks, w;
 };
@@ -65,9 +83,9 @@ struct Plan {
 int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
 
 // Fewest tokens per call that go to the int8-MFMA products: 0 leaves the
-// choice to gemm_min_tokens (by format and waves per workgroup);
-// SLQ_MFMA_MIN_T sets a fixed count instead.
-int mfma_min_tokens() { return clampi(env_int("SLQ_MFMA_MIN_T", 0), 0, MAX_T + 1); }
+// choice to gemm_min_tokens (by format and waves per workgroup); the override
+// MFMA_MIN_T sets a fixed count instead.
+int mfma_min_tokens() { return clampi(override_int("MFMA_MIN_T", 0), 0, MAX_T + 1); }
 
 Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
   const int nrg = (int)((rows + RG - 1) / RG);
@@ -87,8 +105,8 @@ Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
     // per wave (16 tokens: 474 against 874 us)
     p.w = clampi(k == "GEMV" || k == "HEAD" ? (ntiles / p.ks + 1) / 2 : 4, 1, 4);
   }
-  p.ks = clampi(env_int(("SLQ_KS_" + k).c_str(), p.ks), 1, 16);
-  p.w = clampi(env_int(("SLQ_W_" + k).c_str(), p.w), 1, 8);
+  p.ks = clampi(override_int("KS_" + k, p.ks), 1, 16);
+  p.w = clampi(override_int("W_" + k, p.w), 1, 8);
   return p;
 }
 
@@ -98,7 +116,7 @@ Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
 // is the fastest shape, or within 6 % of it, for every product of the
 // hidden-5120 hybrid in Q4_0 and Q8_0 (standalone sweep; e.g. gate/up 53.5
 // against 57.1 us with the decode shape, attention input 31.1 against 39.2).
-// SLQ_KS_<kind>P / SLQ_W_<kind>P override.
+// Overrides KS_<kind>P / W_<kind>P.
 Plan plan_pass(const char* kind, int64_t rows, int64_t cols) {
   const int nrg = (int)((rows + RG - 1) / RG);
   const int ntiles = (int)((cols / QK + TB - 1) / TB);
@@ -106,8 +124,8 @@ Plan plan_pass(const char* kind, int64_t rows, int64_t cols) {
   Plan p;
   p.w = clampi(ntiles, 1, 4);
   p.ks = clampi((4096 + p.w * nrg) / (2 * p.w * nrg), 1, std::max(1, ntiles / p.w));   // round(2048 / (w nrg))
-  p.ks = clampi(env_int(("SLQ_KS_" + k + "P").c_str(), p.ks), 1, 16);
-  p.w = clampi(env_int(("SLQ_W_" + k + "P").c_str(), p.w), 1, 8);
+  p.ks = clampi(override_int("KS_" + k + "P", p.ks), 1, 16);
+  p.w = clampi(override_int("W_" + k + "P", p.w), 1, 8);
   return p;
 }
 
@@ -527,11 +545,82 @@ static int run_step(slice* s, int T, int mode, const void* in, void* out, hipStr
   return SLICE_OK;
 }
 
+// Shape of tensor `tid` of `layer` for config c: rows x cols blocks of the
+// slice's format (kind = qtype) or an fp32 vector of rows entries (kind 0,
+// cols 1).  Returns "" or the reason the tensor is not part of the slice.
+namespace {
+
+std::string tensor_shape(const slice_config& c, int layer, int tid, int64_t& rows, int64_t& cols, int& kind) {
+  const int H = c.hidden;
+  const int nkd = c.dn_heads * c.dn_dk, nvd = c.dn_heads * c.dn_dv;
+  const int nq = c.q_heads * c.head_dim, nkv = c.kv_heads * c.head_dim;
+  auto mat = [&](int64_t r, int64_t cc) { rows = r; cols = cc; kind = c.qtype; return std::string(); };
+  auto vec = [&](int64_t n) { rows = n; cols = 1; kind = 0; return std::string(); };
+  if (tid == SLICE_T_EMBED) {
+    if (!(c.has_embed || (c.has_head && c.tied_head))) return "slice has no embedding";
+    return mat(c.vocab, H);
+  }
+  if (tid == SLICE_T_HEAD) {
+    if (!c.has_head || c.tied_head) return "slice has no untied head";
+    return mat(c.vocab, H);
+  }
+  if (tid == SLICE_T_OUT_NORM) return vec(H);
+  if (layer < c.layer_begin || layer >= c.layer_end) return "layer outside the slice";
+  const bool attn = c.attn_period == 0 || (layer % c.attn_period) == c.attn_period - 1;
+  switch (tid) {
+    case SLICE_T_ATTN_NORM: return vec(H);
+    case SLICE_T_FFN_NORM: return c.ffn ? vec(H) : "no FFN in this slice";
+    case SLICE_T_W_GATE:
+    case SLICE_T_W_UP: return c.ffn ? mat(c.ffn, H) : "no FFN in this slice";
+    case SLICE_T_W_DOWN: return c.ffn ? mat(H, c.ffn) : "no FFN in this slice";
+    default: break;
+  }
+  if (attn) {
+    switch (tid) {
+      case SLICE_T_WQ: return mat(nq, H);
+      case SLICE_T_WG: return c.attn_gate ? mat(nq, H) : "no attention gate";
+      case SLICE_T_WK:
+      case SLICE_T_WV: return mat(nkv, H);
+      case SLICE_T_WO: return mat(H, nq);
+      case SLICE_T_Q_NORM:
+      case SLICE_T_K_NORM: return vec(c.head_dim);
+      default: return "not an attention-layer tensor";
+    }
+  }
+  switch (tid) {
+    case SLICE_T_DN_Q:
+    case SLICE_T_DN_K: return mat(nkd, H);
+    case SLICE_T_DN_V:
+    case SLICE_T_DN_Z: return mat(nvd, H);
+    case SLICE_T_DN_A:
+    case SLICE_T_DN_B: return mat(c.dn_heads, H);
+    case SLICE_T_DN_OUT: return mat(H, nvd);
+    default: return "not a DeltaNet-layer tensor";
+  }
+}
+
+size_t tensor_src_bytes(int64_t rows, int64_t cols, int kind) {
+  if (kind == 0) return (size_t)rows * 4;
+  return (size_t)rows * (size_t)(cols / QK) * (kind == SLICE_Q4_0 ? 18 : 34);
+}
+
+}  // namespace
+
 // ====================================================================== ABI
 
 extern "C" {
 
 const char* slice_last_error(void) { return g_err.c_str(); }
+
+int slq_debug_override(const char* name, int value) {
+  if (!name) return fail(SLICE_EINVAL, "slq_debug_override: null name");
+  const std::string n(name);
+  if (!override_name_ok(n)) return fail(SLICE_EINVAL, "slq_debug_override: unknown name " + n);
+  std::lock_guard<std::mutex> lk(g_ovr_mu);
+  if (value < 0) g_ovr.erase(n);
+  else g_ovr[n] = value;
+  return SLICE_OK;
+}
 
 size_t slq_packed_bytes(int qtype, int64_t rows, int64_t cols) {
   if ((qtype != SLICE_Q4_0 && qtype != SLICE_Q8_0) || rows < 0 || cols <= 0 || cols % QK) return 0;
@@ -638,7 +727,7 @@ int slice_load(const slice_config* cfg, void* weights_dev, void* workspace_dev, 
   s->L = make_layout(*cfg);
   s->w = static_cast<uint8_t*>(weights_dev);
   s->ws = static_cast<uint8_t*>(workspace_dev);
-  s->eager = env_int("SLQ_EAGER", 0) != 0;
+  s->eager = override_int("EAGER", 0) != 0;
   s->mx_min_t = mfma_min_tokens();
   hipError_t he = hipMemsetAsync(s->w, 0, s->L.wbytes, S(stream));
   if (he == hipSuccess) he = hipMemsetAsync(s->ws, 0, s->L.wsbytes, S(stream));
@@ -653,8 +742,35 @@ int slice_load(const slice_config* cfg, void* weights_dev, void* workspace_dev, 
   return SLICE_OK;
 }
 
-int slice_set_tensor(slice_t* s, int layer, int tid, const void* src, void* stream) {
+int slice_tensor_info(const slice_config* cfg, int layer, int tid, int64_t* rows, int64_t* cols, int32_t* kind,
+                      size_t* src_bytes) {
+  if (!cfg) return fail(SLICE_EINVAL, "slice_tensor_info: null config");
+  std::string e = validate(*cfg);
+  if (!e.empty()) return fail(SLICE_EINVAL, e);
+  int64_t r = 0, c = 0;
+  int k = 0;
+  e = tensor_shape(*cfg, layer, tid, r, c, k);
+  if (!e.empty()) return fail(SLICE_EINVAL, "slice_tensor_info: " + e);
+  if (rows) *rows = r;
+  if (cols) *cols = c;
+  if (kind) *kind = k;
+  if (src_bytes) *src_bytes = tensor_src_bytes(r, c, k);
+  return SLICE_OK;
+}
+
+int slice_set_tensor(slice_t* s, int layer, int tid, const void* src, size_t src_bytes, void* stream) {
   if (!s || !src) return fail(SLICE_EINVAL, "slice_set_tensor: null argument");
+  {
+    int64_t r = 0, cc = 0;
+    int k = 0;
+    const std::string e = tensor_shape(s->cfg, layer, tid, r, cc, k);
+    if (!e.empty()) return fail(SLICE_EINVAL, "slice_set_tensor: " + e);
+    const size_t need = tensor_src_bytes(r, cc, k);
+    if (src_bytes != need)
+      return fail(SLICE_ESHAPE, "slice_set_tensor: tensor " + std::to_string(tid) + " of layer " + std::to_string(layer) +
+                                    " needs " + std::to_string(need) + " source bytes (" + std::to_string(r) + " x " +
+                                    std::to_string(cc) + (k ? " blocks" : " fp32") + "), got " + std::to_string(src_bytes));
+  }
   const slice_config& c = s->cfg;
   const Layout& L = s->L;
   const int qt = c.qtype;

@@ -274,23 +274,58 @@ def slice_tensors(g: GGUFFile, layer: int, names: dict = DEFAULT_NAMES) -> dict:
     return out
 
 
-def load_into_slice(s, g: GGUFFile, names: dict = DEFAULT_NAMES, qtype: int | None = None) -> int:
-    """Stream the file's tensors for s's layer range (and its embedding / head
-    when the slice has them) into the slice.  Quantised tensors must be in the
-    slice's format.  Returns the number of tensors loaded."""
-    qt = s.cfg.qtype if qtype is None else qtype
-    n = 0
-    glob = {}
+def check_against_config(g: GGUFFile, cfg, names: dict = DEFAULT_NAMES) -> list:
+    """Check every tensor the file holds for cfg's layer range (and its
+    embedding / head / output norm when the slice has them) against the shape
+    and format the slice expects (slice_tensor_info, host only).  Returns the
+    [(slice name, layer, GGUF name)] that would be loaded; raises GGUFError on
+    the first mismatch, before anything touches the GPU."""
+    from . import tensor_info, SliceError
+    todo = []
     for ours in _GLOBAL:
         key = names.get(ours)
-        if key and key in g.tensors:
-            glob[ours] = g.array(key)
+        if not key or key not in g.tensors:
+            continue
+        if ours == "embed" and not (cfg.has_embed or (cfg.has_head and cfg.tied_head)):
+            continue
+        if ours in ("head", "out_norm") and not cfg.has_head:
+            continue
+        todo.append((ours, 0, key))
+    for layer in range(cfg.layer_begin, cfg.layer_end):
+        for ours, theirs in names.items():
+            key = theirs.format(l=layer)
+            if ours not in _GLOBAL and key in g.tensors:
+                todo.append((ours, layer, key))
+    for ours, layer, key in todo:
+        info = g.tensors[key]
+        try:
+            want = tensor_info(cfg, layer, ours)
+        except SliceError as e:
+            raise GGUFError(f"{key}: not part of this slice ({e})") from None
+        if want["kind"] == 0:
+            ok = info.ttype == T_F32 and tuple(int(d) for d in info.dims) == (want["rows"],)
+            what = f"F32 vector of {want['rows']}"
+        else:
+            ok = info.ttype == want["kind"] and tuple(int(d) for d in info.dims) == (want["cols"], want["rows"])
+            what = f"type {want['kind']} matrix of {want['rows']} x {want['cols']}"
+        if not ok:
+            raise GGUFError(f"{key}: type {info.ttype} with dims {tuple(info.dims)}; the slice needs a {what}")
+        if tensor_nbytes(info.ttype, info.dims) != want["src_bytes"]:
+            raise GGUFError(f"{key}: {tensor_nbytes(info.ttype, info.dims)} bytes, the slice needs {want['src_bytes']}")
+    return todo
+
+
+def load_into_slice(s, g: GGUFFile, names: dict = DEFAULT_NAMES) -> int:
+    """Stream the file's tensors for s's layer range (and its embedding / head
+    when the slice has them) into the slice.  Every tensor is checked against
+    the slice's configuration first (check_against_config); a file with a
+    tensor of another shape or format is refused before any upload.  Returns
+    the number of tensors loaded."""
+    todo = check_against_config(g, s.cfg, names)
+    glob = {o: g.array(k) for o, _, k in todo if o in _GLOBAL}
+    n = 0
     for layer in range(s.cfg.layer_begin, s.cfg.layer_end):
-        d = slice_tensors(g, layer, names)
-        for ours, key in ((o, names[o].format(l=layer)) for o in d):
-            t = g.tensors[key].ttype
-            if t in _BLOCK and t != qt:
-                raise GGUFError(f"{key}: tensor type {t}, the slice holds type {qt}")
+        d = {o: g.array(k) for o, l, k in todo if l == layer and o not in _GLOBAL}
         s.load_numpy({layer: d})
         n += len(d)
     if glob:

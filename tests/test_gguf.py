@@ -143,3 +143,80 @@ def test_metadata_of_every_value_type_round_trips(tmp_path):
             assert list(got) == v, k
         else:
             assert got == v, k
+
+
+# --------------------------------------- files checked against a slice config
+
+_LIB = __import__("os").path.join(__import__("os").path.dirname(__import__("os").path.dirname(
+    __import__("os").path.abspath(__file__))), "layer_sliced_quantized_amd", "libslq.so")
+needs_lib = pytest.mark.skipif(not __import__("os").path.exists(_LIB), reason="libslq.so not built")
+
+
+def _cfg(qtype=synth.Q4_0):
+    import layer_sliced_quantized_amd as slq
+    return slq.make_config(SHAPE, qtype, 0, 4, max_seq=256, max_verify=4, io_fp32=True)
+
+
+@needs_lib
+@pytest.mark.parametrize("qtype", [synth.Q4_0, synth.Q8_0])
+def test_well_formed_file_passes_the_config_check(tmp_path, qtype):
+    tensors = {l: synth.layer_tensors(SHAPE, qtype, 0, 93, l) for l in range(4)}
+    p = tmp_path / "ok.gguf"
+    gguf.write_gguf(str(p), {}, gguf_tensors(SHAPE, tensors, qtype))
+    todo = gguf.check_against_config(gguf.GGUFFile(str(p)), _cfg(qtype))
+    assert len(todo) == sum(len(d) for d in tensors.values())
+
+
+def _mutated_file(tmp_path, key, value):
+    tensors = {l: synth.layer_tensors(SHAPE, synth.Q4_0, 0, 93, l) for l in range(4)}
+    t = gguf_tensors(SHAPE, tensors, synth.Q4_0)
+    t[key] = value
+    p = tmp_path / "bad.gguf"
+    gguf.write_gguf(str(p), {}, t)
+    return gguf.GGUFFile(str(p))
+
+
+@needs_lib
+def test_misshaped_or_misformatted_tensors_are_refused(tmp_path):
+    """A real file with other head counts, an F16 or Q8_0 matrix where the
+    slice holds Q4_0, or a vector of the wrong length is refused by the host
+    check, before any byte reaches the GPU (no GPU is used here)."""
+    cases = {
+        # 3 DeltaNet heads' worth of q rows (192) where the slice has 2 heads (128)
+        "blk.0.dn_q.weight": (gguf.T_Q4_0, (128, 192), bytes(192 * 4 * 18)),
+        # the right shape in F16
+        "blk.0.dn_k.weight": (gguf.T_F16, (128, 128), bytes(128 * 128 * 2)),
+        # the right shape in another block format
+        "blk.3.attn_q.weight": (gguf.T_Q8_0, (128, 256), bytes(256 * 4 * 34)),
+        # the FFN down projection stored transposed (256 x 128 instead of 128 x 256)
+        "blk.1.ffn_down.weight": (gguf.T_Q4_0, (128, 256), bytes(256 * 4 * 18)),
+        # a norm vector of the wrong length
+        "blk.2.attn_norm.weight": np.ones(64, np.float32),
+    }
+    for key, val in cases.items():
+        g = _mutated_file(tmp_path, key, val)
+        with pytest.raises(gguf.GGUFError) as e:
+            gguf.check_against_config(g, _cfg())
+        assert key in str(e.value)
+
+
+@needs_lib
+def test_tensor_info_and_overrides_are_host_only():
+    import layer_sliced_quantized_amd as slq
+    cfg = _cfg()
+    assert slq.tensor_info(cfg, 0, "dn_q") == {"rows": 128, "cols": 128, "kind": 2, "src_bytes": 128 * 4 * 18}
+    assert slq.tensor_info(cfg, 3, "wo") == {"rows": 128, "cols": 256, "kind": 2, "src_bytes": 128 * 8 * 18}
+    assert slq.tensor_info(cfg, 1, "w_down")["cols"] == 256
+    assert slq.tensor_info(cfg, 3, "q_norm") == {"rows": 64, "cols": 1, "kind": 0, "src_bytes": 256}
+    with pytest.raises(slq.SliceError):
+        slq.tensor_info(cfg, 3, "dn_q")          # an attention layer has no DeltaNet tensors
+    with pytest.raises(slq.SliceError):
+        slq.tensor_info(cfg, 4, "attn_norm")     # outside the layer range
+    with pytest.raises(slq.SliceError):
+        slq.tensor_info(cfg, 0, "embed")         # no embedding in this slice
+    slq.debug_override("KS_F1", 3)
+    slq.debug_override("KS_F1", -1)
+    with pytest.raises(slq.SliceError):
+        slq.debug_override("KS_NOPE", 1)
+    with slq.overrides(MFMA_MIN_T=2, EAGER=1):
+        pass

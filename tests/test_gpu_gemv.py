@@ -77,10 +77,10 @@ SPLITS = [(1, 1), (1, 8), (3, 2), (16, 1), (2, 8), (5, 3)]
 @pytest.mark.parametrize("qtype", QTYPES)
 @pytest.mark.parametrize("ks,w", SPLITS)
 @pytest.mark.parametrize("rows,cols", [(200, 32 * 19), (1000, 32 * 37), (64, 32 * 130)])
-def test_gemm_batch_equals_single_bitwise(qtype, ks, w, rows, cols, monkeypatch):
-    monkeypatch.setenv("SLQ_MFMA_MIN_T", "2")      # every batched call on the matrix cores
-    monkeypatch.setenv("SLQ_KS_GEMV", str(ks))
-    monkeypatch.setenv("SLQ_W_GEMV", str(w))
+def test_gemm_batch_equals_single_bitwise(qtype, ks, w, rows, cols, ovr):
+    ovr(MFMA_MIN_T="2")      # every batched call on the matrix cores
+    ovr(KS_GEMV=ks)
+    ovr(W_GEMV=w)
     raw = _raw(qtype, rows, cols, 9)
     packed = slq.repack(qtype, _dev(raw), rows, cols)
     x = synth.gemv_x(12, 16, cols, tag=ks * 10 + w)
@@ -99,15 +99,15 @@ def test_gemm_batch_equals_single_bitwise(qtype, ks, w, rows, cols, monkeypatch)
 
 @pytest.mark.parametrize("qtype", QTYPES)
 @pytest.mark.parametrize("batch,min_t", [(1, "0"), (5, "17"), (5, "2"), (16, "2")])
-def test_split_tickets_reset_on_reuse(qtype, batch, min_t, monkeypatch):
+def test_split_tickets_reset_on_reuse(qtype, batch, min_t, ovr):
     """The split that takes a row group's last ticket resets it: one workspace
     reused for different inputs gives each call the result of a fresh
     workspace, and its tickets end at zero.  (min_t 17 keeps a 5-token call on
     the per-row GEMV, 2 sends it to the MFMA products.)"""
     ks, w = 5, 2
-    monkeypatch.setenv("SLQ_KS_GEMV", str(ks))
-    monkeypatch.setenv("SLQ_W_GEMV", str(w))
-    monkeypatch.setenv("SLQ_MFMA_MIN_T", min_t)
+    ovr(KS_GEMV=ks)
+    ovr(W_GEMV=w)
+    ovr(MFMA_MIN_T=min_t)
     rows, cols = 1000, 32 * 37
     raw = _raw(qtype, rows, cols, 14)
     packed = slq.repack(qtype, _dev(raw), rows, cols)
@@ -124,14 +124,14 @@ def test_split_tickets_reset_on_reuse(qtype, batch, min_t, monkeypatch):
 
 
 @pytest.mark.parametrize("qtype", QTYPES)
-def test_gemm_single_token_through_mfma(qtype, monkeypatch):
+def test_gemm_single_token_through_mfma(qtype, ovr):
     """With the MFMA path forced for one token the result equals the GEMV's."""
     rows, cols = 1000, 32 * 37
     raw = _raw(qtype, rows, cols, 10)
     packed = slq.repack(qtype, _dev(raw), rows, cols)
     x = synth.gemv_x(13, 1, cols)
     y_gemv = slq.gemv(qtype, packed, rows, cols, _dev(x)).cpu().numpy()
-    monkeypatch.setenv("SLQ_MFMA_MIN_T", "1")
+    ovr(MFMA_MIN_T="1")
     y_mfma = slq.gemv(qtype, packed, rows, cols, _dev(x)).cpu().numpy()
     np.testing.assert_array_equal(y_gemv, y_mfma)
 

@@ -38,7 +38,7 @@ def _read_blocks():
 
 def test_golden_blocks_decode_exactly():
     blocks = _read_blocks()
-    assert len(blocks) == 5
+    assert len(blocks) == 7
     for b in blocks:
         assert b["bytes"].size == synth.BLOCK_BYTES[b["type"]]
         got = qref.dequant(b["type"], b["bytes"][None, :], 1, 32)[0]
