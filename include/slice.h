@@ -98,6 +98,26 @@ size_t slq_gemv_workspace_bytes(int qtype, int64_t rows, int64_t cols, int batch
 int slq_gemv(int qtype, const void *packed_dev, int64_t rows, int64_t cols, int batch,
              const float *x_dev, float *y_dev, void *ws_dev, size_t ws_bytes, void *stream);
 
+/* Bytes of the static device scratch of slq_gemv_noalloc (16 MiB per GPU). */
+#define SLQ_GEMV_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* slq_gemv for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  Same
+ * arguments, kernels and results (bit for bit) as slq_gemv, but the
+ * workspace is a file-scope device array of SLQ_GEMV_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends; no
+ * call allocates or frees memory.  SLICE_ESHAPE when the shape needs more
+ * scratch than that (slq_gemv_workspace_bytes() > the limit; every shape with
+ * rows <= 262144 and cols <= 32768 fits at any batch), or for an unsupported
+ * qtype, shape or batch; SLICE_EINVAL for a null pointer; SLICE_EHIP if the
+ * scratch's device address cannot be obtained.  Three kernel launches: the
+ * row-group tickets are cleared by a fill kernel, then the two of slq_gemv.
+ * All calls on one GPU share its scratch, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (different streams or
+ * threads without ordering between them) race and give wrong results.     */
+int slq_gemv_noalloc(int qtype, const void *packed_dev, int64_t rows, int64_t cols, int batch,
+                     const float *x_dev, float *y_dev, void *stream);
+
 /* ------------------------------------------------------------------------ */
 /* Slice executor                                                            */
 /* ------------------------------------------------------------------------ */

@@ -65,6 +65,7 @@ _SIGS = {
     "slq_dequant": (_I, [_I, _V, _I64, _I64, _V, _V]),
     "slq_gemv_workspace_bytes": (_SZ, [_I, _I64, _I64, _I]),
     "slq_gemv": (_I, [_I, _V, _I64, _I64, _I, _V, _V, _V, _SZ, _V]),
+    "slq_gemv_noalloc": (_I, [_I, _V, _I64, _I64, _I, _V, _V, _V]),
     "slice_weights_bytes": (_SZ, [ctypes.POINTER(SliceConfig)]),
     "slice_workspace_bytes": (_SZ, [ctypes.POINTER(SliceConfig)]),
     "slice_load": (_I, [ctypes.POINTER(SliceConfig), _V, _V, _V, ctypes.POINTER(_V)]),

@@ -28,6 +28,18 @@ hipError_t launch_store_out(const float* h, int T, int H, void* out, int fp32, C
   return hipGetLastError();
 }
 
+__global__ void k_fill_zero_u32(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+hipError_t launch_fill_zero_u32(uint32_t* p, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const size_t nb = (n + 255) / 256;
+  const unsigned grid = (unsigned)(nb < 1024 ? nb : 1024);
+  k_fill_zero_u32<<<grid, 256, 0, s>>>(p, n);
+  return hipGetLastError();
+}
+
 __global__ void k_ctrl_io(Ctrl* c, const void* in, void* out) {
   c->in = in;
   c->out = out;

@@ -606,6 +606,36 @@ size_t tensor_src_bytes(int64_t rows, int64_t cols, int kind) {
 
 }  // namespace
 
+// Scratch of the allocation-free standalone GEMV (slq_gemv_noalloc): one
+// file-scope device array, which every GPU the library runs on holds until the
+// process ends.  Host code never uses its name as an address: the device
+// address is taken once per device with hipGetSymbolAddress (with that device
+// current) and kept here.
+static __device__ __align__(256) uint8_t scratch[SLQ_GEMV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+std::mutex g_scratch_mu;
+std::map<int, uint8_t*> g_scratch_ptr;   // device id -> address of `scratch` on it
+
+int scratch_on_current_device(uint8_t** out) {
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it == g_scratch_ptr.end()) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(SLICE_EHIP, std::string("slq_gemv_noalloc: hipGetSymbolAddress: ") + hipGetErrorString(e));
+    it = g_scratch_ptr.emplace(dev, static_cast<uint8_t*>(p)).first;
+  }
+  *out = it->second;
+  return SLICE_OK;
+}
+
+}  // namespace
+
 // ====================================================================== ABI
 
 extern "C" {
@@ -644,11 +674,9 @@ int slq_dequant(int qtype, const void* packed_dev, int64_t rows, int64_t cols, f
   return SLICE_OK;
 }
 
-// Standalone GEMV workspace: activation digits (room for both layouts), their
-// scales, split-K partials, ticket counters.
 // Standalone GEMV workspace, in order: lane-row digits [batch][nblk][24],
 // their scales, MFMA-layout block records, split-K partials
-// [nrg][ks][batch][64], ticket counters [nrg].
+// [nrg][ks][batch][64] (only when the plan splits K), ticket counters [nrg].
 struct GemvWs {
   size_t dig, sc, mdig, part, cnt, total;
 };
@@ -661,10 +689,32 @@ static GemvWs gemv_ws(int qtype, int64_t rows, int64_t cols, int batch) {
   w.dig = o; o += al256((size_t)batch * nblk * XW * 4);
   w.sc = o; o += al256((size_t)batch * nblk * 4);
   w.mdig = o; o += al256((size_t)nblk * mx_block_bytes(qtype));
-  w.part = o; o += al256((size_t)nrg * p.ks * batch * RG * 4);
+  w.part = o; o += p.ks > 1 ? al256((size_t)nrg * p.ks * batch * RG * 4) : 0;
   w.cnt = o; o += al256((size_t)nrg * 4);
   w.total = o;
   return w;
+}
+
+// The two launches of a standalone GEMV on a workspace laid out by gemv_ws:
+// activation digits, then the product.
+static int run_gemv(int qtype, const void* packed_dev, int64_t rows, int64_t cols, int batch, const float* x_dev,
+                    float* y_dev, uint8_t* ws, const GemvWs& L, hipStream_t st) {
+  const int nblk = (int)(cols / QK);
+  const int min_t = mfma_min_tokens();
+  const bool mx = batch >= (min_t ? min_t : 2);
+  Act a{reinterpret_cast<int32_t*>(ws + L.dig), reinterpret_cast<float*>(ws + L.sc), nblk,
+        mx ? reinterpret_cast<int32_t*>(ws + L.mdig) : nullptr, min_t};
+  HIPCHK(launch_quant_act(qtype, x_dev, batch, (int)cols, cols, a, st));
+  const Plan pl = plan_gemv("GEMV", rows, cols);
+  const Packed W{static_cast<const uint8_t*>(packed_dev), rows, cols, qtype};
+  GemvOut o{};
+  o.kind = EPI_STORE;
+  o.y = y_dev;
+  o.y_tstride = rows;
+  o.part = reinterpret_cast<float*>(ws + L.part);
+  o.cnt = reinterpret_cast<unsigned*>(ws + L.cnt);
+  HIPCHK(launch_gemv(W, batch, a, NormIn{nullptr, 0, 0.f, 0.f}, o, pl.ks, pl.w, st));
+  return SLICE_OK;
 }
 
 size_t slq_gemv_workspace_bytes(int qtype, int64_t rows, int64_t cols, int batch) {
@@ -678,26 +728,27 @@ int slq_gemv(int qtype, const void* packed_dev, int64_t rows, int64_t cols, int 
   if (!need) return fail(SLICE_ESHAPE, "slq_gemv: bad qtype, shape or batch (1..16)");
   if (ws_bytes < need) return fail(SLICE_EINVAL, "slq_gemv: workspace too small");
   if (!packed_dev || !x_dev || !y_dev || !ws_dev) return fail(SLICE_EINVAL, "slq_gemv: null pointer");
-  const int nblk = (int)(cols / QK);
-  uint8_t* ws = static_cast<uint8_t*>(ws_dev);
+  return run_gemv(qtype, packed_dev, rows, cols, batch, x_dev, y_dev, static_cast<uint8_t*>(ws_dev),
+                  gemv_ws(qtype, rows, cols, batch), S(stream));
+}
+
+int slq_gemv_noalloc(int qtype, const void* packed_dev, int64_t rows, int64_t cols, int batch, const float* x_dev,
+                     float* y_dev, void* stream) {
+  const size_t need = slq_gemv_workspace_bytes(qtype, rows, cols, batch);
+  if (!need) return fail(SLICE_ESHAPE, "slq_gemv_noalloc: bad qtype, shape or batch (1..16)");
+  if (need > SLQ_GEMV_NOALLOC_SCRATCH_BYTES)
+    return fail(SLICE_ESHAPE, "slq_gemv_noalloc: this shape needs " + std::to_string(need) +
+                                  " bytes of scratch; the static scratch holds " +
+                                  std::to_string((size_t)SLQ_GEMV_NOALLOC_SCRATCH_BYTES) + " (use slq_gemv)");
+  if (!packed_dev || !x_dev || !y_dev) return fail(SLICE_EINVAL, "slq_gemv_noalloc: null pointer");
+  uint8_t* ws = nullptr;
+  int rc = scratch_on_current_device(&ws);
+  if (rc) return rc;
   const GemvWs L = gemv_ws(qtype, rows, cols, batch);
-  const int min_t = mfma_min_tokens();
-  const bool mx = batch >= (min_t ? min_t : 2);
-  Act a{reinterpret_cast<int32_t*>(ws + L.dig), reinterpret_cast<float*>(ws + L.sc), nblk,
-        mx ? reinterpret_cast<int32_t*>(ws + L.mdig) : nullptr, min_t};
-  float* part = reinterpret_cast<float*>(ws + L.part);
-  unsigned* cnt = reinterpret_cast<unsigned*>(ws + L.cnt);
-  HIPCHK(launch_quant_act(qtype, x_dev, batch, (int)cols, cols, a, S(stream)));
-  const Plan pl = plan_gemv("GEMV", rows, cols);
-  const Packed W{static_cast<const uint8_t*>(packed_dev), rows, cols, qtype};
-  GemvOut o{};
-  o.kind = EPI_STORE;
-  o.y = y_dev;
-  o.y_tstride = rows;
-  o.part = part;
-  o.cnt = cnt;
-  HIPCHK(launch_gemv(W, batch, a, NormIn{nullptr, 0, 0.f, 0.f}, o, pl.ks, pl.w, S(stream)));
-  return SLICE_OK;
+  // the row-group tickets must start at zero: a fill kernel (no memset node,
+  // no allocation), then the same two launches as slq_gemv
+  HIPCHK(launch_fill_zero_u32(reinterpret_cast<uint32_t*>(ws + L.cnt), (size_t)((rows + RG - 1) / RG), S(stream)));
+  return run_gemv(qtype, packed_dev, rows, cols, batch, x_dev, y_dev, ws, L, S(stream));
 }
 
 size_t slice_weights_bytes(const slice_config* cfg) {
