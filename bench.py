@@ -331,6 +331,8 @@ def main() -> int:
     ap.add_argument("--no-attn-sweep", action="store_true", help="skip the decode-attention timing at 512/4096/32768 KV rows")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--no-chain", action="store_true",
+                    help="decode with every product as its own kernel instead of the chained products (same results)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run 3 plain copies of a 512 MiB buffer (a known-size reference for PMC byte counters)")
     args = ap.parse_args()
@@ -342,7 +344,10 @@ def main() -> int:
 
     import torch
     import synth
+    import layer_sliced_quantized_amd as slq
     torch.cuda.set_device(0)
+    if args.no_chain:
+        slq.debug_override("CHAIN", 0)
     threads = min(16, os.cpu_count() or 8)
     shape = synth.HYBRID_5120
     n_in = args.warmup + args.steps + args.profile_steps + 4 * (args.verify_rounds + 1) + 32 * (args.prefill_chunks + 1) + 16

@@ -209,8 +209,8 @@ int slice_set_tensor(slice_t *s, int layer, int tensor_id, const void *src_dev, 
                      void *stream);
 
 /* Set the decode position to kv_len (rows [0, kv_len) of every KV cache are
- * the context) and drop any uncommitted verify.  DeltaNet states are left as
- * they are.  The stage's prior context is its own cache ("Unstable Legion",
+ * the context) and drop any uncommitted verify; clears the condition that
+ * slice_sync_check reports.  DeltaNet states are left as they are.  The stage's prior context is its own cache ("Unstable Legion",
  * "Splitting the workload").  SLICE_ERANGE if kv_len is outside 0..max_seq. */
 int slice_reset(slice_t *s, int kv_len, void *stream);
 
@@ -233,7 +233,10 @@ enum {
     SLICE_OP_ATT_OUT = 6,    /* attention output projection + residual (GEMV)         */
     SLICE_OP_FFN_IN = 7,     /* RMSNorm + fused gate/up projection + SwiGLU (GEMV)    */
     SLICE_OP_FFN_OUT = 8,    /* down projection + residual (GEMV)                     */
-    SLICE_OP_EXIT = 9        /* boundary vector out                                   */
+    SLICE_OP_EXIT = 9,       /* boundary vector out                                   */
+    SLICE_OP_CHAIN = 10      /* one layer's products after its mixer, chained in one
+                                kernel: mixer output + residual, gate/up + SwiGLU,
+                                down + residual, next layer's input projections    */
 };
 
 /* Measurement (the pages' engine ships tok/s harnesses and a kernel-family
@@ -247,7 +250,8 @@ int slice_decode_profiled(slice_t *s, const void *hid_in_dev, void *hid_out_dev,
 
 /* Measurement, as above.
  * Launch, back to back on `stream`, the GEMV of one op kind (SLICE_OP_DN_IN,
- * _DN_OUT, _ATT_IN, _ATT_OUT, _FFN_IN or _FFN_OUT) for every layer of the
+ * _DN_OUT, _ATT_IN, _ATT_OUT, _FFN_IN or _FFN_OUT; or SLICE_OP_CHAIN, the
+ * chained-product kernel decode uses) for every layer of the
  * slice that has it, on the activations the last decode left in the
  * workspace; nothing else runs.  For timing one kernel in isolation.  The
  * residual-update kinds (_OUT) modify the workspace copy of h, which the next
@@ -303,6 +307,14 @@ int slice_embed(slice_t *s, const int32_t *tok_dev, void *hid_out_dev, void *str
 int slice_head_argmax(slice_t *s, const void *hid_in_dev, int32_t *tok_dev,
                       float *logits_dev, void *stream);
 
+/* Decode steps run each layer's products after its mixer as one kernel whose
+ * workgroups wait, with a bounded wait, for the product before theirs (the
+ * pages' engine submits one command buffer per token: SwarmLLM README,
+ * engine paragraph).  Synchronises `stream`, then returns SLICE_EHIP if such
+ * a wait gave up since the last slice_reset (the step's outputs are then
+ * invalid), else SLICE_OK. */
+int slice_sync_check(slice_t *s, void *stream);
+
 /* Host-side position p (-1 for NULL). */
 int  slice_position(const slice_t *s);
 /* Releases host objects and graphs only; the caller frees its buffers. */
@@ -315,7 +327,9 @@ const char *slice_last_error(void);
  * "KS_<kind>" / "W_<kind>" (split-K workgroups / waves per workgroup; kinds
  * G1, G2, F1, F2, HEAD, GEMV, and G1P, G2P, F1P, F2P for prompt passes),
  * "MFMA_MIN_T" (fewest tokens sent to the matrix-core products), "EAGER"
- * (1: slices launch op by op instead of replaying graphs).  value < 0 removes
+ * (1: slices launch op by op instead of replaying graphs), "CHAIN" (0: decode
+ * launches every product as its own kernel; the results are the same bits),
+ * "CHAIN_MAX" (1..4: products per chained kernel).  value < 0 removes
  * the override.  Process-wide; slices take them at slice_load, slq_gemv at
  * each call.  Nothing else (no environment variable) changes a launch shape,
  * and so the summation order.  SLICE_EINVAL for an unknown name. */

@@ -216,7 +216,7 @@ class Slice:
         return h_out
 
     OP_NAMES = ["entry", "dn_in", "deltanet", "dn_out", "att_in", "attention", "att_out", "ffn_in", "ffn_out",
-                "exit"]
+                "exit", "chain"]
 
     def decode_profiled(self, h_in: torch.Tensor, h_out: torch.Tensor | None = None, stream=None):
         """One decode step, op by op, with a HIP event at every op boundary.
@@ -265,6 +265,11 @@ class Slice:
             tok = torch.empty(1, dtype=torch.int32, device=self.device)
         check(lib().slice_head_argmax(self.handle, _ptr(h), _ptr(tok), _ptr(logits), _stream(stream)))
         return tok
+
+    def sync_check(self, stream=None):
+        """Wait for the stream; raise SliceError if a bounded wait inside a
+        chained decode kernel gave up since the last reset."""
+        check(lib().slice_sync_check(self.handle, _stream(stream)))
 
     @property
     def position(self) -> int:

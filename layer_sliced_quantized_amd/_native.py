@@ -84,6 +84,7 @@ _SIGS = {
     "slice_embed": (_I, [_V, _V, _V, _V]),
     "slice_head_argmax": (_I, [_V, _V, _V, _V, _V]),
     "slice_position": (_I, [_V]),
+    "slice_sync_check": (_I, [_V, _V]),
     "slice_free": (None, [_V]),
     "slice_last_error": (ctypes.c_char_p, []),
     "slice_dbg_set_state": (_I, [_V, _I, _V, _V]),

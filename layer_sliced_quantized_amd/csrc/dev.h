@@ -65,6 +65,22 @@ __device__ __forceinline__ float half_max(float v) {
 
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + expf(-x)); }
 
+// Stores and loads of values that workgroups of the same kernel hand to each
+// other (COH = true): agent-scope relaxed atomics, which gfx950 issues as
+// global stores / loads with the sc1 bit (written through to, and read from,
+// the point where all XCDs see the same value).  With COH = false, plain
+// accesses (the kernel boundary makes them visible).
+template <bool COH, class V>
+__device__ __forceinline__ void st_(V* p, V v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+template <bool COH, class V>
+__device__ __forceinline__ V ld_(const V* p) {
+  if constexpr (COH) return __hip_atomic_load(const_cast<V*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+
 // RMSNorm factor from a producer's partial sums of squares: one load per lane
 // (all in flight together), then a butterfly sum, so every wave that calls
 // this gets the same value.
@@ -86,11 +102,12 @@ __device__ __forceinline__ float rnorm_from(const NormIn& n, int t) {
 struct RnRaw {
   float a, b;
 };
+template <bool COH = false>
 __device__ __forceinline__ RnRaw rnorm_fetch(const NormIn& n, int t) {
   const int lane = threadIdx.x & 63;
   if (!n.ssq || n.n_part > 128) return {0.0f, 0.0f};
   const float* s = n.ssq + (size_t)t * n.n_part;
-  return {lane < n.n_part ? s[lane] : 0.0f, lane + 64 < n.n_part ? s[lane + 64] : 0.0f};
+  return {lane < n.n_part ? ld_<COH>(s + lane) : 0.0f, lane + 64 < n.n_part ? ld_<COH>(s + lane + 64) : 0.0f};
 }
 __device__ __forceinline__ float rnorm_finish(const RnRaw& r, const NormIn& n, int t) {
   if (!n.ssq) return 1.0f;
@@ -128,7 +145,7 @@ __device__ __forceinline__ uint32_t quant_int(float v, float& scale) {
 //   Q4_0: nibble 2k of dword (d, m) <- digit d of element 4m+k, nibble 2k+1 <- of
 //         element 4m+k+16  (byte j of a Q4_0 block holds weights j, j+16)
 //   Q8_0: byte k of dword (d, m) <- digit d of element 4m+k
-template <int QT>
+template <int QT, bool COH = false>
 __device__ __forceinline__ void quant_block_half(float v, int32_t* xd, float* xs, bool write) {
   const int lane = threadIdx.x & 63;
   const int e = lane & 31;
@@ -155,8 +172,8 @@ __device__ __forceinline__ void quant_block_half(float v, int32_t* xd, float* xs
     }
   }
   if (write) {
-    if (e < XW) xd[e] = (int32_t)word;
-    if (e == 0) *xs = sc;
+    if (e < XW) st_<COH>(xd + e, (int32_t)word);
+    if (e == 0) st_<COH>(xs, sc);
   }
 }
 
@@ -205,11 +222,12 @@ __device__ __forceinline__ void quant_block_mx(float v, const Act& a, int t, int
 // Digits of block blk of token t of `a`, in the lane-row layout and, when a
 // has one, the MFMA layout.  Every lane of the wave must call this; `write`
 // selects which 32-lane halves store.
+template <bool COH = false>
 __device__ __forceinline__ void put_digits(const Act& a, int qt, int t, int blk, float v, bool write) {
   int32_t* xd = a.xd + ((size_t)t * a.nblk + blk) * XW;
   float* xs = a.xs + (size_t)t * a.nblk + blk;
-  if (qt == QT_Q4) quant_block_half<QT_Q4>(v, xd, xs, write);
-  else quant_block_half<QT_Q8>(v, xd, xs, write);
+  if (qt == QT_Q4) quant_block_half<QT_Q4, COH>(v, xd, xs, write);
+  else quant_block_half<QT_Q8, COH>(v, xd, xs, write);
   if (a.mxd) {
     if (qt == QT_Q4) quant_block_mx<QT_Q4>(v, a, t, blk, write);
     else quant_block_mx<QT_Q8>(v, a, t, blk, write);
@@ -220,22 +238,24 @@ __device__ __forceinline__ void put_digits(const Act& a, int qt, int t, int blk,
 // for row rg*64+lane (0 beyond H).  Writes h, the sum of squares of the 64 rows,
 // and the digits of norm_w*h for blocks 2rg and 2rg+1.
 // `w` is norm_w of this lane's row (0 beyond H).
+template <bool COH = false>
 __device__ __forceinline__ void resid_tail_w(int t, int rg, int H, float hn, float w, float* h, int64_t h_ts, int qt,
                                              const Act& next, float* ssq_out, int nrg) {
   const int lane = threadIdx.x & 63;
   const int row = rg * RG + lane;
-  if (row < H) h[(size_t)t * h_ts + row] = hn;
+  if (row < H) st_<COH>(h + (size_t)t * h_ts + row, hn);
   const float ss = wave_sum(hn * hn);
-  if (lane == 0) ssq_out[(size_t)t * nrg + rg] = ss;
+  if (lane == 0) st_<COH>(ssq_out + (size_t)t * nrg + rg, ss);
   const int blk = 2 * rg + (lane >> 5);
-  put_digits(next, qt, t, blk, w * hn, blk < next.nblk);
+  put_digits<COH>(next, qt, t, blk, w * hn, blk < next.nblk);
 }
+template <bool COH = false>
 __device__ __forceinline__ void resid_tail(int t, int rg, int H, float hn, float* h, int64_t h_ts,
                                            const float* norm_w, int qt, const Act& next,
                                            float* ssq_out, int nrg) {
   const int row = rg * RG + (int)(threadIdx.x & 63);
   const float w = row < H ? norm_w[row] : 0.0f;
-  resid_tail_w(t, rg, H, hn, w, h, h_ts, qt, next, ssq_out, nrg);
+  resid_tail_w<COH>(t, rg, H, hn, w, h, h_ts, qt, next, ssq_out, nrg);
 }
 
 }  // namespace slq

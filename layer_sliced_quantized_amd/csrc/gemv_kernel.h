@@ -179,6 +179,106 @@ __device__ __forceinline__ void tile_math(const TileRegs<QT>& r, int nb, int kb,
   }
 }
 
+// Tile range [t0, t1) of wave `wave` of `nw` in split ks of ksplit (uniform:
+// readfirstlane keeps the loop and the digit addresses in scalar registers).
+__device__ __forceinline__ void wave_tiles(int ntiles, int ks, int ksplit, int wave, int nw, int& t0, int& t1) {
+  const int w0 = ntiles * ks / ksplit, w1 = ntiles * (ks + 1) / ksplit;
+  t0 = __builtin_amdgcn_readfirstlane(w0 + (w1 - w0) * wave / nw);
+  t1 = __builtin_amdgcn_readfirstlane(w0 + (w1 - w0) * (wave + 1) / nw);
+}
+
+// The waves of a workgroup meet in LDS, summed in wave order; wave 0 ends
+// with the workgroup's sums.
+template <int T>
+__device__ __forceinline__ void reduce_waves(float (&acc)[T], float (*red)[RG], int wave, int nw, int lane) {
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    if (nw > 1) {
+      red[wave][lane] = acc[j];
+      __syncthreads();
+      if (wave == 0) {
+        float s = red[0][lane];
+        for (int w = 1; w < nw; ++w) s += red[w][lane];
+        acc[j] = s;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Split-K exchange, called by wave 0 of every split of row group rg when
+// ksplit > 1.  Each split publishes its sums and takes a ticket; the last
+// split of the row group adds all of them in split order (so the result does
+// not depend on arrival order), resets the ticket and returns true; the
+// others return false.  Partials and the ticket move only through
+// agent-scope atomic accesses (global stores / loads with sc1 on gfx950,
+// which write through to and read from the point where all XCDs agree);
+// waiting for the stores to complete (vmcnt 0) before the ticket is taken
+// orders them before it, so the split that sees the last ticket reads every
+// partial in full.  No cache-wide write-back or invalidate is needed.
+template <int T>
+__device__ __forceinline__ bool split_exchange(float (&acc)[T], const GemvOut& out, int rg, int ks, int ksplit,
+                                               int lane) {
+  float* my = out.part + ((size_t)rg * ksplit + ks) * T * RG;
+#pragma unroll
+  for (int j = 0; j < T; ++j)
+    __hip_atomic_store(my + j * RG + lane, acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  unsigned ticket = 0;
+  if (lane == 0) ticket = __hip_atomic_fetch_add(out.cnt + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  ticket = __shfl(ticket, 0, 64);
+  if (ticket != (unsigned)(ksplit - 1)) return false;
+  const float* all = out.part + (size_t)rg * ksplit * T * RG;
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    // all loads in flight before the first add; the adds run in split order
+    float pv[16];
+#pragma unroll
+    for (int k2 = 0; k2 < 16; ++k2)
+      pv[k2] = k2 < ksplit ? __hip_atomic_load(all + ((size_t)k2 * T + j) * RG + lane, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)
+                           : 0.0f;
+    float s = 0.0f;
+#pragma unroll
+    for (int k2 = 0; k2 < 16; ++k2)
+      if (k2 < ksplit) s += pv[k2];
+    acc[j] = s;
+  }
+  if (lane == 0) __hip_atomic_store(out.cnt + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return true;
+}
+
+// Epilogue of row group rg (wave 0, whole K summed): store y, or the SwiGLU
+// of lane pairs (row, row + 32) and the digits of the product, or the
+// residual update with the next RMSNorm's statistics and digits.  COH: the
+// results are read by later workgroups of the same kernel (coherent stores,
+// and the residual read coherently).
+template <int QT, int T, int EPI, bool COH>
+__device__ __forceinline__ void gemv_epilogue(const float (&acc)[T], const float (&rn)[T], const Packed& W,
+                                              const GemvOut& out, int rg, int lane) {
+  const int64_t row = (int64_t)rg * RG + lane;
+  const bool rv = row < W.rows;
+#pragma unroll
+  for (int j = 0; j < T; ++j) {
+    if constexpr (EPI == EPI_STORE) {
+      if (rv) st_<COH>(out.y + (size_t)j * out.y_tstride + row, acc[j] * rn[j]);
+    } else if constexpr (EPI == EPI_SWIGLU) {
+      // lanes 0..31: gate rows, lanes 32..63: the matching up rows
+      const float v = acc[j] * rn[j];
+      const float up = xor_lane<32>(v);   // row lane ^ 32
+      const float m = (v / (1.0f + expf(-v))) * up;
+      if (out.y && lane < 32) st_<COH>(out.y + (size_t)j * out.y_tstride + rg * 32 + lane, m);
+      put_digits<COH>(out.next, out.next_qt, j, rg, m, lane < 32);
+    } else {  // EPI_RESID, whole K in this workgroup
+      const float hn = rv ? ld_<COH>(out.y + (size_t)j * out.y_tstride + row) + acc[j] : 0.0f;
+      resid_tail<COH>(j, rg, (int)W.rows, hn, out.y, out.y_tstride, out.norm_w, out.next_qt, out.next,
+                      out.ssq_out, W.nrg());
+    }
+  }
+}
+
 template <int QT, int T, int EPI>
 __global__ __launch_bounds__(512) void k_gemv(Packed W, Act x, NormIn nin, GemvOut out, int ksplit) {
   constexpr int TBY = tile_bytes(QT);
@@ -188,11 +288,8 @@ __global__ __launch_bounds__(512) void k_gemv(Packed W, Act x, NormIn nin, GemvO
   const int nw = blockDim.x >> 6;
   const int rg = blockIdx.x / ksplit, ks = blockIdx.x % ksplit;
   const int nblk = W.nblk(), ntiles = W.ntiles(), full = nblk / TB;
-  const int w0 = ntiles * ks / ksplit, w1 = ntiles * (ks + 1) / ksplit;
-  // tile range of this wave; readfirstlane keeps the loop and the digit
-  // addresses in scalar registers
-  const int t0 = __builtin_amdgcn_readfirstlane(w0 + (w1 - w0) * wave / nw);
-  const int t1 = __builtin_amdgcn_readfirstlane(w0 + (w1 - w0) * (wave + 1) / nw);
+  int t0, t1;
+  wave_tiles(ntiles, ks, ksplit, wave, nw, t0, t1);
   const uint8_t* base = W.w + (size_t)rg * rg_bytes(QT, W.cols);
 
   float acc[T];
@@ -231,78 +328,10 @@ __global__ __launch_bounds__(512) void k_gemv(Packed W, Act x, NormIn nin, GemvO
 #pragma unroll
   for (int j = 0; j < T; ++j) rn[j] = (EPI != EPI_RESID && wave == 0) ? rnorm_finish(rr[j], nin, j) : 1.0f;
 
-  // waves meet in LDS, summed in wave order
-#pragma unroll
-  for (int j = 0; j < T; ++j) {
-    if (nw > 1) {
-      red[wave][lane] = acc[j];
-      __syncthreads();
-      if (wave == 0) {
-        float s = red[0][lane];
-        for (int w = 1; w < nw; ++w) s += red[w][lane];
-        acc[j] = s;
-      }
-      __syncthreads();
-    }
-  }
+  reduce_waves<T>(acc, red, wave, nw, lane);
   if (wave != 0) return;
-
-  if (ksplit > 1) {
-    // Publish this split's sums and take a ticket; the last split of the row
-    // group adds all of them in split order (so the result does not depend on
-    // arrival order) and runs the epilogue.  Partials and the ticket only move
-    // through agent-scope atomic accesses, which are coherent across the XCDs
-    // by themselves; waiting for the stores (vmcnt 0) before taking the ticket
-    // orders them.  No cache-wide write-back or invalidate is needed.
-    float* my = out.part + ((size_t)rg * ksplit + ks) * T * RG;
-#pragma unroll
-    for (int j = 0; j < T; ++j)
-      __hip_atomic_store(my + j * RG + lane, acc[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    __builtin_amdgcn_s_waitcnt(0);
-    __atomic_signal_fence(__ATOMIC_SEQ_CST);
-    unsigned ticket = 0;
-    if (lane == 0) ticket = __hip_atomic_fetch_add(out.cnt + rg, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    ticket = __shfl(ticket, 0, 64);
-    if (ticket != (unsigned)(ksplit - 1)) return;
-    const float* all = out.part + (size_t)rg * ksplit * T * RG;
-#pragma unroll
-    for (int j = 0; j < T; ++j) {
-      // all loads in flight before the first add; the adds run in split order
-      float pv[16];
-#pragma unroll
-      for (int k2 = 0; k2 < 16; ++k2)
-        pv[k2] = k2 < ksplit ? __hip_atomic_load(all + ((size_t)k2 * T + j) * RG + lane, __ATOMIC_RELAXED,
-                                                 __HIP_MEMORY_SCOPE_AGENT)
-                             : 0.0f;
-      float s = 0.0f;
-#pragma unroll
-      for (int k2 = 0; k2 < 16; ++k2)
-        if (k2 < ksplit) s += pv[k2];
-      acc[j] = s;
-    }
-    if (lane == 0) __hip_atomic_store(out.cnt + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-
-  const int64_t row = (int64_t)rg * RG + lane;
-  const bool rv = row < W.rows;
-#pragma unroll
-  for (int j = 0; j < T; ++j) {
-    if constexpr (EPI == EPI_STORE) {
-      if (rv) out.y[(size_t)j * out.y_tstride + row] = acc[j] * rn[j];
-    } else if constexpr (EPI == EPI_SWIGLU) {
-      // lanes 0..31: gate rows, lanes 32..63: the matching up rows
-      const float v = acc[j] * rn[j];
-      const float up = xor_lane<32>(v);   // row lane ^ 32
-      const float m = (v / (1.0f + expf(-v))) * up;
-      if (out.y && lane < 32) out.y[(size_t)j * out.y_tstride + rg * 32 + lane] = m;
-      put_digits(out.next, out.next_qt, j, rg, m, lane < 32);
-    } else {  // EPI_RESID, whole K in this workgroup
-      const float hn = rv ? out.y[(size_t)j * out.y_tstride + row] + acc[j] : 0.0f;
-      resid_tail(j, rg, (int)W.rows, hn, out.y, out.y_tstride, out.norm_w, out.next_qt, out.next,
-                 out.ssq_out, W.nrg());
-    }
-  }
+  if (ksplit > 1 && !split_exchange<T>(acc, out, rg, ks, ksplit, lane)) return;
+  gemv_epilogue<QT, T, EPI, false>(acc, rn, W, out, rg, lane);
 }
 
 

@@ -56,7 +56,7 @@ int override_int(const std::string& name, int dflt) {
 }
 
 bool override_name_ok(const std::string& n) {
-  if (n == "MFMA_MIN_T" || n == "EAGER") return true;
+  if (n == "MFMA_MIN_T" || n == "EAGER" || n == "CHAIN" || n == "CHAIN_MAX") return true;
   static const char* kinds[] = {"G1", "G2", "F1", "F2", "HEAD", "GEMV", "G1P", "G2P", "F1P", "F2P"};
   for (const char* k : kinds)
     if (n == std::string("KS_") + k || n == std::string("W_") + k) return true;
@@ -156,6 +156,12 @@ struct Layout {
   size_t ctrl = 0, h = 0, xa_d = 0, xa_s = 0, xu_d = 0, xu_s = 0, xm_d = 0, xm_s = 0, ssq = 0, y1 = 0,
          xa_md = 0, xu_md = 0, xm_md = 0,
          part = 0, cnt = 0, apart = 0, rope = 0, logits = 0, amax_v = 0, amax_i = 0, kv = 0, dn = 0;
+  // chained decode: digits and statistics of the mixer inputs (the FFN input
+  // keeps xa / ssq), per-product split-K regions, per-layer descriptors and
+  // sync regions
+  size_t xb_d = 0, xb_s = 0, ssq_b = 0, chain_sync = 0;
+  size_t cpart[CHAIN_MAX_PHASES] = {}, ccnt[CHAIN_MAX_PHASES] = {};
+  size_t ccnt_n = 0;      // u32 tickets in each ccnt region
   size_t kv_layer_bytes = 0, dn_layer_bytes = 0;
   size_t wsbytes = 0;
   int64_t g1_rows_max = 0;
@@ -311,6 +317,22 @@ Layout make_layout(const slice_config& c) {
   if (c.has_head) upd(c.tied_head ? L.embed : L.head, L.phead, nullptr, "HEAD");
   L.part = take(part_floats * 4);
   L.cnt = take((size_t)std::max<int64_t>(rg_max, 1) * 4);
+  if (!L.layers.empty()) {
+    L.xb_d = take((size_t)XW * 4 * nblkH);
+    L.xb_s = take((size_t)4 * nblkH);
+    L.ssq_b = take((size_t)(H / RG) * 4);
+    size_t cpf = 0;
+    for (const LayerLayout& ll : L.layers)
+      for (const auto& mp : {std::make_pair(&ll.g1, &ll.pg1), std::make_pair(&ll.g2, &ll.pg2),
+                             std::make_pair(&ll.f1, &ll.pf1), std::make_pair(&ll.f2, &ll.pf2)})
+        if (mp.first->present) cpf = std::max<size_t>(cpf, (size_t)((mp.first->rows + RG - 1) / RG) * mp.second->ks * RG);
+    L.ccnt_n = (size_t)std::max<int64_t>(rg_max, 1);
+    for (int p = 0; p < CHAIN_MAX_PHASES; ++p) {
+      L.cpart[p] = take(cpf * 4);
+      L.ccnt[p] = take(L.ccnt_n * 4);
+    }
+    L.chain_sync = take(L.layers.size() * CHAIN_MAX_PHASES * CHAIN_SYNC_BYTES);
+  }
   if (L.n_attn) {
     L.nchunk = (c.max_seq + ATT_CHUNK - 1) / ATT_CHUNK;
     L.apart = take((size_t)mt * c.q_heads * L.nchunk * (c.head_dim + 2) * 4);
@@ -365,6 +387,16 @@ struct slice {
   template <class X> X* wsp(size_t off) const { return reinterpret_cast<X*>(ws + off); }
   Packed packed(const Mat& m) const { return Packed{w + m.off, m.rows, m.cols, cfg.qtype}; }
   int mx_min_t = 0;   // GEMVs with at least this many tokens use the MFMA products (0: by format and plan)
+  bool chain = false;                 // decode steps run the chained GEMV kernels
+  struct ChainLaunch {
+    int layer;                        // the layer whose mixer it follows
+    ChainArgs args;                   // descriptors (kernel arguments)
+    unsigned grid;                    // workgroups
+    size_t sync;                      // sync region (workspace offset)
+  };
+  std::vector<ChainLaunch> chain_launch;   // in step order
+  Act act_b() const { return Act{wsp<int32_t>(L.xb_d), wsp<float>(L.xb_s), cfg.hidden / QK, nullptr, mx_min_t}; }
+  NormIn norm_b() const { return NormIn{wsp<float>(L.ssq_b), cfg.hidden / RG, 1.0f / (float)cfg.hidden, cfg.eps}; }
   // digits of a step of T tokens; the MFMA layout is written when it may be used
   Act act(size_t d, size_t s_, size_t md, int nblk, int T) const {
     const bool mx = T >= (mx_min_t ? mx_min_t : 2) && L.mt > 1;
@@ -377,6 +409,63 @@ struct slice {
     return NormIn{wsp<float>(L.ssq), cfg.hidden / RG, 1.0f / (float)cfg.hidden, cfg.eps};
   }
 };
+
+// Norm weights of the RMSNorm in front of layer i (past the last layer the
+// digits are not consumed; any valid vector will do): offset in the weights.
+static size_t attn_norm_off(const slice* s, int i) {
+  const Layout& L = s->L;
+  return i < (int)L.layers.size() ? L.layers[i].attn_norm : L.out_norm;
+}
+
+// The mixer of layer i (DeltaNet update or attention) on the G1 output y1;
+// its output digits go to xu.
+static int enqueue_mixer(slice* s, int i, int T, int mode, hipStream_t st) {
+  const slice_config& c = s->cfg;
+  const Layout& L = s->L;
+  const LayerLayout& ll = L.layers[i];
+  float* y1 = s->wsp<float>(L.y1);
+  if (ll.attn) {
+    AttnParams p{};
+    p.y = y1;
+    p.y_stride = ll.g1.rows;
+    p.off_q = ll.off_q; p.off_g = ll.off_g; p.off_k = ll.off_k; p.off_v = ll.off_v;
+    p.q_heads = c.q_heads; p.kv_heads = c.kv_heads; p.hd = c.head_dim; p.rope_dims = c.rope_dims;
+    p.rope_theta = c.rope_theta;
+    p.rope_cs = s->wsp<float>(L.rope);
+    p.qk_norm = c.qk_norm;
+    p.q_norm = reinterpret_cast<const float*>(s->w + ll.q_norm);
+    p.k_norm = reinterpret_cast<const float*>(s->w + ll.k_norm);
+    p.eps = c.eps;
+    uint8_t* kvb = s->ws + L.kv + (size_t)ll.attn_index * L.kv_layer_bytes;
+    p.kc = reinterpret_cast<__half*>(kvb);
+    p.vc = reinterpret_cast<__half*>(kvb + (size_t)c.kv_heads * c.max_seq * c.head_dim * 2);
+    p.max_seq = c.max_seq;
+    p.ctrl = s->ctrl();
+    p.part = s->wsp<float>(L.apart);
+    p.nchunk = L.nchunk;
+    p.u_out = nullptr;
+    p.next = s->act_u(T);
+    p.next_qt = c.qtype;
+    HIPCHK(launch_attention(p, T, st));
+  } else {
+    DnParams p{};
+    p.y = y1;
+    p.y_stride = ll.g1.rows;
+    p.off_q = ll.off_q; p.off_k = ll.off_k; p.off_v = ll.off_v;
+    p.off_a = ll.off_a; p.off_b = ll.off_b; p.off_z = ll.off_z;
+    p.heads = c.dn_heads; p.dk = c.dn_dk; p.dv = c.dn_dv;
+    p.a_scale = c.dn_a_scale; p.a_bias = c.dn_a_bias; p.b_scale = c.dn_b_scale; p.z_scale = c.dn_z_scale;
+    p.state = reinterpret_cast<float*>(s->ws + L.dn + (size_t)ll.dn_index * L.dn_layer_bytes);
+    p.nslots = L.nslots;
+    p.mode = mode;
+    p.ctrl = s->ctrl();
+    p.u_out = nullptr;
+    p.next = s->act_u(T);
+    p.next_qt = c.qtype;
+    HIPCHK(launch_deltanet(p, T, st));
+  }
+  return SLICE_OK;
+}
 
 // One step with T tokens: entry, every layer, exit.  Reads the input/output
 // pointers from the control block so a captured graph serves any buffers.
@@ -395,18 +484,55 @@ static int enqueue_step(slice* s, int T, int mode, hipStream_t st, Prof* prof = 
   float* y1 = s->wsp<float>(L.y1);
   Ctrl* ctrl = s->ctrl();
   const int nlay = (int)L.layers.size();
-  // norm weights of the RMSNorm in front of layer i (past the last layer the
-  // digits are not consumed; any valid vector will do)
-  auto attn_norm_of = [&](int i) -> const float* {
-    if (i < nlay) return reinterpret_cast<const float*>(s->w + L.layers[i].attn_norm);
-    return reinterpret_cast<const float*>(s->w + L.out_norm);
-  };
-  // entry: boundary vector -> h, digits of attn_norm(first layer) * h
-  SLQ_MARK(-1);
-  if (only < 0) HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, nullptr, ctrl, H, T, H, h, attn_norm_of(0), qt, s->act_a(T), ssq, st));
-  SLQ_MARK(SLICE_OP_ENTRY);
+  auto norm_at = [&](size_t off) { return reinterpret_cast<const float*>(s->w + off); };
   float* part = s->wsp<float>(L.part);
   unsigned* cnt = s->wsp<unsigned>(L.cnt);
+  auto g1_out = [&]() {
+    GemvOut o{};
+    o.kind = EPI_STORE;
+    o.y = y1;
+    o.part = part;
+    o.cnt = cnt;
+    return o;
+  };
+
+  if (decode && s->chain && nlay > 0 && (only < 0 || only == SLICE_OP_CHAIN)) {
+    // Chained decode: entry, the first layer's input projections, then per
+    // layer its mixer and one kernel for the products after it (mixer output,
+    // gate/up, down, the next layer's input projections), then the exit.
+    if (only < 0) {
+      SLQ_MARK(-1);
+      HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, nullptr, ctrl, H, 1, H, h, norm_at(attn_norm_off(s, 0)), qt,
+                                 s->act_b(), s->wsp<float>(L.ssq_b), st));
+      SLQ_MARK(SLICE_OP_ENTRY);
+      const LayerLayout& l0 = L.layers[0];
+      GemvOut o = g1_out();
+      o.y_tstride = l0.g1.rows;
+      HIPCHK(launch_gemv(s->packed(l0.g1), 1, s->act_b(), s->norm_b(), o, l0.pg1.ks, l0.pg1.w, st));
+      SLQ_MARK(l0.attn ? SLICE_OP_ATT_IN : SLICE_OP_DN_IN);
+    }
+    for (int i = 0; i < nlay; ++i) {
+      if (only < 0) {
+        int rc = enqueue_mixer(s, i, 1, DN_DECODE, st);
+        if (rc) return rc;
+        SLQ_MARK(L.layers[i].attn ? SLICE_OP_ATTENTION : SLICE_OP_DELTANET);
+      }
+      for (const slice::ChainLaunch& cl : s->chain_launch) {
+        if (cl.layer != i) continue;
+        HIPCHK(launch_chain(qt, cl.args, cl.grid, s->w, s->ws, reinterpret_cast<unsigned*>(s->ws + cl.sync), ctrl, st));
+        SLQ_MARK(SLICE_OP_CHAIN);
+      }
+    }
+    if (only < 0) HIPCHK(launch_store_out(h, 1, H, nullptr, c.io_fp32, ctrl, 1, st));
+    SLQ_MARK(SLICE_OP_EXIT);
+    return SLICE_OK;
+  }
+  if (only == SLICE_OP_CHAIN) return fail(SLICE_EINVAL, "the slice does not run chained products");
+
+  // entry: boundary vector -> h, digits of attn_norm(first layer) * h
+  SLQ_MARK(-1);
+  if (only < 0) HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, nullptr, ctrl, H, T, H, h, norm_at(attn_norm_off(s, 0)), qt, s->act_a(T), ssq, st));
+  SLQ_MARK(SLICE_OP_ENTRY);
   for (int i = 0; i < nlay; ++i) {
     const LayerLayout& ll = L.layers[i];
     const int k_in = ll.attn ? SLICE_OP_ATT_IN : SLICE_OP_DN_IN;
@@ -415,62 +541,20 @@ static int enqueue_step(slice* s, int T, int mode, hipStream_t st, Prof* prof = 
     // mixer input projections: G1 = [q|k|v|a|b|z] or [q|g|k|v] of RMSNorm(h)
     if (only < 0 || only == k_in) {
       const Packed W = s->packed(ll.g1);
-      GemvOut o{};
-      o.kind = EPI_STORE;
-      o.y = y1;
+      GemvOut o = g1_out();
       o.y_tstride = W.rows;
-      o.part = part;
-      o.cnt = cnt;
       const Plan pl = pass ? ll.qg1 : ll.pg1;
       HIPCHK(launch_gemv(W, T, s->act_a(T), s->norm_h(), o, pl.ks, pl.w, st));
-      SLQ_MARK(ll.attn ? SLICE_OP_ATT_IN : SLICE_OP_DN_IN);
+      SLQ_MARK(k_in);
     }
-    if (only >= 0 && only != k_mix) {
-    } else if (ll.attn) {
-      AttnParams p{};
-      p.y = y1;
-      p.y_stride = ll.g1.rows;
-      p.off_q = ll.off_q; p.off_g = ll.off_g; p.off_k = ll.off_k; p.off_v = ll.off_v;
-      p.q_heads = c.q_heads; p.kv_heads = c.kv_heads; p.hd = c.head_dim; p.rope_dims = c.rope_dims;
-      p.rope_theta = c.rope_theta;
-      p.rope_cs = s->wsp<float>(L.rope);
-      p.qk_norm = c.qk_norm;
-      p.q_norm = reinterpret_cast<const float*>(s->w + ll.q_norm);
-      p.k_norm = reinterpret_cast<const float*>(s->w + ll.k_norm);
-      p.eps = c.eps;
-      uint8_t* kvb = s->ws + L.kv + (size_t)ll.attn_index * L.kv_layer_bytes;
-      p.kc = reinterpret_cast<__half*>(kvb);
-      p.vc = reinterpret_cast<__half*>(kvb + (size_t)c.kv_heads * c.max_seq * c.head_dim * 2);
-      p.max_seq = c.max_seq;
-      p.ctrl = ctrl;
-      p.part = s->wsp<float>(L.apart);
-      p.nchunk = L.nchunk;
-      p.u_out = nullptr;
-      p.next = s->act_u(T);
-      p.next_qt = qt;
-      HIPCHK(launch_attention(p, T, st));
-      SLQ_MARK(SLICE_OP_ATTENTION);
-    } else {
-      DnParams p{};
-      p.y = y1;
-      p.y_stride = ll.g1.rows;
-      p.off_q = ll.off_q; p.off_k = ll.off_k; p.off_v = ll.off_v;
-      p.off_a = ll.off_a; p.off_b = ll.off_b; p.off_z = ll.off_z;
-      p.heads = c.dn_heads; p.dk = c.dn_dk; p.dv = c.dn_dv;
-      p.a_scale = c.dn_a_scale; p.a_bias = c.dn_a_bias; p.b_scale = c.dn_b_scale; p.z_scale = c.dn_z_scale;
-      p.state = reinterpret_cast<float*>(s->ws + L.dn + (size_t)ll.dn_index * L.dn_layer_bytes);
-      p.nslots = L.nslots;
-      p.mode = mode;
-      p.ctrl = ctrl;
-      p.u_out = nullptr;
-      p.next = s->act_u(T);
-      p.next_qt = qt;
-      HIPCHK(launch_deltanet(p, T, st));
-      SLQ_MARK(SLICE_OP_DELTANET);
+    if (only < 0 || only == k_mix) {
+      int rc = enqueue_mixer(s, i, T, mode, st);
+      if (rc) return rc;
+      SLQ_MARK(k_mix);
     }
     // residual update after the mixer: h += W_o u, then digits for the next RMSNorm
-    const float* nw_after_mixer = c.ffn ? reinterpret_cast<const float*>(s->w + ll.ffn_norm) : attn_norm_of(i + 1);
-    auto residual = [&](const Mat& m, Act in, const float* next_norm, const Plan& pl) -> int {
+    const size_t nw_after_mixer = c.ffn ? ll.ffn_norm : attn_norm_off(s, i + 1);
+    auto residual = [&](const Mat& m, Act in, size_t next_norm, const Plan& pl) -> int {
       const Packed W = s->packed(m);
       GemvOut o{};
       o.kind = EPI_RESID;
@@ -479,7 +563,7 @@ static int enqueue_step(slice* s, int T, int mode, hipStream_t st, Prof* prof = 
       o.next = s->act_a(T);
       o.next_qt = qt;
       o.ssq_out = ssq;
-      o.norm_w = next_norm;
+      o.norm_w = norm_at(next_norm);
       o.part = part;
       o.cnt = cnt;
       HIPCHK(launch_gemv(W, T, in, NormIn{nullptr, 0, 0.f, 0.f}, o, pl.ks, pl.w, st));
@@ -503,7 +587,7 @@ static int enqueue_step(slice* s, int T, int mode, hipStream_t st, Prof* prof = 
       SLQ_MARK(SLICE_OP_FFN_IN);
     }
     if (c.ffn && (only < 0 || only == SLICE_OP_FFN_OUT)) {
-      rc = residual(ll.f2, s->act_m(T), attn_norm_of(i + 1), pass ? ll.qf2 : ll.pf2);
+      rc = residual(ll.f2, s->act_m(T), attn_norm_off(s, i + 1), pass ? ll.qf2 : ll.pf2);
       if (rc) return rc;
       SLQ_MARK(SLICE_OP_FFN_OUT);
     }
@@ -514,6 +598,113 @@ static int enqueue_step(slice* s, int T, int mode, hipStream_t st, Prof* prof = 
   SLQ_MARK(SLICE_OP_EXIT);
   return SLICE_OK;
 #undef SLQ_MARK
+}
+
+// Descriptors of the chained products after each layer's mixer (decode, one
+// token): [mixer output (+ residual), gate/up + SwiGLU, down (+ residual),
+// next layer's input projections], with the launch shapes of the separate
+// kernels, so that results are the same bit for bit.  The mixer output writes
+// the FFN input's digits to xa (statistics in ssq), the down projection the
+// next mixer input's digits to xb (ssq_b): every buffer a chain hands on is
+// written once per launch.
+static void build_chains(slice* s) {
+  const slice_config& c = s->cfg;
+  const Layout& L = s->L;
+  const int H = c.hidden, nblkH = H / QK;
+  const int nlay = (int)L.layers.size();
+  s->chain_launch.clear();
+  // products per chained kernel (tuning; 4 = all of a layer's)
+  const int per = clampi(override_int("CHAIN_MAX", CHAIN_MAX_PHASES), 1, CHAIN_MAX_PHASES);
+  for (int i = 0; i < nlay; ++i) {
+    const LayerLayout& ll = L.layers[i];
+    ChainPhase ph[CHAIN_MAX_PHASES];
+    int n = 0;
+    auto add = [&](const Mat& m, const Plan& pl, int epi) -> ChainPhase& {
+      ChainPhase& q = ph[n];
+      q = ChainPhase{};
+      q.w_off = (int64_t)m.off;
+      q.rows = m.rows;
+      q.cols = m.cols;
+      q.ssq_off = q.y_off = q.nd_off = q.ns_off = q.ssq_out_off = q.norm_w_off = -1;
+      q.part_off = (int64_t)L.cpart[n % per];
+      q.cnt_off = (int64_t)L.ccnt[n % per];
+      q.qt = c.qtype;
+      q.ksplit = pl.ks;
+      q.nwg = (int)((m.rows + RG - 1) / RG) * pl.ks;
+      q.epi = epi;
+      q.w = pl.w;
+      ++n;
+      return q;
+    };
+    auto input = [&](ChainPhase& q, size_t d, size_t sc, int nblk, int64_t ssq) {
+      q.xd_off = (int64_t)d;
+      q.xs_off = (int64_t)sc;
+      q.x_nblk = nblk;
+      q.ssq_off = ssq;
+      q.n_part = H / RG;
+      q.inv_n = 1.0f / (float)H;
+      q.eps = c.eps;
+    };
+    auto resid = [&](ChainPhase& q, size_t nd, size_t ns, size_t ssq_out, size_t norm_w) {
+      q.y_off = (int64_t)L.h;
+      q.y_tstride = H;
+      q.nd_off = (int64_t)nd;
+      q.ns_off = (int64_t)ns;
+      q.n_nblk = nblkH;
+      q.ssq_out_off = (int64_t)ssq_out;
+      q.norm_w_off = (int64_t)norm_w;
+    };
+    const int nblkU = (L.nu + QK - 1) / QK;
+    ChainPhase& g2 = add(ll.g2, ll.pg2, EPI_RESID);
+    input(g2, L.xu_d, L.xu_s, nblkU, -1);
+    if (c.ffn) {
+      resid(g2, L.xa_d, L.xa_s, L.ssq, ll.ffn_norm);
+      ChainPhase& f1 = add(ll.f1, ll.pf1, EPI_SWIGLU);
+      input(f1, L.xa_d, L.xa_s, nblkH, (int64_t)L.ssq);
+      f1.nd_off = (int64_t)L.xm_d;
+      f1.ns_off = (int64_t)L.xm_s;
+      f1.n_nblk = c.ffn / QK;
+      ChainPhase& f2 = add(ll.f2, ll.pf2, EPI_RESID);
+      input(f2, L.xm_d, L.xm_s, c.ffn / QK, -1);
+      resid(f2, L.xb_d, L.xb_s, L.ssq_b, attn_norm_off(s, i + 1));
+    } else {
+      resid(g2, L.xb_d, L.xb_s, L.ssq_b, attn_norm_off(s, i + 1));
+    }
+    if (i + 1 < nlay) {
+      const LayerLayout& nx = L.layers[i + 1];
+      ChainPhase& g1 = add(nx.g1, nx.pg1, EPI_STORE);
+      input(g1, L.xb_d, L.xb_s, nblkH, (int64_t)L.ssq_b);
+      g1.y_off = (int64_t)L.y1;
+      g1.y_tstride = nx.g1.rows;
+    }
+    for (int first = 0; first < n; first += per) {
+      slice::ChainLaunch cl{};
+      cl.layer = i;
+      cl.args.nph = std::min(per, n - first);
+      cl.args.first_wg[0] = 0;
+      for (int k = 0; k < cl.args.nph; ++k) {
+        const ChainPhase& q = ph[first + k];
+        cl.args.ph[k] = q;
+        cl.args.first_wg[k + 1] = cl.args.first_wg[k] + q.nwg;
+        const int nrg = (int)((q.rows + RG - 1) / RG);
+        cl.args.gsize[k] = (nrg + 31) / 32;   // at most 32 completion groups
+      }
+      cl.grid = (unsigned)cl.args.first_wg[cl.args.nph];
+      cl.sync = L.chain_sync + ((size_t)i * CHAIN_MAX_PHASES + first / per) * CHAIN_SYNC_BYTES;
+      s->chain_launch.push_back(cl);
+    }
+  }
+}
+
+// Chained decode needs every product's plan within the chain kernel's four
+// waves per workgroup.
+static bool chains_possible(const slice* s) {
+  // the RMSNorm statistics must fit the coherent two-load fetch (rnorm_fetch)
+  if (s->cfg.hidden / RG > 128) return false;
+  for (const LayerLayout& ll : s->L.layers)
+    for (const Plan* p : {&ll.pg1, &ll.pg2, &ll.pf1, &ll.pf2})
+      if (p->w > 4) return false;
+  return !s->L.layers.empty();
 }
 
 static int run_step(slice* s, int T, int mode, const void* in, void* out, hipStream_t st) {
@@ -784,6 +975,8 @@ int slice_load(const slice_config* cfg, void* weights_dev, void* workspace_dev, 
   if (he == hipSuccess) he = hipMemsetAsync(s->ws, 0, s->L.wsbytes, S(stream));
   if (he == hipSuccess && s->L.n_attn && cfg->rope_dims > 0)
     he = launch_rope_table(s->wsp<float>(s->L.rope), cfg->max_seq, cfg->rope_dims, cfg->rope_theta, S(stream));
+  s->chain = chains_possible(s) && override_int("CHAIN", 1) != 0;
+  if (s->chain) build_chains(s);
   if (he == hipSuccess) he = hipStreamCreate(&s->cap);
   if (he != hipSuccess) {
     delete s;
@@ -885,6 +1078,13 @@ int slice_reset(slice_t* s, int kv_len, void* stream) {
   if (!s) return fail(SLICE_EINVAL, "null slice");
   if (kv_len < 0 || (s->L.n_attn && kv_len > s->cfg.max_seq)) return fail(SLICE_ERANGE, "kv_len out of range");
   HIPCHK(launch_ctrl_set(s->ctrl(), kv_len, s->cur, S(stream)));
+  if (s->chain) {
+    HIPCHK(launch_chain_reset(reinterpret_cast<unsigned*>(s->ws + s->L.chain_sync),
+                              s->L.layers.size() * CHAIN_MAX_PHASES * CHAIN_SYNC_BYTES / 4, s->ctrl(), S(stream)));
+    // split-K tickets of the chained products (zero unless a wait gave up mid-exchange)
+    for (int p = 0; p < CHAIN_MAX_PHASES; ++p)
+      HIPCHK(launch_fill_zero_u32(reinterpret_cast<uint32_t*>(s->ws + s->L.ccnt[p]), s->L.ccnt_n, S(stream)));
+  }
   s->pos = kv_len;
   s->pending = 0;
   return SLICE_OK;
@@ -932,7 +1132,8 @@ int slice_decode_profiled(slice_t* s, const void* in, void* out, int* op_kind, f
 int slice_run_gemv_op(slice_t* s, int op_kind, void* stream) {
   if (!s) return fail(SLICE_EINVAL, "null slice");
   if (op_kind != SLICE_OP_DN_IN && op_kind != SLICE_OP_DN_OUT && op_kind != SLICE_OP_ATT_IN &&
-      op_kind != SLICE_OP_ATT_OUT && op_kind != SLICE_OP_FFN_IN && op_kind != SLICE_OP_FFN_OUT)
+      op_kind != SLICE_OP_ATT_OUT && op_kind != SLICE_OP_FFN_IN && op_kind != SLICE_OP_FFN_OUT &&
+      op_kind != SLICE_OP_CHAIN)
     return fail(SLICE_EINVAL, "slice_run_gemv_op: not a GEMV op kind");
   if (s->pending) return fail(SLICE_ESTATE, "slice_run_gemv_op: a verify is waiting for slice_commit");
   return enqueue_step(s, 1, DN_DECODE, S(stream), nullptr, op_kind);
@@ -1003,6 +1204,17 @@ int slice_head_argmax(slice_t* s, const void* in, int32_t* tok, float* logits, v
 }
 
 int slice_position(const slice_t* s) { return s ? s->pos : -1; }
+
+int slice_sync_check(slice_t* s, void* stream) {
+  if (!s) return fail(SLICE_EINVAL, "null slice");
+  HIPCHK(hipStreamSynchronize(S(stream)));
+  int err = 0;
+  HIPCHK(hipMemcpy(&err, &s->ctrl()->err, sizeof(int), hipMemcpyDeviceToHost));
+  if (err)
+    return fail(SLICE_EHIP, "a bounded wait between chained products gave up; outputs since the last "
+                            "slice_reset are invalid (slice_reset clears the condition)");
+  return SLICE_OK;
+}
 
 void slice_free(slice_t* s) {
   if (!s) return;
