@@ -119,6 +119,73 @@ int slq_gemv_noalloc(int qtype, const void *packed_dev, int64_t rows, int64_t co
                      const float *x_dev, float *y_dev, void *stream);
 
 /* ------------------------------------------------------------------------ */
+/* Mixers on caller buffers (kernel level)                                   */
+/* ------------------------------------------------------------------------ */
+
+/* Gated DeltaNet, the hybrid's linear-attention layers (ChatTorrent README,
+ * "What it can run"), one token after the other as the pages' engine runs
+ * the recurrence (SwarmLLM README, bench paragraph).  Per head h and token t:
+ *   q^ = q / sqrt(sum q^2 + 1e-6), k^ likewise; alpha = sigmoid(a),
+ *   beta = sigmoid(b); S <- alpha S (I - beta k^ k^T) + beta v k^T;
+ *   o = S q^; out = o * sigmoid(z) elementwise.
+ * in_dev: fp32 [T][ q (heads x dk) | k (heads x dk) | v (heads x dv) |
+ *   a (heads) | b (heads) | z (heads x dv) ]: the pre-activations of the decay,
+ *   write strength and output gate are inputs here (in a slice they come from
+ *   the layer's projections).  state_dev: fp32 heads x dv x dk in the
+ *   library's layout (slq_dn_state_layout converts), read and updated in place
+ *   to the state after token T-1.  out_dev: fp32 [T][heads x dv].
+ * T in 1..16; dk in {32, 64, 96, 128}; dv a multiple of 32.  The same kernel
+ * as a slice's decode step.  Errors: SLICE_ESHAPE, SLICE_ERANGE (T),
+ * SLICE_EINVAL (null pointer); nothing is enqueued then.                     */
+int slq_dn_step(int heads, int dk, int dv, int T, const float *in_dev, float *state_dev, float *out_dev,
+                void *stream);
+
+/* Convert a DeltaNet state between canonical fp32 [heads][dv][dk] (S[h][i][j]:
+ * i indexes values, j keys) and the library's layout used by slq_dn_step.
+ * to_lib != 0: canon_dev -> lib_dev, else lib_dev -> canon_dev.             */
+int slq_dn_state_layout(int heads, int dk, int dv, float *canon_dev, float *lib_dev, int to_lib, void *stream);
+
+/* Decode attention over an fp16 KV cache: the hybrid's full-attention layers
+ * (QK-norm, RoPE on part of each head, sigmoid output gate) or Llama-style GQA
+ * (ChatTorrent README, "What it can run"), each stage keeping its own cache
+ * ("Unstable Legion", "Splitting the workload").                          */
+typedef struct slq_attn_desc {
+    int32_t q_heads, kv_heads, head_dim; /* query head h reads KV head h / (q_heads / kv_heads) */
+    int32_t rope_dims;                   /* entries 0..rope_dims-1 rotated in pairs (i, i + rope_dims/2) */
+    double  rope_theta;                  /* angle pos * theta^(-2i / rope_dims), fp64            */
+    int32_t qk_norm;                     /* RMSNorm of every q and k head before RoPE           */
+    int32_t has_gate;                    /* output multiplied by sigmoid(g)                      */
+    float   eps;                         /* QK-norm epsilon                                      */
+    int32_t max_seq;                     /* cache rows (multiple of 64)                          */
+    const float *q_norm_dev, *k_norm_dev;/* [head_dim] fp32 norm weights (qk_norm only)          */
+} slq_attn_desc;
+
+/* Workspace for T tokens (the RoPE table, then split partials); 0 for an
+ * invalid descriptor or T outside 1..16.                                    */
+size_t slq_attn_workspace_bytes(const slq_attn_desc *d, int T);
+
+/* Build the RoPE table at the start of ws_dev (once per workspace). */
+int slq_attn_prepare(const slq_attn_desc *d, void *ws_dev, size_t ws_bytes, void *stream);
+
+/* T tokens at positions pos .. pos+T-1: in_dev fp32 [T][ q (q_heads x hd) |
+ * g (q_heads x hd, if has_gate) | k (kv_heads x hd) | v (kv_heads x hd) ].
+ * Appends the T new K/V rows (QK-norm, RoPE, fp16 rounding) to the caches at
+ * pos .. pos+T-1; query t attends causally to rows 0 .. pos+t with scale
+ * 1/sqrt(head_dim).  out_dev: fp32 [T][q_heads x hd] (o, or o * sigmoid(g)).
+ * k_cache_dev / v_cache_dev: kv_heads x max_seq x head_dim fp16 each, in the
+ * library's layout (slq_kv_layout converts).  ws_dev: slq_attn_workspace_bytes
+ * bytes, prepared by slq_attn_prepare for this descriptor.  Errors:
+ * SLICE_ESHAPE (descriptor), SLICE_ERANGE (T or positions), SLICE_EINVAL.    */
+int slq_attn_decode(const slq_attn_desc *d, int T, int pos, const float *in_dev, uint16_t *k_cache_dev,
+                    uint16_t *v_cache_dev, float *out_dev, void *ws_dev, size_t ws_bytes, void *stream);
+
+/* Copy rows [0, rows) between canonical fp16 [kv_heads][rows][head_dim] K and
+ * V arrays and caches in the library's layout (to_cache != 0: into the
+ * caches).                                                                   */
+int slq_kv_layout(int kv_heads, int max_seq, int head_dim, int rows, uint16_t *k_canon_dev, uint16_t *v_canon_dev,
+                  uint16_t *k_cache_dev, uint16_t *v_cache_dev, int to_cache, void *stream);
+
+/* ------------------------------------------------------------------------ */
 /* Slice executor                                                            */
 /* ------------------------------------------------------------------------ */
 

@@ -13,11 +13,11 @@ import ctypes
 import numpy as np
 import torch
 
-from ._native import (Q4_0, Q8_0, TENSOR_IDS, SliceConfig, SliceError, check, lib)  # noqa: F401
+from ._native import (Q4_0, Q8_0, TENSOR_IDS, AttnDesc, SliceConfig, SliceError, check, lib)  # noqa: F401
 
 __all__ = ["Q4_0", "Q8_0", "SliceConfig", "SliceError", "Slice", "make_config", "tensor_info",
            "packed_bytes", "repack", "dequant", "gemv", "gemv_workspace_bytes", "debug_override",
-           "overrides", "lib"]
+           "overrides", "dn_step", "dn_state_to_lib", "dn_state_from_lib", "AttnDecoder", "lib"]
 
 
 def _stream(stream=None) -> ctypes.c_void_p:
@@ -91,6 +91,87 @@ def overrides(**kw):
     finally:
         for k in kw:
             debug_override(k, -1)
+
+
+# ------------------------------------------------- mixers on caller buffers
+
+def dn_state_to_lib(S: torch.Tensor, stream=None) -> torch.Tensor:
+    """Canonical fp32 [heads][dv][dk] state (device) -> the library's layout."""
+    heads, dv, dk = S.shape
+    S = S.contiguous()
+    out = torch.empty_like(S)
+    check(lib().slq_dn_state_layout(heads, dk, dv, _ptr(S), _ptr(out), 1, _stream(stream)))
+    return out
+
+
+def dn_state_from_lib(S_lib: torch.Tensor, heads: int, dk: int, dv: int, stream=None) -> torch.Tensor:
+    out = torch.empty((heads, dv, dk), dtype=torch.float32, device=S_lib.device)
+    check(lib().slq_dn_state_layout(heads, dk, dv, _ptr(out), _ptr(S_lib), 0, _stream(stream)))
+    return out
+
+
+def dn_step(heads: int, dk: int, dv: int, inp: torch.Tensor, state_lib: torch.Tensor,
+            out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """T Gated DeltaNet tokens (slq_dn_step): inp fp32 [T][q|k|v|a|b|z], state in the
+    library's layout, updated in place.  Returns out fp32 [T][heads*dv]."""
+    T = inp.shape[0]
+    if out is None:
+        out = torch.empty((T, heads * dv), dtype=torch.float32, device=inp.device)
+    check(lib().slq_dn_step(heads, dk, dv, T, _ptr(inp), _ptr(state_lib), _ptr(out), _stream(stream)))
+    return out
+
+
+class AttnDecoder:
+    """Decode attention on caller buffers (slq_attn_decode): the descriptor,
+    the workspace (RoPE table, partials) and fp16 K/V caches in the library's
+    layout, all device memory from torch."""
+
+    def __init__(self, q_heads, kv_heads, head_dim, rope_dims, rope_theta, qk_norm, has_gate, eps, max_seq,
+                 q_norm=None, k_norm=None, t_max=16, device="cuda", stream=None):
+        self.device = torch.device(device)
+        self.q_norm = None if q_norm is None else torch.as_tensor(q_norm, dtype=torch.float32).to(self.device)
+        self.k_norm = None if k_norm is None else torch.as_tensor(k_norm, dtype=torch.float32).to(self.device)
+        d = AttnDesc()
+        d.q_heads, d.kv_heads, d.head_dim, d.rope_dims = q_heads, kv_heads, head_dim, rope_dims
+        d.rope_theta, d.qk_norm, d.has_gate, d.eps, d.max_seq = float(rope_theta), int(qk_norm), int(has_gate), \
+            float(eps), max_seq
+        d.q_norm_dev = self.q_norm.data_ptr() if self.q_norm is not None else None
+        d.k_norm_dev = self.k_norm.data_ptr() if self.k_norm is not None else None
+        self.desc = d
+        n = int(lib().slq_attn_workspace_bytes(ctypes.byref(d), t_max))
+        if n == 0:
+            check(-2)
+        self.ws = torch.empty(n, dtype=torch.uint8, device=self.device)
+        check(lib().slq_attn_prepare(ctypes.byref(d), _ptr(self.ws), n, _stream(stream)))
+        shape = (kv_heads * max_seq * head_dim,)
+        self.kc = torch.zeros(shape, dtype=torch.int16, device=self.device)
+        self.vc = torch.zeros(shape, dtype=torch.int16, device=self.device)
+
+    def set_kv(self, K: torch.Tensor, V: torch.Tensor, stream=None):
+        """Rows [0, n) from canonical fp16 [kv_heads][n][head_dim]."""
+        K = K.to(self.device).contiguous().view(torch.int16)
+        V = V.to(self.device).contiguous().view(torch.int16)
+        d = self.desc
+        check(lib().slq_kv_layout(d.kv_heads, d.max_seq, d.head_dim, K.shape[1], _ptr(K), _ptr(V), _ptr(self.kc),
+                                  _ptr(self.vc), 1, _stream(stream)))
+
+    def get_kv(self, rows: int, stream=None):
+        d = self.desc
+        K = torch.empty((d.kv_heads, rows, d.head_dim), dtype=torch.float16, device=self.device)
+        V = torch.empty_like(K)
+        check(lib().slq_kv_layout(d.kv_heads, d.max_seq, d.head_dim, rows, _ptr(K), _ptr(V), _ptr(self.kc),
+                                  _ptr(self.vc), 0, _stream(stream)))
+        return K, V
+
+    def decode(self, inp: torch.Tensor, pos: int, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+        """inp fp32 [T][q|g|k|v] at positions pos..pos+T-1 -> out fp32 [T][q_heads*head_dim]."""
+        T = inp.shape[0]
+        d = self.desc
+        if out is None:
+            out = torch.empty((T, d.q_heads * d.head_dim), dtype=torch.float32, device=self.device)
+        check(lib().slq_attn_decode(ctypes.byref(d), T, pos, _ptr(inp), _ptr(self.kc), _ptr(self.vc), _ptr(out),
+                                    _ptr(self.ws), self.ws.numel(), _stream(stream)))
+        return out
 
 
 # ------------------------------------------------------------------- slice

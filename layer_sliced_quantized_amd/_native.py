@@ -46,6 +46,15 @@ class SliceConfig(ctypes.Structure):
     ]
 
 
+class AttnDesc(ctypes.Structure):
+    _fields_ = [
+        ("q_heads", ctypes.c_int32), ("kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+        ("rope_dims", ctypes.c_int32), ("rope_theta", ctypes.c_double),
+        ("qk_norm", ctypes.c_int32), ("has_gate", ctypes.c_int32), ("eps", ctypes.c_float),
+        ("max_seq", ctypes.c_int32), ("q_norm_dev", ctypes.c_void_p), ("k_norm_dev", ctypes.c_void_p),
+    ]
+
+
 class SliceError(RuntimeError):
     def __init__(self, code: int, msg: str):
         super().__init__(f"libslq error {code}: {msg}")
@@ -66,6 +75,12 @@ _SIGS = {
     "slq_gemv_workspace_bytes": (_SZ, [_I, _I64, _I64, _I]),
     "slq_gemv": (_I, [_I, _V, _I64, _I64, _I, _V, _V, _V, _SZ, _V]),
     "slq_gemv_noalloc": (_I, [_I, _V, _I64, _I64, _I, _V, _V, _V]),
+    "slq_dn_step": (_I, [_I, _I, _I, _I, _V, _V, _V, _V]),
+    "slq_dn_state_layout": (_I, [_I, _I, _I, _V, _V, _I, _V]),
+    "slq_attn_workspace_bytes": (_SZ, [ctypes.POINTER(AttnDesc), _I]),
+    "slq_attn_prepare": (_I, [ctypes.POINTER(AttnDesc), _V, _SZ, _V]),
+    "slq_attn_decode": (_I, [ctypes.POINTER(AttnDesc), _I, _I, _V, _V, _V, _V, _V, _SZ, _V]),
+    "slq_kv_layout": (_I, [_I, _I, _I, _I, _V, _V, _V, _V, _I, _V]),
     "slice_weights_bytes": (_SZ, [ctypes.POINTER(SliceConfig)]),
     "slice_workspace_bytes": (_SZ, [ctypes.POINTER(SliceConfig)]),
     "slice_load": (_I, [ctypes.POINTER(SliceConfig), _V, _V, _V, ctypes.POINTER(_V)]),

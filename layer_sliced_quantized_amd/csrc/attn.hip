@@ -136,7 +136,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   if (pair >= p.kv_heads * p.nchunk) return;
   const int g = pair / p.nchunk, c = pair % p.nchunk;
   const int h0 = (g * nsub + sub) * GRP;            // first query head of this workgroup
-  const int p0 = p.ctrl->pos;
+  const int p0 = p.ctrl ? p.ctrl->pos : p.pos;
   const int r0 = c * C;
   if (r0 > p0 + T - 1) return;
   const int tid = threadIdx.x;
@@ -334,7 +334,7 @@ __global__ __launch_bounds__(64 * CW) void k_attn_combine(AttnParams p) {
   const int d = (blockIdx.x % ndg) * 64 + lane;
   // the gate input does not depend on the position: request it first
   const float gz = p.off_g >= 0 && w == 0 ? p.y[(size_t)t * p.y_stride + p.off_g + h * p.hd + d] : 0.0f;
-  const int P = p.ctrl->pos + t;
+  const int P = (p.ctrl ? p.ctrl->pos : p.pos) + t;
   const int nc = P / ATT_CHUNK + 1;
   const int stride = p.hd + 2;
   const float* base = p.part + ((size_t)t * p.q_heads + h) * p.nchunk * stride;
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(64 * CW) void k_attn_combine(AttnParams p) {
   const int nu = p.q_heads * p.hd;
   if (p.u_out) p.u_out[(size_t)t * nu + h * p.hd + d] = o;
   const int blk = (h * p.hd + d) / QK;
-  put_digits(p.next, p.next_qt, t, blk, o, true);
+  if (p.next.xd) put_digits(p.next, p.next_qt, t, blk, o, true);
 }
 
 hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {

@@ -88,7 +88,7 @@ __global__ __launch_bounds__(256) void k_deltanet(DnParams p, int T) {
     z1 = p.y[p.off_z + h * p.dv + i];
   }
 
-  const int cur = p.ctrl->cur;
+  const int cur = p.ctrl ? p.ctrl->cur : 0;
   const size_t hs = (size_t)DK * p.dv;
   const float* S_in = p.state + ((size_t)cur * p.heads + h) * hs;
   const int j0 = part * DKP;
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(256) void k_deltanet(DnParams p, int T) {
   for (int t = wave; t < T; t += 4) {
     const float uo = osh[t][lane & 31];
     if (p.u_out && lane < 32) p.u_out[(size_t)t * nv + h * p.dv + ib * 32 + lane] = uo;
-    put_digits(p.next, p.next_qt, t, blk, uo, lane < 32);
+    if (p.next.xd) put_digits(p.next, p.next_qt, t, blk, uo, lane < 32);
   }
 }
 
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(1024) void k_deltanet_chunk(DnParams p, int T) {
   const int part = lane >> 3, r = lane & 7;
   const int ii = rg * 8 + r;
   const int i = ib * 32 + ii;
-  const int cur = p.ctrl->cur;
+  const int cur = p.ctrl ? p.ctrl->cur : 0;
   const size_t hs = (size_t)DK * p.dv;
   float* Sp = p.state + ((size_t)cur * p.heads + h) * hs;
   const int j0 = part * DKP;
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(1024) void k_deltanet_chunk(DnParams p, int T) {
     const int blk = (h * p.dv + ib * 32) / QK;
     const float uo = osh[w][lane & 31];
     if (p.u_out && lane < 32) p.u_out[(size_t)w * (p.heads * p.dv) + h * p.dv + ib * 32 + lane] = uo;
-    put_digits(p.next, p.next_qt, w, blk, uo, lane < 32);
+    if (p.next.xd) put_digits(p.next, p.next_qt, w, blk, uo, lane < 32);
   }
 }
 
@@ -391,7 +391,7 @@ __global__ void k_state_io(float* state, int nslots, const Ctrl* ctrl, int heads
   const int h = (int)(idx / ((size_t)dk * dv));
   const int rem = (int)(idx % ((size_t)dk * dv));
   const int i = rem / dk, j = rem % dk;     // canonical index (h, i, j)
-  float* dev = state + (size_t)ctrl->cur * n + (size_t)h * dk * dv + dn_off(i, j, dk / 8);
+  float* dev = state + (size_t)(ctrl ? ctrl->cur : 0) * n + (size_t)h * dk * dv + dn_off(i, j, dk / 8);
   if (to_device) *dev = canon[idx];
   else canon[idx] = *dev;
   (void)nslots;

@@ -827,6 +827,26 @@ int scratch_on_current_device(uint8_t** out) {
 
 }  // namespace
 
+namespace {
+
+std::string attn_desc_error(const slq_attn_desc* d) {
+  if (!d) return "null descriptor";
+  if (d->q_heads <= 0 || d->kv_heads <= 0 || d->q_heads % d->kv_heads) return "q_heads must be a multiple of kv_heads";
+  if (d->q_heads / d->kv_heads > 8) return "at most 8 query heads per KV head";
+  if (d->head_dim <= 0 || d->head_dim % 64 || d->head_dim > 256) return "head_dim must be 64, 128, 192 or 256";
+  if (d->rope_dims < 0 || d->rope_dims % 2 || d->rope_dims > d->head_dim) return "bad rope_dims";
+  if (d->max_seq <= 0 || d->max_seq % 64) return "max_seq must be a positive multiple of 64";
+  if (d->qk_norm && (!d->q_norm_dev || !d->k_norm_dev)) return "qk_norm needs both norm weight vectors";
+  return "";
+}
+
+// attention workspace: the RoPE table, then the split partials [T][q_heads][nchunk][head_dim + 2]
+size_t attn_rope_bytes(const slq_attn_desc* d) {
+  return al256((size_t)d->max_seq * (d->rope_dims / 2 > 0 ? d->rope_dims / 2 : 1) * 8);
+}
+
+}  // namespace
+
 // ====================================================================== ABI
 
 extern "C" {
@@ -940,6 +960,103 @@ int slq_gemv_noalloc(int qtype, const void* packed_dev, int64_t rows, int64_t co
   // no allocation), then the same two launches as slq_gemv
   HIPCHK(launch_fill_zero_u32(reinterpret_cast<uint32_t*>(ws + L.cnt), (size_t)((rows + RG - 1) / RG), S(stream)));
   return run_gemv(qtype, packed_dev, rows, cols, batch, x_dev, y_dev, ws, L, S(stream));
+}
+
+// ------------------------------------------------ mixers on caller buffers
+
+int slq_dn_state_layout(int heads, int dk, int dv, float* canon_dev, float* lib_dev, int to_lib, void* stream) {
+  if (heads <= 0 || dk <= 0 || dk % 32 || dk > 128 || dv <= 0 || dv % 32)
+    return fail(SLICE_ESHAPE, "slq_dn_state_layout: heads > 0, dk in {32, 64, 96, 128}, dv a multiple of 32");
+  if (!canon_dev || !lib_dev) return fail(SLICE_EINVAL, "slq_dn_state_layout: null pointer");
+  HIPCHK(launch_state_io(lib_dev, 1, nullptr, heads, dk, dv, canon_dev, to_lib ? 1 : 0, S(stream)));
+  return SLICE_OK;
+}
+
+int slq_dn_step(int heads, int dk, int dv, int T, const float* in_dev, float* state_dev, float* out_dev,
+                void* stream) {
+  if (heads <= 0 || dk <= 0 || dk % 32 || dk > 128 || dv <= 0 || dv % 32)
+    return fail(SLICE_ESHAPE, "slq_dn_step: heads > 0, dk in {32, 64, 96, 128}, dv a multiple of 32");
+  if (T < 1 || T > MAX_T) return fail(SLICE_ERANGE, "slq_dn_step: T outside 1..16");
+  if (!in_dev || !state_dev || !out_dev) return fail(SLICE_EINVAL, "slq_dn_step: null pointer");
+  DnParams p{};
+  p.y = in_dev;
+  p.off_q = 0;
+  p.off_k = heads * dk;
+  p.off_v = 2 * heads * dk;
+  p.off_a = p.off_v + heads * dv;
+  p.off_b = p.off_a + heads;
+  p.off_z = p.off_b + heads;
+  p.y_stride = p.off_z + heads * dv;
+  p.heads = heads; p.dk = dk; p.dv = dv;
+  p.a_scale = 1.0f; p.a_bias = 0.0f; p.b_scale = 1.0f; p.z_scale = 1.0f;
+  p.state = state_dev;
+  p.nslots = 1;
+  p.mode = DN_DECODE;     // one token after the other, the state updated in place
+  p.ctrl = nullptr;
+  p.u_out = out_dev;
+  HIPCHK(launch_deltanet(p, T, S(stream)));
+  return SLICE_OK;
+}
+
+size_t slq_attn_workspace_bytes(const slq_attn_desc* d, int T) {
+  if (!attn_desc_error(d).empty() || T < 1 || T > MAX_T) return 0;
+  const size_t nchunk = (size_t)(d->max_seq + ATT_CHUNK - 1) / ATT_CHUNK;
+  return attn_rope_bytes(d) + al256((size_t)T * d->q_heads * nchunk * (d->head_dim + 2) * 4);
+}
+
+int slq_attn_prepare(const slq_attn_desc* d, void* ws_dev, size_t ws_bytes, void* stream) {
+  const std::string e = attn_desc_error(d);
+  if (!e.empty()) return fail(SLICE_ESHAPE, "slq_attn_prepare: " + e);
+  if (!ws_dev) return fail(SLICE_EINVAL, "slq_attn_prepare: null workspace");
+  if (ws_bytes < attn_rope_bytes(d)) return fail(SLICE_EINVAL, "slq_attn_prepare: workspace too small");
+  HIPCHK(launch_rope_table(static_cast<float*>(ws_dev), d->max_seq, d->rope_dims, d->rope_theta, S(stream)));
+  return SLICE_OK;
+}
+
+int slq_attn_decode(const slq_attn_desc* d, int T, int pos, const float* in_dev, uint16_t* k_cache_dev,
+                    uint16_t* v_cache_dev, float* out_dev, void* ws_dev, size_t ws_bytes, void* stream) {
+  const std::string e = attn_desc_error(d);
+  if (!e.empty()) return fail(SLICE_ESHAPE, "slq_attn_decode: " + e);
+  if (T < 1 || T > MAX_T) return fail(SLICE_ERANGE, "slq_attn_decode: T outside 1..16");
+  if (pos < 0 || pos + T > d->max_seq) return fail(SLICE_ERANGE, "slq_attn_decode: positions outside the cache");
+  if (!in_dev || !k_cache_dev || !v_cache_dev || !out_dev || !ws_dev) return fail(SLICE_EINVAL, "slq_attn_decode: null pointer");
+  if (ws_bytes < slq_attn_workspace_bytes(d, T)) return fail(SLICE_EINVAL, "slq_attn_decode: workspace too small");
+  const int nq = d->q_heads * d->head_dim, nkv = d->kv_heads * d->head_dim;
+  AttnParams p{};
+  p.y = in_dev;
+  p.off_q = 0;
+  p.off_g = d->has_gate ? nq : -1;
+  p.off_k = d->has_gate ? 2 * nq : nq;
+  p.off_v = p.off_k + nkv;
+  p.y_stride = p.off_v + nkv;
+  p.q_heads = d->q_heads; p.kv_heads = d->kv_heads; p.hd = d->head_dim; p.rope_dims = d->rope_dims;
+  p.rope_theta = d->rope_theta;
+  p.rope_cs = static_cast<const float*>(ws_dev);
+  p.qk_norm = d->qk_norm;
+  p.q_norm = d->q_norm_dev;
+  p.k_norm = d->k_norm_dev;
+  p.eps = d->eps;
+  p.kc = reinterpret_cast<__half*>(k_cache_dev);
+  p.vc = reinterpret_cast<__half*>(v_cache_dev);
+  p.max_seq = d->max_seq;
+  p.ctrl = nullptr;
+  p.pos = pos;
+  p.part = reinterpret_cast<float*>(static_cast<uint8_t*>(ws_dev) + attn_rope_bytes(d));
+  p.nchunk = (d->max_seq + ATT_CHUNK - 1) / ATT_CHUNK;
+  p.u_out = out_dev;
+  HIPCHK(launch_attention(p, T, S(stream)));
+  return SLICE_OK;
+}
+
+int slq_kv_layout(int kv_heads, int max_seq, int head_dim, int rows, uint16_t* k_canon_dev, uint16_t* v_canon_dev,
+                  uint16_t* k_cache_dev, uint16_t* v_cache_dev, int to_cache, void* stream) {
+  if (kv_heads <= 0 || head_dim <= 0 || head_dim % 64 || head_dim > 256 || max_seq <= 0 || max_seq % 64)
+    return fail(SLICE_ESHAPE, "slq_kv_layout: bad kv_heads, head_dim or max_seq");
+  if (rows < 0 || rows > max_seq) return fail(SLICE_ERANGE, "slq_kv_layout: rows outside 0..max_seq");
+  if (!k_canon_dev || !v_canon_dev || !k_cache_dev || !v_cache_dev) return fail(SLICE_EINVAL, "slq_kv_layout: null pointer");
+  HIPCHK(launch_kv_io(reinterpret_cast<__half*>(k_cache_dev), reinterpret_cast<__half*>(v_cache_dev), kv_heads, max_seq,
+                      head_dim, k_canon_dev, v_canon_dev, rows, to_cache ? 1 : 0, S(stream)));
+  return SLICE_OK;
 }
 
 size_t slice_weights_bytes(const slice_config* cfg) {

@@ -211,9 +211,9 @@ struct DnParams {
   float* state;          // slot 0 of this layer: [nslots][heads][dv/8][dk/8][8][8] (see k_deltanet)
   int nslots;
   int mode;              // DN_DECODE, DN_VERIFY or DN_CHUNK (below)
-  const Ctrl* ctrl;
+  const Ctrl* ctrl;      // state slot index ctrl->cur; nullptr: slot 0
   float* u_out;          // [T][heads*dv] (nullable)
-  Act next; int next_qt;
+  Act next; int next_qt; // digits of the output (next.xd == nullptr: none)
 };
 hipError_t launch_deltanet(const DnParams& p, int T, hipStream_t s);
 hipError_t launch_state_io(float* state, int nslots, const Ctrl* ctrl, int heads, int dk, int dv,
@@ -232,11 +232,12 @@ struct AttnParams {
   __half* kc;            // K cache, tiled: [kv][max_seq/64][hd/8][64][8]
   __half* vc;            // V cache: [kv][max_seq][hd]
   int max_seq;
-  const Ctrl* ctrl;
+  const Ctrl* ctrl;      // position ctrl->pos; nullptr: pos below
+  int pos;
   float* part;           // [T][q_heads][nchunk][hd + 2]
   int nchunk;            // max_seq / chunk
   float* u_out;          // [T][q_heads*hd] (nullable)
-  Act next; int next_qt;
+  Act next; int next_qt; // digits of the output (next.xd == nullptr: none)
 };
 constexpr int ATT_CHUNK = 32;    // KV rows per split-attention workgroup
 hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s);

@@ -111,6 +111,80 @@ def deltanet_update(S: np.ndarray, q: np.ndarray, k: np.ndarray, v: np.ndarray,
     return S_new, S_new @ np.asarray(q, dtype=np.float64)
 
 
+# ------------------------------------------------------- mixers, one token
+
+def deltanet_heads(S: np.ndarray, q, k, v, alpha, beta, gate, dk: int, dv: int) -> np.ndarray:
+    """One token of the Gated DeltaNet mixer over all heads.
+
+    S: [heads, d_v, d_k] fp32, updated in place (each head's new state is
+    rounded to fp32, as it is stored between tokens).  q, k: [heads * d_k];
+    v, gate: [heads * d_v]; alpha, beta: [heads] (decay and write strength,
+    already passed through their sigmoids).  Head h uses the h-th slice of q,
+    k and v; q and k are L2-normalised per head.  Returns the gated output
+    o * gate, [heads * d_v] in fp64.
+    """
+    heads = S.shape[0]
+    o = np.empty(heads * dv)
+    for hh in range(heads):
+        qh = l2normalize(q[hh * dk:(hh + 1) * dk])
+        kh = l2normalize(k[hh * dk:(hh + 1) * dk])
+        vh = v[hh * dv:(hh + 1) * dv]
+        S_new, o[hh * dv:(hh + 1) * dv] = deltanet_update(S[hh], qh, kh, vh, alpha[hh], beta[hh])
+        S[hh] = S_new.astype(np.float32)
+    return o * np.asarray(gate, dtype=np.float64)
+
+
+def deltanet_token(S: np.ndarray, row: np.ndarray, dk: int, dv: int) -> np.ndarray:
+    """The DeltaNet mixer fed its pre-activations directly: row = [q | k | v |
+    a | b | z] (heads*d_k, heads*d_k, heads*d_v, heads, heads, heads*d_v) with
+    alpha = sigmoid(a), beta = sigmoid(b), gate = sigmoid(z).  Updates S in
+    place and returns the gated output."""
+    heads = S.shape[0]
+    row = np.asarray(row, dtype=np.float64)
+    o = 0
+    q = row[o:o + heads * dk]; o += heads * dk
+    k = row[o:o + heads * dk]; o += heads * dk
+    v = row[o:o + heads * dv]; o += heads * dv
+    a = row[o:o + heads]; o += heads
+    b = row[o:o + heads]; o += heads
+    z = row[o:o + heads * dv]
+    return deltanet_heads(S, q, k, v, sigmoid(a), sigmoid(b), sigmoid(z), dk, dv)
+
+
+def attention_heads(s, q, g, k, v, K: np.ndarray, V: np.ndarray, p: int, q_norm=None, k_norm=None) -> np.ndarray:
+    """One token of (gated) grouped-query attention at position p.
+
+    s: the attention geometry (head_dim, q_heads, kv_heads, rope_dims,
+    rope_theta, qk_norm, attn_gate, eps).  q, g: [q_heads * head_dim] (g only
+    with the gate); k, v: [kv_heads * head_dim]; q_norm, k_norm: [head_dim]
+    QK-norm weights.  The token's key (QK-norm, then RoPE at p) and value are
+    rounded to fp16 into row p of the caches K, V [kv_heads, rows, head_dim];
+    query head i (QK-norm, RoPE at p) attends to rows 0..p of KV head
+    i // (q_heads / kv_heads) with scale 1/sqrt(head_dim).  Returns the heads'
+    outputs, times sigmoid(g) with the gate, [q_heads * head_dim] in fp64.
+    """
+    hd, nq, nkv = s.head_dim, s.q_heads, s.kv_heads
+    grp = nq // nkv
+    q = np.asarray(q, dtype=np.float64).reshape(nq, hd)
+    k = np.asarray(k, dtype=np.float64).reshape(nkv, hd)
+    v = np.asarray(v, dtype=np.float64).reshape(nkv, hd)
+    for j in range(nkv):
+        kj = rmsnorm(k[j], k_norm, s.eps) if s.qk_norm else k[j]
+        K[j, p] = rope(kj, p, s.rope_dims, s.rope_theta).astype(np.float16)
+        V[j, p] = v[j].astype(np.float16)
+    scale = 1.0 / np.sqrt(hd)
+    o = np.empty((nq, hd))
+    for i in range(nq):
+        qi = rmsnorm(q[i], q_norm, s.eps) if s.qk_norm else q[i]
+        qi = rope(qi, p, s.rope_dims, s.rope_theta)
+        j = i // grp
+        o[i] = attend(qi, K[j, :p + 1], V[j, :p + 1], scale)
+    u = o.reshape(-1)
+    if s.attn_gate:
+        u = u * sigmoid(g)
+    return u
+
+
 # --------------------------------------------------------------------- slice
 
 class SliceOracle:
@@ -173,42 +247,19 @@ class SliceOracle:
         alpha = sigmoid(np.float64(np.float32(s.dn_a_scale)) * a + np.float64(np.float32(s.dn_a_bias)))
         beta = sigmoid(np.float64(np.float32(s.dn_b_scale)) * b)
         gate = sigmoid(np.float64(np.float32(s.dn_z_scale)) * z)
-        dk, dv = s.dn_dk, s.dn_dv
-        o = np.empty(s.dn_heads * dv)
-        S = self.dn[l]
-        for hh in range(s.dn_heads):
-            qh = l2normalize(q[hh * dk:(hh + 1) * dk])
-            kh = l2normalize(k[hh * dk:(hh + 1) * dk])
-            vh = v[hh * dv:(hh + 1) * dv]
-            S_new, o[hh * dv:(hh + 1) * dv] = deltanet_update(S[hh], qh, kh, vh, alpha[hh], beta[hh])
-            S[hh] = S_new.astype(np.float32)
-        return h + self._mv(l, "dn_out", o * gate)
+        u = deltanet_heads(self.dn[l], q, k, v, alpha, beta, gate, s.dn_dk, s.dn_dv)
+        return h + self._mv(l, "dn_out", u)
 
     def attention(self, l: int, h: np.ndarray) -> np.ndarray:
         s, W = self.s, self.W[l]
         hd, nq, nkv = s.head_dim, s.q_heads, s.kv_heads
-        grp = nq // nkv
         x = rmsnorm(h, W["attn_norm"], s.eps)
         q = self._mv(l, "wq", x).reshape(nq, hd)
         g = self._mv(l, "wg", x) if s.attn_gate else None
         k = self._mv(l, "wk", x).reshape(nkv, hd)
         v = self._mv(l, "wv", x).reshape(nkv, hd)
-        p = self.pos
         K, V = self.kv[l]
-        for j in range(nkv):
-            kj = rmsnorm(k[j], W["k_norm"], s.eps) if s.qk_norm else k[j]
-            K[j, p] = rope(kj, p, s.rope_dims, s.rope_theta).astype(np.float16)
-            V[j, p] = v[j].astype(np.float16)
-        scale = 1.0 / np.sqrt(hd)
-        o = np.empty((nq, hd))
-        for i in range(nq):
-            qi = rmsnorm(q[i], W["q_norm"], s.eps) if s.qk_norm else q[i]
-            qi = rope(qi, p, s.rope_dims, s.rope_theta)
-            j = i // grp
-            o[i] = attend(qi, K[j, :p + 1], V[j, :p + 1], scale)
-        u = o.reshape(-1)
-        if s.attn_gate:
-            u = u * sigmoid(g)
+        u = attention_heads(s, q, g, k, v, K, V, self.pos, W.get("q_norm"), W.get("k_norm"))
         return h + self._mv(l, "wo", u)
 
     def ffn(self, l: int, h: np.ndarray) -> np.ndarray:

@@ -238,3 +238,32 @@ def tiny_llama_token(seed: int = 0) -> int:
 def accept_pattern(seed: int, rounds: int, k: int) -> np.ndarray:
     """Number of accepted draft tokens per verify round, uniform on 0..k."""
     return stream(seed, WL_SLICE, 0, TENSOR_IDS["accept"]).integers(0, k + 1, size=rounds)
+
+
+def dn_kernel_inputs(seed: int, T: int, heads: int, dk: int, dv: int, step0: int = 0) -> np.ndarray:
+    """Inputs of the DeltaNet kernel on its own, fp32 [T][q|k|v|a|b|z] (heads
+    x dk, heads x dk, heads x dv, heads, heads, heads x dv): q, k, v ~ N(0,1);
+    decay pre-activation a ~ N(2, 0.5); write strength b ~ N(0,1); output
+    gate z ~ N(0,1) (second parameters are standard deviations)."""
+    out = np.empty((T, 2 * heads * dk + 2 * heads * dv + 2 * heads), dtype=np.float32)
+    for t in range(T):
+        r = stream(seed, WL_DELTANET, 1000 + step0 + t, TENSOR_IDS["hidden"])
+        q = r.standard_normal(heads * dk)
+        k = r.standard_normal(heads * dk)
+        v = r.standard_normal(heads * dv)
+        a = r.normal(2.0, 0.5, heads)
+        b = r.standard_normal(heads)
+        z = r.standard_normal(heads * dv)
+        out[t] = np.concatenate([q, k, v, a, b, z]).astype(np.float32)
+    return out
+
+
+def attn_kernel_inputs(seed: int, T: int, q_heads: int, kv_heads: int, head_dim: int, gate: bool,
+                       step0: int = 0) -> np.ndarray:
+    """Inputs of the attention kernel on its own, fp32 [T][q|g|k|v], every
+    entry N(0,1)."""
+    n = (2 if gate else 1) * q_heads * head_dim + 2 * kv_heads * head_dim
+    out = np.empty((T, n), dtype=np.float32)
+    for t in range(T):
+        out[t] = stream(seed, WL_ATTENTION, 1000 + step0 + t, TENSOR_IDS["hidden"]).standard_normal(n)
+    return out

@@ -283,43 +283,93 @@ def test_deltanet_wiring_closed_form():
 
 # (method of SliceOracle, text in its source, replacement): each is a
 # plausible wiring mistake that one of the pins above must catch.
+def pin_deltanet_token():
+    """The DeltaNet mixer fed its pre-activations as one row [q|k|v|a|b|z],
+    three heads of d_k = 4, d_v = 3, each with q = c_q e_{jq} and k = c_k e_{jk}
+    at distinct dimensions (jq != jk): after L2 normalisation kh = kappa e_jk
+    and qh = rho e_jq, so S' = alpha S (I - beta kh kh^T) + beta v kh^T keeps
+    column jq at alpha S[:, jq] and o = rho alpha S[:, jq]; column jk becomes
+    alpha (1 - beta kappa^2) S[:, jk] + beta kappa v.  alpha = sigmoid(a),
+    beta = sigmoid(b), and the output is o * sigmoid(z)."""
+    heads, dk, dv = 3, 4, 3
+    jq, jk = [0, 2, 3], [1, 0, 2]
+    cq, ck = [2.0, -0.5, 1.25], [0.75, 3.0, -1.5]
+    a, b = [0.5, -1.0, 2.5], [1.0, -0.25, 0.0]
+    v = np.array([[1.0, -2.0, 0.5], [0.25, 0.0, -1.0], [3.0, 1.5, -0.75]])
+    z = np.array([[0.1, -0.2, 0.3], [1.0, 0.0, -1.0], [2.0, -2.0, 0.5]])
+    q = np.zeros((heads, dk))
+    k = np.zeros((heads, dk))
+    for h in range(heads):
+        q[h, jq[h]], k[h, jk[h]] = cq[h], ck[h]
+    row = np.concatenate([q.ravel(), k.ravel(), v.ravel(), a, b, z.ravel()])
+    S0 = synth.dn_state0(0, 93, 0, heads, dv, dk) * 10
+    S = S0.copy()
+    out = omodel.deltanet_token(S, row, dk, dv)
+    for h in range(heads):
+        def unit(c):
+            return c / math.sqrt(c * c + 1e-6)
+        al, be = sig(a[h]), sig(b[h])
+        kap, rho = unit(ck[h]), unit(cq[h])
+        S0h = S0[h].astype(np.float64)
+        col_q = al * S0h[:, jq[h]]
+        col_k = al * (1 - be * kap * kap) * S0h[:, jk[h]] + be * kap * v[h]
+        want_o = rho * col_q * np.array([sig(t) for t in z[h]])
+        np.testing.assert_allclose(out[h * dv:(h + 1) * dv], want_o, rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(S[h][:, jq[h]], col_q.astype(np.float32), rtol=1e-6, atol=1e-7)
+        np.testing.assert_allclose(S[h][:, jk[h]], col_k.astype(np.float32), rtol=1e-6, atol=1e-7)
+        for j in range(dk):
+            if j not in (jq[h], jk[h]):
+                np.testing.assert_allclose(S[h][:, j], (al * S0h[:, j]).astype(np.float32), rtol=1e-6, atol=1e-7)
+
+
+def test_deltanet_token_closed_form():
+    pin_deltanet_token()
+
+
 MUTANTS = {
-    "ffn_gate_up_swapped": ("ffn", 'silu(self._mv(l, "w_gate", x)) * self._mv(l, "w_up", x)',
+    "ffn_gate_up_swapped": ("SliceOracle.ffn", 'silu(self._mv(l, "w_gate", x)) * self._mv(l, "w_up", x)',
                             'silu(self._mv(l, "w_up", x)) * self._mv(l, "w_gate", x)'),
-    "attn_scale_dropped": ("attention", "scale = 1.0 / np.sqrt(hd)", "scale = 1.0"),
-    "attn_scale_head_count": ("attention", "scale = 1.0 / np.sqrt(hd)", "scale = 1.0 / np.sqrt(nq)"),
-    "attn_q_rope_next_pos": ("attention", "qi = rope(qi, p, ", "qi = rope(qi, p + 1, "),
-    "attn_q_rope_prev_pos": ("attention", "qi = rope(qi, p, ", "qi = rope(qi, p - 1, "),
-    "attn_q_norm_dropped": ("attention", 'qi = rmsnorm(q[i], W["q_norm"], s.eps) if s.qk_norm else q[i]',
+    "attn_scale_dropped": ("attention_heads", "scale = 1.0 / np.sqrt(hd)", "scale = 1.0"),
+    "attn_scale_head_count": ("attention_heads", "scale = 1.0 / np.sqrt(hd)", "scale = 1.0 / np.sqrt(nq)"),
+    "attn_q_rope_next_pos": ("attention_heads", "qi = rope(qi, p, ", "qi = rope(qi, p + 1, "),
+    "attn_q_rope_prev_pos": ("attention_heads", "qi = rope(qi, p, ", "qi = rope(qi, p - 1, "),
+    "attn_q_norm_dropped": ("attention_heads", "qi = rmsnorm(q[i], q_norm, s.eps) if s.qk_norm else q[i]",
                             "qi = q[i]"),
-    "attn_k_rope_dropped": ("attention", "rope(kj, p, s.rope_dims, s.rope_theta)", "kj"),
-    "attn_head_map_mod": ("attention", "j = i // grp", "j = i % nkv"),
-    "attn_gate_dropped": ("attention", "u = u * sigmoid(g)", "u = u"),
-    "dn_q_k_swapped": ("deltanet", 'q = self._mv(l, "dn_q", x)\n    k = self._mv(l, "dn_k", x)',
+    "attn_k_rope_dropped": ("attention_heads", "rope(kj, p, s.rope_dims, s.rope_theta)", "kj"),
+    "attn_head_map_mod": ("attention_heads", "j = i // grp", "j = i % nkv"),
+    "attn_gate_dropped": ("attention_heads", "u = u * sigmoid(g)", "u = u"),
+    "dn_q_k_swapped": ("SliceOracle.deltanet", 'q = self._mv(l, "dn_q", x)\n    k = self._mv(l, "dn_k", x)',
                        'k = self._mv(l, "dn_q", x)\n    q = self._mv(l, "dn_k", x)'),
-    "dn_beta_coeff": ("deltanet", "np.float32(s.dn_b_scale)", "np.float32(s.dn_a_scale)"),
-    "dn_gate_coeff": ("deltanet", "np.float32(s.dn_z_scale)", "np.float32(s.dn_a_scale)"),
-    "dn_gate_dropped": ("deltanet", "o * gate", "o"),
-    "dn_alpha_bias": ("deltanet", "+ np.float64(np.float32(s.dn_a_bias))", ""),
-    "dn_head_slice": ("deltanet", "kh = l2normalize(k[hh * dk:(hh + 1) * dk])", "kh = l2normalize(k[0:dk])"),
-    "dn_v_for_k": ("deltanet", "vh = v[hh * dv:(hh + 1) * dv]", "vh = k[hh * dv:(hh + 1) * dv]"),
+    "dn_beta_coeff": ("SliceOracle.deltanet", "np.float32(s.dn_b_scale)", "np.float32(s.dn_a_scale)"),
+    "dn_gate_coeff": ("SliceOracle.deltanet", "np.float32(s.dn_z_scale)", "np.float32(s.dn_a_scale)"),
+    "dn_gate_dropped": ("deltanet_heads", "return o * np.asarray(gate, dtype=np.float64)", "return o"),
+    "dn_alpha_bias": ("SliceOracle.deltanet", "+ np.float64(np.float32(s.dn_a_bias))", ""),
+    "dn_head_slice": ("deltanet_heads", "kh = l2normalize(k[hh * dk:(hh + 1) * dk])", "kh = l2normalize(k[0:dk])"),
+    "dn_token_a_b_swapped": ("deltanet_token", "sigmoid(a), sigmoid(b)", "sigmoid(b), sigmoid(a)"),
+    "dn_token_q_k_swapped": ("deltanet_token", "deltanet_heads(S, q, k, v,", "deltanet_heads(S, k, q, v,"),
+    "dn_token_z_offset": ("deltanet_token", "z = row[o:o + heads * dv]", "z = row[o - heads:o - heads + heads * dv]"),
+    "dn_v_for_k": ("deltanet_heads", "vh = v[hh * dv:(hh + 1) * dv]", "vh = k[hh * dv:(hh + 1) * dv]"),
 }
 
-PINS = [pin_ffn, pin_attention, pin_attention_key, pin_deltanet]
+PINS = [pin_ffn, pin_attention, pin_attention_key, pin_deltanet, pin_deltanet_token]
 
 
-def _mutant_method(meth: str, old: str, new: str):
-    src = textwrap.dedent(inspect.getsource(getattr(oracle.SliceOracle, meth)))
+def _mutant(where: str, old: str, new: str):
+    """(owner, name, function) with the planted mistake; owner is the class or
+    the oracle module the function lives in."""
+    owner, _, name = where.rpartition(".")
+    owner = getattr(omodel, owner) if owner else omodel
+    src = textwrap.dedent(inspect.getsource(getattr(owner, name)))
     assert old in src, f"planted mistake no longer matches the oracle source: {old!r}"
     g = dict(vars(omodel))
-    exec(compile(src.replace(old, new, 1), f"<mutant {meth}>", "exec"), g)
-    return g[meth]
+    exec(compile(src.replace(old, new, 1), f"<mutant {where}>", "exec"), g)
+    return owner, name, g[name]
 
 
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_pins_catch_planted_mistake(name, monkeypatch):
-    meth, old, new = MUTANTS[name]
-    monkeypatch.setattr(oracle.SliceOracle, meth, _mutant_method(meth, old, new))
+    owner, fn, mutant = _mutant(*MUTANTS[name])
+    monkeypatch.setattr(owner, fn, mutant)
     caught = []
     for pin in PINS:
         try:
