@@ -8,10 +8,15 @@ in every layer; all matrices Q4_0, 13.4 GB), synthetic seeded weights, a
 fresh N(0,1) fp16 hidden state per step, as a middle pipeline stage receives
 it.  One step = one token through all 64 layers (one HIP graph launch).
 
-Printed JSON (one line on stdout): decode tok/s, the roofline of the dominant
-kernel (the fused RMSNorm + gate/up + SwiGLU GEMV, measured with HIP events),
-the CPU oracle timed on a bounded sample, 4-draft verify with rollback, the
-Q8_0 slice, and the standalone GEMV sweep.  Progress goes to stderr.
+Printed JSON (one line on stdout): decode tok/s; the roofline of the dominant
+kernel (the chained products of each layer: mixer output, RMSNorm + gate/up +
+SwiGLU, down + residual, next layer's input projections, one launch per layer,
+timed with HIP events) and of the whole step; the measured streaming-read
+ceiling; the CPU oracle timed on a bounded sample (all cores and one thread);
+each GEMV timed as its own kernel; the DeltaNet and attention kernels on
+caller buffers (decode and 16-query verify at 512, 4096 and 32768 KV rows);
+4-draft verify with rollback; prompt passes; the Q8_0 slice; and the
+standalone GEMV sweep.  Progress goes to stderr.
 """
 from __future__ import annotations
 
@@ -33,30 +38,31 @@ PREFILL = 512
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_hybrid64_q4_decode.md")
-F1_SOURCES = ("slq.h", "dev.h", "gemv_kernel.h", "gemv_q4_swiglu.hip")
+CHAIN_SOURCES = ("slq.h", "dev.h", "gemv_kernel.h", "chain.hip")
 
 
-def f1_source_hash() -> str:
-    """sha256 over the sources that define the fused gate/up GEMV kernel."""
+def chain_source_hash() -> str:
+    """sha256 over the sources that define the chained-products kernel."""
     import hashlib
     h = hashlib.sha256()
-    for name in F1_SOURCES:
+    for name in CHAIN_SOURCES:
         with open(os.path.join(ROOT, "layer_sliced_quantized_amd", "csrc", name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()
 
 
 def profiled_traffic():
-    """HBM bytes per launch of the gate/up GEMV from the committed PMC summary
-    (FETCH_SIZE and WRITE_SIZE scaled by a known-size copy), or None when the
-    kernel sources changed after the counters were taken."""
+    """HBM bytes per launch of the chained-products kernel from the committed
+    PMC summary (FETCH_SIZE and WRITE_SIZE scaled by a known-size copy, mean
+    over the 64 layers' launches), or None when the kernel sources changed
+    after the counters were taken."""
     try:
         text = open(TRAFFIC_PROFILE).read()
     except OSError:
         return None
     m_b = re.search(r"traffic_bytes_per_launch: (\d+)", text)
     m_h = re.search(r"kernel_sources_sha256: ([0-9a-f]{64})", text)
-    if not m_b or not m_h or m_h.group(1) != f1_source_hash():
+    if not m_b or not m_h or m_h.group(1) != chain_source_hash():
         return None
     return int(m_b.group(1))
 
@@ -69,6 +75,120 @@ def gemv_bytes(rows: int, cols: int, qtype: int, batch: int = 1) -> int:
     """Algorithmic bytes of one GEMV: packed weights + fp32 activations in and out."""
     bb = 18 if qtype == 2 else 34
     return rows * cols // 32 * bb + 4 * batch * (rows + cols)
+
+
+def mixer_rows_cols(shape, l):
+    """(rows of the input projections, columns of the output projection) of layer l's mixer."""
+    if shape.is_attention(l):
+        return 2 * shape.q_heads * shape.head_dim + 2 * shape.kv_heads * shape.head_dim, shape.q_heads * shape.head_dim
+    nk, nv = shape.dn_heads * shape.dn_dk, shape.dn_heads * shape.dn_dv
+    return 2 * nk + 2 * nv + 2 * shape.dn_heads, nv
+
+
+def chain_step_bytes(shape, qtype) -> int:
+    """Algorithmic bytes of one decode step's chained-product launches (one per
+    layer): mixer output, gate/up, down and, except after the last layer, the
+    next layer's input projections -- packed weights plus fp32 activations."""
+    H, F, n = shape.hidden, shape.ffn, shape.n_layers
+    total = 0
+    for l in range(n):
+        total += gemv_bytes(H, mixer_rows_cols(shape, l)[1], qtype) + gemv_bytes(2 * F, H, qtype) + \
+            gemv_bytes(H, F, qtype)
+        if l + 1 < n:
+            total += gemv_bytes(mixer_rows_cols(shape, l + 1)[0], H, qtype)
+    return total
+
+
+def read_ceiling(gib=2, reps=30):
+    """Streaming-read bandwidth of the device: slq_read_probe over a buffer
+    eight times the 256 MB last-level cache, HIP events around reps reads."""
+    import torch
+    import layer_sliced_quantized_amd as slq
+    buf = torch.zeros(gib << 30, dtype=torch.uint8, device="cuda")
+    sink = torch.empty(4 * slq.READ_PROBE_GRID, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        slq.read_probe(buf, sink)
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        slq.read_probe(buf, sink)
+    ev1.record()
+    torch.cuda.synchronize()
+    us = ev0.elapsed_time(ev1) / reps * 1e3
+    gbs = buf.numel() / (us * 1e-6) / 1e9
+    del buf
+    torch.cuda.empty_cache()
+    return {"GB_s": round(gbs, 1), "frac_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": gib << 30, "us": round(us, 2),
+            "kernel": "slq_read_probe: nontemporal 16-byte loads, 4 in flight per lane, 4096 x 256 threads"}
+
+
+def _event_time_us(fn, reps):
+    import torch
+    fn()
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0.record()
+    for _ in range(reps):
+        fn()
+    ev1.record()
+    torch.cuda.synchronize()
+    return ev0.elapsed_time(ev1) / reps * 1e3
+
+
+def mixer_kernels(seed, reps=100):
+    """The mixers on caller buffers at the hidden-5120 hybrid's geometry: the
+    DeltaNet step (32 heads of 128 x 128, 1 and 16 tokens; bytes = the fp32
+    state read and written) and decode attention (24 query / 4 KV heads of
+    256, 1 and 16 queries at 512, 4096 and 32768 prior rows; bytes = the fp16
+    K and V rows read)."""
+    import torch
+    import synth
+    import layer_sliced_quantized_amd as slq
+    g = synth.HYBRID_5120
+    out = {"deltanet": [], "attention": []}
+    heads, dk, dv = g.dn_heads, g.dn_dk, g.dn_dv
+    S = slq.dn_state_to_lib(torch.from_numpy(synth.dn_state0(seed, synth.WL_DELTANET, 0, heads, dv, dk)).cuda())
+    for T in (1, 16):
+        rows = torch.from_numpy(synth.dn_kernel_inputs(seed, T, heads, dk, dv)).cuda()
+        o = torch.empty((T, heads * dv), dtype=torch.float32, device="cuda")
+        us = _event_time_us(lambda: slq.dn_step(heads, dk, dv, rows, S, out=o), reps)
+        nbytes = 2 * S.numel() * 4
+        out["deltanet"].append({"tokens": T, "us": round(us, 2), "state_MB": round(nbytes / 1e6, 2),
+                                "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1)})
+        log(f"deltanet kernel {out['deltanet'][-1]}")
+    Lmax = 32768
+    K, V = synth.kv_prefill(seed, synth.WL_ATTENTION, 0, g.kv_heads, Lmax, g.head_dim)
+    rng = synth.stream(seed, synth.WL_ATTENTION, 99, synth.TENSOR_IDS["q_norm"])
+    qn = (1.0 + 0.25 * rng.standard_normal(g.head_dim)).astype(np.float32)
+    kn = (1.0 + 0.25 * rng.standard_normal(g.head_dim)).astype(np.float32)
+    for L in (512, 4096, Lmax):
+        dec = slq.AttnDecoder(g.q_heads, g.kv_heads, g.head_dim, g.rope_dims, g.rope_theta, g.qk_norm, g.attn_gate,
+                              g.eps, (L + 16 + 63) // 64 * 64, qn, kn)
+        dec.set_kv(torch.from_numpy(K[:, :L]), torch.from_numpy(V[:, :L]))
+        for T in (1, 16):
+            rows = torch.from_numpy(synth.attn_kernel_inputs(seed, T, g.q_heads, g.kv_heads, g.head_dim, True,
+                                                             step0=L)).cuda()
+            o = torch.empty((T, g.q_heads * g.head_dim), dtype=torch.float32, device="cuda")
+            us = _event_time_us(lambda: dec.decode(rows, L, out=o), reps)
+            nbytes = (L + T) * g.kv_heads * g.head_dim * 2 * 2
+            out["attention"].append({"kv_rows": L, "queries": T, "us": round(us, 2), "kv_MB": round(nbytes / 1e6, 2),
+                                     "GB_s": round(nbytes / (us * 1e-6) / 1e9, 1)})
+            log(f"attention kernel {out['attention'][-1]}")
+        del dec
+    torch.cuda.empty_cache()
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
 
 
 def build_slice(shape, qtype, max_seq, max_verify, seed, threads):
@@ -286,20 +406,28 @@ def gemv_sweep(seed, reps):
     return res
 
 
-def cpu_baseline(shape, qtype, tensors, H, n_tokens, seed, gpu_first):
-    """The oracle, as it stands, decoding n_tokens of the same slice on the host cores."""
+def _oracle_slice(shape, qtype, tensors, seed, end):
     import synth
     from oracle import SliceOracle
-    from oracle import qref
-    qref.build(force=False)
-    orc = SliceOracle(shape, qtype, 0, shape.n_layers, tensors, max_seq=PREFILL + 64, io_fp32=False)
-    for l in range(shape.n_layers):
+    orc = SliceOracle(shape, qtype, 0, end, {l: tensors[l] for l in range(end)}, max_seq=PREFILL + 64, io_fp32=False)
+    for l in range(end):
         if shape.is_attention(l):
             K, V = synth.kv_prefill(seed, synth.WL_SLICE, l, shape.kv_heads, PREFILL, shape.head_dim)
             orc.set_kv(l, K, V)
         else:
             orc.set_state(l, synth.dn_state0(seed, synth.WL_SLICE, l, shape.dn_heads, shape.dn_dv, shape.dn_dk))
     orc.reset(PREFILL)
+    return orc
+
+
+def cpu_baseline(shape, qtype, tensors, H, n_tokens, seed, gpu_first, layers_1t=4, tokens_1t=2):
+    """The oracle, as it stands, decoding n_tokens of the same slice on the host
+    cores; then on one thread, over layers 0..layers_1t-1 (three DeltaNet and
+    one attention layer: the slice's mix), scaled to the 64 layers."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    from oracle import qref
+    qref.build(force=False)
+    orc = _oracle_slice(shape, qtype, tensors, seed, shape.n_layers)
     t0 = time.perf_counter()
     outs = []
     for i in range(n_tokens):
@@ -310,9 +438,22 @@ def cpu_baseline(shape, qtype, tensors, H, n_tokens, seed, gpu_first):
     got = gpu_first.astype(np.float64)
     rms = np.sqrt(np.mean(ref * ref))
     rel = float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), rms)))
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": round(n_tokens / sec, 4), "unit": "tok/s", "cores": cores, "kind": "oracle",
-            "sample": f"{n_tokens} decode tokens of the same 64-layer slice (fp64 C GEMV + numpy)"}, rel
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "openmp"] or
+                  [int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))])
+    del orc
+    orc1 = _oracle_slice(shape, qtype, tensors, seed, layers_1t)
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for i in range(tokens_1t):
+            orc1.decode(H[i], raw=True)
+        sec1 = time.perf_counter() - t0
+    per_token_64 = sec1 / tokens_1t * shape.n_layers / layers_1t
+    log(f"oracle on one thread: {sec1:.1f}s for {tokens_1t} tokens of {layers_1t} layers")
+    return {"value": round(n_tokens / sec, 4), "unit": "tok/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_tokens} decode tokens of the same 64-layer slice (fp64 C GEMV with OpenMP + numpy)",
+            "cpu_model": cpu_model(), "value_1thread": round(1.0 / per_token_64, 5),
+            "sample_1thread": f"{tokens_1t} tokens through layers 0-{layers_1t - 1} (3 DeltaNet + 1 attention) "
+                              f"on one thread, {sec1:.1f} s, scaled by {shape.n_layers // layers_1t} to 64 layers"}, rel
 
 
 def main() -> int:
@@ -330,6 +471,8 @@ def main() -> int:
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-attn-sweep", action="store_true", help="skip the decode-attention timing at 512/4096/32768 KV rows")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-mixers", action="store_true", help="skip the DeltaNet / attention kernel timings")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-chain", action="store_true",
                     help="decode with every product as its own kernel instead of the chained products (same results)")
@@ -380,13 +523,8 @@ def main() -> int:
     gemv_ms = {op: time_gemv_op(s, op, args.gemv_reps) / n_op
                for op, n_op in (("ffn_in", 64), ("ffn_out", 64), ("dn_in", 48), ("dn_out", 48), ("att_in", 16),
                                 ("att_out", 16))}
-    f1_ms = gemv_ms["ffn_in"]
-    f1_launches = 64 * args.gemv_reps
-    f1_bytes = gemv_bytes(f1_rows, f1_cols, synth.Q4_0)
-    achieved = f1_bytes / (f1_ms * 1e-3) / 1e9
     weight_bytes = s.weights.numel()
     slice_bytes_tok = weight_bytes + 48 * 2 * 32 * 128 * 128 * 4 + 16 * (PREFILL + args.steps // 2) * 4096
-    log(f"F1 GEMV {f1_rows}x{f1_cols}: {f1_ms * 1e3:.2f} us -> {achieved:.0f} GB/s; eager op sum per step {step_ms:.3f} ms")
     gemv_shapes = {"ffn_in": (2 * shape.ffn, shape.hidden), "ffn_out": (shape.hidden, shape.ffn),
                    "dn_in": (3 * 4096 + 64 + 4096, shape.hidden), "dn_out": (shape.hidden, 4096),
                    "att_in": (2 * 6144 + 2 * 1024, shape.hidden), "att_out": (shape.hidden, 6144)}
@@ -394,7 +532,23 @@ def main() -> int:
                           "GB_s": round(gemv_bytes(r, c, synth.Q4_0) / (ms * 1e-3) / 1e9, 1)}
                      for op, ms in gemv_ms.items() for r, c in [gemv_shapes[op]]}
     for op, v in gemv_in_slice.items():
-        log(f"gemv {op:8s} {v}")
+        log(f"gemv {op:8s} (own kernel) {v}")
+    if not args.no_chain:
+        chain_ms = time_gemv_op(s, "chain", args.gemv_reps) / shape.n_layers
+        chain_launches = shape.n_layers * args.gemv_reps
+        rl_bytes = chain_step_bytes(shape, synth.Q4_0) // shape.n_layers
+        rl_kernel = (f"k_chain<2>: one launch per layer of the chained products (mixer output, RMSNorm + gate/up + "
+                     f"SwiGLU, down + residual, next layer's input projections), mean of {chain_launches} launches "
+                     f"over the 64 layers' weights in layer order, HIP events")
+        rl_ms = chain_ms
+    else:
+        rl_bytes = gemv_bytes(f1_rows, f1_cols, synth.Q4_0)
+        rl_kernel = (f"k_gemv<2,1,2>: fused RMSNorm + gate/up ({f1_rows}x{f1_cols} Q4_0) + SwiGLU, mean of "
+                     f"{64 * args.gemv_reps} launches over the 64 layers' weights, HIP events")
+        rl_ms = gemv_ms["ffn_in"]
+    achieved = rl_bytes / (rl_ms * 1e-3) / 1e9
+    log(f"roofline kernel: {rl_ms * 1e3:.2f} us per launch, {rl_bytes / 1e6:.2f} MB -> {achieved:.0f} GB/s; "
+        f"eager op sum per step {step_ms:.3f} ms")
 
     # ---- verify with rollback
     base += args.profile_steps
@@ -407,10 +561,16 @@ def main() -> int:
     base += 16 * (args.prefill_chunks + 1)
     pre_c = run_prefill_chunked(s, H[base:], args.prefill_chunks) if args.prefill_chunks > 0 else None
     log(f"prefill (16-token passes, chunked DeltaNet): {pre_c}")
+    s_chained = not args.no_chain
     del s
     torch.cuda.empty_cache()
 
     extra = {}
+    if not args.no_ceiling:
+        extra["read_ceiling"] = read_ceiling()
+        log(f"read ceiling {extra['read_ceiling']}")
+    if not args.no_mixers:
+        extra["mixer_kernels"] = mixer_kernels(args.seed)
     # ---- decode attention at three KV lengths
     if not args.no_attn_sweep:
         extra["attention_decode"] = attention_sweep(args.seed)
@@ -450,10 +610,14 @@ def main() -> int:
                                f"Q4_0 {weight_bytes / 1e9:.2f} GB, batch 1 decode from position {PREFILL}",
                    "global_batch": 1, "seq_len": PREFILL, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": profiled_traffic(),
-                     "kernel": f"k_gemv<2,1,2>: fused RMSNorm + gate/up ({f1_rows}x{f1_cols} Q4_0) + SwiGLU, "
-                               f"mean of {f1_launches} back-to-back launches over the 64 layers' weights, HIP events",
-                     "bytes_per_launch": f1_bytes},
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic() if s_chained else None,
+                     "kernel": rl_kernel, "bytes_per_launch": rl_bytes, "us_per_launch": round(rl_ms * 1e3, 3)},
+        "roofline_step": {"achieved": round(slice_bytes_tok * tok_s / 1e9, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(slice_bytes_tok * tok_s / 1e9 / HBM_PEAK_GBS, 4),
+                          "bytes_per_step": slice_bytes_tok,
+                          "what": "all bytes a decode step must read (weights, DeltaNet states read and written, "
+                                  "KV rows) x tok/s"},
         "cpu_baseline": cpu,
         "slice_GB_per_token": round(slice_bytes_tok / 1e9, 3),
         "slice_effective_GB_s": round(slice_bytes_tok * tok_s / 1e9, 1),

@@ -17,7 +17,7 @@ from ._native import (Q4_0, Q8_0, TENSOR_IDS, AttnDesc, SliceConfig, SliceError,
 
 __all__ = ["Q4_0", "Q8_0", "SliceConfig", "SliceError", "Slice", "make_config", "tensor_info",
            "packed_bytes", "repack", "dequant", "gemv", "gemv_workspace_bytes", "debug_override",
-           "overrides", "dn_step", "dn_state_to_lib", "dn_state_from_lib", "AttnDecoder", "lib"]
+           "overrides", "read_probe", "dn_step", "dn_state_to_lib", "dn_state_from_lib", "AttnDecoder", "lib"]
 
 
 def _stream(stream=None) -> ctypes.c_void_p:
@@ -91,6 +91,14 @@ def overrides(**kw):
     finally:
         for k in kw:
             debug_override(k, -1)
+
+
+READ_PROBE_GRID = 4096     # SLQ_READ_PROBE_GRID: workgroups of slq_read_probe
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """One streaming read of buf's bytes (slq_read_probe); sink: >= 4 * 4096 int32."""
+    check(lib().slq_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 
 # ------------------------------------------------- mixers on caller buffers

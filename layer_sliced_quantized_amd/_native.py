@@ -75,6 +75,7 @@ _SIGS = {
     "slq_gemv_workspace_bytes": (_SZ, [_I, _I64, _I64, _I]),
     "slq_gemv": (_I, [_I, _V, _I64, _I64, _I, _V, _V, _V, _SZ, _V]),
     "slq_gemv_noalloc": (_I, [_I, _V, _I64, _I64, _I, _V, _V, _V]),
+    "slq_read_probe": (_I, [_V, _SZ, _V, _V]),
     "slq_dn_step": (_I, [_I, _I, _I, _I, _V, _V, _V, _V]),
     "slq_dn_state_layout": (_I, [_I, _I, _I, _V, _V, _I, _V]),
     "slq_attn_workspace_bytes": (_SZ, [ctypes.POINTER(AttnDesc), _I]),

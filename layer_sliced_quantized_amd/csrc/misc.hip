@@ -40,6 +40,34 @@ hipError_t launch_fill_zero_u32(uint32_t* p, size_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Streaming read of n16 16-byte words, each read once with a nontemporal
+// load (as the GEMVs read weights), four loads in flight per lane.  The words
+// are folded by XOR into one value per wave, stored to sink, so that no load
+// can be dropped; sink needs gridDim.x * 4 entries.
+typedef uint32_t rp_u32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void k_read_probe(const rp_u32x4* __restrict__ p, size_t n16, uint32_t* sink) {
+  const size_t stride = (size_t)gridDim.x * 256;
+  size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
+  rp_u32x4 acc = {0u, 0u, 0u, 0u};
+  for (; i + 3 * stride < n16; i += 4 * stride) {
+    const rp_u32x4 a = __builtin_nontemporal_load(p + i);
+    const rp_u32x4 b = __builtin_nontemporal_load(p + i + stride);
+    const rp_u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride);
+    const rp_u32x4 d = __builtin_nontemporal_load(p + i + 3 * stride);
+    acc ^= a ^ b ^ c ^ d;
+  }
+  for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
+  uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  for (int o = 32; o > 0; o >>= 1) v ^= __shfl_xor(v, o, 64);
+  if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = v;
+}
+
+hipError_t launch_read_probe(const void* p, size_t n16, uint32_t* sink, unsigned grid, hipStream_t s) {
+  k_read_probe<<<grid, 256, 0, s>>>(reinterpret_cast<const rp_u32x4*>(p), n16, sink);
+  return hipGetLastError();
+}
+
 __global__ void k_ctrl_io(Ctrl* c, const void* in, void* out) {
   c->in = in;
   c->out = out;

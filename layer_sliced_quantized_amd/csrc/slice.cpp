@@ -964,6 +964,13 @@ int slq_gemv_noalloc(int qtype, const void* packed_dev, int64_t rows, int64_t co
 
 // ------------------------------------------------ mixers on caller buffers
 
+int slq_read_probe(const void* buf_dev, size_t bytes, uint32_t* sink_dev, void* stream) {
+  if (!buf_dev || !sink_dev) return fail(SLICE_EINVAL, "slq_read_probe: null pointer");
+  if (bytes == 0 || bytes % 16) return fail(SLICE_EINVAL, "slq_read_probe: bytes must be a positive multiple of 16");
+  HIPCHK(launch_read_probe(buf_dev, bytes / 16, sink_dev, SLQ_READ_PROBE_GRID, S(stream)));
+  return SLICE_OK;
+}
+
 int slq_dn_state_layout(int heads, int dk, int dv, float* canon_dev, float* lib_dev, int to_lib, void* stream) {
   if (heads <= 0 || dk <= 0 || dk % 32 || dk > 128 || dv <= 0 || dv % 32)
     return fail(SLICE_ESHAPE, "slq_dn_state_layout: heads > 0, dk in {32, 64, 96, 128}, dv a multiple of 32");

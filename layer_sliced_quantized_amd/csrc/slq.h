@@ -143,6 +143,7 @@ hipError_t launch_store_out(const float* h, int T, int H, void* out, int fp32, C
 hipError_t launch_ctrl_io(Ctrl* c, const void* in, void* out, hipStream_t s);
 // p[0..n) = 0 with a kernel (usable where a memset node is not wanted)
 hipError_t launch_fill_zero_u32(uint32_t* p, size_t n, hipStream_t s);
+hipError_t launch_read_probe(const void* p, size_t n16, uint32_t* sink, unsigned grid, hipStream_t s);
 hipError_t launch_ctrl_set(Ctrl* c, int pos, int cur, hipStream_t s);
 hipError_t launch_embed(const Packed& E, const int32_t* tok, void* out, int fp32, hipStream_t s);
 hipError_t launch_argmax(const float* logits, int n, float* part_v, int* part_i, int nparts,

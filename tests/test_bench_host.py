@@ -20,13 +20,38 @@ def test_more_than_one_gpu_is_refused():
 
 
 def test_traffic_is_withheld_when_the_sources_differ(monkeypatch):
-    monkeypatch.setattr(bench, "f1_source_hash", lambda: "0" * 64)
+    monkeypatch.setattr(bench, "chain_source_hash", lambda: "0" * 64)
     assert bench.profiled_traffic() is None
 
 
+def _chain_weight_bytes(shape):
+    """Packed Q4_0 bytes of every matrix the chained launches read: all of the
+    slice's matrices except layer 0's mixer input projections (which run before
+    the first chain)."""
+    import synth
+    total = 0
+    for l in range(shape.n_layers):
+        for name, (r, c) in synth.matrix_shapes(shape, l).items():
+            if l == 0 and name in ("dn_q", "dn_k", "dn_v", "dn_a", "dn_b", "dn_z", "wq", "wg", "wk", "wv"):
+                continue
+            total += r * c // 32 * 18
+    return total
+
+
+def test_chain_bytes_cover_the_slice_weights():
+    import synth
+    sh = synth.HYBRID_5120
+    w = _chain_weight_bytes(sh)
+    b = bench.chain_step_bytes(sh, synth.Q4_0)
+    # 255 products over the step, each with its fp32 input and output vectors (< 200 KB each)
+    assert w < b < w + 255 * 200_000
+
+
 def test_traffic_of_the_committed_profile():
+    import synth
     t = bench.profiled_traffic()
     if t is None:
-        pytest.skip("the gate/up GEMV sources changed after its PMC traffic was taken")
-    # measured HBM bytes per launch against 100 429 824 algorithmic bytes
-    assert 100_429_824 <= t <= 1.01 * 100_429_824
+        pytest.skip("the chained-products kernel sources changed after its PMC traffic was taken")
+    alg = bench.chain_step_bytes(synth.HYBRID_5120, synth.Q4_0) / 64
+    # measured HBM bytes per launch against the algorithmic bytes: no re-read of weights
+    assert 0.99 * alg <= t <= 1.05 * alg

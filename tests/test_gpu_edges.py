@@ -179,3 +179,17 @@ def test_hybrid_64_layer_q8_slice():
     assert rel_err(s.get_hidden().cpu().numpy()[0], orc.decode(H[5], raw=True)) <= TOL
     del s
     torch.cuda.empty_cache()
+
+
+@pytest.mark.parametrize("n16", [1, 4096 * 256 * 4 * 2 + 12345])
+def test_read_probe_reads_every_word_once(n16):
+    """The XOR of the probe's per-wave folds equals the XOR of every 32-bit
+    word of the buffer: each word was read exactly once (both the four-load
+    loop and the tail)."""
+    import layer_sliced_quantized_amd as slq
+    words = synth.stream(0, synth.WL_GEMV, 300, n16).integers(0, 2**32, size=4 * n16, dtype=np.uint32)
+    buf = torch.from_numpy(words.view(np.int32)).cuda()
+    sink = torch.zeros(4 * slq.READ_PROBE_GRID, dtype=torch.int32, device="cuda")
+    slq.read_probe(buf, sink)
+    got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+    assert got == np.bitwise_xor.reduce(words)
