@@ -85,13 +85,17 @@ def mixer_rows_cols(shape, l):
     return 2 * nk + 2 * nv + 2 * shape.dn_heads, nv
 
 
-def chain_step_bytes(shape, qtype) -> int:
-    """Algorithmic bytes of one decode step's chained-product launches (one per
-    layer): mixer output, gate/up, down and, except after the last layer, the
-    next layer's input projections -- packed weights plus fp32 activations."""
+def chain_step_bytes(shape, qtype, deltanet: bool = True) -> int:
+    """Algorithmic bytes of one decode step's chained launches (one per layer):
+    a DeltaNet layer's state update (fp32 state read and written, its input
+    projections' outputs read), mixer output, gate/up, down and, except after
+    the last layer, the next layer's input projections -- packed weights plus
+    fp32 activations."""
     H, F, n = shape.hidden, shape.ffn, shape.n_layers
     total = 0
     for l in range(n):
+        if deltanet and not shape.is_attention(l):
+            total += 2 * shape.dn_heads * shape.dn_dk * shape.dn_dv * 4 + 4 * mixer_rows_cols(shape, l)[0]
         total += gemv_bytes(H, mixer_rows_cols(shape, l)[1], qtype) + gemv_bytes(2 * F, H, qtype) + \
             gemv_bytes(H, F, qtype)
         if l + 1 < n:
@@ -476,6 +480,8 @@ def main() -> int:
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-chain", action="store_true",
                     help="decode with every product as its own kernel instead of the chained products (same results)")
+    ap.add_argument("--no-chain-dn", action="store_true",
+                    help="run the DeltaNet update as its own kernel before each layer's chained products (same results)")
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run 3 plain copies of a 512 MiB buffer (a known-size reference for PMC byte counters)")
     args = ap.parse_args()
@@ -491,6 +497,8 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.no_chain:
         slq.debug_override("CHAIN", 0)
+    if args.no_chain_dn:
+        slq.debug_override("CHAIN_DN", 0)
     threads = min(16, os.cpu_count() or 8)
     shape = synth.HYBRID_5120
     n_in = args.warmup + args.steps + args.profile_steps + 4 * (args.verify_rounds + 1) + 32 * (args.prefill_chunks + 1) + 16
@@ -536,10 +544,11 @@ def main() -> int:
     if not args.no_chain:
         chain_ms = time_gemv_op(s, "chain", args.gemv_reps) / shape.n_layers
         chain_launches = shape.n_layers * args.gemv_reps
-        rl_bytes = chain_step_bytes(shape, synth.Q4_0) // shape.n_layers
-        rl_kernel = (f"k_chain<2>: one launch per layer of the chained products (mixer output, RMSNorm + gate/up + "
-                     f"SwiGLU, down + residual, next layer's input projections), mean of {chain_launches} launches "
-                     f"over the 64 layers' weights in layer order, HIP events")
+        rl_bytes = chain_step_bytes(shape, synth.Q4_0, deltanet=not args.no_chain_dn) // shape.n_layers
+        rl_kernel = (f"k_chain<2>: one launch per layer of the chained phases (the DeltaNet state update in "
+                     f"DeltaNet layers, mixer output, RMSNorm + gate/up + SwiGLU, down + residual, next layer's "
+                     f"input projections), mean of {chain_launches} launches over the 64 layers in layer order, "
+                     f"HIP events")
         rl_ms = chain_ms
     else:
         rl_bytes = gemv_bytes(f1_rows, f1_cols, synth.Q4_0)

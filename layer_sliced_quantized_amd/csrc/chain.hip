@@ -47,6 +47,7 @@
 // can hold an older copy of it from this kernel, and the kernel boundary
 // drops copies from earlier kernels.
 #include "gemv_kernel.h"
+#include "deltanet.h"
 
 namespace slq {
 
@@ -56,7 +57,7 @@ constexpr int CHAIN_COPIES = 64;   // copies of each ready flag (pollers spread 
 constexpr int CHAIN_GROUPS = 32;   // completion groups per product
 __device__ __forceinline__ unsigned* chain_count(unsigned* sync, int p, int g) { return sync + 32 * (33 * p + g); }
 __device__ __forceinline__ unsigned* chain_ready(unsigned* sync, int p, int c) {
-  return sync + 32 * (132 + CHAIN_COPIES * p + c);
+  return sync + 32 * (33 * CHAIN_MAX_PHASES + CHAIN_COPIES * p + c);
 }
 
 // Poll one copy of a ready flag until it reaches `epoch` (wrap-safe compare).
@@ -74,6 +75,29 @@ __device__ __forceinline__ bool chain_wait(const unsigned* flag, unsigned epoch,
     }
   }
   return true;
+}
+
+// Row group rg of product p is done (wave 0, after its stores completed).
+// Row groups count in groups of gsize (one counter line each); the workgroup
+// that completes a group counts it on the product's line, and the one that
+// completes the last group sets the product's ready flags, so that no counter
+// line takes more than about 32 increments per launch.
+__device__ __forceinline__ void chain_complete(int p, int rg, int nrg, int gsize, unsigned* sync,
+                                               const unsigned& epoch_v, int lane) {
+  const unsigned epoch = __builtin_amdgcn_readfirstlane(epoch_v);
+  const int g = rg / gsize;
+  const int ngroups = (nrg + gsize - 1) / gsize;
+  const unsigned in_group = (unsigned)min(gsize, nrg - g * gsize);
+  unsigned old = 0;
+  if (lane == 0) old = __hip_atomic_fetch_add(chain_count(sync, p, g), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __builtin_amdgcn_readfirstlane(old);   // the whole wave is active here: lane 0's value
+  if (old + 1u != epoch * in_group) return;
+  if (lane == 0)
+    old = __hip_atomic_fetch_add(chain_count(sync, p, CHAIN_GROUPS), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  old = __builtin_amdgcn_readfirstlane(old);
+  // the workgroup that completes the product sets its ready flags, one copy per lane
+  if (old + 1u == epoch * (unsigned)ngroups)
+    __hip_atomic_store(chain_ready(sync, p, lane % CHAIN_COPIES), epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The restrict-qualified bases tell the compiler which memory this workgroup
@@ -184,29 +208,27 @@ __device__ __forceinline__ void chain_phase(const ChainPhase& ph, int p, int id,
     gemv_epilogue<QT, 1, EPI, true>(acc, rn, W, out, rg, lane);
   }
 
-  // This row group is done once its stores have completed.  Row groups count
-  // in groups of gsize (one counter line each); the workgroup that completes a
-  // group counts it on the product's line, and the one that completes the
-  // last group sets the product's ready flags, so that no counter line takes
-  // more than about 32 increments per launch.
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
-  const unsigned epoch = __builtin_amdgcn_readfirstlane(epoch_v);
-  const int nrg = W.nrg();
-  const int g = rg / gsize;
-  const int ngroups = (nrg + gsize - 1) / gsize;
-  const unsigned in_group = (unsigned)min(gsize, nrg - g * gsize);
-  unsigned old = 0;
-  if (lane == 0) old = __hip_atomic_fetch_add(chain_count(sync, p, g), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  old = __builtin_amdgcn_readfirstlane(old);   // the whole wave is active here: lane 0's value
-  if (old + 1u != epoch * in_group) return;
-  if (lane == 0)
-    old = __hip_atomic_fetch_add(chain_count(sync, p, CHAIN_GROUPS), 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  old = __builtin_amdgcn_readfirstlane(old);
-  // the workgroup that completes the product sets its ready flags, one copy per lane
-  if (old + 1u == epoch * (unsigned)ngroups)
-    __hip_atomic_store(chain_ready(sync, p, lane % CHAIN_COPIES), epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  chain_complete(p, rg, (int)W.nrg(), gsize, sync, epoch_v, lane);
+}
+
+// A DeltaNet layer's recurrent update as the chain's first phase (one decode
+// token): the separate kernel's workgroup body, with the output digits stored
+// coherently for the mixer output projection that follows in this kernel.
+// Each workgroup (a head's 32 state rows) counts as one row group once the
+// stores of all its waves have completed.
+template <int DKP>
+__device__ __forceinline__ void chain_dn_phase(const ChainArgs& args, int p, int id, unsigned* __restrict__ sync,
+                                               const unsigned& epoch_v) {
+  deltanet_rows<DKP, 1, true>(args.dn, 1, id);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (wave_id() != 0) return;
+  chain_complete(p, id, args.ph[p].nwg, args.gsize[p], sync, epoch_v, (int)(threadIdx.x & 63));
 }
 
 template <int QT>
@@ -226,6 +248,14 @@ __global__ __launch_bounds__(256) void k_chain(const ChainArgs args, const uint8
   while (p + 1 < args.nph && b >= args.first_wg[p + 1]) ++p;
   const int id = b - args.first_wg[p];
   switch (args.ph[p].epi) {
+    case EPI_DN:
+      switch (args.dn_dkp) {
+        case 4: chain_dn_phase<4>(args, p, id, sync, epoch_v); break;
+        case 8: chain_dn_phase<8>(args, p, id, sync, epoch_v); break;
+        case 12: chain_dn_phase<12>(args, p, id, sync, epoch_v); break;
+        default: chain_dn_phase<16>(args, p, id, sync, epoch_v); break;
+      }
+      break;
     case EPI_STORE:
       chain_phase<QT, EPI_STORE>(args.ph[p], p, id, args.gsize[p], wts, dig, ws, sync, ctrl, epoch_v, red, &s_ok);
       break;
@@ -242,6 +272,13 @@ hipError_t launch_chain(int qt, const ChainArgs& args, unsigned grid, const uint
                         unsigned* sync, Ctrl* ctrl, hipStream_t s) {
   if (args.nph < 1 || args.nph > CHAIN_MAX_PHASES || grid == 0 || (int)grid != args.first_wg[args.nph])
     return hipErrorInvalidValue;
+  // a DeltaNet phase comes first (it waits for nothing), with one workgroup per 32 state rows
+  for (int p = 0; p < args.nph; ++p)
+    if (args.ph[p].epi == EPI_DN &&
+        (p != 0 || args.ph[p].nwg != args.dn.heads * (args.dn.dv / 32) || args.dn.dv % 32 ||
+         args.dn.dk != 8 * args.dn_dkp || (args.dn_dkp != 4 && args.dn_dkp != 8 && args.dn_dkp != 12 &&
+                                           args.dn_dkp != 16) || args.dn.mode != DN_DECODE))
+      return hipErrorInvalidValue;
   if (qt == QT_Q4) k_chain<QT_Q4><<<grid, 256, 0, s>>>(args, weights, ws, ws, sync, ctrl);
   else k_chain<QT_Q8><<<grid, 256, 0, s>>>(args, weights, ws, ws, sync, ctrl);
   return hipGetLastError();

@@ -56,7 +56,7 @@ int override_int(const std::string& name, int dflt) {
 }
 
 bool override_name_ok(const std::string& n) {
-  if (n == "MFMA_MIN_T" || n == "EAGER" || n == "CHAIN" || n == "CHAIN_MAX") return true;
+  if (n == "MFMA_MIN_T" || n == "EAGER" || n == "CHAIN" || n == "CHAIN_MAX" || n == "CHAIN_DN") return true;
   static const char* kinds[] = {"G1", "G2", "F1", "F2", "HEAD", "GEMV", "G1P", "G2P", "F1P", "F2P"};
   for (const char* k : kinds)
     if (n == std::string("KS_") + k || n == std::string("W_") + k) return true;
@@ -388,6 +388,7 @@ struct slice {
   Packed packed(const Mat& m) const { return Packed{w + m.off, m.rows, m.cols, cfg.qtype}; }
   int mx_min_t = 0;   // GEMVs with at least this many tokens use the MFMA products (0: by format and plan)
   bool chain = false;                 // decode steps run the chained GEMV kernels
+  bool chain_dn = false;              // ... with each DeltaNet layer's update as their first phase
   struct ChainLaunch {
     int layer;                        // the layer whose mixer it follows
     ChainArgs args;                   // descriptors (kernel arguments)
@@ -419,6 +420,28 @@ static size_t attn_norm_off(const slice* s, int i) {
 
 // The mixer of layer i (DeltaNet update or attention) on the G1 output y1;
 // its output digits go to xu.
+// The DeltaNet update of layer i for T tokens in `mode`.
+static DnParams dn_params(slice* s, int i, int T, int mode) {
+  const slice_config& c = s->cfg;
+  const Layout& L = s->L;
+  const LayerLayout& ll = L.layers[i];
+  DnParams p{};
+  p.y = s->wsp<float>(L.y1);
+  p.y_stride = ll.g1.rows;
+  p.off_q = ll.off_q; p.off_k = ll.off_k; p.off_v = ll.off_v;
+  p.off_a = ll.off_a; p.off_b = ll.off_b; p.off_z = ll.off_z;
+  p.heads = c.dn_heads; p.dk = c.dn_dk; p.dv = c.dn_dv;
+  p.a_scale = c.dn_a_scale; p.a_bias = c.dn_a_bias; p.b_scale = c.dn_b_scale; p.z_scale = c.dn_z_scale;
+  p.state = reinterpret_cast<float*>(s->ws + L.dn + (size_t)ll.dn_index * L.dn_layer_bytes);
+  p.nslots = L.nslots;
+  p.mode = mode;
+  p.ctrl = s->ctrl();
+  p.u_out = nullptr;
+  p.next = s->act_u(T);
+  p.next_qt = c.qtype;
+  return p;
+}
+
 static int enqueue_mixer(slice* s, int i, int T, int mode, hipStream_t st) {
   const slice_config& c = s->cfg;
   const Layout& L = s->L;
@@ -448,21 +471,7 @@ static int enqueue_mixer(slice* s, int i, int T, int mode, hipStream_t st) {
     p.next_qt = c.qtype;
     HIPCHK(launch_attention(p, T, st));
   } else {
-    DnParams p{};
-    p.y = y1;
-    p.y_stride = ll.g1.rows;
-    p.off_q = ll.off_q; p.off_k = ll.off_k; p.off_v = ll.off_v;
-    p.off_a = ll.off_a; p.off_b = ll.off_b; p.off_z = ll.off_z;
-    p.heads = c.dn_heads; p.dk = c.dn_dk; p.dv = c.dn_dv;
-    p.a_scale = c.dn_a_scale; p.a_bias = c.dn_a_bias; p.b_scale = c.dn_b_scale; p.z_scale = c.dn_z_scale;
-    p.state = reinterpret_cast<float*>(s->ws + L.dn + (size_t)ll.dn_index * L.dn_layer_bytes);
-    p.nslots = L.nslots;
-    p.mode = mode;
-    p.ctrl = s->ctrl();
-    p.u_out = nullptr;
-    p.next = s->act_u(T);
-    p.next_qt = c.qtype;
-    HIPCHK(launch_deltanet(p, T, st));
+    HIPCHK(launch_deltanet(dn_params(s, i, T, mode), T, st));
   }
   return SLICE_OK;
 }
@@ -512,7 +521,7 @@ static int enqueue_step(slice* s, int T, int mode, hipStream_t st, Prof* prof = 
       SLQ_MARK(l0.attn ? SLICE_OP_ATT_IN : SLICE_OP_DN_IN);
     }
     for (int i = 0; i < nlay; ++i) {
-      if (only < 0) {
+      if (only < 0 && (L.layers[i].attn || !s->chain_dn)) {
         int rc = enqueue_mixer(s, i, 1, DN_DECODE, st);
         if (rc) return rc;
         SLQ_MARK(L.layers[i].attn ? SLICE_OP_ATTENTION : SLICE_OP_DELTANET);
@@ -655,6 +664,21 @@ static void build_chains(slice* s) {
       q.norm_w_off = (int64_t)norm_w;
     };
     const int nblkU = (L.nu + QK - 1) / QK;
+    if (s->chain_dn && !ll.attn) {
+      // the layer's DeltaNet update: one workgroup per 32 state rows of a head
+      ChainPhase& d = ph[n];
+      d = ChainPhase{};
+      d.epi = EPI_DN;
+      d.nwg = c.dn_heads * (c.dn_dv / 32);
+      d.rows = (int64_t)d.nwg * RG;   // counted as nwg row groups
+      d.ksplit = 1;
+      d.w = 4;
+      d.qt = c.qtype;
+      d.part_off = (int64_t)L.cpart[n % per];
+      d.cnt_off = (int64_t)L.ccnt[n % per];
+      d.xd_off = d.xs_off = d.ssq_off = d.y_off = d.nd_off = d.ns_off = d.ssq_out_off = d.norm_w_off = -1;
+      ++n;
+    }
     ChainPhase& g2 = add(ll.g2, ll.pg2, EPI_RESID);
     input(g2, L.xu_d, L.xu_s, nblkU, -1);
     if (c.ffn) {
@@ -690,6 +714,10 @@ static void build_chains(slice* s) {
         cl.args.gsize[k] = (nrg + 31) / 32;   // at most 32 completion groups
       }
       cl.grid = (unsigned)cl.args.first_wg[cl.args.nph];
+      if (!ll.attn && s->chain_dn) {
+        cl.args.dn = dn_params(s, i, 1, DN_DECODE);
+        cl.args.dn_dkp = c.dn_dk / 8;
+      }
       cl.sync = L.chain_sync + ((size_t)i * CHAIN_MAX_PHASES + first / per) * CHAIN_SYNC_BYTES;
       s->chain_launch.push_back(cl);
     }
@@ -1100,6 +1128,7 @@ int slice_load(const slice_config* cfg, void* weights_dev, void* workspace_dev, 
   if (he == hipSuccess && s->L.n_attn && cfg->rope_dims > 0)
     he = launch_rope_table(s->wsp<float>(s->L.rope), cfg->max_seq, cfg->rope_dims, cfg->rope_theta, S(stream));
   s->chain = chains_possible(s) && override_int("CHAIN", 1) != 0;
+  s->chain_dn = s->chain && override_int("CHAIN_DN", 1) != 0;
   if (s->chain) build_chains(s);
   if (he == hipSuccess) he = hipStreamCreate(&s->cap);
   if (he != hipSuccess) {

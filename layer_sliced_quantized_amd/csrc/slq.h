@@ -84,7 +84,7 @@ struct NormIn {
 };
 
 // GEMV epilogues
-enum Epi { EPI_STORE = 0, EPI_SWIGLU = 2, EPI_RESID = 3 };
+enum Epi { EPI_STORE = 0, EPI_SWIGLU = 2, EPI_RESID = 3, EPI_DN = 7 /* chained DeltaNet decode phase */ };
 
 // With ksplit > 1 the K tiles of a 64-row group are spread over ksplit
 // workgroups; each publishes its partial sums, and the last one to finish
@@ -149,53 +149,6 @@ hipError_t launch_embed(const Packed& E, const int32_t* tok, void* out, int fp32
 hipError_t launch_argmax(const float* logits, int n, float* part_v, int* part_i, int nparts,
                          int32_t* tok, hipStream_t s);
 
-// ------------------------------------------------------- chained single-token GEMVs
-// One kernel runs up to CHAIN_MAX_PHASES dependent single-token GEMVs of a
-// decode step (a layer's mixer output projection, the gate/up projection,
-// the down projection, the next layer's input projections).  Workgroups take
-// their place in start order from a ticket; phase p's workgroups first load
-// their weight tiles, then wait until every row group of phase p - 1 has
-// finished, then compute exactly what the separate GEMV kernel computes.
-constexpr int CHAIN_MAX_PHASES = 4;
-constexpr int CHAIN_SYNC_BYTES = 50176;  // per chain launch: completion counters and 64 ready-flag copies per product
-struct ChainPhase {   // one GEMV of the chain; lives in device memory
-  // every location is a byte offset: weights and norm weights into the
-  // weights buffer, everything else into the workspace
-  int64_t w_off, rows, cols;          // packed matrix
-  int64_t xd_off, xs_off;             // input digits and their block scales
-  int64_t ssq_off;                    // RMSNorm partial sums of the input (-1: none)
-  int64_t y_off, y_tstride;           // STORE: y; RESID: h; SWIGLU: -1
-  int64_t nd_off, ns_off;             // SWIGLU / RESID: output digits and scales
-  int64_t ssq_out_off;                // RESID: sums of squares of h
-  int64_t norm_w_off;                 // RESID: weights of the next RMSNorm
-  int64_t part_off, cnt_off;          // split-K partials and tickets
-  int x_nblk, n_nblk;                 // blocks per token of the input / output digits
-  int n_part;                         // partial sums per token of the input statistics
-  float inv_n, eps;                   // RMSNorm of the input: 1 / width, epsilon
-  int qt;                             // weight format (also of the output digits)
-  int ksplit;                         // split-K workgroups per row group
-  int nwg;                            // workgroups of this phase: row groups x ksplit
-  int epi;                            // EPI_STORE, EPI_SWIGLU or EPI_RESID
-  int w;                              // waves of the product (<= 4; the others idle)
-};
-// Kernel arguments of one chained launch (by value, so the workgroups read
-// their product's descriptor without a dependent memory load).
-struct ChainArgs {
-  ChainPhase ph[CHAIN_MAX_PHASES];
-  int nph;
-  int first_wg[CHAIN_MAX_PHASES + 1];   // workgroup index where product p starts; [nph] = grid
-  int gsize[CHAIN_MAX_PHASES];          // row groups per completion group of product p
-};
-// sync region of one chain launch (CHAIN_SYNC_BYTES, zero before its first
-// launch), each counter and flag in its own 128-byte line (u32 index):
-//   [32 (33 p + g)], g < 32: row groups of group g of product p finished (over
-//                    all launches); g = 32: groups of product p finished;
-//   [32 (132 + 64 p + c)]: copy c of product p's ready flag, the last launch
-//                    (1, 2, ...) whose product p is complete.
-hipError_t launch_chain(int qt, const ChainArgs& args, unsigned grid, const uint8_t* weights, uint8_t* ws,
-                        unsigned* sync, Ctrl* ctrl, hipStream_t s);
-// ctrl->err = 0 and the sync regions cleared (n_u32 words)
-hipError_t launch_chain_reset(unsigned* sync, size_t n_u32, Ctrl* ctrl, hipStream_t s);
 
 // DeltaNet update modes: DN_DECODE updates slot cur in place (one token);
 // DN_VERIFY writes the state after token t to slot (cur+1+t) % nslots and
@@ -219,6 +172,57 @@ struct DnParams {
 hipError_t launch_deltanet(const DnParams& p, int T, hipStream_t s);
 hipError_t launch_state_io(float* state, int nslots, const Ctrl* ctrl, int heads, int dk, int dv,
                            float* canon, int to_device, hipStream_t s);
+
+// ------------------------------------------------------- chained single-token GEMVs
+// One kernel runs up to CHAIN_MAX_PHASES dependent phases of a decode step: a
+// DeltaNet layer's recurrent update (EPI_DN), its mixer output projection,
+// the gate/up projection, the down projection, the next layer's input
+// projections.  A GEMV phase's workgroups first load their first weight tile,
+// then wait until every row group of the phase before has finished, then
+// compute exactly what the separate kernel computes (chain.hip).
+constexpr int CHAIN_MAX_PHASES = 5;
+// per chain launch: 33 counter lines and 64 ready-flag lines per product
+constexpr int CHAIN_SYNC_BYTES = (33 + 64) * CHAIN_MAX_PHASES * 128;
+struct ChainPhase {   // one GEMV of the chain; lives in device memory
+  // every location is a byte offset: weights and norm weights into the
+  // weights buffer, everything else into the workspace
+  int64_t w_off, rows, cols;          // packed matrix
+  int64_t xd_off, xs_off;             // input digits and their block scales
+  int64_t ssq_off;                    // RMSNorm partial sums of the input (-1: none)
+  int64_t y_off, y_tstride;           // STORE: y; RESID: h; SWIGLU: -1
+  int64_t nd_off, ns_off;             // SWIGLU / RESID: output digits and scales
+  int64_t ssq_out_off;                // RESID: sums of squares of h
+  int64_t norm_w_off;                 // RESID: weights of the next RMSNorm
+  int64_t part_off, cnt_off;          // split-K partials and tickets
+  int x_nblk, n_nblk;                 // blocks per token of the input / output digits
+  int n_part;                         // partial sums per token of the input statistics
+  float inv_n, eps;                   // RMSNorm of the input: 1 / width, epsilon
+  int qt;                             // weight format (also of the output digits)
+  int ksplit;                         // split-K workgroups per row group
+  int nwg;                            // workgroups of this phase: row groups x ksplit
+  int epi;                            // EPI_STORE, EPI_SWIGLU, EPI_RESID, or EPI_DN (rows = nwg workgroups)
+  int w;                              // waves of the product (<= 4; the others idle)
+};
+// Kernel arguments of one chained launch (by value, so the workgroups read
+// their product's descriptor without a dependent memory load).
+struct ChainArgs {
+  ChainPhase ph[CHAIN_MAX_PHASES];
+  int nph;
+  int first_wg[CHAIN_MAX_PHASES + 1];   // workgroup index where product p starts; [nph] = grid
+  int gsize[CHAIN_MAX_PHASES];          // row groups per completion group of product p
+  DnParams dn;                          // the EPI_DN phase: one decode token (T = 1)
+  int dn_dkp;                           // its d_k / 8
+};
+// sync region of one chain launch (CHAIN_SYNC_BYTES, zero before its first
+// launch), each counter and flag in its own 128-byte line (u32 index):
+//   [32 (33 p + g)], g < 32: row groups of group g of product p finished (over
+//                    all launches); g = 32: groups of product p finished;
+//   [32 (33 CHAIN_MAX_PHASES + 64 p + c)]: copy c of product p's ready flag, the last launch
+//                    (1, 2, ...) whose product p is complete.
+hipError_t launch_chain(int qt, const ChainArgs& args, unsigned grid, const uint8_t* weights, uint8_t* ws,
+                        unsigned* sync, Ctrl* ctrl, hipStream_t s);
+// ctrl->err = 0 and the sync regions cleared (n_u32 words)
+hipError_t launch_chain_reset(unsigned* sync, size_t n_u32, Ctrl* ctrl, hipStream_t s);
 
 struct AttnParams {
   const float* y;        // G1 output [T][y_stride]

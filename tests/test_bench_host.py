@@ -42,9 +42,12 @@ def test_chain_bytes_cover_the_slice_weights():
     import synth
     sh = synth.HYBRID_5120
     w = _chain_weight_bytes(sh)
-    b = bench.chain_step_bytes(sh, synth.Q4_0)
+    b = bench.chain_step_bytes(sh, synth.Q4_0, deltanet=False)
     # 255 products over the step, each with its fp32 input and output vectors (< 200 KB each)
     assert w < b < w + 255 * 200_000
+    # with the DeltaNet updates inside: the 48 layers' fp32 states (2 MB) read and written, plus their inputs
+    state = 48 * 2 * 32 * 128 * 128 * 4
+    assert b + state < bench.chain_step_bytes(sh, synth.Q4_0) < b + state + 48 * 100_000
 
 
 def test_traffic_of_the_committed_profile():
@@ -52,6 +55,6 @@ def test_traffic_of_the_committed_profile():
     t = bench.profiled_traffic()
     if t is None:
         pytest.skip("the chained-products kernel sources changed after its PMC traffic was taken")
-    alg = bench.chain_step_bytes(synth.HYBRID_5120, synth.Q4_0) / 64
+    alg = bench.chain_step_bytes(synth.HYBRID_5120, synth.Q4_0, deltanet="DeltaNet" in open(bench.TRAFFIC_PROFILE).read()) / 64
     # measured HBM bytes per launch against the algorithmic bytes: no re-read of weights
     assert 0.99 * alg <= t <= 1.05 * alg

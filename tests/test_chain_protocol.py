@@ -120,6 +120,7 @@ def run_launches(products, launches, resident, seed, xcds=8, reverse=False):
 # the model runs quickly, with the same split counts
 SHAPES = {
     "deltanet_layer": [(10, 4), (68, 2), (10, 8), (33, 4)],
+    "deltanet_layer_with_update": [(16, 1), (10, 4), (68, 2), (10, 8), (33, 4)],
     "attention_layer": [(10, 4), (68, 2), (10, 8), (32, 4)],
     "last_layer": [(10, 4), (68, 2), (10, 8)],
     "no_ffn": [(3, 1), (5, 2)],

@@ -1,8 +1,8 @@
 """Chained decode products against separate kernels, through the C ABI.
 
-Decode runs each layer's products after its mixer (mixer output, gate/up +
-SwiGLU, down, the next layer's input projections) as one kernel whose
-workgroups wait for the product before theirs.  With the same launch shapes
+Decode runs each layer's DeltaNet update (in DeltaNet layers) and the products
+after its mixer (mixer output, gate/up + SwiGLU, down, the next layer's input
+projections) as one kernel whose workgroups wait for the phase before theirs.  With the same launch shapes
 as the separate GEMV kernels, the results must be the same bits; they are
 also checked against the CPU oracle, and slice_sync_check must report no
 wait that gave up.
@@ -103,3 +103,13 @@ def test_chain_with_verify_and_graph_replays(ovr):
         x = _t(H[t])
         np.testing.assert_array_equal(a.decode(x).cpu().numpy(), b.decode(x).cpu().numpy())
     b.sync_check()
+
+
+@pytest.mark.parametrize("extra", [{"CHAIN_DN": 0}, {"CHAIN_MAX": 2}, {"CHAIN_MAX": 1}],
+                         ids=["deltanet_own_kernel", "two_phases_per_launch", "one_phase_per_launch"])
+def test_chain_variants_equal_separate_kernels(extra, ovr):
+    """The DeltaNet update as its own kernel, or the layer's phases spread over
+    several launches (the DeltaNet phase then alone in its launch): the same
+    bits as separate kernels, states included."""
+    ovr(**extra)
+    _compare(TINY_H, synth.Q4_0, 0, 4, ovr, 4, 99, [0, 1, 2], 3, prefill=20, max_seq=128, max_verify=4)
