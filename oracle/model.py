@@ -33,6 +33,17 @@ Readings where the pages are silent (each listed in the design notes):
   QK-norm before RoPE; RoPE rotates pairs (i, i + rope_dims/2);
   the new K/V row is rounded to fp16 before it is attended;
   attention scale 1/sqrt(head_dim); head h reads KV head h // (q_heads/kv_heads).
+
+The qwen3_5 form of the DeltaNet layers (deltanet_q35, selected by the
+shape's dn_variant): the pages name the layer kind only, so its details are
+read from the published form of the Gated DeltaNet mixer -- a depthwise causal
+conv (width dn_conv) over q|k|v then SiLU, its state the last dn_conv - 1
+inputs (rolled back with the recurrent state); value head h shares query/key
+head h // (heads / k_heads); q and k L2-normalised, q scaled by 1/sqrt(d_k);
+alpha = exp(-exp(A_log) softplus(c_a a + dt_bias)), beta = sigmoid(c_b b);
+the head output through rmsnorm(o) * w * silu(c_z z).  Parity with a real
+checkpoint is unpinned (no weights or reference outputs exist here); the
+functions are pinned by closed forms in the tests.
 """
 from __future__ import annotations
 
@@ -56,6 +67,11 @@ def sigmoid(z):
 def silu(z):
     z = np.asarray(z, dtype=np.float64)
     return z / (1.0 + np.exp(-z))
+
+
+def softplus(z):
+    """log(1 + e^z), computed as logaddexp(0, z) so large z does not overflow."""
+    return np.logaddexp(0.0, np.asarray(z, dtype=np.float64))
 
 
 def l2normalize(x: np.ndarray, eps: float = 1e-6) -> np.ndarray:
@@ -151,6 +167,49 @@ def deltanet_token(S: np.ndarray, row: np.ndarray, dk: int, dv: int) -> np.ndarr
     return deltanet_heads(S, q, k, v, sigmoid(a), sigmoid(b), sigmoid(z), dk, dv)
 
 
+def conv_silu(state: np.ndarray, x: np.ndarray, w: np.ndarray):
+    """Depthwise causal convolution of one token, then SiLU.
+
+    state: [C][K-1] the channels' previous K-1 inputs, oldest first; x: [C]
+    this token's inputs; w: [C][K] taps, tap K-1 applied to x.  Returns
+    (silu(sum_j w[c][j] window[c][j]) in fp64, the new state [C][K-1]: the
+    window without its oldest input, stored in fp32).
+    """
+    win = np.concatenate([np.asarray(state, dtype=np.float64), np.asarray(x, dtype=np.float64)[:, None]], axis=1)
+    y = np.sum(win * np.asarray(w, dtype=np.float64), axis=1)
+    return silu(y), win[:, 1:].astype(np.float32)
+
+
+def gated_rmsnorm(o: np.ndarray, z: np.ndarray, w: np.ndarray, eps: float) -> np.ndarray:
+    """RMSNorm of one head's output, weighted, times silu of the gate input."""
+    return rmsnorm(o, w, eps) * silu(z)
+
+
+def deltanet_heads_q35(S: np.ndarray, q, k, v, alpha, beta, z, norm_w, eps: float, dk: int, dv: int,
+                       k_heads: int) -> np.ndarray:
+    """One token of the qwen3_5-form Gated DeltaNet mixer over all value heads.
+
+    S: [heads, d_v, d_k] fp32, updated in place.  q, k: [k_heads * d_k]
+    (after the conv); v, z: [heads * d_v]; alpha, beta: [heads].  Value head h
+    reads query/key head h // (heads / k_heads); q and k are L2-normalised per
+    head and q is then scaled by 1/sqrt(d_k).  The update is the same rank-one
+    rule as deltanet_update; the head's output o goes through
+    rmsnorm(o) * norm_w * silu(z_h).  Returns [heads * d_v] in fp64.
+    """
+    heads = S.shape[0]
+    ratio = heads // k_heads
+    out = np.empty(heads * dv)
+    for hh in range(heads):
+        kh = hh // ratio
+        qh = l2normalize(q[kh * dk:(kh + 1) * dk]) / np.sqrt(dk)
+        kk = l2normalize(k[kh * dk:(kh + 1) * dk])
+        vh = v[hh * dv:(hh + 1) * dv]
+        S_new, o = deltanet_update(S[hh], qh, kk, vh, alpha[hh], beta[hh])
+        S[hh] = S_new.astype(np.float32)
+        out[hh * dv:(hh + 1) * dv] = gated_rmsnorm(o, z[hh * dv:(hh + 1) * dv], norm_w, eps)
+    return out
+
+
 def attention_heads(s, q, g, k, v, K: np.ndarray, V: np.ndarray, p: int, q_norm=None, k_norm=None) -> np.ndarray:
     """One token of (gated) grouped-query attention at position p.
 
@@ -206,12 +265,15 @@ class SliceOracle:
         self.pos = 0
         self.kv = {}
         self.dn = {}
+        self.conv = {}
         for l in range(begin, end):
             if shape.is_attention(l):
                 shp = (shape.kv_heads, max_seq, shape.head_dim)
                 self.kv[l] = (np.zeros(shp, np.float16), np.zeros(shp, np.float16))
             else:
                 self.dn[l] = np.zeros((shape.dn_heads, shape.dn_dv, shape.dn_dk), np.float32)
+                if shape.dn_variant:
+                    self.conv[l] = np.zeros((shape.conv_dim, shape.dn_conv - 1), np.float32)
         self._pending = None
 
     # ---- state setters (the synthetic prior context)
@@ -227,6 +289,9 @@ class SliceOracle:
     def set_state(self, layer: int, S: np.ndarray):
         self.dn[layer][...] = S.astype(np.float32)
 
+    def set_conv_state(self, layer: int, C: np.ndarray):
+        self.conv[layer][...] = C.astype(np.float32)
+
     # ---- matrix helper
     def _mv(self, layer, name, x):
         raw = self.W[layer][name]
@@ -237,6 +302,8 @@ class SliceOracle:
     # ---- sublayers
     def deltanet(self, l: int, h: np.ndarray) -> np.ndarray:
         s, W = self.s, self.W[l]
+        if s.dn_variant:
+            return self.deltanet_q35(l, h)
         x = rmsnorm(h, W["attn_norm"], s.eps)
         q = self._mv(l, "dn_q", x)
         k = self._mv(l, "dn_k", x)
@@ -248,6 +315,31 @@ class SliceOracle:
         beta = sigmoid(np.float64(np.float32(s.dn_b_scale)) * b)
         gate = sigmoid(np.float64(np.float32(s.dn_z_scale)) * z)
         u = deltanet_heads(self.dn[l], q, k, v, alpha, beta, gate, s.dn_dk, s.dn_dv)
+        return h + self._mv(l, "dn_out", u)
+
+    def deltanet_q35(self, l: int, h: np.ndarray) -> np.ndarray:
+        """The qwen3_5 form: the conv + SiLU on q|k|v with its state, the
+        decay alpha = exp(-exp(A_log) softplus(c_a a + dt_bias)), beta =
+        sigmoid(c_b b), gate input c_z z for the gated RMSNorm."""
+        s, W = self.s, self.W[l]
+        x = rmsnorm(h, W["attn_norm"], s.eps)
+        q = self._mv(l, "dn_q", x)
+        k = self._mv(l, "dn_k", x)
+        v = self._mv(l, "dn_v", x)
+        a = self._mv(l, "dn_a", x)
+        b = self._mv(l, "dn_b", x)
+        z = self._mv(l, "dn_z", x)
+        nk = s.k_heads * s.dn_dk
+        taps = np.asarray(W["dn_conv"], dtype=np.float64).reshape(s.conv_dim, s.dn_conv)
+        qkv, self.conv[l][...] = conv_silu(self.conv[l], np.concatenate([q, k, v]), taps)
+        q, k, v = qkv[:nk], qkv[nk:2 * nk], qkv[2 * nk:]
+        a_log = np.asarray(W["dn_alog"], dtype=np.float64)
+        dt_bias = np.asarray(W["dn_dtb"], dtype=np.float64)
+        alpha = np.exp(-np.exp(a_log) * softplus(np.float64(np.float32(s.dn_a_scale)) * a + dt_bias))
+        beta = sigmoid(np.float64(np.float32(s.dn_b_scale)) * b)
+        zg = np.float64(np.float32(s.dn_z_scale)) * z
+        u = deltanet_heads_q35(self.dn[l], q, k, v, alpha, beta, zg, W["dn_norm"], s.eps, s.dn_dk, s.dn_dv,
+                               s.k_heads)
         return h + self._mv(l, "dn_out", u)
 
     def attention(self, l: int, h: np.ndarray) -> np.ndarray:
@@ -294,11 +386,15 @@ class SliceOracle:
         if self._pending is not None:
             raise RuntimeError("verify while a verify is uncommitted")
         p0 = self.pos
-        saved = [{l: S.copy() for l, S in self.dn.items()}]
+
+        def snapshot():
+            return ({l: S.copy() for l, S in self.dn.items()}, {l: C.copy() for l, C in self.conv.items()})
+
+        saved = [snapshot()]
         outs = []
         for t in range(hid_in.shape[0]):
             outs.append(self._step(np.asarray(hid_in[t]).astype(np.float64)))
-            saved.append({l: S.copy() for l, S in self.dn.items()})
+            saved.append(snapshot())
         self._pending = (p0, saved)
         outs = np.stack(outs)
         return outs if raw else self._round_out(outs)
@@ -308,7 +404,9 @@ class SliceOracle:
         if not 0 <= accepted < len(saved):
             raise ValueError("accepted out of range")
         for l in self.dn:
-            self.dn[l][...] = saved[accepted][l]
+            self.dn[l][...] = saved[accepted][0][l]
+        for l in self.conv:
+            self.conv[l][...] = saved[accepted][1][l]
         self.pos = p0 + accepted
         self._pending = None
 

@@ -48,6 +48,8 @@ TENSOR_IDS = {
     # activations / state / cache
     "hidden": 50, "dn_state": 51, "kv_k": 52, "kv_v": 53, "gemv_x": 54,
     "accept": 55, "token": 56,
+    # qwen3_5 form of the DeltaNet layers: conv taps, decay parameters, gated-norm weights, conv state
+    "dn_conv": 17, "dn_alog": 18, "dn_dtb": 19, "dn_norm": 28, "dn_conv_state": 57,
 }
 
 
@@ -77,6 +79,22 @@ class ModelShape:
     dn_a_bias: float = 2.0
     dn_b_scale: float = 0.25
     dn_z_scale: float = 0.25
+    # qwen3_5 form of the DeltaNet layers (dn_variant = 1): a short causal
+    # conv of width dn_conv over q|k|v then SiLU, dn_k_heads query/key heads
+    # shared by the dn_heads value heads, q scaled by 1/sqrt(dk), decay
+    # exp(-exp(A_log) softplus(a + dt_bias)), output through a gated RMSNorm
+    dn_variant: int = 0
+    dn_k_heads: int = 0       # 0: dn_heads
+    dn_conv: int = 0
+
+    @property
+    def k_heads(self) -> int:
+        return self.dn_k_heads or self.dn_heads
+
+    @property
+    def conv_dim(self) -> int:
+        """Channels of the short conv: q | k | v."""
+        return 2 * self.k_heads * self.dn_dk + self.dn_heads * self.dn_dv
 
     def is_attention(self, layer: int) -> bool:
         if self.attn_period == 0:
@@ -100,6 +118,10 @@ HYBRID_5120 = ModelShape(
     dn_heads=32, dn_dk=128, dn_dv=128,
     q_heads=24, kv_heads=4, head_dim=256, rope_dims=64, rope_theta=1e7,
     qk_norm=True, attn_gate=True, eps=1e-6, ffn=17408, vocab=248320, tied_head=False)
+
+# The same hybrid with DeltaNet layers in the qwen3_5 form: 16 query/key heads
+# shared by the 32 value heads, a width-4 causal conv, gated RMSNorm output.
+HYBRID_5120_Q35 = dataclasses.replace(HYBRID_5120, name="hybrid_5120_q35", dn_variant=1, dn_k_heads=16, dn_conv=4)
 
 # Matrix shapes of the standalone GEMV sweep (rows x cols).
 GEMV_SHAPES = [(5120, 5120), (17408, 5120), (5120, 17408), (12288, 5120), (248320, 5120)]
@@ -146,7 +168,7 @@ def matrix_shapes(shape: ModelShape, layer: int) -> dict:
         m["wv"] = (nkv, H)
         m["wo"] = (H, nq)
     else:
-        nk = shape.dn_heads * shape.dn_dk
+        nk = shape.k_heads * shape.dn_dk
         nv = shape.dn_heads * shape.dn_dv
         m["dn_q"] = (nk, H)
         m["dn_k"] = (nk, H)
@@ -163,8 +185,15 @@ def matrix_shapes(shape: ModelShape, layer: int) -> dict:
 
 
 def vector_shapes(shape: ModelShape, layer: int) -> dict:
-    """Lengths of the fp32 norm-weight vectors of one layer (all ones)."""
+    """Lengths of the fp32 vectors of one layer: norm weights (all ones), and in
+    the qwen3_5 DeltaNet form the conv taps ([conv_dim][dn_conv]), A_log and
+    dt_bias per value head and the gated-norm weights (dn_extra_tensors)."""
     v = {"attn_norm": shape.hidden}
+    if shape.dn_variant and not shape.is_attention(layer):
+        v["dn_conv"] = shape.conv_dim * shape.dn_conv
+        v["dn_alog"] = shape.dn_heads
+        v["dn_dtb"] = shape.dn_heads
+        v["dn_norm"] = shape.dn_dv
     if shape.ffn:
         v["ffn_norm"] = shape.hidden
     if shape.is_attention(layer) and shape.qk_norm:
@@ -177,6 +206,8 @@ def layer_tensors(shape: ModelShape, qtype: int, seed: int, workload: int, layer
                   threads: int = 1) -> dict:
     """All tensors of one layer: raw GGUF blocks for matrices, fp32 ones for norm weights."""
     out = {name: np.ones(n, dtype=np.float32) for name, n in vector_shapes(shape, layer).items()}
+    if shape.dn_variant and not shape.is_attention(layer):
+        out.update(dn_extra_tensors(shape, seed, workload, layer))
     mats = matrix_shapes(shape, layer)
 
     def gen(item):
@@ -189,6 +220,32 @@ def layer_tensors(shape: ModelShape, qtype: int, seed: int, workload: int, layer
     else:
         out.update(dict(map(gen, mats.items())))
     return out
+
+
+def dn_extra_tensors(shape: ModelShape, seed: int, workload: int, layer: int) -> dict:
+    """fp32 parameters of a qwen3_5-form DeltaNet layer, drawn like a fresh
+    model's: conv taps U[-0.5, 0.5] ([conv_dim][dn_conv], tap dn_conv-1 on
+    the current input); A = U[1, 16] stored as A_log = log(A); dt =
+    exp(U[log 0.001, log 0.1]) stored as dt_bias = dt + log(1 - exp(-dt)) (the
+    value whose softplus is dt); gated-norm weights 1 + 0.1 N(0,1)."""
+    r = stream(seed, workload, layer, TENSOR_IDS["dn_conv"])
+    conv = r.uniform(-0.5, 0.5, size=shape.conv_dim * shape.dn_conv)
+    r = stream(seed, workload, layer, TENSOR_IDS["dn_alog"])
+    alog = np.log(r.uniform(1.0, 16.0, size=shape.dn_heads))
+    r = stream(seed, workload, layer, TENSOR_IDS["dn_dtb"])
+    dt = np.exp(r.uniform(np.log(0.001), np.log(0.1), size=shape.dn_heads))
+    dtb = dt + np.log(-np.expm1(-dt))
+    r = stream(seed, workload, layer, TENSOR_IDS["dn_norm"])
+    norm = 1.0 + 0.1 * r.standard_normal(shape.dn_dv)
+    return {"dn_conv": conv.astype(np.float32), "dn_alog": alog.astype(np.float32),
+            "dn_dtb": dtb.astype(np.float32), "dn_norm": norm.astype(np.float32)}
+
+
+def dn_conv_state0(seed: int, workload: int, layer: int, conv_dim: int, width: int) -> np.ndarray:
+    """Prior conv inputs of a qwen3_5-form DeltaNet layer: N(0,1) fp32,
+    [conv_dim][width - 1], oldest first."""
+    rng = stream(seed, workload, layer, TENSOR_IDS["dn_conv_state"])
+    return rng.standard_normal((conv_dim, width - 1)).astype(np.float32)
 
 
 def global_tensors(shape: ModelShape, qtype: int, seed: int, workload: int) -> dict:

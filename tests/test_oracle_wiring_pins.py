@@ -326,6 +326,158 @@ def test_deltanet_token_closed_form():
     pin_deltanet_token()
 
 
+# ------------------------------------------------ qwen3_5-form DeltaNet
+
+def silu_(z):
+    return z / (1.0 + math.exp(-z))
+
+
+def pin_conv_silu():
+    """Two channels, width 4: window = state (oldest first) then the input,
+    tap 3 on the input.  Channel 0: taps (0.5, -1, 2, 0.25) over (1, 2, 3, 5)
+    give 0.5 - 2 + 6 + 1.25 = 5.75; channel 1: taps (1, 0, 0, 0) pick the
+    oldest input, -1.  The new state drops the oldest input."""
+    state = np.array([[1.0, 2.0, 3.0], [-1.0, 0.0, 4.0]], np.float32)
+    x = np.array([5.0, -2.0])
+    w = np.array([[0.5, -1.0, 2.0, 0.25], [1.0, 0.0, 0.0, 0.0]])
+    y, st = omodel.conv_silu(state, x, w)
+    np.testing.assert_allclose(y, [silu_(5.75), silu_(-1.0)], rtol=1e-15)
+    np.testing.assert_array_equal(st, np.array([[2.0, 3.0, 5.0], [0.0, 4.0, -2.0]], np.float32))
+
+
+def pin_gated_rmsnorm():
+    """o = (3, 4): mean square 12.5; weights (1, 2); gate inputs (0, 1):
+    silu(0) = 0 silences the first entry, the second is 4 / sqrt(12.5 + eps)
+    * 2 * silu(1)."""
+    out = omodel.gated_rmsnorm(np.array([3.0, 4.0]), np.array([0.0, 1.0]), np.array([1.0, 2.0]), 1e-6)
+    np.testing.assert_allclose(out, [0.0, 4.0 / math.sqrt(12.5 + 1e-6) * 2.0 * silu_(1.0)], rtol=1e-14, atol=1e-300)
+
+
+def pin_deltanet_heads_q35():
+    """Four value heads of d_v = 3 sharing two query/key heads of d_k = 4
+    (heads 0, 1 read key head 0; heads 2, 3 key head 1).  Key head m has
+    q = c_q e_{jq} and k = c_k e_{jk} (jq != jk), so qh = rho e_jq / 2
+    (rho = c_q / sqrt(c_q^2 + 1e-6), 1/sqrt(d_k) = 1/2) and kh = kappa e_jk.
+    Column jq of S' is alpha S[:, jq], so o = (rho / 2) alpha S[:, jq]; the
+    head's output is rmsnorm(o) * w * silu(z_h)."""
+    heads, kheads, dk, dv = 4, 2, 4, 3
+    jq, jk = [0, 3], [2, 1]
+    cq, ck = [2.0, -0.5], [0.75, 3.0]
+    q = np.zeros(kheads * dk)
+    k = np.zeros(kheads * dk)
+    for m in range(kheads):
+        q[m * dk + jq[m]], k[m * dk + jk[m]] = cq[m], ck[m]
+    v = np.arange(heads * dv, dtype=np.float64) * 0.25 - 1.0
+    z = np.linspace(-1.5, 2.0, heads * dv)
+    alpha = np.array([0.9, 0.5, 0.25, 0.75])
+    beta = np.array([0.1, 0.6, 0.3, 0.8])
+    w = np.array([1.0, 0.5, 2.0])
+    S0 = synth.dn_state0(0, 94, 0, heads, dv, dk) * 10
+    S = S0.copy()
+    out = omodel.deltanet_heads_q35(S, q, k, v, alpha, beta, z, w, 1e-6, dk, dv, kheads)
+    for h in range(heads):
+        m = h // 2
+        rho = cq[m] / math.sqrt(cq[m] ** 2 + 1e-6)
+        o = (rho / 2.0) * alpha[h] * S0[h][:, jq[m]].astype(np.float64)
+        ms = np.mean(o * o)
+        want = o / math.sqrt(ms + 1e-6) * w * np.array([silu_(zz) for zz in z[h * dv:(h + 1) * dv]])
+        np.testing.assert_allclose(out[h * dv:(h + 1) * dv], want, rtol=1e-10, atol=1e-12)
+        np.testing.assert_allclose(S[h][:, jq[m]], (alpha[h] * S0[h][:, jq[m]].astype(np.float64)).astype(np.float32),
+                                   rtol=1e-6)
+
+
+TINY_Q35 = synth.ModelShape(
+    name="tiny_hybrid_q35", hidden=64, n_layers=4, attn_period=4,
+    dn_heads=2, dn_dk=32, dn_dv=32, q_heads=4, kv_heads=2, head_dim=32, rope_dims=16,
+    rope_theta=1e7, qk_norm=True, attn_gate=True, eps=1e-6, ffn=96, vocab=0,
+    dn_variant=1, dn_k_heads=1, dn_conv=4)
+
+
+def pin_deltanet_q35_layer():
+    """Layer 0 of a qwen3_5-form slice: two value heads of 32 sharing one
+    query/key head, conv taps (0, 0, 0, 1) on every channel (the conv passes
+    the current input; then SiLU) from a zero conv state.  q is one-hot at key
+    dimension 3 (0.5 x[7]), k at 10 (0.75 x[11]); head 0's v at 5 (x[21]),
+    head 1's at 2 (-0.5 x[23]); a = 2 x[30] and -x[31], b = 1.5 x[32] and
+    x[33]; every gate row is +-0.5 times one input entry.  alpha = exp(-exp(A_log)
+    softplus(0.125 a + dt_bias)), beta = sigmoid(0.25 b); column 3 of S' is
+    alpha S[:, 3], so o = alpha rho / sqrt(32) S[:, 3] with rho = unit(silu(0.5 x[7]));
+    column 10 becomes alpha (1 - beta kappa^2) S[:, 10] + beta kappa silu(v)
+    (kappa = unit(silu(0.75 x[11]))).  The new conv state's last column holds
+    the pre-conv q | k | v."""
+    sh = TINY_Q35
+    T = synth.layer_tensors(sh, synth.Q4_0, 0, 95, 0)
+    H, nk, nv = sh.hidden, sh.k_heads * sh.dn_dk, sh.dn_heads * sh.dn_dv
+    T["dn_q"] = onehot_q4(nk, H, {3: (7, 0.5, 1)})
+    T["dn_k"] = onehot_q4(nk, H, {10: (11, 0.75, 1)})
+    T["dn_v"] = onehot_q4(nv, H, {5: (21, 1.0, 1), 32 + 2: (23, 0.5, -1)})
+    T["dn_a"] = onehot_q4(2, H, {0: (30, 2.0, 1), 1: (31, 1.0, -1)})
+    T["dn_b"] = onehot_q4(2, H, {0: (32, 1.5, 1), 1: (33, 1.0, 1)})
+    zrows = {r: ((r * 7) % 64, 0.5, 1 if r % 2 == 0 else -1) for r in range(nv)}
+    T["dn_z"] = onehot_q4(nv, H, zrows)
+    taps = np.zeros((sh.conv_dim, 4), np.float32)
+    taps[:, 3] = 1.0
+    T["dn_conv"] = taps.reshape(-1)
+    shapes = synth.matrix_shapes(sh, 0)
+    for n in ("w_gate", "w_up", "w_down"):
+        T[n] = onehot_q4(*shapes[n], {})
+    orc = oracle.SliceOracle(sh, synth.Q4_0, 0, 1, {0: T}, max_seq=16, io_fp32=True)
+    S0 = synth.dn_state0(0, 95, 0, 2, 32, 32) * 10
+    orc.set_state(0, S0)
+    orc.reset(2)
+    h = _pm1(6, H)
+    out = orc.decode(h, raw=True)
+    x = S_NORM * h.astype(np.float64)
+
+    def unit(c):
+        return c / math.sqrt(c * c + 1e-6)
+
+    def softplus(t):
+        return math.log1p(math.exp(t))
+
+    alog, dtb, wn = (T[n].astype(np.float64) for n in ("dn_alog", "dn_dtb", "dn_norm"))
+    a = [2.0 * x[30], -1.0 * x[31]]
+    b = [1.5 * x[32], 1.0 * x[33]]
+    alpha = [math.exp(-math.exp(alog[hh]) * softplus(0.125 * a[hh] + dtb[hh])) for hh in range(2)]
+    beta = [sig(0.25 * b[hh]) for hh in range(2)]
+    rho = unit(silu_(0.5 * x[7]))
+    kappa = unit(silu_(0.75 * x[11]))
+    vv = np.zeros((2, 32))
+    vv[0, 5], vv[1, 2] = silu_(1.0 * x[21]), silu_(-0.5 * x[23])
+    S = S0.astype(np.float64)
+    u = np.empty(nv)
+    for hh in range(2):
+        Sn = alpha[hh] * S[hh]
+        Sn[:, 10] = alpha[hh] * (1 - beta[hh] * kappa ** 2) * S[hh][:, 10] + beta[hh] * kappa * vv[hh]
+        np.testing.assert_allclose(orc.dn[0][hh], Sn.astype(np.float32), rtol=1e-6, atol=1e-9)
+        o = rho / math.sqrt(32.0) * Sn[:, 3]
+        zg = np.array([0.25 * zrows[r][2] * 0.5 * x[zrows[r][0]] for r in range(hh * 32, hh * 32 + 32)])
+        u[hh * 32:(hh + 1) * 32] = o / math.sqrt(np.mean(o * o) + 1e-6) * wn * np.array([silu_(t) for t in zg])
+    Wout = qref.dequant(synth.Q4_0, T["dn_out"], H, nv)
+    np.testing.assert_allclose(out, h.astype(np.float64) + Wout @ u, rtol=1e-9, atol=1e-12)
+    pre = np.zeros(sh.conv_dim)
+    pre[3], pre[nk + 10] = 0.5 * x[7], 0.75 * x[11]
+    pre[2 * nk + 5], pre[2 * nk + 32 + 2] = 1.0 * x[21], -0.5 * x[23]
+    np.testing.assert_allclose(orc.conv[0][:, 2], pre.astype(np.float32), rtol=1e-6, atol=1e-12)
+    assert not orc.conv[0][:, :2].any()
+
+
+def test_conv_silu_closed_form():
+    pin_conv_silu()
+
+
+def test_gated_rmsnorm_closed_form():
+    pin_gated_rmsnorm()
+
+
+def test_deltanet_heads_q35_closed_form():
+    pin_deltanet_heads_q35()
+
+
+def test_deltanet_q35_layer_closed_form():
+    pin_deltanet_q35_layer()
+
+
 MUTANTS = {
     "ffn_gate_up_swapped": ("SliceOracle.ffn", 'silu(self._mv(l, "w_gate", x)) * self._mv(l, "w_up", x)',
                             'silu(self._mv(l, "w_up", x)) * self._mv(l, "w_gate", x)'),
@@ -348,10 +500,26 @@ MUTANTS = {
     "dn_token_a_b_swapped": ("deltanet_token", "sigmoid(a), sigmoid(b)", "sigmoid(b), sigmoid(a)"),
     "dn_token_q_k_swapped": ("deltanet_token", "deltanet_heads(S, q, k, v,", "deltanet_heads(S, k, q, v,"),
     "dn_token_z_offset": ("deltanet_token", "z = row[o:o + heads * dv]", "z = row[o - heads:o - heads + heads * dv]"),
+    "q35_conv_taps_reversed": ("conv_silu", "y = np.sum(win * np.asarray(w, dtype=np.float64), axis=1)",
+                               "y = np.sum(win * np.asarray(w, dtype=np.float64)[:, ::-1], axis=1)"),
+    "q35_conv_state_not_shifted": ("conv_silu", "win[:, 1:].astype(np.float32)", "win[:, :-1].astype(np.float32)"),
+    "q35_q_scale_dropped": ("deltanet_heads_q35", "l2normalize(q[kh * dk:(kh + 1) * dk]) / np.sqrt(dk)",
+                            "l2normalize(q[kh * dk:(kh + 1) * dk])"),
+    "q35_head_share_mod": ("deltanet_heads_q35", "kh = hh // ratio", "kh = hh % k_heads"),
+    "q35_gate_sigmoid": ("gated_rmsnorm", "* silu(z)", "* sigmoid(z)"),
+    "q35_norm_weight_dropped": ("gated_rmsnorm", "rmsnorm(o, w, eps)", "rmsnorm(o, np.ones_like(w), eps)"),
+    "q35_softplus_dropped": ("SliceOracle.deltanet_q35", "softplus(np.float64(np.float32(s.dn_a_scale)) * a + dt_bias)",
+                             "(np.float64(np.float32(s.dn_a_scale)) * a + dt_bias)"),
+    "q35_alog_not_exp": ("SliceOracle.deltanet_q35", "-np.exp(a_log)", "-a_log"),
+    "q35_qkv_order": ("SliceOracle.deltanet_q35", "np.concatenate([q, k, v])", "np.concatenate([k, q, v])"),
+    "q35_beta_coeff": ("SliceOracle.deltanet_q35", "sigmoid(np.float64(np.float32(s.dn_b_scale)) * b)",
+                       "sigmoid(np.float64(np.float32(s.dn_a_scale)) * b)"),
+    "q35_gate_coeff": ("SliceOracle.deltanet_q35", "zg = np.float64(np.float32(s.dn_z_scale)) * z", "zg = z"),
     "dn_v_for_k": ("deltanet_heads", "vh = v[hh * dv:(hh + 1) * dv]", "vh = k[hh * dv:(hh + 1) * dv]"),
 }
 
-PINS = [pin_ffn, pin_attention, pin_attention_key, pin_deltanet, pin_deltanet_token]
+PINS = [pin_ffn, pin_attention, pin_attention_key, pin_deltanet, pin_deltanet_token, pin_conv_silu,
+        pin_gated_rmsnorm, pin_deltanet_heads_q35, pin_deltanet_q35_layer]
 
 
 def _mutant(where: str, old: str, new: str):
@@ -377,3 +545,27 @@ def test_pins_catch_planted_mistake(name, monkeypatch):
         except AssertionError:
             caught.append(pin.__name__)
     assert caught, f"no pin fails when the oracle has the mistake {name}"
+
+
+def test_q35_commit_restores_conv_state():
+    """verify(3) then commit(1) leaves the states (recurrent and conv) of one
+    plain decode step, and the next steps agree."""
+    sh = TINY_Q35
+    tensors = {l: synth.layer_tensors(sh, synth.Q4_0, 0, 96, l) for l in range(4)}
+    orcs = [oracle.SliceOracle(sh, synth.Q4_0, 0, 4, tensors, max_seq=32, io_fp32=True) for _ in range(2)]
+    for orc in orcs:
+        for l in range(3):
+            orc.set_state(l, synth.dn_state0(0, 96, l, sh.dn_heads, sh.dn_dv, sh.dn_dk))
+            orc.set_conv_state(l, synth.dn_conv_state0(0, 96, l, sh.conv_dim, sh.dn_conv))
+        orc.reset(5)
+    H = synth.hidden_inputs(0, 96, 6, sh.hidden).astype(np.float32)
+    a, b = orcs
+    a.verify(H[0:3], raw=True)
+    a.commit(1)
+    b.decode(H[0], raw=True)
+    for l in range(3):
+        np.testing.assert_array_equal(a.dn[l], b.dn[l])
+        np.testing.assert_array_equal(a.conv[l], b.conv[l])
+        assert not np.array_equal(a.conv[l], synth.dn_conv_state0(0, 96, l, sh.conv_dim, sh.dn_conv))
+    for t in range(3, 6):
+        np.testing.assert_array_equal(a.decode(H[t], raw=True), b.decode(H[t], raw=True))
