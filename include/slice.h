@@ -222,14 +222,28 @@ typedef struct slice_config {
     int32_t max_verify;             /* largest k for slice_verify (<= 16)               */
     int32_t qtype;                  /* SLICE_Q4_0 or SLICE_Q8_0                         */
     int32_t io_fp32;                /* boundary vectors: 0 = fp16, 1 = fp32             */
+    /* The qwen3_5 form of the Gated DeltaNet layers (ChatTorrent README, "What
+     * it can run", names the layer kind; the form is the published mixer):
+     * dn_variant = 1 runs a depthwise causal conv of width dn_conv (2..4) over
+     * the q | k | v projections, then SiLU; dn_k_heads query/key heads are
+     * shared by the dn_heads value heads (dn_heads % dn_k_heads == 0); q is
+     * L2-normalised then scaled by 1/sqrt(dn_dk); alpha = exp(-exp(A_log) *
+     * softplus(a_scale * (W_a x) + dt_bias)), beta = sigmoid(b_scale * (W_b x));
+     * each head's output o becomes rmsnorm(o) * w * silu(z_scale * (W_z x)).
+     * dn_a_bias is unused then.  dn_variant = 0: the form described above. */
+    int32_t dn_variant;
+    int32_t dn_k_heads;             /* 0: dn_heads                                      */
+    int32_t dn_conv;                /* conv width (dn_variant = 1)                      */
 } slice_config;
 
 /* Tensor ids for slice_set_tensor.  Matrices take raw GGUF blocks
  * (rows x cols/32 blocks, device); vectors take fp32 (device).
  *   layer tensors: attention layers use WQ, WG (if attn_gate), WK, WV, WO,
- *   Q_NORM/K_NORM (if qk_norm); DeltaNet layers use DN_Q/K/V ([heads*dk or
- *   heads*dv] x H), DN_A/DN_B ([heads] x H), DN_Z ([heads*dv] x H), DN_OUT
- *   (H x [heads*dv]); every layer uses ATTN_NORM, and FFN_NORM, W_GATE, W_UP
+ *   Q_NORM/K_NORM (if qk_norm); DeltaNet layers use DN_Q/K ([k_heads*dk] x H,
+ *   k_heads = dn_k_heads or dn_heads), DN_V ([heads*dv] x H), DN_A/DN_B
+ *   ([heads] x H), DN_Z ([heads*dv] x H), DN_OUT (H x [heads*dv]), and with
+ *   dn_variant = 1 also DN_CONV, DN_ALOG, DN_DTB, DN_NORM (below); every
+ *   layer uses ATTN_NORM, and FFN_NORM, W_GATE, W_UP
  *   (ffn x H), W_DOWN (H x ffn) if ffn > 0.
  *   global tensors (layer argument ignored): EMBED (vocab x H), HEAD (if not
  *   tied), OUT_NORM.                                                         */
@@ -240,7 +254,12 @@ enum {
     SLICE_T_WQ = 20, SLICE_T_WG = 21, SLICE_T_WK = 22, SLICE_T_WV = 23, SLICE_T_WO = 24,
     SLICE_T_Q_NORM = 25, SLICE_T_K_NORM = 26,
     SLICE_T_W_GATE = 30, SLICE_T_W_UP = 31, SLICE_T_W_DOWN = 32,
-    SLICE_T_EMBED = 40, SLICE_T_HEAD = 41, SLICE_T_OUT_NORM = 42
+    SLICE_T_EMBED = 40, SLICE_T_HEAD = 41, SLICE_T_OUT_NORM = 42,
+    /* DeltaNet layers with dn_variant = 1 (fp32): DN_CONV [conv_dim][dn_conv]
+     * taps (conv_dim = 2*dn_k_heads*dn_dk + dn_heads*dn_dv channels in the
+     * order q | k | v, tap dn_conv-1 on the current input), DN_ALOG and DN_DTB
+     * [dn_heads], DN_NORM [dn_dv] (gated-norm weights, shared by the heads) */
+    SLICE_T_DN_CONV = 17, SLICE_T_DN_ALOG = 18, SLICE_T_DN_DTB = 19, SLICE_T_DN_NORM = 28
 };
 
 /* A stage owns the weights, cache and recurrent state of its own layer range
@@ -424,6 +443,12 @@ int slice_dbg_set_kv(slice_t *s, int layer, const uint16_t *k_dev, const uint16_
                      int rows, void *stream);
 int slice_dbg_get_kv(slice_t *s, int layer, uint16_t *k_dev, uint16_t *v_dev,
                      int rows, void *stream);
+
+/* Conv state of DeltaNet `layer` (dn_variant = 1): the last dn_conv - 1 inputs
+ * of every conv channel, canonical fp32 [conv_dim][dn_conv - 1], oldest
+ * first, current slot (rolled back with the recurrent state).               */
+int slice_dbg_set_conv(slice_t *s, int layer, const float *src_dev, void *stream);
+int slice_dbg_get_conv(slice_t *s, int layer, float *dst_dev, void *stream);
 
 /* fp32 residual stream h [k][hidden] at the end of the last decode (k = 1) or
  * verify (k tokens) step, before the boundary conversion.  For checking

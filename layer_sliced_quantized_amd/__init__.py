@@ -208,6 +208,9 @@ def make_config(shape, qtype: int, begin: int, end: int, *, max_seq: int = 1024,
     c.max_seq, c.max_verify = max_seq, max_verify
     c.qtype = qtype
     c.io_fp32 = int(io_fp32)
+    c.dn_variant = int(getattr(shape, "dn_variant", 0))
+    c.dn_k_heads = int(getattr(shape, "dn_k_heads", 0))
+    c.dn_conv = int(getattr(shape, "dn_conv", 0))
     return c
 
 
@@ -276,6 +279,21 @@ class Slice:
         c = self.cfg
         out = torch.empty((c.dn_heads, c.dn_dv, c.dn_dk), dtype=torch.float32, device=self.device)
         check(lib().slice_dbg_get_state(self.handle, layer, _ptr(out), _stream(stream)))
+        return out
+
+    def conv_dim(self) -> int:
+        c = self.cfg
+        return 2 * (c.dn_k_heads or c.dn_heads) * c.dn_dk + c.dn_heads * c.dn_dv
+
+    def set_conv_state(self, layer: int, C: torch.Tensor, stream=None):
+        """Conv inputs of a qwen3_5-form DeltaNet layer, fp32 [conv_dim][dn_conv - 1]."""
+        C = C.to(device=self.device, dtype=torch.float32).contiguous()
+        check(lib().slice_dbg_set_conv(self.handle, layer, _ptr(C), _stream(stream)))
+        torch.cuda.synchronize()
+
+    def get_conv_state(self, layer: int, stream=None) -> torch.Tensor:
+        out = torch.empty((self.conv_dim(), self.cfg.dn_conv - 1), dtype=torch.float32, device=self.device)
+        check(lib().slice_dbg_get_conv(self.handle, layer, _ptr(out), _stream(stream)))
         return out
 
     def set_kv(self, layer: int, K: torch.Tensor, V: torch.Tensor, stream=None):

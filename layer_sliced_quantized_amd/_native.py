@@ -22,6 +22,7 @@ TENSOR_IDS = {
     "wq": 20, "wg": 21, "wk": 22, "wv": 23, "wo": 24, "q_norm": 25, "k_norm": 26,
     "w_gate": 30, "w_up": 31, "w_down": 32,
     "embed": 40, "head": 41, "out_norm": 42,
+    "dn_conv": 17, "dn_alog": 18, "dn_dtb": 19, "dn_norm": 28,
 }
 
 
@@ -43,6 +44,7 @@ class SliceConfig(ctypes.Structure):
         ("tied_head", ctypes.c_int32),
         ("max_seq", ctypes.c_int32), ("max_verify", ctypes.c_int32),
         ("qtype", ctypes.c_int32), ("io_fp32", ctypes.c_int32),
+        ("dn_variant", ctypes.c_int32), ("dn_k_heads", ctypes.c_int32), ("dn_conv", ctypes.c_int32),
     ]
 
 
@@ -105,6 +107,8 @@ _SIGS = {
     "slice_last_error": (ctypes.c_char_p, []),
     "slice_dbg_set_state": (_I, [_V, _I, _V, _V]),
     "slice_dbg_get_state": (_I, [_V, _I, _V, _V]),
+    "slice_dbg_get_conv": (_I, [_V, _I, _V, _V]),
+    "slice_dbg_set_conv": (_I, [_V, _I, _V, _V]),
     "slice_dbg_set_kv": (_I, [_V, _I, _V, _V, _I, _V]),
     "slice_dbg_get_kv": (_I, [_V, _I, _V, _V, _I, _V]),
     "slice_dbg_get_hidden": (_I, [_V, _V, _I, _V]),

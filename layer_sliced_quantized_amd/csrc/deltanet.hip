@@ -220,9 +220,172 @@ __global__ __launch_bounds__(1024) void k_deltanet_chunk(DnParams p, int T) {
   }
 }
 
+// The qwen3_5 form (DnParams::variant = 1): one workgroup per value head h,
+// dv / 8 waves with eight lanes per row of S as in deltanet_rows, the T
+// tokens in order.  Per token:
+//   1. conv: thread c < 2 dk + dv owns channel c of this head's q | k | v
+//      (q, k of query/key head kh = h / (heads / k_heads)); it keeps the
+//      channel's last conv - 1 inputs, applies the taps to them (oldest
+//      first) and to the new input, then SiLU.  Every value head keeps its own
+//      copy of the q and k windows, so no two workgroups share state.  The
+//      windows go to the conv-state slot of the token (decode: slot cur in
+//      place; verify: slot (cur + 1 + t), slot cur untouched).
+//   2. q and k L2-normalised (one wave each), q scaled by 1/sqrt(dk); alpha =
+//      exp(-exp(A_log) softplus(a_scale a + dt_bias)), beta = sigmoid(b_scale b);
+//   3. the row update of deltanet_rows;
+//   4. rmsnorm of the head's output over its dv rows, times the weights and
+//      silu(z_scale z), quantised into the output digits.
+// Conv-state slot layout: [head][2 dk + dv channels][conv - 1], oldest first.
+template <int DKP>
+__global__ __launch_bounds__(1024) void k_deltanet_q35(DnParams p, int T) {
+  constexpr int DK = 8 * DKP;
+  __shared__ float qraw[DK], kraw[DK], qs[DK], ksh[DK];
+  __shared__ float vsh[128], zsh[128], osh[128];
+  __shared__ float sc[3];
+  const int h = blockIdx.x;
+  const int kh = h / (p.heads / p.k_heads);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int part = lane >> 3, r = lane & 7;
+  const int i = wave * 8 + r;     // row of S (value index); the launch has dv / 8 waves
+  const int K = p.conv;
+  const int nch = 2 * DK + p.dv;  // this head's conv channels
+  const int nv = p.heads * p.dv;
+  const int cur = p.ctrl ? p.ctrl->cur : 0;
+
+  // 1. this thread's conv channel: taps, window, and where its input lies in y
+  int yoff = -1;
+  if (tid < DK) yoff = p.off_q + kh * DK + tid;
+  else if (tid < 2 * DK) yoff = p.off_k + kh * DK + (tid - DK);
+  else if (tid < nch) yoff = p.off_v + h * p.dv + (tid - 2 * DK);
+  const int cglob = tid < DK ? kh * DK + tid
+                  : tid < 2 * DK ? p.k_heads * DK + kh * DK + (tid - DK)
+                                 : 2 * p.k_heads * DK + h * p.dv + (tid - 2 * DK);
+  const size_t cst = ((size_t)h * nch + tid) * (K - 1);   // this channel's window inside a slot
+  float win[3] = {0.0f, 0.0f, 0.0f}, taps[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  if (yoff >= 0) {
+    const float* st = p.conv_state + (size_t)cur * p.conv_slot + cst;
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < K - 1) win[j] = st[j];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j < K) taps[j] = p.conv_w[(size_t)cglob * K + j];
+  }
+  const size_t hs = (size_t)DK * p.dv;
+  const float* S_in = p.state + ((size_t)cur * p.heads + h) * hs;
+  const int j0 = part * DKP;
+  const size_t sbase = dn_off(i, j0, DKP);
+  float S[DKP];
+#pragma unroll
+  for (int jj = 0; jj < DKP; ++jj) S[jj] = S_in[sbase + (size_t)jj * 64];
+  const float wn = tid < p.dv ? p.norm_w[tid] : 0.0f;
+  const float a_coef = expf(p.a_log[h]), dtb = p.dt_bias[h];
+
+  for (int t = 0; t < T; ++t) {
+    const float* y = p.y + (size_t)t * p.y_stride;
+    if (yoff >= 0) {
+      const float x = y[yoff];
+      float c = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (j < K - 1) c = __builtin_fmaf(taps[j], win[j], c);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (j == K - 1) c = __builtin_fmaf(taps[j], x, c);
+      const float sv = c / (1.0f + expf(-c));
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        if (j + 1 < K - 1) win[j] = win[j + 1];
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (j == K - 2) win[j] = x;
+      float* dst = p.conv_state + (size_t)(p.mode == DN_VERIFY ? (cur + 1 + t) % p.nslots : cur) * p.conv_slot + cst;
+#pragma unroll
+      for (int j = 0; j < 3; ++j)
+        if (j < K - 1) dst[j] = win[j];
+      if (tid < DK) qraw[tid] = sv;
+      else if (tid < 2 * DK) kraw[tid - DK] = sv;
+      else vsh[tid - 2 * DK] = sv;
+    }
+    if (tid < p.dv) zsh[tid] = p.z_scale * y[p.off_z + h * p.dv + tid];
+    if (tid == 0) {
+      const float av = p.a_scale * y[p.off_a + h] + dtb;
+      const float spl = av > 20.0f ? av : log1pf(expf(av));
+      sc[0] = expf(-a_coef * spl);
+      sc[1] = sigmoidf_(p.b_scale * y[p.off_b + h]);
+    }
+    __syncthreads();
+    // 2. q (wave 0) and k (wave 1) normalised
+    if (wave < 2) {
+      const float* src = wave == 0 ? qraw : kraw;
+      const float a0 = lane < DK ? src[lane] : 0.0f, a1 = lane + 64 < DK ? src[lane + 64] : 0.0f;
+      const float ss = wave_sum(a0 * a0 + a1 * a1);
+      float rn = 1.0f / sqrtf(ss + 1e-6f);
+      if (wave == 0) rn *= 1.0f / sqrtf((float)DK);
+      float* dst = wave == 0 ? qs : ksh;
+      if (lane < DK) dst[lane] = a0 * rn;
+      if (lane + 64 < DK) dst[lane + 64] = a1 * rn;
+    }
+    __syncthreads();
+    // 3. the rows of S
+    const float alpha = sc[0], beta = sc[1];
+    float up = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < DKP; ++jj) up = __builtin_fmaf(S[jj], ksh[j0 + jj], up);
+    up = row_sum8(up);
+    const float cc = beta * (vsh[i] - alpha * up);
+    float op = 0.0f;
+#pragma unroll
+    for (int jj = 0; jj < DKP; ++jj) {
+      S[jj] = __builtin_fmaf(cc, ksh[j0 + jj], alpha * S[jj]);
+      op = __builtin_fmaf(S[jj], qs[j0 + jj], op);
+    }
+    op = row_sum8(op);
+    if (part == 0) osh[i] = op;
+    float* S_out = p.mode == DN_VERIFY ? p.state + ((size_t)((cur + 1 + t) % p.nslots) * p.heads + h) * hs
+                            : const_cast<float*>(S_in);
+#pragma unroll
+    for (int jj = 0; jj < DKP; ++jj) S_out[sbase + (size_t)jj * 64] = S[jj];
+    __syncthreads();
+    // 4. gated RMSNorm of the head's output, then its digits (half-wave per 32 rows)
+    if (wave == 0) {
+      const float a0 = lane < p.dv ? osh[lane] : 0.0f, a1 = lane + 64 < p.dv ? osh[lane + 64] : 0.0f;
+      const float ss = wave_sum(a0 * a0 + a1 * a1);
+      if (lane == 0) sc[2] = 1.0f / sqrtf(ss / (float)p.dv + p.eps);
+    }
+    __syncthreads();
+    if (tid < (p.dv + 63) / 64 * 64) {
+      const bool valid = tid < p.dv;
+      float uo = 0.0f;
+      if (valid) {
+        const float zz = zsh[tid];
+        uo = osh[tid] * sc[2] * wn * (zz / (1.0f + expf(-zz)));
+      }
+      if (p.u_out && valid) p.u_out[(size_t)t * nv + h * p.dv + tid] = uo;
+      if (p.next.xd) put_digits(p.next, p.next_qt, t, (h * p.dv + (tid & ~31)) / QK, uo, valid);
+    }
+    __syncthreads();
+  }
+}
+
 hipError_t launch_deltanet(const DnParams& p, int T, hipStream_t s) {
   if (p.dk % 32 || p.dk > 128 || p.dv % 32 || T < 1 || T > MAX_T) return hipErrorInvalidValue;
   if (p.mode != DN_DECODE && p.mode != DN_VERIFY && p.mode != DN_CHUNK) return hipErrorInvalidValue;
+  if (p.variant) {
+    if (p.mode == DN_CHUNK || p.dv > 128 || 7 * p.dv < 2 * p.dk || p.conv < 2 || p.conv > 4 || p.k_heads <= 0 ||
+        p.heads % p.k_heads ||
+        !p.conv_w || !p.a_log || !p.dt_bias || !p.norm_w || !p.conv_state)
+      return hipErrorInvalidValue;
+    const unsigned block = (unsigned)(p.dv / 8) * 64;   // 8 lanes per row of S
+    switch (p.dk) {
+      case 32: k_deltanet_q35<4><<<p.heads, block, 0, s>>>(p, T); break;
+      case 64: k_deltanet_q35<8><<<p.heads, block, 0, s>>>(p, T); break;
+      case 96: k_deltanet_q35<12><<<p.heads, block, 0, s>>>(p, T); break;
+      case 128: k_deltanet_q35<16><<<p.heads, block, 0, s>>>(p, T); break;
+      default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+  }
   const unsigned grid = (unsigned)(p.heads * (p.dv / 32));
   const bool chunk = p.mode == DN_CHUNK;
   switch (p.dk) {

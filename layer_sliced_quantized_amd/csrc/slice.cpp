@@ -143,6 +143,7 @@ struct LayerLayout {
   size_t attn_norm = 0, ffn_norm = 0, q_norm = 0, k_norm = 0;
   // row offsets inside g1
   int off_q = 0, off_k = 0, off_v = 0, off_a = 0, off_b = 0, off_z = 0, off_g = -1;
+  size_t dn_conv_w = 0, dn_alog = 0, dn_dtb = 0, dn_normw = 0;   // qwen3_5-form DeltaNet vectors
   int dn_index = -1, attn_index = -1;
 };
 
@@ -163,6 +164,8 @@ struct Layout {
   size_t cpart[CHAIN_MAX_PHASES] = {}, ccnt[CHAIN_MAX_PHASES] = {};
   size_t ccnt_n = 0;      // u32 tickets in each ccnt region
   size_t kv_layer_bytes = 0, dn_layer_bytes = 0;
+  size_t conv = 0, conv_layer_bytes = 0;   // qwen3_5-form DeltaNet conv states
+  int64_t conv_slot = 0;                   // floats per conv-state slot
   size_t wsbytes = 0;
   int64_t g1_rows_max = 0;
   int nu = 0;              // width of the mixer output (G2 input)
@@ -193,10 +196,21 @@ std::string validate(const slice_config& c) {
   if (any_dn) {
     if (c.dn_heads <= 0 || c.dn_dk % 32 || c.dn_dk > 128 || c.dn_dk <= 0 || c.dn_dv % 32 || c.dn_dv <= 0)
       return "DeltaNet needs dk in {32,64,96,128} and dv a multiple of 32";
+    if (c.dn_variant != 0 && c.dn_variant != 1) return "dn_variant must be 0 or 1";
+    if (c.dn_variant) {
+      if (c.dn_conv < 2 || c.dn_conv > 4) return "dn_conv must be in 2..4";
+      if (c.dn_k_heads < 0 || (c.dn_k_heads && c.dn_heads % c.dn_k_heads)) return "dn_heads must be a multiple of dn_k_heads";
+      if (c.dn_dv > 128 || 7 * c.dn_dv < 2 * c.dn_dk)
+        return "the qwen3_5 DeltaNet form needs dv <= 128 and 7 dv >= 2 dk (a thread per conv channel)";
+    }
   }
   if ((c.has_embed || c.has_head) && c.vocab <= 0) return "vocab must be > 0 with an embedding or head";
   return "";
 }
+
+// Query/key heads of the DeltaNet layers, and the conv channels of the qwen3_5 form.
+int dn_kh(const slice_config& c) { return c.dn_variant && c.dn_k_heads > 0 ? c.dn_k_heads : c.dn_heads; }
+int dn_conv_dim(const slice_config& c) { return 2 * dn_kh(c) * c.dn_dk + c.dn_heads * c.dn_dv; }
 
 Layout make_layout(const slice_config& c) {
   Layout L;
@@ -219,7 +233,7 @@ Layout make_layout(const slice_config& c) {
   };
   L.mt = c.max_verify;
   L.nslots = c.max_verify + 1;
-  const int nkd = c.dn_heads * c.dn_dk, nvd = c.dn_heads * c.dn_dv;
+  const int nkd = dn_kh(c) * c.dn_dk, nvd = c.dn_heads * c.dn_dv;
   const int nq = c.q_heads * c.head_dim, nkv = c.kv_heads * c.head_dim;
   for (int l = c.layer_begin; l < c.layer_end; ++l) {
     LayerLayout ll;
@@ -256,6 +270,11 @@ Layout make_layout(const slice_config& c) {
     if (ll.attn) {
       ll.q_norm = vec(c.head_dim);
       ll.k_norm = vec(c.head_dim);
+    } else if (c.dn_variant) {
+      ll.dn_conv_w = vec((int64_t)dn_conv_dim(c) * c.dn_conv);
+      ll.dn_alog = vec(c.dn_heads);
+      ll.dn_dtb = vec(c.dn_heads);
+      ll.dn_normw = vec(c.dn_dv);
     }
     L.layers.push_back(ll);
   }
@@ -347,6 +366,12 @@ Layout make_layout(const slice_config& c) {
   L.kv = take((size_t)L.n_attn * L.kv_layer_bytes);
   L.dn_layer_bytes = al256((size_t)L.nslots * c.dn_heads * c.dn_dk * c.dn_dv * 4);
   L.dn = take((size_t)L.n_dn * L.dn_layer_bytes);
+  if (c.dn_variant && L.n_dn) {
+    // every value head keeps its own q / k windows: [head][2 dk + dv][conv - 1]
+    L.conv_slot = (int64_t)c.dn_heads * (2 * c.dn_dk + c.dn_dv) * (c.dn_conv - 1);
+    L.conv_layer_bytes = al256((size_t)L.nslots * L.conv_slot * 4);
+    L.conv = take((size_t)L.n_dn * L.conv_layer_bytes);
+  }
   L.wsbytes = o;
   return L;
 }
@@ -439,6 +464,18 @@ static DnParams dn_params(slice* s, int i, int T, int mode) {
   p.u_out = nullptr;
   p.next = s->act_u(T);
   p.next_qt = c.qtype;
+  if (c.dn_variant) {
+    p.variant = 1;
+    p.k_heads = dn_kh(c);
+    p.conv = c.dn_conv;
+    p.eps = c.eps;
+    p.conv_w = reinterpret_cast<const float*>(s->w + ll.dn_conv_w);
+    p.a_log = reinterpret_cast<const float*>(s->w + ll.dn_alog);
+    p.dt_bias = reinterpret_cast<const float*>(s->w + ll.dn_dtb);
+    p.norm_w = reinterpret_cast<const float*>(s->w + ll.dn_normw);
+    p.conv_state = reinterpret_cast<float*>(s->ws + L.conv + (size_t)ll.dn_index * L.conv_layer_bytes);
+    p.conv_slot = L.conv_slot;
+  }
   return p;
 }
 
@@ -771,7 +808,7 @@ namespace {
 
 std::string tensor_shape(const slice_config& c, int layer, int tid, int64_t& rows, int64_t& cols, int& kind) {
   const int H = c.hidden;
-  const int nkd = c.dn_heads * c.dn_dk, nvd = c.dn_heads * c.dn_dv;
+  const int nkd = dn_kh(c) * c.dn_dk, nvd = c.dn_heads * c.dn_dv;
   const int nq = c.q_heads * c.head_dim, nkv = c.kv_heads * c.head_dim;
   auto mat = [&](int64_t r, int64_t cc) { rows = r; cols = cc; kind = c.qtype; return std::string(); };
   auto vec = [&](int64_t n) { rows = n; cols = 1; kind = 0; return std::string(); };
@@ -814,6 +851,10 @@ std::string tensor_shape(const slice_config& c, int layer, int tid, int64_t& row
     case SLICE_T_DN_A:
     case SLICE_T_DN_B: return mat(c.dn_heads, H);
     case SLICE_T_DN_OUT: return mat(H, nvd);
+    case SLICE_T_DN_CONV: return c.dn_variant ? vec((int64_t)dn_conv_dim(c) * c.dn_conv) : "dn_variant is 0";
+    case SLICE_T_DN_ALOG:
+    case SLICE_T_DN_DTB: return c.dn_variant ? vec(c.dn_heads) : "dn_variant is 0";
+    case SLICE_T_DN_NORM: return c.dn_variant ? vec(c.dn_dv) : "dn_variant is 0";
     default: return "not a DeltaNet-layer tensor";
   }
 }
@@ -1128,7 +1169,8 @@ int slice_load(const slice_config* cfg, void* weights_dev, void* workspace_dev, 
   if (he == hipSuccess && s->L.n_attn && cfg->rope_dims > 0)
     he = launch_rope_table(s->wsp<float>(s->L.rope), cfg->max_seq, cfg->rope_dims, cfg->rope_theta, S(stream));
   s->chain = chains_possible(s) && override_int("CHAIN", 1) != 0;
-  s->chain_dn = s->chain && override_int("CHAIN_DN", 1) != 0;
+  // the qwen3_5 form's update takes a workgroup per head, too wide for the chain
+  s->chain_dn = s->chain && !cfg->dn_variant && override_int("CHAIN_DN", 1) != 0;
   if (s->chain) build_chains(s);
   if (he == hipSuccess) he = hipStreamCreate(&s->cap);
   if (he != hipSuccess) {
@@ -1193,7 +1235,7 @@ int slice_set_tensor(slice_t* s, int layer, int tid, const void* src, size_t src
   if (layer < c.layer_begin || layer >= c.layer_end) return fail(SLICE_ERANGE, "slice_set_tensor: layer outside the slice");
   const LayerLayout& ll = L.layers[layer - c.layer_begin];
   const int H = c.hidden;
-  const int nkd = c.dn_heads * c.dn_dk, nvd = c.dn_heads * c.dn_dv;
+  const int nkd = dn_kh(c) * c.dn_dk, nvd = c.dn_heads * c.dn_dv;
   const int nq = c.q_heads * c.head_dim, nkv = c.kv_heads * c.head_dim;
   switch (tid) {
     case SLICE_T_ATTN_NORM: return copyv(ll.attn_norm, H);
@@ -1223,6 +1265,10 @@ int slice_set_tensor(slice_t* s, int layer, int tid, const void* src, size_t src
     case SLICE_T_DN_B: return repack(ll.g1, c.dn_heads, H, 0, ll.off_b);
     case SLICE_T_DN_Z: return repack(ll.g1, nvd, H, 0, ll.off_z);
     case SLICE_T_DN_OUT: return repack(ll.g2, H, nvd, 0, 0);
+    case SLICE_T_DN_CONV: return copyv(ll.dn_conv_w, (int64_t)dn_conv_dim(c) * c.dn_conv);
+    case SLICE_T_DN_ALOG: return copyv(ll.dn_alog, c.dn_heads);
+    case SLICE_T_DN_DTB: return copyv(ll.dn_dtb, c.dn_heads);
+    case SLICE_T_DN_NORM: return copyv(ll.dn_normw, c.dn_dv);
     default: return fail(SLICE_EINVAL, "slice_set_tensor: not a DeltaNet-layer tensor");
   }
 }
@@ -1308,6 +1354,16 @@ int slice_prefill(slice_t* s, int k, const void* in, void* out, void* stream) {
   if (s->pending) return fail(SLICE_ESTATE, "slice_prefill: a verify is waiting for slice_commit");
   if (k < 1 || k > s->cfg.max_verify) return fail(SLICE_ERANGE, "slice_prefill: k outside 1..max_verify");
   if (s->L.n_attn && s->pos + k > s->cfg.max_seq) return fail(SLICE_ERANGE, "slice_prefill: positions pass max_seq");
+  if (s->cfg.dn_variant && s->L.n_dn) {
+    // the qwen3_5 form has no chunked update: a verify pass whose k tokens are all kept
+    int rc = run_step(s, k, DN_VERIFY, in, out, S(stream));
+    if (rc) return rc;
+    const int cur = (s->cur + k) % s->L.nslots;
+    HIPCHK(launch_ctrl_set(s->ctrl(), s->pos + k, cur, S(stream)));
+    s->cur = cur;
+    s->pos += k;
+    return SLICE_OK;
+  }
   int rc = run_step(s, k, DN_CHUNK, in, out, S(stream));
   if (rc) return rc;
   s->pos += k;
@@ -1397,6 +1453,44 @@ int slice_dbg_get_state(slice_t* s, int layer, float* dst, void* stream) {
   HIPCHK(launch_state_io(st, s->L.nslots, s->ctrl(), c.dn_heads, c.dn_dk, c.dn_dv, dst, 0, S(stream)));
   return SLICE_OK;
 }
+
+static int conv_io(slice_t* s, int layer, float* buf, int to_device, void* stream) {
+  if (!s || !buf) return fail(SLICE_EINVAL, "null argument");
+  const slice_config& c = s->cfg;
+  if (layer < c.layer_begin || layer >= c.layer_end) return fail(SLICE_ERANGE, "layer outside the slice");
+  const LayerLayout& ll = s->L.layers[layer - c.layer_begin];
+  if (ll.attn || !c.dn_variant) return fail(SLICE_EINVAL, "not a DeltaNet layer of the qwen3_5 form");
+  // canonical [conv_dim][conv - 1] (q | k | v channels) <-> the slot's
+  // [head][q of its key head | k of its key head | its v][conv - 1]
+  float* slot = reinterpret_cast<float*>(s->ws + s->L.conv + (size_t)ll.dn_index * s->L.conv_layer_bytes) +
+                (size_t)s->cur * s->L.conv_slot;
+  const int kh = dn_kh(c), ratio = c.dn_heads / kh, w = c.dn_conv - 1, dk = c.dn_dk, dv = c.dn_dv;
+  const size_t per_head = (size_t)(2 * dk + dv) * w;
+  auto mv = [&](size_t canon_off, size_t dev_off, size_t n) -> int {
+    float* a = buf + canon_off * w;
+    float* b = slot + dev_off;
+    HIPCHK(hipMemcpyAsync(to_device ? b : a, to_device ? a : b, n * w * 4, hipMemcpyDeviceToDevice, S(stream)));
+    return SLICE_OK;
+  };
+  for (int h = 0; h < c.dn_heads; ++h) {
+    const int g = h / ratio;
+    const size_t base = (size_t)h * per_head;
+    int rc = SLICE_OK;
+    if (to_device || h % ratio == 0) {   // the copies of a key head's windows are identical
+      rc = mv((size_t)g * dk, base, dk);
+      if (!rc) rc = mv((size_t)kh * dk + (size_t)g * dk, base + (size_t)dk * w, dk);
+    }
+    if (!rc) rc = mv((size_t)2 * kh * dk + (size_t)h * dv, base + (size_t)2 * dk * w, dv);
+    if (rc) return rc;
+  }
+  return SLICE_OK;
+}
+
+int slice_dbg_set_conv(slice_t* s, int layer, const float* src, void* stream) {
+  return conv_io(s, layer, const_cast<float*>(src), 1, stream);
+}
+
+int slice_dbg_get_conv(slice_t* s, int layer, float* dst, void* stream) { return conv_io(s, layer, dst, 0, stream); }
 
 static int kv_io(slice_t* s, int layer, uint16_t* k, uint16_t* v, int rows, int to_device, void* stream) {
   if (!s || !k || !v) return fail(SLICE_EINVAL, "null argument");

@@ -168,6 +168,16 @@ struct DnParams {
   const Ctrl* ctrl;      // state slot index ctrl->cur; nullptr: slot 0
   float* u_out;          // [T][heads*dv] (nullable)
   Act next; int next_qt; // digits of the output (next.xd == nullptr: none)
+  // qwen3_5 form (variant 1): conv over q | k | v (k_heads query/key heads of
+  // dk, heads value heads of dv), decay exp(-exp(a_log) softplus(.)), gated norm
+  int variant, k_heads, conv;
+  float eps;                  // gated-norm epsilon
+  const float* conv_w;        // [conv_dim][conv]
+  const float* a_log;         // [heads]
+  const float* dt_bias;       // [heads]
+  const float* norm_w;        // [dv]
+  float* conv_state;          // slot 0: [nslots][conv_dim][conv - 1]
+  int64_t conv_slot;          // floats per slot
 };
 hipError_t launch_deltanet(const DnParams& p, int T, hipStream_t s);
 hipError_t launch_state_io(float* state, int nslots, const Ctrl* ctrl, int heads, int dk, int dv,

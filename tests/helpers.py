@@ -46,6 +46,11 @@ def make_pair(shape, qtype, begin, end, *, workload, seed=0, max_seq=1024, max_v
             s.set_state(l, torch.from_numpy(S0))
             if orc:
                 orc.set_state(l, S0)
+            if getattr(shape, "dn_variant", 0):
+                C0 = synth.dn_conv_state0(seed, workload, l, shape.conv_dim, shape.dn_conv)
+                s.set_conv_state(l, torch.from_numpy(C0))
+                if orc:
+                    orc.set_conv_state(l, C0)
     s.reset(prefill)
     if orc:
         orc.reset(prefill)

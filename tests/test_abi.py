@@ -83,3 +83,22 @@ def test_config_validation_and_slice_sizes():
     assert L.slice_workspace_bytes(ctypes.byref(bad)) == 0
     tiny = slq.make_config(synth.TINY_LLAMA, 2, 0, 30, max_seq=256, has_embed=True, has_head=True)
     assert L.slice_weights_bytes(ctypes.byref(tiny)) > 4096 * 576 * 18 // 32
+
+
+def test_q35_tensor_shapes_and_validation():
+    """The qwen3_5 DeltaNet tensors' shapes (host only) and rejected configs."""
+    import dataclasses
+    import layer_sliced_quantized_amd as slq
+    import synth
+    sh = synth.HYBRID_5120_Q35
+    cfg = slq.make_config(sh, synth.Q4_0, 0, 4, max_seq=1024, max_verify=4)
+    assert slq.tensor_info(cfg, 0, "dn_conv")["rows"] == sh.conv_dim * sh.dn_conv
+    assert slq.tensor_info(cfg, 0, "dn_alog")["rows"] == sh.dn_heads
+    assert slq.tensor_info(cfg, 0, "dn_norm")["rows"] == sh.dn_dv
+    assert slq.tensor_info(cfg, 0, "dn_q")["rows"] == sh.k_heads * sh.dn_dk
+    assert slq.tensor_info(cfg, 0, "dn_v")["rows"] == sh.dn_heads * sh.dn_dv
+    with pytest.raises(slq.SliceError):
+        slq.tensor_info(slq.make_config(synth.HYBRID_5120, synth.Q4_0, 0, 4), 0, "dn_conv")
+    for bad in (dict(dn_conv=5), dict(dn_k_heads=5), dict(dn_dv=32, dn_dk=128), dict(dn_variant=2)):
+        with pytest.raises(slq.SliceError):
+            slq.tensor_info(slq.make_config(dataclasses.replace(sh, **bad), synth.Q4_0, 0, 4), 0, "dn_q")
