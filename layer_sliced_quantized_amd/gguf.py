@@ -252,6 +252,10 @@ DEFAULT_NAMES = {
     "dn_b": "blk.{l}.dn_b.weight",
     "dn_z": "blk.{l}.dn_z.weight",
     "dn_out": "blk.{l}.dn_out.weight",
+    "dn_conv": "blk.{l}.dn_conv.weight",
+    "dn_alog": "blk.{l}.dn_a_log",
+    "dn_dtb": "blk.{l}.dn_dt_bias",
+    "dn_norm": "blk.{l}.dn_norm.weight",
     "w_gate": "blk.{l}.ffn_gate.weight",
     "w_up": "blk.{l}.ffn_up.weight",
     "w_down": "blk.{l}.ffn_down.weight",

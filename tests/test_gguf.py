@@ -3,6 +3,8 @@ published layout (independently of the writer), writer/reader round trips of
 a slice's tensors, and the rejection of malformed files.  CPU only."""
 import struct
 
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -220,3 +222,28 @@ def test_tensor_info_and_overrides_are_host_only():
         slq.debug_override("KS_NOPE", 1)
     with slq.overrides(MFMA_MIN_T=2, EAGER=1):
         pass
+
+
+SHAPE_Q35 = dataclasses.replace(SHAPE, name="tiny_hybrid_q35_128", dn_heads=4, dn_variant=1, dn_k_heads=2, dn_conv=4)
+
+
+@needs_lib
+def test_q35_file_round_trip_and_config_check(tmp_path):
+    """A qwen3_5-form slice's tensors (conv taps, A_log, dt_bias, gated-norm
+    weights and the narrower q/k projections) survive a GGUF round trip and
+    pass the shape check; the plain form's config refuses them."""
+    import layer_sliced_quantized_amd as slq
+    tensors = {l: synth.layer_tensors(SHAPE_Q35, synth.Q4_0, 0, 97, l) for l in range(4)}
+    assert {"dn_conv", "dn_alog", "dn_dtb", "dn_norm"} <= set(tensors[0])
+    p = tmp_path / "q35.gguf"
+    gguf.write_gguf(str(p), {}, gguf_tensors(SHAPE_Q35, tensors, synth.Q4_0))
+    g = gguf.GGUFFile(str(p))
+    for l in range(4):
+        back = gguf.slice_tensors(g, l)
+        for name, arr in tensors[l].items():
+            np.testing.assert_array_equal(np.asarray(back[name]).reshape(-1).view(np.uint8),
+                                          np.asarray(arr).reshape(-1).view(np.uint8))
+    cfg = slq.make_config(SHAPE_Q35, synth.Q4_0, 0, 4, max_seq=256, max_verify=4, io_fp32=True)
+    assert len(gguf.check_against_config(g, cfg)) == sum(len(d) for d in tensors.values())
+    with pytest.raises(gguf.GGUFError):
+        gguf.check_against_config(g, _cfg())
