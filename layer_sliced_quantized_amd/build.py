@@ -6,6 +6,7 @@ Run as ``python -m layer_sliced_quantized_amd.build`` or through
 from __future__ import annotations
 
 import os
+import re
 import subprocess
 import sys
 from concurrent.futures import ThreadPoolExecutor
@@ -30,12 +31,41 @@ FLAGS = [
 ]
 
 
+# Kernels whose hand-placed memory waits count only their own loads: the
+# batched MFMA products (k_gemm_*) wait for a fixed number of outstanding
+# vector loads per block, which holds only if the compiler adds none (a
+# scratch spill would).  Their sources are compiled with the resource-usage
+# remarks and the build fails if any of them uses scratch.
+NO_SCRATCH = {"gemm_q4.hip": "k_gemm_", "gemm_q8.hip": "k_gemm_", "gemm.hip": "k_gemm_"}
+
+
+def scratch_users(remarks: str, prefix: str) -> list:
+    """(kernel, bytes per lane) of every kernel whose mangled name holds
+    `prefix` and whose resource-usage remark reports scratch."""
+    out, name = [], None
+    for line in remarks.splitlines():
+        m = re.search(r"Function Name: (\S+)", line)
+        if m:
+            name = m.group(1)
+            continue
+        m = re.search(r"ScratchSize \[bytes/lane\]: (\d+)", line)
+        if m and name and prefix in name and int(m.group(1)) > 0:
+            out.append((name, int(m.group(1))))
+    return out
+
+
 def _compile(src: str) -> str:
     out = os.path.join(OBJ, os.path.splitext(src)[0] + ".o")
     cmd = [HIPCC, *FLAGS, "-x", "hip", "-c", os.path.join(CSRC, src), "-o", out]
+    if src in NO_SCRATCH:
+        cmd.append("-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode:
         raise RuntimeError(f"compile of {src} failed:\n{r.stderr[-8000:]}")
+    if src in NO_SCRATCH:
+        bad = scratch_users(r.stderr, NO_SCRATCH[src])
+        if bad:
+            raise RuntimeError(f"{src}: kernels with hand-counted memory waits use scratch: {bad}")
     return out
 
 

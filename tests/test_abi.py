@@ -102,3 +102,16 @@ def test_q35_tensor_shapes_and_validation():
     for bad in (dict(dn_conv=5), dict(dn_k_heads=5), dict(dn_dv=32, dn_dk=128), dict(dn_variant=2)):
         with pytest.raises(slq.SliceError):
             slq.tensor_info(slq.make_config(dataclasses.replace(sh, **bad), synth.Q4_0, 0, 4), 0, "dn_q")
+
+
+def test_build_refuses_scratch_in_kernels_with_counted_waits():
+    """The build parses the compiler's resource-usage remarks and names every
+    batched-product kernel that uses scratch (host logic only)."""
+    from layer_sliced_quantized_amd import build
+    text = ("x.hip:1:1: remark: Function Name: _ZN3slq11k_gemm_diagILi2EEEvv [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 0 [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark: Function Name: _ZN3slq12k_gemm_denseILi8EEEvv [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 16 [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark: Function Name: _ZN3slq6k_gemvILi2EEEvv [-Rpass-analysis=kernel-resource-usage]\n"
+            "x.hip:1:1: remark:     ScratchSize [bytes/lane]: 12 [-Rpass-analysis=kernel-resource-usage]\n")
+    assert build.scratch_users(text, "k_gemm_") == [("_ZN3slq12k_gemm_denseILi8EEEvv", 16)]
