@@ -103,9 +103,10 @@ def chain_step_bytes(shape, qtype, deltanet: bool = True) -> int:
     return total
 
 
-def read_ceiling(gib=2, reps=30):
-    """Streaming-read bandwidth of the device: slq_read_probe over a buffer
-    eight times the 256 MB last-level cache, HIP events around reps reads."""
+def read_ceiling(gib=4, reps=20):
+    """Streaming-read bandwidth of the device: slq_read_probe over a 4 GiB
+    buffer (16 times the 256 MB last-level cache), HIP events around reps
+    reads."""
     import torch
     import layer_sliced_quantized_amd as slq
     buf = torch.zeros(gib << 30, dtype=torch.uint8, device="cuda")
@@ -124,7 +125,7 @@ def read_ceiling(gib=2, reps=30):
     del buf
     torch.cuda.empty_cache()
     return {"GB_s": round(gbs, 1), "frac_peak": round(gbs / HBM_PEAK_GBS, 4), "bytes": gib << 30, "us": round(us, 2),
-            "kernel": "slq_read_probe: nontemporal 16-byte loads, 4 in flight per lane, 4096 x 256 threads"}
+            "kernel": "slq_read_probe: nontemporal 16-byte loads, 16 in flight per lane, 16384 x 256 threads"}
 
 
 def _event_time_us(fn, reps):

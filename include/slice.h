@@ -119,13 +119,15 @@ int slq_gemv_noalloc(int qtype, const void *packed_dev, int64_t rows, int64_t co
                      const float *x_dev, float *y_dev, void *stream);
 
 /* Streaming-read ceiling of the device: reads `bytes` (a multiple of 16) at
- * buf_dev once, as the GEMVs read weights, and stores an XOR fold of what it
- * read to sink_dev (SLQ_READ_PROBE_GRID * 4 uint32).  The pages judge their
- * decode against the read bandwidth they measured on their device (SwarmLLM
- * README, bench paragraph); timing this call over a buffer larger than the
- * last-level cache gives that ceiling here.  SLICE_EINVAL for a null pointer
- * or a size that is not a positive multiple of 16.                          */
-#define SLQ_READ_PROBE_GRID 4096
+ * buf_dev once, as the GEMVs read weights (nontemporal 16-byte loads, sixteen
+ * in flight per lane, up to SLQ_READ_PROBE_GRID workgroups of 256), and
+ * stores an XOR fold of what it read to sink_dev (SLQ_READ_PROBE_GRID * 4
+ * uint32; the XOR of all of them is the XOR of every 32-bit word read).  The
+ * pages judge their decode against the read bandwidth they measured on their
+ * device (SwarmLLM README, bench paragraph); timing this call over a buffer
+ * well beyond the last-level cache gives that ceiling here.  SLICE_EINVAL for
+ * a null pointer or a size that is not a positive multiple of 16.           */
+#define SLQ_READ_PROBE_GRID 16384
 int slq_read_probe(const void *buf_dev, size_t bytes, uint32_t *sink_dev, void *stream);
 
 /* ------------------------------------------------------------------------ */

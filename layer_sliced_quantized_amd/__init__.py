@@ -93,11 +93,11 @@ def overrides(**kw):
             debug_override(k, -1)
 
 
-READ_PROBE_GRID = 4096     # SLQ_READ_PROBE_GRID: workgroups of slq_read_probe
+READ_PROBE_GRID = 16384    # SLQ_READ_PROBE_GRID: most workgroups of slq_read_probe
 
 
 def read_probe(buf: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
-    """One streaming read of buf's bytes (slq_read_probe); sink: >= 4 * 4096 int32."""
+    """One streaming read of buf's bytes (slq_read_probe); sink: >= 4 * READ_PROBE_GRID int32."""
     check(lib().slq_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), _stream(stream)))
 
 

@@ -41,21 +41,24 @@ hipError_t launch_fill_zero_u32(uint32_t* p, size_t n, hipStream_t s) {
 }
 
 // Streaming read of n16 16-byte words, each read once with a nontemporal
-// load (as the GEMVs read weights), four loads in flight per lane.  The words
-// are folded by XOR into one value per wave, stored to sink, so that no load
-// can be dropped; sink needs gridDim.x * 4 entries.
+// load (as the GEMVs read weights), sixteen loads in flight per lane (the
+// fastest of 2 to 16 loads and 1024 to 16384 workgroups over 4 GiB on
+// MI355X: 6.9 TB/s).  The words are folded by XOR into one value per wave,
+// stored to sink, so that no load can be dropped; sink needs gridDim.x * 4
+// entries.
 typedef uint32_t rp_u32x4 __attribute__((ext_vector_type(4)));
+constexpr int RP_LOADS = 16;
 
 __global__ __launch_bounds__(256) void k_read_probe(const rp_u32x4* __restrict__ p, size_t n16, uint32_t* sink) {
   const size_t stride = (size_t)gridDim.x * 256;
   size_t i = (size_t)blockIdx.x * 256 + threadIdx.x;
   rp_u32x4 acc = {0u, 0u, 0u, 0u};
-  for (; i + 3 * stride < n16; i += 4 * stride) {
-    const rp_u32x4 a = __builtin_nontemporal_load(p + i);
-    const rp_u32x4 b = __builtin_nontemporal_load(p + i + stride);
-    const rp_u32x4 c = __builtin_nontemporal_load(p + i + 2 * stride);
-    const rp_u32x4 d = __builtin_nontemporal_load(p + i + 3 * stride);
-    acc ^= a ^ b ^ c ^ d;
+  for (; i + (RP_LOADS - 1) * stride < n16; i += RP_LOADS * stride) {
+    rp_u32x4 v[RP_LOADS];
+#pragma unroll
+    for (int u = 0; u < RP_LOADS; ++u) v[u] = __builtin_nontemporal_load(p + i + u * stride);
+#pragma unroll
+    for (int u = 0; u < RP_LOADS; ++u) acc ^= v[u];
   }
   for (; i < n16; i += stride) acc ^= __builtin_nontemporal_load(p + i);
   uint32_t v = acc.x ^ acc.y ^ acc.z ^ acc.w;
@@ -63,7 +66,12 @@ __global__ __launch_bounds__(256) void k_read_probe(const rp_u32x4* __restrict__
   if ((threadIdx.x & 63) == 0) sink[blockIdx.x * 4 + (threadIdx.x >> 6)] = v;
 }
 
-hipError_t launch_read_probe(const void* p, size_t n16, uint32_t* sink, unsigned grid, hipStream_t s) {
+// grid: at most max_grid workgroups, fewer for a buffer under max_grid full
+// rounds of sixteen loads per lane
+hipError_t launch_read_probe(const void* p, size_t n16, uint32_t* sink, unsigned max_grid, hipStream_t s) {
+  const size_t per = (size_t)RP_LOADS * 256;
+  const size_t want = (n16 + per - 1) / per;
+  const unsigned grid = (unsigned)(want < max_grid ? (want ? want : 1) : max_grid);
   k_read_probe<<<grid, 256, 0, s>>>(reinterpret_cast<const rp_u32x4*>(p), n16, sink);
   return hipGetLastError();
 }

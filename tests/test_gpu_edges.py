@@ -181,11 +181,11 @@ def test_hybrid_64_layer_q8_slice():
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("n16", [1, 4096 * 256 * 4 * 2 + 12345])
+@pytest.mark.parametrize("n16", [1, 16 * 256 * 4096 + 12345, 16 * 256 * 16384 + 777])
 def test_read_probe_reads_every_word_once(n16):
     """The XOR of the probe's per-wave folds equals the XOR of every 32-bit
-    word of the buffer: each word was read exactly once (both the four-load
-    loop and the tail)."""
+    word of the buffer: each word was read exactly once (the sixteen-load
+    loop and the tail; grids of one workgroup, below the cap and at it)."""
     import layer_sliced_quantized_amd as slq
     words = synth.stream(0, synth.WL_GEMV, 300, n16).integers(0, 2**32, size=4 * n16, dtype=np.uint32)
     buf = torch.from_numpy(words.view(np.int32)).cuda()
