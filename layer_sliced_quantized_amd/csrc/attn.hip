@@ -6,7 +6,9 @@
 // KV cache ("Unstable Legion", section "Splitting the workload").
 //
 // Two kernels per layer:
-//   split:   one workgroup per (KV head, group of query heads, 32-row chunk).
+//   split:   one workgroup per (KV head, group of query heads, 32-row chunk);
+//            for one token on a long cache (k_attn_split_range) one workgroup
+//            per (KV head, range of chunks) with all the KV head's query heads.
 //            It first appends the K/V rows of this step that fall in its
 //            chunk (RMSNorm if QK-norm, RoPE on the first rope_dims entries
 //            with the angle pos * theta^(-2i/r) taken in fp64, fp16
@@ -22,6 +24,7 @@
 // K cache layout: [kv][pos/64][head_dim/8][64 pos][8] (a wave reads 64 rows'
 // 16-byte pieces as one contiguous 1 KiB); V cache: [kv][pos][head_dim].
 #include "dev.h"
+#include <algorithm>
 
 namespace slq {
 
@@ -95,6 +98,233 @@ __device__ __forceinline__ void head_prep(float (&x)[NC], const AttnParams& p, c
       }
     }
     asm volatile("" ::: "memory");
+  }
+}
+
+// One workgroup per (KV head g, group of GRP of its query heads, range of cpw
+// consecutive 32-row chunks), 4 waves, for all T (<= TM) tokens of the pass:
+//   1. the pass's K/V rows that fall in the range are prepared (wave w takes
+//      tokens w, w + 4, ...) and appended to the cache;
+//   2. the first chunk's keys (thread (row rr = tid / 8, part = tid % 8): an
+//      eighth of the head dimensions of key row rr) and values (thread =
+//      dimension) are requested;
+//   3. every (token, query head) that reaches the range is prepared into LDS
+//      once (wave w takes pairs w, w + 4, ...) while those loads are in flight;
+//   then chunk after chunk, with the next chunk's keys and values requested
+//   as soon as the current ones are in registers:
+//   4. scores for every (token, head): the eight parts meet in three butterfly
+//      steps; then one wave per (token, head) takes the chunk max, the
+//      weights exp(s - max) and their sum;
+//   5. P V per (token, head): one thread per dimension over the chunk's rows,
+//      written as the chunk's partial.
+// Each chunk's partial is computed by exactly the operations of k_attn_split
+// below, whatever GRP and cpw are, so a decode step through this kernel (one
+// token on a long cache: all query heads of a KV head per workgroup, several
+// chunks per workgroup) and a verify pass through k_attn_split give the same
+// bits.
+// Every group of query heads of a range appends the same rows itself (the
+// same bits), so each reads them back after its own stores.
+template <int GRP, int HD, int TM>   // GRP: query heads per workgroup; TM: most tokens
+__global__ __launch_bounds__(256) void k_attn_split_range(AttnParams p, int T, int cpw) {
+  constexpr int C = ATT_CHUNK;
+  constexpr int NC = HD / 64;   // entries per lane of a head vector; 8-dim pieces per eighth of the head
+  constexpr int TW = (TM + 3) / 4;   // tokens per wave in step 1
+  // prepared queries; every 32 floats of a row are followed by 4 of padding,
+  // so the eight key parts of a score step (32 floats apart) read 16-byte
+  // pieces in eight different bank groups instead of two
+  constexpr int QW = HD + HD / 8;
+  __shared__ __attribute__((aligned(16))) float qsh[TM][GRP][QW];
+  __shared__ __attribute__((aligned(16))) float pl[TM][GRP][C];
+  __shared__ float rbuf[4][HD];
+  __shared__ float ml[TM][GRP][2];
+  const int nsub = p.q_heads / p.kv_heads / GRP;   // query-head groups per KV head
+  const int nrange = (p.nchunk + cpw - 1) / cpw;
+  // Workgroups go to the XCDs round robin by index.  The nsub workgroups that
+  // read the same (KV head, range) pair take indices 8 apart, i.e. one XCD and
+  // close in time, so the later ones find its keys and values in that XCD's
+  // L2: pairs come in groups of 8, each group once per query-head group.
+  const int pair = ((int)blockIdx.x / (8 * nsub)) * 8 + (int)blockIdx.x % 8;
+  const int sub = ((int)blockIdx.x / 8) % nsub;
+  if (pair >= p.kv_heads * nrange) return;
+  const int g = pair / nrange, rng = pair % nrange;
+  const int cb = rng * cpw;
+  const int h0 = (g * nsub + sub) * GRP;            // first query head of this workgroup
+  const int p0 = p.ctrl ? p.ctrl->pos : p.pos;
+  if (cb * C > p0 + T - 1) return;
+  const int ce = min(min(cb + cpw, p.nchunk), (p0 + T - 1) / C + 1);   // chunks [cb, ce) hold visible rows
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = wave_id();
+  const bool dact = tid < HD;
+  float* rb = rbuf[wave];
+
+  // 1. this pass's K/V rows inside the range: positions p0 + t in [cb C, ce C);
+  // wave w takes tokens ta + w + 4 m, all its loads first
+  {
+    const int ta = max(0, cb * C - p0), tb = min(T, ce * C - p0);
+    if (tb > ta) {
+      float k[TW][NC], v[TW][NC];
+#pragma unroll
+      for (int m = 0; m < TW; ++m) {
+        const int t = ta + wave + 4 * m;
+        if (t < tb) {
+          const float* y = p.y + (size_t)t * p.y_stride;
+#pragma unroll
+          for (int e = 0; e < NC; ++e) {
+            k[m][e] = y[p.off_k + g * HD + lane + 64 * e];
+            v[m][e] = y[p.off_v + g * HD + lane + 64 * e];
+          }
+        }
+      }
+#pragma unroll
+      for (int m = 0; m < TW; ++m) {
+        const int t = ta + wave + 4 * m;
+        if (t < tb) {
+          const int pos = p0 + t;
+          head_prep<NC>(k[m], p, p.k_norm, pos, rb);
+#pragma unroll
+          for (int e = 0; e < NC; ++e) {
+            const int d = lane + 64 * e;
+            p.kc[kidx(g, pos, d, p.max_seq, HD)] = __float2half_rn(k[m][e]);
+            p.vc[((size_t)g * p.max_seq + pos) * HD + d] = __float2half_rn(v[m][e]);
+          }
+        }
+      }
+      __threadfence_block();
+      __syncthreads();
+    }
+  }
+
+  // 2. the first chunk's keys (this thread's eighth of row rr) and values
+  // (dimension tid of every row); rows past the pass's last position lie
+  // inside the cache, get weight 0 and a value of 0
+  const int rr = tid >> 3, part = tid & 7;
+  uint4 kw[NC];
+  unsigned short vv[C];
+  auto request = [&](int c) {
+    const int r = c * C + rr;
+#pragma unroll
+    for (int i = 0; i < NC; ++i)
+      kw[i] = *reinterpret_cast<const uint4*>(p.kc + kidx(g, r, (part * NC + i) * 8, p.max_seq, HD));
+    const unsigned short* vrow =
+        reinterpret_cast<const unsigned short*>(p.vc) + ((size_t)g * p.max_seq + c * C) * HD + (dact ? tid : 0);
+#pragma unroll
+    for (int q = 0; q < C; ++q) vv[q] = vrow[(size_t)q * HD];
+  };
+  request(cb);
+
+  // 3. queries of tokens tq0.. (those whose position reaches the range):
+  // pair q = (t - tq0) GRP + h, wave w takes pairs w + 4 m, all its loads first
+  const int tq0 = max(0, cb * C - p0);
+  {
+    const int npair = (T - tq0) * GRP;
+    constexpr int MQ = (TM * GRP + 3) / 4;
+    float x[MQ][NC];
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+      const int q = wave + 4 * m;
+      if (q < npair) {
+        const float* y = p.y + (size_t)(tq0 + q / GRP) * p.y_stride + p.off_q + (h0 + q % GRP) * HD;
+#pragma unroll
+        for (int e = 0; e < NC; ++e) x[m][e] = y[lane + 64 * e];
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < MQ; ++m) {
+      const int q = wave + 4 * m;
+      if (q < npair) {
+        const int t = tq0 + q / GRP, h = q % GRP;
+        head_prep<NC>(x[m], p, p.q_norm, p0 + t, rb);
+#pragma unroll
+        for (int e = 0; e < NC; ++e) {
+          const int d = lane + 64 * e;
+          qsh[t][h][d + (d >> 5) * 4] = x[m][e] * (1.0f / sqrtf((float)HD));
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int c = cb; c < ce; ++c) {
+    const int r0 = c * C;
+    const int nvmax = min(C, p0 + T - r0);   // rows valid for the pass's last token
+    float kf[NC][8];
+#pragma unroll
+    for (int i = 0; i < NC; ++i) {
+      const uint32_t ws[4] = {kw[i].x, kw[i].y, kw[i].z, kw[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        kf[i][2 * e] = __half2float(__ushort_as_half((unsigned short)(ws[e] & 0xffff)));
+        kf[i][2 * e + 1] = __half2float(__ushort_as_half((unsigned short)(ws[e] >> 16)));
+      }
+    }
+    float vf[C];
+#pragma unroll
+    for (int q = 0; q < C; ++q) vf[q] = q < nvmax ? __half2float(__ushort_as_half(vv[q])) : 0.0f;
+    if (c + 1 < ce) request(c + 1);
+    const int tq = max(0, r0 - p0);
+    const int npair = (T - tq) * GRP;
+
+    // 4. scores, then per (token, head) the max, weights and their sum
+    for (int t = tq; t < T; ++t) {
+      const int nvalid = min(C, p0 + t + 1 - r0);
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) {
+        float sc = 0.0f;
+#pragma unroll
+        for (int i = 0; i < NC; ++i) {
+          const int dc = part * NC + i;
+          const int q8 = dc * 8 + (dc >> 2) * 4;   // dims dc*8 .. dc*8+7 lie in one padded group of 32
+          const float4 qa = *reinterpret_cast<const float4*>(&qsh[t][h][q8]);
+          const float4 qb = *reinterpret_cast<const float4*>(&qsh[t][h][q8 + 4]);
+          sc = __builtin_fmaf(kf[i][0], qa.x, sc);
+          sc = __builtin_fmaf(kf[i][1], qa.y, sc);
+          sc = __builtin_fmaf(kf[i][2], qa.z, sc);
+          sc = __builtin_fmaf(kf[i][3], qa.w, sc);
+          sc = __builtin_fmaf(kf[i][4], qb.x, sc);
+          sc = __builtin_fmaf(kf[i][5], qb.y, sc);
+          sc = __builtin_fmaf(kf[i][6], qb.z, sc);
+          sc = __builtin_fmaf(kf[i][7], qb.w, sc);
+        }
+        sc += xor_lane<1>(sc);
+        sc += xor_lane<2>(sc);
+        sc += xor_lane<4>(sc);
+        if (part == 0) pl[t][h][rr] = rr < nvalid ? sc : -INFINITY;
+      }
+    }
+    __syncthreads();
+    for (int q = wave; q < npair; q += 4) {
+      const int t = tq + q / GRP, h = q % GRP;
+      const int nvalid = min(C, p0 + t + 1 - r0);
+      const float sc = lane < C ? pl[t][h][lane] : -INFINITY;
+      const float m = wave_max(sc);
+      const float e = lane < nvalid ? __expf(sc - m) : 0.0f;
+      if (lane < C) pl[t][h][lane] = e;
+      const float l = wave_sum(e);
+      if (lane == 0) { ml[t][h][0] = m; ml[t][h][1] = l; }
+    }
+    __syncthreads();
+
+    // 5. P V
+    if (dact) {
+      for (int t = tq; t < T; ++t) {
+#pragma unroll
+        for (int h = 0; h < GRP; ++h) {
+          float o = 0.0f;
+#pragma unroll
+          for (int q = 0; q < C; q += 4) {
+            const float4 w = *reinterpret_cast<const float4*>(&pl[t][h][q]);
+            o = __builtin_fmaf(w.x, vf[q], o);
+            o = __builtin_fmaf(w.y, vf[q + 1], o);
+            o = __builtin_fmaf(w.z, vf[q + 2], o);
+            o = __builtin_fmaf(w.w, vf[q + 3], o);
+          }
+          float* dst = p.part + (((size_t)t * p.q_heads + h0 + h) * p.nchunk + c) * (HD + 2);
+          dst[2 + tid] = o;
+          if (tid == 0) { dst[0] = ml[t][h][0]; dst[1] = ml[t][h][1]; }
+        }
+      }
+    }
+    __syncthreads();   // pl and ml are rewritten by the next chunk
   }
 }
 
@@ -429,21 +659,40 @@ __global__ __launch_bounds__(64 * CW) void k_attn_combine(AttnParams p) {
 hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {
   if (p.hd % 64 || p.hd > 256 || p.rope_dims % 2 || p.rope_dims > p.hd || p.max_seq % 64 ||
       p.nchunk * ATT_CHUNK < p.max_seq || (p.rope_dims && !p.rope_cs) ||
-      p.q_heads % p.kv_heads)
+      p.q_heads % p.kv_heads || T < 1 || T > MAX_T)
     return hipErrorInvalidValue;
-  // query heads per split workgroup: at most 2 of a KV head's group, so that
-  // the work of a chunk spreads over several workgroups
+  // Query heads per split workgroup: with one token and a cache of at least
+  // 512 (KV head, chunk) pairs, all of a KV head's group (its keys and values
+  // are then read once per chunk: 100.6 -> 71.9 us at 32768 rows, 22.3 -> 17.2
+  // at 4096 on MI355X); otherwise at most 2 (more workgroups for a short cache,
+  // 9.6 against 11.6 us at 512 rows; and the prepared queries of 16 tokens
+  // fill LDS).  Chunks per workgroup: enough that the grid stays near 1024
+  // workgroups on long caches.
   const int grp = p.q_heads / p.kv_heads;
-  const int hpw = grp % 2 == 0 ? 2 : 1;
-  const int pairs = p.kv_heads * p.nchunk;         // (KV head, chunk) pairs, padded to groups of 8
-  const unsigned grid = (unsigned)(((pairs + 7) / 8) * 8 * (grp / hpw));
+  const bool one = T == 1 && p.kv_heads * p.nchunk >= 512 &&
+                   (grp == 1 || grp == 2 || grp == 3 || grp == 4 || grp == 6 || grp == 8);
+  const int hpw = one ? grp : (grp % 2 == 0 ? 2 : 1);
+  const int nsub = grp / hpw;
+  const int units = p.kv_heads * p.nchunk * nsub;
+  const int cpw = one && units > 1024 ? std::min(16, (units + 1023) / 1024) : 1;
+  const int nrange = (p.nchunk + cpw - 1) / cpw;
+  const int pairs = p.kv_heads * nrange;           // (KV head, chunk range) pairs, padded to groups of 8
+  const unsigned grid = (unsigned)(((pairs + 7) / 8) * 8 * nsub);
+#define SLQ_R(n, hd) case n: k_attn_split_range<n, hd, 1><<<grid, 256, 0, s>>>(p, T, cpw); break;
 #define SLQ_G(n, hd) case n: k_attn_split<n, hd><<<grid, 256, 0, s>>>(p, T); break;
-#define SLQ_HD(hd)                                          \
-  case hd:                                                  \
-    switch (hpw) {                                          \
-      SLQ_G(1, hd) SLQ_G(2, hd)                             \
-      default: return hipErrorInvalidValue;                 \
-    }                                                       \
+#define SLQ_HD(hd)                                                              \
+  case hd:                                                                      \
+    if (one) {                                                                  \
+      switch (hpw) {                                                            \
+        SLQ_R(1, hd) SLQ_R(2, hd) SLQ_R(3, hd) SLQ_R(4, hd) SLQ_R(6, hd) SLQ_R(8, hd) \
+        default: return hipErrorInvalidValue;                                   \
+      }                                                                         \
+    } else {                                                                    \
+      switch (hpw) {                                                            \
+        SLQ_G(1, hd) SLQ_G(2, hd)                                               \
+        default: return hipErrorInvalidValue;                                   \
+      }                                                                         \
+    }                                                                           \
     break;
   switch (p.hd) {
     SLQ_HD(64) SLQ_HD(128) SLQ_HD(192) SLQ_HD(256)
@@ -451,6 +700,7 @@ hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {
   }
 #undef SLQ_HD
 #undef SLQ_G
+#undef SLQ_R
   k_attn_combine<<<T * p.q_heads * (p.hd / 64), p.nchunk > 64 ? 64 * CW : 64, 0, s>>>(p);
   return hipGetLastError();
 }

@@ -178,10 +178,13 @@ def test_attn_first_position_returns_v():
         np.testing.assert_array_equal(out[i], v[i // grp].astype(np.float16).astype(np.float32))
 
 
-def test_attn_tokens_in_one_call_equal_one_at_a_time():
+@pytest.mark.parametrize("L", [1000, 5000, 9000])
+def test_attn_tokens_in_one_call_equal_one_at_a_time(L):
     """Sixteen tokens in one call (a verify pass) and one call per token (decode)
-    give the same bits, and leave the same cache rows."""
-    L = 1000
+    give the same bits, and leave the same cache rows.  From 5000 cached rows a
+    decode call takes all six query heads of a KV head per workgroup (and at
+    9000 two chunks per workgroup), the verify pass two heads and one chunk:
+    each chunk's partial is the same computation either way."""
     a, out_a = _attn_case(GEOM, L, 16, seed=21, check_rows=False)
     b, _, _ = _decoder(GEOM, a.desc.max_seq, seed=21)
     K, V = synth.kv_prefill(21, synth.WL_ATTENTION, 0, GEOM.kv_heads, L, GEOM.head_dim)
