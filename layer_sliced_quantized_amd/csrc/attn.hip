@@ -117,11 +117,14 @@ __device__ __forceinline__ void head_prep(float (&x)[NC], const AttnParams& p, c
 //      weights exp(s - max) and their sum;
 //   5. P V per (token, head): one thread per dimension over the chunk's rows,
 //      written as the chunk's partial.
-// Each chunk's partial is computed by exactly the operations of k_attn_split
-// below, whatever GRP and cpw are, so a decode step through this kernel (one
-// token on a long cache: all query heads of a KV head per workgroup, several
-// chunks per workgroup) and a verify pass through k_attn_split give the same
-// bits.
+// Each chunk's (max, sum, P V) is computed by exactly the operations of
+// k_attn_split below.  The chunks of a range are then merged in order into
+// one partial per (token, head): M' = max(M, m_c), L = L e^(M - M') + l_c
+// e^(m_c - M'), O likewise, from M = -inf, L = O = 0; with one chunk per
+// range that is the chunk's own partial bit for bit (both factors are exp(0)
+// = 1 and 0 * 0 = 0).  The range size comes from the cache size alone, so a
+// decode step (all query heads of a KV head per workgroup) and a verify pass
+// (two) merge the same chunks in the same order and give the same bits.
 // Every group of query heads of a range appends the same rows itself (the
 // same bits), so each reads them back after its own stores.
 template <int GRP, int HD, int TM>   // GRP: query heads per workgroup; TM: most tokens
@@ -137,6 +140,8 @@ __global__ __launch_bounds__(256) void k_attn_split_range(AttnParams p, int T, i
   __shared__ __attribute__((aligned(16))) float pl[TM][GRP][C];
   __shared__ float rbuf[4][HD];
   __shared__ float ml[TM][GRP][2];
+  __shared__ float run[TM][GRP][2];   // running max and sum of the range
+  __shared__ float fac[TM][GRP][2];   // this chunk's rescaling of the running output and of its own
   const int nsub = p.q_heads / p.kv_heads / GRP;   // query-head groups per KV head
   const int nrange = (p.nchunk + cpw - 1) / cpw;
   // Workgroups go to the XCDs round robin by index.  The nsub workgroups that
@@ -215,6 +220,15 @@ __global__ __launch_bounds__(256) void k_attn_split_range(AttnParams p, int T, i
   // 3. queries of tokens tq0.. (those whose position reaches the range):
   // pair q = (t - tq0) GRP + h, wave w takes pairs w + 4 m, all its loads first
   const int tq0 = max(0, cb * C - p0);
+  float orun[TM][GRP];   // this thread's dimension of the range's output, per (token, head)
+#pragma unroll
+  for (int t = 0; t < TM; ++t)
+#pragma unroll
+    for (int h = 0; h < GRP; ++h) orun[t][h] = 0.0f;
+  if (tid < TM * GRP) {
+    run[tid / GRP][tid % GRP][0] = -INFINITY;
+    run[tid / GRP][tid % GRP][1] = 0.0f;
+  }
   {
     const int npair = (T - tq0) * GRP;
     constexpr int MQ = (TM * GRP + 3) / 4;
@@ -300,13 +314,24 @@ __global__ __launch_bounds__(256) void k_attn_split_range(AttnParams p, int T, i
       const float e = lane < nvalid ? __expf(sc - m) : 0.0f;
       if (lane < C) pl[t][h][lane] = e;
       const float l = wave_sum(e);
-      if (lane == 0) { ml[t][h][0] = m; ml[t][h][1] = l; }
+      if (lane == 0) {
+        // merge into the range: running max M' and the two rescaling factors
+        const float M = run[t][h][0];
+        const float Mn = fmaxf(M, m);
+        const float fa = __expf(M - Mn), fb = __expf(m - Mn);
+        fac[t][h][0] = fa;
+        fac[t][h][1] = fb;
+        run[t][h][0] = Mn;
+        run[t][h][1] = __builtin_fmaf(run[t][h][1], fa, l * fb);
+      }
     }
     __syncthreads();
 
-    // 5. P V
+    // 5. P V, merged into the range's output
     if (dact) {
-      for (int t = tq; t < T; ++t) {
+#pragma unroll
+      for (int t = 0; t < TM; ++t) {
+        if (t < tq || t >= T) continue;
 #pragma unroll
         for (int h = 0; h < GRP; ++h) {
           float o = 0.0f;
@@ -318,13 +343,25 @@ __global__ __launch_bounds__(256) void k_attn_split_range(AttnParams p, int T, i
             o = __builtin_fmaf(w.z, vf[q + 2], o);
             o = __builtin_fmaf(w.w, vf[q + 3], o);
           }
-          float* dst = p.part + (((size_t)t * p.q_heads + h0 + h) * p.nchunk + c) * (HD + 2);
-          dst[2 + tid] = o;
-          if (tid == 0) { dst[0] = ml[t][h][0]; dst[1] = ml[t][h][1]; }
+          orun[t][h] = __builtin_fmaf(orun[t][h], fac[t][h][0], o * fac[t][h][1]);
         }
       }
     }
-    __syncthreads();   // pl and ml are rewritten by the next chunk
+    __syncthreads();   // pl, ml and fac are rewritten by the next chunk
+  }
+
+  // the range's partial for every (token, head) that reached it
+  if (dact) {
+#pragma unroll
+    for (int t = 0; t < TM; ++t) {
+      if (t < tq0 || t >= T) continue;
+#pragma unroll
+      for (int h = 0; h < GRP; ++h) {
+        float* dst = p.part + (((size_t)t * p.q_heads + h0 + h) * p.nchunk + rng) * (HD + 2);
+        dst[2 + tid] = orun[t][h];
+        if (tid == 0) { dst[0] = run[t][h][0]; dst[1] = run[t][h][1]; }
+      }
+    }
   }
 }
 
@@ -548,9 +585,10 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
 // contiguous chunk range [nc w / NW, nc (w+1) / NW): the waves' maxima, their
 // sums of weighted chunk sums and their partial outputs meet in LDS in wave
 // order, and wave 0 finishes.  32 value loads per wave are in flight at a
-// time.  The launch takes CW waves when the cache has more than 64 chunks,
-// else one (the long branch is then never taken), so a slice's decode and
-// verify steps always sum in the same order.
+// time.  The launch takes CW waves when the cache holds more than 64
+// partials (chunks, or ranges of chunks on long caches), else one (the long
+// branch is then never taken), so a slice's decode and verify steps always
+// sum in the same order.
 constexpr int CW = 8;
 __global__ __launch_bounds__(64 * CW) void k_attn_combine(AttnParams p) {
   constexpr int VPRE = 32;   // chunks whose values are requested with the statistics
@@ -565,7 +603,7 @@ __global__ __launch_bounds__(64 * CW) void k_attn_combine(AttnParams p) {
   // the gate input does not depend on the position: request it first
   const float gz = p.off_g >= 0 && w == 0 ? p.y[(size_t)t * p.y_stride + p.off_g + h * p.hd + d] : 0.0f;
   const int P = (p.ctrl ? p.ctrl->pos : p.pos) + t;
-  const int nc = P / ATT_CHUNK + 1;
+  const int nc = P / ATT_CHUNK / p.rchunks + 1;   // partials that token t reaches
   const int stride = p.hd + 2;
   const float* base = p.part + ((size_t)t * p.q_heads + h) * p.nchunk * stride;
   float o = 0.0f, L = 0.0f;
@@ -661,38 +699,52 @@ hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {
       p.nchunk * ATT_CHUNK < p.max_seq || (p.rope_dims && !p.rope_cs) ||
       p.q_heads % p.kv_heads || T < 1 || T > MAX_T)
     return hipErrorInvalidValue;
-  // Query heads per split workgroup: with one token and a cache of at least
-  // 512 (KV head, chunk) pairs, all of a KV head's group (its keys and values
-  // are then read once per chunk: 100.6 -> 71.9 us at 32768 rows, 22.3 -> 17.2
-  // at 4096 on MI355X); otherwise at most 2 (more workgroups for a short cache,
-  // 9.6 against 11.6 us at 512 rows; and the prepared queries of 16 tokens
-  // fill LDS).  Chunks per workgroup: enough that the grid stays near 1024
-  // workgroups on long caches.
+  // Chunks per partial, from the cache size alone (decode and verify must
+  // merge alike): one up to 1024 (KV head, chunk) pairs, beyond that enough
+  // that about 1024 ranges remain.  A partial is 4 (hd + 2) bytes per token and
+  // head: per 32-row chunk that is three times its K/V for 16 tokens, so long
+  // caches merge their chunks in the split kernel.
   const int grp = p.q_heads / p.kv_heads;
-  const bool one = T == 1 && p.kv_heads * p.nchunk >= 512 &&
-                   (grp == 1 || grp == 2 || grp == 3 || grp == 4 || grp == 6 || grp == 8);
-  const int hpw = one ? grp : (grp % 2 == 0 ? 2 : 1);
+  const int npairs = p.kv_heads * p.nchunk;
+  const int R = npairs > 1024 ? std::min(16, (npairs + 1023) / 1024) : 1;
+  AttnParams q = p;
+  q.rchunks = R;
+  // Query heads per split workgroup: with one token on a cache of at least
+  // 512 pairs, all of a KV head's group (its keys and values are then read
+  // once per chunk: 100.6 -> 71.9 us at 32768 rows, 22.3 -> 17.2 at 4096 on
+  // MI355X); otherwise at most 2 (more workgroups for a short cache, 9.6
+  // against 11.6 us at 512 rows; and the prepared queries of 16 tokens fill
+  // LDS).  The range kernel runs whenever chunks are merged or all heads go
+  // to one workgroup; the per-chunk kernel otherwise.
+  const bool all_heads = T == 1 && npairs >= 512 &&
+                         (grp == 1 || grp == 2 || grp == 3 || grp == 4 || grp == 6 || grp == 8);
+  const bool range = R > 1 || all_heads;
+  const int hpw = all_heads ? grp : (grp % 2 == 0 ? 2 : 1);
   const int nsub = grp / hpw;
-  const int units = p.kv_heads * p.nchunk * nsub;
-  const int cpw = one && units > 1024 ? std::min(16, (units + 1023) / 1024) : 1;
-  const int nrange = (p.nchunk + cpw - 1) / cpw;
-  const int pairs = p.kv_heads * nrange;           // (KV head, chunk range) pairs, padded to groups of 8
+  const int nrange = (p.nchunk + R - 1) / R;
+  const int pairs = p.kv_heads * (range ? nrange : p.nchunk);   // padded to groups of 8
   const unsigned grid = (unsigned)(((pairs + 7) / 8) * 8 * nsub);
-#define SLQ_R(n, hd) case n: k_attn_split_range<n, hd, 1><<<grid, 256, 0, s>>>(p, T, cpw); break;
-#define SLQ_G(n, hd) case n: k_attn_split<n, hd><<<grid, 256, 0, s>>>(p, T); break;
-#define SLQ_HD(hd)                                                              \
-  case hd:                                                                      \
-    if (one) {                                                                  \
-      switch (hpw) {                                                            \
-        SLQ_R(1, hd) SLQ_R(2, hd) SLQ_R(3, hd) SLQ_R(4, hd) SLQ_R(6, hd) SLQ_R(8, hd) \
-        default: return hipErrorInvalidValue;                                   \
-      }                                                                         \
-    } else {                                                                    \
-      switch (hpw) {                                                            \
-        SLQ_G(1, hd) SLQ_G(2, hd)                                               \
-        default: return hipErrorInvalidValue;                                   \
-      }                                                                         \
-    }                                                                           \
+#define SLQ_R1(n, hd) case n: k_attn_split_range<n, hd, 1><<<grid, 256, 0, s>>>(q, T, R); break;
+#define SLQ_RT(n, hd) case n: k_attn_split_range<n, hd, MAX_T><<<grid, 256, 0, s>>>(q, T, R); break;
+#define SLQ_G(n, hd) case n: k_attn_split<n, hd><<<grid, 256, 0, s>>>(q, T); break;
+#define SLQ_HD(hd)                                                                  \
+  case hd:                                                                          \
+    if (range && T == 1) {                                                          \
+      switch (hpw) {                                                                \
+        SLQ_R1(1, hd) SLQ_R1(2, hd) SLQ_R1(3, hd) SLQ_R1(4, hd) SLQ_R1(6, hd) SLQ_R1(8, hd) \
+        default: return hipErrorInvalidValue;                                       \
+      }                                                                             \
+    } else if (range) {                                                             \
+      switch (hpw) {                                                                \
+        SLQ_RT(1, hd) SLQ_RT(2, hd)                                                 \
+        default: return hipErrorInvalidValue;                                       \
+      }                                                                             \
+    } else {                                                                        \
+      switch (hpw) {                                                                \
+        SLQ_G(1, hd) SLQ_G(2, hd)                                                   \
+        default: return hipErrorInvalidValue;                                       \
+      }                                                                             \
+    }                                                                               \
     break;
   switch (p.hd) {
     SLQ_HD(64) SLQ_HD(128) SLQ_HD(192) SLQ_HD(256)
@@ -700,8 +752,9 @@ hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {
   }
 #undef SLQ_HD
 #undef SLQ_G
-#undef SLQ_R
-  k_attn_combine<<<T * p.q_heads * (p.hd / 64), p.nchunk > 64 ? 64 * CW : 64, 0, s>>>(p);
+#undef SLQ_RT
+#undef SLQ_R1
+  k_attn_combine<<<T * p.q_heads * (p.hd / 64), nrange > 64 ? 64 * CW : 64, 0, s>>>(q);
   return hipGetLastError();
 }
 

@@ -249,8 +249,9 @@ struct AttnParams {
   int max_seq;
   const Ctrl* ctrl;      // position ctrl->pos; nullptr: pos below
   int pos;
-  float* part;           // [T][q_heads][nchunk][hd + 2]
+  float* part;           // [T][q_heads][nchunk][hd + 2]: one partial per rchunks chunks
   int nchunk;            // max_seq / chunk
+  int rchunks;           // chunks per partial (set by launch_attention from the cache size)
   float* u_out;          // [T][q_heads*hd] (nullable)
   Act next; int next_qt; // digits of the output (next.xd == nullptr: none)
 };
