@@ -701,12 +701,15 @@ hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {
     return hipErrorInvalidValue;
   // Chunks per partial, from the cache size alone (decode and verify must
   // merge alike): one up to 1024 (KV head, chunk) pairs, beyond that enough
-  // that about 1024 ranges remain.  A partial is 4 (hd + 2) bytes per token and
-  // head: per 32-row chunk that is three times its K/V for 16 tokens, so long
-  // caches merge their chunks in the split kernel.
+  // that about 512 ranges remain (a sweep of 256 to 4096 at 32768 rows on
+  // MI355X: 512 is the fastest for one query, 51 us, and for sixteen, 460 us;
+  // the decode grid then fits the machine's resident workgroups at once).  A
+  // partial is 4 (hd + 2) bytes per token and head: per 32-row chunk that is
+  // three times its K/V for 16 tokens, so long caches merge their chunks in the
+  // split kernel.
   const int grp = p.q_heads / p.kv_heads;
   const int npairs = p.kv_heads * p.nchunk;
-  const int R = npairs > 1024 ? std::min(16, (npairs + 1023) / 1024) : 1;
+  const int R = npairs > 1024 ? std::min(16, (npairs + 511) / 512) : 1;
   AttnParams q = p;
   q.rchunks = R;
   // Query heads per split workgroup: with one token on a cache of at least

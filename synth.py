@@ -131,11 +131,13 @@ def stream(seed: int, *key: int) -> np.random.Generator:
     return np.random.Generator(np.random.PCG64(np.random.SeedSequence(seed, spawn_key=tuple(int(k) for k in key))))
 
 
-def quant_blocks(rng: np.random.Generator, qtype: int, rows: int, cols: int) -> np.ndarray:
+def quant_blocks(rng: np.random.Generator, qtype: int, rows: int, cols: int, centered: bool = False) -> np.ndarray:
     """Random GGUF blocks, returned as uint8 [rows, cols // 32 * block_bytes].
 
     Scales: uniform [0.002, 0.02] drawn in fp64 and rounded to fp16 (RNE).
-    Q4_0 codes: uniform bytes, i.e. every nibble uniform on 0..15.
+    Q4_0 codes: uniform bytes, i.e. every nibble uniform on 0..15 (weights
+    q - 8 of mean -0.5); with centered, every nibble uniform on 1..15
+    (weights of mean 0, so deep slices keep their residual stream in range).
     Q8_0 codes: uniform on -127..127 inclusive.
     """
     if cols % QK:
@@ -145,7 +147,11 @@ def quant_blocks(rng: np.random.Generator, qtype: int, rows: int, cols: int) -> 
     bb = BLOCK_BYTES[qtype]
     out = np.empty((rows, nb, bb), dtype=np.uint8)
     out[:, :, 0:2] = d.view(np.uint8).reshape(rows, nb, 2)
-    if qtype == Q4_0:
+    if qtype == Q4_0 and centered:
+        lo = rng.integers(1, 16, size=(rows, nb, 16), dtype=np.uint8)
+        hi = rng.integers(1, 16, size=(rows, nb, 16), dtype=np.uint8)
+        out[:, :, 2:] = lo | (hi << 4)
+    elif qtype == Q4_0:
         out[:, :, 2:] = rng.integers(0, 256, size=(rows, nb, 16), dtype=np.uint8)
     elif qtype == Q8_0:
         out[:, :, 2:] = rng.integers(-127, 128, size=(rows, nb, 32), dtype=np.int8).view(np.uint8)
@@ -203,7 +209,7 @@ def vector_shapes(shape: ModelShape, layer: int) -> dict:
 
 
 def layer_tensors(shape: ModelShape, qtype: int, seed: int, workload: int, layer: int,
-                  threads: int = 1) -> dict:
+                  threads: int = 1, centered: bool = False) -> dict:
     """All tensors of one layer: raw GGUF blocks for matrices, fp32 ones for norm weights."""
     out = {name: np.ones(n, dtype=np.float32) for name, n in vector_shapes(shape, layer).items()}
     if shape.dn_variant and not shape.is_attention(layer):
@@ -212,7 +218,7 @@ def layer_tensors(shape: ModelShape, qtype: int, seed: int, workload: int, layer
 
     def gen(item):
         name, (r, c) = item
-        return name, quant_blocks(stream(seed, workload, layer, TENSOR_IDS[name]), qtype, r, c)
+        return name, quant_blocks(stream(seed, workload, layer, TENSOR_IDS[name]), qtype, r, c, centered)
 
     if threads > 1:
         with ThreadPoolExecutor(threads) as ex:

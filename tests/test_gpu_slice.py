@@ -322,3 +322,31 @@ def test_hybrid_q8_slice_8_layers():
     ref = orc.verify(H[1:5], raw=True)
     for t in range(4):
         assert rel_err(out[t], ref[t]) <= TOL, t
+
+
+DEEP = synth.ModelShape(
+    name="deep_hybrid_128", hidden=128, n_layers=64, attn_period=4,
+    dn_heads=2, dn_dk=64, dn_dv=64, q_heads=4, kv_heads=2, head_dim=64, rope_dims=32,
+    rope_theta=1e7, qk_norm=True, attn_gate=True, eps=1e-6, ffn=256, vocab=0)
+
+
+def test_deep_slice_in_range_through_the_fp16_boundary():
+    """64 layers whose weights have mean 0 (centred Q4_0 codes), so the
+    residual stream stays in fp16 range and every layer sees an input that
+    is not dominated by one direction: the fp16 outputs of decode steps and a
+    verify pass match the oracle, and |h| stays far below the fp16 limit.
+    (Random Q8_0 codes span +-127 and make rows ~10x larger, so the stream
+    leaves fp16 range whatever their mean; Q8_0 is covered elsewhere.)"""
+    s, orc, _, _ = make_pair(DEEP, synth.Q4_0, 0, 64, workload=120, prefill=24, max_seq=128, max_verify=4,
+                             io_fp32=False, centered=True)
+    H = inputs(DEEP, 8, workload=120, io_fp32=False)
+    for t in range(4):
+        got = s.decode(torch.from_numpy(H[t]).cuda()).cpu().numpy().astype(np.float64)
+        want = orc.decode(H[t], raw=True)
+        assert np.max(np.abs(want)) < 1e3
+        assert rel_err(got, want) <= TOL, t
+    got = s.verify(torch.from_numpy(H[4:8]).cuda()).cpu().numpy().astype(np.float64)
+    want = orc.verify(H[4:8], raw=True)
+    for t in range(4):
+        assert rel_err(got[t], want[t]) <= TOL, t
+    s.sync_check()

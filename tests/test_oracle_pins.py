@@ -353,3 +353,15 @@ def test_attention_layer_closed_form():
     np.testing.assert_allclose(out, h.astype(np.float64) + Wo @ u, rtol=1e-12, atol=1e-12)
     # the new row was written to the cache, rounded to fp16 (k = 0 after QK-norm)
     assert np.all(orc.kv[3][0][:, L] == 0) and np.all(orc.kv[3][1][:, L] == 0)
+
+
+def test_centered_q4_codes_have_zero_mean_weights():
+    """The centred Q4_0 draw: nibbles 1..15 only, so weights (q - 8) d are
+    symmetric about 0; the default draw keeps nibble 0 (mean -0.5)."""
+    import synth
+    raw = synth.quant_blocks(synth.stream(0, 1, 2, 3), synth.Q4_0, 64, 256, centered=True).reshape(64, 8, 18)
+    nib = np.concatenate([raw[:, :, 2:] & 15, raw[:, :, 2:] >> 4]).ravel()
+    assert nib.min() == 1 and nib.max() == 15
+    assert abs(nib.astype(np.float64).mean() - 8.0) < 0.05
+    plain = synth.quant_blocks(synth.stream(0, 1, 2, 3), synth.Q4_0, 64, 256).reshape(64, 8, 18)
+    assert (np.concatenate([plain[:, :, 2:] & 15, plain[:, :, 2:] >> 4]) == 0).any()
