@@ -13,4 +13,4 @@ unpinned: fidelity to a real trained checkpoint (no weights or golden outputs
 exist for it).
 """
 from . import qref  # noqa: F401
-from .model import SliceOracle, rmsnorm, sigmoid, silu, l2normalize, rope, attend, deltanet_update  # noqa: F401
+from .model import SliceOracle, DraftHead, mtp_input, rmsnorm, sigmoid, silu, l2normalize, rope, attend, deltanet_update  # noqa: F401

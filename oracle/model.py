@@ -34,6 +34,17 @@ Readings where the pages are silent (each listed in the design notes):
   the new K/V row is rounded to fp16 before it is attended;
   attention scale 1/sqrt(head_dim); head h reads KV head h // (q_heads/kv_heads).
 
+The draft head (mtp_input, DraftHead): the pages say only that a draft head
+guesses the token after the one just sampled, on the last stage, and that the
+engine follows llama.cpp's graph for this model family (SwarmLLM README,
+pipeline diagram and credits), so its form is read from the published
+multi-token-prediction module of that family -- the embedding of the sampled
+token and the hidden state it was sampled from (before the final norm), each
+RMS-normalised with weights of its own, concatenated embedding first,
+projected back to the hidden width, then one decoder layer of the
+full-attention kind with its own KV cache, the head's own final norm and the
+shared LM head; further drafts feed the draft and the layer's output back in.
+
 The qwen3_5 form of the DeltaNet layers (deltanet_q35, selected by the
 shape's dn_variant): the pages name the layer kind only, so its details are
 read from the published form of the Gated DeltaNet mixer -- a depthwise causal
@@ -427,3 +438,59 @@ class SliceOracle:
     def argmax(logits: np.ndarray) -> int:
         """Greedy choice; the lowest index wins an exact tie."""
         return int(np.argmax(logits))
+
+
+# ------------------------------------------------------------- draft head
+
+def mtp_input(qtype: int, E: np.ndarray, token: int, h: np.ndarray, w_e, w_h, fc: np.ndarray,
+              hidden: int, eps: float) -> np.ndarray:
+    """Input of the draft head's layer: fc [H][2H] times the concatenation of
+    RMSNorm(embedding row `token`; w_e) and RMSNorm(h; w_h), embedding first.
+    E: the embedding table's raw blocks [vocab][H/32 blocks]; h: the hidden
+    state the token was sampled from."""
+    if not 0 <= token < E.shape[0]:
+        raise ValueError("token outside the vocabulary")
+    e = qref.dequant(qtype, E[token:token + 1], 1, hidden)[0]
+    c = np.concatenate([rmsnorm(e, w_e, eps), rmsnorm(np.asarray(h, dtype=np.float64), w_h, eps)])
+    return qref.gemv(qtype, fc, hidden, 2 * hidden, c)
+
+
+class DraftHead:
+    """The draft head as a stage of its own: one full-attention decoder layer
+    (layer 0 of `shape`, which must be an attention layer) with its own KV
+    cache and position, mtp_input in front of it, and behind it its final
+    norm (glob["out_norm"]) and the shared LM head (glob["embed"] / ["head"]).
+    mtp: {"mtp_fc", "mtp_norm_e", "mtp_norm_h"}.  Boundary vectors (the input
+    h, the layer's input and output) are in the boundary dtype."""
+
+    def __init__(self, shape, qtype: int, layer: dict, mtp: dict, glob: dict, max_seq: int = 1024,
+                 io_fp32: bool = False):
+        if not shape.is_attention(0):
+            raise ValueError("the draft head's layer is an attention layer")
+        self.s = shape
+        self.qtype = qtype
+        self.mtp = mtp
+        self.stage = SliceOracle(shape, qtype, 0, 1, {0: layer}, glob=glob, max_seq=max_seq, io_fp32=io_fp32)
+
+    def reset(self, pos: int):
+        self.stage.reset(pos)
+
+    def set_kv(self, K: np.ndarray, V: np.ndarray):
+        self.stage.set_kv(0, K, V)
+
+    @property
+    def pos(self) -> int:
+        return self.stage.pos
+
+    def input(self, token: int, h: np.ndarray) -> np.ndarray:
+        """The layer's input, rounded to the boundary dtype."""
+        x = mtp_input(self.qtype, self.stage.G["embed"], token, h, self.mtp["mtp_norm_e"], self.mtp["mtp_norm_h"],
+                      self.mtp["mtp_fc"], self.s.hidden, self.s.eps)
+        return self.stage._round_out(x)
+
+    def draft(self, token: int, h: np.ndarray):
+        """One draft at the head's position (which then advances): (draft
+        token, the layer's output in the boundary dtype, its logits)."""
+        out = self.stage.decode(self.input(token, h))
+        logits = self.stage.head_logits(out)
+        return SliceOracle.argmax(logits), out, logits

@@ -37,6 +37,7 @@ WL_GEMV = 1
 WL_DELTANET = 2
 WL_ATTENTION = 3
 WL_SLICE = 4
+WL_MTP = 5                   # the draft head's own layer and tensors
 
 # tensor ids used in the stream keys (stable; never renumber)
 TENSOR_IDS = {
@@ -50,6 +51,8 @@ TENSOR_IDS = {
     "accept": 55, "token": 56,
     # qwen3_5 form of the DeltaNet layers: conv taps, decay parameters, gated-norm weights, conv state
     "dn_conv": 17, "dn_alog": 18, "dn_dtb": 19, "dn_norm": 28, "dn_conv_state": 57,
+    # the draft head: input projection [H][2H], the norms of its two inputs, its final norm
+    "mtp_fc": 43, "mtp_norm_e": 44, "mtp_norm_h": 45, "mtp_out_norm": 46,
 }
 
 
@@ -264,6 +267,24 @@ def global_tensors(shape: ModelShape, qtype: int, seed: int, workload: int) -> d
         if not shape.tied_head:
             out["head"] = quant_blocks(stream(seed, workload, 0, TENSOR_IDS["head"]), qtype,
                                        shape.vocab, shape.hidden)
+    return out
+
+
+def mtp_shape(shape: ModelShape) -> ModelShape:
+    """The draft head's stage: one layer of the model's full-attention kind."""
+    return dataclasses.replace(shape, name=shape.name + "_mtp", n_layers=1, attn_period=0)
+
+
+def mtp_tensors(shape: ModelShape, qtype: int, seed: int, workload: int = WL_MTP) -> dict:
+    """The draft head's own tensors besides its layer: the input projection
+    mtp_fc [H][2H] (GGUF blocks as quant_blocks), and fp32 weights 1 + 0.25
+    N(0,1) of the embedding-side and hidden-side input norms and of its final
+    norm (unequal, so that a swap of the two inputs shows)."""
+    H = shape.hidden
+    out = {"mtp_fc": quant_blocks(stream(seed, workload, 0, TENSOR_IDS["mtp_fc"]), qtype, H, 2 * H)}
+    for name in ("mtp_norm_e", "mtp_norm_h", "mtp_out_norm"):
+        r = stream(seed, workload, 0, TENSOR_IDS[name])
+        out[name] = (1.0 + 0.25 * r.standard_normal(H)).astype(np.float32)
     return out
 
 

@@ -21,6 +21,7 @@ scale, RoPE of q one position off, a dropped q-norm, swapped q/k projections,
 wrong decay / write-strength / gate coefficients, a wrong head slice.  Every
 mutant must fail at least one pin.
 """
+import dataclasses
 import inspect
 import math
 import textwrap
@@ -478,6 +479,91 @@ def test_deltanet_q35_layer_closed_form():
     pin_deltanet_q35_layer()
 
 
+# ------------------------------------------------------------ draft head
+
+def _const_rows_q4(values: list, cols: int) -> np.ndarray:
+    """Q4_0 rows whose every weight is the given (code, scale): value (code - 8) * scale."""
+    nb = cols // 32
+    blk = np.zeros((len(values), nb, 18), np.uint8)
+    for r, (code, d) in enumerate(values):
+        blk[r, :, 0:2] = np.array([d], np.float16).view(np.uint8)
+        blk[r, :, 2:] = code | (code << 4)
+    return blk.reshape(len(values), nb * 18)
+
+
+def pin_mtp_input():
+    """The draft head's input projection on one-hot rows of fc: each output is a
+    known multiple of one entry of [RMSNorm(e; w_e), RMSNorm(h; w_h)].  The
+    embedding rows are constant (value v, so RMSNorm gives v / sqrt(v^2 + eps)
+    times w_e) and h is a +-3 pattern (RMSNorm h / sqrt(9 + eps) times w_h)."""
+    H = 64
+    rows = [(9, 0.5), (5, 0.25), (12, 2.0), (8, 1.0)]          # values 0.5, -0.75, 8, 0
+    E = _const_rows_q4(rows, H)
+    h = 3.0 * _pm1(7, H).astype(np.float64)
+    w_e = (1.0 + np.arange(H) / 64.0).astype(np.float32)
+    w_h = (2.0 - np.arange(H) / 128.0).astype(np.float32)
+    ent = {0: (3, 1.0, 1), 1: (H + 5, 0.5, -1), 2: (H - 1, 2.0, 1), 3: (2 * H - 1, 0.25, 1), 6: (H, 1.5, -1)}
+    fc = onehot_q4(H, 2 * H, ent)
+    for tok, (code, d) in enumerate(rows):
+        v = (code - 8) * d
+        ne = v / math.sqrt(v * v + EPS)
+        nh = h / math.sqrt(9.0 + EPS)
+        c = np.concatenate([ne * w_e.astype(np.float64), nh * w_h.astype(np.float64)])
+        exp = np.zeros(H)
+        for r, (col, dd, sgn) in ent.items():
+            exp[r] = sgn * dd * c[col]
+        got = omodel.mtp_input(synth.Q4_0, E, tok, h, w_e, w_h, fc, H, EPS)
+        np.testing.assert_allclose(got, exp, rtol=1e-12, atol=1e-15)
+
+
+def test_mtp_input_closed_form():
+    pin_mtp_input()
+
+
+def test_mtp_input_rejects_a_token_outside_the_vocabulary():
+    E = _const_rows_q4([(9, 0.5)], 64)
+    with pytest.raises(ValueError):
+        omodel.mtp_input(synth.Q4_0, E, 1, np.ones(64), np.ones(64), np.ones(64), onehot_q4(64, 128, {}), 64, EPS)
+
+
+def test_draft_head_through_an_identity_layer():
+    """With every matrix of the draft head's layer zero the layer leaves its
+    input unchanged, so a draft is argmax(W_head RMSNorm(x; out_norm)) of the
+    rounded projection x, computed here from the dequantised matrices with
+    numpy products."""
+    sh = synth.mtp_shape(dataclasses.replace(TINY, vocab=48, tied_head=False))
+    T = synth.layer_tensors(sh, synth.Q4_0, 0, synth.WL_MTP, 0)
+    _zero_all_shape(T, sh, 0)
+    M = synth.mtp_tensors(sh, synth.Q4_0, 3)
+    G = synth.global_tensors(sh, synth.Q4_0, 3, 0)
+    G["out_norm"] = M["mtp_out_norm"]
+    dh = oracle.DraftHead(sh, synth.Q4_0, T, M, G, max_seq=16, io_fp32=False)
+    dh.reset(2)
+    H = sh.hidden
+    h = synth.hidden_inputs(3, 0, 1, H)[0]
+    Ed = qref.dequant(synth.Q4_0, G["embed"], sh.vocab, H)
+    Fd = qref.dequant(synth.Q4_0, M["mtp_fc"], H, 2 * H)
+    Hd = qref.dequant(synth.Q4_0, G["head"], sh.vocab, H)
+
+    def rms(v, w):
+        return v / np.sqrt(np.mean(v * v) + EPS) * w.astype(np.float64)
+
+    for tok in (0, 17, 47):
+        x = Fd @ np.concatenate([rms(Ed[tok], M["mtp_norm_e"]), rms(h.astype(np.float64), M["mtp_norm_h"])])
+        xr = x.astype(np.float16)
+        logits = Hd @ rms(xr.astype(np.float64), M["mtp_out_norm"])
+        d, out, lg = dh.draft(tok, h)
+        np.testing.assert_array_equal(out, xr)
+        np.testing.assert_allclose(lg, logits, rtol=1e-9, atol=1e-12)
+        assert d == int(np.argmax(logits))
+    assert dh.pos == 5
+
+
+def _zero_all_shape(T, shape, layer):
+    for n, (r, c) in synth.matrix_shapes(shape, layer).items():
+        T[n] = onehot_q4(r, c, {})
+
+
 MUTANTS = {
     "ffn_gate_up_swapped": ("SliceOracle.ffn", 'silu(self._mv(l, "w_gate", x)) * self._mv(l, "w_up", x)',
                             'silu(self._mv(l, "w_up", x)) * self._mv(l, "w_gate", x)'),
@@ -516,10 +602,18 @@ MUTANTS = {
                        "sigmoid(np.float64(np.float32(s.dn_a_scale)) * b)"),
     "q35_gate_coeff": ("SliceOracle.deltanet_q35", "zg = np.float64(np.float32(s.dn_z_scale)) * z", "zg = z"),
     "dn_v_for_k": ("deltanet_heads", "vh = v[hh * dv:(hh + 1) * dv]", "vh = k[hh * dv:(hh + 1) * dv]"),
+    "mtp_inputs_swapped": ("mtp_input", "np.concatenate([rmsnorm(e, w_e, eps), rmsnorm(np.asarray(h, dtype=np.float64), w_h, eps)])",
+                           "np.concatenate([rmsnorm(np.asarray(h, dtype=np.float64), w_h, eps), rmsnorm(e, w_e, eps)])"),
+    "mtp_norm_weights_swapped": ("mtp_input", "rmsnorm(e, w_e, eps), rmsnorm(np.asarray(h, dtype=np.float64), w_h, eps)",
+                                 "rmsnorm(e, w_h, eps), rmsnorm(np.asarray(h, dtype=np.float64), w_e, eps)"),
+    "mtp_embed_norm_dropped": ("mtp_input", "rmsnorm(e, w_e, eps)", "e * np.asarray(w_e, dtype=np.float64)"),
+    "mtp_hidden_norm_dropped": ("mtp_input", "rmsnorm(np.asarray(h, dtype=np.float64), w_h, eps)",
+                                "np.asarray(h, dtype=np.float64) * np.asarray(w_h, dtype=np.float64)"),
+    "mtp_next_token_row": ("mtp_input", "E[token:token + 1]", "E[token + 1:token + 2]"),
 }
 
 PINS = [pin_ffn, pin_attention, pin_attention_key, pin_deltanet, pin_deltanet_token, pin_conv_silu,
-        pin_gated_rmsnorm, pin_deltanet_heads_q35, pin_deltanet_q35_layer]
+        pin_gated_rmsnorm, pin_deltanet_heads_q35, pin_deltanet_q35_layer, pin_mtp_input]
 
 
 def _mutant(where: str, old: str, new: str):
