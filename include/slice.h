@@ -236,6 +236,12 @@ typedef struct slice_config {
     int32_t dn_variant;
     int32_t dn_k_heads;             /* 0: dn_heads                                      */
     int32_t dn_conv;                /* conv width (dn_variant = 1)                      */
+    /* 1: the slice is a draft head (see slice_mtp_input): it also holds the
+     * input projection MTP_FC and the norms MTP_NORM_E / MTP_NORM_H, and
+     * needs has_embed.  Its layers are normally one attention layer
+     * (attn_period 0, layer range [0, 1)), OUT_NORM is the head's own final
+     * norm and the head matrix the model's LM head.                       */
+    int32_t has_mtp;
 } slice_config;
 
 /* Tensor ids for slice_set_tensor.  Matrices take raw GGUF blocks
@@ -261,7 +267,11 @@ enum {
      * taps (conv_dim = 2*dn_k_heads*dn_dk + dn_heads*dn_dv channels in the
      * order q | k | v, tap dn_conv-1 on the current input), DN_ALOG and DN_DTB
      * [dn_heads], DN_NORM [dn_dv] (gated-norm weights, shared by the heads) */
-    SLICE_T_DN_CONV = 17, SLICE_T_DN_ALOG = 18, SLICE_T_DN_DTB = 19, SLICE_T_DN_NORM = 28
+    SLICE_T_DN_CONV = 17, SLICE_T_DN_ALOG = 18, SLICE_T_DN_DTB = 19, SLICE_T_DN_NORM = 28,
+    /* draft head (has_mtp; global, layer argument ignored): MTP_FC (H x 2H,
+     * columns 0..H-1 read the embedding side), MTP_NORM_E and MTP_NORM_H
+     * (fp32 [H]) */
+    SLICE_T_MTP_FC = 43, SLICE_T_MTP_NORM_E = 44, SLICE_T_MTP_NORM_H = 45
 };
 
 /* A stage owns the weights, cache and recurrent state of its own layer range
@@ -404,6 +414,21 @@ int slice_embed(slice_t *s, const int32_t *tok_dev, void *hid_out_dev, void *str
  * may be NULL.  SLICE_EINVAL if the slice has no head. */
 int slice_head_argmax(slice_t *s, const void *hid_in_dev, int32_t *tok_dev,
                       float *logits_dev, void *stream);
+
+/* The draft head's input (SwarmLLM README, pipeline diagram: the last stage's
+ * draft head guesses the token after the one it just sampled; the form is the
+ * published multi-token-prediction module of the model family the engine
+ * follows).  x_out_dev [H] <- W_fc [RMSNorm(E[*tok_dev]) * w_e ;
+ * RMSNorm(hid_in_dev) * w_h], embedding side first, each RMSNorm over its
+ * own H entries with the slice's eps.  tok_dev: int32 on the device (an id
+ * outside 0..vocab-1 reads row 0, as slice_embed); hid_in_dev: the hidden
+ * state the token was sampled from (before the final norm); both vectors in
+ * the boundary format.  x_out_dev then goes to slice_decode of the same
+ * slice, whose output goes to slice_head_argmax for the draft token and, with
+ * the draft, back in here for the next draft.  Stream-ordered; touches no
+ * position or state.  SLICE_EINVAL if the slice is not a draft head or an
+ * argument is NULL.  */
+int slice_mtp_input(slice_t *s, const int32_t *tok_dev, const void *hid_in_dev, void *x_out_dev, void *stream);
 
 /* Decode steps run each layer's products after its mixer as one kernel whose
  * workgroups wait, with a bounded wait, for the product before theirs (the

@@ -185,7 +185,8 @@ class AttnDecoder:
 # ------------------------------------------------------------------- slice
 
 def make_config(shape, qtype: int, begin: int, end: int, *, max_seq: int = 1024, max_verify: int = 16,
-                io_fp32: bool = False, has_embed: bool = False, has_head: bool = False) -> SliceConfig:
+                io_fp32: bool = False, has_embed: bool = False, has_head: bool = False,
+                has_mtp: bool = False) -> SliceConfig:
     """Build a slice_config from any object with the model-shape attributes."""
     c = SliceConfig()
     c.hidden = shape.hidden
@@ -211,6 +212,7 @@ def make_config(shape, qtype: int, begin: int, end: int, *, max_seq: int = 1024,
     c.dn_variant = int(getattr(shape, "dn_variant", 0))
     c.dn_k_heads = int(getattr(shape, "dn_k_heads", 0))
     c.dn_conv = int(getattr(shape, "dn_conv", 0))
+    c.has_mtp = int(has_mtp)
     return c
 
 
@@ -262,6 +264,8 @@ class Slice:
             if name == "embed" and not (self.cfg.has_embed or (self.cfg.has_head and self.cfg.tied_head)):
                 continue
             if name in ("head", "out_norm") and not self.cfg.has_head:
+                continue
+            if name.startswith("mtp_") and not self.cfg.has_mtp:
                 continue
             self.set_tensor(0, name, _dev(arr, self.device), stream)
         torch.cuda.synchronize()
@@ -372,6 +376,15 @@ class Slice:
             tok = torch.empty(1, dtype=torch.int32, device=self.device)
         check(lib().slice_head_argmax(self.handle, _ptr(h), _ptr(tok), _ptr(logits), _stream(stream)))
         return tok
+
+    def mtp_input(self, tok: torch.Tensor, h: torch.Tensor, out: torch.Tensor | None = None,
+                  stream=None) -> torch.Tensor:
+        """Draft head's layer input from the sampled token (int32 on the device)
+        and the hidden state it was sampled from (boundary dtype)."""
+        if out is None:
+            out = torch.empty(self.cfg.hidden, dtype=self.io_dtype, device=self.device)
+        check(lib().slice_mtp_input(self.handle, _ptr(tok), _ptr(h), _ptr(out), _stream(stream)))
+        return out
 
     def sync_check(self, stream=None):
         """Wait for the stream; raise SliceError if a bounded wait inside a

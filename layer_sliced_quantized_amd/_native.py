@@ -23,6 +23,7 @@ TENSOR_IDS = {
     "w_gate": 30, "w_up": 31, "w_down": 32,
     "embed": 40, "head": 41, "out_norm": 42,
     "dn_conv": 17, "dn_alog": 18, "dn_dtb": 19, "dn_norm": 28,
+    "mtp_fc": 43, "mtp_norm_e": 44, "mtp_norm_h": 45,
 }
 
 
@@ -45,6 +46,7 @@ class SliceConfig(ctypes.Structure):
         ("max_seq", ctypes.c_int32), ("max_verify", ctypes.c_int32),
         ("qtype", ctypes.c_int32), ("io_fp32", ctypes.c_int32),
         ("dn_variant", ctypes.c_int32), ("dn_k_heads", ctypes.c_int32), ("dn_conv", ctypes.c_int32),
+        ("has_mtp", ctypes.c_int32),
     ]
 
 
@@ -101,6 +103,7 @@ _SIGS = {
     "slice_prefill": (_I, [_V, _I, _V, _V, _V]),
     "slice_embed": (_I, [_V, _V, _V, _V]),
     "slice_head_argmax": (_I, [_V, _V, _V, _V, _V]),
+    "slice_mtp_input": (_I, [_V, _V, _V, _V, _V]),
     "slice_position": (_I, [_V]),
     "slice_sync_check": (_I, [_V, _V]),
     "slice_free": (None, [_V]),

@@ -138,6 +138,80 @@ hipError_t launch_embed(const Packed& E, const int32_t* tok, void* out, int fp32
   return hipGetLastError();
 }
 
+// The draft head's input digits.  Workgroup 0 takes the embedding row *tok
+// (dequantised from the packed table, as k_embed), workgroup 1 the boundary
+// vector h; each RMS-normalises its H values with its own weights (sum of
+// squares in a fixed order: per thread, then per wave, then waves in order)
+// and writes the digits of its half of the 2H-wide input: blocks 0..H/32-1
+// the embedding side, H/32.. the hidden side.
+template <int QT>
+__global__ __launch_bounds__(256) void k_mtp_in(Packed E, const int32_t* __restrict__ tok, const void* hin,
+                                                int fp32, const float* __restrict__ w_e,
+                                                const float* __restrict__ w_h, float eps, Act x) {
+  constexpr int NH = QT == QT_Q4 ? 1 : 2;
+  extern __shared__ float sv[];          // [H] values, then [4] wave sums
+  const int H = (int)E.cols;
+  const int half = blockIdx.x;
+  const int tid = threadIdx.x;
+  float ss = 0.0f;
+  if (half == 0) {
+    int64_t r = *tok;
+    if (r < 0 || r >= E.rows) r = 0;
+    const int64_t rg = r / RG;
+    const int lane = (int)(r % RG);
+    const int nblk = E.nblk();
+    for (int i = tid; i < H; i += 256) {
+      const int b = i / QK, j = i % QK;
+      const int t = b / TB, bi = b % TB;
+      const int nb_t = min(TB, nblk - t * TB);
+      const uint8_t* tile = E.w + rg * rg_bytes(QT, E.cols) + (size_t)t * tile_bytes(QT);
+      const uint8_t* sc = tile + (size_t)nb_t * NH * RG * 16 + lane * 16 + bi * 2;
+      const float d = __half2float(__ushort_as_half((unsigned short)(sc[0] | (sc[1] << 8))));
+      float v;
+      if (QT == QT_Q4) {
+        const uint8_t c = tile[(size_t)bi * RG * 16 + lane * 16 + (j & 15)];
+        v = (float)((int)(((j < 16 ? c : c >> 4) & 15) ^ 8) - 8) * d;
+      } else {
+        v = (float)(int8_t)tile[(size_t)(bi * NH + (j >> 4)) * RG * 16 + lane * 16 + (j & 15)] * d;
+      }
+      sv[i] = v;
+      ss += v * v;
+    }
+  } else {
+    for (int i = tid; i < H; i += 256) {
+      const float v = fp32 ? reinterpret_cast<const float*>(hin)[i]
+                           : __half2float(reinterpret_cast<const __half*>(hin)[i]);
+      sv[i] = v;
+      ss += v * v;
+    }
+  }
+  ss = wave_sum(ss);
+  const int wave = wave_id(), lane = tid & 63;
+  if (lane == 0) sv[H + wave] = ss;
+  __syncthreads();
+  const float tot = ((sv[H] + sv[H + 1]) + sv[H + 2]) + sv[H + 3];
+  const float rn = 1.0f / sqrtf(tot / (float)H + eps);
+  const float* w = half == 0 ? w_e : w_h;
+  const int nb = H / QK;
+  for (int rg = wave; 2 * rg < nb; rg += 4) {
+    const int i = rg * RG + lane;
+    const bool ok = i < H;
+    const float v = ok ? (sv[i] * rn) * w[i] : 0.0f;
+    const int blk = 2 * rg + (lane >> 5);
+    put_digits(x, QT, 0, half * nb + blk, v, blk < nb);
+  }
+}
+
+hipError_t launch_mtp_input(const Packed& E, const int32_t* tok, const void* hin, int fp32, const float* w_e,
+                            const float* w_h, float eps, Act x, hipStream_t s) {
+  const int H = (int)E.cols;
+  if (H % QK || x.nblk != 2 * H / QK || x.mxd) return hipErrorInvalidValue;
+  const size_t lds = ((size_t)H + 4) * 4;
+  if (E.qt == QT_Q4) k_mtp_in<QT_Q4><<<2, 256, lds, s>>>(E, tok, hin, fp32, w_e, w_h, eps, x);
+  else k_mtp_in<QT_Q8><<<2, 256, lds, s>>>(E, tok, hin, fp32, w_e, w_h, eps, x);
+  return hipGetLastError();
+}
+
 // Greedy argmax in two passes; the larger value wins, the lower index wins a tie.
 __device__ __forceinline__ void better(float& bv, int& bi, float v, int i) {
   if (v > bv || (v == bv && i < bi)) { bv = v; bi = i; }

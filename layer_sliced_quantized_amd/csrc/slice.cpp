@@ -151,6 +151,9 @@ struct Layout {
   std::vector<LayerLayout> layers;   // index l - begin
   Mat embed, head;
   Plan phead{1, 1};
+  Mat mtp_fc;                         // draft head: input projection [H][2H]
+  Plan pmtp{1, 1};
+  size_t mtp_ne = 0, mtp_nh = 0;      // ... and the norms of its two inputs
   size_t out_norm = 0;
   size_t wbytes = 0;
   // workspace
@@ -161,6 +164,7 @@ struct Layout {
   // keeps xa / ssq), per-product split-K regions, per-layer descriptors and
   // sync regions
   size_t xb_d = 0, xb_s = 0, ssq_b = 0, chain_sync = 0;
+  size_t xe_d = 0, xe_s = 0, mtp_y = 0;   // draft head: input digits (2H wide) and projection
   size_t cpart[CHAIN_MAX_PHASES] = {}, ccnt[CHAIN_MAX_PHASES] = {};
   size_t ccnt_n = 0;      // u32 tickets in each ccnt region
   size_t kv_layer_bytes = 0, dn_layer_bytes = 0;
@@ -205,6 +209,9 @@ std::string validate(const slice_config& c) {
     }
   }
   if ((c.has_embed || c.has_head) && c.vocab <= 0) return "vocab must be > 0 with an embedding or head";
+  if (c.has_mtp != 0 && c.has_mtp != 1) return "has_mtp must be 0 or 1";
+  if (c.has_mtp && !c.has_embed) return "a draft head (has_mtp) needs has_embed";
+  if (c.has_mtp && c.hidden > 8192) return "a draft head needs hidden <= 8192";
   return "";
 }
 
@@ -281,6 +288,11 @@ Layout make_layout(const slice_config& c) {
   if (c.has_embed || (c.has_head && c.tied_head)) L.embed = mat(c.vocab, H);
   if (c.has_head && !c.tied_head) L.head = mat(c.vocab, H);
   L.out_norm = vec(H);
+  if (c.has_mtp) {
+    L.mtp_fc = mat(H, 2 * (int64_t)H);
+    L.mtp_ne = vec(H);
+    L.mtp_nh = vec(H);
+  }
   L.wbytes = w;
 
   // workspace
@@ -334,6 +346,7 @@ Layout make_layout(const slice_config& c) {
     upd(ll.f2, ll.pf2, &ll.qf2, "F2");
   }
   if (c.has_head) upd(c.tied_head ? L.embed : L.head, L.phead, nullptr, "HEAD");
+  if (c.has_mtp) upd(L.mtp_fc, L.pmtp, nullptr, "F2");
   L.part = take(part_floats * 4);
   L.cnt = take((size_t)std::max<int64_t>(rg_max, 1) * 4);
   if (!L.layers.empty()) {
@@ -356,6 +369,11 @@ Layout make_layout(const slice_config& c) {
     L.nchunk = (c.max_seq + ATT_CHUNK - 1) / ATT_CHUNK;
     L.apart = take((size_t)mt * c.q_heads * L.nchunk * (c.head_dim + 2) * 4);
     L.rope = take((size_t)c.max_seq * (c.rope_dims / 2 > 0 ? c.rope_dims / 2 : 1) * 8);
+  }
+  if (c.has_mtp) {
+    L.xe_d = take((size_t)XW * 4 * (2 * H / QK));
+    L.xe_s = take((size_t)4 * (2 * H / QK));
+    L.mtp_y = take((size_t)H * 4);
   }
   if (c.has_head) {
     L.logits = take((size_t)c.vocab * 4);
@@ -821,6 +839,10 @@ std::string tensor_shape(const slice_config& c, int layer, int tid, int64_t& row
     return mat(c.vocab, H);
   }
   if (tid == SLICE_T_OUT_NORM) return vec(H);
+  if (tid == SLICE_T_MTP_FC || tid == SLICE_T_MTP_NORM_E || tid == SLICE_T_MTP_NORM_H) {
+    if (!c.has_mtp) return "slice is not a draft head";
+    return tid == SLICE_T_MTP_FC ? mat(H, 2 * (int64_t)H) : vec(H);
+  }
   if (layer < c.layer_begin || layer >= c.layer_end) return "layer outside the slice";
   const bool attn = c.attn_period == 0 || (layer % c.attn_period) == c.attn_period - 1;
   switch (tid) {
@@ -1232,6 +1254,9 @@ int slice_set_tensor(slice_t* s, int layer, int tid, const void* src, size_t src
     return repack(L.head, c.vocab, c.hidden, 0, 0);
   }
   if (tid == SLICE_T_OUT_NORM) return copyv(L.out_norm, c.hidden);
+  if (tid == SLICE_T_MTP_FC) return repack(L.mtp_fc, c.hidden, 2 * (int64_t)c.hidden, 0, 0);
+  if (tid == SLICE_T_MTP_NORM_E) return copyv(L.mtp_ne, c.hidden);
+  if (tid == SLICE_T_MTP_NORM_H) return copyv(L.mtp_nh, c.hidden);
   if (layer < c.layer_begin || layer >= c.layer_end) return fail(SLICE_ERANGE, "slice_set_tensor: layer outside the slice");
   const LayerLayout& ll = L.layers[layer - c.layer_begin];
   const int H = c.hidden;
@@ -1409,6 +1434,28 @@ int slice_head_argmax(slice_t* s, const void* in, int32_t* tok, float* logits, v
   const Plan pl = L.phead;
   HIPCHK(launch_gemv(W, 1, s->act_a(1), s->norm_h(), o, pl.ks, pl.w, st));
   HIPCHK(launch_argmax(lg, c.vocab, s->wsp<float>(L.amax_v), s->wsp<int>(L.amax_i), L.amax_parts, tok, st));
+  return SLICE_OK;
+}
+
+int slice_mtp_input(slice_t* s, const int32_t* tok, const void* in, void* out, void* stream) {
+  if (!s || !tok || !in || !out) return fail(SLICE_EINVAL, "slice_mtp_input: null argument");
+  const slice_config& c = s->cfg;
+  const Layout& L = s->L;
+  if (!c.has_mtp || !L.mtp_fc.present) return fail(SLICE_EINVAL, "slice_mtp_input: slice is not a draft head");
+  const hipStream_t st = S(stream);
+  const int H = c.hidden;
+  const Act x{s->wsp<int32_t>(L.xe_d), s->wsp<float>(L.xe_s), 2 * H / QK, nullptr, 0};
+  HIPCHK(launch_mtp_input(s->packed(L.embed), tok, in, c.io_fp32,
+                          reinterpret_cast<const float*>(s->w + L.mtp_ne),
+                          reinterpret_cast<const float*>(s->w + L.mtp_nh), c.eps, x, st));
+  GemvOut o{};
+  o.kind = EPI_STORE;
+  o.y = c.io_fp32 ? static_cast<float*>(out) : s->wsp<float>(L.mtp_y);
+  o.y_tstride = H;
+  o.part = s->wsp<float>(L.part);
+  o.cnt = s->wsp<unsigned>(L.cnt);
+  HIPCHK(launch_gemv(s->packed(L.mtp_fc), 1, x, NormIn{nullptr, 0, 0.0f, 0.0f}, o, L.pmtp.ks, L.pmtp.w, st));
+  if (!c.io_fp32) HIPCHK(launch_store_out(s->wsp<float>(L.mtp_y), 1, H, out, 0, s->ctrl(), 0, st));
   return SLICE_OK;
 }
 

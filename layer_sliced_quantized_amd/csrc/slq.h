@@ -146,6 +146,9 @@ hipError_t launch_fill_zero_u32(uint32_t* p, size_t n, hipStream_t s);
 hipError_t launch_read_probe(const void* p, size_t n16, uint32_t* sink, unsigned grid, hipStream_t s);
 hipError_t launch_ctrl_set(Ctrl* c, int pos, int cur, hipStream_t s);
 hipError_t launch_embed(const Packed& E, const int32_t* tok, void* out, int fp32, hipStream_t s);
+// digits of [RMSNorm(E[*tok]) w_e ; RMSNorm(hin) w_h] (x: 2 H / 32 blocks, one token)
+hipError_t launch_mtp_input(const Packed& E, const int32_t* tok, const void* hin, int fp32, const float* w_e,
+                            const float* w_h, float eps, Act x, hipStream_t s);
 hipError_t launch_argmax(const float* logits, int n, float* part_v, int* part_i, int nparts,
                          int32_t* tok, hipStream_t s);
 

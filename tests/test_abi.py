@@ -104,6 +104,33 @@ def test_q35_tensor_shapes_and_validation():
             slq.tensor_info(slq.make_config(dataclasses.replace(sh, **bad), synth.Q4_0, 0, 4), 0, "dn_q")
 
 
+def test_draft_head_tensor_shapes_and_validation():
+    """The draft head's tensors (host only): the 2H-wide input projection and
+    the two input norms; a draft head needs the embedding; a plain slice
+    holds none of them."""
+    import dataclasses
+    import layer_sliced_quantized_amd as slq
+    import synth
+    base = dataclasses.replace(synth.HYBRID_5120, vocab=2048)
+    sh = synth.mtp_shape(base)
+    cfg = slq.make_config(sh, synth.Q4_0, 0, 1, max_seq=1024, max_verify=1, has_embed=True, has_head=True,
+                          has_mtp=True)
+    fc = slq.tensor_info(cfg, 0, "mtp_fc")
+    assert (fc["rows"], fc["cols"], fc["kind"]) == (5120, 10240, synth.Q4_0)
+    assert fc["src_bytes"] == 5120 * 10240 // 32 * 18
+    for n in ("mtp_norm_e", "mtp_norm_h"):
+        assert slq.tensor_info(cfg, 0, n) == {"rows": 5120, "cols": 1, "kind": 0, "src_bytes": 4 * 5120}
+    assert slq.tensor_info(cfg, 0, "wq")["rows"] == sh.q_heads * sh.head_dim     # its layer is attention
+    with pytest.raises(slq.SliceError):   # no embedding
+        slq.tensor_info(slq.make_config(sh, synth.Q4_0, 0, 1, has_head=True, has_mtp=True), 0, "mtp_fc")
+    with pytest.raises(slq.SliceError):   # not a draft head
+        slq.tensor_info(slq.make_config(sh, synth.Q4_0, 0, 1, has_embed=True), 0, "mtp_fc")
+    # the weights buffer holds the projection and the norms on top of a plain slice's tensors
+    plain = slq.make_config(sh, synth.Q4_0, 0, 1, max_seq=1024, max_verify=1, has_embed=True, has_head=True)
+    extra = slq.lib().slice_weights_bytes(ctypes.byref(cfg)) - slq.lib().slice_weights_bytes(ctypes.byref(plain))
+    assert fc["src_bytes"] <= extra <= fc["src_bytes"] + 2 * 4 * 5120 + 3 * 256
+
+
 def test_build_refuses_scratch_in_kernels_with_counted_waits():
     """The build parses the compiler's resource-usage remarks and names every
     batched-product kernel that uses scratch (host logic only)."""
