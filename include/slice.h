@@ -242,6 +242,10 @@ typedef struct slice_config {
      * (attn_period 0, layer range [0, 1)), OUT_NORM is the head's own final
      * norm and the head matrix the model's LM head.                       */
     int32_t has_mtp;
+    /* Tokens a slice_prefill pass may carry: 0 = max_verify; up to 64 (more
+     * than 16 needs dn_variant 0).  The activation buffers are sized for
+     * max(max_verify, max_prefill) tokens.                                   */
+    int32_t max_prefill;
 } slice_config;
 
 /* Tensor ids for slice_set_tensor.  Matrices take raw GGUF blocks
@@ -377,15 +381,19 @@ int slice_run_gemv_op(slice_t *s, int op_kind, void *stream);
  * own slot.  Must be followed by slice_commit before the next decode/verify.  */
 int slice_verify(slice_t *s, int k, const void *hid_in_dev, void *hid_out_dev, void *stream);
 
-/* Prompt ingestion of k inputs (1..max_verify) at positions p .. p+k-1:
+/* Prompt ingestion of k inputs (1..max(max_verify, max_prefill), at most 64)
+ * at positions p .. p+k-1 (the pages batch 16 prompt tokens per round trip,
+ * SwarmLLM README, feature list; a stage can take more at once):
  * hid_in_dev [k][H] -> hid_out_dev [k][H] (caller-owned device buffers in the
  * boundary format), then p <- p + k (no commit).  The result is that of k
  * slice_decode calls up to floating-point rounding, not bit for bit: the
- * DeltaNet layers take all k tokens at once in the chunked form of the
- * recurrence and keep only the final state (the pages name the serial
+ * DeltaNet layers take the tokens in the chunked form of the recurrence, 16
+ * at a time, and keep only the final state (the pages name the serial
  * recurrence as what makes prefill slow; SwarmLLM README, bench paragraph),
  * and the products use launch shapes of their own, so their sums run in
- * another order.  For a bit-exact pass use slice_verify + slice_commit(k).
+ * another order.  Past 16 tokens every product still reads its weights once
+ * for all k tokens; the mixers run in sub-passes of 16 tokens, in order.  For
+ * a bit-exact pass use slice_verify + slice_commit(k) (k <= 16).
  * Errors: SLICE_EINVAL for a null argument, SLICE_ESTATE while a verify is
  * pending, SLICE_ERANGE for k or positions out of range; nothing is enqueued
  * then.  */

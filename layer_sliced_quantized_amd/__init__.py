@@ -186,7 +186,7 @@ class AttnDecoder:
 
 def make_config(shape, qtype: int, begin: int, end: int, *, max_seq: int = 1024, max_verify: int = 16,
                 io_fp32: bool = False, has_embed: bool = False, has_head: bool = False,
-                has_mtp: bool = False) -> SliceConfig:
+                has_mtp: bool = False, max_prefill: int = 0) -> SliceConfig:
     """Build a slice_config from any object with the model-shape attributes."""
     c = SliceConfig()
     c.hidden = shape.hidden
@@ -213,6 +213,7 @@ def make_config(shape, qtype: int, begin: int, end: int, *, max_seq: int = 1024,
     c.dn_k_heads = int(getattr(shape, "dn_k_heads", 0))
     c.dn_conv = int(getattr(shape, "dn_conv", 0))
     c.has_mtp = int(has_mtp)
+    c.max_prefill = int(max_prefill)
     return c
 
 

@@ -46,7 +46,7 @@ class SliceConfig(ctypes.Structure):
         ("max_seq", ctypes.c_int32), ("max_verify", ctypes.c_int32),
         ("qtype", ctypes.c_int32), ("io_fp32", ctypes.c_int32),
         ("dn_variant", ctypes.c_int32), ("dn_k_heads", ctypes.c_int32), ("dn_conv", ctypes.c_int32),
-        ("has_mtp", ctypes.c_int32),
+        ("has_mtp", ctypes.c_int32), ("max_prefill", ctypes.c_int32),
     ]
 
 

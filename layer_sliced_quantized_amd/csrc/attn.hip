@@ -154,7 +154,7 @@ __global__ __launch_bounds__(256) void k_attn_split_range(AttnParams p, int T, i
   const int g = pair / nrange, rng = pair % nrange;
   const int cb = rng * cpw;
   const int h0 = (g * nsub + sub) * GRP;            // first query head of this workgroup
-  const int p0 = p.ctrl ? p.ctrl->pos : p.pos;
+  const int p0 = (p.ctrl ? p.ctrl->pos : p.pos) + p.pos_off;
   if (cb * C > p0 + T - 1) return;
   const int ce = min(min(cb + cpw, p.nchunk), (p0 + T - 1) / C + 1);   // chunks [cb, ce) hold visible rows
   const int tid = threadIdx.x;
@@ -403,7 +403,7 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   if (pair >= p.kv_heads * p.nchunk) return;
   const int g = pair / p.nchunk, c = pair % p.nchunk;
   const int h0 = (g * nsub + sub) * GRP;            // first query head of this workgroup
-  const int p0 = p.ctrl ? p.ctrl->pos : p.pos;
+  const int p0 = (p.ctrl ? p.ctrl->pos : p.pos) + p.pos_off;
   const int r0 = c * C;
   if (r0 > p0 + T - 1) return;
   const int tid = threadIdx.x;
@@ -602,7 +602,7 @@ __global__ __launch_bounds__(64 * CW) void k_attn_combine(AttnParams p) {
   const int d = (blockIdx.x % ndg) * 64 + lane;
   // the gate input does not depend on the position: request it first
   const float gz = p.off_g >= 0 && w == 0 ? p.y[(size_t)t * p.y_stride + p.off_g + h * p.hd + d] : 0.0f;
-  const int P = (p.ctrl ? p.ctrl->pos : p.pos) + t;
+  const int P = (p.ctrl ? p.ctrl->pos : p.pos) + p.pos_off + t;
   const int nc = P / ATT_CHUNK / p.rchunks + 1;   // partials that token t reaches
   const int stride = p.hd + 2;
   const float* base = p.part + ((size_t)t * p.q_heads + h) * p.nchunk * stride;

@@ -179,10 +179,13 @@ __device__ __forceinline__ void quant_block_half(float v, int32_t* xd, float* xs
 
 // MFMA layout (see Act): the same x_int and scale as the lane-row layout.
 template <int QT>
-__device__ __forceinline__ void quant_block_mx(float v, const Act& a, int t, int blk, bool write) {
+__device__ __forceinline__ void quant_block_mx(float v, const Act& a, int tok, int blk, bool write) {
   const int lane = threadIdx.x & 63;
   const int e = lane & 31;
   const int base = lane & 32;
+  // token group tok / 16 has a record of its own per block; t is the slot in it
+  int32_t* rec = a.mxd + ((size_t)(tok / MX_SLOTS) * a.nblk + blk) * (mx_block_bytes(QT) / 4);
+  const int t = tok % MX_SLOTS;
   float sc;
   const uint32_t u = quant_int<QT>(v, sc);
   if (QT == QT_Q4) {
@@ -201,7 +204,7 @@ __device__ __forceinline__ void quant_block_mx(float v, const Act& a, int t, int
         if (g >= 2) dig *= 16;
         word |= ((uint32_t)dig & 255u) << (8 * k);
       }
-      if (write && w < 48) a.mxd[(size_t)blk * (mx_block_bytes(QT) / 4) + (c * MX_SLOTS + t) * 4 + q] = (int32_t)word;
+      if (write && w < 48) rec[(c * MX_SLOTS + t) * 4 + q] = (int32_t)word;
     }
   } else {
     // 24 dwords: w = e < 24, chunk c = w >> 2 (p = c >> 1, h = c & 1), dword q = w & 3
@@ -213,10 +216,9 @@ __device__ __forceinline__ void quant_block_mx(float v, const Act& a, int t, int
       const uint32_t uk = (uint32_t)__shfl((int)u, base + 16 * h + 4 * q + k, 64);
       word |= (((uk >> (8 * p)) & 255u) ^ 0x80u) << (8 * k);
     }
-    if (write && e < 24) a.mxd[(size_t)blk * (mx_block_bytes(QT) / 4) + (c * MX_SLOTS + t) * 4 + q] = (int32_t)word;
+    if (write && e < 24) rec[(c * MX_SLOTS + t) * 4 + q] = (int32_t)word;
   }
-  if (write && e == 0)
-    reinterpret_cast<float*>(a.mxd + (size_t)blk * (mx_block_bytes(QT) / 4) + mx_scale_off(QT) / 4)[t] = sc;
+  if (write && e == 0) reinterpret_cast<float*>(rec + mx_scale_off(QT) / 4)[t] = sc;
 }
 
 // Digits of block blk of token t of `a`, in the lane-row layout and, when a

@@ -89,9 +89,11 @@ __host__ __device__ constexpr int gemm_region(int qt, int T) {
 }
 constexpr int GEMM_LDS_MAX = 160 * 1024;
 // at most 8 waves (256 registers each: the explicit wait counts rely on the
-// kernel never spilling to scratch) and the LDS of every wave's ring
+// kernel never spilling to scratch), a whole number of waves per token group,
+// and the LDS of every wave's ring
 __host__ __device__ constexpr bool gemm_fits(int qt, int T, int waves) {
-  return T >= 1 && T <= MX_SLOTS && waves <= 8 && waves * gemm_region(qt, T) <= GEMM_LDS_MAX;
+  return T >= 1 && T <= MAX_PASS && waves <= 8 && waves % gemm_groups(T) == 0 &&
+         waves * gemm_region(qt, T) <= GEMM_LDS_MAX;
 }
 
 // s_waitcnt immediate on gfx9: wait until at most n vector-memory operations
@@ -105,8 +107,9 @@ __host__ __device__ constexpr unsigned vmcnt_imm(int n) {
 // the compiler's wait tracking takes a global->LDS load as touching two
 // address spaces and then turns every later register wait into a full drain,
 // while buffer loads keep the ordinary in-order counting.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const Act& x, int qt) {
-  return __builtin_amdgcn_make_buffer_rsrc(x.mxd, 0, x.nblk * mx_block_bytes(qt), 0x00020000);
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t mx_rsrc(const Act& x, int qt, int grp = 0) {
+  return __builtin_amdgcn_make_buffer_rsrc(x.mxd + (size_t)grp * x.nblk * (mx_block_bytes(qt) / 4), 0,
+                                           x.nblk * mx_block_bytes(qt), 0x00020000);
 }
 
 // 16 bytes per lane from byte off + 16-byte-piece voff of the buffer straight
@@ -561,7 +564,11 @@ __global__ __launch_bounds__(512) void k_gemm_diag(Packed W, Act x, NormIn nin, 
   if (threadIdx.x == 0) __hip_atomic_store(out.cnt + rg, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-template <int QT, int EPI>
+// NGR token groups (prompt passes of 17..64 tokens): wave w multiplies group
+// w % NGR over K part w / NGR of the split, so the waves of one K part read
+// the same weight tiles (from HBM once, the repeats from L2); tokens of group
+// g are summed over the K parts in order.  NGR = 1 is the 9..16-token form.
+template <int QT, int EPI, int NGR>
 __global__ __launch_bounds__(512) void k_gemm_dense(Packed W, Act x, NormIn nin, GemvOut out, int ksplit, int T) {
   constexpr int TBY = tile_bytes(QT);
   constexpr int TP = DENSE_TP;
@@ -570,11 +577,12 @@ __global__ __launch_bounds__(512) void k_gemm_dense(Packed W, Act x, NormIn nin,
   const int lane = threadIdx.x & 63;
   const int wave = wave_id();
   const int nw = blockDim.x >> 6;
+  const int grp = wave % NGR, kw = wave / NGR, nkw = nw / NGR;
   const int rg = blockIdx.x / ksplit, ks = blockIdx.x % ksplit;
   const int nblk = W.nblk(), ntiles = W.ntiles(), full = nblk / TB;
   const int w0 = ntiles * ks / ksplit, w1 = ntiles * (ks + 1) / ksplit;
-  const int t0 = __builtin_amdgcn_readfirstlane(w0 + (w1 - w0) * wave / nw);
-  const int t1 = __builtin_amdgcn_readfirstlane(w0 + (w1 - w0) * (wave + 1) / nw);
+  const int t0 = __builtin_amdgcn_readfirstlane(w0 + (w1 - w0) * kw / nkw);
+  const int t1 = __builtin_amdgcn_readfirstlane(w0 + (w1 - w0) * (kw + 1) / nkw);
   const uint8_t* base = W.w + (size_t)rg * rg_bytes(QT, W.cols);
   uint8_t* ring = lds + (size_t)wave * REGION;
   auto nb_of = [&](int t) { return t < full ? TB : nblk - full * TB; };
@@ -586,7 +594,7 @@ __global__ __launch_bounds__(512) void k_gemm_dense(Packed W, Act x, NormIn nin,
 #pragma unroll
     for (int i = 0; i < 4; ++i) acc[r][i] = 0.0f;
 
-  const __amdgpu_buffer_rsrc_t rs = mx_rsrc(x, QT);
+  const __amdgpu_buffer_rsrc_t rs = mx_rsrc(x, QT, grp);
   TileRegs<QT> R;
   if (t0 < t1) {
     // prologue: the records of tile t0's first DENSE_RING blocks into the
@@ -642,10 +650,12 @@ __global__ __launch_bounds__(512) void k_gemm_dense(Packed W, Act x, NormIn nin,
       *reinterpret_cast<float4*>(red + 16 * r) = float4{acc[r][0], acc[r][1], acc[r][2], acc[r][3]};
   }
   __syncthreads();
-  // token j of this wave: sum of the waves' values in wave order
+  // token j: slot j % 16 of the waves of group j / 16, added in K-part order
   auto wave_sum_of = [&](int j) {
-    float a = reinterpret_cast<const float*>(lds)[(size_t)j * RG + lane];
-    for (int w = 1; w < nw; ++w) a += reinterpret_cast<const float*>(lds + (size_t)w * REGION)[(size_t)j * RG + lane];
+    const int g = j / MX_SLOTS, sl = j % MX_SLOTS;
+    float a = reinterpret_cast<const float*>(lds + (size_t)g * REGION)[(size_t)sl * RG + lane];
+    for (int k = 1; k < nkw; ++k)
+      a += reinterpret_cast<const float*>(lds + (size_t)(k * NGR + g) * REGION)[(size_t)sl * RG + lane];
     return a;
   };
   auto pre_of = [&](int q, int j) {
@@ -698,7 +708,9 @@ hipError_t gemm_inst(const Packed& W, int T, Act x, NormIn nin, GemvOut out, int
   const size_t lds = (size_t)waves * gemm_region(QT, T);
   if (T <= 4) k_gemm_diag<QT, EPI, 1><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T);
   else if (T <= 8) k_gemm_diag<QT, EPI, 2><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T);
-  else k_gemm_dense<QT, EPI><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T);
+  else if (T <= MX_SLOTS) k_gemm_dense<QT, EPI, 1><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T);
+  else if (gemm_groups(T) == 2) k_gemm_dense<QT, EPI, 2><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T);
+  else k_gemm_dense<QT, EPI, 4><<<grid, block, lds, s>>>(W, x, nin, out, ksplit, T);
   return hipGetLastError();
 }
 

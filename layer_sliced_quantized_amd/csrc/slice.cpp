@@ -129,6 +129,20 @@ Plan plan_pass(const char* kind, int64_t rows, int64_t cols) {
   return p;
 }
 
+// Launch shape of the products of prompt passes of 17..64 tokens (token
+// groups of 16, each group its own waves): four waves per workgroup (one K
+// part of four groups, or two of two) and splits for about 1024 workgroups,
+// at most one per tile.  Overrides KS_<kind>W.
+Plan plan_wide(const char* kind, int64_t rows, int64_t cols) {
+  const int nrg = (int)((rows + RG - 1) / RG);
+  const int ntiles = (int)((cols / QK + TB - 1) / TB);
+  Plan p;
+  p.w = 4;
+  p.ks = clampi((1024 + nrg / 2) / nrg, 1, std::min(16, std::max(1, ntiles)));
+  p.ks = clampi(override_int(std::string("KS_") + kind + "W", p.ks), 1, 16);
+  return p;
+}
+
 struct Mat {
   size_t off = 0;      // into the weights buffer
   int64_t rows = 0, cols = 0;
@@ -140,6 +154,7 @@ struct LayerLayout {
   Mat g1, g2, f1, f2;
   Plan pg1{1, 1}, pg2{1, 1}, pf1{1, 1}, pf2{1, 1};   // GEMV splits, fixed at load
   Plan qg1{1, 1}, qg2{1, 1}, qf1{1, 1}, qf2{1, 1};   // the same for prompt passes
+  Plan wg1{1, 1}, wg2{1, 1}, wf1{1, 1}, wf2{1, 1};   // ... of more than 16 tokens
   size_t attn_norm = 0, ffn_norm = 0, q_norm = 0, k_norm = 0;
   // row offsets inside g1
   int off_q = 0, off_k = 0, off_v = 0, off_a = 0, off_b = 0, off_z = 0, off_g = -1;
@@ -182,6 +197,7 @@ std::string validate(const slice_config& c) {
   if (c.layer_begin < 0 || c.layer_end < c.layer_begin || c.layer_end > c.n_layers) return "bad layer range";
   if (c.attn_period < 0) return "attn_period must be >= 0";
   if (c.max_verify < 1 || c.max_verify > MAX_T) return "max_verify must be in 1..16";
+  if (c.max_prefill < 0 || c.max_prefill > MAX_PASS) return "max_prefill must be in 0..64";
   if (c.ffn < 0 || c.ffn % 32) return "ffn must be a multiple of 32";
   if (!(c.eps >= 0)) return "eps must be >= 0";
   bool any_attn = false, any_dn = false;
@@ -210,6 +226,8 @@ std::string validate(const slice_config& c) {
   }
   if ((c.has_embed || c.has_head) && c.vocab <= 0) return "vocab must be > 0 with an embedding or head";
   if (c.has_mtp != 0 && c.has_mtp != 1) return "has_mtp must be 0 or 1";
+  if (c.max_prefill > MAX_T && c.dn_variant && any_dn)
+    return "prompt passes of more than 16 tokens need the chunked DeltaNet (dn_variant 0)";
   if (c.has_mtp && !c.has_embed) return "a draft head (has_mtp) needs has_embed";
   if (c.has_mtp && c.hidden > 8192) return "a draft head needs hidden <= 8192";
   return "";
@@ -238,7 +256,7 @@ Layout make_layout(const slice_config& c) {
     w = al256(w + (size_t)n * 4);
     return o;
   };
-  L.mt = c.max_verify;
+  L.mt = std::max(c.max_verify, c.max_prefill);   // tokens a step may carry
   L.nslots = c.max_verify + 1;
   const int nkd = dn_kh(c) * c.dn_dk, nvd = c.dn_heads * c.dn_dv;
   const int nq = c.q_heads * c.head_dim, nkv = c.kv_heads * c.head_dim;
@@ -312,7 +330,9 @@ Layout make_layout(const slice_config& c) {
   // MFMA layout for steps of several tokens
   auto digits = [&](int nblk) { return (size_t)mt * XW * 4 * (nblk ? nblk : 1); };
   auto scales = [&](int nblk) { return (size_t)mt * (nblk ? nblk : 1) * 4; };
-  auto mdigits = [&](int nblk) { return mt > 1 ? (size_t)mx_block_bytes(c.qtype) * (nblk ? nblk : 1) : 0; };
+  auto mdigits = [&](int nblk) {
+    return mt > 1 ? (size_t)mx_block_bytes(c.qtype) * (nblk ? nblk : 1) * gemm_groups(mt) : 0;
+  };
   L.xa_d = take(digits(nblkH));
   L.xa_s = take(scales(nblkH));
   L.xu_d = take(digits(nblkU));
@@ -339,11 +359,20 @@ Layout make_layout(const slice_config& c) {
       part_floats = std::max<size_t>(part_floats, (size_t)nrg * q->ks * mt * RG);
     }
   };
+  auto updw = [&](const Mat& m, Plan& p, const char* kind) {
+    if (!m.present || mt <= MAX_T) return;
+    p = plan_wide(kind, m.rows, m.cols);
+    part_floats = std::max<size_t>(part_floats, (size_t)((m.rows + RG - 1) / RG) * p.ks * mt * RG);
+  };
   for (LayerLayout& ll : L.layers) {
     upd(ll.g1, ll.pg1, &ll.qg1, "G1");
     upd(ll.g2, ll.pg2, &ll.qg2, "G2");
     upd(ll.f1, ll.pf1, &ll.qf1, "F1");
     upd(ll.f2, ll.pf2, &ll.qf2, "F2");
+    updw(ll.g1, ll.wg1, "G1");
+    updw(ll.g2, ll.wg2, "G2");
+    updw(ll.f1, ll.wf1, "F1");
+    updw(ll.f2, ll.wf2, "F2");
   }
   if (c.has_head) upd(c.tied_head ? L.embed : L.head, L.phead, nullptr, "HEAD");
   if (c.has_mtp) upd(L.mtp_fc, L.pmtp, nullptr, "F2");
@@ -367,7 +396,7 @@ Layout make_layout(const slice_config& c) {
   }
   if (L.n_attn) {
     L.nchunk = (c.max_seq + ATT_CHUNK - 1) / ATT_CHUNK;
-    L.apart = take((size_t)mt * c.q_heads * L.nchunk * (c.head_dim + 2) * 4);
+    L.apart = take((size_t)std::min(mt, MAX_T) * c.q_heads * L.nchunk * (c.head_dim + 2) * 4);
     L.rope = take((size_t)c.max_seq * (c.rope_dims / 2 > 0 ? c.rope_dims / 2 : 1) * 8);
   }
   if (c.has_mtp) {
@@ -497,11 +526,22 @@ static DnParams dn_params(slice* s, int i, int T, int mode) {
   return p;
 }
 
-static int enqueue_mixer(slice* s, int i, int T, int mode, hipStream_t st) {
+// The same activations seen from token t0 on (t0 a multiple of 16: token
+// group t0 / 16 starts a record of its own in the MFMA layout).
+static Act act_from(const Act& a, int t0, int qt) {
+  Act r = a;
+  r.xd += (size_t)t0 * a.nblk * XW;
+  r.xs += (size_t)t0 * a.nblk;
+  if (r.mxd) r.mxd += (size_t)(t0 / MX_SLOTS) * a.nblk * (mx_block_bytes(qt) / 4);
+  return r;
+}
+
+// Layer i's mixer for tokens t0 .. t0 + T - 1 of a step of Tall tokens.
+static int enqueue_mixer_part(slice* s, int i, int Tall, int t0, int T, int mode, hipStream_t st) {
   const slice_config& c = s->cfg;
   const Layout& L = s->L;
   const LayerLayout& ll = L.layers[i];
-  float* y1 = s->wsp<float>(L.y1);
+  float* y1 = s->wsp<float>(L.y1) + (size_t)t0 * ll.g1.rows;
   if (ll.attn) {
     AttnParams p{};
     p.y = y1;
@@ -522,11 +562,29 @@ static int enqueue_mixer(slice* s, int i, int T, int mode, hipStream_t st) {
     p.part = s->wsp<float>(L.apart);
     p.nchunk = L.nchunk;
     p.u_out = nullptr;
-    p.next = s->act_u(T);
+    p.pos_off = t0;
+    p.next = act_from(s->act_u(Tall), t0, c.qtype);
     p.next_qt = c.qtype;
     HIPCHK(launch_attention(p, T, st));
   } else {
-    HIPCHK(launch_deltanet(dn_params(s, i, T, mode), T, st));
+    DnParams p = dn_params(s, i, T, mode);
+    p.y = y1;
+    p.next = act_from(s->act_u(Tall), t0, c.qtype);
+    HIPCHK(launch_deltanet(p, T, st));
+  }
+  return SLICE_OK;
+}
+
+// A prompt pass of more than 16 tokens runs each mixer in sub-passes of 16
+// (tokens t0 .. t0 + 15 at positions pos + t0 ..): attention appends and
+// attends causally in order, the chunked DeltaNet carries its state from one
+// sub-pass to the next; the products around the mixers take all tokens at once.
+static int enqueue_mixer(slice* s, int i, int T, int mode, hipStream_t st) {
+  if (T <= MAX_T) return enqueue_mixer_part(s, i, T, 0, T, mode, st);
+  if (mode != DN_CHUNK) return fail(SLICE_EINVAL, "more than 16 tokens only in a prompt pass");
+  for (int t0 = 0; t0 < T; t0 += MAX_T) {
+    int rc = enqueue_mixer_part(s, i, T, t0, std::min(MAX_T, T - t0), mode, st);
+    if (rc) return rc;
   }
   return SLICE_OK;
 }
@@ -607,7 +665,7 @@ static int enqueue_step(slice* s, int T, int mode, hipStream_t st, Prof* prof = 
       const Packed W = s->packed(ll.g1);
       GemvOut o = g1_out();
       o.y_tstride = W.rows;
-      const Plan pl = pass ? ll.qg1 : ll.pg1;
+      const Plan pl = pass ? (T > MAX_T ? ll.wg1 : ll.qg1) : ll.pg1;
       HIPCHK(launch_gemv(W, T, s->act_a(T), s->norm_h(), o, pl.ks, pl.w, st));
       SLQ_MARK(k_in);
     }
@@ -633,7 +691,9 @@ static int enqueue_step(slice* s, int T, int mode, hipStream_t st, Prof* prof = 
       HIPCHK(launch_gemv(W, T, in, NormIn{nullptr, 0, 0.f, 0.f}, o, pl.ks, pl.w, st));
       return SLICE_OK;
     };
-    int rc = (only < 0 || only == k_out) ? residual(ll.g2, s->act_u(T), nw_after_mixer, pass ? ll.qg2 : ll.pg2) : SLICE_OK;
+    int rc = (only < 0 || only == k_out)
+                 ? residual(ll.g2, s->act_u(T), nw_after_mixer, pass ? (T > MAX_T ? ll.wg2 : ll.qg2) : ll.pg2)
+                 : SLICE_OK;
     if (rc) return rc;
     SLQ_MARK(k_out);
     if (c.ffn && (only < 0 || only == SLICE_OP_FFN_IN)) {
@@ -646,12 +706,12 @@ static int enqueue_step(slice* s, int T, int mode, hipStream_t st, Prof* prof = 
       o.next_qt = qt;
       o.part = part;
       o.cnt = cnt;
-      const Plan pl = pass ? ll.qf1 : ll.pf1;
+      const Plan pl = pass ? (T > MAX_T ? ll.wf1 : ll.qf1) : ll.pf1;
       HIPCHK(launch_gemv(W, T, s->act_a(T), s->norm_h(), o, pl.ks, pl.w, st));
       SLQ_MARK(SLICE_OP_FFN_IN);
     }
     if (c.ffn && (only < 0 || only == SLICE_OP_FFN_OUT)) {
-      rc = residual(ll.f2, s->act_m(T), attn_norm_off(s, i + 1), pass ? ll.qf2 : ll.pf2);
+      rc = residual(ll.f2, s->act_m(T), attn_norm_off(s, i + 1), pass ? (T > MAX_T ? ll.wf2 : ll.qf2) : ll.pf2);
       if (rc) return rc;
       SLQ_MARK(SLICE_OP_FFN_OUT);
     }
@@ -1377,7 +1437,8 @@ int slice_verify(slice_t* s, int k, const void* in, void* out, void* stream) {
 int slice_prefill(slice_t* s, int k, const void* in, void* out, void* stream) {
   if (!s || !in || !out) return fail(SLICE_EINVAL, "slice_prefill: null argument");
   if (s->pending) return fail(SLICE_ESTATE, "slice_prefill: a verify is waiting for slice_commit");
-  if (k < 1 || k > s->cfg.max_verify) return fail(SLICE_ERANGE, "slice_prefill: k outside 1..max_verify");
+  if (k < 1 || k > s->L.mt)
+    return fail(SLICE_ERANGE, "slice_prefill: k outside 1..max(max_verify, max_prefill)");
   if (s->L.n_attn && s->pos + k > s->cfg.max_seq) return fail(SLICE_ERANGE, "slice_prefill: positions pass max_seq");
   if (s->cfg.dn_variant && s->L.n_dn) {
     // the qwen3_5 form has no chunked update: a verify pass whose k tokens are all kept
@@ -1555,7 +1616,7 @@ static int kv_io(slice_t* s, int layer, uint16_t* k, uint16_t* v, int rows, int 
 
 int slice_dbg_get_hidden(slice_t* s, float* dst, int k, void* stream) {
   if (!s || !dst) return fail(SLICE_EINVAL, "null argument");
-  if (k < 1 || k > s->L.mt) return fail(SLICE_ERANGE, "k outside 1..max_verify");
+  if (k < 1 || k > s->L.mt) return fail(SLICE_ERANGE, "k outside 1..max(max_verify, max_prefill)");
   HIPCHK(hipMemcpyAsync(dst, s->ws + s->L.h, (size_t)k * s->cfg.hidden * 4, hipMemcpyDeviceToDevice, S(stream)));
   return SLICE_OK;
 }

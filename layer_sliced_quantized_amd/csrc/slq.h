@@ -11,7 +11,8 @@ constexpr int QK = 32;          // weights per block
 constexpr int TB = 8;           // blocks per tile along K
 constexpr int RG = 64;          // rows per row group: one row per lane of a wave64
 constexpr int XW = 24;          // digit dwords per activation block (both formats)
-constexpr int MAX_T = 16;       // tokens per batched pass
+constexpr int MAX_T = 16;       // tokens per batched pass (verify, the mixers' kernels)
+constexpr int MAX_PASS = 64;    // tokens per prompt pass (products in token groups of 16)
 constexpr int QT_Q4 = 2;
 constexpr int QT_Q8 = 8;
 
@@ -61,11 +62,17 @@ struct Act {
   int32_t* xd;
   float* xs;
   int nblk;      // blocks per token
-  int32_t* mxd;  // MFMA layout records, or nullptr (not written)
+  int32_t* mxd;  // MFMA layout records, or nullptr (not written); tokens 16 g .. 16 g + 15
+                 // of block b in the record at mxd + (g nblk + b) mx_block_bytes / 4
   int min_t;     // calls with at least this many tokens use the MFMA products (when they
                  // fit); 0: the measured default, gemm_min_tokens
 };
 constexpr int MX_SLOTS = 16;
+// Token groups of 16 a batched product multiplies at once: past 16 tokens
+// (prompt passes) the dense form gives each of 2 or 4 groups its own waves (a
+// group past the last token multiplies whatever its records hold and is never
+// read), so the records of every such group must exist.
+__host__ __device__ constexpr int gemm_groups(int T) { return T <= MX_SLOTS ? 1 : T <= 2 * MX_SLOTS ? 2 : 4; }
 __host__ __device__ constexpr int mx_chunks(int qt) { return qt == QT_Q4 ? 12 : 6; }
 // Bytes of one block's MFMA-layout record: digits, then the token scales at
 // byte mx_scale_off(qt).
@@ -252,6 +259,7 @@ struct AttnParams {
   int max_seq;
   const Ctrl* ctrl;      // position ctrl->pos; nullptr: pos below
   int pos;
+  int pos_off;           // added to that position (token t sits at position + pos_off + t)
   float* part;           // [T][q_heads][nchunk][hd + 2]: one partial per rchunks chunks
   int nchunk;            // max_seq / chunk
   int rchunks;           // chunks per partial (set by launch_attention from the cache size)

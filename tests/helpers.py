@@ -21,7 +21,8 @@ TOL = 2e-3   # max relative error on hidden states (fp32 accumulation)
 
 
 def make_pair(shape, qtype, begin, end, *, workload, seed=0, max_seq=1024, max_verify=16, io_fp32=True,
-              prefill=0, has_embed=False, has_head=False, threads=8, with_oracle=True, centered=False):
+              prefill=0, has_embed=False, has_head=False, threads=8, with_oracle=True, centered=False,
+              max_prefill=0):
     """Build (gpu Slice, SliceOracle, tensors) with identical weights, states and KV prefix."""
     import torch
     import layer_sliced_quantized_amd as slq
@@ -31,7 +32,7 @@ def make_pair(shape, qtype, begin, end, *, workload, seed=0, max_seq=1024, max_v
                for l in range(begin, end)}
     glob = synth.global_tensors(shape, qtype, seed, workload) if (has_embed or has_head) else {}
     cfg = slq.make_config(shape, qtype, begin, end, max_seq=max_seq, max_verify=max_verify, io_fp32=io_fp32,
-                          has_embed=has_embed, has_head=has_head)
+                          has_embed=has_embed, has_head=has_head, max_prefill=max_prefill)
     s = slq.Slice(cfg)
     s.load_numpy(tensors, glob)
     orc = SliceOracle(shape, qtype, begin, end, tensors, glob, max_seq=max_seq, io_fp32=io_fp32) if with_oracle else None

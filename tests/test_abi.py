@@ -131,6 +131,27 @@ def test_draft_head_tensor_shapes_and_validation():
     assert fc["src_bytes"] <= extra <= fc["src_bytes"] + 2 * 4 * 5120 + 3 * 256
 
 
+def test_prompt_pass_width_validation():
+    """max_prefill (tokens per prompt pass) is 0..64; past 16 the DeltaNet
+    layers must be of the chunked form; the activation buffers grow with it."""
+    import dataclasses
+    import layer_sliced_quantized_amd as slq
+    import synth
+    sh = synth.HYBRID_5120
+
+    def ws(**kw):
+        cfg = slq.make_config(sh, synth.Q4_0, 0, 4, max_seq=1024, max_verify=4, **kw)
+        return slq.lib().slice_workspace_bytes(ctypes.byref(cfg))
+
+    assert ws(max_prefill=64) > ws(max_prefill=16) > ws() > 0
+    assert ws(max_prefill=65) == 0 and ws(max_prefill=-1) == 0
+    q35 = synth.HYBRID_5120_Q35
+    cfg = slq.make_config(q35, synth.Q4_0, 0, 4, max_seq=1024, max_verify=4, max_prefill=32)
+    assert slq.lib().slice_workspace_bytes(ctypes.byref(cfg)) == 0
+    cfg = slq.make_config(q35, synth.Q4_0, 3, 4, max_seq=1024, max_verify=4, max_prefill=32)   # attention only
+    assert slq.lib().slice_workspace_bytes(ctypes.byref(cfg)) > 0
+
+
 def test_build_refuses_scratch_in_kernels_with_counted_waits():
     """The build parses the compiler's resource-usage remarks and names every
     batched-product kernel that uses scratch (host logic only)."""

@@ -28,8 +28,9 @@ def _t(a):
     return torch.from_numpy(np.ascontiguousarray(a)).cuda()
 
 
-def _check_prefill(shape, qtype, k, prefill, *, workload=WL, max_seq=512, layers=4):
-    s, orc, _, _ = make_pair(shape, qtype, 0, layers, workload=workload, prefill=prefill, max_seq=max_seq)
+def _check_prefill(shape, qtype, k, prefill, *, workload=WL, max_seq=512, layers=4, max_prefill=0):
+    s, orc, _, _ = make_pair(shape, qtype, 0, layers, workload=workload, prefill=prefill, max_seq=max_seq,
+                             max_prefill=max_prefill)
     H = inputs(shape, k + 1, workload=workload)
     out = s.prefill(_t(H[:k])).cpu().numpy()
     for t in range(k):
@@ -144,3 +145,92 @@ def test_hybrid_64_layer_q4_prefill_16():
     assert s.position == 528
     s.decode(_t(H[16]))
     assert rel_err(s.get_hidden().cpu().numpy()[0], orc.decode(H[16], raw=True)) <= TOL
+
+
+# ---------------------------------------------- passes of more than 16 tokens
+
+@pytest.mark.parametrize("k", [17, 32, 33, 48, 64])
+def test_tiny_hybrid_wide_prefill(k):
+    """17..64 tokens in one pass: the products take every token at once in
+    token groups of 16 (the last group ragged), the mixers run in sub-passes
+    of 16; from position 300 the pass crosses the attention's 32-row chunks."""
+    _check_prefill(TINY_H, synth.Q4_0, k, 300, max_prefill=64)
+
+
+def test_tiny_hybrid_wide_prefill_from_empty_q8():
+    _check_prefill(TINY_H, synth.Q8_0, 40, 0, max_prefill=48)
+
+
+def test_wide_prefill_limits():
+    s, orc, _, _ = make_pair(TINY_H, synth.Q4_0, 0, 4, workload=WL, prefill=100, max_seq=256, max_verify=4,
+                             max_prefill=32)
+    H = inputs(TINY_H, 40, workload=WL)
+    with pytest.raises(slq.SliceError):
+        s.prefill(_t(H[:33]))            # more than max_prefill
+    with pytest.raises(slq.SliceError):
+        s.verify(_t(H[:5]))              # verify stays within max_verify
+    out = s.prefill(_t(H[:32])).cpu().numpy()
+    for t in range(32):
+        assert rel_err(out[t], orc.decode(H[t], raw=True)) <= TOL, t
+    # a 4-token verify and commit after the wide pass
+    Y = s.verify(_t(H[32:36])).cpu().numpy()
+    ref = orc.verify(H[32:36], raw=True)
+    for t in range(4):
+        assert rel_err(Y[t], ref[t]) <= TOL, t
+    s.commit(3)
+    orc.commit(3)
+    assert s.position == orc.pos == 135
+    assert rel_err(s.decode(_t(H[36])).cpu().numpy(), orc.decode(H[36], raw=True)) <= TOL
+
+
+def test_tiny_llama_wide_prefill():
+    sh = synth.TINY_LLAMA
+    s, orc, _, _ = make_pair(sh, synth.Q4_0, 0, 6, workload=synth.WL_TINY_LLAMA, prefill=128, max_seq=256,
+                             max_prefill=64)
+    H = inputs(sh, 41, workload=synth.WL_TINY_LLAMA)
+    out = s.prefill(_t(H[:40])).cpu().numpy()
+    for t in range(40):
+        assert rel_err(out[t], orc.decode(H[t], raw=True)) <= TOL, t
+    assert s.position == 168
+    assert rel_err(s.decode(_t(H[40])).cpu().numpy(), orc.decode(H[40], raw=True)) <= TOL
+
+
+@pytest.mark.timeout(300)
+def test_deltanet_layer_5120_prefill_64():
+    s, orc, _, _ = make_pair(DN_LAYER, synth.Q4_0, 0, 1, workload=synth.WL_DELTANET, max_seq=128, max_prefill=64)
+    H = inputs(DN_LAYER, 65, workload=synth.WL_DELTANET)
+    s.decode(_t(H[0]))
+    orc.decode(H[0], raw=True)
+    out = s.prefill(_t(H[1:])).cpu().numpy()
+    for t in range(64):
+        assert rel_err(out[t], orc.decode(H[1 + t], raw=True)) <= TOL, t
+    assert rel_err(s.get_state(0).cpu().numpy(), orc.dn[0]) <= TOL
+
+
+ATT_LAYER = dataclasses.replace(synth.HYBRID_5120, name="attention_layer_5120", ffn=0)
+FFN_DN_LAYER = dataclasses.replace(synth.HYBRID_5120, name="deltanet_ffn_layer_5120")
+
+
+@pytest.mark.timeout(300)
+def test_attention_layer_5120_prefill_64():
+    s, orc, _, _ = make_pair(ATT_LAYER, synth.Q4_0, 3, 4, workload=synth.WL_ATTENTION, prefill=512, max_seq=640,
+                             max_prefill=64)
+    H = inputs(ATT_LAYER, 64, workload=synth.WL_ATTENTION, step0=512)
+    out = s.prefill(_t(H)).cpu().numpy()
+    for t in range(64):
+        assert rel_err(out[t], orc.decode(H[t], raw=True)) <= TOL, t
+    K, V = s.get_kv(3, 576)
+    assert rel_err(K.cpu().numpy()[:, 512:], orc.kv[3][0][:, 512:576]) <= TOL
+    assert rel_err(V.cpu().numpy()[:, 512:], orc.kv[3][1][:, 512:576]) <= TOL
+
+
+@pytest.mark.timeout(300)
+def test_deltanet_and_ffn_layer_5120_prefill_48():
+    """A whole hidden-5120 layer (DeltaNet, SwiGLU 17408): every product of the
+    pass with three token groups (the fourth past the last token)."""
+    s, orc, _, _ = make_pair(FFN_DN_LAYER, synth.Q4_0, 0, 1, workload=synth.WL_DELTANET, max_seq=128,
+                             max_prefill=64, centered=True)
+    H = inputs(FFN_DN_LAYER, 48, workload=synth.WL_DELTANET)
+    out = s.prefill(_t(H)).cpu().numpy()
+    for t in range(48):
+        assert rel_err(out[t], orc.decode(H[t], raw=True)) <= TOL, t
