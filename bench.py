@@ -201,7 +201,8 @@ def build_slice(shape, qtype, max_seq, max_verify, seed, threads):
     import synth
     import layer_sliced_quantized_amd as slq
     t0 = time.time()
-    cfg = slq.make_config(shape, qtype, 0, shape.n_layers, max_seq=max_seq, max_verify=max_verify, io_fp32=False)
+    cfg = slq.make_config(shape, qtype, 0, shape.n_layers, max_seq=max_seq, max_verify=max_verify, io_fp32=False,
+                          max_prefill=64 if max_verify == 16 else 0)
     s = slq.Slice(cfg)
     tensors = {}
     for l in range(shape.n_layers):
@@ -366,6 +367,67 @@ def attention_sweep(seed, steps=32):
     return res
 
 
+def draft_head(seed, threads, drafts=96, reps=20):
+    """The draft head at the full shape: the input projection (5120 x 10240),
+    one attention layer of the hybrid (24/4 heads of 256, SwiGLU 17408) over a
+    512-row cache, the final norm and the 248320-row LM head with its argmax.
+    Drafts are chained on the device (each takes the previous draft token and
+    layer output without a host round trip); HIP events around `drafts`
+    drafts, and around `reps` of each part alone."""
+    import torch
+    import synth
+    import layer_sliced_quantized_amd as slq
+    t0 = time.time()
+    base = synth.HYBRID_5120
+    sh = synth.mtp_shape(base)
+    T = synth.layer_tensors(sh, synth.Q4_0, seed, synth.WL_MTP, 0, threads=threads)
+    M = synth.mtp_tensors(sh, synth.Q4_0, seed)
+    G = synth.global_tensors(base, synth.Q4_0, seed, synth.WL_SLICE)
+    G["out_norm"] = M["mtp_out_norm"]
+    max_seq = ((PREFILL + drafts + reps + 64 + 63) // 64) * 64
+    # the host stage keeps the head's vectors in fp32 (with synthetic weights
+    # the layer's output can leave the fp16 range)
+    cfg = slq.make_config(sh, synth.Q4_0, 0, 1, max_seq=max_seq, max_verify=1, io_fp32=True, has_embed=True,
+                          has_head=True, has_mtp=True)
+    s = slq.Slice(cfg)
+    s.load_numpy({0: T}, {**G, **{k: M[k] for k in ("mtp_fc", "mtp_norm_e", "mtp_norm_h")}})
+    del T, G
+    K, V = synth.kv_prefill(seed, synth.WL_MTP, 0, sh.kv_heads, PREFILL, sh.head_dim)
+    s.set_kv(0, torch.from_numpy(K), torch.from_numpy(V))
+    s.reset(PREFILL)
+    torch.cuda.synchronize()
+    log(f"draft head: {s.weights.numel() / 1e9:.2f} GB weights generated and loaded in {time.time() - t0:.1f}s")
+    tok = torch.tensor([17], dtype=torch.int32, device="cuda")
+    h = torch.from_numpy(synth.hidden_inputs(seed, synth.WL_MTP, 1, sh.hidden)[0].astype(np.float32)).cuda()
+    x = torch.empty(sh.hidden, dtype=torch.float32, device="cuda")
+    y = torch.empty(sh.hidden, dtype=torch.float32, device="cuda")
+
+    def one():
+        s.mtp_input(tok, h, out=x)
+        s.decode(x, y)
+        s.head_argmax(y, tok=tok)
+        h.copy_(y)
+
+    for _ in range(3):
+        one()
+    s.reset(PREFILL)
+    torch.cuda.synchronize()
+    chain_us = _event_time_us(one, drafts)
+    s.reset(PREFILL)
+    parts = {"input_us": _event_time_us(lambda: s.mtp_input(tok, h, out=x), reps),
+             "layer_us": _event_time_us(lambda: s.decode(x, y), reps),
+             "head_argmax_us": _event_time_us(lambda: s.head_argmax(y, tok=tok), reps)}
+    s.sync_check()
+    head_bytes = gemv_bytes(base.vocab, base.hidden, synth.Q4_0)
+    out = {"us_per_draft": round(chain_us, 2), **{k: round(v, 2) for k, v in parts.items()},
+           "head_GB_s": round(head_bytes / (parts["head_argmax_us"] * 1e-6) / 1e9, 1),
+           "what": "draft head at hidden 5120: input projection 5120x10240, one attention layer + SwiGLU 17408 "
+                   "over 512 cached rows, final norm, 248320x5120 head + argmax (Q4_0); synthetic weights"}
+    del s
+    torch.cuda.empty_cache()
+    return out
+
+
 def gemv_sweep(seed, reps):
     import torch
     import synth
@@ -478,6 +540,7 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-mixers", action="store_true", help="skip the DeltaNet / attention kernel timings")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the streaming-read ceiling")
+    ap.add_argument("--no-draft", action="store_true", help="skip the draft-head timing")
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--no-chain", action="store_true",
                     help="decode with every product as its own kernel instead of the chained products (same results)")
@@ -502,7 +565,8 @@ def main() -> int:
         slq.debug_override("CHAIN_DN", 0)
     threads = min(16, os.cpu_count() or 8)
     shape = synth.HYBRID_5120
-    n_in = args.warmup + args.steps + args.profile_steps + 4 * (args.verify_rounds + 1) + 32 * (args.prefill_chunks + 1) + 16
+    n_in = (args.warmup + args.steps + args.profile_steps + 4 * (args.verify_rounds + 1) +
+            (32 + 32 + 64) * (args.prefill_chunks + 1) + 16)
     max_seq = ((PREFILL + n_in + 63) // 64) * 64
     log(f"inputs: {n_in} fresh fp16 hidden states; max_seq {max_seq}")
     H_host = synth.hidden_inputs(args.seed, synth.WL_SLICE, n_in, shape.hidden)
@@ -571,6 +635,15 @@ def main() -> int:
     base += 16 * (args.prefill_chunks + 1)
     pre_c = run_prefill_chunked(s, H[base:], args.prefill_chunks) if args.prefill_chunks > 0 else None
     log(f"prefill (16-token passes, chunked DeltaNet): {pre_c}")
+    # wider prompt passes: every product reads its weights once for 32 / 64 tokens
+    base += 16 * (args.prefill_chunks + 1)
+    pre_w = {}
+    for kw in (32, 64):
+        if args.prefill_chunks > 0:
+            npass = max(1, args.prefill_chunks * 16 // kw)     # about as many tokens as the 16-token legs
+            pre_w[kw] = run_prefill_chunked(s, H[base:], npass, k=kw)
+            base += kw * (npass + 1)
+            log(f"prefill ({kw}-token passes, chunked DeltaNet): {pre_w[kw]}")
     s_chained = not args.no_chain
     del s
     torch.cuda.empty_cache()
@@ -584,6 +657,16 @@ def main() -> int:
     # ---- decode attention at three KV lengths
     if not args.no_attn_sweep:
         extra["attention_decode"] = attention_sweep(args.seed)
+    # ---- the draft head at full size, and the speculative round it completes
+    if not args.no_draft:
+        dh = draft_head(args.seed, threads)
+        round_us = ver["us_per_verify"] + 3 * dh["us_per_draft"]
+        dh["spec_round_us"] = round(round_us, 1)
+        dh["committed_tok_s_with_drafts"] = round(ver["accepted_tokens"] / (args.verify_rounds * round_us * 1e-6), 2)
+        dh["note"] = ("a speculative round: the 4-token verify plus 3 chained drafts; committed tokens from the "
+                      "seeded accept pattern of the verify leg (synthetic drafts carry no acceptance rate)")
+        extra["draft_head"] = dh
+        log(f"draft head: {dh}")
     # ---- standalone GEMV sweep
     if not args.no_sweep:
         extra["gemv_sweep"] = gemv_sweep(args.seed, args.sweep_reps)
@@ -637,6 +720,8 @@ def main() -> int:
         "verify": ver,
         "prefill_16": pre,
         "prefill_16_chunked": pre_c,
+        "prefill_32_chunked": pre_w.get(32),
+        "prefill_64_chunked": pre_w.get(64),
     }
     res.update(extra)
     print(json.dumps(res), flush=True)
