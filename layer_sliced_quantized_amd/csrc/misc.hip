@@ -143,13 +143,14 @@ hipError_t launch_embed(const Packed& E, const int32_t* tok, void* out, int fp32
 // vector h; each RMS-normalises its H values with its own weights (sum of
 // squares in a fixed order: per thread, then per wave, then waves in order)
 // and writes the digits of its half of the 2H-wide input: blocks 0..H/32-1
-// the embedding side, H/32.. the hidden side.
+// the embedding side, H/32.. the hidden side.  MTP_THREADS threads each.
+constexpr int MTP_THREADS = 1024;
 template <int QT>
-__global__ __launch_bounds__(256) void k_mtp_in(Packed E, const int32_t* __restrict__ tok, const void* hin,
+__global__ __launch_bounds__(MTP_THREADS) void k_mtp_in(Packed E, const int32_t* __restrict__ tok, const void* hin,
                                                 int fp32, const float* __restrict__ w_e,
                                                 const float* __restrict__ w_h, float eps, Act x) {
   constexpr int NH = QT == QT_Q4 ? 1 : 2;
-  extern __shared__ float sv[];          // [H] values, then [4] wave sums
+  extern __shared__ float sv[];          // [H] values, then [MTP_THREADS / 64] wave sums
   const int H = (int)E.cols;
   const int half = blockIdx.x;
   const int tid = threadIdx.x;
@@ -160,7 +161,7 @@ __global__ __launch_bounds__(256) void k_mtp_in(Packed E, const int32_t* __restr
     const int64_t rg = r / RG;
     const int lane = (int)(r % RG);
     const int nblk = E.nblk();
-    for (int i = tid; i < H; i += 256) {
+    for (int i = tid; i < H; i += MTP_THREADS) {
       const int b = i / QK, j = i % QK;
       const int t = b / TB, bi = b % TB;
       const int nb_t = min(TB, nblk - t * TB);
@@ -178,7 +179,7 @@ __global__ __launch_bounds__(256) void k_mtp_in(Packed E, const int32_t* __restr
       ss += v * v;
     }
   } else {
-    for (int i = tid; i < H; i += 256) {
+    for (int i = tid; i < H; i += MTP_THREADS) {
       const float v = fp32 ? reinterpret_cast<const float*>(hin)[i]
                            : __half2float(reinterpret_cast<const __half*>(hin)[i]);
       sv[i] = v;
@@ -189,11 +190,12 @@ __global__ __launch_bounds__(256) void k_mtp_in(Packed E, const int32_t* __restr
   const int wave = wave_id(), lane = tid & 63;
   if (lane == 0) sv[H + wave] = ss;
   __syncthreads();
-  const float tot = ((sv[H] + sv[H + 1]) + sv[H + 2]) + sv[H + 3];
+  float tot = sv[H];
+  for (int w = 1; w < MTP_THREADS / 64; ++w) tot += sv[H + w];   // waves in order
   const float rn = 1.0f / sqrtf(tot / (float)H + eps);
   const float* w = half == 0 ? w_e : w_h;
   const int nb = H / QK;
-  for (int rg = wave; 2 * rg < nb; rg += 4) {
+  for (int rg = wave; 2 * rg < nb; rg += MTP_THREADS / 64) {
     const int i = rg * RG + lane;
     const bool ok = i < H;
     const float v = ok ? (sv[i] * rn) * w[i] : 0.0f;
@@ -206,9 +208,9 @@ hipError_t launch_mtp_input(const Packed& E, const int32_t* tok, const void* hin
                             const float* w_h, float eps, Act x, hipStream_t s) {
   const int H = (int)E.cols;
   if (H % QK || x.nblk != 2 * H / QK || x.mxd) return hipErrorInvalidValue;
-  const size_t lds = ((size_t)H + 4) * 4;
-  if (E.qt == QT_Q4) k_mtp_in<QT_Q4><<<2, 256, lds, s>>>(E, tok, hin, fp32, w_e, w_h, eps, x);
-  else k_mtp_in<QT_Q8><<<2, 256, lds, s>>>(E, tok, hin, fp32, w_e, w_h, eps, x);
+  const size_t lds = ((size_t)H + MTP_THREADS / 64) * 4;
+  if (E.qt == QT_Q4) k_mtp_in<QT_Q4><<<2, MTP_THREADS, lds, s>>>(E, tok, hin, fp32, w_e, w_h, eps, x);
+  else k_mtp_in<QT_Q8><<<2, MTP_THREADS, lds, s>>>(E, tok, hin, fp32, w_e, w_h, eps, x);
   return hipGetLastError();
 }
 
