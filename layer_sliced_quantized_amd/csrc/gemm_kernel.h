@@ -270,7 +270,7 @@ __device__ __forceinline__ void tile_diag(TileRegs<QT>& r, int kb, int nb, __amd
 // next tile and the ring slot with the record DENSE_RING blocks on (in this
 // tile or the next).  kb: first block of this tile; nb: its blocks; ntile,
 // nbn: the next tile's bytes and blocks (nbn = 0: none).
-template <int QT, int TP>
+template <int QT, int TP, bool NT>
 __device__ __forceinline__ void tile_dense(TileRegs<QT>& w, int kb, int nb, __amdgpu_buffer_rsrc_t rs,
                                            const uint8_t* ntile, int kb_next, int nbn, uint8_t* ring,
                                            float (&acc)[4][4]) {
@@ -297,7 +297,7 @@ __device__ __forceinline__ void tile_dense(TileRegs<QT>& w, int kb, int nb, __am
 #pragma unroll
   for (int b = 0; b < TB; ++b) sct[b * 64 + lane] = scale_of(w.sc, b);
   SLQ_COMPILER_FENCE();
-  w.sc = load_scales_fixed(ntile, lane, nbn, NH);
+  w.sc = load_scales_fixed<NT>(ntile, lane, nbn, NH);
   SLQ_COMPILER_FENCE();
 #pragma unroll
   for (int b = 0; b < TB; ++b) {
@@ -365,7 +365,7 @@ __device__ __forceinline__ void tile_dense(TileRegs<QT>& w, int kb, int nb, __am
     // loads (the last block again, or block 0's record into the unused slot)
     // keep the load count fixed
     SLQ_COMPILER_FENCE();
-    load_block_fixed<QT>(ntile, lane, nbn, b, w);
+    load_block_fixed<QT, NT>(ntile, lane, nbn, b, w);
     const int nxt = b < TB - DR ? (b + DR < nb ? kb + b + DR : 0) : (b + DR - TB < nbn ? kb_next + b + DR - TB : 0);
     dma_block<QT, DPB>(rs, nxt, TP, ring + (b % DR) * SLOT);
     SLQ_COMPILER_FENCE();
@@ -566,8 +566,10 @@ __global__ __launch_bounds__(512) void k_gemm_diag(Packed W, Act x, NormIn nin, 
 
 // NGR token groups (prompt passes of 17..64 tokens): wave w multiplies group
 // w % NGR over K part w / NGR of the split, so the waves of one K part read
-// the same weight tiles (from HBM once, the repeats from L2); tokens of group
-// g are summed over the K parts in order.  NGR = 1 is the 9..16-token form.
+// the same weight tiles: with ordinary loads (not nontemporal ones) L2 keeps
+// a tile for the other groups' waves, and HBM delivers it once; tokens of
+// group g are summed over the K parts in order.  NGR = 1 is the 9..16-token
+// form (nontemporal weight loads).
 template <int QT, int EPI, int NGR>
 __global__ __launch_bounds__(512) void k_gemm_dense(Packed W, Act x, NormIn nin, GemvOut out, int ksplit, int T) {
   constexpr int TBY = tile_bytes(QT);
@@ -603,7 +605,7 @@ __global__ __launch_bounds__(512) void k_gemm_dense(Packed W, Act x, NormIn nin,
     for (int b = 0; b < DENSE_RING; ++b)
       dma_block<QT, gemm_dpb(QT, TP)>(rs, b < nb_of(t0) ? t0 * TB + b : 0, TP, ring + b * gemm_slot(QT, TP));
     SLQ_COMPILER_FENCE();
-    load_tile_fixed<QT>(base + (size_t)t0 * TBY, lane, nb_of(t0), R);
+    load_tile_fixed<QT, NGR == 1>(base + (size_t)t0 * TBY, lane, nb_of(t0), R);
     SLQ_COMPILER_FENCE();
   }
 
@@ -624,8 +626,8 @@ __global__ __launch_bounds__(512) void k_gemm_dense(Packed W, Act x, NormIn nin,
     // the loop, as in the block-diagonal form
     auto one = [&](int t) {
       const bool n1 = t + 1 < t1;
-      tile_dense<QT, TP>(R, t * TB, nb_of(t), rs, base + (size_t)(n1 ? t + 1 : t) * TBY, (t + 1) * TB,
-                         n1 ? nb_of(t + 1) : 0, ring, acc);
+      tile_dense<QT, TP, NGR == 1>(R, t * TB, nb_of(t), rs, base + (size_t)(n1 ? t + 1 : t) * TBY, (t + 1) * TB,
+                                   n1 ? nb_of(t + 1) : 0, ring, acc);
     };
     one(t0);
     for (int t = t0 + 1; t < t1; ++t) one(t);

@@ -31,25 +31,34 @@ __device__ __forceinline__ void load_tile(const uint8_t* tile, int lane, int nb,
   r.sc = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(tile + (size_t)nb * NH * RG * 16) + lane);
 }
 
+// One 16-byte weight load: nontemporal (streamed past the caches, the usual
+// case: every weight is read once) or, NT = false, an ordinary load that L2
+// keeps for other waves reading the same tile soon after.
+template <bool NT>
+__device__ __forceinline__ u32x4 ld_w(const u32x4* p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
 // A tile's weights into registers with always TB * NH + 1 loads, whatever the
 // tile: the codes of a ragged tile (nb < TB) repeat its last block, and nb = 0
 // (no tile) reads the first 16 bytes at tile from every lane.  Every path thus
 // issues the same loads, which keeps the compiler's own waits on these
 // registers (and the explicit ring waits) exact.
-template <int QT>
+template <int QT, bool NT = true>
 __device__ __forceinline__ void load_tile_fixed(const uint8_t* tile, int lane, int nb, TileRegs<QT>& r) {
   constexpr int NH = TileRegs<QT>::NH;
   const int nc = nb * NH;
   const u32x4* cp = reinterpret_cast<const u32x4*>(tile) + (nb ? lane : 0);
 #pragma unroll
-  for (int b = 0; b < TB * NH; ++b) r.c[b] = __builtin_nontemporal_load(cp + (nb ? (b < nc ? b : nc - 1) : 0) * RG);
-  r.sc = __builtin_nontemporal_load(nb ? reinterpret_cast<const u32x4*>(tile + (size_t)nc * RG * 16) + lane : cp);
+  for (int b = 0; b < TB * NH; ++b) r.c[b] = ld_w<NT>(cp + (nb ? (b < nc ? b : nc - 1) : 0) * RG);
+  r.sc = ld_w<NT>(nb ? reinterpret_cast<const u32x4*>(tile + (size_t)nc * RG * 16) + lane : cp);
 }
 
 // One block's codes of a tile (r.c[b * NH + h], h < NH) with always NH loads,
 // and the tile's scales (r.sc) with always one, choosing their sources as
 // load_tile_fixed does; together they issue its loads one block at a time.
-template <int QT>
+template <int QT, bool NT = true>
 __device__ __forceinline__ void load_block_fixed(const uint8_t* tile, int lane, int nb, int b, TileRegs<QT>& r) {
   constexpr int NH = TileRegs<QT>::NH;
   const int nc = nb * NH;
@@ -57,12 +66,13 @@ __device__ __forceinline__ void load_block_fixed(const uint8_t* tile, int lane, 
 #pragma unroll
   for (int h = 0; h < NH; ++h) {
     const int i = b * NH + h;
-    r.c[i] = __builtin_nontemporal_load(cp + (nb ? (i < nc ? i : nc - 1) : 0) * RG);
+    r.c[i] = ld_w<NT>(cp + (nb ? (i < nc ? i : nc - 1) : 0) * RG);
   }
 }
+template <bool NT = true>
 __device__ __forceinline__ u32x4 load_scales_fixed(const uint8_t* tile, int lane, int nb, int nh) {
   const u32x4* cp = reinterpret_cast<const u32x4*>(tile) + (nb ? lane : 0);
-  return __builtin_nontemporal_load(nb ? reinterpret_cast<const u32x4*>(tile + (size_t)nb * nh * RG * 16) + lane : cp);
+  return ld_w<NT>(nb ? reinterpret_cast<const u32x4*>(tile + (size_t)nb * nh * RG * 16) + lane : cp);
 }
 
 __device__ __forceinline__ float scale_of(const u32x4& sc, int b) {
