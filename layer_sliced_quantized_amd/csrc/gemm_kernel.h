@@ -126,6 +126,15 @@ __device__ __forceinline__ uint32_t sext_nibbles(uint32_t t) {
 
 #define SLQ_COMPILER_FENCE() asm volatile("" ::: "memory")
 
+// The exact block sum of three digit-pair products, D = P0 + 256 (P1 + 256 P2),
+// as two shift-adds: the empty asm keeps the compiler from distributing the
+// outer shift over the inner sum (which takes three instructions).
+__device__ __forceinline__ int digit_sum3(int p0, int p1, int p2) {
+  int t = p1 + (p2 << 8);
+  asm volatile("" : "+v"(t));
+  return p0 + (t << 8);
+}
+
 // Digits (token slots 0..tp-1) and scales of block blk into a ring slot:
 // piece q < NCH*tp is chunk q / tp, slot q % tp; the last 4 pieces are the
 // block's 16 scales.  Exactly DPB instructions (lane 0 is always active).
@@ -241,7 +250,7 @@ __device__ __forceinline__ void tile_diag(TileRegs<QT>& r, int kb, int nb, __amd
         for (int i = 0; i < 4; ++i) {
           float bf;
           if constexpr (QT == QT_Q4) {
-            bf = (float)(P[0][i] + ((P[1][i] + (P[2][i] << 8)) << 8));
+            bf = (float)digit_sum3(P[0][i], P[1][i], P[2][i]);
           } else {
             bf = __builtin_fmaf((float)P[2][i], 65536.0f, (float)(P[0][i] + (P[1][i] << 8)));
           }
@@ -352,7 +361,7 @@ __device__ __forceinline__ void tile_dense(TileRegs<QT>& w, int kb, int nb, __am
         for (int i = 0; i < 4; ++i) {
           float bf;
           if constexpr (QT == QT_Q4) {
-            bf = (float)(P0[i] + ((P1[i] + (P2[i] << 8)) << 8));
+            bf = (float)digit_sum3(P0[i], P1[i], P2[i]);
           } else {
             bf = __builtin_fmaf((float)P2[i], 65536.0f, (float)(P0[i] + (P1[i] << 8)));
           }
