@@ -324,6 +324,28 @@ def test_hybrid_q8_slice_8_layers():
         assert rel_err(out[t], ref[t]) <= TOL, t
 
 
+@pytest.mark.timeout(900)
+def test_hybrid_64_layer_q8_slice():
+    """The Q8_0 slice the benchmark times: all 64 layers (25.3 GB of Q8_0
+    weights), decode, a 4-token verify, a commit and one more decode, on the
+    fp32 residual stream against the oracle."""
+    sh = synth.HYBRID_5120
+    s, orc, _, _ = make_pair(sh, synth.Q8_0, 0, 64, workload=synth.WL_SLICE, prefill=512, max_seq=1024,
+                             max_verify=4, io_fp32=False, threads=16)
+    H = inputs(sh, 6, workload=synth.WL_SLICE, io_fp32=False, step0=300)
+    s.decode(_t(H[0]))
+    assert rel_err(s.get_hidden().cpu().numpy()[0], orc.decode(H[0], raw=True)) <= TOL
+    s.verify(_t(H[1:5]))
+    out = s.get_hidden(4).cpu().numpy()
+    ref = orc.verify(H[1:5], raw=True)
+    for t in range(4):
+        assert rel_err(out[t], ref[t]) <= TOL, t
+    s.commit(2)
+    orc.commit(2)
+    s.decode(_t(H[5]))
+    assert rel_err(s.get_hidden().cpu().numpy()[0], orc.decode(H[5], raw=True)) <= TOL
+
+
 DEEP = synth.ModelShape(
     name="deep_hybrid_128", hidden=128, n_layers=64, attn_period=4,
     dn_heads=2, dn_dk=64, dn_dv=64, q_heads=4, kv_heads=2, head_dim=64, rope_dims=32,
