@@ -1,10 +1,10 @@
 """The draft head (multi-token prediction) on the GPU against the oracle, and
 the speculative loop driven by its drafts.
 
-The last stage samples a token and its draft head guesses the one after
-(SwarmLLM README, pipeline diagram); drafts are verified in one batched pass
-and the speculative stream equals the plain one (feature list, benchmark
-table).  The head's form is the oracle's reading (oracle.model.mtp_input,
+The last stage samples a token and its draft head predicts the token that
+follows it (SwarmLLM README, pipeline diagram); drafts are checked in one
+batched pass and the speculative stream equals the plain one (feature list,
+benchmark table).  The head's form is the oracle's reading (oracle.model.mtp_input,
 DraftHead): the input projection of the normalised embedding and hidden
 state, one full-attention layer with its own cache, its own final norm, the
 model's LM head.  Its weights are synthetic, so its drafts are poor guesses;
