@@ -38,7 +38,7 @@ PREFILL = 512
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_hybrid64_q4_decode.md")
-CHAIN_SOURCES = ("slq.h", "dev.h", "gemv_kernel.h", "chain.hip")
+CHAIN_SOURCES = ("slq.h", "dev.h", "gemv_kernel.h", "deltanet.h", "chain.hip")
 
 
 def chain_source_hash() -> str:
