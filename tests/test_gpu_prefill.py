@@ -234,3 +234,23 @@ def test_deltanet_and_ffn_layer_5120_prefill_48():
     out = s.prefill(_t(H)).cpu().numpy()
     for t in range(48):
         assert rel_err(out[t], orc.decode(H[t], raw=True)) <= TOL, t
+
+
+@pytest.mark.timeout(600)
+def test_hybrid_8_layer_prefill_64():
+    """The benchmark's 64-token pass on the first 8 layers of the hidden-5120
+    hybrid (6 DeltaNet, 2 attention, SwiGLU 17408; 512 prior KV rows, fp16
+    inputs): every token's fp32 residual stream against 64 plain oracle
+    steps, then one decode."""
+    sh = synth.HYBRID_5120
+    s, orc, _, _ = make_pair(sh, synth.Q4_0, 0, 8, workload=synth.WL_SLICE, prefill=512, max_seq=1024,
+                             max_verify=16, io_fp32=False, threads=16, max_prefill=64)
+    H = inputs(sh, 65, workload=synth.WL_SLICE, io_fp32=False, step0=400)
+    s.prefill(_t(H[:64]))
+    out = s.get_hidden(64).cpu().numpy()
+    for t in range(64):
+        assert rel_err(out[t], orc.decode(H[t], raw=True)) <= TOL, t
+    assert s.position == 576
+    s.decode(_t(H[64]))
+    assert rel_err(s.get_hidden().cpu().numpy()[0], orc.decode(H[64], raw=True)) <= TOL
+
