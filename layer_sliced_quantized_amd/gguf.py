@@ -263,7 +263,23 @@ DEFAULT_NAMES = {
     "head": "output.weight",
     "out_norm": "output_norm.weight",
 }
-_GLOBAL = ("embed", "head", "out_norm")
+_GLOBAL = ("embed", "head", "out_norm", "mtp_fc", "mtp_norm_e", "mtp_norm_h")
+_MTP = ("mtp_fc", "mtp_norm_e", "mtp_norm_h")
+
+# A draft head (a slice with has_mtp: one layer plus its input projection and
+# norms) stored in the same file under "mtp.": its layer's tensors take the
+# layer names above with "mtp." for "blk.{l}.", its final norm is
+# "mtp.output_norm.weight", and it shares the model's embedding and head.
+# These names are this library's own, like the hybrid's above.
+MTP_NAMES = {
+    **{k: v.replace("blk.{l}.", "mtp.") for k, v in DEFAULT_NAMES.items() if v.startswith("blk.{l}.")},
+    "mtp_fc": "mtp.fc.weight",
+    "mtp_norm_e": "mtp.norm_e.weight",
+    "mtp_norm_h": "mtp.norm_h.weight",
+    "out_norm": "mtp.output_norm.weight",
+    "embed": "token_embd.weight",
+    "head": "output.weight",
+}
 
 
 def slice_tensors(g: GGUFFile, layer: int, names: dict = DEFAULT_NAMES) -> dict:
@@ -293,6 +309,8 @@ def check_against_config(g: GGUFFile, cfg, names: dict = DEFAULT_NAMES) -> list:
         if ours == "embed" and not (cfg.has_embed or (cfg.has_head and cfg.tied_head)):
             continue
         if ours in ("head", "out_norm") and not cfg.has_head:
+            continue
+        if ours in _MTP and not cfg.has_mtp:
             continue
         todo.append((ours, 0, key))
     for layer in range(cfg.layer_begin, cfg.layer_end):

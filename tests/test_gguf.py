@@ -247,3 +247,57 @@ def test_q35_file_round_trip_and_config_check(tmp_path):
     assert len(gguf.check_against_config(g, cfg)) == sum(len(d) for d in tensors.values())
     with pytest.raises(gguf.GGUFError):
         gguf.check_against_config(g, _cfg())
+
+
+
+def draft_head_gguf_tensors(base, T, M, G, qtype):
+    """A draft head's tensors under the "mtp." names (its layer T, its own
+    tensors M) and the model's embedding and untied head (G), as write_gguf
+    takes them."""
+    qt = gguf.T_Q4_0 if qtype == synth.Q4_0 else gguf.T_Q8_0
+    sh = synth.mtp_shape(base)
+    H = sh.hidden
+    mats = synth.matrix_shapes(sh, 0)
+    out = {}
+    for name, arr in T.items():
+        key = gguf.MTP_NAMES[name]
+        out[key] = (qt, tuple(reversed(mats[name])), arr.tobytes()) if name in mats else np.asarray(arr, np.float32)
+    out["mtp.fc.weight"] = (qt, (2 * H, H), M["mtp_fc"].tobytes())
+    out["mtp.norm_e.weight"] = M["mtp_norm_e"]
+    out["mtp.norm_h.weight"] = M["mtp_norm_h"]
+    out["mtp.output_norm.weight"] = M["mtp_out_norm"]
+    out["token_embd.weight"] = (qt, (H, base.vocab), G["embed"].tobytes())
+    out["output.weight"] = (qt, (H, base.vocab), G["head"].tobytes())
+    return out
+
+
+def test_draft_head_file_names_and_config_check(tmp_path):
+    """A draft head stored under "mtp." beside a model: its layer, input
+    projection, norms and final norm, with the model's embedding and head;
+    the draft head's configuration takes exactly those, a plain stage of the
+    model none of them."""
+    import dataclasses
+    import layer_sliced_quantized_amd as slq
+    base = dataclasses.replace(SHAPE, vocab=64, tied_head=False)
+    sh = synth.mtp_shape(base)
+    T = synth.layer_tensors(sh, synth.Q4_0, 0, synth.WL_MTP, 0)
+    M = synth.mtp_tensors(sh, synth.Q4_0, 0)
+    G = synth.global_tensors(base, synth.Q4_0, 0, 91)
+    p = tmp_path / "draft.gguf"
+    gguf.write_gguf(str(p), {}, draft_head_gguf_tensors(base, T, M, G, synth.Q4_0))
+    g = gguf.GGUFFile(str(p))
+    # the arrays read back are the ones written
+    np.testing.assert_array_equal(g.array("mtp.fc.weight").reshape(-1), M["mtp_fc"].reshape(-1))
+    np.testing.assert_array_equal(g.array("mtp.norm_h.weight"), M["mtp_norm_h"])
+    cfg = slq.make_config(sh, synth.Q4_0, 0, 1, max_seq=64, max_verify=1, has_embed=True, has_head=True,
+                          has_mtp=True)
+    todo = gguf.check_against_config(g, cfg, gguf.MTP_NAMES)
+    assert {o for o, _, _ in todo} == set(T) | {"mtp_fc", "mtp_norm_e", "mtp_norm_h", "out_norm", "embed", "head"}
+    assert all(l == 0 for _, l, _ in todo)
+    # a plain stage reading the same file with the model's names loads nothing of the draft head
+    plain = slq.make_config(base, synth.Q4_0, 0, 4, has_embed=True, has_head=True)
+    assert {k for _, _, k in gguf.check_against_config(g, plain)} == {"token_embd.weight", "output.weight"}
+    # the draft head's names refused by a slice that is not a draft head
+    nomtp = slq.make_config(sh, synth.Q4_0, 0, 1, max_seq=64, max_verify=1, has_embed=True, has_head=True)
+    assert not {o for o, _, _ in gguf.check_against_config(g, nomtp, gguf.MTP_NAMES)} & {"mtp_fc", "mtp_norm_e", "mtp_norm_h"}
+

@@ -48,3 +48,35 @@ def test_gguf_in_another_block_format_is_refused(tmp_path):
     s = slq.Slice(slq.make_config(SHAPE, synth.Q4_0, 0, 4, max_seq=256, max_verify=4, io_fp32=True))
     with pytest.raises(gguf.GGUFError):
         gguf.load_into_slice(s, gguf.GGUFFile(str(path)))
+
+
+def test_draft_head_from_gguf_drafts_like_direct_load(tmp_path):
+    """A draft head read from its "mtp." tensors in a file gives the input
+    projection, layer output and logits of one loaded from the same arrays
+    directly, bit for bit, over three chained drafts."""
+    from test_gguf import draft_head_gguf_tensors
+    from test_gpu_mtp import TINY_LM, WL_MAIN, make_draft_head
+    base, qt = TINY_LM, synth.Q4_0
+    ref, _, sh = make_draft_head(base, qt, max_seq=64)
+    T = synth.layer_tensors(sh, qt, 0, synth.WL_MTP, 0, threads=8)
+    M = synth.mtp_tensors(sh, qt, 0)
+    G = synth.global_tensors(base, qt, 0, WL_MAIN)
+    path = tmp_path / "draft.gguf"
+    gguf.write_gguf(str(path), {}, draft_head_gguf_tensors(base, T, M, G, qt))
+    s = slq.Slice(slq.make_config(sh, qt, 0, 1, max_seq=64, max_verify=1, has_embed=True, has_head=True,
+                                  has_mtp=True))
+    assert gguf.load_into_slice(s, gguf.GGUFFile(str(path)), gguf.MTP_NAMES) == len(T) + 6
+    s.reset(0)
+    tok = torch.tensor([5], dtype=torch.int32, device="cuda")
+    h = torch.from_numpy(synth.hidden_inputs(5, synth.WL_MTP, 1, sh.hidden)[0]).cuda()
+    la = torch.empty(sh.vocab, dtype=torch.float32, device="cuda")
+    lb = torch.empty_like(la)
+    for _ in range(3):
+        xa, xb = s.mtp_input(tok, h), ref.mtp_input(tok, h)
+        np.testing.assert_array_equal(xa.cpu().numpy(), xb.cpu().numpy())
+        ya, yb = s.decode(xa), ref.decode(xb)
+        np.testing.assert_array_equal(ya.cpu().numpy(), yb.cpu().numpy())
+        da, db = s.head_argmax(ya, logits=la), ref.head_argmax(yb, logits=lb)
+        np.testing.assert_array_equal(la.cpu().numpy(), lb.cpu().numpy())
+        assert int(da.item()) == int(db.item())
+        tok, h = da.reshape(1).to(torch.int32), ya
