@@ -38,7 +38,7 @@ PREFILL = 512
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_hybrid64_q4_decode.md")
-CHAIN_SOURCES = ("slq.h", "dev.h", "gemv_kernel.h", "deltanet.h", "chain.hip")
+CHAIN_SOURCES = ("slq.h", "dev.h", "gemv_kernel.h", "deltanet.h", "chain.hip", "slice.cpp")
 
 
 def chain_source_hash() -> str:
@@ -86,7 +86,7 @@ def mixer_rows_cols(shape, l):
 
 
 def chain_step_bytes(shape, qtype, deltanet: bool = True) -> int:
-    """Algorithmic bytes of one decode step's chained launches (one per layer):
+    """Algorithmic bytes of one decode step's chained launches (all layers):
     a DeltaNet layer's state update (fp32 state read and written, its input
     projections' outputs read), mixer output, gate/up, down and, except after
     the last layer, the next layer's input projections -- packed weights plus
@@ -549,6 +549,7 @@ def main() -> int:
     ap.add_argument("--copy-calib", action="store_true",
                     help="also run 3 plain copies of a 512 MiB buffer (a known-size reference for PMC byte counters)")
     args = ap.parse_args()
+    args.profile_steps = max(1, args.profile_steps)   # the per-op profile counts the chained launches
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the slice runs on a single MI355X and this build has no "
               "multi-GPU path (a layer pipeline across GPUs is described in the design notes); run with --gpus 1",
@@ -607,13 +608,17 @@ def main() -> int:
     for op, v in gemv_in_slice.items():
         log(f"gemv {op:8s} (own kernel) {v}")
     if not args.no_chain:
-        chain_ms = time_gemv_op(s, "chain", args.gemv_reps) / shape.n_layers
-        chain_launches = shape.n_layers * args.gemv_reps
-        rl_bytes = chain_step_bytes(shape, synth.Q4_0, deltanet=not args.no_chain_dn) // shape.n_layers
-        rl_kernel = (f"k_chain<2>: one launch per layer of the chained phases (the DeltaNet state update in "
-                     f"DeltaNet layers, mixer output, RMSNorm + gate/up + SwiGLU, down + residual, next layer's "
-                     f"input projections), mean of {chain_launches} launches over the 64 layers in layer order, "
-                     f"HIP events")
+        # the chained launches of one step (from the eager per-op profile): each
+        # runs the phases of consecutive layers up to the next attention layer
+        n_launch = ops["chain"][1]
+        chain_ms = time_gemv_op(s, "chain", args.gemv_reps) / n_launch
+        chain_launches = n_launch * args.gemv_reps
+        rl_bytes = chain_step_bytes(shape, synth.Q4_0, deltanet=not args.no_chain_dn) // n_launch
+        rl_kernel = (f"k_chain<2>: {n_launch} launches per step, each running the chained phases of consecutive "
+                     f"layers up to the next attention layer (per layer: the DeltaNet state update in DeltaNet "
+                     f"layers, mixer output, RMSNorm + gate/up + SwiGLU, down + residual, next layer's input "
+                     f"projections); bytes and time are means over {chain_launches} launches ({args.gemv_reps} "
+                     f"passes over the step's launches in step order), HIP events")
         rl_ms = chain_ms
     else:
         rl_bytes = gemv_bytes(f1_rows, f1_cols, synth.Q4_0)

@@ -36,16 +36,17 @@
 //
 // Visibility.  Whatever a product hands to a later one inside the kernel
 // (the residual h, the RMSNorm partial sums, the activation digits, split-K
-// partials) is stored with agent-scope atomic stores (global stores with sc1
-// on gfx950, written through to the level that every XCD reads), and h and
-// the partial sums are read back with agent-scope atomic loads.  The last
+// partials, the input projections a DeltaNet update reads) is stored with
+// agent-scope atomic stores (global stores with sc1 on gfx950, written
+// through to the level that every XCD reads), and h, the partial sums and
+// the update's inputs are read back with agent-scope atomic loads.  The last
 // workgroup of each row group waits for its stores to complete (vmcnt 0)
 // before it counts the row group as finished; the workgroup that finishes
 // the product's last row group then sets the product's ready flags.  The
 // digits are read by scalar loads; each digit buffer is written once per
-// kernel and read only after its ready flag, so no cache of the reading XCD
-// can hold an older copy of it from this kernel, and the kernel boundary
-// drops copies from earlier kernels.
+// kernel (every layer of a launch has its own) and read only after its ready
+// flag, so no cache of the reading XCD can hold an older copy of it from this
+// kernel, and the kernel boundary drops copies from earlier kernels.
 #include "gemv_kernel.h"
 #include "deltanet.h"
 
@@ -55,9 +56,14 @@ constexpr unsigned CHAIN_SPIN_LIMIT = 1u << 20;
 
 constexpr int CHAIN_COPIES = 64;   // copies of each ready flag (pollers spread over 64 lines)
 constexpr int CHAIN_GROUPS = 32;   // completion groups per product
-__device__ __forceinline__ unsigned* chain_count(unsigned* sync, int p, int g) { return sync + 32 * (33 * p + g); }
+static_assert(CHAIN_PHASE_LINES == CHAIN_GROUPS + 1 + CHAIN_COPIES, "sync lines per phase");
+// kernel arguments are passed in a 4 KiB segment
+static_assert(sizeof(ChainArgs) <= 4096, "chain launch arguments");
+__device__ __forceinline__ unsigned* chain_count(unsigned* sync, int p, int g) {
+  return sync + 32 * (CHAIN_PHASE_LINES * p + g);
+}
 __device__ __forceinline__ unsigned* chain_ready(unsigned* sync, int p, int c) {
-  return sync + 32 * (33 * CHAIN_MAX_PHASES + CHAIN_COPIES * p + c);
+  return sync + 32 * (CHAIN_PHASE_LINES * p + CHAIN_GROUPS + 1 + c);
 }
 
 // Poll one copy of a ready flag until it reaches `epoch` (wrap-safe compare).
@@ -214,15 +220,46 @@ __device__ __forceinline__ void chain_phase(const ChainPhase& ph, int p, int id,
   chain_complete(p, rg, (int)W.nrg(), gsize, sync, epoch_v, lane);
 }
 
-// A DeltaNet layer's recurrent update as the chain's first phase (one decode
-// token): the separate kernel's workgroup body, with the output digits stored
-// coherently for the mixer output projection that follows in this kernel.
+// The wait of a DeltaNet update that follows another phase: thread 0 polls
+// the phase before's ready flag, and the workgroup learns the outcome at a
+// barrier.
+struct ChainWait {
+  static constexpr bool active = true;
+  const unsigned* flag;
+  unsigned epoch;
+  Ctrl* ctrl;
+  int* s_ok;
+  __device__ bool operator()() const {
+    if (threadIdx.x == 0) *s_ok = chain_wait(flag, epoch, ctrl) ? 1 : 0;
+    __syncthreads();
+    return *s_ok != 0;
+  }
+};
+
+// A DeltaNet layer's recurrent update (one decode token): the separate
+// kernel's workgroup body, with the output digits stored coherently for the
+// mixer output projection that follows in this kernel.  As the launch's
+// first phase it reads inputs written before the launch; after another phase
+// (the layer's input projections, earlier in the same launch) it requests
+// its state rows, waits for that phase, then reads the inputs coherently.
 // Each workgroup (a head's 32 state rows) counts as one row group once the
 // stores of all its waves have completed.
 template <int DKP>
 __device__ __forceinline__ void chain_dn_phase(const ChainArgs& args, int p, int id, unsigned* __restrict__ sync,
-                                               const unsigned& epoch_v) {
-  deltanet_rows<DKP, 1, true>(args.dn, 1, id);
+                                               Ctrl* __restrict__ ctrl, uint8_t* __restrict__ ws,
+                                               const unsigned& epoch_v, int* s_ok) {
+  const ChainPhase& ph = args.ph[p];
+  DnParams dn = args.dn;
+  dn.state = reinterpret_cast<float*>(ws + ph.y_off);
+  dn.next.xd = reinterpret_cast<int32_t*>(ws + ph.nd_off);
+  dn.next.xs = reinterpret_cast<float*>(ws + ph.ns_off);
+  if (p == 0) {
+    deltanet_rows<DKP, 1, true>(dn, 1, id);
+  } else {
+    const ChainWait w{chain_ready(sync, p - 1, blockIdx.x % CHAIN_COPIES), (unsigned)__builtin_amdgcn_readfirstlane(epoch_v),
+                      ctrl, s_ok};
+    if (!deltanet_rows<DKP, 1, true>(dn, 1, id, w)) return;
+  }
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
   __builtin_amdgcn_s_waitcnt(0);
   __atomic_signal_fence(__ATOMIC_SEQ_CST);
@@ -250,10 +287,10 @@ __global__ __launch_bounds__(256) void k_chain(const ChainArgs args, const uint8
   switch (args.ph[p].epi) {
     case EPI_DN:
       switch (args.dn_dkp) {
-        case 4: chain_dn_phase<4>(args, p, id, sync, epoch_v); break;
-        case 8: chain_dn_phase<8>(args, p, id, sync, epoch_v); break;
-        case 12: chain_dn_phase<12>(args, p, id, sync, epoch_v); break;
-        default: chain_dn_phase<16>(args, p, id, sync, epoch_v); break;
+        case 4: chain_dn_phase<4>(args, p, id, sync, ctrl, ws, epoch_v, &s_ok); break;
+        case 8: chain_dn_phase<8>(args, p, id, sync, ctrl, ws, epoch_v, &s_ok); break;
+        case 12: chain_dn_phase<12>(args, p, id, sync, ctrl, ws, epoch_v, &s_ok); break;
+        default: chain_dn_phase<16>(args, p, id, sync, ctrl, ws, epoch_v, &s_ok); break;
       }
       break;
     case EPI_STORE:
@@ -272,10 +309,10 @@ hipError_t launch_chain(int qt, const ChainArgs& args, unsigned grid, const uint
                         unsigned* sync, Ctrl* ctrl, hipStream_t s) {
   if (args.nph < 1 || args.nph > CHAIN_MAX_PHASES || grid == 0 || (int)grid != args.first_wg[args.nph])
     return hipErrorInvalidValue;
-  // a DeltaNet phase comes first (it waits for nothing), with one workgroup per 32 state rows
+  // a DeltaNet phase has one workgroup per 32 state rows
   for (int p = 0; p < args.nph; ++p)
     if (args.ph[p].epi == EPI_DN &&
-        (p != 0 || args.ph[p].nwg != args.dn.heads * (args.dn.dv / 32) || args.dn.dv % 32 ||
+        (args.ph[p].nwg != args.dn.heads * (args.dn.dv / 32) || args.dn.dv % 32 ||
          args.dn.dk != 8 * args.dn_dkp || (args.dn_dkp != 4 && args.dn_dkp != 8 && args.dn_dkp != 12 &&
                                            args.dn_dkp != 16) || args.dn.mode != DN_DECODE))
       return hipErrorInvalidValue;

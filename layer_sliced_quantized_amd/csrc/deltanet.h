@@ -37,8 +37,19 @@ __host__ __device__ inline size_t dn_off(int i, int j, int dkp) {
 // deltanet_rows is the body of one workgroup (block = head * dv / 32 + row
 // block), for at most TM tokens; COH makes the output digits coherent stores,
 // for a consumer inside the same kernel (the chained decode products).
-template <int DKP, int TM, bool COH>
-__device__ __forceinline__ void deltanet_rows(const DnParams& p, int T, int block) {
+//
+// With an active Wait (one token only) the inputs are written earlier in the
+// same kernel: the state rows are requested first, then wait() (uniform over
+// the workgroup; false: give up and return false), then the inputs are read
+// with coherent loads.  The arithmetic is the same either way.
+struct NoWait {
+  static constexpr bool active = false;
+  __device__ bool operator()() const { return true; }
+};
+template <int DKP, int TM, bool COH, class Wait = NoWait>
+__device__ __forceinline__ bool deltanet_rows(const DnParams& p, int T, int block, const Wait& wait = Wait{}) {
+  constexpr bool AFTER = Wait::active;
+  static_assert(!AFTER || TM == 1, "a waiting update takes one token");
   constexpr int DK = 8 * DKP;
   constexpr int NM = TM > 4 ? 4 : TM;   // tokens per wave
   __shared__ float qs[TM][DK], ksh[TM][DK];
@@ -60,21 +71,27 @@ __device__ __forceinline__ void deltanet_rows(const DnParams& p, int T, int bloc
   // loads; requested here they would hold up the slot index, so they follow
   // the state loads.)
   float q0[NM], q1[NM], k0[NM], k1[NM];
-#pragma unroll
-  for (int m = 0; m < NM; ++m) {
-    const int t = wave + 4 * m;
-    q0[m] = q1[m] = k0[m] = k1[m] = 0.0f;
-    if (t < T) {
-      const float* y = p.y + (size_t)t * p.y_stride;
-      if (lane < DK) { q0[m] = y[p.off_q + h * DK + lane]; k0[m] = y[p.off_k + h * DK + lane]; }
-      if (lane + 64 < DK) { q1[m] = y[p.off_q + h * DK + lane + 64]; k1[m] = y[p.off_k + h * DK + lane + 64]; }
-    }
-  }
   float v1 = 0.0f, z1 = 0.0f;
-  if (one) {
-    v1 = p.y[p.off_v + h * p.dv + i];
-    z1 = p.y[p.off_z + h * p.dv + i];
-  }
+  auto inputs = [&]() {
+#pragma unroll
+    for (int m = 0; m < NM; ++m) {
+      const int t = wave + 4 * m;
+      q0[m] = q1[m] = k0[m] = k1[m] = 0.0f;
+      if (t < T) {
+        const float* y = p.y + (size_t)t * p.y_stride;
+        if (lane < DK) { q0[m] = ld_<AFTER>(y + p.off_q + h * DK + lane); k0[m] = ld_<AFTER>(y + p.off_k + h * DK + lane); }
+        if (lane + 64 < DK) {
+          q1[m] = ld_<AFTER>(y + p.off_q + h * DK + lane + 64);
+          k1[m] = ld_<AFTER>(y + p.off_k + h * DK + lane + 64);
+        }
+      }
+    }
+    if (one) {
+      v1 = ld_<AFTER>(p.y + p.off_v + h * p.dv + i);
+      z1 = ld_<AFTER>(p.y + p.off_z + h * p.dv + i);
+    }
+  };
+  if constexpr (!AFTER) inputs();
 
   const int cur = p.ctrl ? p.ctrl->cur : 0;
   const size_t hs = (size_t)DK * p.dv;
@@ -86,6 +103,10 @@ __device__ __forceinline__ void deltanet_rows(const DnParams& p, int T, int bloc
   float S[DKP];
 #pragma unroll
   for (int jj = 0; jj < DKP; ++jj) S[jj] = S_in[sbase + (size_t)jj * 64];
+  if constexpr (AFTER) {
+    if (!wait()) return false;
+    inputs();
+  }
 
   // normalised q, k into LDS
 #pragma unroll
@@ -103,8 +124,8 @@ __device__ __forceinline__ void deltanet_rows(const DnParams& p, int T, int bloc
   // tokens tid / 32 and tid / 32 + 8, and the gates of token tid, go to LDS
   float a1 = 0.0f, b1 = 0.0f;
   if (one) {
-    a1 = sigmoidf_(p.a_scale * p.y[p.off_a + h] + p.a_bias);
-    b1 = sigmoidf_(p.b_scale * p.y[p.off_b + h]);
+    a1 = sigmoidf_(p.a_scale * ld_<AFTER>(p.y + p.off_a + h) + p.a_bias);
+    b1 = sigmoidf_(p.b_scale * ld_<AFTER>(p.y + p.off_b + h));
   } else {
 #pragma unroll
     for (int m = 0; m < 2; ++m) {
@@ -156,6 +177,7 @@ __device__ __forceinline__ void deltanet_rows(const DnParams& p, int T, int bloc
     if (p.u_out && lane < 32) p.u_out[(size_t)t * nv + h * p.dv + ib * 32 + lane] = uo;
     if (p.next.xd) put_digits<COH>(p.next, p.next_qt, t, blk, uo, lane < 32);
   }
+  return true;
 }
 
 }  // namespace slq

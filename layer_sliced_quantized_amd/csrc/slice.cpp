@@ -162,6 +162,11 @@ struct LayerLayout {
   int off_q = 0, off_k = 0, off_v = 0, off_a = 0, off_b = 0, off_z = 0, off_g = -1;
   size_t dn_conv_w = 0, dn_alog = 0, dn_dtb = 0, dn_normw = 0;   // qwen3_5-form DeltaNet vectors
   int dn_index = -1, attn_index = -1;
+  // chained decode: the digits this layer's phases hand on (the update's
+  // output, the FFN input, the SwiGLU output, the next mixer input), each
+  // layer its own so that a launch over several layers writes every digit
+  // buffer once
+  size_t cxu_d = 0, cxu_s = 0, cxa_d = 0, cxa_s = 0, cxm_d = 0, cxm_s = 0, cxb_d = 0, cxb_s = 0;
 };
 
 struct Layout {
@@ -182,7 +187,8 @@ struct Layout {
   // sync regions
   size_t xb_d = 0, xb_s = 0, ssq_b = 0, chain_sync = 0;
   size_t xe_d = 0, xe_s = 0, mtp_y = 0;   // draft head: input digits (2H wide) and projection
-  size_t cpart[CHAIN_MAX_PHASES] = {}, ccnt[CHAIN_MAX_PHASES] = {};
+  size_t cpart[CHAIN_PART_BUFS] = {}, ccnt[CHAIN_PART_BUFS] = {};
+  size_t chain_sync_bytes = 0;
   size_t ccnt_n = 0;      // u32 tickets in each ccnt region
   size_t kv_layer_bytes = 0, dn_layer_bytes = 0;
   size_t conv = 0, conv_layer_bytes = 0;   // qwen3_5-form DeltaNet conv states
@@ -390,11 +396,25 @@ Layout make_layout(const slice_config& c) {
                              std::make_pair(&ll.f1, &ll.pf1), std::make_pair(&ll.f2, &ll.pf2)})
         if (mp.first->present) cpf = std::max<size_t>(cpf, (size_t)((mp.first->rows + RG - 1) / RG) * mp.second->ks * RG);
     L.ccnt_n = (size_t)std::max<int64_t>(rg_max, 1);
-    for (int p = 0; p < CHAIN_MAX_PHASES; ++p) {
+    for (int p = 0; p < CHAIN_PART_BUFS; ++p) {
       L.cpart[p] = take(cpf * 4);
       L.ccnt[p] = take(L.ccnt_n * 4);
     }
-    L.chain_sync = take(L.layers.size() * CHAIN_MAX_PHASES * CHAIN_SYNC_BYTES);
+    // at most five phases per layer (update, mixer output, gate/up, down, next input projections)
+    L.chain_sync_bytes = L.layers.size() * 5 * CHAIN_PHASE_SYNC_BYTES;
+    L.chain_sync = take(L.chain_sync_bytes);
+    for (LayerLayout& ll : L.layers) {
+      ll.cxu_d = take((size_t)XW * 4 * nblkU);
+      ll.cxu_s = take((size_t)4 * nblkU);
+      ll.cxa_d = take((size_t)XW * 4 * nblkH);
+      ll.cxa_s = take((size_t)4 * nblkH);
+      if (nblkM) {
+        ll.cxm_d = take((size_t)XW * 4 * nblkM);
+        ll.cxm_s = take((size_t)4 * nblkM);
+      }
+      ll.cxb_d = take((size_t)XW * 4 * nblkH);
+      ll.cxb_s = take((size_t)4 * nblkH);
+    }
   }
   if (L.n_attn) {
     L.nchunk = (c.max_seq + ATT_CHUNK - 1) / ATT_CHUNK;
@@ -726,41 +746,82 @@ static int enqueue_step(slice* s, int T, int mode, hipStream_t st, Prof* prof = 
 #undef SLQ_MARK
 }
 
-// Descriptors of the chained products after each layer's mixer (decode, one
-// token): [mixer output (+ residual), gate/up + SwiGLU, down (+ residual),
-// next layer's input projections], with the launch shapes of the separate
-// kernels, so that results are the same bit for bit.  The mixer output writes
-// the FFN input's digits to xa (statistics in ssq), the down projection the
-// next mixer input's digits to xb (ssq_b): every buffer a chain hands on is
-// written once per launch.
+// Descriptors of the chained decode phases (one token), in step order: per
+// layer [DeltaNet update (DeltaNet layers, when chained), mixer output (+
+// residual), gate/up + SwiGLU, down (+ residual), next layer's input
+// projections], with the launch shapes of the separate kernels, so that
+// results are the same bit for bit.  A launch runs the phases of consecutive
+// layers up to the next layer whose mixer is a kernel of its own (attention,
+// or every mixer when the updates are not chained), at most CHAIN_MAX phases
+// (a layer whose phases do not fit starts the next launch).  Each layer's
+// phases hand on digits through buffers of its own (cxu, cxa, cxm, cxb), and
+// the statistics through ssq (FFN input) and ssq_b (next mixer input), so a
+// launch writes every digit buffer once.
 static void build_chains(slice* s) {
   const slice_config& c = s->cfg;
   const Layout& L = s->L;
   const int H = c.hidden, nblkH = H / QK;
   const int nlay = (int)L.layers.size();
   s->chain_launch.clear();
-  // products per chained kernel (tuning; 4 = all of a layer's)
+  // phases per chained kernel (tuning; CHAIN_MAX_PHASES at most)
   const int per = clampi(override_int("CHAIN_MAX", CHAIN_MAX_PHASES), 1, CHAIN_MAX_PHASES);
+  const int nblkU = (L.nu + QK - 1) / QK;
+  struct Step {
+    ChainPhase ph;
+    int layer;   // the layer whose step the phase belongs to (the next input projections: the layer before)
+  };
+  std::vector<Step> open;   // phases of the launch being built
+  size_t sync = L.chain_sync;
+  auto close = [&]() {
+    if (open.empty()) return;
+    slice::ChainLaunch cl{};
+    cl.layer = open[0].layer;
+    cl.args.nph = (int)open.size();
+    cl.args.first_wg[0] = 0;
+    int dn_layer = -1;
+    for (int k = 0; k < cl.args.nph; ++k) {
+      ChainPhase q = open[k].ph;
+      // split-K regions in turn: a phase runs only after the one before has
+      // completed, so phase k + CHAIN_PART_BUFS finds phase k's regions free
+      q.part_off = (int64_t)L.cpart[k % CHAIN_PART_BUFS];
+      q.cnt_off = (int64_t)L.ccnt[k % CHAIN_PART_BUFS];
+      cl.args.ph[k] = q;
+      cl.args.first_wg[k + 1] = cl.args.first_wg[k] + q.nwg;
+      const int nrg = (int)((q.rows + RG - 1) / RG);
+      cl.args.gsize[k] = (nrg + 31) / 32;   // at most 32 completion groups
+      if (q.epi == EPI_DN && dn_layer < 0) dn_layer = open[k].layer;
+    }
+    cl.grid = (unsigned)cl.args.first_wg[cl.args.nph];
+    if (dn_layer >= 0) {
+      // shared by the launch's updates; state and output digits come per phase
+      cl.args.dn = dn_params(s, dn_layer, 1, DN_DECODE);
+      cl.args.dn_dkp = c.dn_dk / 8;
+    }
+    cl.sync = sync;
+    sync += (size_t)cl.args.nph * CHAIN_PHASE_SYNC_BYTES;
+    s->chain_launch.push_back(cl);
+    open.clear();
+  };
   for (int i = 0; i < nlay; ++i) {
     const LayerLayout& ll = L.layers[i];
-    ChainPhase ph[CHAIN_MAX_PHASES];
-    int n = 0;
+    const bool dn_phase = s->chain_dn && !ll.attn;
+    // a mixer that runs as a kernel of its own comes between two launches
+    if (!dn_phase) close();
+    std::vector<ChainPhase> ph;
+    ph.reserve(5);   // add() hands out references into it
     auto add = [&](const Mat& m, const Plan& pl, int epi) -> ChainPhase& {
-      ChainPhase& q = ph[n];
-      q = ChainPhase{};
+      ChainPhase q{};
       q.w_off = (int64_t)m.off;
       q.rows = m.rows;
       q.cols = m.cols;
       q.ssq_off = q.y_off = q.nd_off = q.ns_off = q.ssq_out_off = q.norm_w_off = -1;
-      q.part_off = (int64_t)L.cpart[n % per];
-      q.cnt_off = (int64_t)L.ccnt[n % per];
       q.qt = c.qtype;
       q.ksplit = pl.ks;
       q.nwg = (int)((m.rows + RG - 1) / RG) * pl.ks;
       q.epi = epi;
       q.w = pl.w;
-      ++n;
-      return q;
+      ph.push_back(q);
+      return ph.back();
     };
     auto input = [&](ChainPhase& q, size_t d, size_t sc, int nblk, int64_t ssq) {
       q.xd_off = (int64_t)d;
@@ -780,65 +841,53 @@ static void build_chains(slice* s) {
       q.ssq_out_off = (int64_t)ssq_out;
       q.norm_w_off = (int64_t)norm_w;
     };
-    const int nblkU = (L.nu + QK - 1) / QK;
-    if (s->chain_dn && !ll.attn) {
+    if (dn_phase) {
       // the layer's DeltaNet update: one workgroup per 32 state rows of a head
-      ChainPhase& d = ph[n];
-      d = ChainPhase{};
+      ChainPhase d{};
       d.epi = EPI_DN;
       d.nwg = c.dn_heads * (c.dn_dv / 32);
       d.rows = (int64_t)d.nwg * RG;   // counted as nwg row groups
       d.ksplit = 1;
       d.w = 4;
       d.qt = c.qtype;
-      d.part_off = (int64_t)L.cpart[n % per];
-      d.cnt_off = (int64_t)L.ccnt[n % per];
-      d.xd_off = d.xs_off = d.ssq_off = d.y_off = d.nd_off = d.ns_off = d.ssq_out_off = d.norm_w_off = -1;
-      ++n;
+      d.xd_off = d.xs_off = d.ssq_off = d.ssq_out_off = d.norm_w_off = -1;
+      d.y_off = (int64_t)(L.dn + (size_t)ll.dn_index * L.dn_layer_bytes);
+      d.nd_off = (int64_t)ll.cxu_d;
+      d.ns_off = (int64_t)ll.cxu_s;
+      ph.push_back(d);
     }
     ChainPhase& g2 = add(ll.g2, ll.pg2, EPI_RESID);
-    input(g2, L.xu_d, L.xu_s, nblkU, -1);
+    // the update's digits, or the separate mixer's (written before the launch)
+    if (dn_phase) input(g2, ll.cxu_d, ll.cxu_s, nblkU, -1);
+    else input(g2, L.xu_d, L.xu_s, nblkU, -1);
     if (c.ffn) {
-      resid(g2, L.xa_d, L.xa_s, L.ssq, ll.ffn_norm);
+      resid(g2, ll.cxa_d, ll.cxa_s, L.ssq, ll.ffn_norm);
       ChainPhase& f1 = add(ll.f1, ll.pf1, EPI_SWIGLU);
-      input(f1, L.xa_d, L.xa_s, nblkH, (int64_t)L.ssq);
-      f1.nd_off = (int64_t)L.xm_d;
-      f1.ns_off = (int64_t)L.xm_s;
+      input(f1, ll.cxa_d, ll.cxa_s, nblkH, (int64_t)L.ssq);
+      f1.nd_off = (int64_t)ll.cxm_d;
+      f1.ns_off = (int64_t)ll.cxm_s;
       f1.n_nblk = c.ffn / QK;
       ChainPhase& f2 = add(ll.f2, ll.pf2, EPI_RESID);
-      input(f2, L.xm_d, L.xm_s, c.ffn / QK, -1);
-      resid(f2, L.xb_d, L.xb_s, L.ssq_b, attn_norm_off(s, i + 1));
+      input(f2, ll.cxm_d, ll.cxm_s, c.ffn / QK, -1);
+      resid(f2, ll.cxb_d, ll.cxb_s, L.ssq_b, attn_norm_off(s, i + 1));
     } else {
-      resid(g2, L.xb_d, L.xb_s, L.ssq_b, attn_norm_off(s, i + 1));
+      resid(g2, ll.cxb_d, ll.cxb_s, L.ssq_b, attn_norm_off(s, i + 1));
     }
     if (i + 1 < nlay) {
       const LayerLayout& nx = L.layers[i + 1];
       ChainPhase& g1 = add(nx.g1, nx.pg1, EPI_STORE);
-      input(g1, L.xb_d, L.xb_s, nblkH, (int64_t)L.ssq_b);
+      input(g1, ll.cxb_d, ll.cxb_s, nblkH, (int64_t)L.ssq_b);
       g1.y_off = (int64_t)L.y1;
       g1.y_tstride = nx.g1.rows;
     }
-    for (int first = 0; first < n; first += per) {
-      slice::ChainLaunch cl{};
-      cl.layer = i;
-      cl.args.nph = std::min(per, n - first);
-      cl.args.first_wg[0] = 0;
-      for (int k = 0; k < cl.args.nph; ++k) {
-        const ChainPhase& q = ph[first + k];
-        cl.args.ph[k] = q;
-        cl.args.first_wg[k + 1] = cl.args.first_wg[k] + q.nwg;
-        const int nrg = (int)((q.rows + RG - 1) / RG);
-        cl.args.gsize[k] = (nrg + 31) / 32;   // at most 32 completion groups
-      }
-      cl.grid = (unsigned)cl.args.first_wg[cl.args.nph];
-      if (!ll.attn && s->chain_dn) {
-        cl.args.dn = dn_params(s, i, 1, DN_DECODE);
-        cl.args.dn_dkp = c.dn_dk / 8;
-      }
-      cl.sync = L.chain_sync + ((size_t)i * CHAIN_MAX_PHASES + first / per) * CHAIN_SYNC_BYTES;
-      s->chain_launch.push_back(cl);
+    // a layer whose phases do not fit the open launch starts the next one
+    if (open.size() + ph.size() > (size_t)per) close();
+    for (const ChainPhase& q : ph) {
+      if (open.size() == (size_t)per) close();
+      open.push_back(Step{q, i});
     }
   }
+  close();
 }
 
 // Chained decode needs every product's plan within the chain kernel's four
@@ -1365,10 +1414,10 @@ int slice_reset(slice_t* s, int kv_len, void* stream) {
   if (kv_len < 0 || (s->L.n_attn && kv_len > s->cfg.max_seq)) return fail(SLICE_ERANGE, "kv_len out of range");
   HIPCHK(launch_ctrl_set(s->ctrl(), kv_len, s->cur, S(stream)));
   if (s->chain) {
-    HIPCHK(launch_chain_reset(reinterpret_cast<unsigned*>(s->ws + s->L.chain_sync),
-                              s->L.layers.size() * CHAIN_MAX_PHASES * CHAIN_SYNC_BYTES / 4, s->ctrl(), S(stream)));
+    HIPCHK(launch_chain_reset(reinterpret_cast<unsigned*>(s->ws + s->L.chain_sync), s->L.chain_sync_bytes / 4,
+                              s->ctrl(), S(stream)));
     // split-K tickets of the chained products (zero unless a wait gave up mid-exchange)
-    for (int p = 0; p < CHAIN_MAX_PHASES; ++p)
+    for (int p = 0; p < CHAIN_PART_BUFS; ++p)
       HIPCHK(launch_fill_zero_u32(reinterpret_cast<uint32_t*>(s->ws + s->L.ccnt[p]), s->L.ccnt_n, S(stream)));
   }
   s->pos = kv_len;

@@ -194,18 +194,26 @@ hipError_t launch_state_io(float* state, int nslots, const Ctrl* ctrl, int heads
                            float* canon, int to_device, hipStream_t s);
 
 // ------------------------------------------------------- chained single-token GEMVs
-// One kernel runs up to CHAIN_MAX_PHASES dependent phases of a decode step: a
-// DeltaNet layer's recurrent update (EPI_DN), its mixer output projection,
-// the gate/up projection, the down projection, the next layer's input
-// projections.  A GEMV phase's workgroups first load their first weight tile,
-// then wait until every row group of the phase before has finished, then
-// compute exactly what the separate kernel computes (chain.hip).
-constexpr int CHAIN_MAX_PHASES = 5;
-// per chain launch: 33 counter lines and 64 ready-flag lines per product
-constexpr int CHAIN_SYNC_BYTES = (33 + 64) * CHAIN_MAX_PHASES * 128;
+// One kernel runs up to CHAIN_MAX_PHASES dependent phases of a decode step,
+// in step order and across layers: a DeltaNet layer's recurrent update
+// (EPI_DN), its mixer output projection, the gate/up projection, the down
+// projection, the next layer's input projections, then the next DeltaNet
+// layer's update, and so on.  A phase's workgroups first request what does
+// not depend on the phase before (a GEMV its first weight tile, an update
+// its state rows), then wait until every row group of the phase before has
+// finished, then compute exactly what the separate kernel computes
+// (chain.hip).
+constexpr int CHAIN_MAX_PHASES = 20;
+// split-K partial and ticket regions, taken in turn by the phases of a launch
+constexpr int CHAIN_PART_BUFS = 5;
+// per phase of a chain launch: 33 counter lines, then 64 ready-flag lines
+constexpr int CHAIN_PHASE_LINES = 33 + 64;
+constexpr int CHAIN_PHASE_SYNC_BYTES = CHAIN_PHASE_LINES * 128;
 struct ChainPhase {   // one GEMV of the chain; lives in device memory
   // every location is a byte offset: weights and norm weights into the
-  // weights buffer, everything else into the workspace
+  // weights buffer, everything else into the workspace.  EPI_DN: y_off is
+  // the layer's state (slot 0), nd_off / ns_off its output digits; the rest
+  // of the update's parameters come from ChainArgs::dn
   int64_t w_off, rows, cols;          // packed matrix
   int64_t xd_off, xs_off;             // input digits and their block scales
   int64_t ssq_off;                    // RMSNorm partial sums of the input (-1: none)
@@ -230,14 +238,16 @@ struct ChainArgs {
   int nph;
   int first_wg[CHAIN_MAX_PHASES + 1];   // workgroup index where product p starts; [nph] = grid
   int gsize[CHAIN_MAX_PHASES];          // row groups per completion group of product p
-  DnParams dn;                          // the EPI_DN phase: one decode token (T = 1)
+  DnParams dn;                          // the EPI_DN phases: one decode token (T = 1); state and
+                                        // output digits per phase (ChainPhase)
   int dn_dkp;                           // its d_k / 8
 };
-// sync region of one chain launch (CHAIN_SYNC_BYTES, zero before its first
-// launch), each counter and flag in its own 128-byte line (u32 index):
-//   [32 (33 p + g)], g < 32: row groups of group g of product p finished (over
+// sync region of one chain launch (nph * CHAIN_PHASE_SYNC_BYTES, zero before
+// its first launch), each counter and flag in its own 128-byte line (u32
+// index), in block p = 32 * CHAIN_PHASE_LINES * p of product p:
+//   [block + 32 g], g < 32: row groups of group g of product p finished (over
 //                    all launches); g = 32: groups of product p finished;
-//   [32 (33 CHAIN_MAX_PHASES + 64 p + c)]: copy c of product p's ready flag, the last launch
+//   [block + 32 (33 + c)]: copy c of product p's ready flag, the last launch
 //                    (1, 2, ...) whose product p is complete.
 hipError_t launch_chain(int qt, const ChainArgs& args, unsigned grid, const uint8_t* weights, uint8_t* ws,
                         unsigned* sync, Ctrl* ctrl, hipStream_t s);

@@ -124,6 +124,11 @@ SHAPES = {
     "attention_layer": [(10, 4), (68, 2), (10, 8), (32, 4)],
     "last_layer": [(10, 4), (68, 2), (10, 8)],
     "no_ffn": [(3, 1), (5, 2)],
+    # a launch over a run of DeltaNet layers: each layer's update waits for the
+    # input projections before it, in the same launch
+    "three_deltanet_layers": [(16, 1), (10, 4), (68, 2), (10, 8), (33, 4)] * 3,
+    "attention_then_deltanet_layers": [(10, 4), (68, 2), (10, 8), (33, 4)] +
+                                      [(16, 1), (10, 4), (68, 2), (10, 8), (33, 4)] * 3,
     "many_row_groups": [(70, 1), (300, 2), (33, 3)],
 }
 

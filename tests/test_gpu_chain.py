@@ -2,7 +2,8 @@
 
 Decode runs each layer's DeltaNet update (in DeltaNet layers) and the products
 after its mixer (mixer output, gate/up + SwiGLU, down, the next layer's input
-projections) as one kernel whose workgroups wait for the phase before theirs.  With the same launch shapes
+projections) in kernels whose workgroups wait for the phase before theirs; one
+launch runs the phases of consecutive layers up to the next attention layer.  With the same launch shapes
 as the separate GEMV kernels, the results must be the same bits; they are
 also checked against the CPU oracle, and slice_sync_check must report no
 wait that gave up.
@@ -105,11 +106,14 @@ def test_chain_with_verify_and_graph_replays(ovr):
     b.sync_check()
 
 
-@pytest.mark.parametrize("extra", [{"CHAIN_DN": 0}, {"CHAIN_MAX": 2}, {"CHAIN_MAX": 1}],
-                         ids=["deltanet_own_kernel", "two_phases_per_launch", "one_phase_per_launch"])
+@pytest.mark.parametrize("extra", [{"CHAIN_DN": 0}, {"CHAIN_MAX": 5}, {"CHAIN_MAX": 2}, {"CHAIN_MAX": 1}],
+                         ids=["deltanet_own_kernel", "one_layer_per_launch", "two_phases_per_launch",
+                              "one_phase_per_launch"])
 def test_chain_variants_equal_separate_kernels(extra, ovr):
-    """The DeltaNet update as its own kernel, or the layer's phases spread over
-    several launches (the DeltaNet phase then alone in its launch): the same
-    bits as separate kernels, states included."""
+    """The DeltaNet update as its own kernel, one layer's phases per launch
+    (the update first, waiting for nothing), or the layer's phases spread over
+    several launches: the same bits as separate kernels, states included.  (By
+    default one launch runs all three DeltaNet layers, each update waiting for
+    the input projections before it.)"""
     ovr(**extra)
     _compare(TINY_H, synth.Q4_0, 0, 4, ovr, 4, 99, [0, 1, 2], 3, prefill=20, max_seq=128, max_verify=4)
