@@ -9,8 +9,9 @@ fresh N(0,1) fp16 hidden state per step, as a middle pipeline stage receives
 it.  One step = one token through all 64 layers (one HIP graph launch).
 
 Printed JSON (one line on stdout): decode tok/s; the roofline of the dominant
-kernel (the chained products of each layer: mixer output, RMSNorm + gate/up +
-SwiGLU, down + residual, next layer's input projections, one launch per layer,
+kernel (the chained phases of the layers: DeltaNet state update, mixer
+output, RMSNorm + gate/up + SwiGLU, down + residual, next layer's input
+projections, one launch per run of layers up to the next attention layer,
 timed with HIP events) and of the whole step; the measured streaming-read
 ceiling; the CPU oracle timed on a bounded sample (all cores and one thread);
 each GEMV timed as its own kernel; the DeltaNet and attention kernels on
@@ -54,7 +55,7 @@ def chain_source_hash() -> str:
 def profiled_traffic():
     """HBM bytes per launch of the chained-products kernel from the committed
     PMC summary (FETCH_SIZE and WRITE_SIZE scaled by a known-size copy, mean
-    over the 64 layers' launches), or None when the kernel sources changed
+    over the launches of whole decode steps), or None when the kernel sources changed
     after the counters were taken."""
     try:
         text = open(TRAFFIC_PROFILE).read()
@@ -256,8 +257,9 @@ def profile_ops(s, H, n):
 
 
 def time_gemv_op(s, op, reps):
-    """Mean duration of one GEMV op kind: HIP events on the launch stream around
-    reps x (one launch per layer), back to back, on the last step's activations."""
+    """Duration of one pass of a GEMV op kind over the slice (one launch per
+    layer; for "chain", the step's chained launches): HIP events on the launch
+    stream around reps passes, back to back, on the last step's activations."""
     import torch
     s.run_gemv_op(op)
     torch.cuda.synchronize()

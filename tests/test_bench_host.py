@@ -2,6 +2,7 @@
 the PMC traffic figure is reported only for the kernel sources it was
 measured on."""
 import os
+import re
 import subprocess
 import sys
 
@@ -55,6 +56,8 @@ def test_traffic_of_the_committed_profile():
     t = bench.profiled_traffic()
     if t is None:
         pytest.skip("the chained-products kernel sources changed after its PMC traffic was taken")
-    alg = bench.chain_step_bytes(synth.HYBRID_5120, synth.Q4_0, deltanet="DeltaNet" in open(bench.TRAFFIC_PROFILE).read()) / 64
+    text = open(bench.TRAFFIC_PROFILE).read()
+    launches = int(re.search(r"launches_per_step: (\d+)", text).group(1))
+    alg = bench.chain_step_bytes(synth.HYBRID_5120, synth.Q4_0, deltanet="DeltaNet" in text) / launches
     # measured HBM bytes per launch against the algorithmic bytes: no re-read of weights
     assert 0.99 * alg <= t <= 1.05 * alg
