@@ -101,13 +101,73 @@ __device__ __forceinline__ void head_prep(float (&x)[NC], const AttnParams& p, c
   }
 }
 
+// Values of a 32-row chunk.  Thread (dim group vg = tid / 8, row quarter vq =
+// tid % 8) holds dims 8 vg .. 8 vg + 7 of rows 4 vq .. 4 vq + 3: four 16-byte
+// loads, one per row (a wave's load covers 8 rows x 64 dims, 8 whole lines).
+__device__ __forceinline__ void v_request(const AttnParams& p, int g, int r0, int hd, uint4 (&vw)[4]) {
+  const int vg = (int)threadIdx.x >> 3, vq = (int)threadIdx.x & 7;
+  const __half* base = p.vc + ((size_t)g * p.max_seq + r0 + 4 * vq) * hd + 8 * (8 * vg < hd ? vg : 0);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) vw[j] = *reinterpret_cast<const uint4*>(base + (size_t)j * hd);
+}
+// fp32 values; rows at or past nvmax (past the pass's last position) are 0
+__device__ __forceinline__ void v_convert(const uint4 (&vw)[4], int nvmax, float (&vf)[4][8]) {
+  const int vq = (int)threadIdx.x & 7;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t w4[4] = {vw[j].x, vw[j].y, vw[j].z, vw[j].w};
+    const bool ok = 4 * vq + j < nvmax;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      vf[j][2 * e] = ok ? __half2float(__ushort_as_half((unsigned short)(w4[e] & 0xffff))) : 0.0f;
+      vf[j][2 * e + 1] = ok ? __half2float(__ushort_as_half((unsigned short)(w4[e] >> 16))) : 0.0f;
+    }
+  }
+}
+// The dimension whose chunk sum this thread ends with in pv_sum.
+__device__ __forceinline__ int pv_dim() {
+  const int t = (int)threadIdx.x;
+  return 8 * (t >> 3) + 4 * (t & 1) + 2 * ((t >> 1) & 1) + ((t >> 2) & 1);
+}
+// P V of one (token, head) over a chunk: this thread's 8 dims over its 4 rows
+// (weights w[4 vq .. 4 vq + 3]), then the 8 row quarters of a dim group (lanes
+// l ^ 1, l ^ 2, l ^ 4) are summed in three exchange steps, each lane handing
+// on half of its sums and keeping the other half, so that lane l ends with
+// the whole sum of dim pv_dim().  A fixed order: the same bits wherever it runs.
+__device__ __forceinline__ float pv_sum(const float* w, const float (&vf)[4][8]) {
+  const int t = (int)threadIdx.x;
+  const float4 p4 = *reinterpret_cast<const float4*>(w + 4 * (t & 7));
+  float o[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    float x = p4.x * vf[0][e];
+    x = __builtin_fmaf(p4.y, vf[1][e], x);
+    x = __builtin_fmaf(p4.z, vf[2][e], x);
+    o[e] = __builtin_fmaf(p4.w, vf[3][e], x);
+  }
+  const bool b0 = t & 1, b1 = t & 2, b2 = t & 4;
+  float a[4], b[2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {   // keep dims 4 b0 + i
+    const float send = b0 ? o[i] : o[4 + i];
+    a[i] = (b0 ? o[4 + i] : o[i]) + xor_lane<1>(send);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {   // keep dims 4 b0 + 2 b1 + i
+    const float send = b1 ? a[i] : a[2 + i];
+    b[i] = (b1 ? a[2 + i] : a[i]) + xor_lane<2>(send);
+  }
+  const float send = b2 ? b[0] : b[1];
+  return (b2 ? b[1] : b[0]) + xor_lane<4>(send);
+}
+
 // One workgroup per (KV head g, group of GRP of its query heads, range of cpw
 // consecutive 32-row chunks), 4 waves, for all T (<= TM) tokens of the pass:
 //   1. the pass's K/V rows that fall in the range are prepared (wave w takes
 //      tokens w, w + 4, ...) and appended to the cache;
 //   2. the first chunk's keys (thread (row rr = tid / 8, part = tid % 8): an
-//      eighth of the head dimensions of key row rr) and values (thread =
-//      dimension) are requested;
+//      eighth of the head dimensions of key row rr) and values (v_request: 8
+//      dims of 4 rows per thread) are requested;
 //   3. every (token, query head) that reaches the range is prepared into LDS
 //      once (wave w takes pairs w, w + 4, ...) while those loads are in flight;
 //   then chunk after chunk, with the next chunk's keys and values requested
@@ -115,8 +175,8 @@ __device__ __forceinline__ void head_prep(float (&x)[NC], const AttnParams& p, c
 //   4. scores for every (token, head): the eight parts meet in three butterfly
 //      steps; then one wave per (token, head) takes the chunk max, the
 //      weights exp(s - max) and their sum;
-//   5. P V per (token, head): one thread per dimension over the chunk's rows,
-//      written as the chunk's partial.
+//   5. P V per (token, head) (pv_sum: each dimension's sum ends in one
+//      thread), merged into the range's output.
 // Each chunk's (max, sum, P V) is computed by exactly the operations of
 // k_attn_split below.  The chunks of a range are then merged in order into
 // one partial per (token, head): M' = max(M, m_c), L = L e^(M - M') + l_c
@@ -199,21 +259,18 @@ __global__ __launch_bounds__(256) void k_attn_split_range(AttnParams p, int T, i
     }
   }
 
-  // 2. the first chunk's keys (this thread's eighth of row rr) and values
-  // (dimension tid of every row); rows past the pass's last position lie
-  // inside the cache, get weight 0 and a value of 0
+  // 2. the first chunk's keys (this thread's eighth of row rr) and values (8
+  // dims of 4 rows); rows past the pass's last position lie inside the cache,
+  // get weight 0 and a value of 0
   const int rr = tid >> 3, part = tid & 7;
   uint4 kw[NC];
-  unsigned short vv[C];
+  uint4 vw[4];
   auto request = [&](int c) {
     const int r = c * C + rr;
 #pragma unroll
     for (int i = 0; i < NC; ++i)
       kw[i] = *reinterpret_cast<const uint4*>(p.kc + kidx(g, r, (part * NC + i) * 8, p.max_seq, HD));
-    const unsigned short* vrow =
-        reinterpret_cast<const unsigned short*>(p.vc) + ((size_t)g * p.max_seq + c * C) * HD + (dact ? tid : 0);
-#pragma unroll
-    for (int q = 0; q < C; ++q) vv[q] = vrow[(size_t)q * HD];
+    v_request(p, g, c * C, HD, vw);
   };
   request(cb);
 
@@ -271,9 +328,8 @@ __global__ __launch_bounds__(256) void k_attn_split_range(AttnParams p, int T, i
         kf[i][2 * e + 1] = __half2float(__ushort_as_half((unsigned short)(ws[e] >> 16)));
       }
     }
-    float vf[C];
-#pragma unroll
-    for (int q = 0; q < C; ++q) vf[q] = q < nvmax ? __half2float(__ushort_as_half(vv[q])) : 0.0f;
+    float vf[4][8];
+    v_convert(vw, nvmax, vf);
     if (c + 1 < ce) request(c + 1);
     const int tq = max(0, r0 - p0);
     const int npair = (T - tq) * GRP;
@@ -327,22 +383,14 @@ __global__ __launch_bounds__(256) void k_attn_split_range(AttnParams p, int T, i
     }
     __syncthreads();
 
-    // 5. P V, merged into the range's output
+    // 5. P V, merged into the range's output (this thread: dim pv_dim())
     if (dact) {
 #pragma unroll
       for (int t = 0; t < TM; ++t) {
         if (t < tq || t >= T) continue;
 #pragma unroll
         for (int h = 0; h < GRP; ++h) {
-          float o = 0.0f;
-#pragma unroll
-          for (int q = 0; q < C; q += 4) {
-            const float4 w = *reinterpret_cast<const float4*>(&pl[t][h][q]);
-            o = __builtin_fmaf(w.x, vf[q], o);
-            o = __builtin_fmaf(w.y, vf[q + 1], o);
-            o = __builtin_fmaf(w.z, vf[q + 2], o);
-            o = __builtin_fmaf(w.w, vf[q + 3], o);
-          }
+          const float o = pv_sum(pl[t][h], vf);
           orun[t][h] = __builtin_fmaf(orun[t][h], fac[t][h][0], o * fac[t][h][1]);
         }
       }
@@ -358,7 +406,7 @@ __global__ __launch_bounds__(256) void k_attn_split_range(AttnParams p, int T, i
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
         float* dst = p.part + (((size_t)t * p.q_heads + h0 + h) * p.nchunk + rng) * (HD + 2);
-        dst[2 + tid] = orun[t][h];
+        dst[2 + pv_dim()] = orun[t][h];
         if (tid == 0) { dst[0] = run[t][h][0]; dst[1] = run[t][h][1]; }
       }
     }
@@ -370,14 +418,14 @@ __global__ __launch_bounds__(256) void k_attn_split_range(AttnParams p, int T, i
 //   1. the pass's K/V rows that fall in the chunk are prepared (wave w takes
 //      tokens w, w + 4, ...) and appended to the cache;
 //   2. the chunk's keys (thread (row rr = tid / 8, part = tid % 8): an eighth
-//      of the head dimensions of key row rr) and values (thread = dimension)
-//      are requested once;
+//      of the head dimensions of key row rr) and values (v_request: 8 dims of
+//      4 rows per thread) are requested once;
 //   3. every (token, query head) is prepared into LDS (wave w takes pairs w,
 //      w + 4, ...) while those loads are in flight;
 //   4. scores for every (token, head): the eight parts meet in three butterfly
 //      steps; then one wave per (token, head) takes the chunk max, the
 //      weights exp(s - max) and their sum;
-//   5. P V per (token, head): one thread per dimension over the chunk's rows.
+//   5. P V per (token, head) (pv_sum: each dimension's sum ends in one thread).
 // Four workgroup barriers in all, whatever T.  Every group of query heads of
 // the chunk appends the same rows itself (the same bits), so each reads them
 // back after its own stores.
@@ -446,10 +494,10 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
     __syncthreads();
   }
 
-  // 2. the chunk's keys (this thread's eighth of row rr) and values
-  // (dimension tid of every row) are requested now and converted after the
-  // queries are prepared; rows past the pass's last position lie inside the
-  // cache, get weight 0 and a value of 0
+  // 2. the chunk's keys (this thread's eighth of row rr) and values (8 dims
+  // of 4 rows) are requested now and converted after the queries are
+  // prepared; rows past the pass's last position lie inside the cache, get
+  // weight 0 and a value of 0
   const int rr = tid >> 3, part = tid & 7;
   const int r = r0 + rr;
   uint4 kw[NC];
@@ -457,13 +505,8 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   for (int i = 0; i < NC; ++i)
     kw[i] = *reinterpret_cast<const uint4*>(p.kc + kidx(g, r, (part * NC + i) * 8, p.max_seq, HD));
   const int nvmax = min(C, p0 + T - r0);   // rows valid for the pass's last token
-  unsigned short vv[C];
-  {
-    const unsigned short* vrow =
-        reinterpret_cast<const unsigned short*>(p.vc) + ((size_t)g * p.max_seq + r0) * HD + (dact ? tid : 0);
-#pragma unroll
-    for (int q = 0; q < C; ++q) vv[q] = vrow[(size_t)q * HD];
-  }
+  uint4 vw[4];
+  v_request(p, g, r0, HD, vw);
 
   // 3. queries of tokens tq.. (those whose position reaches this chunk):
   // pair q = (t - tq) GRP + h, wave w takes pairs w + 4 m, all its loads first
@@ -506,9 +549,8 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
       kf[i][2 * e + 1] = __half2float(__ushort_as_half((unsigned short)(ws[e] >> 16)));
     }
   }
-  float vf[C];
-#pragma unroll
-  for (int q = 0; q < C; ++q) vf[q] = q < nvmax ? __half2float(__ushort_as_half(vv[q])) : 0.0f;
+  float vf[4][8];
+  v_convert(vw, nvmax, vf);
 
   // 4. scores, then per (token, head) the max, weights and their sum
   for (int t = tq; t < T; ++t) {
@@ -550,22 +592,14 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
   }
   __syncthreads();
 
-  // 5. P V
+  // 5. P V (this thread: dim pv_dim())
   if (dact) {
     for (int t = tq; t < T; ++t) {
 #pragma unroll
       for (int h = 0; h < GRP; ++h) {
-        float o = 0.0f;
-#pragma unroll
-        for (int q = 0; q < C; q += 4) {
-          const float4 w = *reinterpret_cast<const float4*>(&pl[t][h][q]);
-          o = __builtin_fmaf(w.x, vf[q], o);
-          o = __builtin_fmaf(w.y, vf[q + 1], o);
-          o = __builtin_fmaf(w.z, vf[q + 2], o);
-          o = __builtin_fmaf(w.w, vf[q + 3], o);
-        }
+        const float o = pv_sum(pl[t][h], vf);
         float* dst = p.part + (((size_t)t * p.q_heads + h0 + h) * p.nchunk + c) * (HD + 2);
-        dst[2 + tid] = o;
+        dst[2 + pv_dim()] = o;
         if (tid == 0) { dst[0] = ml[t][h][0]; dst[1] = ml[t][h][1]; }
       }
     }
