@@ -186,13 +186,14 @@ def mixer_kernels(seed, reps=100):
     return out
 
 
-def q35_deltanet(seed, threads, steps=20):
+def q35_deltanet(seed, threads, chain_dn_restore=-1, steps=20):
     """The qwen3_5 form of the DeltaNet layers (k_deltanet_q35: causal conv +
     SiLU, 16 query/key heads for 32 value heads of 128 x 128, softplus decay,
     gated RMSNorm) against the synthetic form (k_deltanet), each as its own
     kernel in eager decode steps of layers 0..3 of the hidden-5120 hybrid (3
     DeltaNet layers, 1 attention) with HIP events at every op boundary (times
-    include the dispatch gap)."""
+    include the dispatch gap).  The CHAIN_DN override is set back to
+    chain_dn_restore (-1: removed) afterwards."""
     import dataclasses
     import torch
     import synth
@@ -201,8 +202,10 @@ def q35_deltanet(seed, threads, steps=20):
     for name, base in (("qwen3_5", synth.HYBRID_5120_Q35), ("synthetic", synth.HYBRID_5120)):
         shape = dataclasses.replace(base, n_layers=4)
         slq.debug_override("CHAIN_DN", 0)   # the synthetic form's update as its own kernel too
-        s, _ = build_slice(shape, synth.Q4_0, PREFILL + 64, 4, seed, threads)
-        slq.debug_override("CHAIN_DN", 1)
+        try:
+            s, _ = build_slice(shape, synth.Q4_0, PREFILL + 64, 4, seed, threads)
+        finally:
+            slq.debug_override("CHAIN_DN", chain_dn_restore)
         H = torch.from_numpy(synth.hidden_inputs(seed, synth.WL_SLICE, steps + 2, shape.hidden)).cuda()
         o = torch.empty(shape.hidden, dtype=torch.float16, device="cuda")
         for i in range(2):
@@ -695,7 +698,8 @@ def main() -> int:
         log(f"read ceiling {extra['read_ceiling']}")
     if not args.no_mixers:
         extra["mixer_kernels"] = mixer_kernels(args.seed)
-        extra["mixer_kernels"]["deltanet_qwen3_5_form"] = q35_deltanet(args.seed, threads)
+        extra["mixer_kernels"]["deltanet_qwen3_5_form"] = q35_deltanet(args.seed, threads,
+                                                                       0 if args.no_chain_dn else -1)
         log(f"qwen3_5-form DeltaNet: {extra['mixer_kernels']['deltanet_qwen3_5_form']}")
     # ---- decode attention at three KV lengths
     if not args.no_attn_sweep:
