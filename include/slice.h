@@ -346,9 +346,10 @@ enum {
     SLICE_OP_FFN_IN = 7,     /* RMSNorm + fused gate/up projection + SwiGLU (GEMV)    */
     SLICE_OP_FFN_OUT = 8,    /* down projection + residual (GEMV)                     */
     SLICE_OP_EXIT = 9,       /* boundary vector out                                   */
-    SLICE_OP_CHAIN = 10      /* one layer's products after its mixer, chained in one
-                                kernel: mixer output + residual, gate/up + SwiGLU,
-                                down + residual, next layer's input projections    */
+    SLICE_OP_CHAIN = 10      /* one chained kernel: the phases of consecutive layers
+                                up to the next attention layer (DeltaNet update,
+                                mixer output + residual, gate/up + SwiGLU, down +
+                                residual, next layer's input projections)          */
 };
 
 /* Measurement (the pages' engine ships tok/s harnesses and a kernel-family
@@ -438,10 +439,10 @@ int slice_head_argmax(slice_t *s, const void *hid_in_dev, int32_t *tok_dev,
  * argument is NULL.  */
 int slice_mtp_input(slice_t *s, const int32_t *tok_dev, const void *hid_in_dev, void *x_out_dev, void *stream);
 
-/* Decode steps run each layer's products after its mixer as one kernel whose
- * workgroups wait, with a bounded wait, for the product before theirs (the
- * pages' engine submits one command buffer per token: SwarmLLM README,
- * engine paragraph).  Synchronises `stream`, then returns SLICE_EHIP if such
+/* Decode steps run the products and DeltaNet updates of consecutive layers as
+ * one kernel whose workgroups wait, with a bounded wait, for the phase before
+ * theirs (the pages' engine submits one command buffer per token: SwarmLLM
+ * README, engine paragraph).  Synchronises `stream`, then returns SLICE_EHIP if such
  * a wait gave up since the last slice_reset (the step's outputs are then
  * invalid), else SLICE_OK. */
 int slice_sync_check(slice_t *s, void *stream);

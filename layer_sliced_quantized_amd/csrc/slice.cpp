@@ -482,7 +482,7 @@ struct slice {
   Packed packed(const Mat& m) const { return Packed{w + m.off, m.rows, m.cols, cfg.qtype}; }
   int mx_min_t = 0;   // GEMVs with at least this many tokens use the MFMA products (0: by format and plan)
   bool chain = false;                 // decode steps run the chained GEMV kernels
-  bool chain_dn = false;              // ... with each DeltaNet layer's update as their first phase
+  bool chain_dn = false;              // ... with each DeltaNet layer's update as a phase
   struct ChainLaunch {
     int layer;                        // the layer whose mixer it follows
     ChainArgs args;                   // descriptors (kernel arguments)
