@@ -72,7 +72,10 @@ bool override_name_ok(const std::string& n) {
 //   down projection (5120 x 17408):         ks 8, w 4
 //   mixer output (5120 x 4096 / 6144):      ks 4, w 4
 // (one token: within 1 % of the best shape for every kind; at most 4 waves
-// per workgroup also lets a verify pass of 4 tokens use the MFMA products)
+// per workgroup also lets a verify pass of 4 tokens use the MFMA products).
+// Q8_0 input projections take 2 splits: their tiles carry twice the bytes
+// (64-layer Q8_0 slice in chained decode: 182.4 against 180.5 tok/s with 4,
+// 169.7 with 1).
 // Other shapes: enough splits for ~1000 workgroups, about two tiles per wave,
 // at most 4 waves per workgroup.
 // Overrides KS_<kind> / W_<kind> (kinds G1, G2, F1, F2, HEAD, GEMV) through
@@ -88,7 +91,7 @@ int clampi(int v, int lo, int hi) { return v < lo ? lo : v > hi ? hi : v; }
 // MFMA_MIN_T sets a fixed count instead.
 int mfma_min_tokens() { return clampi(override_int("MFMA_MIN_T", 0), 0, MAX_T + 1); }
 
-Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
+Plan plan_gemv(const char* kind, int64_t rows, int64_t cols, int qt = QT_Q4) {
   const int nrg = (int)((rows + RG - 1) / RG);
   const int ntiles = (int)((cols / QK + TB - 1) / TB);
   const std::string k(kind);
@@ -100,7 +103,7 @@ Plan plan_gemv(const char* kind, int64_t rows, int64_t cols) {
   } else {
     p.ks = clampi((1024 + nrg - 1) / nrg, 1, ntiles < 16 ? ntiles : 16);
     if (k == "F1") p.ks = clampi(p.ks, 1, 2);
-    if (k == "F2" || k == "G1") p.ks = clampi(p.ks, 1, k == "F2" ? 8 : 4);
+    if (k == "F2" || k == "G1") p.ks = clampi(p.ks, 1, k == "F2" ? 8 : qt == QT_Q8 ? 2 : 4);
     // at most 4 waves: one token is as fast as with 8 (LM head 248320 x 5120:
     // 114.8 against 115.1 us) and the batched products fit and stream longer
     // per wave (16 tokens: 474 against 874 us)
@@ -358,7 +361,7 @@ Layout make_layout(const slice_config& c) {
   size_t part_floats = 0;
   auto upd = [&](const Mat& m, Plan& p, Plan* q, const char* kind) {
     if (!m.present) return;
-    p = plan_gemv(kind, m.rows, m.cols);
+    p = plan_gemv(kind, m.rows, m.cols, c.qtype);
     const int64_t nrg = (m.rows + RG - 1) / RG;
     rg_max = std::max<int64_t>(rg_max, nrg);
     part_floats = std::max<size_t>(part_floats, (size_t)nrg * p.ks * mt * RG);
