@@ -39,7 +39,7 @@ PREFILL = 512
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "hbm_traffic_hybrid64_q4_decode.md")
-CHAIN_SOURCES = ("slq.h", "dev.h", "gemv_kernel.h", "deltanet.h", "chain.hip", "slice.cpp")
+CHAIN_SOURCES = ("slq.h", "dev.h", "gemv_kernel.h", "deltanet.h", "attn_merge.h", "chain.hip", "slice.cpp")
 
 
 def chain_source_hash() -> str:
@@ -654,10 +654,11 @@ def main() -> int:
         chain_launches = n_launch * args.gemv_reps
         rl_bytes = chain_step_bytes(shape, synth.Q4_0, deltanet=not args.no_chain_dn) // n_launch
         rl_kernel = (f"k_chain<2>: {n_launch} launches per step, each running the chained phases of consecutive "
-                     f"layers up to the next attention layer (per layer: the DeltaNet state update in DeltaNet "
-                     f"layers, mixer output, RMSNorm + gate/up + SwiGLU, down + residual, next layer's input "
-                     f"projections); bytes and time are means over {chain_launches} launches ({args.gemv_reps} "
-                     f"passes over the step's launches in step order), HIP events")
+                     f"layers up to the next attention layer's split kernel (per layer: the DeltaNet state update, "
+                     f"or first in the launch the attention merge, then mixer output, RMSNorm + gate/up + SwiGLU, "
+                     f"down + residual, next layer's input projections); bytes (weights, activations, DeltaNet "
+                     f"states; not the attention partials) and time are means over {chain_launches} launches "
+                     f"({args.gemv_reps} passes over the step's launches in step order), HIP events")
         rl_ms = chain_ms
     else:
         rl_bytes = gemv_bytes(f1_rows, f1_cols, synth.Q4_0)

@@ -23,7 +23,7 @@
 //
 // K cache layout: [kv][pos/64][head_dim/8][64 pos][8] (a wave reads 64 rows'
 // 16-byte pieces as one contiguous 1 KiB); V cache: [kv][pos][head_dim].
-#include "dev.h"
+#include "attn_merge.h"
 #include <algorithm>
 
 namespace slq {
@@ -625,7 +625,6 @@ __global__ __launch_bounds__(256) void k_attn_split(AttnParams p, int T) {
 // sum in the same order.
 constexpr int CW = 8;
 __global__ __launch_bounds__(64 * CW) void k_attn_combine(AttnParams p) {
-  constexpr int VPRE = 32;   // chunks whose values are requested with the statistics
   __shared__ float wsh[2048];
   __shared__ float red[CW][64];
   __shared__ float mred[CW], lred[CW];
@@ -634,46 +633,18 @@ __global__ __launch_bounds__(64 * CW) void k_attn_combine(AttnParams p) {
   const int h = (blockIdx.x / ndg) % p.q_heads;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, nw = blockDim.x >> 6;
   const int d = (blockIdx.x % ndg) * 64 + lane;
-  // the gate input does not depend on the position: request it first
-  const float gz = p.off_g >= 0 && w == 0 ? p.y[(size_t)t * p.y_stride + p.off_g + h * p.hd + d] : 0.0f;
   const int P = (p.ctrl ? p.ctrl->pos : p.pos) + p.pos_off + t;
   const int nc = P / ATT_CHUNK / p.rchunks + 1;   // partials that token t reaches
+  if (nc <= 64) {   // one wave
+    if (w == 0) merge_wave<false>(p, t, h, (blockIdx.x % ndg) * 64, nc, wsh);
+    return;
+  }
+  // the gate input does not depend on the position
+  const float gz = p.off_g >= 0 && w == 0 ? p.y[(size_t)t * p.y_stride + p.off_g + h * p.hd + d] : 0.0f;
   const int stride = p.hd + 2;
   const float* base = p.part + ((size_t)t * p.q_heads + h) * p.nchunk * stride;
   float o = 0.0f, L = 0.0f;
-  if (nc <= 64) {
-    float M = -INFINITY;
-    float v0[VPRE];
-    if (w == 0) {
-      // one round of requests: every chunk's max and sum (lane c) and the
-      // first VPRE chunks' values of dimension d
-      float m0 = -INFINITY, l0 = 0.0f;
-      if (lane < nc) {
-        m0 = base[(size_t)lane * stride];
-        l0 = base[(size_t)lane * stride + 1];
-      }
-#pragma unroll
-      for (int u = 0; u < VPRE; ++u) v0[u] = u < nc ? base[(size_t)u * stride + 2 + d] : 0.0f;
-      M = wave_max(m0);
-      const float wt = lane < nc ? __expf(m0 - M) : 0.0f;
-      L = wave_sum((lane < nc ? l0 : 0.0f) * wt);
-      if (lane < nc) wsh[lane] = wt;
-    }
-    __syncthreads();
-    if (w != 0) return;
-    // the weighted values, added in chunk order
-#pragma unroll
-    for (int u = 0; u < VPRE; ++u)
-      if (u < nc) o = __builtin_fmaf(v0[u], wsh[u], o);
-    for (int c0 = VPRE; c0 < nc; c0 += 8) {
-      float v[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = c0 + u < nc ? base[(size_t)(c0 + u) * stride + 2 + d] : 0.0f;
-#pragma unroll
-      for (int u = 0; u < 8; ++u)
-        if (c0 + u < nc) o = __builtin_fmaf(v[u], wsh[c0 + u], o);
-    }
-  } else {
+  {
     const int c_lo = nc * w / nw, c_hi = nc * (w + 1) / nw;
     float mw = -INFINITY;
     for (int c = c_lo + lane; c < c_hi; c += 64) mw = fmaxf(mw, base[(size_t)c * stride]);
@@ -731,7 +702,7 @@ __global__ __launch_bounds__(64 * CW) void k_attn_combine(AttnParams p) {
 hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {
   if (p.hd % 64 || p.hd > 256 || p.rope_dims % 2 || p.rope_dims > p.hd || p.max_seq % 64 ||
       p.nchunk * ATT_CHUNK < p.max_seq || (p.rope_dims && !p.rope_cs) ||
-      p.q_heads % p.kv_heads || T < 1 || T > MAX_T)
+      p.q_heads % p.kv_heads || T < 1 || T > MAX_T || (p.split_only && (T != 1 || p.nchunk > 64)))
     return hipErrorInvalidValue;
   // Chunks per partial, from the cache size alone (decode and verify must
   // merge alike): one up to 1024 (KV head, chunk) pairs, beyond that enough
@@ -744,6 +715,7 @@ hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {
   const int grp = p.q_heads / p.kv_heads;
   const int npairs = p.kv_heads * p.nchunk;
   const int R = npairs > 1024 ? std::min(16, (npairs + 511) / 512) : 1;
+  if (p.split_only && R != 1) return hipErrorInvalidValue;
   AttnParams q = p;
   q.rchunks = R;
   // Query heads per split workgroup: with one token on a cache of at least
@@ -791,7 +763,8 @@ hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s) {
 #undef SLQ_G
 #undef SLQ_RT
 #undef SLQ_R1
-  k_attn_combine<<<T * p.q_heads * (p.hd / 64), nrange > 64 ? 64 * CW : 64, 0, s>>>(q);
+  // the chained decode kernel merges (merge_wave) what the split leaves
+  if (!p.split_only) k_attn_combine<<<T * p.q_heads * (p.hd / 64), nrange > 64 ? 64 * CW : 64, 0, s>>>(q);
   return hipGetLastError();
 }
 

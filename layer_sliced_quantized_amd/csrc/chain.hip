@@ -49,6 +49,7 @@
 // kernel, and the kernel boundary drops copies from earlier kernels.
 #include "gemv_kernel.h"
 #include "deltanet.h"
+#include "attn_merge.h"
 
 namespace slq {
 
@@ -268,6 +269,32 @@ __device__ __forceinline__ void chain_dn_phase(const ChainArgs& args, int p, int
   chain_complete(p, id, args.ph[p].nwg, args.gsize[p], sync, epoch_v, (int)(threadIdx.x & 63));
 }
 
+// An attention layer's merge (one decode token) as the first phase of the
+// launch after its split kernel: wave w of workgroup id merges (head, 64 dims)
+// number 4 id + w over the partials the token reaches (merge_wave, as the
+// combine kernel does; the partials and the gate input were written before
+// the launch), the output digits stored coherently for the mixer output
+// projection that follows.  Each workgroup counts as one row group.
+__device__ __forceinline__ void chain_att_merge_phase(const ChainArgs& args, int p, int id, uint8_t* __restrict__ ws,
+                                                      unsigned* __restrict__ sync, const unsigned& epoch_v,
+                                                      float (*red)[RG]) {
+  const ChainPhase& ph = args.ph[p];
+  AttnParams a = args.att;
+  a.next.xd = reinterpret_cast<int32_t*>(ws + ph.nd_off);
+  a.next.xs = reinterpret_cast<float*>(ws + ph.ns_off);
+  const int wave = wave_id();
+  const int ndg = a.hd / 64;
+  const int job = 4 * id + wave;
+  const int pos = (a.ctrl ? a.ctrl->pos : a.pos) + a.pos_off;
+  if (job < a.q_heads * ndg) merge_wave<true>(a, 0, job / ndg, (job % ndg) * 64, pos / ATT_CHUNK + 1, red[wave]);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0);
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __syncthreads();
+  if (wave != 0) return;
+  chain_complete(p, id, ph.nwg, args.gsize[p], sync, epoch_v, (int)(threadIdx.x & 63));
+}
+
 template <int QT>
 __global__ __launch_bounds__(256) void k_chain(const ChainArgs args, const uint8_t* __restrict__ wts,
                                                const uint8_t* __restrict__ dig, uint8_t* __restrict__ ws,
@@ -293,6 +320,9 @@ __global__ __launch_bounds__(256) void k_chain(const ChainArgs args, const uint8
         default: chain_dn_phase<16>(args, p, id, sync, ctrl, ws, epoch_v, &s_ok); break;
       }
       break;
+    case EPI_ATT_COMB:
+      chain_att_merge_phase(args, p, id, ws, sync, epoch_v, red);
+      break;
     case EPI_STORE:
       chain_phase<QT, EPI_STORE>(args.ph[p], p, id, args.gsize[p], wts, dig, ws, sync, ctrl, epoch_v, red, &s_ok);
       break;
@@ -316,6 +346,15 @@ hipError_t launch_chain(int qt, const ChainArgs& args, unsigned grid, const uint
          args.dn.dk != 8 * args.dn_dkp || (args.dn_dkp != 4 && args.dn_dkp != 8 && args.dn_dkp != 12 &&
                                            args.dn_dkp != 16) || args.dn.mode != DN_DECODE))
       return hipErrorInvalidValue;
+  // an attention merge comes first (its split ran as the kernel before), one
+  // workgroup per four (head, 64 dims), at most 64 partials of one chunk each
+  for (int p = 0; p < args.nph; ++p) {
+    if (args.ph[p].epi != EPI_ATT_COMB) continue;
+    const AttnParams& a = args.att;
+    if (p != 0 || a.hd % 64 || a.hd > 256 || a.q_heads <= 0 || a.nchunk > 64 ||
+        args.ph[p].nwg != (a.q_heads * (a.hd / 64) + 3) / 4)
+      return hipErrorInvalidValue;
+  }
   if (qt == QT_Q4) k_chain<QT_Q4><<<grid, 256, 0, s>>>(args, weights, ws, ws, sync, ctrl);
   else k_chain<QT_Q8><<<grid, 256, 0, s>>>(args, weights, ws, ws, sync, ctrl);
   return hipGetLastError();

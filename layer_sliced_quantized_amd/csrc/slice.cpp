@@ -56,7 +56,8 @@ int override_int(const std::string& name, int dflt) {
 }
 
 bool override_name_ok(const std::string& n) {
-  if (n == "MFMA_MIN_T" || n == "EAGER" || n == "CHAIN" || n == "CHAIN_MAX" || n == "CHAIN_DN") return true;
+  if (n == "MFMA_MIN_T" || n == "EAGER" || n == "CHAIN" || n == "CHAIN_MAX" || n == "CHAIN_DN" || n == "CHAIN_ATT")
+    return true;
   static const char* kinds[] = {"G1", "G2", "F1", "F2", "HEAD", "GEMV", "G1P", "G2P", "F1P", "F2P",
                                 "G1W", "G2W", "F1W", "F2W"};
   for (const char* k : kinds)
@@ -486,6 +487,8 @@ struct slice {
   int mx_min_t = 0;   // GEMVs with at least this many tokens use the MFMA products (0: by format and plan)
   bool chain = false;                 // decode steps run the chained GEMV kernels
   bool chain_dn = false;              // ... with each DeltaNet layer's update as a phase
+  bool chain_att = false;             // ... and each attention layer's merge as the first phase of
+                                      // the launch after its split kernel
   struct ChainLaunch {
     int layer;                        // the layer whose mixer it follows
     ChainArgs args;                   // descriptors (kernel arguments)
@@ -561,6 +564,37 @@ static Act act_from(const Act& a, int t0, int qt) {
   return r;
 }
 
+// Attention parameters of layer i for tokens t0 .. of a step of Tall tokens.
+static AttnParams attn_params(slice* s, int i, int Tall, int t0) {
+  const slice_config& c = s->cfg;
+  const Layout& L = s->L;
+  const LayerLayout& ll = L.layers[i];
+  AttnParams p{};
+  p.y = s->wsp<float>(L.y1) + (size_t)t0 * ll.g1.rows;
+  p.y_stride = ll.g1.rows;
+  p.off_q = ll.off_q; p.off_g = ll.off_g; p.off_k = ll.off_k; p.off_v = ll.off_v;
+  p.q_heads = c.q_heads; p.kv_heads = c.kv_heads; p.hd = c.head_dim; p.rope_dims = c.rope_dims;
+  p.rope_theta = c.rope_theta;
+  p.rope_cs = s->wsp<float>(L.rope);
+  p.qk_norm = c.qk_norm;
+  p.q_norm = reinterpret_cast<const float*>(s->w + ll.q_norm);
+  p.k_norm = reinterpret_cast<const float*>(s->w + ll.k_norm);
+  p.eps = c.eps;
+  uint8_t* kvb = s->ws + L.kv + (size_t)ll.attn_index * L.kv_layer_bytes;
+  p.kc = reinterpret_cast<__half*>(kvb);
+  p.vc = reinterpret_cast<__half*>(kvb + (size_t)c.kv_heads * c.max_seq * c.head_dim * 2);
+  p.max_seq = c.max_seq;
+  p.ctrl = s->ctrl();
+  p.part = s->wsp<float>(L.apart);
+  p.nchunk = L.nchunk;
+  p.rchunks = 1;
+  p.u_out = nullptr;
+  p.pos_off = t0;
+  p.next = act_from(s->act_u(Tall), t0, c.qtype);
+  p.next_qt = c.qtype;
+  return p;
+}
+
 // Layer i's mixer for tokens t0 .. t0 + T - 1 of a step of Tall tokens.
 static int enqueue_mixer_part(slice* s, int i, int Tall, int t0, int T, int mode, hipStream_t st) {
   const slice_config& c = s->cfg;
@@ -568,28 +602,7 @@ static int enqueue_mixer_part(slice* s, int i, int Tall, int t0, int T, int mode
   const LayerLayout& ll = L.layers[i];
   float* y1 = s->wsp<float>(L.y1) + (size_t)t0 * ll.g1.rows;
   if (ll.attn) {
-    AttnParams p{};
-    p.y = y1;
-    p.y_stride = ll.g1.rows;
-    p.off_q = ll.off_q; p.off_g = ll.off_g; p.off_k = ll.off_k; p.off_v = ll.off_v;
-    p.q_heads = c.q_heads; p.kv_heads = c.kv_heads; p.hd = c.head_dim; p.rope_dims = c.rope_dims;
-    p.rope_theta = c.rope_theta;
-    p.rope_cs = s->wsp<float>(L.rope);
-    p.qk_norm = c.qk_norm;
-    p.q_norm = reinterpret_cast<const float*>(s->w + ll.q_norm);
-    p.k_norm = reinterpret_cast<const float*>(s->w + ll.k_norm);
-    p.eps = c.eps;
-    uint8_t* kvb = s->ws + L.kv + (size_t)ll.attn_index * L.kv_layer_bytes;
-    p.kc = reinterpret_cast<__half*>(kvb);
-    p.vc = reinterpret_cast<__half*>(kvb + (size_t)c.kv_heads * c.max_seq * c.head_dim * 2);
-    p.max_seq = c.max_seq;
-    p.ctrl = s->ctrl();
-    p.part = s->wsp<float>(L.apart);
-    p.nchunk = L.nchunk;
-    p.u_out = nullptr;
-    p.pos_off = t0;
-    p.next = act_from(s->act_u(Tall), t0, c.qtype);
-    p.next_qt = c.qtype;
+    const AttnParams p = attn_params(s, i, Tall, t0);
     HIPCHK(launch_attention(p, T, st));
   } else {
     DnParams p = dn_params(s, i, T, mode);
@@ -659,7 +672,13 @@ static int enqueue_step(slice* s, int T, int mode, hipStream_t st, Prof* prof = 
       SLQ_MARK(l0.attn ? SLICE_OP_ATT_IN : SLICE_OP_DN_IN);
     }
     for (int i = 0; i < nlay; ++i) {
-      if (only < 0 && (L.layers[i].attn || !s->chain_dn)) {
+      if (only < 0 && L.layers[i].attn && s->chain_att) {
+        // the split only: the next chained launch merges it first
+        AttnParams p = attn_params(s, i, 1, 0);
+        p.split_only = 1;
+        HIPCHK(launch_attention(p, 1, st));
+        SLQ_MARK(SLICE_OP_ATTENTION);
+      } else if (only < 0 && (L.layers[i].attn || !s->chain_dn)) {
         int rc = enqueue_mixer(s, i, 1, DN_DECODE, st);
         if (rc) return rc;
         SLQ_MARK(L.layers[i].attn ? SLICE_OP_ATTENTION : SLICE_OP_DELTANET);
@@ -781,7 +800,7 @@ static void build_chains(slice* s) {
     cl.layer = open[0].layer;
     cl.args.nph = (int)open.size();
     cl.args.first_wg[0] = 0;
-    int dn_layer = -1;
+    int dn_layer = -1, att_layer = -1;
     for (int k = 0; k < cl.args.nph; ++k) {
       ChainPhase q = open[k].ph;
       // split-K regions in turn: a phase runs only after the one before has
@@ -793,6 +812,7 @@ static void build_chains(slice* s) {
       const int nrg = (int)((q.rows + RG - 1) / RG);
       cl.args.gsize[k] = (nrg + 31) / 32;   // at most 32 completion groups
       if (q.epi == EPI_DN && dn_layer < 0) dn_layer = open[k].layer;
+      if (q.epi == EPI_ATT_COMB && att_layer < 0) att_layer = open[k].layer;
     }
     cl.grid = (unsigned)cl.args.first_wg[cl.args.nph];
     if (dn_layer >= 0) {
@@ -800,6 +820,7 @@ static void build_chains(slice* s) {
       cl.args.dn = dn_params(s, dn_layer, 1, DN_DECODE);
       cl.args.dn_dkp = c.dn_dk / 8;
     }
+    if (att_layer >= 0) cl.args.att = attn_params(s, att_layer, 1, 0);   // output digits come per phase
     cl.sync = sync;
     sync += (size_t)cl.args.nph * CHAIN_PHASE_SYNC_BYTES;
     s->chain_launch.push_back(cl);
@@ -859,9 +880,24 @@ static void build_chains(slice* s) {
       d.ns_off = (int64_t)ll.cxu_s;
       ph.push_back(d);
     }
+    const bool merge_phase = s->chain_att && ll.attn;
+    if (merge_phase) {
+      // the layer's attention merge, four (head, 64 dims) per workgroup, into this layer's digits
+      ChainPhase m{};
+      m.epi = EPI_ATT_COMB;
+      m.nwg = (c.q_heads * (c.head_dim / 64) + 3) / 4;
+      m.rows = (int64_t)m.nwg * RG;   // counted as nwg row groups
+      m.ksplit = 1;
+      m.w = 4;
+      m.qt = c.qtype;
+      m.xd_off = m.xs_off = m.ssq_off = m.ssq_out_off = m.y_off = m.norm_w_off = -1;
+      m.nd_off = (int64_t)ll.cxu_d;
+      m.ns_off = (int64_t)ll.cxu_s;
+      ph.push_back(m);
+    }
     ChainPhase& g2 = add(ll.g2, ll.pg2, EPI_RESID);
-    // the update's digits, or the separate mixer's (written before the launch)
-    if (dn_phase) input(g2, ll.cxu_d, ll.cxu_s, nblkU, -1);
+    // the update's or the merge's digits, or the separate mixer's (written before the launch)
+    if (dn_phase || merge_phase) input(g2, ll.cxu_d, ll.cxu_s, nblkU, -1);
     else input(g2, L.xu_d, L.xu_s, nblkU, -1);
     if (c.ffn) {
       resid(g2, ll.cxa_d, ll.cxa_s, L.ssq, ll.ffn_norm);
@@ -1307,6 +1343,9 @@ int slice_load(const slice_config* cfg, void* weights_dev, void* workspace_dev, 
   s->chain = chains_possible(s) && override_int("CHAIN", 1) != 0;
   // the qwen3_5 form's update takes a workgroup per head, too wide for the chain
   s->chain_dn = s->chain && !cfg->dn_variant && override_int("CHAIN_DN", 1) != 0;
+  // the chained merge takes one token's partials of single chunks, at most 64
+  s->chain_att = s->chain && s->L.n_attn > 0 && s->L.nchunk <= 64 && (int64_t)cfg->kv_heads * s->L.nchunk <= 1024 &&
+                 override_int("CHAIN_ATT", 1) != 0;
   if (s->chain) build_chains(s);
   if (he == hipSuccess) he = hipStreamCreate(&s->cap);
   if (he != hipSuccess) {

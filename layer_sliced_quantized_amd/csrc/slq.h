@@ -91,7 +91,11 @@ struct NormIn {
 };
 
 // GEMV epilogues
-enum Epi { EPI_STORE = 0, EPI_SWIGLU = 2, EPI_RESID = 3, EPI_DN = 7 /* chained DeltaNet decode phase */ };
+enum Epi {
+  EPI_STORE = 0, EPI_SWIGLU = 2, EPI_RESID = 3,
+  EPI_DN = 7,          // chained DeltaNet decode phase
+  EPI_ATT_COMB = 9     // chained attention merge (four (head, 64-dim) merges per workgroup)
+};
 
 // With ksplit > 1 the K tiles of a 64-row group are spread over ksplit
 // workgroups; each publishes its partial sums, and the last one to finish
@@ -193,67 +197,6 @@ hipError_t launch_deltanet(const DnParams& p, int T, hipStream_t s);
 hipError_t launch_state_io(float* state, int nslots, const Ctrl* ctrl, int heads, int dk, int dv,
                            float* canon, int to_device, hipStream_t s);
 
-// ------------------------------------------------------- chained single-token GEMVs
-// One kernel runs up to CHAIN_MAX_PHASES dependent phases of a decode step,
-// in step order and across layers: a DeltaNet layer's recurrent update
-// (EPI_DN), its mixer output projection, the gate/up projection, the down
-// projection, the next layer's input projections, then the next DeltaNet
-// layer's update, and so on.  A phase's workgroups first request what does
-// not depend on the phase before (a GEMV its first weight tile, an update
-// its state rows), then wait until every row group of the phase before has
-// finished, then compute exactly what the separate kernel computes
-// (chain.hip).
-constexpr int CHAIN_MAX_PHASES = 20;
-// split-K partial and ticket regions, taken in turn by the phases of a launch
-constexpr int CHAIN_PART_BUFS = 5;
-// per phase of a chain launch: 33 counter lines, then 64 ready-flag lines
-constexpr int CHAIN_PHASE_LINES = 33 + 64;
-constexpr int CHAIN_PHASE_SYNC_BYTES = CHAIN_PHASE_LINES * 128;
-struct ChainPhase {   // one GEMV of the chain; lives in device memory
-  // every location is a byte offset: weights and norm weights into the
-  // weights buffer, everything else into the workspace.  EPI_DN: y_off is
-  // the layer's state (slot 0), nd_off / ns_off its output digits; the rest
-  // of the update's parameters come from ChainArgs::dn
-  int64_t w_off, rows, cols;          // packed matrix
-  int64_t xd_off, xs_off;             // input digits and their block scales
-  int64_t ssq_off;                    // RMSNorm partial sums of the input (-1: none)
-  int64_t y_off, y_tstride;           // STORE: y; RESID: h; SWIGLU: -1
-  int64_t nd_off, ns_off;             // SWIGLU / RESID: output digits and scales
-  int64_t ssq_out_off;                // RESID: sums of squares of h
-  int64_t norm_w_off;                 // RESID: weights of the next RMSNorm
-  int64_t part_off, cnt_off;          // split-K partials and tickets
-  int x_nblk, n_nblk;                 // blocks per token of the input / output digits
-  int n_part;                         // partial sums per token of the input statistics
-  float inv_n, eps;                   // RMSNorm of the input: 1 / width, epsilon
-  int qt;                             // weight format (also of the output digits)
-  int ksplit;                         // split-K workgroups per row group
-  int nwg;                            // workgroups of this phase: row groups x ksplit
-  int epi;                            // EPI_STORE, EPI_SWIGLU, EPI_RESID, or EPI_DN (rows = nwg workgroups)
-  int w;                              // waves of the product (<= 4; the others idle)
-};
-// Kernel arguments of one chained launch (by value, so the workgroups read
-// their product's descriptor without a dependent memory load).
-struct ChainArgs {
-  ChainPhase ph[CHAIN_MAX_PHASES];
-  int nph;
-  int first_wg[CHAIN_MAX_PHASES + 1];   // workgroup index where product p starts; [nph] = grid
-  int gsize[CHAIN_MAX_PHASES];          // row groups per completion group of product p
-  DnParams dn;                          // the EPI_DN phases: one decode token (T = 1); state and
-                                        // output digits per phase (ChainPhase)
-  int dn_dkp;                           // its d_k / 8
-};
-// sync region of one chain launch (nph * CHAIN_PHASE_SYNC_BYTES, zero before
-// its first launch), each counter and flag in its own 128-byte line (u32
-// index), in block p = 32 * CHAIN_PHASE_LINES * p of product p:
-//   [block + 32 g], g < 32: row groups of group g of product p finished (over
-//                    all launches); g = 32: groups of product p finished;
-//   [block + 32 (33 + c)]: copy c of product p's ready flag, the last launch
-//                    (1, 2, ...) whose product p is complete.
-hipError_t launch_chain(int qt, const ChainArgs& args, unsigned grid, const uint8_t* weights, uint8_t* ws,
-                        unsigned* sync, Ctrl* ctrl, hipStream_t s);
-// ctrl->err = 0 and the sync regions cleared (n_u32 words)
-hipError_t launch_chain_reset(unsigned* sync, size_t n_u32, Ctrl* ctrl, hipStream_t s);
-
 struct AttnParams {
   const float* y;        // G1 output [T][y_stride]
   int64_t y_stride;
@@ -275,11 +218,78 @@ struct AttnParams {
   int rchunks;           // chunks per partial (set by launch_attention from the cache size)
   float* u_out;          // [T][q_heads*hd] (nullable)
   Act next; int next_qt; // digits of the output (next.xd == nullptr: none)
+  int split_only;        // 1: one token on at most 64 partials, merged later by the chained decode
+                         // kernel's first phase (launch_attention runs the split only)
 };
 constexpr int ATT_CHUNK = 32;    // KV rows per split-attention workgroup
 hipError_t launch_attention(const AttnParams& p, int T, hipStream_t s);
 hipError_t launch_rope_table(float* cs, int max_seq, int rope_dims, double theta, hipStream_t s);
 hipError_t launch_kv_io(__half* kc, __half* vc, int kv_heads, int max_seq, int hd,
                         uint16_t* k, uint16_t* v, int rows, int to_device, hipStream_t s);
+
+// ------------------------------------------------------- chained single-token GEMVs
+// One kernel runs up to CHAIN_MAX_PHASES dependent phases of a decode step,
+// in step order and across layers: a DeltaNet layer's recurrent update
+// (EPI_DN), its mixer output projection, the gate/up projection, the down
+// projection, the next layer's input projections, then the next DeltaNet
+// layer's update, and so on.  A phase's workgroups first request what does
+// not depend on the phase before (a GEMV its first weight tile, an update
+// its state rows), then wait until every row group of the phase before has
+// finished, then compute exactly what the separate kernel computes
+// (chain.hip).
+constexpr int CHAIN_MAX_PHASES = 20;
+// split-K partial and ticket regions, taken in turn by the phases of a launch
+constexpr int CHAIN_PART_BUFS = 5;
+// per phase of a chain launch: 33 counter lines, then 64 ready-flag lines
+constexpr int CHAIN_PHASE_LINES = 33 + 64;
+constexpr int CHAIN_PHASE_SYNC_BYTES = CHAIN_PHASE_LINES * 128;
+struct ChainPhase {   // one GEMV of the chain; lives in device memory
+  // every location is a byte offset: weights and norm weights into the
+  // weights buffer, everything else into the workspace.  EPI_DN: y_off is
+  // the layer's state (slot 0), nd_off / ns_off its output digits; the rest
+  // of the update's parameters come from ChainArgs::dn.  EPI_ATT_COMB: nd_off / ns_off
+  // its output digits; the rest from ChainArgs::att
+  int64_t w_off, rows, cols;          // packed matrix
+  int64_t xd_off, xs_off;             // input digits and their block scales
+  int64_t ssq_off;                    // RMSNorm partial sums of the input (-1: none)
+  int64_t y_off, y_tstride;           // STORE: y; RESID: h; SWIGLU: -1
+  int64_t nd_off, ns_off;             // SWIGLU / RESID: output digits and scales
+  int64_t ssq_out_off;                // RESID: sums of squares of h
+  int64_t norm_w_off;                 // RESID: weights of the next RMSNorm
+  int64_t part_off, cnt_off;          // split-K partials and tickets
+  int x_nblk, n_nblk;                 // blocks per token of the input / output digits
+  int n_part;                         // partial sums per token of the input statistics
+  float inv_n, eps;                   // RMSNorm of the input: 1 / width, epsilon
+  int qt;                             // weight format (also of the output digits)
+  int ksplit;                         // split-K workgroups per row group
+  int nwg;                            // workgroups of this phase: row groups x ksplit
+  int epi;                            // EPI_STORE, EPI_SWIGLU, EPI_RESID, or EPI_DN / EPI_ATT_COMB (rows = nwg workgroups)
+  int w;                              // waves of the product (<= 4; the others idle)
+};
+// Kernel arguments of one chained launch (by value, so the workgroups read
+// their product's descriptor without a dependent memory load).
+struct ChainArgs {
+  ChainPhase ph[CHAIN_MAX_PHASES];
+  int nph;
+  int first_wg[CHAIN_MAX_PHASES + 1];   // workgroup index where product p starts; [nph] = grid
+  int gsize[CHAIN_MAX_PHASES];          // row groups per completion group of product p
+  DnParams dn;                          // the EPI_DN phases: one decode token (T = 1); state and
+                                        // output digits per phase (ChainPhase)
+  int dn_dkp;                           // its d_k / 8
+  AttnParams att;                       // the EPI_ATT_COMB phases: one decode token; output digits
+                                        // per phase (ChainPhase)
+};
+// sync region of one chain launch (nph * CHAIN_PHASE_SYNC_BYTES, zero before
+// its first launch), each counter and flag in its own 128-byte line (u32
+// index), in block p = 32 * CHAIN_PHASE_LINES * p of product p:
+//   [block + 32 g], g < 32: row groups of group g of product p finished (over
+//                    all launches); g = 32: groups of product p finished;
+//   [block + 32 (33 + c)]: copy c of product p's ready flag, the last launch
+//                    (1, 2, ...) whose product p is complete.
+hipError_t launch_chain(int qt, const ChainArgs& args, unsigned grid, const uint8_t* weights, uint8_t* ws,
+                        unsigned* sync, Ctrl* ctrl, hipStream_t s);
+// ctrl->err = 0 and the sync regions cleared (n_u32 words)
+hipError_t launch_chain_reset(unsigned* sync, size_t n_u32, Ctrl* ctrl, hipStream_t s);
+
 
 }  // namespace slq

@@ -106,14 +106,27 @@ def test_chain_with_verify_and_graph_replays(ovr):
     b.sync_check()
 
 
-@pytest.mark.parametrize("extra", [{"CHAIN_DN": 0}, {"CHAIN_MAX": 5}, {"CHAIN_MAX": 2}, {"CHAIN_MAX": 1}],
-                         ids=["deltanet_own_kernel", "one_layer_per_launch", "two_phases_per_launch",
-                              "one_phase_per_launch"])
+@pytest.mark.parametrize("extra", [{"CHAIN_DN": 0}, {"CHAIN_ATT": 0}, {"CHAIN_MAX": 5}, {"CHAIN_MAX": 2},
+                                   {"CHAIN_MAX": 1}],
+                         ids=["deltanet_own_kernel", "attention_merge_own_kernel", "one_layer_per_launch",
+                              "two_phases_per_launch", "one_phase_per_launch"])
 def test_chain_variants_equal_separate_kernels(extra, ovr):
-    """The DeltaNet update as its own kernel, one layer's phases per launch
-    (the update first, waiting for nothing), or the layer's phases spread over
-    several launches: the same bits as separate kernels, states included.  (By
-    default one launch runs all three DeltaNet layers, each update waiting for
-    the input projections before it.)"""
+    """The DeltaNet update or the attention merge as kernels of their own,
+    one layer's phases per launch (the update first, waiting for nothing), or
+    a layer's phases spread over several launches: the same bits as separate
+    kernels, states and caches included.  (By default one launch runs all
+    three DeltaNet layers, each update waiting for the input projections
+    before it, and the attention layer's launch starts with its merge.)"""
     ovr(**extra)
     _compare(TINY_H, synth.Q4_0, 0, 4, ovr, 4, 99, [0, 1, 2], 3, prefill=20, max_seq=128, max_verify=4)
+
+
+@pytest.mark.timeout(300)
+def test_chained_attention_merge_at_its_limit(ovr):
+    """A cache of 64 chunks (2048 rows), the most the chained merge takes,
+    with the position in its last chunk: the same bits as separate kernels,
+    and so for a cache one chunk past the limit (the merge as its own
+    kernel)."""
+    for max_seq in (2048, 2112):
+        _compare(TINY_H, synth.Q4_0, 0, 4, ovr, 3, 98, [0, 1, 2], 3, prefill=max_seq - 8, max_seq=max_seq,
+                 max_verify=4)
