@@ -86,14 +86,15 @@ def mixer_rows_cols(shape, l):
     return 2 * nk + 2 * nv + 2 * shape.dn_heads, nv
 
 
-def chain_step_bytes(shape, qtype, deltanet: bool = True) -> int:
+def chain_step_bytes(shape, qtype, deltanet: bool = True, first_g1: bool = False) -> int:
     """Algorithmic bytes of one decode step's chained launches (all layers):
     a DeltaNet layer's state update (fp32 state read and written, its input
     projections' outputs read), mixer output, gate/up, down and, except after
     the last layer, the next layer's input projections -- packed weights plus
-    fp32 activations."""
+    fp32 activations; with first_g1 also the first layer's input projections
+    (which then open the first launch)."""
     H, F, n = shape.hidden, shape.ffn, shape.n_layers
-    total = 0
+    total = gemv_bytes(mixer_rows_cols(shape, 0)[0], H, qtype) if first_g1 else 0
     for l in range(n):
         if deltanet and not shape.is_attention(l):
             total += 2 * shape.dn_heads * shape.dn_dk * shape.dn_dv * 4 + 4 * mixer_rows_cols(shape, l)[0]
@@ -652,7 +653,9 @@ def main() -> int:
         n_launch = ops["chain"][1]
         chain_ms = time_gemv_op(s, "chain", args.gemv_reps) / n_launch
         chain_launches = n_launch * args.gemv_reps
-        rl_bytes = chain_step_bytes(shape, synth.Q4_0, deltanet=not args.no_chain_dn) // n_launch
+        # the first layer's input projections open the first launch unless they show as their own op
+        first_g1 = "dn_in" not in ops and "att_in" not in ops
+        rl_bytes = chain_step_bytes(shape, synth.Q4_0, deltanet=not args.no_chain_dn, first_g1=first_g1) // n_launch
         rl_kernel = (f"k_chain<2>: {n_launch} launches per step, each running the chained phases of consecutive "
                      f"layers up to the next attention layer's split kernel (per layer: the DeltaNet state update, "
                      f"or first in the launch the attention merge, then mixer output, RMSNorm + gate/up + SwiGLU, "

@@ -461,9 +461,10 @@ const char *slice_last_error(void);
  * "MFMA_MIN_T" (fewest tokens sent to the matrix-core products), "EAGER"
  * (1: slices launch op by op instead of replaying graphs), "CHAIN" (0: decode
  * launches every product as its own kernel; the results are the same bits),
- * "CHAIN_MAX" (1..20: phases per chained kernel), "CHAIN_DN" / "CHAIN_ATT"
- * (0: the DeltaNet update / the attention merge as kernels of their own
- * instead of phases of the chained kernel).  value < 0 removes
+ * "CHAIN_MAX" (1..20: phases per chained kernel), "CHAIN_DN" / "CHAIN_ATT" /
+ * "CHAIN_G1" (0: the DeltaNet update / the attention merge / the first
+ * layer's input projections as kernels of their own instead of phases of the
+ * chained kernel).  value < 0 removes
  * the override.  Process-wide; slices take them at slice_load, slq_gemv at
  * each call.  Nothing else (no environment variable) changes a launch shape,
  * and so the summation order.  SLICE_EINVAL for an unknown name. */

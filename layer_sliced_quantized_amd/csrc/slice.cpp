@@ -56,7 +56,8 @@ int override_int(const std::string& name, int dflt) {
 }
 
 bool override_name_ok(const std::string& n) {
-  if (n == "MFMA_MIN_T" || n == "EAGER" || n == "CHAIN" || n == "CHAIN_MAX" || n == "CHAIN_DN" || n == "CHAIN_ATT")
+  if (n == "MFMA_MIN_T" || n == "EAGER" || n == "CHAIN" || n == "CHAIN_MAX" || n == "CHAIN_DN" || n == "CHAIN_ATT" ||
+      n == "CHAIN_G1")
     return true;
   static const char* kinds[] = {"G1", "G2", "F1", "F2", "HEAD", "GEMV", "G1P", "G2P", "F1P", "F2P",
                                 "G1W", "G2W", "F1W", "F2W"};
@@ -405,7 +406,8 @@ Layout make_layout(const slice_config& c) {
       L.ccnt[p] = take(L.ccnt_n * 4);
     }
     // at most five phases per layer (update, mixer output, gate/up, down, next input projections)
-    L.chain_sync_bytes = L.layers.size() * 5 * CHAIN_PHASE_SYNC_BYTES;
+    // (and the first layer's input projections)
+    L.chain_sync_bytes = (L.layers.size() * 5 + 1) * CHAIN_PHASE_SYNC_BYTES;
     L.chain_sync = take(L.chain_sync_bytes);
     for (LayerLayout& ll : L.layers) {
       ll.cxu_d = take((size_t)XW * 4 * nblkU);
@@ -489,6 +491,8 @@ struct slice {
   bool chain_dn = false;              // ... with each DeltaNet layer's update as a phase
   bool chain_att = false;             // ... and each attention layer's merge as the first phase of
                                       // the launch after its split kernel
+  bool chain_g1_first = false;        // ... and the first layer's input projections (a DeltaNet layer)
+                                      // as the first phase of the first launch
   struct ChainLaunch {
     int layer;                        // the layer whose mixer it follows
     ChainArgs args;                   // descriptors (kernel arguments)
@@ -665,11 +669,13 @@ static int enqueue_step(slice* s, int T, int mode, hipStream_t st, Prof* prof = 
       HIPCHK(launch_resid_finish(c.io_fp32 ? 2 : 1, nullptr, ctrl, H, 1, H, h, norm_at(attn_norm_off(s, 0)), qt,
                                  s->act_b(), s->wsp<float>(L.ssq_b), st));
       SLQ_MARK(SLICE_OP_ENTRY);
-      const LayerLayout& l0 = L.layers[0];
-      GemvOut o = g1_out();
-      o.y_tstride = l0.g1.rows;
-      HIPCHK(launch_gemv(s->packed(l0.g1), 1, s->act_b(), s->norm_b(), o, l0.pg1.ks, l0.pg1.w, st));
-      SLQ_MARK(l0.attn ? SLICE_OP_ATT_IN : SLICE_OP_DN_IN);
+      if (!s->chain_g1_first) {   // else the first chained launch starts with them
+        const LayerLayout& l0 = L.layers[0];
+        GemvOut o = g1_out();
+        o.y_tstride = l0.g1.rows;
+        HIPCHK(launch_gemv(s->packed(l0.g1), 1, s->act_b(), s->norm_b(), o, l0.pg1.ks, l0.pg1.w, st));
+        SLQ_MARK(l0.attn ? SLICE_OP_ATT_IN : SLICE_OP_DN_IN);
+      }
     }
     for (int i = 0; i < nlay; ++i) {
       if (only < 0 && L.layers[i].attn && s->chain_att) {
@@ -832,7 +838,7 @@ static void build_chains(slice* s) {
     // a mixer that runs as a kernel of its own comes between two launches
     if (!dn_phase) close();
     std::vector<ChainPhase> ph;
-    ph.reserve(5);   // add() hands out references into it
+    ph.reserve(6);   // add() hands out references into it
     auto add = [&](const Mat& m, const Plan& pl, int epi) -> ChainPhase& {
       ChainPhase q{};
       q.w_off = (int64_t)m.off;
@@ -865,6 +871,13 @@ static void build_chains(slice* s) {
       q.ssq_out_off = (int64_t)ssq_out;
       q.norm_w_off = (int64_t)norm_w;
     };
+    if (i == 0 && s->chain_g1_first) {
+      // the first layer's input projections, from the entry kernel's digits
+      ChainPhase& g1 = add(ll.g1, ll.pg1, EPI_STORE);
+      input(g1, L.xb_d, L.xb_s, nblkH, (int64_t)L.ssq_b);
+      g1.y_off = (int64_t)L.y1;
+      g1.y_tstride = ll.g1.rows;
+    }
     if (dn_phase) {
       // the layer's DeltaNet update: one workgroup per 32 state rows of a head
       ChainPhase d{};
@@ -1344,6 +1357,8 @@ int slice_load(const slice_config* cfg, void* weights_dev, void* workspace_dev, 
   // the qwen3_5 form's update takes a workgroup per head, too wide for the chain
   s->chain_dn = s->chain && !cfg->dn_variant && override_int("CHAIN_DN", 1) != 0;
   // the chained merge takes one token's partials of single chunks, at most 64
+  s->chain_g1_first = s->chain_dn && !s->L.layers.empty() && !s->L.layers[0].attn &&
+                      override_int("CHAIN_G1", 1) != 0;
   s->chain_att = s->chain && s->L.n_attn > 0 && s->L.nchunk <= 64 && (int64_t)cfg->kv_heads * s->L.nchunk <= 1024 &&
                  override_int("CHAIN_ATT", 1) != 0;
   if (s->chain) build_chains(s);

@@ -58,6 +58,8 @@ def test_traffic_of_the_committed_profile():
         pytest.skip("the chained-products kernel sources changed after its PMC traffic was taken")
     text = open(bench.TRAFFIC_PROFILE).read()
     launches = int(re.search(r"launches_per_step: (\d+)", text).group(1))
-    alg = bench.chain_step_bytes(synth.HYBRID_5120, synth.Q4_0, deltanet="DeltaNet" in text) / launches
+    m = re.search(r"first_input_projections_chained: (\d)", text)
+    alg = bench.chain_step_bytes(synth.HYBRID_5120, synth.Q4_0, deltanet="DeltaNet" in text,
+                                 first_g1=bool(m and m.group(1) == "1")) / launches
     # measured HBM bytes per launch against the algorithmic bytes: no re-read of weights
     assert 0.99 * alg <= t <= 1.05 * alg

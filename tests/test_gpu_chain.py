@@ -106,17 +106,18 @@ def test_chain_with_verify_and_graph_replays(ovr):
     b.sync_check()
 
 
-@pytest.mark.parametrize("extra", [{"CHAIN_DN": 0}, {"CHAIN_ATT": 0}, {"CHAIN_MAX": 5}, {"CHAIN_MAX": 2},
-                                   {"CHAIN_MAX": 1}],
-                         ids=["deltanet_own_kernel", "attention_merge_own_kernel", "one_layer_per_launch",
-                              "two_phases_per_launch", "one_phase_per_launch"])
+@pytest.mark.parametrize("extra", [{"CHAIN_DN": 0}, {"CHAIN_ATT": 0}, {"CHAIN_G1": 0}, {"CHAIN_MAX": 5},
+                                   {"CHAIN_MAX": 2}, {"CHAIN_MAX": 1}],
+                         ids=["deltanet_own_kernel", "attention_merge_own_kernel", "first_input_own_kernel",
+                              "one_layer_per_launch", "two_phases_per_launch", "one_phase_per_launch"])
 def test_chain_variants_equal_separate_kernels(extra, ovr):
-    """The DeltaNet update or the attention merge as kernels of their own,
-    one layer's phases per launch (the update first, waiting for nothing), or
-    a layer's phases spread over several launches: the same bits as separate
-    kernels, states and caches included.  (By default one launch runs all
-    three DeltaNet layers, each update waiting for the input projections
-    before it, and the attention layer's launch starts with its merge.)"""
+    """The DeltaNet update, the attention merge or the first layer's input
+    projections as kernels of their own, one layer's phases per launch, or a
+    layer's phases spread over several launches: the same bits as separate
+    kernels, states and caches included.  (By default the first launch starts
+    with the first layer's input projections and runs all three DeltaNet
+    layers, each update waiting for the input projections before it, and the
+    attention layer's launch starts with its merge.)"""
     ovr(**extra)
     _compare(TINY_H, synth.Q4_0, 0, 4, ovr, 4, 99, [0, 1, 2], 3, prefill=20, max_seq=128, max_verify=4)
 
